@@ -1,0 +1,436 @@
+"""Pins of the CPU oracle against facts fixed independently of it.
+
+Every test here runs on the CPU.  None re-types the oracle's formulas: each
+compares it with an independent computation (PyTorch autograd through a dense
+attention, central finite differences, brute-force loops, closed forms) or
+checks an invariant the mathematics fixes.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _dense_torch(q, k, v, scale, causal, G):
+    """Independent dense attention: torch CPU float64 with autograd.
+    q [N1, S, D], k/v [N2, S, D] (one batch)."""
+    qt = torch.tensor(q, dtype=torch.float64, requires_grad=True)
+    kt = torch.tensor(k, dtype=torch.float64, requires_grad=True)
+    vt = torch.tensor(v, dtype=torch.float64, requires_grad=True)
+    kr = kt.repeat_interleave(G, dim=0)
+    vr = vt.repeat_interleave(G, dim=0)
+    out = torch.nn.functional.scaled_dot_product_attention(
+        qt[None], kr[None], vr[None], is_causal=causal, scale=scale)[0]
+    return qt, kt, vt, out
+
+
+# ----------------------------------------------------------------------------
+# Dense special case: every block selected == textbook attention
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N1,N2", [(2, 2), (4, 2)])
+def test_bsa_all_blocks_equals_dense_attention(causal, N1, N2):
+    r = _rng(1)
+    S, D, bq, bkv = 40, 16, 8, 8          # ragged: 40 = 5 blocks of 8
+    q = r.standard_normal((1, N1, S, D))
+    k = r.standard_normal((1, N2, S, D))
+    v = r.standard_normal((1, N2, S, D))
+    do = r.standard_normal((1, N1, S, D))
+    scale = 1 / math.sqrt(D)
+    mask = np.ones((1, N1, 5, 5), np.uint8)
+    out, lse = oracle.bsa_fwd(q, k, v, mask, bq, bkv, scale, 2 if causal else 0)
+    qt, kt, vt, ref = _dense_torch(q[0], k[0], v[0], scale, causal, N1 // N2)
+    np.testing.assert_allclose(out[0], ref.detach().numpy(), rtol=0, atol=1e-12)
+    # LSE against torch.logsumexp over the dense scores
+    s = scale * torch.tensor(q[0]) @ torch.tensor(k[0]).repeat_interleave(N1 // N2, 0).transpose(1, 2)
+    if causal:
+        s = s.masked_fill(torch.ones(S, S, dtype=torch.bool).triu(1), -math.inf)
+    np.testing.assert_allclose(lse[0], torch.logsumexp(s, -1).numpy(), rtol=0, atol=1e-12)
+    # gradients against autograd
+    ref.backward(torch.tensor(do[0]))
+    dq, dk, dv = oracle.bsa_bwd(q, k, v, out, do, mask, bq, bkv, scale, 2 if causal else 0)
+    for mine, theirs in ((dq[0], qt.grad), (dk[0], kt.grad), (dv[0], vt.grad)):
+        t = theirs.numpy()
+        assert np.abs(mine - t).max() <= 1e-10 * np.abs(t).max()
+
+
+def test_nsa_all_blocks_equals_dense_attention():
+    r = _rng(2)
+    seqlens, N1, N2, D, sbs = [16, 24], 4, 2, 8, 4
+    cu = np.array([0, 16, 40])
+    T = 40
+    q, k, v = r.standard_normal((T, N1, D)), r.standard_normal((T, N2, D)), r.standard_normal((T, N2, D))
+    do = r.standard_normal((T, N1, D))
+    scale = 0.3
+    # every token selects every block of its sequence (sbc = blocks of the longest; the
+    # shorter sequence lists its 4 blocks; use one topk width per call -> two calls)
+    for b, S in enumerate(seqlens):
+        sl = slice(cu[b], cu[b + 1])
+        nb = S // sbs
+        topk = np.tile(r.permutation(nb), (S, N2, 1)).astype(np.int32)
+        cu1 = np.array([0, S])
+        out, lse = oracle.nsa_fwd(q[sl], k[sl], v[sl], topk, cu1, cu1, sbs, scale, 2)
+        qt, kt, vt, ref = _dense_torch(q[sl].transpose(1, 0, 2), k[sl].transpose(1, 0, 2),
+                                       v[sl].transpose(1, 0, 2), scale, True, N1 // N2)
+        np.testing.assert_allclose(out, ref.detach().numpy().transpose(1, 0, 2), atol=1e-12, rtol=0)
+        ref.backward(torch.tensor(do[sl].transpose(1, 0, 2)))
+        dq, dk, dv = oracle.nsa_bwd(q[sl], k[sl], v[sl], out, do[sl], topk, cu1, cu1, sbs, scale, 2)
+        for mine, theirs in ((dq, qt.grad), (dk, kt.grad), (dv, vt.grad)):
+            t = theirs.numpy().transpose(1, 0, 2)
+            assert np.abs(mine - t).max() <= 1e-10 * np.abs(t).max()
+
+
+def test_sfa_identity_pages_all_tokens_equals_dense_mqa():
+    r = _rng(3)
+    B, Sq, N1, D, Dr, page, kv_len = 2, 3, 4, 16, 8, 8, 24
+    q, qr = r.standard_normal((B, Sq, N1, D)), r.standard_normal((B, Sq, N1, Dr))
+    P = B * kv_len // page
+    kc, krc = r.standard_normal((P, page, 1, D)), r.standard_normal((P, page, 1, Dr))
+    bt = np.arange(P).reshape(B, kv_len // page)
+    kv_lens = np.full(B, kv_len)
+    topk = np.tile(np.arange(kv_len), (B, Sq, 1, 1))
+    scale = 1 / math.sqrt(D + Dr)
+    out, lse = oracle.sfa_fwd(q, qr, kc, krc, kc, bt, kv_lens, topk, scale, sparse_mode=3)
+    for b in range(B):
+        keys = kc[bt[b]].reshape(kv_len, D)
+        kro = krc[bt[b]].reshape(kv_len, Dr)
+        qcat = torch.tensor(np.concatenate([q[b], qr[b]], -1)).transpose(0, 1)   # [N1, Sq, D+Dr]
+        kcat = torch.tensor(np.concatenate([keys, kro], -1))[None].expand(N1, -1, -1)
+        vals = torch.tensor(keys)[None].expand(N1, -1, -1)
+        # rightDownCausal: query s at position kv_len - Sq + s
+        allowed = torch.arange(kv_len)[None, :] <= (kv_len - Sq + torch.arange(Sq))[:, None]
+        ref = torch.nn.functional.scaled_dot_product_attention(qcat, kcat, vals, attn_mask=allowed,
+                                                               scale=scale)
+        np.testing.assert_allclose(out[b], ref.numpy().transpose(1, 0, 2), atol=1e-12, rtol=0)
+
+
+def test_sfa_page_table_permutation_is_invisible():
+    """Moving pages around the physical cache (and the table with them) changes nothing."""
+    r = _rng(4)
+    B, Sq, N1, D, Dr, page, kv_len = 2, 2, 2, 8, 4, 4, 16
+    P = 10
+    q, qr = r.standard_normal((B, Sq, N1, D)), r.standard_normal((B, Sq, N1, Dr))
+    kc, krc = r.standard_normal((P, page, 1, D)), r.standard_normal((P, page, 1, Dr))
+    bt = r.permutation(P)[:8].reshape(B, 4)
+    kv_lens = np.array([16, 13])
+    topk = np.stack([np.stack([np.sort(r.choice(kv_lens[b] - Sq + s + 1, 6, replace=False))
+                               for s in range(Sq)]) for b in range(B)])[:, :, None, :]
+    o1, l1 = oracle.sfa_fwd(q, qr, kc, krc, kc, bt, kv_lens, topk, 0.25)
+    perm = r.permutation(P)                       # physical page p moves to perm[p]
+    kc2, krc2 = np.empty_like(kc), np.empty_like(krc)
+    kc2[perm], krc2[perm] = kc, krc
+    o2, l2 = oracle.sfa_fwd(q, qr, kc2, krc2, kc2, perm[bt], kv_lens, topk, 0.25)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+# ----------------------------------------------------------------------------
+# Finite differences of L = sum(dO * O)
+# ----------------------------------------------------------------------------
+
+def _fd_check(f, args, idx_names, grads, n_probe=12, h=1e-6, seed=0):
+    r = _rng(seed)
+    for name, g in zip(idx_names, grads):
+        x = args[name]
+        flat = x.reshape(-1)
+        for p in r.choice(flat.size, n_probe, replace=False):
+            old = flat[p]
+            flat[p] = old + h
+            lp = f()
+            flat[p] = old - h
+            lm = f()
+            flat[p] = old
+            fd = (lp - lm) / (2 * h)
+            an = g.reshape(-1)[p]
+            assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (name, p, fd, an)
+
+
+@pytest.mark.parametrize("mode", [0, 2])
+def test_bsa_finite_differences_gqa(mode):
+    r = _rng(5)
+    B, N1, N2, S, D, bq, bkv = 1, 2, 1, 16, 8, 4, 4
+    a = dict(q=r.standard_normal((B, N1, S, D)), k=r.standard_normal((B, N2, S, D)),
+             v=r.standard_normal((B, N2, S, D)))
+    do = r.standard_normal((B, N1, S, D))
+    mask = W.mask_random(r, B, N1, 4, 4, 0.5)
+    scale = 0.37
+
+    def loss():
+        o, _ = oracle.bsa_fwd(a["q"], a["k"], a["v"], mask, bq, bkv, scale, mode)
+        return float((do * o).sum())
+
+    o, _ = oracle.bsa_fwd(a["q"], a["k"], a["v"], mask, bq, bkv, scale, mode)
+    dq, dk, dv = oracle.bsa_bwd(a["q"], a["k"], a["v"], o, do, mask, bq, bkv, scale, mode)
+    _fd_check(loss, a, ["q", "k", "v"], [dq, dk, dv])
+
+
+@pytest.mark.parametrize("mode", [0, 2])
+def test_nsa_finite_differences(mode):
+    r = _rng(6)
+    seqlens, N1, N2, D, sbs, sbc = [12, 8], 4, 2, 8, 4, 2
+    cu = np.array([0, 12, 20])
+    T = 20
+    a = dict(q=r.standard_normal((T, N1, D)), k=r.standard_normal((T, N2, D)),
+             v=r.standard_normal((T, N2, D)))
+    do = r.standard_normal((T, N1, D))
+    topk = W.nsa_topk_causal(r, seqlens, N2, sbs, sbc)
+
+    def loss():
+        o, _ = oracle.nsa_fwd(a["q"], a["k"], a["v"], topk, cu, cu, sbs, 0.4, mode)
+        return float((do * o).sum())
+
+    o, _ = oracle.nsa_fwd(a["q"], a["k"], a["v"], topk, cu, cu, sbs, 0.4, mode)
+    dq, dk, dv = oracle.nsa_bwd(a["q"], a["k"], a["v"], o, do, topk, cu, cu, sbs, 0.4, mode)
+    _fd_check(loss, a, ["q", "k", "v"], [dq, dk, dv])
+
+
+def test_nsa_duplicate_slot_counts_twice():
+    """Gather is literal: listing a block twice doubles its weight in the softmax,
+    and its keys' gradient is the sum over both gathered copies (checked by FD)."""
+    r = _rng(7)
+    cu = np.array([0, 8])
+    a = dict(q=r.standard_normal((8, 2, 4)), k=r.standard_normal((8, 1, 4)),
+             v=r.standard_normal((8, 1, 4)))
+    do = r.standard_normal((8, 2, 4))
+    topk = np.tile(np.array([0, 0, 1], np.int32), (8, 1, 1))
+    o, _ = oracle.nsa_fwd(a["q"], a["k"], a["v"], topk, cu, cu, 4, 0.5, 0)
+    # closed form: weights of block 0 keys doubled -> same as attention with
+    # log(2) added to their scores
+    s = 0.5 * np.einsum("thd,jd->thj", a["q"], a["k"][:, 0])
+    s[:, :, :4] += math.log(2)
+    p = np.exp(s - s.max(-1, keepdims=True))
+    p /= p.sum(-1, keepdims=True)
+    np.testing.assert_allclose(o, p @ a["v"][:, 0], atol=1e-12, rtol=0)
+
+    def loss():
+        oo, _ = oracle.nsa_fwd(a["q"], a["k"], a["v"], topk, cu, cu, 4, 0.5, 0)
+        return float((do * oo).sum())
+    dq, dk, dv = oracle.nsa_bwd(a["q"], a["k"], a["v"], o, do, topk, cu, cu, 4, 0.5, 0)
+    _fd_check(loss, a, ["q", "k", "v"], [dq, dk, dv], n_probe=8)
+
+
+# ----------------------------------------------------------------------------
+# Invariants
+# ----------------------------------------------------------------------------
+
+def test_softmax_rows_sum_to_one_and_softmax_grad_identity():
+    r = _rng(8)
+    q, k, v = r.standard_normal((7, 5)), r.standard_normal((11, 5)), r.standard_normal((11, 3))
+    allowed = r.random((7, 11)) < 0.6
+    allowed[:, 0] = True
+    out, lse, p = oracle.attend_fwd(q, k, v, allowed, 0.8)
+    assert np.abs(p.sum(1) - 1).max() <= 1e-12
+    assert np.all(p[~allowed] == 0)
+    do = r.standard_normal((7, 3))
+    # softmaxGrad read as rowsum(dO * O) equals rowsum(P * dP): the identity the
+    # softmax Jacobian requires of it
+    dp = do @ v.T
+    assert np.abs((do * out).sum(1) - (p * dp).sum(1)).max() <= 1e-12
+    # LSE is the log of the softmax denominator: exp(S - LSE) == P
+    s = np.where(allowed, 0.8 * q @ k.T, -np.inf)
+    np.testing.assert_allclose(np.exp(s - lse[:, None]), p, atol=1e-14, rtol=0)
+
+
+def test_empty_row_convention():
+    q, k, v = np.ones((2, 3)), np.ones((4, 3)), np.ones((4, 2))
+    allowed = np.array([[True, False, False, False], [False] * 4])
+    out, lse, p = oracle.attend_fwd(q, k, v, allowed, 1.0)
+    assert np.all(out[1] == 0) and lse[1] == -np.inf and np.all(p[1] == 0)
+    dq, dk, dv = oracle.attend_bwd(q, k, v, allowed, out, np.ones((2, 2)), 1.0)
+    assert np.all(dq[1] == 0)
+
+
+@pytest.mark.parametrize("mode", [0, 2])
+def test_bsa_unselected_blocks_do_not_matter(mode):
+    r = _rng(9)
+    B, N1, N2, S, D, bq, bkv = 1, 2, 2, 32, 8, 8, 8
+    q, k, v = (r.standard_normal((B, N1, S, D)), r.standard_normal((B, N2, S, D)),
+               r.standard_normal((B, N2, S, D)))
+    do = r.standard_normal((B, N1, S, D))
+    mask = W.mask_random(r, B, N1, 4, 4, 0.4)
+    mask[:, :, :, 3] = 0                       # KV block 3 selected by nobody
+    o, l = oracle.bsa_fwd(q, k, v, mask, bq, bkv, 0.3, mode)
+    g = oracle.bsa_bwd(q, k, v, o, do, mask, bq, bkv, 0.3, mode)
+    k2, v2 = k.copy(), v.copy()
+    k2[:, :, 24:] += 10 * r.standard_normal((B, N2, 8, D))
+    v2[:, :, 24:] += 10 * r.standard_normal((B, N2, 8, D))
+    o2, l2 = oracle.bsa_fwd(q, k2, v2, mask, bq, bkv, 0.3, mode)
+    g2 = oracle.bsa_bwd(q, k2, v2, o2, do, mask, bq, bkv, 0.3, mode)
+    assert np.array_equal(o, o2) and np.array_equal(l, l2)
+    assert np.array_equal(g[0], g2[0])
+    assert np.array_equal(g[1][:, :, :24], g2[1][:, :, :24])
+    assert np.array_equal(g[2][:, :, :24], g2[2][:, :, :24])
+    assert np.all(g2[1][:, :, 24:] == 0) and np.all(g2[2][:, :, 24:] == 0)
+
+
+def test_nsa_slot_order_only_changes_rounding():
+    r = _rng(10)
+    cu = np.array([0, 32])
+    q, k, v = r.standard_normal((32, 4, 8)), r.standard_normal((32, 2, 8)), r.standard_normal((32, 2, 8))
+    topk = W.nsa_topk_causal(r, [32], 2, 4, 3)
+    o1, l1 = oracle.nsa_fwd(q, k, v, topk, cu, cu, 4, 0.3, 2)
+    o2, l2 = oracle.nsa_fwd(q, k, v, topk[:, :, ::-1].copy(), cu, cu, 4, 0.3, 2)
+    np.testing.assert_allclose(o1, o2, atol=1e-13, rtol=0)
+    np.testing.assert_allclose(l1, l2, atol=1e-13, rtol=0)
+
+
+# ----------------------------------------------------------------------------
+# Closed forms
+# ----------------------------------------------------------------------------
+
+def test_constant_values_closed_form():
+    """V rows all equal to c: O = c for every non-empty row, dP - softmax_grad = 0
+    so dQ = dK = 0 exactly, and dV_j = sum_i P_ij dO_i."""
+    r = _rng(11)
+    B, N1, N2, S, D, bq, bkv = 1, 2, 1, 24, 8, 8, 8
+    q, k = r.standard_normal((B, N1, S, D)), r.standard_normal((B, N2, S, D))
+    c = r.standard_normal(D)
+    v = np.broadcast_to(c, (B, N2, S, D)).copy()
+    do = r.standard_normal((B, N1, S, D))
+    mask = W.mask_random(r, B, N1, 3, 3, 0.5)
+    o, _ = oracle.bsa_fwd(q, k, v, mask, bq, bkv, 0.5)
+    np.testing.assert_allclose(o, np.broadcast_to(c, o.shape), atol=1e-13, rtol=0)
+    dq, dk, dv = oracle.bsa_bwd(q, k, v, o, do, mask, bq, bkv, 0.5)
+    assert np.abs(dq).max() <= 1e-13 and np.abs(dk).max() <= 1e-13
+    # dV from the explicit probabilities of one tile
+    keys = oracle.bsa_keys(mask[0, 1, 2], bkv, S)
+    _, _, p = oracle.attend_fwd(q[0, 1, 16:24], k[0, 0, keys], v[0, 0, keys],
+                                np.ones((8, len(keys)), bool), 0.5)
+    contrib = p.T @ do[0, 1, 16:24]
+    # head 1 tile 2's contribution is part of dv; check a KV block only it selects
+    only = [kb for kb in range(3) if mask[0, 1, 2, kb] and mask[0, :, :, kb].sum() == 1]
+    for kb in only:
+        sel = np.searchsorted(keys, np.arange(kb * 8, kb * 8 + 8))
+        np.testing.assert_allclose(dv[0, 0, kb * 8:kb * 8 + 8], contrib[sel], atol=1e-13, rtol=0)
+
+
+def test_zero_query_gives_uniform_average():
+    r = _rng(12)
+    B, N, S, D = 1, 1, 16, 4
+    q = np.zeros((B, N, S, D))
+    k, v = r.standard_normal((B, N, S, D)), r.standard_normal((B, N, S, D))
+    mask = np.array([[[[1, 0], [1, 1]]]], np.uint8)
+    o, lse = oracle.bsa_fwd(q, k, v, mask, 8, 8, 1.0)
+    np.testing.assert_allclose(o[0, 0, :8], np.broadcast_to(v[0, 0, :8].mean(0), (8, D)), atol=1e-14)
+    np.testing.assert_allclose(o[0, 0, 8:], np.broadcast_to(v[0, 0, :].mean(0), (8, D)), atol=1e-14)
+    np.testing.assert_allclose(lse[0, 0, :8], math.log(8), atol=1e-14)
+    np.testing.assert_allclose(lse[0, 0, 8:], math.log(16), atol=1e-14)
+
+
+# ----------------------------------------------------------------------------
+# Cross-path: NSA with G = 1 and block-constant selection is block-sparse attention
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("mode", [0, 2])
+def test_nsa_equals_bsa_for_block_constant_selection(mode):
+    r = _rng(13)
+    S, N, D, sbs, sbc = 32, 2, 8, 4, 3
+    nb = S // sbs
+    q, k, v = r.standard_normal((S, N, D)), r.standard_normal((S, N, D)), r.standard_normal((S, N, D))
+    do = r.standard_normal((S, N, D))
+    # one selection per (query block, head): own block + 2 distinct others
+    sel = np.zeros((N, nb, sbc), np.int32)
+    mask = np.zeros((1, N, nb, nb), np.uint8)
+    for n in range(N):
+        for qb in range(nb):
+            others = r.choice([x for x in range(nb) if x != qb], sbc - 1, replace=False)
+            sel[n, qb] = np.concatenate([[qb], others])
+            mask[0, n, qb, sel[n, qb]] = 1
+    topk = np.stack([sel[:, t // sbs] for t in range(S)])          # [S, N, sbc]
+    cu = np.array([0, S])
+    on, ln = oracle.nsa_fwd(q, k, v, topk, cu, cu, sbs, 0.35, mode)
+    qb_, kb_, vb_ = (x.transpose(1, 0, 2)[None] for x in (q, k, v))
+    ob, lb = oracle.bsa_fwd(qb_, kb_, vb_, mask, sbs, sbs, 0.35, mode)
+    np.testing.assert_allclose(on, ob[0].transpose(1, 0, 2), atol=1e-13, rtol=0)
+    np.testing.assert_allclose(ln, lb[0].T, atol=1e-13, rtol=0)
+    gn = oracle.nsa_bwd(q, k, v, on, do, topk, cu, cu, sbs, 0.35, mode)
+    gb = oracle.bsa_bwd(qb_, kb_, vb_, ob, do.transpose(1, 0, 2)[None], mask, sbs, sbs, 0.35, mode)
+    for a_, b_ in zip(gn, gb):
+        np.testing.assert_allclose(a_, b_[0].transpose(1, 0, 2), atol=1e-12, rtol=0)
+
+
+# ----------------------------------------------------------------------------
+# Compaction: brute force and closed-form counts
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("shape,n2", [((2, 4, 5, 7), 2), ((1, 3, 1, 1), 3), ((1, 2, 6, 4), 1)])
+def test_bsa_compact_brute_force(shape, n2):
+    r = _rng(14)
+    B, N1, QB, KB = shape
+    mask = (r.random(shape) < 0.4).astype(np.uint8) * r.integers(1, 5, shape).astype(np.uint8)
+    mask[0, 0, 0, :] = 0                                          # an empty row
+    rp, col, rvp, rv = oracle.bsa_compact(mask, n2)
+    G = N1 // n2
+    fwd_rows, rev_rows = [], []
+    for b in range(B):
+        for n in range(N1):
+            for qb in range(QB):
+                fwd_rows.append([kb for kb in range(KB) if mask[b, n, qb, kb]])
+    for b in range(B):
+        for h in range(n2):
+            for kb in range(KB):
+                rev_rows.append([g * QB + qb for g in range(G) for qb in range(QB)
+                                 if mask[b, h * G + g, qb, kb]])
+    for ptr, ent, rows in ((rp, col, fwd_rows), (rvp, rv, rev_rows)):
+        assert ptr.dtype == np.int32 and ent.dtype == np.int32
+        assert len(ptr) == len(rows) + 1 and ptr[0] == 0
+        for i, row in enumerate(rows):
+            assert ent[ptr[i]:ptr[i + 1]].tolist() == row
+
+
+def test_nsa_compact_brute_force():
+    r = _rng(15)
+    seqlens, N2, sbs, sbc = [12, 20, 8], 2, 4, 2
+    cu = np.concatenate([[0], np.cumsum(seqlens)])
+    topk = W.nsa_topk_causal(r, seqlens, N2, sbs, sbc)
+    topk[3, 1] = [2, 2]                                           # a duplicate
+    for mode in (0, 2):
+        rp, col, rvp, rv, nb = oracle.nsa_compact(topk, cu, cu, sbs, mode)
+        assert nb == 3 + 5 + 2
+        blk_off = [0, 3, 8]
+        T = cu[-1]
+        fwd = []
+        for t in range(T):
+            b = int(np.searchsorted(cu, t, side="right") - 1)
+            pos = t - cu[b]
+            for h in range(N2):
+                ids = sorted(topk[t, h].tolist())
+                fwd.append([i for i in ids if mode == 0 or i * sbs <= pos])
+        for i, row in enumerate(fwd):
+            assert col[rp[i]:rp[i + 1]].tolist() == row
+        for h in range(N2):
+            for gb in range(nb):
+                b = max(j for j in range(3) if blk_off[j] <= gb)
+                want = []
+                for t in range(T):
+                    if cu[b] <= t < cu[b + 1]:
+                        want += [t] * fwd[t * N2 + h].count(gb - blk_off[b])
+                row = h * nb + gb
+                assert rv[rvp[row]:rvp[row + 1]].tolist() == want
+
+
+def test_workload_closed_form_counts():
+    with open(os.path.join(GOLDEN, "workload_counts.json")) as f:
+        gold = json.load(f)
+    cu, _, _, _, _, topk = W.nsa_inputs()
+    rp, _, _, _, _ = oracle.nsa_compact(topk, cu, cu, 64, 2)
+    assert int(rp[-1]) == gold["nsa_varlen_effective_triples"]
+    mask = W.bsa_mask(W.bsa_workload(5), 1005)
+    assert int((mask != 0).sum()) == gold["bsa_window_128k_selected_pairs"]
+    # recipe properties of the NSA selection: distinct ids, own block present
+    own = (np.arange(topk.shape[0]) - np.repeat(cu[:-1], np.diff(cu))) // 64
+    assert np.all(np.sort(topk, -1)[..., 1:] != np.sort(topk, -1)[..., :-1])
+    assert np.all((topk == own[:, None, None]).any(-1))
