@@ -1,0 +1,313 @@
+/*
+ * top_selected_attention.h -- C ABI of the MI355X (gfx950) library for
+ * attention restricted to selected key blocks.
+ *
+ * Three front-ends share one engine:
+ *   - block-sparse attention (BSA): a BlockSparseMask names, per Q block, the
+ *     KV blocks it attends to ("aclnnBlockSparseAttentionGrad", function
+ *     description and formula section);
+ *   - NSA selected attention: per (token, KV head) topk_indices name the
+ *     selected key blocks ("aclnnNsaSelectedAttention", formulas section);
+ *   - sparse flash attention (SFA) decode over a paged, shared KV cache with
+ *     per-token top-k positions ("aclnnSparseFlashAttention", formulas and
+ *     constraints sections; "SparseAttnSharedkvMetadata", parameter list).
+ *
+ * Calling pattern (the two-phase pattern of the CANN operator pages, "calls"
+ * section of each): first XXX_workspace_size(args, &bytes) validates the
+ * arguments on the host -- it never touches the device and never reads device
+ * memory -- and returns the workspace size; then XXX(args, ws, ws_bytes,
+ * stream) re-validates and enqueues the kernels on `stream`.
+ *
+ * Ownership: the caller owns every buffer, including the workspace.  The
+ * library never allocates or frees device memory and keeps no device state
+ * besides its loaded code objects; calls are reentrant.  Device pointers are
+ * borrowed until the work enqueued on `stream` completes.  Host pointers
+ * (marked HOST) are read during the call only.
+ *
+ * Pointers marked DEVICE must be device memory of the current HIP device.
+ * All tensors are dense and contiguous in the stated layout.  `stream` is a
+ * hipStream_t (NULL = the null stream).
+ *
+ * Errors: every function returns a tsa_status.  No exceptions cross the ABI
+ * and nothing calls exit().  The CANN pages' own error-code tables were lost,
+ * so the values below are this library's.
+ */
+#ifndef TOP_SELECTED_ATTENTION_H
+#define TOP_SELECTED_ATTENTION_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define TSA_API __attribute__((visibility("default")))
+#else
+#define TSA_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TSA_OK = 0,
+  TSA_ERR_NULL = 1,          /* a required pointer is NULL */
+  TSA_ERR_INVALID = 2,       /* a value or shape violates a documented constraint */
+  TSA_ERR_UNSUPPORTED = 3,   /* valid for the operator, not built in this library */
+  TSA_ERR_WORKSPACE = 4,     /* workspace NULL or smaller than XXX_workspace_size */
+  TSA_ERR_HIP = 5,           /* a HIP launch or runtime call failed */
+  TSA_ERR_DATA = 6           /* validate = 1 found bad data (ids out of range) */
+} tsa_status;
+
+enum { TSA_BF16 = 0, TSA_FP16 = 1 };
+enum { TSA_LAYOUT_BNSD = 0, TSA_LAYOUT_TND = 1, TSA_LAYOUT_BSND = 2 };
+
+/* Text for a status code (static storage, never NULL). */
+TSA_API const char* tsa_status_string(int status);
+
+/* sizeof of each argument struct, for binding checks: which = 0 bsa_fwd,
+ * 1 bsa_bwd, 2 nsa_select_fwd, 3 nsa_select_bwd, 4 sfa_paged_fwd;
+ * returns 0 for an unknown value. */
+TSA_API size_t tsa_args_sizeof(int which);
+
+/* ------------------------------------------------------------------------
+ * Block-sparse attention.
+ *
+ * Forward ("aclnnBlockSparseAttentionGrad", formula section):
+ *   Out = Softmax(Mask(scale * Q * K_sparse^T, atten_mask)) * V_sparse,
+ * where K_sparse/V_sparse of a Q block are the rows of the KV blocks its mask
+ * row selects.  Also writes LSE = row max + ln(row sum of exp), fp32 (natural
+ * log), which the backward uses.
+ *
+ * Layout: BNSD only (the page's constraints section: only BNSD is supported).
+ *   q [B, N1, Sq, D], k [B, N2, Skv, D], v [B, N2, Skv, D], out like q,
+ *   lse fp32 [B, N1, Sq].  D must be 128 (constraints section: headdim=128).
+ *   N1 % N2 == 0 (constraints section); query head n1 reads KV head n1/(N1/N2).
+ * block_mask: u8 DEVICE [B, N1, ceil(Sq/block_q), ceil(Skv/block_kv)],
+ *   non-zero = the Q block attends to that KV block (blockShapeX = block_q
+ *   rows, blockShapeY = block_kv keys; function description).  Tail blocks of
+ *   a ragged Sq / Skv are partial.
+ * sparse_mode: 0 = the selected blocks in full; 2 = additionally causal,
+ *   key position j <= query position i (top-left aligned).
+ * block_q, block_kv: 1..65536 (any size; partial tiles are masked).
+ * A Q block that selects nothing gets Out = 0 and LSE = -inf.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  int32_t dtype;            /* TSA_BF16 or TSA_FP16 (q, k, v, out, dout, dq, dk, dv) */
+  int32_t q_layout;         /* TSA_LAYOUT_BNSD */
+  int32_t kv_layout;        /* TSA_LAYOUT_BNSD */
+  int32_t B, N1, N2, Sq, Skv, D;
+  int32_t block_q, block_kv;
+  int32_t sparse_mode;      /* 0 or 2 */
+  float scale;              /* typically 1/sqrt(D) */
+  int32_t validate;         /* reserved for BSA (masks cannot hold bad data); 0 */
+  const uint8_t* block_mask;/* DEVICE */
+  const void* q;            /* DEVICE */
+  const void* k;            /* DEVICE */
+  const void* v;            /* DEVICE */
+  void* out;                /* DEVICE, written */
+  float* lse;               /* DEVICE, written */
+} bsa_fwd_args;
+
+TSA_API int bsa_fwd_workspace_size(const bsa_fwd_args* args, size_t* bytes);
+TSA_API int bsa_fwd(const bsa_fwd_args* args, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward ("aclnnBlockSparseAttentionGrad", formula section):
+ *   softmax_grad = rowsum(dOut * Out)   (the page's softmaxGrad(dOut, Out))
+ *   dP = dOut V^T,  dS = P * (dP - softmax_grad),  dV = P^T dOut,
+ *   dQ = (dS K) scale,  dK = (dS^T Q) scale,
+ * over the selected blocks only; P is recomputed from Q, K and the forward's
+ * LSE.  dK/dV of a KV head sum over its N1/N2 query heads and every Q block
+ * that selected the row; rows nobody selects get 0.  Deterministic: no atomics,
+ * a fixed summation order, bit-identical results across runs.
+ * Same shape fields as the forward; out/dout like q, lse from bsa_fwd.
+ * dq like q, dk/dv like k/v (all written in full). */
+typedef struct {
+  int32_t dtype;
+  int32_t q_layout;
+  int32_t kv_layout;
+  int32_t B, N1, N2, Sq, Skv, D;
+  int32_t block_q, block_kv;
+  int32_t sparse_mode;
+  float scale;
+  int32_t validate;
+  const uint8_t* block_mask;/* DEVICE */
+  const void* q;            /* DEVICE */
+  const void* k;            /* DEVICE */
+  const void* v;            /* DEVICE */
+  const void* out;          /* DEVICE, the forward output */
+  const void* dout;         /* DEVICE */
+  const float* lse;         /* DEVICE, the forward LSE */
+  void* dq;                 /* DEVICE, written */
+  void* dk;                 /* DEVICE, written */
+  void* dv;                 /* DEVICE, written */
+} bsa_bwd_args;
+
+TSA_API int bsa_bwd_workspace_size(const bsa_bwd_args* args, size_t* bytes);
+TSA_API int bsa_bwd(const bsa_bwd_args* args, void* workspace, size_t workspace_bytes, void* stream);
+
+/* The selected-block lists of a BlockSparseMask, as the kernels use them
+ * (exposed so they can be checked bit for bit).  Uses args->B, N1, N2, Sq,
+ * Skv, block_q, block_kv and block_mask only.  With R = B*N1*QB rows and
+ * C = B*N2*KB KV blocks (QB = ceil(Sq/block_q), KB = ceil(Skv/block_kv)):
+ *   row_ptr int32 DEVICE [R+1]: CSR pointers, row (b, n1, qb) row-major;
+ *   col     int32 DEVICE [R*KB]: ascending kb per row (first row_ptr[R] used);
+ *   rev_ptr int32 DEVICE [C+1]: CSR pointers, row (b, n2, kb) row-major;
+ *   rev     int32 DEVICE [R*KB]: per KV block, ascending ids g*QB + qb of the
+ *           Q blocks of query heads n1 = n2*G + g that selected it.
+ * Needs a workspace of bsa_compact_workspace_size bytes. */
+TSA_API int bsa_compact_workspace_size(const bsa_fwd_args* args, size_t* bytes);
+TSA_API int bsa_compact(const bsa_fwd_args* args, int32_t* row_ptr, int32_t* col, int32_t* rev_ptr,
+                int32_t* rev, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * NSA selected attention ("aclnnNsaSelectedAttention").
+ *
+ * Forward (formulas section): selected_key/value = Gather(key/value,
+ * topk_indices[i]) for 0 <= i < selected_block_count; attention_out =
+ * Softmax(Mask(scale * query @ selected_key^T, atten_mask)) @ selected_value.
+ * Backward: the chain of "aclnnBlockSparseAttentionGrad" (formula section)
+ * applied to the gathered keys, each gathered row's gradient added back to
+ * its source row (deterministic, no atomics).
+ *
+ * Layout TND only (constraints section): q [T, N1, D], k [Tk, N2, D],
+ * v [Tk, N2, Dv], out [T, N1, Dv], lse fp32 [T, N1].  D = Dv = 128.
+ * cu_seqlens_q / cu_seqlens_kv: HOST int32 [B+1] prefix sums starting at 0
+ *   ("SparseAttnSharedkvMetadata", parameter list: cu_seqlens are B+1 prefix
+ *   sums); cu_seqlens_q[B] == T, cu_seqlens_kv[B] == Tk.
+ * topk: int32 DEVICE [T, N2, sbc], block ids counted in units of sbs from the
+ *   start of the token's own sequence; a listed id counts once per listing.
+ * sbs (selected_block_size): multiple of 16, at most 128 (constraints).
+ * sbc (selected_block_count): 1..128, sbs*sbc <= 8192 (constraints).
+ * Every KV sequence length is >= sbs*sbc and a multiple of sbs (constraints).
+ * N1 % N2 == 0, G = N1/N2 <= 32.
+ * sparse_mode: 0 = no mask; 2 = causal, key j <= query position i within
+ *   the sequence; blocks wholly after the query are skipped.
+ * validate = 1: one extra device pass checks that every id is in range
+ *   (0 <= id < ceil(Skv_b/sbs)) and synchronises `stream`; TSA_ERR_DATA if
+ *   not.  With validate = 0 out-of-range ids are skipped.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  int32_t dtype;
+  int32_t layout;           /* TSA_LAYOUT_TND */
+  int32_t B;                /* number of sequences */
+  int32_t T, Tk;            /* total query / key tokens */
+  int32_t N1, N2, D, Dv;
+  const int32_t* cu_seqlens_q;   /* HOST [B+1] */
+  const int32_t* cu_seqlens_kv;  /* HOST [B+1] */
+  int32_t sbs, sbc;
+  int32_t sparse_mode;      /* 0 or 2 */
+  float scale;
+  int32_t validate;
+  const int32_t* topk;      /* DEVICE [T, N2, sbc] */
+  const void* q;            /* DEVICE */
+  const void* k;            /* DEVICE */
+  const void* v;            /* DEVICE */
+  void* out;                /* DEVICE, written */
+  float* lse;               /* DEVICE, written */
+} nsa_select_fwd_args;
+
+TSA_API int nsa_select_fwd_workspace_size(const nsa_select_fwd_args* args, size_t* bytes);
+TSA_API int nsa_select_fwd(const nsa_select_fwd_args* args, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
+typedef struct {
+  int32_t dtype;
+  int32_t layout;
+  int32_t B;
+  int32_t T, Tk;
+  int32_t N1, N2, D, Dv;
+  const int32_t* cu_seqlens_q;   /* HOST [B+1] */
+  const int32_t* cu_seqlens_kv;  /* HOST [B+1] */
+  int32_t sbs, sbc;
+  int32_t sparse_mode;
+  float scale;
+  int32_t validate;
+  const int32_t* topk;      /* DEVICE */
+  const void* q;            /* DEVICE */
+  const void* k;            /* DEVICE */
+  const void* v;            /* DEVICE */
+  const void* out;          /* DEVICE, forward output */
+  const void* dout;         /* DEVICE */
+  const float* lse;         /* DEVICE, forward LSE */
+  void* dq;                 /* DEVICE, written [T, N1, D] */
+  void* dk;                 /* DEVICE, written [Tk, N2, D] */
+  void* dv;                 /* DEVICE, written [Tk, N2, Dv] */
+} nsa_select_bwd_args;
+
+TSA_API int nsa_select_bwd_workspace_size(const nsa_select_bwd_args* args, size_t* bytes);
+TSA_API int nsa_select_bwd(const nsa_select_bwd_args* args, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
+/* The lists of topk_indices, as the kernels use them.  Uses the shape fields,
+ * cu_seqlens, sbs, sbc, sparse_mode and topk of args.  With R = T*N2 rows and
+ * NB = sum_b ceil(Skv_b/sbs) blocks:
+ *   row_ptr int32 DEVICE [R+1]; col int32 DEVICE [R*sbc]: per (t, n2) the
+ *     block ids sorted ascending (mode 2: blocks wholly after t dropped);
+ *   rev_ptr int32 DEVICE [N2*NB+1]; rev int32 DEVICE [R*sbc]: per (n2, global
+ *     block) the ascending token ids whose row holds it.
+ * nsa_compact_blocks_total() gives NB. */
+TSA_API int nsa_compact_blocks_total(const nsa_select_fwd_args* args, int32_t* blocks_total);
+TSA_API int nsa_compact_workspace_size(const nsa_select_fwd_args* args, size_t* bytes);
+TSA_API int nsa_compact(const nsa_select_fwd_args* args, int32_t* row_ptr, int32_t* col,
+                int32_t* rev_ptr, int32_t* rev, void* workspace, size_t workspace_bytes,
+                void* stream);
+
+/* ------------------------------------------------------------------------
+ * Sparse flash attention, paged shared-KV decode ("aclnnSparseFlashAttention").
+ *
+ * Formulas section: softmax(Q K~^T / sqrt(d_k)) V~ over the selected keys;
+ * a score is scale * (q . k + q_rope . k_rope).  Constraints section:
+ * D = 512 for query/key/value, Dr = 64 for the rope parts, N1 in {1, 2, 4,
+ * ..., 128}, page block_size a multiple of 16 and at most 1024, one dtype
+ * for query/key/value.  "SparseAttnSharedkvMetadata" parameter list: one KV
+ * head, PA_ND paged KV, seqused_kv = active KV length per batch, mask mode
+ * 3 = rightDownCausal.
+ *
+ * q [B, Sq, N1, D], q_rope [B, Sq, N1, Dr] (BSND);
+ * key_cache [num_pages, page_size, N2, D], key_rope_cache [num_pages,
+ *   page_size, N2, Dr], value_cache [num_pages, page_size, N2, Dv] (PA_ND);
+ *   value_cache may equal key_cache (shared KV: V is the key row).
+ * block_table int32 DEVICE [B, max_pages]: physical page of logical page p.
+ * kv_lens int32 DEVICE [B]: active KV tokens of each sequence.
+ * topk_indices int32 DEVICE [B, Sq, N2, topk]: selected sparse-block ids
+ *   (token positions when sparse_block_size == 1); -1 = empty slot.
+ * sparse_block_size: divides page_size (reading of the constraint that ties
+ *   it to block_size: a selected block never straddles a page); 1..page_size.
+ * sparse_mode: 0 = no mask; 3 = rightDownCausal (token s of Sq sits at
+ *   position kv_len - Sq + s; later keys are masked).
+ * out [B, Sq, N1, Dv]; lse fp32 [B, Sq, N1] (may be NULL).
+ * validate = 1: checks ids, kv_lens and page ids on the device, synchronises
+ *   `stream`, TSA_ERR_DATA on a bad value; with validate = 0 positions at or
+ *   beyond kv_len are skipped.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  int32_t dtype;
+  int32_t q_layout;         /* TSA_LAYOUT_BSND */
+  int32_t B, Sq, N1, N2, D, Dr, Dv;
+  int32_t num_pages, page_size, max_pages;
+  int32_t topk;
+  int32_t sparse_block_size;
+  int32_t sparse_mode;      /* 0 or 3 */
+  float scale;
+  int32_t validate;
+  const void* q;            /* DEVICE */
+  const void* q_rope;       /* DEVICE */
+  const void* key_cache;    /* DEVICE */
+  const void* key_rope_cache;/* DEVICE */
+  const void* value_cache;  /* DEVICE */
+  const int32_t* block_table;   /* DEVICE */
+  const int32_t* kv_lens;       /* DEVICE */
+  const int32_t* topk_indices;  /* DEVICE */
+  void* out;                /* DEVICE, written */
+  float* lse;               /* DEVICE, written, or NULL */
+} sfa_paged_fwd_args;
+
+TSA_API int sfa_paged_fwd_workspace_size(const sfa_paged_fwd_args* args, size_t* bytes);
+TSA_API int sfa_paged_fwd(const sfa_paged_fwd_args* args, void* workspace, size_t workspace_bytes,
+                  void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TOP_SELECTED_ATTENTION_H */

@@ -1,0 +1,169 @@
+"""Block-sparse attention on the GPU against the float64 CPU oracle.
+
+Tolerances: outputs max|gpu - ref| <= 2e-2 * max|ref|, gradients <= 3e-2 *
+max|ref| per tensor, LSE <= 2e-3 * max(1, max|ref|); lists bit-exact.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+OUT_TOL, GRAD_TOL, LSE_TOL = 2e-2, 3e-2, 2e-3
+
+
+def _tsa():
+    import top_selected_attention_amd as tsa
+    return tsa
+
+
+def _np(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def _close(gpu, ref, tol, what, rows=None):
+    g = _np(gpu) if isinstance(gpu, torch.Tensor) else gpu
+    if rows is not None:
+        g, ref = g[rows], ref[rows]
+    scale = np.abs(ref).max()
+    err = np.abs(g - ref).max()
+    assert np.isfinite(g).all(), f"{what}: non-finite values"
+    assert err <= tol * max(scale, 1e-30), f"{what}: max err {err:.3e} vs {tol} * {scale:.3e}"
+
+
+def _lse_close(gpu, ref, rows=None):
+    g = _np(gpu)
+    if rows is not None:
+        g, ref = g[rows], ref[rows]
+    fin = np.isfinite(ref)
+    assert np.array_equal(fin, np.isfinite(g)), "LSE: -inf pattern differs"
+    err = np.abs(g[fin] - ref[fin]).max() if fin.any() else 0.0
+    assert err <= LSE_TOL * max(1.0, np.abs(ref[fin]).max() if fin.any() else 1.0), err
+
+
+def _inputs(B, N1, N2, Sq, Skv, dtype, seed, mask_fn):
+    dt = "bf16" if dtype == torch.bfloat16 else "fp16"
+    q = W.normal((B, N1, Sq, 128), seed + 1, dt)
+    k = W.normal((B, N2, Skv, 128), seed + 2, dt)
+    v = W.normal((B, N2, Skv, 128), seed + 3, dt)
+    do = W.normal((B, N1, Sq, 128), seed + 4, dt)
+    mask = mask_fn(np.random.default_rng(seed))
+    return q, k, v, do, mask
+
+
+def _dev(*ts):
+    return [torch.as_tensor(t).cuda() for t in ts]
+
+
+# ----------------------------------------------------------------------------
+# Compaction: bit-exact
+# ----------------------------------------------------------------------------
+
+def _compact_case(mask, N2, Sq, Skv, bq, bkv):
+    tsa = _tsa()
+    rp, col, rvp, rv = tsa.bsa_compact(torch.from_numpy(mask).cuda(), N2, Sq, Skv, bq, bkv)
+    erp, ecol, ervp, erv = oracle.bsa_compact(mask, N2)
+    assert np.array_equal(rp.cpu().numpy(), erp)
+    assert np.array_equal(col.cpu().numpy(), ecol)
+    assert np.array_equal(rvp.cpu().numpy(), ervp)
+    assert np.array_equal(rv.cpu().numpy(), erv)
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 5])
+def test_compact_named_workloads_bit_exact(cfg):
+    w = W.bsa_workload(cfg)
+    mask = W.bsa_mask(w, 1000 + cfg)
+    _compact_case(mask, w["N2"], w["S"], w["S"], w["bq"], w["bkv"])
+
+
+@pytest.mark.parametrize("shape,n2,bq,bkv,S", [
+    ((1, 1, 1, 1), 1, 64, 64, 64),          # a single block
+    ((2, 4, 3, 70), 2, 16, 16, None),        # GQA, columns not a multiple of 64
+    ((1, 2, 130, 5), 1, 16, 16, None),       # rows spanning several row tiles
+    ((1, 3, 7, 129), 3, 32, 32, None),       # ragged both ways
+])
+def test_compact_edge_cases_bit_exact(shape, n2, bq, bkv, S):
+    rng = np.random.default_rng(7)
+    mask = (rng.random(shape) < 0.3).astype(np.uint8)
+    mask[0, 0, 0] = 0                         # an empty row
+    B, N1, QB, KB = shape
+    Sq, Skv = (S, S) if S else (QB * bq - 3 if QB * bq > 3 else QB * bq, KB * bkv - 5)
+    _compact_case(mask, n2, Sq, Skv, bq, bkv)
+    full = np.ones(shape, np.uint8)           # a full mask
+    _compact_case(full, n2, Sq, Skv, bq, bkv)
+
+
+# ----------------------------------------------------------------------------
+# Forward parity
+# ----------------------------------------------------------------------------
+
+def _fwd_check(q, k, v, mask, bq, bkv, scale, mode, q_tiles=None):
+    tsa = _tsa()
+    qd, kd, vd, md = _dev(q, k, v, torch.from_numpy(mask))
+    out, lse = tsa.bsa_fwd(qd, kd, vd, md, bq, bkv, scale, mode)
+    torch.cuda.synchronize()
+    ro, rl = oracle.bsa_fwd(_np(q), _np(k), _np(v), mask, bq, bkv, scale, mode, q_tiles=q_tiles)
+    rows = None
+    if q_tiles is not None:
+        sel = np.zeros(ro.shape[:3], bool)
+        for b, n, qb in q_tiles:
+            sel[b, n, qb * bq:(qb + 1) * bq] = True
+        rows = sel
+    _close(out, ro, OUT_TOL, "out", rows)
+    _lse_close(lse, rl, rows)
+    return out, lse
+
+
+def test_fwd_bsa_small_fp16_64x64():
+    w, q, k, v, do, mask, scale = W.bsa_inputs(1)
+    _fwd_check(q, k, v, mask, 64, 64, scale, 0)
+
+
+@pytest.mark.parametrize("mode", [0, 2])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_fwd_causal_shaped_128_several_tiles(mode, dtype):
+    # config-2 structure at a size the oracle finishes in seconds
+    q, k, v, do, mask = _inputs(1, 2, 2, 1024, 1024, dtype, 200,
+                                lambda r: W.mask_random(r, 1, 2, 8, 8, 0.25, causal=True))
+    _fwd_check(q, k, v, mask, 128, 128, 1 / math.sqrt(128), mode)
+
+
+@pytest.mark.parametrize("Sq,Skv,bq,bkv,N1,N2", [
+    (1000, 1000, 128, 128, 2, 2),   # ragged tail on both axes
+    (300, 520, 64, 96, 4, 2),       # GQA, rectangular, block_kv not a multiple of 64
+    (200, 200, 256, 32, 1, 1),      # block_q larger than a workgroup slice, small block_kv
+    (77, 150, 48, 80, 2, 1),        # odd block sizes
+])
+def test_fwd_ragged_and_gqa(Sq, Skv, bq, bkv, N1, N2):
+    QB, KB = -(-Sq // bq), -(-Skv // bkv)
+    q, k, v, do, mask = _inputs(1, N1, N2, Sq, Skv, torch.bfloat16, 300,
+                                lambda r: W.mask_random(r, 1, N1, QB, KB, 0.4, diagonal=False))
+    mask[0, 0, 0, :] = 0            # an empty Q block: out 0, lse -inf
+    for mode in (0, 2):
+        _fwd_check(q, k, v, mask, bq, bkv, 0.09, mode)
+
+
+def test_fwd_empty_inputs():
+    tsa = _tsa()
+    q = torch.empty((1, 2, 0, 128), dtype=torch.bfloat16, device="cuda")
+    k = torch.empty((1, 2, 0, 128), dtype=torch.bfloat16, device="cuda")
+    m = torch.empty((1, 2, 0, 0), dtype=torch.uint8, device="cuda")
+    out, lse = tsa.bsa_fwd(q, k, k, m, 64, 64)
+    assert out.shape == q.shape and lse.shape == (1, 2, 0)
+
+
+def test_fwd_bsa_causal_8k_sampled():
+    """The full 2x16x8192 workload in the timed launch configuration; every
+    16th Q block of each head plus the first and last are checked."""
+    w, q, k, v, do, mask, scale = W.bsa_inputs(2)
+    QB = w["S"] // w["bq"]
+    tiles = [(b, n, qb) for b in range(w["B"]) for n in range(w["N1"])
+             for qb in sorted(set(list(range(0, QB, 16)) + [QB - 1]))]
+    tiles = tiles[::4]              # a quarter of those keeps the oracle to seconds
+    _fwd_check(q, k, v, mask, w["bq"], w["bkv"], scale, 0, q_tiles=tiles)

@@ -1,0 +1,369 @@
+"""Python binding of the top-selected-attention HIP library (libtsa.so).
+
+Argument marshalling only: every function checks tensor dtypes, shapes and
+devices, sizes and allocates the workspace and outputs with torch, and calls
+the C ABI declared in ``include/top_selected_attention.h`` on torch's current
+stream.  All arithmetic runs in the library's HIP kernels; there is no other
+execution path, and importing this package raises if the library is missing.
+
+Entry points (names as in the C ABI):
+  bsa_fwd, bsa_bwd, bsa_compact             block-sparse attention (BNSD)
+  nsa_select_fwd, nsa_select_bwd, nsa_compact   NSA selected attention (TND)
+  sfa_paged_fwd                              sparse flash attention decode
+The ``*Plan`` classes pre-allocate outputs and workspace for repeated calls.
+"""
+
+import ctypes
+import math
+import os
+
+import torch
+
+from . import _abi
+from ._abi import TsaError, BF16, FP16, LAYOUT_BNSD, LAYOUT_TND, LAYOUT_BSND  # noqa: F401
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtsa.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -m top_selected_attention_amd.build` "
+        "(there is no fallback implementation)")
+
+lib = _abi.load(LIB_PATH)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float16:
+        return FP16
+    raise TypeError(f"expected bfloat16 or float16, got {t.dtype}")
+
+
+def _check(t, name, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr() if t is not None else 0)
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _workspace(nbytes, device):
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def _ceil(a, b):
+    return -(-a // b)
+
+
+# ----------------------------------------------------------------------------
+# Block-sparse attention
+# ----------------------------------------------------------------------------
+
+class BsaPlan:
+    """Forward and backward of block-sparse attention for fixed tensors.
+
+    q [B, N1, Sq, 128], k/v [B, N2, Skv, 128] (bf16 or fp16, BNSD),
+    block_mask u8 [B, N1, ceil(Sq/block_q), ceil(Skv/block_kv)].
+    ``fwd()`` writes ``self.out`` / ``self.lse``; ``bwd(dout)`` writes
+    ``self.dq`` / ``self.dk`` / ``self.dv``.
+    """
+
+    def __init__(self, q, k, v, block_mask, block_q, block_kv, scale=None, sparse_mode=0,
+                 backward=True):
+        _check(q, "q"), _check(k, "k", q.dtype), _check(v, "v", q.dtype)
+        if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+            raise ValueError("q, k, v must be BNSD with k and v of one shape")
+        B, N1, Sq, D = q.shape
+        _, N2, Skv, _ = k.shape
+        if k.shape[0] != B or k.shape[3] != D:
+            raise ValueError("q and k disagree in B or D")
+        QB, KB = _ceil(Sq, block_q), _ceil(Skv, block_kv)
+        _check(block_mask, "block_mask", torch.uint8, (B, N1, QB, KB))
+        self.q, self.k, self.v, self.mask = q, k, v, block_mask
+        self.scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+        dev = q.device
+        self.out = torch.empty_like(q)
+        self.lse = torch.empty((B, N1, Sq), dtype=torch.float32, device=dev)
+        self.fa = _abi.BsaFwdArgs(
+            dtype=_dtype_code(q), q_layout=LAYOUT_BNSD, kv_layout=LAYOUT_BNSD,
+            B=B, N1=N1, N2=N2, Sq=Sq, Skv=Skv, D=D, block_q=block_q, block_kv=block_kv,
+            sparse_mode=sparse_mode, scale=self.scale, validate=0,
+            block_mask=block_mask.data_ptr(), q=q.data_ptr(), k=k.data_ptr(), v=v.data_ptr(),
+            out=self.out.data_ptr(), lse=self.lse.data_ptr())
+        nb = ctypes.c_size_t()
+        _abi.call(lib.bsa_fwd_workspace_size, ctypes.byref(self.fa), ctypes.byref(nb))
+        self.ws_fwd = _workspace(nb.value, dev)
+        self.backward = backward
+        if backward:
+            self.dout = None
+            self.dq = torch.empty_like(q)
+            self.dk = torch.empty_like(k)
+            self.dv = torch.empty_like(v)
+            self.ba = _abi.BsaBwdArgs(
+                dtype=_dtype_code(q), q_layout=LAYOUT_BNSD, kv_layout=LAYOUT_BNSD,
+                B=B, N1=N1, N2=N2, Sq=Sq, Skv=Skv, D=D, block_q=block_q, block_kv=block_kv,
+                sparse_mode=sparse_mode, scale=self.scale, validate=0,
+                block_mask=block_mask.data_ptr(), q=q.data_ptr(), k=k.data_ptr(),
+                v=v.data_ptr(), out=self.out.data_ptr(), dout=0, lse=self.lse.data_ptr(),
+                dq=self.dq.data_ptr(), dk=self.dk.data_ptr(), dv=self.dv.data_ptr())
+
+    def fwd(self):
+        _abi.call(lib.bsa_fwd, ctypes.byref(self.fa), _ptr(self.ws_fwd),
+                  ctypes.c_size_t(self.ws_fwd.numel()), _stream())
+        return self.out, self.lse
+
+    def set_dout(self, dout):
+        _check(dout, "dout", self.q.dtype, self.q.shape)
+        self.dout = dout
+        self.ba.dout = dout.data_ptr()
+        nb = ctypes.c_size_t()
+        _abi.call(lib.bsa_bwd_workspace_size, ctypes.byref(self.ba), ctypes.byref(nb))
+        self.ws_bwd = _workspace(nb.value, self.q.device)
+
+    def set_out(self, out, lse):
+        """Use an externally produced forward output / LSE in the backward."""
+        _check(out, "out", self.q.dtype, self.q.shape)
+        _check(lse, "lse", torch.float32, self.lse.shape)
+        self.ba.out, self.ba.lse = out.data_ptr(), lse.data_ptr()
+        self._ext = (out, lse)
+
+    def bwd(self, dout=None):
+        if dout is not None and dout is not self.dout:
+            self.set_dout(dout)
+        if self.dout is None:
+            raise ValueError("bwd needs dout")
+        _abi.call(lib.bsa_bwd, ctypes.byref(self.ba), _ptr(self.ws_bwd),
+                  ctypes.c_size_t(self.ws_bwd.numel()), _stream())
+        return self.dq, self.dk, self.dv
+
+
+def bsa_fwd(q, k, v, block_mask, block_q, block_kv, scale=None, sparse_mode=0):
+    """Block-sparse attention forward: returns (out, lse)."""
+    plan = BsaPlan(q, k, v, block_mask, block_q, block_kv, scale, sparse_mode, backward=False)
+    return plan.fwd()
+
+
+def bsa_bwd(q, k, v, out, dout, lse, block_mask, block_q, block_kv, scale=None, sparse_mode=0):
+    """Block-sparse attention backward: returns (dq, dk, dv)."""
+    plan = BsaPlan(q, k, v, block_mask, block_q, block_kv, scale, sparse_mode, backward=True)
+    plan.set_out(out, lse)
+    return plan.bwd(dout)
+
+
+def bsa_compact(block_mask, N2, Sq, Skv, block_q, block_kv):
+    """The forward / reverse CSR lists of a BlockSparseMask (int32 device tensors,
+    entry arrays trimmed to their used length)."""
+    B, N1, QB, KB = block_mask.shape
+    _check(block_mask, "block_mask", torch.uint8, (B, N1, _ceil(Sq, block_q), _ceil(Skv, block_kv)))
+    dev = block_mask.device
+    a = _abi.BsaFwdArgs(dtype=BF16, q_layout=LAYOUT_BNSD, kv_layout=LAYOUT_BNSD, B=B, N1=N1,
+                        N2=N2, Sq=Sq, Skv=Skv, D=128, block_q=block_q, block_kv=block_kv,
+                        sparse_mode=0, scale=1.0, validate=0, block_mask=block_mask.data_ptr())
+    nb = ctypes.c_size_t()
+    _abi.call(lib.bsa_compact_workspace_size, ctypes.byref(a), ctypes.byref(nb))
+    ws = _workspace(nb.value, dev)
+    R, C = B * N1 * QB, B * N2 * KB
+    i32 = dict(dtype=torch.int32, device=dev)
+    row_ptr, col = torch.empty(R + 1, **i32), torch.empty(max(R * KB, 1), **i32)
+    rev_ptr, rev = torch.empty(C + 1, **i32), torch.empty(max(R * KB, 1), **i32)
+    _abi.call(lib.bsa_compact, ctypes.byref(a), _ptr(row_ptr), _ptr(col), _ptr(rev_ptr),
+              _ptr(rev), _ptr(ws), ctypes.c_size_t(ws.numel()), _stream())
+    nnz = int(row_ptr[-1].item())
+    return row_ptr, col[:nnz], rev_ptr, rev[:nnz]
+
+
+# ----------------------------------------------------------------------------
+# NSA selected attention
+# ----------------------------------------------------------------------------
+
+def _host_i32(x):
+    t = torch.as_tensor(x, dtype=torch.int32, device="cpu").contiguous()
+    return t
+
+
+class NsaPlan:
+    """Forward and backward of NSA selected attention for fixed tensors.
+
+    q [T, N1, 128], k/v [Tk, N2, 128] (TND), topk int32 [T, N2, sbc] device,
+    cu_seqlens_q / cu_seqlens_kv: B+1 prefix sums (host sequences or tensors).
+    """
+
+    def __init__(self, q, k, v, topk, cu_seqlens_q, cu_seqlens_kv, sbs, scale=None,
+                 sparse_mode=2, validate=False, backward=True):
+        _check(q, "q"), _check(k, "k", q.dtype), _check(v, "v", q.dtype)
+        T, N1, D = q.shape
+        Tk, N2, _ = k.shape
+        sbc = topk.shape[-1]
+        _check(topk, "topk", torch.int32, (T, N2, sbc))
+        self.cu_q, self.cu_kv = _host_i32(cu_seqlens_q), _host_i32(cu_seqlens_kv)
+        B = self.cu_q.numel() - 1
+        self.q, self.k, self.v, self.topk = q, k, v, topk
+        self.scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+        dev = q.device
+        self.out = torch.empty((T, N1, v.shape[2]), dtype=q.dtype, device=dev)
+        self.lse = torch.empty((T, N1), dtype=torch.float32, device=dev)
+        common = dict(dtype=_dtype_code(q), layout=LAYOUT_TND, B=B, T=T, Tk=Tk, N1=N1, N2=N2,
+                      D=D, Dv=v.shape[2],
+                      cu_seqlens_q=ctypes.cast(self.cu_q.data_ptr(), ctypes.POINTER(ctypes.c_int32)),
+                      cu_seqlens_kv=ctypes.cast(self.cu_kv.data_ptr(), ctypes.POINTER(ctypes.c_int32)),
+                      sbs=sbs, sbc=sbc, sparse_mode=sparse_mode, scale=self.scale,
+                      validate=int(bool(validate)), topk=topk.data_ptr(), q=q.data_ptr(),
+                      k=k.data_ptr(), v=v.data_ptr())
+        self.common = common
+        self.fa = _abi.NsaFwdArgs(out=self.out.data_ptr(), lse=self.lse.data_ptr(), **common)
+        nb = ctypes.c_size_t()
+        _abi.call(lib.nsa_select_fwd_workspace_size, ctypes.byref(self.fa), ctypes.byref(nb))
+        self.ws_fwd = _workspace(nb.value, dev)
+        if backward:
+            self.dout = None
+            self.dq = torch.empty_like(q)
+            self.dk = torch.empty_like(k)
+            self.dv = torch.empty_like(v)
+            self.ba = _abi.NsaBwdArgs(out=self.out.data_ptr(), dout=0, lse=self.lse.data_ptr(),
+                                      dq=self.dq.data_ptr(), dk=self.dk.data_ptr(),
+                                      dv=self.dv.data_ptr(), **common)
+
+    def fwd(self):
+        _abi.call(lib.nsa_select_fwd, ctypes.byref(self.fa), _ptr(self.ws_fwd),
+                  ctypes.c_size_t(self.ws_fwd.numel()), _stream())
+        return self.out, self.lse
+
+    def set_dout(self, dout):
+        _check(dout, "dout", self.q.dtype, self.out.shape)
+        self.dout = dout
+        self.ba.dout = dout.data_ptr()
+        nb = ctypes.c_size_t()
+        _abi.call(lib.nsa_select_bwd_workspace_size, ctypes.byref(self.ba), ctypes.byref(nb))
+        self.ws_bwd = _workspace(nb.value, self.q.device)
+
+    def set_out(self, out, lse):
+        _check(out, "out", self.q.dtype, self.out.shape)
+        _check(lse, "lse", torch.float32, self.lse.shape)
+        self.ba.out, self.ba.lse = out.data_ptr(), lse.data_ptr()
+        self._ext = (out, lse)
+
+    def bwd(self, dout=None):
+        if dout is not None and dout is not self.dout:
+            self.set_dout(dout)
+        if self.dout is None:
+            raise ValueError("bwd needs dout")
+        _abi.call(lib.nsa_select_bwd, ctypes.byref(self.ba), _ptr(self.ws_bwd),
+                  ctypes.c_size_t(self.ws_bwd.numel()), _stream())
+        return self.dq, self.dk, self.dv
+
+
+def nsa_select_fwd(q, k, v, topk, cu_seqlens_q, cu_seqlens_kv, sbs, scale=None, sparse_mode=2,
+                   validate=False):
+    """NSA selected attention forward: returns (out, lse)."""
+    return NsaPlan(q, k, v, topk, cu_seqlens_q, cu_seqlens_kv, sbs, scale, sparse_mode,
+                   validate, backward=False).fwd()
+
+
+def nsa_select_bwd(q, k, v, out, dout, lse, topk, cu_seqlens_q, cu_seqlens_kv, sbs, scale=None,
+                   sparse_mode=2, validate=False):
+    """NSA selected attention backward: returns (dq, dk, dv)."""
+    plan = NsaPlan(q, k, v, topk, cu_seqlens_q, cu_seqlens_kv, sbs, scale, sparse_mode, validate)
+    plan.set_out(out, lse)
+    return plan.bwd(dout)
+
+
+def nsa_compact(topk, cu_seqlens_q, cu_seqlens_kv, N1, sbs, sparse_mode=2, validate=False):
+    """The forward / reverse CSR lists of NSA topk_indices:
+    (row_ptr, col, rev_ptr, rev, blocks_total), device int32 tensors."""
+    T, N2, sbc = topk.shape
+    _check(topk, "topk", torch.int32)
+    cu_q, cu_kv = _host_i32(cu_seqlens_q), _host_i32(cu_seqlens_kv)
+    a = _abi.NsaFwdArgs(dtype=BF16, layout=LAYOUT_TND, B=cu_q.numel() - 1, T=T,
+                        Tk=int(cu_kv[-1]), N1=N1, N2=N2, D=128, Dv=128,
+                        cu_seqlens_q=ctypes.cast(cu_q.data_ptr(), ctypes.POINTER(ctypes.c_int32)),
+                        cu_seqlens_kv=ctypes.cast(cu_kv.data_ptr(), ctypes.POINTER(ctypes.c_int32)),
+                        sbs=sbs, sbc=sbc, sparse_mode=sparse_mode, scale=1.0,
+                        validate=int(bool(validate)), topk=topk.data_ptr(), q=1, k=1, v=1, out=1,
+                        lse=1)
+    nb = ctypes.c_size_t()
+    _abi.call(lib.nsa_compact_workspace_size, ctypes.byref(a), ctypes.byref(nb))
+    NB = ctypes.c_int32()
+    _abi.call(lib.nsa_compact_blocks_total, ctypes.byref(a), ctypes.byref(NB))
+    dev = topk.device
+    ws = _workspace(nb.value, dev)
+    i32 = dict(dtype=torch.int32, device=dev)
+    R = T * N2
+    row_ptr, col = torch.empty(R + 1, **i32), torch.empty(max(R * sbc, 1), **i32)
+    rev_ptr, rev = torch.empty(N2 * NB.value + 1, **i32), torch.empty(max(R * sbc, 1), **i32)
+    _abi.call(lib.nsa_compact, ctypes.byref(a), _ptr(row_ptr), _ptr(col), _ptr(rev_ptr),
+              _ptr(rev), _ptr(ws), ctypes.c_size_t(ws.numel()), _stream())
+    nnz = int(row_ptr[-1].item())
+    return row_ptr, col[:nnz], rev_ptr, rev[:nnz], NB.value
+
+
+# ----------------------------------------------------------------------------
+# Sparse flash attention (paged decode)
+# ----------------------------------------------------------------------------
+
+class SfaPlan:
+    """Paged sparse flash attention decode for fixed tensors.
+
+    q [B, Sq, N1, 512], q_rope [B, Sq, N1, 64] (BSND); key_cache [P, page, 1, 512],
+    key_rope_cache [P, page, 1, 64], value_cache [P, page, 1, 512] (may be key_cache);
+    block_table int32 [B, max_pages]; kv_lens int32 [B]; topk_indices int32
+    [B, Sq, 1, K] (-1 = empty).
+    """
+
+    def __init__(self, q, q_rope, key_cache, key_rope_cache, value_cache, block_table, kv_lens,
+                 topk_indices, scale=None, sparse_mode=3, sparse_block_size=1, validate=False):
+        for t, n in ((q, "q"), (q_rope, "q_rope"), (key_cache, "key_cache"),
+                     (key_rope_cache, "key_rope_cache"), (value_cache, "value_cache")):
+            _check(t, n, q.dtype)
+        B, Sq, N1, D = q.shape
+        P, page, N2, _ = key_cache.shape
+        Dr, Dv = q_rope.shape[3], value_cache.shape[3]
+        _check(block_table, "block_table", torch.int32)
+        _check(kv_lens, "kv_lens", torch.int32, (B,))
+        K = topk_indices.shape[-1]
+        _check(topk_indices, "topk_indices", torch.int32, (B, Sq, N2, K))
+        self.keep = (q, q_rope, key_cache, key_rope_cache, value_cache, block_table, kv_lens,
+                     topk_indices)
+        self.scale = 1.0 / math.sqrt(D + Dr) if scale is None else float(scale)
+        dev = q.device
+        self.out = torch.empty((B, Sq, N1, Dv), dtype=q.dtype, device=dev)
+        self.lse = torch.empty((B, Sq, N1), dtype=torch.float32, device=dev)
+        self.a = _abi.SfaArgs(
+            dtype=_dtype_code(q), q_layout=LAYOUT_BSND, B=B, Sq=Sq, N1=N1, N2=N2, D=D, Dr=Dr,
+            Dv=Dv, num_pages=P, page_size=page, max_pages=block_table.shape[1], topk=K,
+            sparse_block_size=sparse_block_size, sparse_mode=sparse_mode, scale=self.scale,
+            validate=int(bool(validate)), q=q.data_ptr(), q_rope=q_rope.data_ptr(),
+            key_cache=key_cache.data_ptr(), key_rope_cache=key_rope_cache.data_ptr(),
+            value_cache=value_cache.data_ptr(), block_table=block_table.data_ptr(),
+            kv_lens=kv_lens.data_ptr(), topk_indices=topk_indices.data_ptr(),
+            out=self.out.data_ptr(), lse=self.lse.data_ptr())
+        nb = ctypes.c_size_t()
+        _abi.call(lib.sfa_paged_fwd_workspace_size, ctypes.byref(self.a), ctypes.byref(nb))
+        self.ws = _workspace(nb.value, dev)
+
+    def fwd(self):
+        _abi.call(lib.sfa_paged_fwd, ctypes.byref(self.a), _ptr(self.ws),
+                  ctypes.c_size_t(self.ws.numel()), _stream())
+        return self.out, self.lse
+
+
+def sfa_paged_fwd(q, q_rope, key_cache, key_rope_cache, value_cache, block_table, kv_lens,
+                  topk_indices, scale=None, sparse_mode=3, sparse_block_size=1, validate=False):
+    """Paged sparse flash attention forward: returns (out, lse)."""
+    return SfaPlan(q, q_rope, key_cache, key_rope_cache, value_cache, block_table, kv_lens,
+                   topk_indices, scale, sparse_mode, sparse_block_size, validate).fwd()

@@ -1,0 +1,584 @@
+// C-ABI layer: argument validation, workspace sizing and kernel dispatch.
+//
+// The two-phase pattern follows the CANN operator pages ("calls" section of
+// each): XXX_workspace_size validates on the host and sizes the workspace;
+// XXX re-validates and enqueues.  Constraints are cited where they are
+// checked.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/top_selected_attention.h"
+#include "tsa_internal.h"
+
+using namespace tsa;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+// Carves aligned sub-buffers out of one workspace; with base == nullptr it
+// only measures.
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base((char*)b) {}
+  template <typename T>
+  T* take(size_t count) {
+    off = (off + kAlign - 1) / kAlign * kAlign;
+    T* p = base ? (T*)(base + off) : nullptr;
+    off += count * sizeof(T);
+    return p;
+  }
+};
+
+inline long cdiv(long a, long b) { return (a + b - 1) / b; }
+inline bool fits_i32(long x) { return x >= 0 && x <= 0x7fffffffL; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? TSA_OK : TSA_ERR_HIP; }
+
+// ---------------------------------------------------------------------------
+// Block-sparse attention
+// ---------------------------------------------------------------------------
+
+// Shape checks shared by forward, backward and compaction.
+int check_bsa_common(int dtype, int ql, int kl, int B, int N1, int N2, int Sq, int Skv, int D,
+                     int bq, int bkv, int mode, float scale) {
+  if (dtype != TSA_BF16 && dtype != TSA_FP16) return TSA_ERR_INVALID;
+  // "aclnnBlockSparseAttentionGrad", constraints: only BNSD is supported
+  // (TND is a documented layout, not built here).
+  if ((ql != TSA_LAYOUT_BNSD && ql != TSA_LAYOUT_TND) ||
+      (kl != TSA_LAYOUT_BNSD && kl != TSA_LAYOUT_TND))
+    return TSA_ERR_INVALID;
+  if (ql != TSA_LAYOUT_BNSD || kl != TSA_LAYOUT_BNSD) return TSA_ERR_UNSUPPORTED;
+  if (B < 0 || Sq < 0 || Skv < 0 || N1 < 1 || N2 < 1) return TSA_ERR_INVALID;
+  // constraints: N1 >= N2 and N1 % N2 == 0
+  if (N1 % N2 != 0) return TSA_ERR_INVALID;
+  // constraints: headdim = 128
+  if (D != 128) return TSA_ERR_INVALID;
+  if (bq < 1 || bkv < 1 || bq > 65536 || bkv > 65536) return TSA_ERR_INVALID;
+  if (mode != 0 && mode != 2) return TSA_ERR_INVALID;
+  if (!std::isfinite(scale)) return TSA_ERR_INVALID;
+  const long QB = cdiv(Sq, bq), KB = cdiv(Skv, bkv);
+  if (!fits_i32((long)B * N1 * QB * KB) || !fits_i32((long)B * N1 * QB + 1)) return TSA_ERR_INVALID;
+  if (!fits_i32(QB * bq) || !fits_i32(KB * bkv)) return TSA_ERR_INVALID;
+  return TSA_OK;
+}
+
+struct BsaWs {
+  int* parts;
+  int* sums;
+  int* row_ptr;
+  int* col;
+  int* rev_ptr;
+  int* rev;
+  float* delta;
+};
+
+template <class A>
+size_t bsa_carve(const A* a, void* ws, BsaWs* out, bool with_delta) {
+  const int QB = (int)cdiv(a->Sq, a->block_q), KB = (int)cdiv(a->Skv, a->block_kv);
+  const long R = (long)a->B * a->N1 * QB, C = (long)a->B * a->N2 * KB;
+  const long nparts = bsa_compact_parts_len(a->B, a->N1, a->N2, QB, KB);
+  Carver c(ws);
+  BsaWs w;
+  w.parts = c.take<int>(nparts);
+  w.sums = c.take<int>(scan_sums_len(nparts));
+  w.row_ptr = c.take<int>(R + 1);
+  w.col = c.take<int>(R * KB);
+  w.rev_ptr = c.take<int>(C + 1);
+  w.rev = c.take<int>(R * KB);
+  w.delta = with_delta ? c.take<float>((long)a->B * a->N1 * a->Sq) : nullptr;
+  if (out) *out = w;
+  return c.off + kAlign;
+}
+
+int check_bsa_fwd(const bsa_fwd_args* a) {
+  if (!a) return TSA_ERR_NULL;
+  int s = check_bsa_common(a->dtype, a->q_layout, a->kv_layout, a->B, a->N1, a->N2, a->Sq, a->Skv,
+                           a->D, a->block_q, a->block_kv, a->sparse_mode, a->scale);
+  if (s) return s;
+  const bool empty = (long)a->B * a->Sq == 0;
+  if (!empty && (!a->q || !a->out || !a->lse || !a->block_mask)) return TSA_ERR_NULL;
+  if (!empty && a->Skv > 0 && (!a->k || !a->v)) return TSA_ERR_NULL;
+  return TSA_OK;
+}
+
+int check_bsa_bwd(const bsa_bwd_args* a) {
+  if (!a) return TSA_ERR_NULL;
+  int s = check_bsa_common(a->dtype, a->q_layout, a->kv_layout, a->B, a->N1, a->N2, a->Sq, a->Skv,
+                           a->D, a->block_q, a->block_kv, a->sparse_mode, a->scale);
+  if (s) return s;
+  const bool empty_q = (long)a->B * a->Sq == 0, empty_k = (long)a->B * a->Skv == 0;
+  if (!empty_q && (!a->q || !a->out || !a->dout || !a->lse || !a->dq || !a->block_mask))
+    return TSA_ERR_NULL;
+  if (!empty_k && (!a->k || !a->v || !a->dk || !a->dv)) return TSA_ERR_NULL;
+  return TSA_OK;
+}
+
+BsaParams bsa_params(int B, int N1, int N2, int Sq, int Skv, int bq, int bkv, int mode,
+                     float scale) {
+  BsaParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.B = B; p.N1 = N1; p.N2 = N2; p.G = N1 / N2;
+  p.Sq = Sq; p.Skv = Skv; p.D = 128;
+  p.bq = bq; p.bkv = bkv;
+  p.QB = (int)cdiv(Sq, bq); p.KB = (int)cdiv(Skv, bkv);
+  p.causal = mode == 2;
+  p.scale = scale;
+  return p;
+}
+
+// ---------------------------------------------------------------------------
+// NSA selected attention
+// ---------------------------------------------------------------------------
+
+template <class A>
+int check_nsa(const A* a) {
+  if (!a) return TSA_ERR_NULL;
+  if (a->dtype != TSA_BF16 && a->dtype != TSA_FP16) return TSA_ERR_INVALID;
+  // "aclnnNsaSelectedAttention", constraints: inputLayout supports only TND.
+  if (a->layout == TSA_LAYOUT_BNSD || a->layout == TSA_LAYOUT_BSND) return TSA_ERR_UNSUPPORTED;
+  if (a->layout != TSA_LAYOUT_TND) return TSA_ERR_INVALID;
+  // constraints (TND shape ranges): B in [1, 1024], N in [1, 128], G <= 32.
+  if (a->B < 1 || a->B > 1024) return TSA_ERR_INVALID;
+  if (a->N1 < 1 || a->N1 > 128 || a->N2 < 1 || a->N1 % a->N2 != 0) return TSA_ERR_INVALID;
+  if (a->N1 / a->N2 > 32) return TSA_ERR_INVALID;
+  if (a->D != 128) return TSA_ERR_INVALID;
+  if (a->Dv != a->D) return TSA_ERR_UNSUPPORTED;
+  // constraints: selected_block_size <= 128 and a multiple of 16;
+  // selected_block_count in [1, 128]; their product at most 8K.
+  if (a->sbs < 16 || a->sbs > 128 || a->sbs % 16 != 0) return TSA_ERR_INVALID;
+  if (a->sbc < 1 || a->sbc > 128 || a->sbs * a->sbc > 8192) return TSA_ERR_INVALID;
+  // constraints: sparseMode 0 or 2.
+  if (a->sparse_mode != 0 && a->sparse_mode != 2) return TSA_ERR_INVALID;
+  if (!std::isfinite(a->scale)) return TSA_ERR_INVALID;
+  if (!a->cu_seqlens_q || !a->cu_seqlens_kv) return TSA_ERR_NULL;
+  const int32_t* cq = a->cu_seqlens_q;
+  const int32_t* ck = a->cu_seqlens_kv;
+  if (cq[0] != 0 || ck[0] != 0) return TSA_ERR_INVALID;
+  for (int b = 0; b < a->B; b++) {
+    const long sq = (long)cq[b + 1] - cq[b], sk = (long)ck[b + 1] - ck[b];
+    if (sq < 0 || sk < 0) return TSA_ERR_INVALID;
+    // constraints: S in [1, 128K], S >= sbs * sbc and a multiple of sbs.
+    if (sk > 131072 || sq > 131072) return TSA_ERR_INVALID;
+    if (sk < (long)a->sbs * a->sbc || sk % a->sbs != 0) return TSA_ERR_INVALID;
+  }
+  if (cq[a->B] != a->T || ck[a->B] != a->Tk) return TSA_ERR_INVALID;
+  if (!fits_i32((long)a->T * a->N2 * a->sbc) || !fits_i32((long)a->T * a->N1 * a->D))
+    return TSA_ERR_INVALID;
+  if (a->T > 0 && (!a->q || !a->out || !a->lse || !a->topk)) return TSA_ERR_NULL;
+  if (a->T > 0 && (!a->k || !a->v)) return TSA_ERR_NULL;
+  return TSA_OK;
+}
+
+int nsa_blocks_total(const int32_t* ck, int B, int sbs) {
+  long nb = 0;
+  for (int b = 0; b < B; b++) nb += cdiv((long)ck[b + 1] - ck[b], sbs);
+  return (int)nb;
+}
+
+struct NsaWs {
+  int* meta;     // cu_q [B+1], cu_kv [B+1], blk_off [B+1]
+  int* cnt;
+  int* sums;
+  int* row_ptr;
+  int* col;
+  int* rcnt;
+  int* rev_ptr;
+  int* rev;
+  int* bad;
+  float* delta;
+};
+
+template <class A>
+size_t nsa_carve(const A* a, void* ws, NsaWs* out, bool with_delta) {
+  const long R = (long)a->T * a->N2;
+  const long NB = nsa_blocks_total(a->cu_seqlens_kv, a->B, a->sbs);
+  const long RR = (long)a->N2 * NB;
+  Carver c(ws);
+  NsaWs w;
+  w.meta = c.take<int>(3 * (a->B + 1));
+  w.cnt = c.take<int>(R);
+  w.sums = c.take<int>(scan_sums_len(R > RR ? R : RR));
+  w.row_ptr = c.take<int>(R + 1);
+  w.col = c.take<int>(R * a->sbc);
+  w.rcnt = c.take<int>(RR);
+  w.rev_ptr = c.take<int>(RR + 1);
+  w.rev = c.take<int>(R * a->sbc);
+  w.bad = c.take<int>(1);
+  w.delta = with_delta ? c.take<float>((long)a->T * a->N1) : nullptr;
+  if (out) *out = w;
+  return c.off + kAlign;
+}
+
+// Uploads cu_seqlens and block offsets into the workspace and fills the
+// device geometry.
+template <class A>
+int nsa_setup(const A* a, const NsaWs& w, NsaGeom* g, hipStream_t st) {
+  const int n = a->B + 1;
+  int* host = new int[3 * n];
+  host[0 * n] = 0;
+  for (int b = 0; b < n; b++) {
+    host[0 * n + b] = a->cu_seqlens_q[b];
+    host[1 * n + b] = a->cu_seqlens_kv[b];
+  }
+  host[2 * n] = 0;
+  for (int b = 0; b < a->B; b++)
+    host[2 * n + b + 1] =
+        host[2 * n + b] + (int)cdiv((long)a->cu_seqlens_kv[b + 1] - a->cu_seqlens_kv[b], a->sbs);
+  hipError_t e = hipMemcpyAsync(w.meta, host, sizeof(int) * 3 * n, hipMemcpyHostToDevice, st);
+  // the copy from pageable memory is staged before hipMemcpyAsync returns
+  delete[] host;
+  if (e != hipSuccess) return TSA_ERR_HIP;
+  g->cu_q = w.meta;
+  g->cu_kv = w.meta + n;
+  g->blk_off = w.meta + 2 * n;
+  g->B = a->B;
+  g->T = a->T;
+  g->N2 = a->N2;
+  g->sbc = a->sbc;
+  g->sbs = a->sbs;
+  g->causal = a->sparse_mode == 2;
+  g->NB = nsa_blocks_total(a->cu_seqlens_kv, a->B, a->sbs);
+  return TSA_OK;
+}
+
+template <class A>
+int nsa_lists(const A* a, const NsaWs& w, const NsaGeom& g, hipStream_t st) {
+  if (a->validate) {
+    hipError_t e = hipMemsetAsync(w.bad, 0, sizeof(int), st);
+    if (e == hipSuccess) e = launch_nsa_check(a->topk, g, w.bad, st);
+    int bad = 0;
+    if (e == hipSuccess) e = hipMemcpyAsync(&bad, w.bad, sizeof(int), hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return TSA_ERR_HIP;
+    if (bad) return TSA_ERR_DATA;
+  }
+  return hip_status(launch_nsa_compact(a->topk, g, w.cnt, w.sums, w.row_ptr, w.col, w.rcnt,
+                                       w.rev_ptr, w.rev, st));
+}
+
+// ---------------------------------------------------------------------------
+// Sparse flash attention
+// ---------------------------------------------------------------------------
+
+int check_sfa(const sfa_paged_fwd_args* a) {
+  if (!a) return TSA_ERR_NULL;
+  if (a->dtype != TSA_BF16 && a->dtype != TSA_FP16) return TSA_ERR_INVALID;
+  if (a->q_layout == TSA_LAYOUT_TND) return TSA_ERR_UNSUPPORTED;
+  if (a->q_layout != TSA_LAYOUT_BSND) return TSA_ERR_INVALID;
+  if (a->B < 0 || a->Sq < 0) return TSA_ERR_INVALID;
+  // "aclnnSparseFlashAttention", constraints: N1 in {1, 2, 4, ..., 128}.
+  if (a->N1 < 1 || a->N1 > 128 || (a->N1 & (a->N1 - 1))) return TSA_ERR_INVALID;
+  if (a->N2 < 1 || a->N1 % a->N2 != 0) return TSA_ERR_INVALID;
+  // "SparseAttnSharedkvMetadata", parameters: one KV head only.
+  if (a->N2 != 1) return TSA_ERR_UNSUPPORTED;
+  // constraints: D = 512 for query/key/value, Dr = 64 for the rope parts.
+  if (a->D != 512 || a->Dr != 64 || a->Dv != 512) return TSA_ERR_INVALID;
+  // constraints: block_size a multiple of 16, at most 1024.
+  if (a->page_size < 16 || a->page_size > 1024 || a->page_size % 16 != 0) return TSA_ERR_INVALID;
+  // constraints: sparse_block_size and block_size tied by exact division
+  // (read: a selected block never straddles a page).
+  if (a->sparse_block_size < 1 || a->page_size % a->sparse_block_size != 0) return TSA_ERR_INVALID;
+  if (a->sparse_mode != 0 && a->sparse_mode != 3) return TSA_ERR_INVALID;
+  if (a->topk < 1 || a->max_pages < 1 || a->num_pages < 1) return TSA_ERR_INVALID;
+  if (!std::isfinite(a->scale)) return TSA_ERR_INVALID;
+  if (!fits_i32((long)a->num_pages * a->page_size) || !fits_i32((long)a->B * a->max_pages))
+    return TSA_ERR_INVALID;
+  if ((long)a->B * a->Sq > 0 &&
+      (!a->q || !a->q_rope || !a->key_cache || !a->key_rope_cache || !a->value_cache ||
+       !a->block_table || !a->kv_lens || !a->topk_indices || !a->out))
+    return TSA_ERR_NULL;
+  return TSA_OK;
+}
+
+SfaParams sfa_params(const sfa_paged_fwd_args* a) {
+  SfaParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.q = a->q; p.q_rope = a->q_rope; p.kc = a->key_cache; p.krc = a->key_rope_cache;
+  p.vc = a->value_cache; p.block_table = a->block_table; p.kv_lens = a->kv_lens;
+  p.topk = a->topk_indices; p.out = a->out; p.lse = a->lse;
+  p.B = a->B; p.Sq = a->Sq; p.N1 = a->N1; p.N2 = a->N2; p.D = a->D; p.Dr = a->Dr; p.Dv = a->Dv;
+  p.num_pages = a->num_pages; p.page = a->page_size; p.max_pages = a->max_pages;
+  p.topk_n = a->topk; p.sbs = a->sparse_block_size;
+  p.causal = a->sparse_mode == 3;
+  p.scale = a->scale;
+  p.splits = sfa_splits(p);
+  return p;
+}
+
+size_t sfa_carve(const SfaParams& p, void* ws, SfaParams* out) {
+  Carver c(ws);
+  const long tok = (long)p.B * p.Sq;
+  float* po = c.take<float>(tok * p.splits * p.N1 * p.Dv);
+  float* pl = c.take<float>(tok * p.splits * p.N1);
+  int* bad = c.take<int>(1);
+  if (out) {
+    *out = p;
+    out->part_o = po;
+    out->part_lse = pl;
+    out->bad = bad;
+  }
+  return c.off + kAlign;
+}
+
+}  // namespace
+
+// ===========================================================================
+// Exported entry points
+// ===========================================================================
+extern "C" {
+
+const char* tsa_status_string(int s) {
+  switch (s) {
+    case TSA_OK: return "ok";
+    case TSA_ERR_NULL: return "a required pointer is NULL";
+    case TSA_ERR_INVALID: return "a value or shape violates a documented constraint";
+    case TSA_ERR_UNSUPPORTED: return "valid for the operator but not built in this library";
+    case TSA_ERR_WORKSPACE: return "workspace missing or too small";
+    case TSA_ERR_HIP: return "a HIP launch or runtime call failed";
+    case TSA_ERR_DATA: return "input data out of range (validate = 1)";
+    default: return "unknown status";
+  }
+}
+
+size_t tsa_args_sizeof(int which) {
+  switch (which) {
+    case 0: return sizeof(bsa_fwd_args);
+    case 1: return sizeof(bsa_bwd_args);
+    case 2: return sizeof(nsa_select_fwd_args);
+    case 3: return sizeof(nsa_select_bwd_args);
+    case 4: return sizeof(sfa_paged_fwd_args);
+    default: return 0;
+  }
+}
+
+// ----- BSA -----------------------------------------------------------------
+
+int bsa_fwd_workspace_size(const bsa_fwd_args* a, size_t* bytes) {
+  if (!bytes) return TSA_ERR_NULL;
+  int s = check_bsa_fwd(a);
+  if (s) return s;
+  *bytes = bsa_carve(a, nullptr, nullptr, false);
+  return TSA_OK;
+}
+
+int bsa_compact_workspace_size(const bsa_fwd_args* a, size_t* bytes) {
+  if (!bytes || !a) return TSA_ERR_NULL;
+  int s = check_bsa_common(a->dtype, a->q_layout, a->kv_layout, a->B, a->N1, a->N2, a->Sq, a->Skv,
+                           a->D, a->block_q, a->block_kv, a->sparse_mode, a->scale);
+  if (s) return s;
+  *bytes = bsa_carve(a, nullptr, nullptr, false);
+  return TSA_OK;
+}
+
+int bsa_compact(const bsa_fwd_args* a, int32_t* row_ptr, int32_t* col, int32_t* rev_ptr,
+                int32_t* rev, void* ws, size_t ws_bytes, void* stream) {
+  size_t need;
+  int s = bsa_compact_workspace_size(a, &need);
+  if (s) return s;
+  if (!row_ptr || !col || !rev_ptr || !rev || (a->B * (long)a->Sq > 0 && !a->block_mask))
+    return TSA_ERR_NULL;
+  if (!ws || ws_bytes < need) return TSA_ERR_WORKSPACE;
+  BsaWs w;
+  bsa_carve(a, ws, &w, false);
+  const int QB = (int)cdiv(a->Sq, a->block_q), KB = (int)cdiv(a->Skv, a->block_kv);
+  hipStream_t st = (hipStream_t)stream;
+  if ((long)a->B * QB * KB == 0) {
+    hipError_t e = hipMemsetAsync(row_ptr, 0, sizeof(int) * ((long)a->B * a->N1 * QB + 1), st);
+    if (e == hipSuccess)
+      e = hipMemsetAsync(rev_ptr, 0, sizeof(int) * ((long)a->B * a->N2 * KB + 1), st);
+    return hip_status(e);
+  }
+  return hip_status(launch_bsa_compact(a->block_mask, a->B, a->N1, a->N2, QB, KB, w.parts, w.sums,
+                                       row_ptr, col, rev_ptr, rev, st));
+}
+
+int bsa_fwd(const bsa_fwd_args* a, void* ws, size_t ws_bytes, void* stream) {
+  size_t need;
+  int s = bsa_fwd_workspace_size(a, &need);
+  if (s) return s;
+  if (!ws || ws_bytes < need) return TSA_ERR_WORKSPACE;
+  if ((long)a->B * a->Sq == 0) return TSA_OK;
+  hipStream_t st = (hipStream_t)stream;
+  BsaWs w;
+  bsa_carve(a, ws, &w, false);
+  BsaParams p = bsa_params(a->B, a->N1, a->N2, a->Sq, a->Skv, a->block_q, a->block_kv,
+                           a->sparse_mode, a->scale);
+  if (p.KB > 0) {
+    hipError_t e = launch_bsa_compact(a->block_mask, a->B, a->N1, a->N2, p.QB, p.KB, w.parts,
+                                      w.sums, w.row_ptr, w.col, w.rev_ptr, w.rev, st);
+    if (e != hipSuccess) return TSA_ERR_HIP;
+  } else {
+    hipError_t e = hipMemsetAsync(w.row_ptr, 0, sizeof(int) * ((long)a->B * a->N1 * p.QB + 1), st);
+    if (e != hipSuccess) return TSA_ERR_HIP;
+  }
+  p.q = a->q; p.k = a->k; p.v = a->v; p.out = a->out; p.lse = a->lse;
+  p.row_ptr = w.row_ptr; p.col = w.col;
+  return hip_status(launch_bsa_fwd(p, a->dtype == TSA_FP16, st));
+}
+
+int bsa_bwd_workspace_size(const bsa_bwd_args* a, size_t* bytes) {
+  if (!bytes) return TSA_ERR_NULL;
+  int s = check_bsa_bwd(a);
+  if (s) return s;
+  *bytes = bsa_carve(a, nullptr, nullptr, true);
+  return TSA_OK;
+}
+
+int bsa_bwd(const bsa_bwd_args* a, void* ws, size_t ws_bytes, void* stream) {
+  size_t need;
+  int s = bsa_bwd_workspace_size(a, &need);
+  if (s) return s;
+  if (!ws || ws_bytes < need) return TSA_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  BsaWs w;
+  bsa_carve(a, ws, &w, true);
+  BsaParams p = bsa_params(a->B, a->N1, a->N2, a->Sq, a->Skv, a->block_q, a->block_kv,
+                           a->sparse_mode, a->scale);
+  const long R = (long)a->B * a->N1 * p.QB, C = (long)a->B * a->N2 * p.KB;
+  if (R > 0 && C > 0) {
+    hipError_t e = launch_bsa_compact(a->block_mask, a->B, a->N1, a->N2, p.QB, p.KB, w.parts,
+                                      w.sums, w.row_ptr, w.col, w.rev_ptr, w.rev, st);
+    if (e != hipSuccess) return TSA_ERR_HIP;
+  } else {
+    hipError_t e = hipMemsetAsync(w.row_ptr, 0, sizeof(int) * (R + 1), st);
+    if (e == hipSuccess) e = hipMemsetAsync(w.rev_ptr, 0, sizeof(int) * (C + 1), st);
+    if (e != hipSuccess) return TSA_ERR_HIP;
+  }
+  p.q = a->q; p.k = a->k; p.v = a->v; p.o = a->out; p.dout = a->dout; p.lse = (float*)a->lse;
+  p.out = a->dq; p.dk = a->dk; p.dv = a->dv; p.delta = w.delta;
+  p.row_ptr = w.row_ptr; p.col = w.col; p.rev_ptr = w.rev_ptr; p.rev = w.rev;
+  return hip_status(launch_bsa_bwd(p, a->dtype == TSA_FP16, st));
+}
+
+// ----- NSA -----------------------------------------------------------------
+
+int nsa_compact_blocks_total(const nsa_select_fwd_args* a, int32_t* nb) {
+  if (!nb) return TSA_ERR_NULL;
+  int s = check_nsa(a);
+  if (s) return s;
+  *nb = nsa_blocks_total(a->cu_seqlens_kv, a->B, a->sbs);
+  return TSA_OK;
+}
+
+int nsa_compact_workspace_size(const nsa_select_fwd_args* a, size_t* bytes) {
+  if (!bytes) return TSA_ERR_NULL;
+  int s = check_nsa(a);
+  if (s) return s;
+  *bytes = nsa_carve(a, nullptr, nullptr, false);
+  return TSA_OK;
+}
+
+int nsa_compact(const nsa_select_fwd_args* a, int32_t* row_ptr, int32_t* col, int32_t* rev_ptr,
+                int32_t* rev, void* ws, size_t ws_bytes, void* stream) {
+  size_t need;
+  int s = nsa_compact_workspace_size(a, &need);
+  if (s) return s;
+  if (!row_ptr || !col || !rev_ptr || !rev) return TSA_ERR_NULL;
+  if (!ws || ws_bytes < need) return TSA_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  NsaWs w;
+  nsa_carve(a, ws, &w, false);
+  w.row_ptr = row_ptr; w.col = col; w.rev_ptr = rev_ptr; w.rev = rev;
+  NsaGeom g;
+  s = nsa_setup(a, w, &g, st);
+  if (s) return s;
+  return nsa_lists(a, w, g, st);
+}
+
+int nsa_select_fwd_workspace_size(const nsa_select_fwd_args* a, size_t* bytes) {
+  return nsa_compact_workspace_size(a, bytes);
+}
+
+int nsa_select_fwd(const nsa_select_fwd_args* a, void* ws, size_t ws_bytes, void* stream) {
+  size_t need;
+  int s = nsa_select_fwd_workspace_size(a, &need);
+  if (s) return s;
+  if (!ws || ws_bytes < need) return TSA_ERR_WORKSPACE;
+  if (a->T == 0) return TSA_OK;
+  hipStream_t st = (hipStream_t)stream;
+  NsaWs w;
+  nsa_carve(a, ws, &w, false);
+  NsaParams p;
+  std::memset(&p, 0, sizeof(p));
+  s = nsa_setup(a, w, &p.g, st);
+  if (s) return s;
+  s = nsa_lists(a, w, p.g, st);
+  if (s) return s;
+  p.q = a->q; p.k = a->k; p.v = a->v; p.out = a->out; p.lse = a->lse;
+  p.row_ptr = w.row_ptr; p.col = w.col; p.rev_ptr = w.rev_ptr; p.rev = w.rev;
+  p.T = a->T; p.Tk = a->Tk; p.N1 = a->N1; p.N2 = a->N2; p.G = a->N1 / a->N2; p.D = a->D;
+  p.scale = a->scale;
+  return hip_status(launch_nsa_fwd(p, a->dtype == TSA_FP16, st));
+}
+
+int nsa_select_bwd_workspace_size(const nsa_select_bwd_args* a, size_t* bytes) {
+  if (!bytes) return TSA_ERR_NULL;
+  int s = check_nsa(a);
+  if (s) return s;
+  if (a->T > 0 && (!a->out || !a->dout || !a->lse || !a->dq)) return TSA_ERR_NULL;
+  if (a->Tk > 0 && (!a->dk || !a->dv)) return TSA_ERR_NULL;
+  *bytes = nsa_carve(a, nullptr, nullptr, true);
+  return TSA_OK;
+}
+
+int nsa_select_bwd(const nsa_select_bwd_args* a, void* ws, size_t ws_bytes, void* stream) {
+  size_t need;
+  int s = nsa_select_bwd_workspace_size(a, &need);
+  if (s) return s;
+  if (!ws || ws_bytes < need) return TSA_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  NsaWs w;
+  nsa_carve(a, ws, &w, true);
+  NsaParams p;
+  std::memset(&p, 0, sizeof(p));
+  s = nsa_setup(a, w, &p.g, st);
+  if (s) return s;
+  if (a->T > 0) {
+    s = nsa_lists(a, w, p.g, st);
+    if (s) return s;
+  }
+  p.q = a->q; p.k = a->k; p.v = a->v; p.o = a->out; p.dout = a->dout; p.lse = (float*)a->lse;
+  p.out = a->dq; p.dk = a->dk; p.dv = a->dv; p.delta = w.delta;
+  p.row_ptr = w.row_ptr; p.col = w.col; p.rev_ptr = w.rev_ptr; p.rev = w.rev;
+  p.T = a->T; p.Tk = a->Tk; p.N1 = a->N1; p.N2 = a->N2; p.G = a->N1 / a->N2; p.D = a->D;
+  p.scale = a->scale;
+  return hip_status(launch_nsa_bwd(p, a->dtype == TSA_FP16, st));
+}
+
+// ----- SFA -----------------------------------------------------------------
+
+int sfa_paged_fwd_workspace_size(const sfa_paged_fwd_args* a, size_t* bytes) {
+  if (!bytes) return TSA_ERR_NULL;
+  int s = check_sfa(a);
+  if (s) return s;
+  *bytes = sfa_carve(sfa_params(a), nullptr, nullptr);
+  return TSA_OK;
+}
+
+int sfa_paged_fwd(const sfa_paged_fwd_args* a, void* ws, size_t ws_bytes, void* stream) {
+  size_t need;
+  int s = sfa_paged_fwd_workspace_size(a, &need);
+  if (s) return s;
+  if (!ws || ws_bytes < need) return TSA_ERR_WORKSPACE;
+  if ((long)a->B * a->Sq == 0) return TSA_OK;
+  hipStream_t st = (hipStream_t)stream;
+  SfaParams p;
+  sfa_carve(sfa_params(a), ws, &p);
+  if (a->validate) {
+    hipError_t e = hipMemsetAsync(p.bad, 0, sizeof(int), st);
+    if (e == hipSuccess) e = launch_sfa_check(p, st);
+    int bad = 0;
+    if (e == hipSuccess) e = hipMemcpyAsync(&bad, p.bad, sizeof(int), hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return TSA_ERR_HIP;
+    if (bad) return TSA_ERR_DATA;
+  }
+  return hip_status(launch_sfa_fwd(p, a->dtype == TSA_FP16, st));
+}
+
+}  // extern "C"

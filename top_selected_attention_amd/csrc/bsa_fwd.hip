@@ -1,0 +1,287 @@
+// Block-sparse attention forward ("aclnnBlockSparseAttentionGrad", formula
+// section): Out = Softmax(Mask(scale * Q K_sparse^T)) V_sparse, plus the
+// natural-log LSE of each row.
+//
+// One workgroup per (b, n1, Q block) slice of up to 128 query rows; each wave
+// owns 64 query rows.  The Q block's selected KV blocks are walked in 64-key
+// chunks: K and V of a chunk are one contiguous slab of BNSD memory (the
+// gather is a base-pointer jump), moved by direct global -> LDS loads into a
+// double buffer while the previous chunk computes.
+//
+// The scores are computed transposed, S^T = K Q^T, on 32x32x16 MFMA: K is the
+// A operand read from LDS, Q the B operand held in registers for the whole
+// kernel.  In the accumulator layout a lane then owns one query column and
+// 16 keys of it, so the online-softmax max and sum are in-lane plus one
+// exchange with lane l^32.  P^T leaves the accumulator directly as the B
+// operand of O^T += V^T P^T, with V^T read from the natural-layout V tile by
+// LDS transpose reads (ds_read_b64_tr_b16).
+#include "tsa_device.h"
+#include "tsa_internal.h"
+
+namespace tsa {
+
+constexpr int kD = 128;        // head dim (the page's constraint: headdim = 128)
+constexpr int kKC = 64;        // keys per chunk
+constexpr int kRowB = kD * 2;  // bytes per K/V row
+constexpr int kTileB = kKC * kRowB;  // bytes per staged K or V chunk
+
+// XOR swizzles of the 16 16-byte pieces of a 256-byte LDS row.  K pieces are
+// read 16 bytes at a time by 32 lanes on 32 rows (same piece): swz_k makes
+// 16 consecutive rows, and 8 rows x 2 adjacent pieces, hit distinct banks.
+// V is read by transpose reads covering 4 consecutive rows x 4 aligned
+// pieces: swz_v gives each of 4 consecutive rows a different 4-piece group.
+__device__ __forceinline__ int swz_k(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+__device__ __forceinline__ int swz_v(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+template <class E>
+__device__ __forceinline__ typename E::V8 zero_v8() {
+  return as_v8<typename E::V8>(make_uint4(0, 0, 0, 0));
+}
+
+template <class E>
+__device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
+  typedef typename E::T T;
+  typedef T T4 __attribute__((ext_vector_type(4)));
+  T4 v = {E::from_f32(a), E::from_f32(b), E::from_f32(c), E::from_f32(d)};
+  return __builtin_bit_cast(uint2, v);
+}
+
+template <class E, int NW>
+__global__ __launch_bounds__(NW * 64) void bsa_fwd_kernel(BsaParams p, int qsub, int n_items) {
+  typedef typename E::T T;
+  typedef typename E::V8 V8;
+  constexpr int NT = NW * 64;
+  __shared__ __attribute__((aligned(1024))) char lds_k[2][kTileB];
+  __shared__ __attribute__((aligned(1024))) char lds_v[2][kTileB];
+
+  const int item = xcd_remap(blockIdx.x, n_items);
+  if (item < 0) return;
+  // Work order: head-major, and within a head the last Q block first (the
+  // longest lists under causal-shaped masks start first).
+  const int qs = item % qsub;
+  const int t1 = item / qsub;
+  const int qb = p.QB - 1 - (t1 % p.QB);
+  const int bn = t1 / p.QB;  // b * N1 + n1
+  const int n1 = bn % p.N1, b = bn / p.N1;
+  const int n2 = n1 / p.G;
+  const int row_lo = qb * p.bq + qs * NT;
+  const int row_hi = min((qb + 1) * p.bq, p.Sq);
+  if (row_lo >= row_hi) return;
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int l32 = lane & 31, h = lane >> 5;
+  const int wrow0 = row_lo + wid * 64;
+
+  const T* qh = (const T*)p.q + (long)bn * p.Sq * kD;
+  const T* kh = (const T*)p.k + ((long)b * p.N2 + n2) * p.Skv * kD;
+  const T* vh = (const T*)p.v + ((long)b * p.N2 + n2) * p.Skv * kD;
+
+  V8 qreg[2][8];
+#pragma unroll
+  for (int qt = 0; qt < 2; qt++) {
+    const int row = wrow0 + qt * 32 + l32;
+#pragma unroll
+    for (int ds = 0; ds < 8; ds++)
+      qreg[qt][ds] = row < row_hi ? as_v8<V8>(ld16(qh + (long)row * kD + ds * 16 + 8 * h))
+                                  : zero_v8<E>();
+  }
+
+  const int tile_row = bn * p.QB + qb;
+  const int e0 = p.row_ptr[tile_row], e1 = p.row_ptr[tile_row + 1];
+  const int cpb = (p.bkv + kKC - 1) / kKC;
+  const int nchunks = (e1 - e0) * cpb;
+  const float sl2 = p.scale * kLog2e;
+
+  // Chunk i covers keys [ks, ke) of KV block col[e0 + i / cpb].  Chunks that
+  // are empty (ragged tail) or wholly after the slice's last row under causal
+  // mode are skipped; the test is uniform across the workgroup.
+  auto chunk_range = [&](int i, int& ks, int& ke) {
+    const int kb = p.col[e0 + i / cpb];
+    ks = kb * p.bkv + (i % cpb) * kKC;
+    ke = min(min(ks + kKC, (kb + 1) * p.bkv), p.Skv);
+  };
+  auto next_valid = [&](int i) {
+    for (; i < nchunks; i++) {
+      int ks, ke;
+      chunk_range(i, ks, ke);
+      if (ks < ke && !(p.causal && ks > row_hi - 1)) break;
+    }
+    return i;
+  };
+
+  // Direct global -> LDS loads (no registers): one instruction moves 1 KB,
+  // four 256-byte rows, into consecutive LDS; the swizzled layout is made by
+  // choosing which 16-byte piece of global memory each lane fetches.  Keys
+  // past the chunk's end re-read its last key (finite data; their scores
+  // are masked, so P = 0 exactly there).
+  auto load_chunk = [&](int ks, int ke, int buf) {
+    const int sub = lane >> 4, pc = lane & 15;
+#pragma unroll
+    for (int u = 0; u < 16 / NW; u++) {
+      const int inst = wid * (16 / NW) + u;
+      const int r = inst * 4 + sub;
+      const long key = min(ks + r, ke - 1);
+      __builtin_amdgcn_global_load_lds(
+          (const void*)((const char*)kh + key * kRowB + ((pc ^ swz_k(r)) << 4)),
+          (__attribute__((address_space(3))) void*)(lds_k[buf] + inst * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(
+          (const void*)((const char*)vh + key * kRowB + ((pc ^ swz_v(r)) << 4)),
+          (__attribute__((address_space(3))) void*)(lds_v[buf] + inst * 1024), 16, 0, 0);
+    }
+  };
+
+  float m[2] = {-INFINITY, -INFINITY};
+  float lsum[2] = {0.f, 0.f};
+  f32x16 o[2][4];
+#pragma unroll
+  for (int qt = 0; qt < 2; qt++)
+#pragma unroll
+    for (int dt = 0; dt < 4; dt++)
+#pragma unroll
+      for (int j = 0; j < 16; j++) o[qt][dt][j] = 0.f;
+
+  int i = next_valid(0);
+  if (i < nchunks) {
+    int ks, ke;
+    chunk_range(i, ks, ke);
+    load_chunk(ks, ke, 0);
+  }
+  wait_vm();
+  __syncthreads();
+  int buf = 0;
+  while (i < nchunks) {
+    int ks, ke;
+    chunk_range(i, ks, ke);
+    const int inext = next_valid(i + 1);
+    if (inext < nchunks) {
+      int ks2, ke2;
+      chunk_range(inext, ks2, ke2);
+      load_chunk(ks2, ke2, buf ^ 1);
+    }
+    const char* Kb = lds_k[buf];
+    const char* Vb = lds_v[buf];
+
+    // S^T = K Q^T over the chunk: 64 keys x 64 queries per wave.
+    f32x16 st[2][2];
+#pragma unroll
+    for (int kt = 0; kt < 2; kt++)
+#pragma unroll
+      for (int qt = 0; qt < 2; qt++)
+#pragma unroll
+        for (int j = 0; j < 16; j++) st[kt][qt][j] = 0.f;
+#pragma unroll
+    for (int ds = 0; ds < 8; ds++) {
+      const int c = 2 * ds + h;
+      const V8 a0 = lds_read16<V8>(Kb + l32 * kRowB + ((c ^ swz_k(l32)) << 4));
+      const V8 a1 = lds_read16<V8>(Kb + (32 + l32) * kRowB + ((c ^ swz_k(32 + l32)) << 4));
+      st[0][0] = E::mfma32(a0, qreg[0][ds], st[0][0]);
+      st[0][1] = E::mfma32(a0, qreg[1][ds], st[0][1]);
+      st[1][0] = E::mfma32(a1, qreg[0][ds], st[1][0]);
+      st[1][1] = E::mfma32(a1, qreg[1][ds], st[1][1]);
+    }
+
+    // Online softmax, base 2.  Element j of a lane is key 8*(j/4) + 4*h + j%4.
+#pragma unroll
+    for (int qt = 0; qt < 2; qt++) {
+      const int qrow = wrow0 + qt * 32 + l32;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 2; kt++)
+#pragma unroll
+        for (int j = 0; j < 16; j++) {
+          const int key = ks + kt * 32 + 8 * (j >> 2) + 4 * h + (j & 3);
+          const bool ok = key < ke && (!p.causal || key <= qrow);
+          const float s = ok ? st[kt][qt][j] * sl2 : -INFINITY;
+          st[kt][qt][j] = s;
+          mx = fmaxf(mx, s);
+        }
+      mx = wave_max_half_swap(mx);
+      const float m_new = fmaxf(m[qt], mx);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = fast_exp2(m[qt] - m_use);
+      m[qt] = m_new;
+      lsum[qt] *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 4; dt++)
+#pragma unroll
+        for (int j = 0; j < 16; j++) o[qt][dt][j] *= alpha;
+#pragma unroll
+      for (int kt = 0; kt < 2; kt++)
+#pragma unroll
+        for (int j = 0; j < 16; j++) {
+          const float pv = fast_exp2(st[kt][qt][j] - m_use);
+          lsum[qt] += pv;
+          st[kt][qt][j] = pv;
+        }
+    }
+
+    // O^T += V^T P^T, 16 keys per step.
+    const int g16 = lane >> 4, i16 = lane & 15;
+#pragma unroll
+    for (int k4 = 0; k4 < 4; k4++) {
+      V8 pb[2];
+#pragma unroll
+      for (int qt = 0; qt < 2; qt++)
+#pragma unroll
+        for (int e = 0; e < 8; e++) pb[qt][e] = E::from_f32(st[k4 >> 1][qt][8 * (k4 & 1) + e]);
+      const int r0 = k4 * 16 + 4 * h + (i16 >> 2);
+      const int r1 = r0 + 8;
+#pragma unroll
+      for (int dt = 0; dt < 4; dt++) {
+        // logical 16-byte piece of the row holding d = dt*32 + 16*(g16&1) + 4*(i16&3)
+        const int c = 4 * dt + 2 * (g16 & 1) + ((i16 & 3) >> 1);
+        const int b8 = 8 * (i16 & 1);
+        const V8 a = lds_read_tr_pair<V8>(Vb + r0 * kRowB + ((c ^ swz_v(r0)) << 4) + b8,
+                                          Vb + r1 * kRowB + ((c ^ swz_v(r1)) << 4) + b8);
+        o[0][dt] = E::mfma32(a, pb[0], o[0][dt]);
+        o[1][dt] = E::mfma32(a, pb[1], o[1][dt]);
+      }
+    }
+
+    wait_vm();
+    __syncthreads();
+    buf ^= 1;
+    i = inext;
+  }
+
+  // Epilogue: O = O^T / l, LSE = (m + log2 l) * ln 2.
+#pragma unroll
+  for (int qt = 0; qt < 2; qt++) {
+    const float lt = lsum[qt] + __shfl_xor(lsum[qt], 32);
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const int row = wrow0 + qt * 32 + l32;
+    if (row < row_hi) {
+      T* orow = (T*)p.out + ((long)bn * p.Sq + row) * kD;
+#pragma unroll
+      for (int dt = 0; dt < 4; dt++)
+#pragma unroll
+        for (int jj = 0; jj < 4; jj++) {
+          const int d0 = dt * 32 + 8 * jj + 4 * h;
+          *reinterpret_cast<uint2*>(orow + d0) =
+              pack4<E>(o[qt][dt][4 * jj] * inv, o[qt][dt][4 * jj + 1] * inv,
+                       o[qt][dt][4 * jj + 2] * inv, o[qt][dt][4 * jj + 3] * inv);
+        }
+      if (h == 0) p.lse[(long)bn * p.Sq + row] = lt > 0.f ? (m[qt] + log2f(lt)) * kLn2 : -INFINITY;
+    }
+  }
+}
+
+template <class E, int NW>
+static hipError_t launch_fwd_t(const BsaParams& p, hipStream_t st) {
+  const int qsub = (p.bq + NW * 64 - 1) / (NW * 64);
+  const int n_items = p.B * p.N1 * p.QB * qsub;
+  const int grid = 8 * ((n_items + 7) / 8);
+  hipLaunchKernelGGL((bsa_fwd_kernel<E, NW>), dim3(grid), dim3(NW * 64), 0, st, p, qsub, n_items);
+  return hipGetLastError();
+}
+
+hipError_t launch_bsa_fwd(const BsaParams& p, int fp16, hipStream_t st) {
+  if (p.B * p.N1 * p.QB == 0) return hipSuccess;
+  const bool one = p.bq <= 64;
+  if (fp16) return one ? launch_fwd_t<FP16, 1>(p, st) : launch_fwd_t<FP16, 2>(p, st);
+  return one ? launch_fwd_t<BF16, 1>(p, st) : launch_fwd_t<BF16, 2>(p, st);
+}
+
+}  // namespace tsa

@@ -1,0 +1,420 @@
+// Selected-block lists.
+//
+// Block-sparse attention ("aclnnBlockSparseAttentionGrad", function
+// description): the BlockSparseMask names, per Q block, the KV blocks it
+// attends to.  The forward and dQ kernels walk, per Q block, the ascending
+// list of selected KV blocks (forward CSR); the dK/dV kernel walks, per KV
+// block, the ascending list of Q blocks that selected it (reverse CSR).
+//
+// NSA selected attention ("aclnnNsaSelectedAttention", formulas section):
+// per (token, KV head) the topk_indices, sorted, with wholly-masked blocks
+// dropped under causal mode (forward CSR), and per (KV head, block) the
+// tokens that selected it (reverse CSR).
+//
+// Every list is built deterministically without atomics: counts, an
+// exclusive scan, then a fill in which each entry's slot is its rank.
+#include "tsa_device.h"
+#include "tsa_internal.h"
+
+namespace tsa {
+
+// ---------------------------------------------------------------------------
+// Exclusive scan of an int32 array (in place), three passes.
+// ---------------------------------------------------------------------------
+constexpr int kScanThreads = 1024;
+constexpr int kScanPer = 4;
+constexpr int kScanTile = kScanThreads * kScanPer;
+
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+// Block-wide exclusive scan of one value per thread; returns the exclusive
+// prefix, *total gets the block sum.
+__device__ __forceinline__ int block_excl_scan(int x, int* total) {
+  __shared__ int wsum[kScanThreads / 64];
+  __shared__ int tot;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  const int incl = wave_incl_scan(x);
+  if (lane == 63) wsum[wid] = incl;
+  __syncthreads();
+  if (wid == 0) {
+    const int v = lane < nw ? wsum[lane] : 0;
+    const int vi = wave_incl_scan(v);
+    if (lane < nw) wsum[lane] = vi - v;
+    if (lane == nw - 1) tot = vi;
+  }
+  __syncthreads();
+  const int excl = wsum[wid] + incl - x;
+  *total = tot;
+  __syncthreads();  // wsum / tot are reused by the next call
+  return excl;
+}
+
+// ptr[i] = scanned[i] for i < n, ptr[n] = *total.
+__global__ void copy_ptr(const int* scanned, long n, const int* total, int* ptr) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) ptr[i] = scanned[i];
+  else if (i == n) ptr[n] = total[0];
+}
+
+__global__ __launch_bounds__(kScanThreads) void scan_tiles(int* data, int n, int* sums) {
+  const int base = blockIdx.x * kScanTile + threadIdx.x * kScanPer;
+  int v[kScanPer];
+  int s = 0;
+#pragma unroll
+  for (int i = 0; i < kScanPer; i++) {
+    v[i] = (base + i < n) ? data[base + i] : 0;
+    s += v[i];
+  }
+  int total;
+  int ex = block_excl_scan(s, &total);
+#pragma unroll
+  for (int i = 0; i < kScanPer; i++) {
+    if (base + i < n) data[base + i] = ex;
+    ex += v[i];
+  }
+  if (threadIdx.x == 0) sums[blockIdx.x] = total;
+}
+
+// Single block: exclusive scan of the tile sums; sums[nt] = grand total.
+__global__ __launch_bounds__(kScanThreads) void scan_sums(int* sums, int nt) {
+  int carry = 0;
+  for (int base = 0; base < nt; base += kScanThreads) {
+    int i = base + threadIdx.x;
+    int x = i < nt ? sums[i] : 0;
+    int total;
+    int ex = block_excl_scan(x, &total);
+    if (i < nt) sums[i] = carry + ex;
+    carry += total;
+  }
+  if (threadIdx.x == 0) sums[nt] = carry;
+}
+
+__global__ __launch_bounds__(kScanThreads) void scan_add(int* data, int n, const int* sums) {
+  const int add = sums[blockIdx.x];
+  const int base = blockIdx.x * kScanTile + threadIdx.x * kScanPer;
+#pragma unroll
+  for (int i = 0; i < kScanPer; i++)
+    if (base + i < n) data[base + i] += add;
+}
+
+int scan_sums_len(long n) { return (int)((n + kScanTile - 1) / kScanTile) + 1; }
+
+hipError_t exclusive_scan(int* data, long n, int* sums, hipStream_t st) {
+  int nt = (int)((n + kScanTile - 1) / kScanTile);
+  if (nt == 0) {
+    hipLaunchKernelGGL(scan_sums, dim3(1), dim3(kScanThreads), 0, st, sums, 0);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(scan_tiles, dim3(nt), dim3(kScanThreads), 0, st, data, (int)n, sums);
+  hipLaunchKernelGGL(scan_sums, dim3(1), dim3(kScanThreads), 0, st, sums, nt);
+  hipLaunchKernelGGL(scan_add, dim3(nt), dim3(kScanThreads), 0, st, data, (int)n, sums);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// BlockSparseMask -> forward / reverse CSR via 64 x 64 bit tiles.
+//
+// Rows of the mask are (b, n1, qb); the G*QB rows of the query heads of one
+// KV head (b, n2) are contiguous.  A tile covers 64 rows of one such group
+// and 64 KV-block columns.  Pass 1 writes per-(row, column tile) and
+// per-(column, row tile) counts into one array; after its exclusive scan,
+// pass 2 writes each selected entry at its rank.
+// ---------------------------------------------------------------------------
+struct MaskTileGeom {
+  int R, KB, QB, G, RG, RTG, CT, groups;  // RG = G*QB rows per group
+};
+
+constexpr int kTileStride = 68;  // bytes per LDS tile row (odd dword count: conflict-free columns)
+
+__device__ __forceinline__ void load_mask_tile(const uint8_t* mask, const MaskTileGeom& g, int grp,
+                                               int rt, int ct, uint8_t* tile) {
+  const int lane = threadIdx.x;
+  const int lrow = rt * 64 + lane;                  // row within group
+  const long row = (long)grp * g.RG + lrow;
+  const int c0 = ct * 64;
+  const int nc = min(64, g.KB - c0);
+  uint8_t* dst = tile + lane * kTileStride;
+  if (lrow < g.RG) {
+    const uint8_t* src = mask + row * g.KB + c0;
+    if ((g.KB & 15) == 0) {
+      for (int i = 0; i < nc; i += 16) {
+        uint4 u = *reinterpret_cast<const uint4*>(src + i);
+        uint32_t w[4] = {u.x, u.y, u.z, u.w};
+        for (int j = 0; j < 4; j++) *reinterpret_cast<uint32_t*>(dst + i + 4 * j) = w[j];
+      }
+    } else {
+      for (int i = 0; i < nc; i++) dst[i] = src[i];
+    }
+    for (int i = nc; i < 64; i++) dst[i] = 0;
+  } else {
+    for (int i = 0; i < 64; i++) dst[i] = 0;
+  }
+}
+
+__global__ __launch_bounds__(64) void bsa_mask_count(const uint8_t* mask, MaskTileGeom g,
+                                                     int* parts) {
+  __shared__ uint8_t tile[64 * kTileStride];
+  const int ct = blockIdx.x % g.CT;
+  const int rtg = blockIdx.x / g.CT;
+  const int grp = rtg / g.RTG, rt = rtg % g.RTG;
+  const int lane = threadIdx.x;
+  load_mask_tile(mask, g, grp, rt, ct, tile);
+  __syncthreads();
+  // row counts within this column tile
+  int rc = 0;
+  for (int c = 0; c < 64; c++) rc += tile[lane * kTileStride + c] != 0;
+  const int lrow = rt * 64 + lane;
+  if (lrow < g.RG) parts[((long)grp * g.RG + lrow) * g.CT + ct] = rc;
+  // column counts within this row tile
+  int myc = 0;
+  for (int c = 0; c < 64; c++) {
+    unsigned long long bits = __ballot(tile[lane * kTileStride + c] != 0);
+    if (lane == c) myc = __popcll(bits);
+  }
+  const int col = ct * 64 + lane;
+  if (col < g.KB) parts[(long)g.R * g.CT + ((long)grp * g.KB + col) * g.RTG + rt] = myc;
+}
+
+__global__ __launch_bounds__(64) void bsa_mask_fill(const uint8_t* mask, MaskTileGeom g,
+                                                    const int* scanned, const int* sums_total,
+                                                    int* row_ptr, int* col, int* rev_ptr,
+                                                    int* rev) {
+  __shared__ uint8_t tile[64 * kTileStride];
+  const int ct = blockIdx.x % g.CT;
+  const int rtg = blockIdx.x / g.CT;
+  const int grp = rtg / g.RTG, rt = rtg % g.RTG;
+  const int lane = threadIdx.x;
+  load_mask_tile(mask, g, grp, rt, ct, tile);
+  __syncthreads();
+  const long colpart0 = (long)g.R * g.CT;
+  // total of the row parts = exclusive prefix of the first column part
+  const int nnz = scanned[colpart0];
+  const int lrow = rt * 64 + lane;
+  const long row = (long)grp * g.RG + lrow;
+  int my_rbase = 0;
+  if (lrow < g.RG) {
+    my_rbase = scanned[row * g.CT + ct];
+    if (ct == 0) row_ptr[row] = my_rbase;
+  }
+  const int mycol = ct * 64 + lane;
+  int my_cbase = 0;
+  if (mycol < g.KB) {
+    my_cbase = scanned[colpart0 + ((long)grp * g.KB + mycol) * g.RTG + rt] - nnz;
+    if (rt == 0) rev_ptr[(long)grp * g.KB + mycol] = my_cbase;
+  }
+  if (blockIdx.x == 0 && lane == 0) {
+    row_ptr[g.R] = nnz;
+    rev_ptr[(long)g.groups * g.KB] = sums_total[0] - nnz;
+  }
+  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  // forward entries: for each row of the tile, lanes are columns
+  for (int r = 0; r < 64; r++) {
+    const bool bit = tile[r * kTileStride + lane] != 0;
+    const unsigned long long bits = __ballot(bit);
+    const int base = __shfl(my_rbase, r);
+    if (bit) col[base + __popcll(bits & below)] = ct * 64 + lane;
+  }
+  // reverse entries: for each column of the tile, lanes are rows
+  for (int c = 0; c < 64; c++) {
+    const bool bit = tile[lane * kTileStride + c] != 0;
+    const unsigned long long bits = __ballot(bit);
+    const int base = __shfl(my_cbase, c);
+    if (bit) rev[base + __popcll(bits & below)] = lrow;
+  }
+}
+
+MaskTileGeom mask_geom(int B, int N1, int N2, int QB, int KB) {
+  MaskTileGeom g;
+  g.R = B * N1 * QB;
+  g.KB = KB;
+  g.QB = QB;
+  g.G = N1 / N2;
+  g.RG = g.G * QB;
+  g.RTG = (g.RG + 63) / 64;
+  g.CT = (KB + 63) / 64;
+  g.groups = B * N2;
+  return g;
+}
+
+long bsa_compact_parts_len(int B, int N1, int N2, int QB, int KB) {
+  MaskTileGeom g = mask_geom(B, N1, N2, QB, KB);
+  return (long)g.R * g.CT + (long)g.groups * g.KB * g.RTG;
+}
+
+hipError_t launch_bsa_compact(const uint8_t* mask, int B, int N1, int N2, int QB, int KB,
+                              int* parts, int* sums, int* row_ptr, int* col, int* rev_ptr,
+                              int* rev, hipStream_t st) {
+  MaskTileGeom g = mask_geom(B, N1, N2, QB, KB);
+  const long nparts = bsa_compact_parts_len(B, N1, N2, QB, KB);
+  const int ntiles = g.groups * g.RTG * g.CT;
+  hipLaunchKernelGGL(bsa_mask_count, dim3(ntiles), dim3(64), 0, st, mask, g, parts);
+  hipError_t e = exclusive_scan(parts, nparts, sums, st);
+  if (e != hipSuccess) return e;
+  const int nt = (int)((nparts + kScanTile - 1) / kScanTile);
+  hipLaunchKernelGGL(bsa_mask_fill, dim3(ntiles), dim3(64), 0, st, mask, g, parts, sums + nt,
+                     row_ptr, col, rev_ptr, rev);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// NSA topk_indices -> forward / reverse CSR.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ int seq_of(const int* cu, int nseq, int t) {
+  int lo = 0, hi = nseq - 1;  // largest b with cu[b] <= t
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// A slot survives if its id is in range and, under causal mode, its block
+// starts at or before the token's position.
+__device__ __forceinline__ bool nsa_keep(int id, int pos, int nblk, int sbs, int causal) {
+  return id >= 0 && id < nblk && (!causal || id * sbs <= pos);
+}
+
+// One thread per (t, n2) row: count of kept slots.
+__global__ __launch_bounds__(256) void nsa_row_count(const int* topk, NsaGeom g, int* cnt) {
+  const long r = (long)blockIdx.x * 256 + threadIdx.x;
+  if (r >= (long)g.T * g.N2) return;
+  const int t = (int)(r / g.N2);
+  const int b = seq_of(g.cu_q, g.B, t);
+  const int pos = t - g.cu_q[b];
+  const int nblk = g.blk_off[b + 1] - g.blk_off[b];
+  const int* row = topk + r * g.sbc;
+  int c = 0;
+  for (int i = 0; i < g.sbc; i++) c += nsa_keep(row[i], pos, nblk, g.sbs, g.causal);
+  cnt[r] = c;
+}
+
+// One thread per (t, n2) row: each kept slot goes to its rank among the kept
+// slots ordered by (id, slot).
+__global__ __launch_bounds__(256) void nsa_row_fill(const int* topk, NsaGeom g, const int* row_ptr,
+                                                    int* col) {
+  const long r = (long)blockIdx.x * 256 + threadIdx.x;
+  if (r >= (long)g.T * g.N2) return;
+  const int t = (int)(r / g.N2);
+  const int b = seq_of(g.cu_q, g.B, t);
+  const int pos = t - g.cu_q[b];
+  const int nblk = g.blk_off[b + 1] - g.blk_off[b];
+  const int* row = topk + r * g.sbc;
+  const int base = row_ptr[r];
+  for (int i = 0; i < g.sbc; i++) {
+    const int vi = row[i];
+    if (!nsa_keep(vi, pos, nblk, g.sbs, g.causal)) continue;
+    int rank = 0;
+    for (int j = 0; j < g.sbc; j++) {
+      const int vj = row[j];
+      if (nsa_keep(vj, pos, nblk, g.sbs, g.causal) && (vj < vi || (vj == vi && j < i))) rank++;
+    }
+    col[base + rank] = vi;
+  }
+}
+
+// Occurrences of block id in a sorted row.
+__device__ __forceinline__ int count_in_sorted(const int* a, int n, int id) {
+  int lo = 0, hi = n;
+  while (lo < hi) { int m = (lo + hi) >> 1; if (a[m] < id) lo = m + 1; else hi = m; }
+  int c = 0;
+  while (lo + c < n && a[lo + c] == id) c++;
+  return c;
+}
+
+// One wave per (n2, global block): lanes walk the tokens of the block's
+// sequence; pass 0 counts, pass 1 writes token ids in ascending order.
+template <int PASS>
+__global__ __launch_bounds__(256) void nsa_rev(NsaGeom g, const int* row_ptr, const int* col,
+                                               int* rev_cnt, const int* rev_ptr, int* rev) {
+  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (wave >= g.N2 * g.NB) return;
+  const int n2 = wave / g.NB, gb = wave % g.NB;
+  const int b = seq_of(g.blk_off, g.B, gb);
+  const int id = gb - g.blk_off[b];
+  const int t0 = g.cu_q[b], t1 = g.cu_q[b + 1];
+  // under causal mode tokens before the block's first key cannot keep it
+  const int tstart = g.causal ? max(t0, t0 + id * g.sbs) : t0;
+  int out = PASS ? rev_ptr[wave] : 0;
+  int total = 0;
+  for (int tb = tstart; tb < t1; tb += 64) {
+    const int t = tb + lane;
+    int c = 0;
+    if (t < t1) {
+      const long r = (long)t * g.N2 + n2;
+      c = count_in_sorted(col + row_ptr[r], row_ptr[r + 1] - row_ptr[r], id);
+    }
+    if (PASS) {
+      int incl = wave_incl_scan(c);
+      int pos = out + incl - c;
+      for (int k = 0; k < c; k++) rev[pos + k] = t;
+      out += __shfl(incl, 63);
+    } else {
+      total += c;
+    }
+  }
+  if (!PASS) {
+    for (int o = 32; o > 0; o >>= 1) total += __shfl_xor(total, o);
+    if (lane == 0) rev_cnt[wave] = total;
+  }
+}
+
+// Data check for validate = 1: counts ids outside [0, nblk).
+__global__ __launch_bounds__(256) void nsa_check_ids(const int* topk, NsaGeom g, int* bad) {
+  const long r = (long)blockIdx.x * 256 + threadIdx.x;
+  if (r >= (long)g.T * g.N2) return;
+  const int t = (int)(r / g.N2);
+  const int b = seq_of(g.cu_q, g.B, t);
+  const int nblk = g.blk_off[b + 1] - g.blk_off[b];
+  int c = 0;
+  for (int i = 0; i < g.sbc; i++) {
+    int v = topk[r * g.sbc + i];
+    c += (v < 0 || v >= nblk);
+  }
+  if (c) bad[0] = 1;  // benign race: every writer stores the same value
+}
+
+hipError_t launch_nsa_check(const int* topk, const NsaGeom& g, int* bad, hipStream_t st) {
+  const long rows = (long)g.T * g.N2;
+  hipLaunchKernelGGL(nsa_check_ids, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, topk,
+                     g, bad);
+  return hipGetLastError();
+}
+
+hipError_t launch_nsa_compact(const int* topk, const NsaGeom& g, int* cnt_scan, int* sums,
+                              int* row_ptr, int* col, int* rev_scan, int* rev_ptr, int* rev,
+                              hipStream_t st) {
+  const long rows = (long)g.T * g.N2;
+  const unsigned rb = (unsigned)((rows + 255) / 256);
+  // forward: counts -> scan -> fill
+  hipLaunchKernelGGL(nsa_row_count, dim3(rb), dim3(256), 0, st, topk, g, cnt_scan);
+  hipError_t e = exclusive_scan(cnt_scan, rows, sums, st);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(copy_ptr, dim3((unsigned)((rows + 256) / 256)), dim3(256), 0, st, cnt_scan,
+                     rows, sums + (rows + kScanTile - 1) / kScanTile, row_ptr);
+  hipLaunchKernelGGL(nsa_row_fill, dim3(rb), dim3(256), 0, st, topk, g, row_ptr, col);
+  // reverse: counts -> scan -> fill
+  const long rrows = (long)g.N2 * g.NB;
+  const unsigned wb = (unsigned)((rrows + 3) / 4);
+  hipLaunchKernelGGL(nsa_rev<0>, dim3(wb), dim3(256), 0, st, g, row_ptr, col, rev_scan,
+                     (const int*)nullptr, (int*)nullptr);
+  e = exclusive_scan(rev_scan, rrows, sums, st);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(copy_ptr, dim3((unsigned)((rrows + 256) / 256)), dim3(256), 0, st, rev_scan,
+                     rrows, sums + (rrows + kScanTile - 1) / kScanTile, rev_ptr);
+  hipLaunchKernelGGL(nsa_rev<1>, dim3(wb), dim3(256), 0, st, g, row_ptr, col, (int*)nullptr,
+                     (const int*)rev_ptr, rev);
+  return hipGetLastError();
+}
+
+}  // namespace tsa

@@ -1,0 +1,108 @@
+// Device-side building blocks for gfx950 (CDNA4, wave64).
+//
+// MFMA operand layouts used throughout (checked on the device by an in-bounds
+// probe of the builtins):
+//   v_mfma_f32_32x32x16_{bf16,f16}: A (32 x 16) lane l holds row l%32 and
+//     8 k-values of half l/32; B (16 x 32) lane l holds column l%32 and the 8
+//     k-values of the same half; C (32 x 32, 16 fp32 per lane) element j of
+//     lane l is row 8*(j/4) + 4*(l/32) + j%4, column l%32.
+//   v_mfma_f32_16x16x32_{bf16,f16}: A lane l holds row l%16 and 8 k-values of
+//     quarter l/16; C element j of lane l is row 4*(l/16) + j, column l%16.
+// Which 8 k-values a lane holds is free as long as A and B agree; the
+// kernels use that freedom to feed accumulator tiles straight back in as
+// operands.
+//
+// ds_read_b64_tr_b16 (LDS transpose read): within each group of 16 lanes,
+// output element j of lane i is element i%4 of the 4 x 16-bit values that
+// lane 4*j + i/4 of the group addressed.  Pointing lane 4*j + c at
+// row_j[4c .. 4c+3] therefore hands lane i the column entries
+// row_0[i], .., row_3[i]: a transposed 16 x 4 tile, used to read V (and K,
+// Q, dO in the backward) as the k-major MFMA operand without transposing it
+// in memory.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tsa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Element type traits: storage type, 8-wide MFMA operand, conversions.
+struct BF16 {
+  typedef __bf16 T;
+  typedef bf16x8 V8;
+  static __device__ __forceinline__ f32x16 mfma32(V8 a, V8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mfma16(V8 a, V8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ T from_f32(float x) { return (T)x; }
+  static __device__ __forceinline__ float to_f32(T x) { return (float)x; }
+};
+
+struct FP16 {
+  typedef _Float16 T;
+  typedef f16x8 V8;
+  static __device__ __forceinline__ f32x16 mfma32(V8 a, V8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mfma16(V8 a, V8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ T from_f32(float x) { return (T)x; }
+  static __device__ __forceinline__ float to_f32(T x) { return (float)x; }
+};
+
+// 16-byte global load / store of 8 16-bit elements.
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+
+template <typename V8>
+__device__ __forceinline__ V8 as_v8(uint4 u) {
+  return __builtin_bit_cast(V8, u);
+}
+
+// Two transposed LDS reads give one 8-wide operand.
+template <typename V8>
+__device__ __forceinline__ V8 lds_read_tr_pair(const void* p0, const void* p1) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)(const char*)p0);
+  s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)(const char*)p1);
+  s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(V8, v);
+}
+
+template <typename V8>
+__device__ __forceinline__ V8 lds_read16(const void* p) {
+  return __builtin_bit_cast(V8, *reinterpret_cast<const uint4*>(p));
+}
+
+__device__ __forceinline__ float wave_max_half_swap(float x) {
+  // combine lanes l and l^32
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// XCD-aware workgroup -> work-item remap.  Workgroups are dispatched to the 8
+// XCDs round-robin (workgroup w runs on XCD w % 8).  Giving XCD x the
+// contiguous range [x * per, (x + 1) * per) of the work order keeps the work
+// items an XCD runs together adjacent in that order, so their shared K/V
+// blocks stay in that XCD's L2.  Returns -1 for the padding workgroups.
+__device__ __forceinline__ int xcd_remap(int w, int n_items, int n_xcd = 8) {
+  int per = (n_items + n_xcd - 1) / n_xcd;
+  int item = (w % n_xcd) * per + (w / n_xcd);
+  return item < n_items ? item : -1;
+}
+
+}  // namespace tsa

@@ -1,0 +1,106 @@
+// Host-side declarations shared by the launchers and the C-ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tsa {
+
+// ----- scans and lists -----------------------------------------------------
+int scan_sums_len(long n);
+hipError_t exclusive_scan(int* data, long n, int* sums, hipStream_t st);
+
+long bsa_compact_parts_len(int B, int N1, int N2, int QB, int KB);
+hipError_t launch_bsa_compact(const uint8_t* mask, int B, int N1, int N2, int QB, int KB,
+                              int* parts, int* sums, int* row_ptr, int* col, int* rev_ptr,
+                              int* rev, hipStream_t st);
+
+// NSA geometry as the device sees it (pointers into the workspace).
+struct NsaGeom {
+  const int* cu_q;     // [B+1] query prefix sums
+  const int* cu_kv;    // [B+1] key prefix sums
+  const int* blk_off;  // [B+1] prefix sums of ceil(Skv_b / sbs)
+  int B, T, N2, sbc, sbs, causal, NB;
+};
+
+hipError_t launch_nsa_compact(const int* topk, const NsaGeom& g, int* cnt_scan, int* sums,
+                              int* row_ptr, int* col, int* rev_scan, int* rev_ptr, int* rev,
+                              hipStream_t st);
+hipError_t launch_nsa_check(const int* topk, const NsaGeom& g, int* bad, hipStream_t st);
+
+// ----- block-sparse attention ---------------------------------------------
+struct BsaParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;      // backward: forward output
+  const void* dout;   // backward
+  void* out;          // forward output / backward dq
+  void* dk;
+  void* dv;
+  float* lse;         // forward: written; backward: read
+  float* delta;       // backward: rowsum(dO * O), fp32 [B, N1, Sq]
+  const int* row_ptr;
+  const int* col;
+  const int* rev_ptr;
+  const int* rev;
+  int B, N1, N2, G, Sq, Skv, D;
+  int bq, bkv, QB, KB;
+  int causal;
+  float scale;
+};
+
+hipError_t launch_bsa_fwd(const BsaParams& p, int fp16, hipStream_t st);
+hipError_t launch_bsa_bwd(const BsaParams& p, int fp16, hipStream_t st);
+
+// ----- NSA selected attention ------------------------------------------------
+struct NsaParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  void* out;          // forward output / backward dq
+  void* dk;
+  void* dv;
+  float* lse;
+  float* delta;
+  const int* row_ptr;
+  const int* col;
+  const int* rev_ptr;
+  const int* rev;
+  NsaGeom g;
+  int T, Tk, N1, N2, G, D;
+  float scale;
+};
+
+hipError_t launch_nsa_fwd(const NsaParams& p, int fp16, hipStream_t st);
+hipError_t launch_nsa_bwd(const NsaParams& p, int fp16, hipStream_t st);
+
+// ----- sparse flash attention (paged decode) ----------------------------------
+struct SfaParams {
+  const void* q;
+  const void* q_rope;
+  const void* kc;
+  const void* krc;
+  const void* vc;
+  const int* block_table;
+  const int* kv_lens;
+  const int* topk;
+  void* out;
+  float* lse;          // may be null
+  float* part_o;       // split partials [B*Sq, splits, N1, Dv] fp32
+  float* part_lse;     // [B*Sq, splits, N1]
+  int* bad;            // validate flag (may be null)
+  int B, Sq, N1, N2, D, Dr, Dv;
+  int num_pages, page, max_pages, topk_n, sbs;
+  int causal;
+  int splits;
+  float scale;
+};
+
+int sfa_splits(const SfaParams& p);
+hipError_t launch_sfa_fwd(const SfaParams& p, int fp16, hipStream_t st);
+hipError_t launch_sfa_check(const SfaParams& p, hipStream_t st);
+
+}  // namespace tsa
