@@ -28,6 +28,13 @@
  * All tensors are dense and contiguous in the stated layout.  `stream` is a
  * hipStream_t (NULL = the null stream).
  *
+ * Every args struct ends with reuse_lists, n_events and events.  Stages
+ * that can be timed, per entry point: bsa_fwd 0 = lists, 1 = attention;
+ * bsa_bwd 0 = lists, 1 = dQ (with softmax_grad), 2 = dK/dV; nsa_select_fwd
+ * 0 = lists, 1 = attention; nsa_select_bwd 0 = lists, 1 = dQ, 2 = dK/dV;
+ * sfa_paged_fwd 0 = split attention, 1 = split combine.  A stage that a call
+ * skips records both of its events back to back.
+ *
  * Errors: every function returns a tsa_status.  No exceptions cross the ABI
  * and nothing calls exit().  The CANN pages' own error-code tables were lost,
  * so the values below are this library's.
@@ -106,6 +113,11 @@ typedef struct {
   const void* v;            /* DEVICE */
   void* out;                /* DEVICE, written */
   float* lse;               /* DEVICE, written */
+  int32_t reuse_lists;      /* 1: the workspace holds this call's lists from an earlier call
+                               with the same mask/indices and workspace; skip building them */
+  int32_t n_events;         /* number of stages to time (0 = off) */
+  void* const* events;      /* HOST array of 2*n_events hipEvent_t: events[2i] / [2i+1] are
+                               recorded on `stream` before / after stage i (see each entry) */
 } bsa_fwd_args;
 
 TSA_API int bsa_fwd_workspace_size(const bsa_fwd_args* args, size_t* bytes);
@@ -140,6 +152,11 @@ typedef struct {
   void* dq;                 /* DEVICE, written */
   void* dk;                 /* DEVICE, written */
   void* dv;                 /* DEVICE, written */
+  int32_t reuse_lists;      /* 1: the workspace holds this call's lists from an earlier call
+                               with the same mask/indices and workspace; skip building them */
+  int32_t n_events;         /* number of stages to time (0 = off) */
+  void* const* events;      /* HOST array of 2*n_events hipEvent_t: events[2i] / [2i+1] are
+                               recorded on `stream` before / after stage i (see each entry) */
 } bsa_bwd_args;
 
 TSA_API int bsa_bwd_workspace_size(const bsa_bwd_args* args, size_t* bytes);
@@ -204,6 +221,11 @@ typedef struct {
   const void* v;            /* DEVICE */
   void* out;                /* DEVICE, written */
   float* lse;               /* DEVICE, written */
+  int32_t reuse_lists;      /* 1: the workspace holds this call's lists from an earlier call
+                               with the same mask/indices and workspace; skip building them */
+  int32_t n_events;         /* number of stages to time (0 = off) */
+  void* const* events;      /* HOST array of 2*n_events hipEvent_t: events[2i] / [2i+1] are
+                               recorded on `stream` before / after stage i (see each entry) */
 } nsa_select_fwd_args;
 
 TSA_API int nsa_select_fwd_workspace_size(const nsa_select_fwd_args* args, size_t* bytes);
@@ -232,6 +254,11 @@ typedef struct {
   void* dq;                 /* DEVICE, written [T, N1, D] */
   void* dk;                 /* DEVICE, written [Tk, N2, D] */
   void* dv;                 /* DEVICE, written [Tk, N2, Dv] */
+  int32_t reuse_lists;      /* 1: the workspace holds this call's lists from an earlier call
+                               with the same mask/indices and workspace; skip building them */
+  int32_t n_events;         /* number of stages to time (0 = off) */
+  void* const* events;      /* HOST array of 2*n_events hipEvent_t: events[2i] / [2i+1] are
+                               recorded on `stream` before / after stage i (see each entry) */
 } nsa_select_bwd_args;
 
 TSA_API int nsa_select_bwd_workspace_size(const nsa_select_bwd_args* args, size_t* bytes);
@@ -300,6 +327,11 @@ typedef struct {
   const int32_t* topk_indices;  /* DEVICE */
   void* out;                /* DEVICE, written */
   float* lse;               /* DEVICE, written, or NULL */
+  int32_t reuse_lists;      /* 1: the workspace holds this call's lists from an earlier call
+                               with the same mask/indices and workspace; skip building them */
+  int32_t n_events;         /* number of stages to time (0 = off) */
+  void* const* events;      /* HOST array of 2*n_events hipEvent_t: events[2i] / [2i+1] are
+                               recorded on `stream` before / after stage i (see each entry) */
 } sfa_paged_fwd_args;
 
 TSA_API int sfa_paged_fwd_workspace_size(const sfa_paged_fwd_args* args, size_t* bytes);

@@ -167,3 +167,118 @@ def test_fwd_bsa_causal_8k_sampled():
              for qb in sorted(set(list(range(0, QB, 16)) + [QB - 1]))]
     tiles = tiles[::4]              # a quarter of those keeps the oracle to seconds
     _fwd_check(q, k, v, mask, w["bq"], w["bkv"], scale, 0, q_tiles=tiles)
+
+
+# ----------------------------------------------------------------------------
+# Backward parity, determinism, perturbation
+# ----------------------------------------------------------------------------
+
+def _bwd_gpu(q, k, v, do, mask, bq, bkv, scale, mode):
+    tsa = _tsa()
+    qd, kd, vd, dod, md = _dev(q, k, v, do, torch.from_numpy(mask))
+    plan = tsa.BsaPlan(qd, kd, vd, md, bq, bkv, scale, mode)
+    out, lse = plan.fwd()
+    dq, dk, dv = plan.bwd(dod)
+    torch.cuda.synchronize()
+    return out, lse, dq, dk, dv
+
+
+def _bwd_check(q, k, v, do, mask, bq, bkv, scale, mode, q_tiles=None, kv_rows=None):
+    out, lse, dq, dk, dv = _bwd_gpu(q, k, v, do, mask, bq, bkv, scale, mode)
+    rdq, rdk, rdv = oracle.bsa_bwd(_np(q), _np(k), _np(v), _np(out), _np(do), mask, bq, bkv,
+                                   scale, mode, q_tiles=q_tiles)
+    qrows = None
+    if q_tiles is not None:
+        qrows = np.zeros(rdq.shape[:3], bool)
+        for b, n, qb in q_tiles:
+            qrows[b, n, qb * bq:(qb + 1) * bq] = True
+    _close(dq, rdq, GRAD_TOL, "dq", qrows)
+    _close(dk, rdk, GRAD_TOL, "dk", kv_rows)
+    _close(dv, rdv, GRAD_TOL, "dv", kv_rows)
+
+
+def test_bwd_bsa_small_fp16_64x64():
+    w, q, k, v, do, mask, scale = W.bsa_inputs(1)
+    _bwd_check(q, k, v, do, mask, 64, 64, scale, 0)
+
+
+@pytest.mark.parametrize("mode", [0, 2])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_bwd_causal_shaped_128_several_tiles(mode, dtype):
+    q, k, v, do, mask = _inputs(1, 2, 2, 1024, 1024, dtype, 400,
+                                lambda r: W.mask_random(r, 1, 2, 8, 8, 0.25, causal=True))
+    _bwd_check(q, k, v, do, mask, 128, 128, 1 / math.sqrt(128), mode)
+
+
+@pytest.mark.parametrize("Sq,Skv,bq,bkv,N1,N2", [
+    (1000, 1000, 128, 128, 2, 2),
+    (300, 520, 64, 96, 4, 2),
+    (200, 200, 256, 32, 1, 1),
+    (77, 150, 48, 80, 2, 1),
+    (256, 384, 128, 192, 2, 2),     # block_kv spanning two dK/dV workgroups
+])
+def test_bwd_ragged_and_gqa(Sq, Skv, bq, bkv, N1, N2):
+    QB, KB = -(-Sq // bq), -(-Skv // bkv)
+    q, k, v, do, mask = _inputs(1, N1, N2, Sq, Skv, torch.bfloat16, 500,
+                                lambda r: W.mask_random(r, 1, N1, QB, KB, 0.4, diagonal=False))
+    mask[0, 0, 0, :] = 0
+    if KB > 1:
+        mask[:, :, :, KB - 1] = 0   # a KV block nobody selects: dK = dV = 0
+    for mode in (0, 2):
+        _bwd_check(q, k, v, do, mask, bq, bkv, 0.09, mode)
+
+
+def test_bwd_bsa_causal_8k_sampled():
+    """Full 2x16x8192 workload: dQ on sampled Q blocks; dK/dV on sampled KV
+    blocks, each with every Q block on its reverse list included."""
+    w, q, k, v, do, mask, scale = W.bsa_inputs(2)
+    bq = w["bq"]
+    QB = w["S"] // bq
+    heads = [(0, 0), (1, 7), (1, 15)]
+    kv_blocks = [0, 31, QB - 1]
+    tiles = set()
+    kv_rows = np.zeros((w["B"], w["N2"], w["S"]), bool)
+    for b, n in heads:
+        for qb in (0, QB // 2, QB - 1):
+            tiles.add((b, n, qb))
+        for kb in kv_blocks:
+            kv_rows[b, n, kb * bq:(kb + 1) * bq] = True
+            for qb in np.nonzero(mask[b, n, :, kb])[0]:
+                tiles.add((b, n, int(qb)))
+    _bwd_check(q, k, v, do, mask, bq, w["bkv"], scale, 0, q_tiles=sorted(tiles), kv_rows=kv_rows)
+
+
+def test_bwd_deterministic_bitwise():
+    """Two backward runs give bit-identical gradients (no atomics)."""
+    w, q, k, v, do, mask, scale = W.bsa_inputs(2)
+    tsa = _tsa()
+    qd, kd, vd, dod, md = _dev(q, k, v, do, torch.from_numpy(mask))
+    plan = tsa.BsaPlan(qd, kd, vd, md, w["bq"], w["bkv"], scale, 0)
+    plan.fwd()
+    g1 = [t.clone() for t in plan.bwd(dod)]
+    g2 = [t.clone() for t in plan.bwd(dod)]
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("mode", [0, 2])
+def test_unselected_blocks_are_never_read(mode):
+    """Noise in KV blocks nobody selects leaves O, LSE and dQ bit-identical and
+    their dK/dV exactly zero."""
+    B, N, S, bq = 1, 2, 1024, 128
+    q, k, v, do, mask = _inputs(B, N, N, S, S, torch.bfloat16, 600,
+                                lambda r: W.mask_random(r, B, N, 8, 8, 0.3, causal=True))
+    mask[:, :, :, 3] = 0
+    mask[:, :, 3, 3] = 0
+    r1 = _bwd_gpu(q, k, v, do, mask, bq, bq, 0.088, mode)
+    k2, v2 = k.clone(), v.clone()
+    k2[:, :, 3 * bq:4 * bq] = W.normal((B, N, bq, 128), 99) * 50
+    v2[:, :, 3 * bq:4 * bq] = W.normal((B, N, bq, 128), 98) * 50
+    r2 = _bwd_gpu(q, k2, v2, do, mask, bq, bq, 0.088, mode)
+    for i in range(3):
+        assert torch.equal(r1[i], r2[i])
+    sel = torch.ones(S, dtype=torch.bool)
+    sel[3 * bq:4 * bq] = False
+    assert torch.equal(r1[3][:, :, sel], r2[3][:, :, sel])
+    assert torch.equal(r1[4][:, :, sel], r2[4][:, :, sel])
+    assert (r2[3][:, :, ~sel] == 0).all() and (r2[4][:, :, ~sel] == 0).all()

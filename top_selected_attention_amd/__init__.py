@@ -27,7 +27,7 @@ LIB_PATH = os.path.join(_HERE, "libtsa.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is missing: build it with `python -m top_selected_attention_amd.build` "
+        f"{LIB_PATH} is missing: build it with `python top_selected_attention_amd/build.py` "
         "(there is no fallback implementation)")
 
 lib = _abi.load(LIB_PATH)

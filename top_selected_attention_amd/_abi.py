@@ -21,6 +21,10 @@ EXPORTS = [
 ]
 
 
+# reuse_lists, n_events, events: the common tail of every args struct
+TRAIL = [("reuse_lists", c_int32), ("n_events", c_int32), ("events", POINTER(c_void_p))]
+
+
 class TsaError(RuntimeError):
     def __init__(self, status, text):
         super().__init__(f"{STATUS.get(status, status)}: {text}")
@@ -35,7 +39,7 @@ class BsaFwdArgs(ctypes.Structure):
         ("scale", c_float), ("validate", c_int32),
         ("block_mask", c_void_p), ("q", c_void_p), ("k", c_void_p), ("v", c_void_p),
         ("out", c_void_p), ("lse", c_void_p),
-    ]
+    ] + TRAIL
 
 
 class BsaBwdArgs(ctypes.Structure):
@@ -47,7 +51,7 @@ class BsaBwdArgs(ctypes.Structure):
         ("block_mask", c_void_p), ("q", c_void_p), ("k", c_void_p), ("v", c_void_p),
         ("out", c_void_p), ("dout", c_void_p), ("lse", c_void_p),
         ("dq", c_void_p), ("dk", c_void_p), ("dv", c_void_p),
-    ]
+    ] + TRAIL
 
 
 _NSA_COMMON = [
@@ -61,14 +65,14 @@ _NSA_COMMON = [
 
 
 class NsaFwdArgs(ctypes.Structure):
-    _fields_ = _NSA_COMMON + [("out", c_void_p), ("lse", c_void_p)]
+    _fields_ = _NSA_COMMON + [("out", c_void_p), ("lse", c_void_p)] + TRAIL
 
 
 class NsaBwdArgs(ctypes.Structure):
     _fields_ = _NSA_COMMON + [
         ("out", c_void_p), ("dout", c_void_p), ("lse", c_void_p),
         ("dq", c_void_p), ("dk", c_void_p), ("dv", c_void_p),
-    ]
+    ] + TRAIL
 
 
 class SfaArgs(ctypes.Structure):
@@ -82,7 +86,7 @@ class SfaArgs(ctypes.Structure):
         ("key_rope_cache", c_void_p), ("value_cache", c_void_p),
         ("block_table", c_void_p), ("kv_lens", c_void_p), ("topk_indices", c_void_p),
         ("out", c_void_p), ("lse", c_void_p),
-    ]
+    ] + TRAIL
 
 
 ARG_STRUCTS = [BsaFwdArgs, BsaBwdArgs, NsaFwdArgs, NsaBwdArgs, SfaArgs]

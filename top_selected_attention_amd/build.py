@@ -1,6 +1,7 @@
 """Builds the HIP library (libtsa.so) for gfx950 with hipcc, in-tree.
 
-Usage: python -m top_selected_attention_amd.build  (or build() from Python).
+Usage: python top_selected_attention_amd/build.py  (or build() from Python; running it as
+a file does not import the package, which needs the library to exist).
 Every call recompiles every source.
 """
 

@@ -39,6 +39,22 @@ inline bool fits_i32(long x) { return x >= 0 && x <= 0x7fffffffL; }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? TSA_OK : TSA_ERR_HIP; }
 
+// Records the caller's timing events around stages (no-op when n == 0).
+struct StageTimer {
+  void* const* ev;
+  int n;
+  hipStream_t st;
+  hipError_t mark(int stage, int end) const {
+    if (!ev || stage >= n) return hipSuccess;
+    return hipEventRecord((hipEvent_t)ev[2 * stage + end], st);
+  }
+};
+
+template <class A>
+StageTimer timer_of(const A* a, hipStream_t st) {
+  return StageTimer{a->events, a->events ? a->n_events : 0, st};
+}
+
 // ---------------------------------------------------------------------------
 // Block-sparse attention
 // ---------------------------------------------------------------------------
@@ -214,6 +230,9 @@ size_t nsa_carve(const A* a, void* ws, NsaWs* out, bool with_delta) {
   return c.off + kAlign;
 }
 
+template <class A>
+void nsa_geom(const A* a, const NsaWs& w, NsaGeom* g);
+
 // Uploads cu_seqlens and block offsets into the workspace and fills the
 // device geometry.
 template <class A>
@@ -233,6 +252,14 @@ int nsa_setup(const A* a, const NsaWs& w, NsaGeom* g, hipStream_t st) {
   // the copy from pageable memory is staged before hipMemcpyAsync returns
   delete[] host;
   if (e != hipSuccess) return TSA_ERR_HIP;
+  nsa_geom(a, w, g);
+  return TSA_OK;
+}
+
+// Device geometry over the workspace's uploaded metadata.
+template <class A>
+void nsa_geom(const A* a, const NsaWs& w, NsaGeom* g) {
+  const int n = a->B + 1;
   g->cu_q = w.meta;
   g->cu_kv = w.meta + n;
   g->blk_off = w.meta + 2 * n;
@@ -243,7 +270,6 @@ int nsa_setup(const A* a, const NsaWs& w, NsaGeom* g, hipStream_t st) {
   g->sbs = a->sbs;
   g->causal = a->sparse_mode == 2;
   g->NB = nsa_blocks_total(a->cu_seqlens_kv, a->B, a->sbs);
-  return TSA_OK;
 }
 
 template <class A>
@@ -408,17 +434,23 @@ int bsa_fwd(const bsa_fwd_args* a, void* ws, size_t ws_bytes, void* stream) {
   bsa_carve(a, ws, &w, false);
   BsaParams p = bsa_params(a->B, a->N1, a->N2, a->Sq, a->Skv, a->block_q, a->block_kv,
                            a->sparse_mode, a->scale);
-  if (p.KB > 0) {
-    hipError_t e = launch_bsa_compact(a->block_mask, a->B, a->N1, a->N2, p.QB, p.KB, w.parts,
-                                      w.sums, w.row_ptr, w.col, w.rev_ptr, w.rev, st);
-    if (e != hipSuccess) return TSA_ERR_HIP;
-  } else {
-    hipError_t e = hipMemsetAsync(w.row_ptr, 0, sizeof(int) * ((long)a->B * a->N1 * p.QB + 1), st);
-    if (e != hipSuccess) return TSA_ERR_HIP;
+  const StageTimer tm = timer_of(a, st);
+  hipError_t e = tm.mark(0, 0);
+  if (e == hipSuccess && !a->reuse_lists) {
+    if (p.KB > 0)
+      e = launch_bsa_compact(a->block_mask, a->B, a->N1, a->N2, p.QB, p.KB, w.parts, w.sums,
+                             w.row_ptr, w.col, w.rev_ptr, w.rev, st);
+    else
+      e = hipMemsetAsync(w.row_ptr, 0, sizeof(int) * ((long)a->B * a->N1 * p.QB + 1), st);
   }
+  if (e == hipSuccess) e = tm.mark(0, 1);
+  if (e != hipSuccess) return TSA_ERR_HIP;
   p.q = a->q; p.k = a->k; p.v = a->v; p.out = a->out; p.lse = a->lse;
   p.row_ptr = w.row_ptr; p.col = w.col;
-  return hip_status(launch_bsa_fwd(p, a->dtype == TSA_FP16, st));
+  e = tm.mark(1, 0);
+  if (e == hipSuccess) e = launch_bsa_fwd(p, a->dtype == TSA_FP16, st);
+  if (e == hipSuccess) e = tm.mark(1, 1);
+  return hip_status(e);
 }
 
 int bsa_bwd_workspace_size(const bsa_bwd_args* a, size_t* bytes) {
@@ -440,19 +472,23 @@ int bsa_bwd(const bsa_bwd_args* a, void* ws, size_t ws_bytes, void* stream) {
   BsaParams p = bsa_params(a->B, a->N1, a->N2, a->Sq, a->Skv, a->block_q, a->block_kv,
                            a->sparse_mode, a->scale);
   const long R = (long)a->B * a->N1 * p.QB, C = (long)a->B * a->N2 * p.KB;
-  if (R > 0 && C > 0) {
-    hipError_t e = launch_bsa_compact(a->block_mask, a->B, a->N1, a->N2, p.QB, p.KB, w.parts,
-                                      w.sums, w.row_ptr, w.col, w.rev_ptr, w.rev, st);
-    if (e != hipSuccess) return TSA_ERR_HIP;
-  } else {
-    hipError_t e = hipMemsetAsync(w.row_ptr, 0, sizeof(int) * (R + 1), st);
-    if (e == hipSuccess) e = hipMemsetAsync(w.rev_ptr, 0, sizeof(int) * (C + 1), st);
-    if (e != hipSuccess) return TSA_ERR_HIP;
+  const StageTimer tm = timer_of(a, st);
+  hipError_t e = tm.mark(0, 0);
+  if (e == hipSuccess && !a->reuse_lists) {
+    if (R > 0 && C > 0) {
+      e = launch_bsa_compact(a->block_mask, a->B, a->N1, a->N2, p.QB, p.KB, w.parts, w.sums,
+                             w.row_ptr, w.col, w.rev_ptr, w.rev, st);
+    } else {
+      e = hipMemsetAsync(w.row_ptr, 0, sizeof(int) * (R + 1), st);
+      if (e == hipSuccess) e = hipMemsetAsync(w.rev_ptr, 0, sizeof(int) * (C + 1), st);
+    }
   }
+  if (e == hipSuccess) e = tm.mark(0, 1);
+  if (e != hipSuccess) return TSA_ERR_HIP;
   p.q = a->q; p.k = a->k; p.v = a->v; p.o = a->out; p.dout = a->dout; p.lse = (float*)a->lse;
   p.out = a->dq; p.dk = a->dk; p.dv = a->dv; p.delta = w.delta;
   p.row_ptr = w.row_ptr; p.col = w.col; p.rev_ptr = w.rev_ptr; p.rev = w.rev;
-  return hip_status(launch_bsa_bwd(p, a->dtype == TSA_FP16, st));
+  return hip_status(launch_bsa_bwd(p, a->dtype == TSA_FP16, st, tm.ev, tm.n));
 }
 
 // ----- NSA -----------------------------------------------------------------
@@ -505,15 +541,25 @@ int nsa_select_fwd(const nsa_select_fwd_args* a, void* ws, size_t ws_bytes, void
   nsa_carve(a, ws, &w, false);
   NsaParams p;
   std::memset(&p, 0, sizeof(p));
-  s = nsa_setup(a, w, &p.g, st);
-  if (s) return s;
-  s = nsa_lists(a, w, p.g, st);
-  if (s) return s;
+  const StageTimer tm = timer_of(a, st);
+  if (tm.mark(0, 0) != hipSuccess) return TSA_ERR_HIP;
+  if (!a->reuse_lists) {
+    s = nsa_setup(a, w, &p.g, st);
+    if (s) return s;
+    s = nsa_lists(a, w, p.g, st);
+    if (s) return s;
+  } else {
+    nsa_geom(a, w, &p.g);
+  }
+  if (tm.mark(0, 1) != hipSuccess) return TSA_ERR_HIP;
   p.q = a->q; p.k = a->k; p.v = a->v; p.out = a->out; p.lse = a->lse;
   p.row_ptr = w.row_ptr; p.col = w.col; p.rev_ptr = w.rev_ptr; p.rev = w.rev;
   p.T = a->T; p.Tk = a->Tk; p.N1 = a->N1; p.N2 = a->N2; p.G = a->N1 / a->N2; p.D = a->D;
   p.scale = a->scale;
-  return hip_status(launch_nsa_fwd(p, a->dtype == TSA_FP16, st));
+  hipError_t e = tm.mark(1, 0);
+  if (e == hipSuccess) e = launch_nsa_fwd(p, a->dtype == TSA_FP16, st);
+  if (e == hipSuccess) e = tm.mark(1, 1);
+  return hip_status(e);
 }
 
 int nsa_select_bwd_workspace_size(const nsa_select_bwd_args* a, size_t* bytes) {
@@ -536,18 +582,28 @@ int nsa_select_bwd(const nsa_select_bwd_args* a, void* ws, size_t ws_bytes, void
   nsa_carve(a, ws, &w, true);
   NsaParams p;
   std::memset(&p, 0, sizeof(p));
-  s = nsa_setup(a, w, &p.g, st);
-  if (s) return s;
-  if (a->T > 0) {
-    s = nsa_lists(a, w, p.g, st);
+  const StageTimer tm = timer_of(a, st);
+  if (tm.mark(0, 0) != hipSuccess) return TSA_ERR_HIP;
+  if (!a->reuse_lists) {
+    s = nsa_setup(a, w, &p.g, st);
     if (s) return s;
+    if (a->T > 0) {
+      s = nsa_lists(a, w, p.g, st);
+      if (s) return s;
+    } else {
+      if (hipMemsetAsync(w.rev_ptr, 0, sizeof(int) * ((long)a->N2 * p.g.NB + 1), st) != hipSuccess)
+        return TSA_ERR_HIP;
+    }
+  } else {
+    nsa_geom(a, w, &p.g);
   }
+  if (tm.mark(0, 1) != hipSuccess) return TSA_ERR_HIP;
   p.q = a->q; p.k = a->k; p.v = a->v; p.o = a->out; p.dout = a->dout; p.lse = (float*)a->lse;
   p.out = a->dq; p.dk = a->dk; p.dv = a->dv; p.delta = w.delta;
   p.row_ptr = w.row_ptr; p.col = w.col; p.rev_ptr = w.rev_ptr; p.rev = w.rev;
   p.T = a->T; p.Tk = a->Tk; p.N1 = a->N1; p.N2 = a->N2; p.G = a->N1 / a->N2; p.D = a->D;
   p.scale = a->scale;
-  return hip_status(launch_nsa_bwd(p, a->dtype == TSA_FP16, st));
+  return hip_status(launch_nsa_bwd(p, a->dtype == TSA_FP16, st, tm.ev, tm.n));
 }
 
 // ----- SFA -----------------------------------------------------------------
@@ -578,7 +634,8 @@ int sfa_paged_fwd(const sfa_paged_fwd_args* a, void* ws, size_t ws_bytes, void* 
     if (e != hipSuccess) return TSA_ERR_HIP;
     if (bad) return TSA_ERR_DATA;
   }
-  return hip_status(launch_sfa_fwd(p, a->dtype == TSA_FP16, st));
+  const StageTimer tm = timer_of(a, st);
+  return hip_status(launch_sfa_fwd(p, a->dtype == TSA_FP16, st, tm.ev, tm.n));
 }
 
 }  // extern "C"

@@ -1,0 +1,432 @@
+// Block-sparse attention backward ("aclnnBlockSparseAttentionGrad", formula
+// section):
+//   softmax_grad = rowsum(dOut * Out),  dP = dOut V^T,
+//   dS = P * (dP - softmax_grad),  dV = P^T dOut,
+//   dQ = (dS K) scale,  dK = (dS^T Q) scale,
+// over the selected blocks only, with P recomputed as exp(scale*S - LSE).
+//
+// Two kernels, each owning its outputs, so nothing is accumulated across
+// workgroups: no atomics, one fixed summation order, bit-identical reruns.
+//   * dQ: one workgroup per Q-block slice walks the Q block's KV list (the
+//     forward CSR).  It first forms softmax_grad for its rows from O and dO
+//     and stores it for the second kernel.
+//   * dK/dV: one workgroup per KV-block slice walks the list of Q blocks that
+//     selected the KV block (the reverse CSR), over all query heads of the
+//     KV head's group.
+// Both stage their streamed operand (K/V resp. Q/dO) in 64-row chunks through
+// double-buffered, swizzled LDS with direct global -> LDS loads, keep the
+// stationary operand in registers, and feed accumulator tiles straight back
+// into the next MFMA as operands (see tsa_device.h).
+#include "tsa_device.h"
+#include "tsa_internal.h"
+
+namespace tsa {
+
+namespace {
+constexpr int kD = 128;
+constexpr int kTileB = 64 * kD * 2;  // one 64-row chunk of a [rows][128] 16-bit tensor
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// dQ (+ softmax_grad).  Each wave owns 64 query rows: two 32-query columns of
+// the transposed products S^T = K Q^T and dP^T = V dO^T, and dQ^T += K^T dS^T.
+// ---------------------------------------------------------------------------
+template <class E, int NW>
+__global__ __launch_bounds__(NW * 64) void bsa_dq_kernel(BsaParams p, int qsub, int n_items) {
+  typedef typename E::T T;
+  typedef typename E::V8 V8;
+  constexpr int NT = NW * 64;
+  __shared__ __attribute__((aligned(1024))) char lds_k[2][kTileB];
+  __shared__ __attribute__((aligned(1024))) char lds_v[2][kTileB];
+
+  const int item = xcd_remap(blockIdx.x, n_items);
+  if (item < 0) return;
+  const int qs = item % qsub;
+  const int t1 = item / qsub;
+  const int qb = p.QB - 1 - (t1 % p.QB);
+  const int bn = t1 / p.QB;
+  const int n1 = bn % p.N1, b = bn / p.N1;
+  const int n2 = n1 / p.G;
+  const int row_lo = qb * p.bq + qs * NT;
+  const int row_hi = min((qb + 1) * p.bq, p.Sq);
+  if (row_lo >= row_hi) return;
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int l32 = lane & 31, h = lane >> 5;
+  const int wrow0 = row_lo + wid * 64;
+
+  const long qoff = (long)bn * p.Sq * kD;
+  const T* qh = (const T*)p.q + qoff;
+  const T* oh = (const T*)p.o + qoff;
+  const T* doh = (const T*)p.dout + qoff;
+  const T* kh = (const T*)p.k + ((long)b * p.N2 + n2) * p.Skv * kD;
+  const T* vh = (const T*)p.v + ((long)b * p.N2 + n2) * p.Skv * kD;
+
+  // Stationary operands: Q^T and dO^T columns of this lane's two queries, and
+  // per-query softmax_grad (computed here from O and dO) and LSE (base 2).
+  V8 qreg[2][8], doreg[2][8];
+  float dlt[2], lse2[2];
+#pragma unroll
+  for (int qt = 0; qt < 2; qt++) {
+    const int row = wrow0 + qt * 32 + l32;
+    const bool ok = row < row_hi;
+    float acc = 0.f;
+#pragma unroll
+    for (int ds = 0; ds < 8; ds++) {
+      const long off = (long)row * kD + ds * 16 + 8 * h;
+      qreg[qt][ds] = ok ? as_v8<V8>(ld16(qh + off)) : zero_v8<V8>();
+      doreg[qt][ds] = ok ? as_v8<V8>(ld16(doh + off)) : zero_v8<V8>();
+      const V8 ov = ok ? as_v8<V8>(ld16(oh + off)) : zero_v8<V8>();
+#pragma unroll
+      for (int e = 0; e < 8; e++) acc += E::to_f32(doreg[qt][ds][e]) * E::to_f32(ov[e]);
+    }
+    acc += __shfl_xor(acc, 32);
+    dlt[qt] = acc;
+    lse2[qt] = ok ? p.lse[(long)bn * p.Sq + row] * kLog2e : 0.f;
+    if (ok && h == 0) p.delta[(long)bn * p.Sq + row] = acc;
+  }
+
+  const int e0 = p.row_ptr[bn * p.QB + qb], e1 = p.row_ptr[bn * p.QB + qb + 1];
+  const int cpb = (p.bkv + 63) / 64;
+  const int nchunks = (e1 - e0) * cpb;
+  const float sl2 = p.scale * kLog2e;
+
+  auto chunk_range = [&](int i, int& ks, int& ke) {
+    const int kb = p.col[e0 + i / cpb];
+    ks = kb * p.bkv + (i % cpb) * 64;
+    ke = min(min(ks + 64, (kb + 1) * p.bkv), p.Skv);
+  };
+  auto next_valid = [&](int i) {
+    for (; i < nchunks; i++) {
+      int ks, ke;
+      chunk_range(i, ks, ke);
+      if (ks < ke && !(p.causal && ks > row_hi - 1)) break;
+    }
+    return i;
+  };
+  auto load_chunk = [&](int ks, int ke, int buf) {
+    auto row_of = [&](int r) { return min(ks + r, ke - 1); };
+    stage_tile64<NW>((const char*)kh, lds_k[buf], row_of);
+    stage_tile64<NW>((const char*)vh, lds_v[buf], row_of);
+  };
+
+  f32x16 dq[2][4];
+#pragma unroll
+  for (int qt = 0; qt < 2; qt++)
+#pragma unroll
+    for (int dt = 0; dt < 4; dt++)
+#pragma unroll
+      for (int j = 0; j < 16; j++) dq[qt][dt][j] = 0.f;
+
+  int i = next_valid(0);
+  if (i < nchunks) {
+    int ks, ke;
+    chunk_range(i, ks, ke);
+    load_chunk(ks, ke, 0);
+  }
+  wait_vm();
+  __syncthreads();
+  int buf = 0;
+  while (i < nchunks) {
+    int ks, ke;
+    chunk_range(i, ks, ke);
+    const int inext = next_valid(i + 1);
+    if (inext < nchunks) {
+      int ks2, ke2;
+      chunk_range(inext, ks2, ke2);
+      load_chunk(ks2, ke2, buf ^ 1);
+    }
+    const char* Kb = lds_k[buf];
+    const char* Vb = lds_v[buf];
+#pragma unroll
+    for (int kt = 0; kt < 2; kt++) {
+      f32x16 st[2], dpt[2];
+#pragma unroll
+      for (int qt = 0; qt < 2; qt++)
+#pragma unroll
+        for (int j = 0; j < 16; j++) st[qt][j] = dpt[qt][j] = 0.f;
+#pragma unroll
+      for (int ds = 0; ds < 8; ds++) {
+        const V8 ak = tile_read16<V8>(Kb, kt * 32 + l32, 2 * ds + h);
+        const V8 av = tile_read16<V8>(Vb, kt * 32 + l32, 2 * ds + h);
+        st[0] = E::mfma32(ak, qreg[0][ds], st[0]);
+        st[1] = E::mfma32(ak, qreg[1][ds], st[1]);
+        dpt[0] = E::mfma32(av, doreg[0][ds], dpt[0]);
+        dpt[1] = E::mfma32(av, doreg[1][ds], dpt[1]);
+      }
+      // dS^T = P^T * (dP^T - softmax_grad), P^T = exp2(S^T * scale*log2e - LSE2)
+#pragma unroll
+      for (int qt = 0; qt < 2; qt++) {
+        const int qrow = wrow0 + qt * 32 + l32;
+#pragma unroll
+        for (int j = 0; j < 16; j++) {
+          const int key = ks + kt * 32 + 8 * (j >> 2) + 4 * h + (j & 3);
+          const bool ok = key < ke && qrow < row_hi && (!p.causal || key <= qrow);
+          const float pv = ok ? fast_exp2(st[qt][j] * sl2 - lse2[qt]) : 0.f;
+          st[qt][j] = pv * (dpt[qt][j] - dlt[qt]);
+        }
+      }
+      // dQ^T += K^T dS^T over the tile's 32 keys (two 16-key steps)
+#pragma unroll
+      for (int k2 = 0; k2 < 2; k2++) {
+        V8 bs[2];
+#pragma unroll
+        for (int qt = 0; qt < 2; qt++)
+#pragma unroll
+          for (int e = 0; e < 8; e++) bs[qt][e] = E::from_f32(st[qt][8 * k2 + e]);
+#pragma unroll
+        for (int dt = 0; dt < 4; dt++) {
+          const V8 a = tile_read_tr<V8>(Kb, kt * 2 + k2, dt);
+          dq[0][dt] = E::mfma32(a, bs[0], dq[0][dt]);
+          dq[1][dt] = E::mfma32(a, bs[1], dq[1][dt]);
+        }
+      }
+    }
+    wait_vm();
+    __syncthreads();
+    buf ^= 1;
+    i = inext;
+  }
+
+#pragma unroll
+  for (int qt = 0; qt < 2; qt++) {
+    const int row = wrow0 + qt * 32 + l32;
+    if (row < row_hi) {
+      T* drow = (T*)p.out + qoff + (long)row * kD;
+#pragma unroll
+      for (int dt = 0; dt < 4; dt++)
+#pragma unroll
+        for (int jj = 0; jj < 4; jj++) {
+          const int d0 = dt * 32 + 8 * jj + 4 * h;
+          *reinterpret_cast<uint2*>(drow + d0) =
+              pack4<E>(dq[qt][dt][4 * jj] * p.scale, dq[qt][dt][4 * jj + 1] * p.scale,
+                       dq[qt][dt][4 * jj + 2] * p.scale, dq[qt][dt][4 * jj + 3] * p.scale);
+        }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK / dV.  Each wave owns 32 keys of the KV block and keeps their K and V as
+// MFMA B operands.  Per 64-query chunk of a selecting Q block:
+//   S = Q K^T and dP = dO V^T (queries x keys, lanes on key columns),
+//   P = exp2(S * scale*log2e - LSE2), dS = P * (dP - softmax_grad),
+//   dV^T += dO^T P and dK^T += Q^T dS, with dO^T / Q^T read from the staged
+//   natural-layout tiles by transpose reads.
+// ---------------------------------------------------------------------------
+template <class E, int NW>
+__global__ __launch_bounds__(NW * 64) void bsa_dkdv_kernel(BsaParams p, int ksub, int n_items) {
+  typedef typename E::T T;
+  typedef typename E::V8 V8;
+  constexpr int NK = NW * 32;  // keys per workgroup
+  __shared__ __attribute__((aligned(1024))) char lds_q[2][kTileB];
+  __shared__ __attribute__((aligned(1024))) char lds_do[2][kTileB];
+  __shared__ float lds_lse[2][64];
+  __shared__ float lds_dlt[2][64];
+
+  const int item = xcd_remap(blockIdx.x, n_items);
+  if (item < 0) return;
+  // Work order: head-major, KV blocks ascending (under causal-shaped masks the
+  // first blocks have the longest reverse lists).
+  const int ksl = item % ksub;
+  const int t1 = item / ksub;
+  const int kb = t1 % p.KB;
+  const int bh = t1 / p.KB;  // b * N2 + n2
+  const int n2 = bh % p.N2, b = bh / p.N2;
+  const int key_lo = kb * p.bkv + ksl * NK;
+  const int key_hi = min((kb + 1) * p.bkv, p.Skv);
+  if (key_lo >= key_hi) return;
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int l32 = lane & 31, h = lane >> 5;
+  const int mykey = key_lo + wid * 32 + l32;
+  const bool key_ok = mykey < key_hi;
+
+  const long kvoff = (long)bh * p.Skv * kD;
+  const T* kh = (const T*)p.k + kvoff;
+  const T* vh = (const T*)p.v + kvoff;
+
+  V8 kreg[8], vreg[8];
+#pragma unroll
+  for (int ds = 0; ds < 8; ds++) {
+    const long off = (long)mykey * kD + ds * 16 + 8 * h;
+    kreg[ds] = key_ok ? as_v8<V8>(ld16(kh + off)) : zero_v8<V8>();
+    vreg[ds] = key_ok ? as_v8<V8>(ld16(vh + off)) : zero_v8<V8>();
+  }
+
+  const int c = bh * p.KB + kb;
+  const int e0 = p.rev_ptr[c], e1 = p.rev_ptr[c + 1];
+  const int cpq = (p.bq + 63) / 64;
+  const int nchunks = (e1 - e0) * cpq;
+  const float sl2 = p.scale * kLog2e;
+
+  // Chunk i: query rows [qs, qe) of query head n1 (entry id g*QB + qb).
+  auto chunk_range = [&](int i, int& n1, int& qs, int& qe) {
+    const int id = p.rev[e0 + i / cpq];
+    const int g = id / p.QB, qb = id % p.QB;
+    n1 = n2 * p.G + g;
+    qs = qb * p.bq + (i % cpq) * 64;
+    qe = min(min(qs + 64, (qb + 1) * p.bq), p.Sq);
+  };
+  auto next_valid = [&](int i) {
+    for (; i < nchunks; i++) {
+      int n1, qs, qe;
+      chunk_range(i, n1, qs, qe);
+      if (qs < qe && !(p.causal && qe - 1 < key_lo)) break;
+    }
+    return i;
+  };
+  auto load_chunk = [&](int n1, int qs, int qe, int buf) {
+    const long hoff = ((long)b * p.N1 + n1) * p.Sq;
+    auto row_of = [&](int r) { return min(qs + r, qe - 1); };
+    stage_tile64<NW>((const char*)((const T*)p.q + hoff * kD), lds_q[buf], row_of);
+    stage_tile64<NW>((const char*)((const T*)p.dout + hoff * kD), lds_do[buf], row_of);
+    if (wid == 0) {
+      const long r = hoff + min(qs + lane, qe - 1);
+      g2lds4(p.lse + r, lds_lse[buf]);
+      g2lds4(p.delta + r, lds_dlt[buf]);
+    }
+  };
+
+  f32x16 dvt[4], dkt[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; dt++)
+#pragma unroll
+    for (int j = 0; j < 16; j++) dvt[dt][j] = dkt[dt][j] = 0.f;
+
+  int i = next_valid(0);
+  if (i < nchunks) {
+    int n1, qs, qe;
+    chunk_range(i, n1, qs, qe);
+    load_chunk(n1, qs, qe, 0);
+  }
+  wait_vm();
+  __syncthreads();
+  int buf = 0;
+  while (i < nchunks) {
+    int n1, qs, qe;
+    chunk_range(i, n1, qs, qe);
+    const int inext = next_valid(i + 1);
+    if (inext < nchunks) {
+      int n1b, qs2, qe2;
+      chunk_range(inext, n1b, qs2, qe2);
+      load_chunk(n1b, qs2, qe2, buf ^ 1);
+    }
+    const char* Qb = lds_q[buf];
+    const char* Db = lds_do[buf];
+
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int qt = 0; qt < 2; qt++)
+#pragma unroll
+      for (int j = 0; j < 16; j++) s[qt][j] = dp[qt][j] = 0.f;
+#pragma unroll
+    for (int ds = 0; ds < 8; ds++) {
+#pragma unroll
+      for (int qt = 0; qt < 2; qt++) {
+        const V8 aq = tile_read16<V8>(Qb, qt * 32 + l32, 2 * ds + h);
+        const V8 ad = tile_read16<V8>(Db, qt * 32 + l32, 2 * ds + h);
+        s[qt] = E::mfma32(aq, kreg[ds], s[qt]);
+        dp[qt] = E::mfma32(ad, vreg[ds], dp[qt]);
+      }
+    }
+    // rows of the accumulators are queries: element j of lane l is query
+    // qt*32 + 8*(j/4) + 4*h + j%4, column key l%32
+#pragma unroll
+    for (int qt = 0; qt < 2; qt++) {
+#pragma unroll
+      for (int j4 = 0; j4 < 4; j4++) {
+        const int rbase = qt * 32 + 8 * j4 + 4 * h;
+        const float4 lse4 = *reinterpret_cast<const float4*>(&lds_lse[buf][rbase]);
+        const float4 dl4 = *reinterpret_cast<const float4*>(&lds_dlt[buf][rbase]);
+        const float lv[4] = {lse4.x, lse4.y, lse4.z, lse4.w};
+        const float dv[4] = {dl4.x, dl4.y, dl4.z, dl4.w};
+#pragma unroll
+        for (int jj = 0; jj < 4; jj++) {
+          const int j = 4 * j4 + jj;
+          const int q = qs + rbase + jj;
+          const bool ok = key_ok && q < qe && (!p.causal || mykey <= q);
+          const float pv = ok ? fast_exp2(s[qt][j] * sl2 - lv[jj] * kLog2e) : 0.f;
+          s[qt][j] = pv;
+          dp[qt][j] = pv * (dp[qt][j] - dv[jj]);
+        }
+      }
+    }
+    // dV^T += dO^T P ; dK^T += Q^T dS  (16 queries per step)
+#pragma unroll
+    for (int k4 = 0; k4 < 4; k4++) {
+      V8 bp, bd;
+#pragma unroll
+      for (int e = 0; e < 8; e++) {
+        bp[e] = E::from_f32(s[k4 >> 1][8 * (k4 & 1) + e]);
+        bd[e] = E::from_f32(dp[k4 >> 1][8 * (k4 & 1) + e]);
+      }
+#pragma unroll
+      for (int dt = 0; dt < 4; dt++) {
+        const V8 ado = tile_read_tr<V8>(Db, k4, dt);
+        const V8 aq = tile_read_tr<V8>(Qb, k4, dt);
+        dvt[dt] = E::mfma32(ado, bp, dvt[dt]);
+        dkt[dt] = E::mfma32(aq, bd, dkt[dt]);
+      }
+    }
+    wait_vm();
+    __syncthreads();
+    buf ^= 1;
+    i = inext;
+  }
+
+  if (key_ok) {
+    T* dkrow = (T*)p.dk + kvoff + (long)mykey * kD;
+    T* dvrow = (T*)p.dv + kvoff + (long)mykey * kD;
+#pragma unroll
+    for (int dt = 0; dt < 4; dt++)
+#pragma unroll
+      for (int jj = 0; jj < 4; jj++) {
+        const int d0 = dt * 32 + 8 * jj + 4 * h;
+        *reinterpret_cast<uint2*>(dkrow + d0) =
+            pack4<E>(dkt[dt][4 * jj] * p.scale, dkt[dt][4 * jj + 1] * p.scale,
+                     dkt[dt][4 * jj + 2] * p.scale, dkt[dt][4 * jj + 3] * p.scale);
+        *reinterpret_cast<uint2*>(dvrow + d0) =
+            pack4<E>(dvt[dt][4 * jj], dvt[dt][4 * jj + 1], dvt[dt][4 * jj + 2], dvt[dt][4 * jj + 3]);
+      }
+  }
+}
+
+template <class E, int NW>
+static hipError_t launch_dq_t(const BsaParams& p, hipStream_t st) {
+  const int qsub = (p.bq + NW * 64 - 1) / (NW * 64);
+  const int n_items = p.B * p.N1 * p.QB * qsub;
+  if (n_items == 0) return hipSuccess;
+  hipLaunchKernelGGL((bsa_dq_kernel<E, NW>), dim3(8 * ((n_items + 7) / 8)), dim3(NW * 64), 0, st,
+                     p, qsub, n_items);
+  return hipGetLastError();
+}
+
+template <class E, int NW>
+static hipError_t launch_dkdv_t(const BsaParams& p, hipStream_t st) {
+  const int ksub = (p.bkv + NW * 32 - 1) / (NW * 32);
+  const int n_items = p.B * p.N2 * p.KB * ksub;
+  if (n_items == 0) return hipSuccess;
+  hipLaunchKernelGGL((bsa_dkdv_kernel<E, NW>), dim3(8 * ((n_items + 7) / 8)), dim3(NW * 64), 0,
+                     st, p, ksub, n_items);
+  return hipGetLastError();
+}
+
+template <class E>
+static hipError_t launch_bwd_t(const BsaParams& p, hipStream_t st, void* const* ev, int n_ev) {
+  hipError_t e = mark_event(ev, n_ev, 1, 0, st);
+  if (e == hipSuccess) e = p.bq <= 64 ? launch_dq_t<E, 1>(p, st) : launch_dq_t<E, 2>(p, st);
+  if (e == hipSuccess) e = mark_event(ev, n_ev, 1, 1, st);
+  if (e == hipSuccess) e = mark_event(ev, n_ev, 2, 0, st);
+  if (e == hipSuccess)
+    e = p.bkv <= 32 ? launch_dkdv_t<E, 1>(p, st)
+                    : (p.bkv <= 64 ? launch_dkdv_t<E, 2>(p, st) : launch_dkdv_t<E, 4>(p, st));
+  if (e == hipSuccess) e = mark_event(ev, n_ev, 2, 1, st);
+  return e;
+}
+
+hipError_t launch_bsa_bwd(const BsaParams& p, int fp16, hipStream_t st, void* const* ev, int n_ev) {
+  return fp16 ? launch_bwd_t<FP16>(p, st, ev, n_ev) : launch_bwd_t<BF16>(p, st, ev, n_ev);
+}
+
+}  // namespace tsa

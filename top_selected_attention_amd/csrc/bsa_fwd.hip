@@ -22,31 +22,7 @@ namespace tsa {
 
 constexpr int kD = 128;        // head dim (the page's constraint: headdim = 128)
 constexpr int kKC = 64;        // keys per chunk
-constexpr int kRowB = kD * 2;  // bytes per K/V row
-constexpr int kTileB = kKC * kRowB;  // bytes per staged K or V chunk
-
-// XOR swizzles of the 16 16-byte pieces of a 256-byte LDS row.  K pieces are
-// read 16 bytes at a time by 32 lanes on 32 rows (same piece): swz_k makes
-// 16 consecutive rows, and 8 rows x 2 adjacent pieces, hit distinct banks.
-// V is read by transpose reads covering 4 consecutive rows x 4 aligned
-// pieces: swz_v gives each of 4 consecutive rows a different 4-piece group.
-__device__ __forceinline__ int swz_k(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
-__device__ __forceinline__ int swz_v(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
-
-__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-template <class E>
-__device__ __forceinline__ typename E::V8 zero_v8() {
-  return as_v8<typename E::V8>(make_uint4(0, 0, 0, 0));
-}
-
-template <class E>
-__device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
-  typedef typename E::T T;
-  typedef T T4 __attribute__((ext_vector_type(4)));
-  T4 v = {E::from_f32(a), E::from_f32(b), E::from_f32(c), E::from_f32(d)};
-  return __builtin_bit_cast(uint2, v);
-}
+constexpr int kTileB = kKC * kD * 2;  // bytes per staged K or V chunk
 
 template <class E, int NW>
 __global__ __launch_bounds__(NW * 64) void bsa_fwd_kernel(BsaParams p, int qsub, int n_items) {
@@ -85,7 +61,7 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_kernel(BsaParams p, int qsub,
 #pragma unroll
     for (int ds = 0; ds < 8; ds++)
       qreg[qt][ds] = row < row_hi ? as_v8<V8>(ld16(qh + (long)row * kD + ds * 16 + 8 * h))
-                                  : zero_v8<E>();
+                                  : zero_v8<V8>();
   }
 
   const int tile_row = bn * p.QB + qb;
@@ -111,25 +87,13 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_kernel(BsaParams p, int qsub,
     return i;
   };
 
-  // Direct global -> LDS loads (no registers): one instruction moves 1 KB,
-  // four 256-byte rows, into consecutive LDS; the swizzled layout is made by
-  // choosing which 16-byte piece of global memory each lane fetches.  Keys
-  // past the chunk's end re-read its last key (finite data; their scores
-  // are masked, so P = 0 exactly there).
+  // Direct global -> LDS loads (no registers) into the swizzled layout.  Keys
+  // past the chunk's end re-read its last key (finite data; their scores are
+  // masked, so P = 0 exactly there).
   auto load_chunk = [&](int ks, int ke, int buf) {
-    const int sub = lane >> 4, pc = lane & 15;
-#pragma unroll
-    for (int u = 0; u < 16 / NW; u++) {
-      const int inst = wid * (16 / NW) + u;
-      const int r = inst * 4 + sub;
-      const long key = min(ks + r, ke - 1);
-      __builtin_amdgcn_global_load_lds(
-          (const void*)((const char*)kh + key * kRowB + ((pc ^ swz_k(r)) << 4)),
-          (__attribute__((address_space(3))) void*)(lds_k[buf] + inst * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(
-          (const void*)((const char*)vh + key * kRowB + ((pc ^ swz_v(r)) << 4)),
-          (__attribute__((address_space(3))) void*)(lds_v[buf] + inst * 1024), 16, 0, 0);
-    }
+    auto row_of = [&](int r) { return min(ks + r, ke - 1); };
+    stage_tile64<NW>((const char*)kh, lds_k[buf], row_of);
+    stage_tile64<NW>((const char*)vh, lds_v[buf], row_of);
   };
 
   float m[2] = {-INFINITY, -INFINITY};
@@ -173,9 +137,8 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_kernel(BsaParams p, int qsub,
         for (int j = 0; j < 16; j++) st[kt][qt][j] = 0.f;
 #pragma unroll
     for (int ds = 0; ds < 8; ds++) {
-      const int c = 2 * ds + h;
-      const V8 a0 = lds_read16<V8>(Kb + l32 * kRowB + ((c ^ swz_k(l32)) << 4));
-      const V8 a1 = lds_read16<V8>(Kb + (32 + l32) * kRowB + ((c ^ swz_k(32 + l32)) << 4));
+      const V8 a0 = tile_read16<V8>(Kb, l32, 2 * ds + h);
+      const V8 a1 = tile_read16<V8>(Kb, 32 + l32, 2 * ds + h);
       st[0][0] = E::mfma32(a0, qreg[0][ds], st[0][0]);
       st[0][1] = E::mfma32(a0, qreg[1][ds], st[0][1]);
       st[1][0] = E::mfma32(a1, qreg[0][ds], st[1][0]);
@@ -218,7 +181,6 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_kernel(BsaParams p, int qsub,
     }
 
     // O^T += V^T P^T, 16 keys per step.
-    const int g16 = lane >> 4, i16 = lane & 15;
 #pragma unroll
     for (int k4 = 0; k4 < 4; k4++) {
       V8 pb[2];
@@ -226,15 +188,9 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_kernel(BsaParams p, int qsub,
       for (int qt = 0; qt < 2; qt++)
 #pragma unroll
         for (int e = 0; e < 8; e++) pb[qt][e] = E::from_f32(st[k4 >> 1][qt][8 * (k4 & 1) + e]);
-      const int r0 = k4 * 16 + 4 * h + (i16 >> 2);
-      const int r1 = r0 + 8;
 #pragma unroll
       for (int dt = 0; dt < 4; dt++) {
-        // logical 16-byte piece of the row holding d = dt*32 + 16*(g16&1) + 4*(i16&3)
-        const int c = 4 * dt + 2 * (g16 & 1) + ((i16 & 3) >> 1);
-        const int b8 = 8 * (i16 & 1);
-        const V8 a = lds_read_tr_pair<V8>(Vb + r0 * kRowB + ((c ^ swz_v(r0)) << 4) + b8,
-                                          Vb + r1 * kRowB + ((c ^ swz_v(r1)) << 4) + b8);
+        const V8 a = tile_read_tr<V8>(Vb, k4, dt);
         o[0][dt] = E::mfma32(a, pb[0], o[0][dt]);
         o[1][dt] = E::mfma32(a, pb[1], o[1][dt]);
       }

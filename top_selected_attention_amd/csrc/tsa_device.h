@@ -94,6 +94,82 @@ __device__ __forceinline__ float wave_max_half_swap(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// XOR swizzle of the 16 16-byte pieces of a 256-byte LDS row (one K, V, Q or
+// dO row of 128 16-bit values).  Row r stores logical piece c at c ^ swz(r).
+// It keeps three read patterns free of bank conflicts: 16 consecutive rows
+// reading one piece (swz is a bijection on r mod 16); 8 rows reading two
+// adjacent pieces (swz(0..7) are all even); and transpose reads of 4
+// consecutive rows x 4 aligned pieces (rows of an aligned group of 4 differ
+// in bits 2-3 of swz).
+__device__ __forceinline__ int swz(int r) {
+  return ((r & 3) << 2) | (((r >> 2) & 1) << 1) | ((r >> 3) & 1);
+}
+
+// Waits for this wave's outstanding vector-memory loads (including direct
+// global -> LDS loads) to land.
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+template <typename V8>
+__device__ __forceinline__ V8 zero_v8() {
+  return __builtin_bit_cast(V8, make_uint4(0, 0, 0, 0));
+}
+
+// Four fp32 values rounded to the element type, packed into 8 bytes.
+template <class E>
+__device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
+  typedef typename E::T T;
+  typedef T T4 __attribute__((ext_vector_type(4)));
+  T4 v = {E::from_f32(a), E::from_f32(b), E::from_f32(c), E::from_f32(d)};
+  return __builtin_bit_cast(uint2, v);
+}
+
+// Direct global -> LDS copy of 16 bytes per lane: lane l's bytes land at
+// lds_base + 16*l.  lds_base must be the same for every lane of the wave.
+__device__ __forceinline__ void g2lds16(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+// Same with 4 bytes per lane (lane l's dword lands at lds_base + 4*l).
+__device__ __forceinline__ void g2lds4(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_base, 4, 0, 0);
+}
+
+// Stages rows [0, 64) of a 64 x 256-byte tile into swizzled LDS.  Row r of
+// the tile is global row row_of(r) (the caller clamps it into range).  The
+// NW waves of the workgroup split the 16 1-KB slices.
+template <int NW, class RowFn>
+__device__ __forceinline__ void stage_tile64(const char* gbase, char* lds_tile, RowFn row_of) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int sub = lane >> 4, pc = lane & 15;
+#pragma unroll
+  for (int u = 0; u < 16 / NW; u++) {
+    const int inst = wid * (16 / NW) + u;
+    const int r = inst * 4 + sub;
+    g2lds16(gbase + (long)row_of(r) * 256 + ((pc ^ swz(r)) << 4), lds_tile + inst * 1024);
+  }
+}
+
+// 16-byte read of logical piece c of row r from a swizzled tile.
+template <typename V8>
+__device__ __forceinline__ V8 tile_read16(const char* tile, int r, int c) {
+  return lds_read16<V8>(tile + r * 256 + ((c ^ swz(r)) << 4));
+}
+
+// k-major operand from a swizzled [rows][128] tile by transpose reads: lane
+// l gets column dt*32 + l%32 and rows k16*16 + {4h..4h+3, 8+4h..8+4h+3}
+// (h = l/32), the row order that a 32x32 accumulator's elements 8*k2..8*k2+7
+// have in their row index (8*(j/4) + 4*h + j%4).
+template <typename V8>
+__device__ __forceinline__ V8 tile_read_tr(const char* tile, int k16, int dt) {
+  const int lane = threadIdx.x & 63;
+  const int g16 = lane >> 4, i16 = lane & 15, h = lane >> 5;
+  const int r0 = k16 * 16 + 4 * h + (i16 >> 2);
+  const int r1 = r0 + 8;
+  const int c = 4 * dt + 2 * (g16 & 1) + ((i16 & 3) >> 1);
+  const int b8 = 8 * (i16 & 1);
+  return lds_read_tr_pair<V8>(tile + r0 * 256 + ((c ^ swz(r0)) << 4) + b8,
+                              tile + r1 * 256 + ((c ^ swz(r1)) << 4) + b8);
+}
+
 // XCD-aware workgroup -> work-item remap.  Workgroups are dispatched to the 8
 // XCDs round-robin (workgroup w runs on XCD w % 8).  Giving XCD x the
 // contiguous range [x * per, (x + 1) * per) of the work order keeps the work

@@ -6,6 +6,12 @@
 
 namespace tsa {
 
+// Records ev[2*stage + end] on st when stage < n (caller-provided timing events).
+inline hipError_t mark_event(void* const* ev, int n, int stage, int end, hipStream_t st) {
+  if (!ev || stage >= n) return hipSuccess;
+  return hipEventRecord((hipEvent_t)ev[2 * stage + end], st);
+}
+
 // ----- scans and lists -----------------------------------------------------
 int scan_sums_len(long n);
 hipError_t exclusive_scan(int* data, long n, int* sums, hipStream_t st);
@@ -51,7 +57,8 @@ struct BsaParams {
 };
 
 hipError_t launch_bsa_fwd(const BsaParams& p, int fp16, hipStream_t st);
-hipError_t launch_bsa_bwd(const BsaParams& p, int fp16, hipStream_t st);
+// ev / n_ev: caller timing events (stage 1 = dQ, stage 2 = dK/dV), may be null.
+hipError_t launch_bsa_bwd(const BsaParams& p, int fp16, hipStream_t st, void* const* ev, int n_ev);
 
 // ----- NSA selected attention ------------------------------------------------
 struct NsaParams {
@@ -75,7 +82,7 @@ struct NsaParams {
 };
 
 hipError_t launch_nsa_fwd(const NsaParams& p, int fp16, hipStream_t st);
-hipError_t launch_nsa_bwd(const NsaParams& p, int fp16, hipStream_t st);
+hipError_t launch_nsa_bwd(const NsaParams& p, int fp16, hipStream_t st, void* const* ev, int n_ev);
 
 // ----- sparse flash attention (paged decode) ----------------------------------
 struct SfaParams {
@@ -100,7 +107,8 @@ struct SfaParams {
 };
 
 int sfa_splits(const SfaParams& p);
-hipError_t launch_sfa_fwd(const SfaParams& p, int fp16, hipStream_t st);
+// stage 0 = split attention, stage 1 = combine
+hipError_t launch_sfa_fwd(const SfaParams& p, int fp16, hipStream_t st, void* const* ev, int n_ev);
 hipError_t launch_sfa_check(const SfaParams& p, hipStream_t st);
 
 }  // namespace tsa
