@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Throughput of the selected-block attention hot path on one MI355X.
+
+Default workload (``bsa_causal_8k``): block-sparse attention forward +
+backward, BNSD, B=2, N1=N2=16, S=8192, D=128, bf16, 128x128 blocks, causal
+block mask with the diagonal kept and every other block kept with p=0.25.
+One step = the whole path over one batch: mask compaction + forward
+attention, then compaction + dQ (with softmax_grad) + dK/dV.
+
+Prints ONE JSON line.  ``value`` is effective TFLOP/s counted on the
+selected blocks only (forward 4*rows*keys*D per selected block pair,
+backward 2.5x that), i.e. algorithmic FLOPs / measured step time.
+
+Other workloads (``--workload``): bsa_small, bsa_window_128k, nsa_varlen
+(forward + backward) and sfa_decode (forward; value in GB/s of algorithmic
+gathered bytes).
+"""
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="bsa_causal_8k",
+                    choices=["bsa_causal_8k", "bsa_small", "bsa_window_128k", "nsa_varlen",
+                             "sfa_decode"])
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle baseline sample (0 = skip)")
+    return ap.parse_args()
+
+
+def _events(n):
+    import torch
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for e in evs:
+        e.record()          # materialise the underlying hipEvent_t
+    return evs
+
+
+def _ev_array(evs):
+    arr = (ctypes.c_void_p * len(evs))(*[e.cuda_event for e in evs])
+    return arr
+
+
+def _src_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "top_selected_attention_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(kernel, src_files, units_per_launch):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when absent or when the kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    ent = t.get(kernel)
+    if not ent or ent.get("src_hash") != _src_hash(*src_files):
+        return None
+    return ent.get("bytes_per_launch")
+
+
+# ----------------------------------------------------------------------------
+# Block-sparse attention
+# ----------------------------------------------------------------------------
+
+CFG_OF = {"bsa_small": 1, "bsa_causal_8k": 2, "bsa_window_128k": 5}
+
+
+def _pair_flops(mask, bq, bkv, Sq, Skv, D=128):
+    """Sum over selected (Q block, KV block) pairs of rows * keys * D."""
+    QB, KB = mask.shape[2], mask.shape[3]
+    rows = np.minimum(bq, Sq - np.arange(QB) * bq)
+    keys = np.minimum(bkv, Skv - np.arange(KB) * bkv)
+    sel = (mask != 0).astype(np.float64)
+    return float(np.einsum("bnqk,q,k->", sel, rows, keys)) * D
+
+
+def bench_bsa(args):
+    import torch
+    import workloads as W
+    import top_selected_attention_amd as tsa
+
+    cfg = CFG_OF[args.workload]
+    w, q, k, v, do, mask, scale = W.bsa_inputs(cfg)
+    unit = _pair_flops(mask, w["bq"], w["bkv"], w["S"], w["S"])
+    fwd_flops, bwd_flops = 4.0 * unit, 10.0 * unit
+    dev = torch.device("cuda", 0)
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
+    md = torch.from_numpy(mask).to(dev)
+    plan = tsa.BsaPlan(qd, kd, vd, md, w["bq"], w["bkv"], scale, 0)
+    plan.set_dout(dod)
+
+    K, Wm = args.steps, args.warmup
+    for _ in range(Wm):
+        plan.fwd()
+        plan.bwd()
+    torch.cuda.synchronize()
+
+    # per-step stage events: fwd lists/attn, bwd lists/dq/dkdv
+    fev = [_events(4) for _ in range(K)]
+    bev = [_events(6) for _ in range(K)]
+    farr = [_ev_array(e) for e in fev]
+    barr = [_ev_array(e) for e in bev]
+    t_start, t_stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for i in range(K):
+        plan.fa.n_events, plan.fa.events = 2, ctypes.cast(farr[i], ctypes.POINTER(ctypes.c_void_p))
+        plan.ba.n_events, plan.ba.events = 3, ctypes.cast(barr[i], ctypes.POINTER(ctypes.c_void_p))
+        plan.fwd()
+        plan.bwd()
+    t_stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    plan.fa.n_events = plan.ba.n_events = 0
+
+    ms_step = wall * 1e3 / K
+    ms_ev = t_start.elapsed_time(t_stop) / K
+
+    def avg(evs, a, b):
+        return sum(e[a].elapsed_time(e[b]) for e in evs) / len(evs)
+
+    st = {
+        "fwd_lists": avg(fev, 0, 1), "fwd_attention": avg(fev, 2, 3),
+        "bwd_lists": avg(bev, 0, 1), "bwd_dq": avg(bev, 2, 3), "bwd_dkdv": avg(bev, 4, 5),
+    }
+    fwd_ms = st["fwd_lists"] + st["fwd_attention"]
+    bwd_ms = st["bwd_lists"] + st["bwd_dq"] + st["bwd_dkdv"]
+    # Per-kernel algorithmic FLOPs per launch, in units of rows*keys*D per
+    # selected pair: forward 2 GEMMs (S, PV) = 4; dQ kernel S, dP, dQ = 6;
+    # dK/dV kernel S, dP, dV, dK = 8 (the split recomputes S and dP).
+    kern = {
+        "bsa_fwd_kernel": (st["fwd_attention"], 4.0 * unit),
+        "bsa_dq_kernel": (st["bwd_dq"], 6.0 * unit),
+        "bsa_dkdv_kernel": (st["bwd_dkdv"], 8.0 * unit),
+    }
+    dom = max(kern, key=lambda n: kern[n][0])
+    dms, dfl = kern[dom]
+    achieved = dfl / (dms * 1e-3) / 1e12
+    files = {"bsa_fwd_kernel": ["bsa_fwd.hip", "tsa_device.h"],
+             "bsa_dq_kernel": ["bsa_bwd.hip", "tsa_device.h"],
+             "bsa_dkdv_kernel": ["bsa_bwd.hip", "tsa_device.h"]}[dom]
+    value = (fwd_flops + bwd_flops) / (ms_step * 1e-3) / 1e12
+    res = {
+        "metric": "effective TFLOP/s on selected blocks (fwd, bwd) and % of bf16 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": K, "warmup": Wm,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w["dtype"],
+        "data": "synthetic",
+        "config": {"workload": w["name"], "layout": "BNSD", "B": w["B"], "N1": w["N1"],
+                   "N2": w["N2"], "S": w["S"], "D": w["D"], "block": f"{w['bq']}x{w['bkv']}",
+                   "selected_pairs": int((mask != 0).sum()), "sparse_mode": 0},
+        "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "fwd_tflops": round(fwd_flops / (fwd_ms * 1e-3) / 1e12, 2),
+        "bwd_tflops": round(bwd_flops / (bwd_ms * 1e-3) / 1e12, 2),
+        "stage_ms": {k_: round(v_, 4) for k_, v_ in st.items()},
+        "ms_per_step_events": round(ms_ev, 4),
+        "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": _traffic(dom, files, None)},
+    }
+    return res, (w, q, k, v, do, mask, scale, unit)
+
+
+def cpu_baseline_bsa(ctx, seconds):
+    """Oracle (float64 numpy) fwd + bwd on a bounded sample of Q blocks."""
+    import oracle
+    w, q, k, v, do, mask, scale, _ = ctx
+    bq, bkv = w["bq"], w["bkv"]
+    qn, kn, vn, don = (t.float().numpy() for t in (q, k, v, do))
+    QB = mask.shape[2]
+    # longest-list-first order within head (0, 0), then the next heads
+    order = [(b, n, qb) for b in range(w["B"]) for n in range(w["N1"]) for qb in range(QB)]
+    done, flops = 0, 0.0
+    t0 = time.perf_counter()
+    for tile in order:
+        b, n, qb = tile
+        out, _ = oracle.bsa_fwd(qn, kn, vn, mask, bq, bkv, scale, 0, q_tiles=[tile])
+        oracle.bsa_bwd(qn, kn, vn, np.nan_to_num(out), don, mask, bq, bkv, scale, 0,
+                       q_tiles=[tile])
+        rows = min(bq, w["S"] - qb * bq)
+        keys = oracle.bsa_keys(mask[b, n, qb], bkv, w["S"]).size
+        flops += 14.0 * rows * keys * w["D"]
+        done += 1
+        if time.perf_counter() - t0 > seconds:
+            break
+    el = time.perf_counter() - t0
+    return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": _threads(),
+            "kind": "oracle",
+            "sample": f"{done} of {len(order)} Q blocks (fwd + bwd, float64) of {w['name']}, "
+                      f"{el:.1f} s"}
+
+
+def _threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        return 1
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the path shards by KV head / batch with no exchange, so per-GPU throughput "
+              "is the single-GPU figure", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.workload in CFG_OF:
+        res, ctx = bench_bsa(args)
+        if args.cpu_seconds > 0:
+            res["cpu_baseline"] = cpu_baseline_bsa(ctx, args.cpu_seconds)
+    else:
+        import bench_other
+        res = bench_other.run(args)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
