@@ -1,0 +1,485 @@
+// NSA selected attention ("aclnnNsaSelectedAttention", formulas section):
+//   selected_key/value = Gather(key/value, topk_indices),
+//   attention_out = Softmax(Mask(scale * query @ selected_key^T)) @ selected_value,
+// TND layout, sparseMode 0 or 2 (causal).  The backward applies the chain of
+// "aclnnBlockSparseAttentionGrad" (formula section) to the gathered keys;
+// the Gather's gradient adds each gathered row's dK/dV back to its source row,
+// which the dK/dV kernel does by walking, per KV block, the tokens that
+// selected it (reverse list) -- one owner per output row, no atomics.
+//
+// Forward and dQ: one wave per (token, KV head).  Its G query heads are the
+// query columns of a 32-wide MFMA tile (G <= 32; columns past G are padding:
+// the work is bound by gathering K/V, at ~16 FLOP per gathered byte, not by
+// MFMA).  The selected blocks are walked in 32-key chunks that the wave stages
+// into its own LDS region (direct global -> LDS loads) -- no workgroup
+// barrier; the other waves on the SIMD cover the load latency.
+#include "tsa_device.h"
+#include "tsa_internal.h"
+
+namespace tsa {
+
+namespace {
+constexpr int kD = 128;
+constexpr int kChunk = 32;                 // keys per chunk (forward / dQ)
+constexpr int kWaveTile = kChunk * kD * 2;  // bytes of one 32-row tile
+
+__device__ __forceinline__ int seq_of_dev(const int* cu, int nseq, int t) {
+  int lo = 0, hi = nseq - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Stages 32 rows of 256 bytes into a swizzled per-wave tile; rowptr(r) gives
+// the global address of row r (0 <= r < 32).
+template <class RowPtr>
+__device__ __forceinline__ void stage32_wave(char* tile, RowPtr rowptr) {
+  const int lane = threadIdx.x & 63;
+  const int sub = lane >> 4, pc = lane & 15;
+#pragma unroll
+  for (int inst = 0; inst < 8; inst++) {
+    const int r = inst * 4 + sub;
+    g2lds16(rowptr(r) + ((pc ^ swz(r)) << 4), tile + inst * 1024);
+  }
+}
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Forward
+// ---------------------------------------------------------------------------
+template <class E>
+__global__ __launch_bounds__(256) void nsa_fwd_kernel(NsaParams p, int n_items) {
+  typedef typename E::T T;
+  typedef typename E::V8 V8;
+  __shared__ __attribute__((aligned(1024))) char lds[4][2][kWaveTile];  // per wave: K, V
+
+  const int item = xcd_remap(blockIdx.x, n_items);
+  if (item < 0) return;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int l32 = lane & 31, h = lane >> 5;
+  // unit order: KV-head-major, tokens ascending (a sequence's K/V stay hot)
+  const int unit = item * 4 + wid;
+  if (unit >= p.T * p.N2) return;
+  const int n2 = unit / p.T, t = unit % p.T;
+  const NsaGeom& g = p.g;
+  const int b = seq_of_dev(g.cu_q, g.B, t);
+  const int pos = t - g.cu_q[b];
+  const int kv0 = g.cu_kv[b];
+  const int G = p.G;
+  char* Kt = lds[wid][0];
+  char* Vt = lds[wid][1];
+
+  const T* qrow = (const T*)p.q + ((long)t * p.N1 + n2 * G + l32) * kD;
+  const bool col_ok = l32 < G;
+  V8 qreg[8];
+#pragma unroll
+  for (int ds = 0; ds < 8; ds++)
+    qreg[ds] = col_ok ? as_v8<V8>(ld16(qrow + ds * 16 + 8 * h)) : zero_v8<V8>();
+
+  const long row = (long)t * p.N2 + n2;
+  const int e0 = p.row_ptr[row], e1 = p.row_ptr[row + 1];
+  const int sbs = g.sbs;
+  const int cpb = (sbs + kChunk - 1) / kChunk;
+  const int nchunks = (e1 - e0) * cpb;
+  const float sl2 = p.scale * kLog2e;
+  const long kstride = (long)p.N2 * kD * 2;  // bytes between consecutive tokens of one KV head
+  const char* kbase = (const char*)p.k + ((long)kv0 * p.N2 + n2) * kD * 2;
+  const char* vbase = (const char*)p.v + ((long)kv0 * p.N2 + n2) * kD * 2;
+
+  float m = -INFINITY, lsum = 0.f;
+  f32x16 o[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; dt++)
+#pragma unroll
+    for (int j = 0; j < 16; j++) o[dt][j] = 0.f;
+
+  for (int i = 0; i < nchunks; i++) {
+    const int blk = p.col[e0 + i / cpb];
+    const int ks = blk * sbs + (i % cpb) * kChunk;     // key position in the sequence
+    const int ke = min(ks + kChunk, (blk + 1) * sbs);
+    if (g.causal && ks > pos) continue;                // wholly after the token
+    auto rp_k = [&](int r) { return kbase + (long)min(ks + r, ke - 1) * kstride; };
+    auto rp_v = [&](int r) { return vbase + (long)min(ks + r, ke - 1) * kstride; };
+    stage32_wave(Kt, rp_k);
+    stage32_wave(Vt, rp_v);
+    wait_vm();
+
+    f32x16 st;
+#pragma unroll
+    for (int j = 0; j < 16; j++) st[j] = 0.f;
+#pragma unroll
+    for (int ds = 0; ds < 8; ds++)
+      st = E::mfma32(tile_read16<V8>(Kt, l32, 2 * ds + h), qreg[ds], st);
+
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+      const int key = ks + 8 * (j >> 2) + 4 * h + (j & 3);
+      const bool ok = key < ke && (!g.causal || key <= pos);
+      const float s = ok ? st[j] * sl2 : -INFINITY;
+      st[j] = s;
+      mx = fmaxf(mx, s);
+    }
+    mx = wave_max_half_swap(mx);
+    const float m_new = fmaxf(m, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(m - m_use);
+    m = m_new;
+    lsum *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < 4; dt++)
+#pragma unroll
+      for (int j = 0; j < 16; j++) o[dt][j] *= alpha;
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+      const float pv = fast_exp2(st[j] - m_use);
+      lsum += pv;
+      st[j] = pv;
+    }
+#pragma unroll
+    for (int k2 = 0; k2 < 2; k2++) {
+      V8 pb;
+#pragma unroll
+      for (int e = 0; e < 8; e++) pb[e] = E::from_f32(st[8 * k2 + e]);
+#pragma unroll
+      for (int dt = 0; dt < 4; dt++) o[dt] = E::mfma32(tile_read_tr<V8>(Vt, k2, dt), pb, o[dt]);
+    }
+  }
+
+  const float lt = lsum + __shfl_xor(lsum, 32);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  if (col_ok) {
+    const long orow = (long)t * p.N1 + n2 * G + l32;
+    T* op = (T*)p.out + orow * kD;
+#pragma unroll
+    for (int dt = 0; dt < 4; dt++)
+#pragma unroll
+      for (int jj = 0; jj < 4; jj++) {
+        const int d0 = dt * 32 + 8 * jj + 4 * h;
+        *reinterpret_cast<uint2*>(op + d0) = pack4<E>(o[dt][4 * jj] * inv, o[dt][4 * jj + 1] * inv,
+                                                      o[dt][4 * jj + 2] * inv, o[dt][4 * jj + 3] * inv);
+      }
+    if (h == 0) p.lse[orow] = lt > 0.f ? (m + log2f(lt)) * kLn2 : -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ (+ softmax_grad): one wave per (token, KV head)
+// ---------------------------------------------------------------------------
+template <class E>
+__global__ __launch_bounds__(256) void nsa_dq_kernel(NsaParams p, int n_items) {
+  typedef typename E::T T;
+  typedef typename E::V8 V8;
+  __shared__ __attribute__((aligned(1024))) char lds[4][2][kWaveTile];
+
+  const int item = xcd_remap(blockIdx.x, n_items);
+  if (item < 0) return;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int l32 = lane & 31, h = lane >> 5;
+  const int unit = item * 4 + wid;
+  if (unit >= p.T * p.N2) return;
+  const int n2 = unit / p.T, t = unit % p.T;
+  const NsaGeom& g = p.g;
+  const int b = seq_of_dev(g.cu_q, g.B, t);
+  const int pos = t - g.cu_q[b];
+  const int kv0 = g.cu_kv[b];
+  const int G = p.G;
+  char* Kt = lds[wid][0];
+  char* Vt = lds[wid][1];
+
+  const bool col_ok = l32 < G;
+  const long qr = (long)t * p.N1 + n2 * G + l32;
+  V8 qreg[8], doreg[8];
+  float acc = 0.f;
+#pragma unroll
+  for (int ds = 0; ds < 8; ds++) {
+    const long off = qr * kD + ds * 16 + 8 * h;
+    qreg[ds] = col_ok ? as_v8<V8>(ld16((const T*)p.q + off)) : zero_v8<V8>();
+    doreg[ds] = col_ok ? as_v8<V8>(ld16((const T*)p.dout + off)) : zero_v8<V8>();
+    const V8 ov = col_ok ? as_v8<V8>(ld16((const T*)p.o + off)) : zero_v8<V8>();
+#pragma unroll
+    for (int e = 0; e < 8; e++) acc += E::to_f32(doreg[ds][e]) * E::to_f32(ov[e]);
+  }
+  acc += __shfl_xor(acc, 32);
+  const float dlt = acc;
+  const float lse2 = col_ok ? p.lse[qr] * kLog2e : 0.f;
+  if (col_ok && h == 0) p.delta[qr] = dlt;
+
+  const long row = (long)t * p.N2 + n2;
+  const int e0 = p.row_ptr[row], e1 = p.row_ptr[row + 1];
+  const int sbs = g.sbs;
+  const int cpb = (sbs + kChunk - 1) / kChunk;
+  const int nchunks = (e1 - e0) * cpb;
+  const float sl2 = p.scale * kLog2e;
+  const long kstride = (long)p.N2 * kD * 2;
+  const char* kbase = (const char*)p.k + ((long)kv0 * p.N2 + n2) * kD * 2;
+  const char* vbase = (const char*)p.v + ((long)kv0 * p.N2 + n2) * kD * 2;
+
+  f32x16 dq[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; dt++)
+#pragma unroll
+    for (int j = 0; j < 16; j++) dq[dt][j] = 0.f;
+
+  for (int i = 0; i < nchunks; i++) {
+    const int blk = p.col[e0 + i / cpb];
+    const int ks = blk * sbs + (i % cpb) * kChunk;
+    const int ke = min(ks + kChunk, (blk + 1) * sbs);
+    if (g.causal && ks > pos) continue;
+    auto rp_k = [&](int r) { return kbase + (long)min(ks + r, ke - 1) * kstride; };
+    auto rp_v = [&](int r) { return vbase + (long)min(ks + r, ke - 1) * kstride; };
+    stage32_wave(Kt, rp_k);
+    stage32_wave(Vt, rp_v);
+    wait_vm();
+
+    f32x16 st, dpt;
+#pragma unroll
+    for (int j = 0; j < 16; j++) st[j] = dpt[j] = 0.f;
+#pragma unroll
+    for (int ds = 0; ds < 8; ds++) {
+      st = E::mfma32(tile_read16<V8>(Kt, l32, 2 * ds + h), qreg[ds], st);
+      dpt = E::mfma32(tile_read16<V8>(Vt, l32, 2 * ds + h), doreg[ds], dpt);
+    }
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+      const int key = ks + 8 * (j >> 2) + 4 * h + (j & 3);
+      const bool ok = col_ok && key < ke && (!g.causal || key <= pos);
+      const float pv = ok ? fast_exp2(st[j] * sl2 - lse2) : 0.f;
+      st[j] = pv * (dpt[j] - dlt);
+    }
+#pragma unroll
+    for (int k2 = 0; k2 < 2; k2++) {
+      V8 bs;
+#pragma unroll
+      for (int e = 0; e < 8; e++) bs[e] = E::from_f32(st[8 * k2 + e]);
+#pragma unroll
+      for (int dt = 0; dt < 4; dt++) dq[dt] = E::mfma32(tile_read_tr<V8>(Kt, k2, dt), bs, dq[dt]);
+    }
+  }
+
+  if (col_ok) {
+    T* dp = (T*)p.out + qr * kD;
+#pragma unroll
+    for (int dt = 0; dt < 4; dt++)
+#pragma unroll
+      for (int jj = 0; jj < 4; jj++) {
+        const int d0 = dt * 32 + 8 * jj + 4 * h;
+        *reinterpret_cast<uint2*>(dp + d0) =
+            pack4<E>(dq[dt][4 * jj] * p.scale, dq[dt][4 * jj + 1] * p.scale,
+                     dq[dt][4 * jj + 2] * p.scale, dq[dt][4 * jj + 3] * p.scale);
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK / dV: one workgroup per (KV head, selected block); each wave owns 32 of
+// the block's keys.  The tokens that selected the block are walked in chunks
+// of 64 query rows (64 / G tokens x G heads): S = Q K^T, dP = dO V^T,
+// P = exp2(S*scale*log2e - LSE2), dS = P (dP - softmax_grad),
+// dV^T += dO^T P, dK^T += Q^T dS.
+// ---------------------------------------------------------------------------
+template <class E, int NW>
+__global__ __launch_bounds__(NW * 64) void nsa_dkdv_kernel(NsaParams p, int n_items) {
+  typedef typename E::T T;
+  typedef typename E::V8 V8;
+  constexpr int kTileB = 64 * kD * 2;
+  __shared__ __attribute__((aligned(1024))) char lds_q[2][kTileB];
+  __shared__ __attribute__((aligned(1024))) char lds_do[2][kTileB];
+  __shared__ float lds_lse[2][64];
+  __shared__ float lds_dlt[2][64];
+  __shared__ int lds_pos[2][64];
+
+  const int item = xcd_remap(blockIdx.x, n_items);
+  if (item < 0) return;
+  const NsaGeom& g = p.g;
+  const int n2 = item / g.NB, gb = item % g.NB;
+  const int b = seq_of_dev(g.blk_off, g.B, gb);
+  const int blk = gb - g.blk_off[b];
+  const int kv0 = g.cu_kv[b], q0 = g.cu_q[b];
+  const int skv = g.cu_kv[b + 1] - kv0;
+  const int sbs = g.sbs;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int l32 = lane & 31, h = lane >> 5;
+  const int key_lo = blk * sbs;
+  const int key_hi = min((blk + 1) * sbs, skv);
+  const int mykey = key_lo + wid * 32 + l32;  // position in the sequence
+  const bool key_ok = mykey < key_hi;
+  const int G = p.G;
+  const int tpc = 64 / G;                     // tokens per 64-row chunk
+
+  const long krow = ((long)(kv0 + mykey) * p.N2 + n2) * kD;
+  V8 kreg[8], vreg[8];
+#pragma unroll
+  for (int ds = 0; ds < 8; ds++) {
+    const long off = krow + ds * 16 + 8 * h;
+    kreg[ds] = key_ok ? as_v8<V8>(ld16((const T*)p.k + off)) : zero_v8<V8>();
+    vreg[ds] = key_ok ? as_v8<V8>(ld16((const T*)p.v + off)) : zero_v8<V8>();
+  }
+
+  const int rr = n2 * g.NB + gb;
+  const int e0 = p.rev_ptr[rr], e1 = p.rev_ptr[rr + 1];
+  const int nchunks = (e1 - e0 + tpc - 1) / tpc;
+  const float sl2 = p.scale * kLog2e;
+
+  // chunk row r -> (token entry e0 + c*tpc + r/G, head r%G); rows past the
+  // chunk's tokens re-read its last valid row and are masked
+  auto row_of = [&](int c, int r) {
+    const int nt = min(tpc, e1 - e0 - c * tpc);
+    const int tk = min(r / G, nt - 1);
+    const int gg = (r / G < nt && r < tpc * G) ? r % G : G - 1;
+    const int t = p.rev[e0 + c * tpc + tk];
+    return (long)t * p.N1 + n2 * G + gg;
+  };
+  auto load_chunk = [&](int c, int buf) {
+    const int sub = lane >> 4, pc = lane & 15;
+#pragma unroll
+    for (int u = 0; u < 16 / NW; u++) {
+      const int inst = wid * (16 / NW) + u;
+      const int r = inst * 4 + sub;
+      const long qrw = row_of(c, r);
+      g2lds16((const char*)((const T*)p.q + qrw * kD) + ((pc ^ swz(r)) << 4), lds_q[buf] + inst * 1024);
+      g2lds16((const char*)((const T*)p.dout + qrw * kD) + ((pc ^ swz(r)) << 4),
+              lds_do[buf] + inst * 1024);
+    }
+    if (wid == 0) {
+      const long qrw = row_of(c, lane);
+      g2lds4(p.lse + qrw, lds_lse[buf]);
+      g2lds4(p.delta + qrw, lds_dlt[buf]);
+      const int nt = min(tpc, e1 - e0 - c * tpc);
+      const bool valid = lane / G < nt && lane < tpc * G;
+      // position of the row's token, or -1 for padding rows (always masked)
+      lds_pos[buf][lane] = valid ? p.rev[e0 + c * tpc + lane / G] - q0 : -1;
+    }
+  };
+
+  f32x16 dvt[4], dkt[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; dt++)
+#pragma unroll
+    for (int j = 0; j < 16; j++) dvt[dt][j] = dkt[dt][j] = 0.f;
+
+  if (nchunks > 0) load_chunk(0, 0);
+  wait_vm();
+  __syncthreads();
+  int buf = 0;
+  for (int c = 0; c < nchunks; c++) {
+    if (c + 1 < nchunks) load_chunk(c + 1, buf ^ 1);
+    const char* Qb = lds_q[buf];
+    const char* Db = lds_do[buf];
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int qt = 0; qt < 2; qt++)
+#pragma unroll
+      for (int j = 0; j < 16; j++) s[qt][j] = dp[qt][j] = 0.f;
+#pragma unroll
+    for (int ds = 0; ds < 8; ds++)
+#pragma unroll
+      for (int qt = 0; qt < 2; qt++) {
+        s[qt] = E::mfma32(tile_read16<V8>(Qb, qt * 32 + l32, 2 * ds + h), kreg[ds], s[qt]);
+        dp[qt] = E::mfma32(tile_read16<V8>(Db, qt * 32 + l32, 2 * ds + h), vreg[ds], dp[qt]);
+      }
+#pragma unroll
+    for (int qt = 0; qt < 2; qt++)
+#pragma unroll
+      for (int j4 = 0; j4 < 4; j4++) {
+        const int rbase = qt * 32 + 8 * j4 + 4 * h;
+        const float4 lse4 = *reinterpret_cast<const float4*>(&lds_lse[buf][rbase]);
+        const float4 dl4 = *reinterpret_cast<const float4*>(&lds_dlt[buf][rbase]);
+        const int4 ps4 = *reinterpret_cast<const int4*>(&lds_pos[buf][rbase]);
+        const float lv[4] = {lse4.x, lse4.y, lse4.z, lse4.w};
+        const float dv[4] = {dl4.x, dl4.y, dl4.z, dl4.w};
+        const int pv4[4] = {ps4.x, ps4.y, ps4.z, ps4.w};
+#pragma unroll
+        for (int jj = 0; jj < 4; jj++) {
+          const int j = 4 * j4 + jj;
+          const bool ok = key_ok && pv4[jj] >= 0 && (!g.causal || mykey <= pv4[jj]);
+          const float pr = ok ? fast_exp2(s[qt][j] * sl2 - lv[jj] * kLog2e) : 0.f;
+          s[qt][j] = pr;
+          dp[qt][j] = pr * (dp[qt][j] - dv[jj]);
+        }
+      }
+#pragma unroll
+    for (int k4 = 0; k4 < 4; k4++) {
+      V8 bp, bd;
+#pragma unroll
+      for (int e = 0; e < 8; e++) {
+        bp[e] = E::from_f32(s[k4 >> 1][8 * (k4 & 1) + e]);
+        bd[e] = E::from_f32(dp[k4 >> 1][8 * (k4 & 1) + e]);
+      }
+#pragma unroll
+      for (int dt = 0; dt < 4; dt++) {
+        dvt[dt] = E::mfma32(tile_read_tr<V8>(Db, k4, dt), bp, dvt[dt]);
+        dkt[dt] = E::mfma32(tile_read_tr<V8>(Qb, k4, dt), bd, dkt[dt]);
+      }
+    }
+    wait_vm();
+    __syncthreads();
+    buf ^= 1;
+  }
+
+  if (key_ok) {
+    T* dkr = (T*)p.dk + krow;
+    T* dvr = (T*)p.dv + krow;
+#pragma unroll
+    for (int dt = 0; dt < 4; dt++)
+#pragma unroll
+      for (int jj = 0; jj < 4; jj++) {
+        const int d0 = dt * 32 + 8 * jj + 4 * h;
+        *reinterpret_cast<uint2*>(dkr + d0) =
+            pack4<E>(dkt[dt][4 * jj] * p.scale, dkt[dt][4 * jj + 1] * p.scale,
+                     dkt[dt][4 * jj + 2] * p.scale, dkt[dt][4 * jj + 3] * p.scale);
+        *reinterpret_cast<uint2*>(dvr + d0) =
+            pack4<E>(dvt[dt][4 * jj], dvt[dt][4 * jj + 1], dvt[dt][4 * jj + 2], dvt[dt][4 * jj + 3]);
+      }
+  }
+}
+
+template <class E>
+static hipError_t fwd_t(const NsaParams& p, hipStream_t st) {
+  const int units = p.T * p.N2;
+  const int n_items = (units + 3) / 4;
+  if (n_items == 0) return hipSuccess;
+  hipLaunchKernelGGL((nsa_fwd_kernel<E>), dim3(8 * ((n_items + 7) / 8)), dim3(256), 0, st, p,
+                     n_items);
+  return hipGetLastError();
+}
+
+hipError_t launch_nsa_fwd(const NsaParams& p, int fp16, hipStream_t st) {
+  return fp16 ? fwd_t<FP16>(p, st) : fwd_t<BF16>(p, st);
+}
+
+template <class E>
+static hipError_t bwd_t(const NsaParams& p, hipStream_t st, void* const* ev, int n_ev) {
+  hipError_t e = mark_event(ev, n_ev, 1, 0, st);
+  const int units = p.T * p.N2;
+  const int n_items = (units + 3) / 4;
+  if (e == hipSuccess && n_items > 0) {
+    hipLaunchKernelGGL((nsa_dq_kernel<E>), dim3(8 * ((n_items + 7) / 8)), dim3(256), 0, st, p,
+                       n_items);
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess) e = mark_event(ev, n_ev, 1, 1, st);
+  if (e == hipSuccess) e = mark_event(ev, n_ev, 2, 0, st);
+  const int nb = p.N2 * p.g.NB;
+  if (e == hipSuccess && nb > 0) {
+    const int nw = (p.g.sbs + 31) / 32;  // 1..4 waves, 32 keys each
+    const dim3 grid(8 * ((nb + 7) / 8));
+    if (nw <= 1)
+      hipLaunchKernelGGL((nsa_dkdv_kernel<E, 1>), grid, dim3(64), 0, st, p, nb);
+    else if (nw <= 2)
+      hipLaunchKernelGGL((nsa_dkdv_kernel<E, 2>), grid, dim3(128), 0, st, p, nb);
+    else
+      hipLaunchKernelGGL((nsa_dkdv_kernel<E, 4>), grid, dim3(256), 0, st, p, nb);
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess) e = mark_event(ev, n_ev, 2, 1, st);
+  return e;
+}
+
+hipError_t launch_nsa_bwd(const NsaParams& p, int fp16, hipStream_t st, void* const* ev, int n_ev) {
+  return fp16 ? bwd_t<FP16>(p, st, ev, n_ev) : bwd_t<BF16>(p, st, ev, n_ev);
+}
+
+}  // namespace tsa
