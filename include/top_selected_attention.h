@@ -293,7 +293,8 @@ TSA_API int nsa_compact(const nsa_select_fwd_args* args, int32_t* row_ptr, int32
  * q [B, Sq, N1, D], q_rope [B, Sq, N1, Dr] (BSND);
  * key_cache [num_pages, page_size, N2, D], key_rope_cache [num_pages,
  *   page_size, N2, Dr], value_cache [num_pages, page_size, N2, Dv] (PA_ND);
- *   value_cache may equal key_cache (shared KV: V is the key row).
+ *   value_cache must equal key_cache (shared KV: V is the key row; a
+ *   separate value cache returns TSA_ERR_UNSUPPORTED).
  * block_table int32 DEVICE [B, max_pages]: physical page of logical page p.
  * kv_lens int32 DEVICE [B]: active KV tokens of each sequence.
  * topk_indices int32 DEVICE [B, Sq, N2, topk]: selected sparse-block ids

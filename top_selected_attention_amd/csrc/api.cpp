@@ -318,6 +318,9 @@ int check_sfa(const sfa_paged_fwd_args* a) {
       (!a->q || !a->q_rope || !a->key_cache || !a->key_rope_cache || !a->value_cache ||
        !a->block_table || !a->kv_lens || !a->topk_indices || !a->out))
     return TSA_ERR_NULL;
+  // Shared KV ("SparseAttnSharedkvMetadata": sharedkv): the value row is the
+  // key row; a separate value cache is not built.
+  if (a->value_cache != a->key_cache) return TSA_ERR_UNSUPPORTED;
   return TSA_OK;
 }
 

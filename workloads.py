@@ -114,10 +114,11 @@ def nsa_topk_causal(rng, seqlens, n2, sbs, sbc):
 # ----------------------------------------------------------------------------
 
 def sfa_paged(rng, B, Sq, kv_len, page, topk):
-    """block_table int32 [B, kv_len/page] = a random permutation of B*kv_len/page
-    physical pages; kv_lens int32 [B]; topk int32 [B, Sq, 1, topk] distinct
-    sorted positions uniform over [0, kv_len - Sq + s] (rightDownCausal)."""
-    pages = kv_len // page
+    """block_table int32 [B, ceil(kv_len/page)] = a random permutation of the
+    B*ceil(kv_len/page) physical pages; kv_lens int32 [B]; topk int32
+    [B, Sq, 1, topk] distinct sorted positions uniform over [0, kv_len - Sq + s]
+    (rightDownCausal)."""
+    pages = -(-kv_len // page)
     block_table = rng.permutation(B * pages).reshape(B, pages).astype(np.int32)
     kv_lens = np.full((B,), kv_len, dtype=np.int32)
     idx = np.empty((B, Sq, 1, topk), dtype=np.int32)
@@ -197,7 +198,7 @@ def sfa_inputs(B=32, Sq=4, N1=64, D=512, Dr=64, page=128, kv_len=65536, topk=204
     The value cache is the key cache (shared KV)."""
     rng = np.random.default_rng(1000 + seed_base // 10)
     block_table, kv_lens, idx = sfa_paged(rng, B, Sq, kv_len, page, topk)
-    P = B * (kv_len // page) + extra_pages
+    P = B * (-(-kv_len // page)) + extra_pages
     q = normal((B, Sq, N1, D), seed_base + 1, dtype)
     q_rope = normal((B, Sq, N1, Dr), seed_base + 2, dtype)
     kc = normal((P, page, 1, D), seed_base + 3, dtype)
