@@ -117,15 +117,16 @@ def sfa_paged(rng, B, Sq, kv_len, page, topk):
     """block_table int32 [B, ceil(kv_len/page)] = a random permutation of the
     B*ceil(kv_len/page) physical pages; kv_lens int32 [B]; topk int32
     [B, Sq, 1, topk] distinct sorted positions uniform over [0, kv_len - Sq + s]
-    (rightDownCausal)."""
+    (rightDownCausal), -1 in the slots left when fewer positions exist."""
     pages = -(-kv_len // page)
     block_table = rng.permutation(B * pages).reshape(B, pages).astype(np.int32)
     kv_lens = np.full((B,), kv_len, dtype=np.int32)
-    idx = np.empty((B, Sq, 1, topk), dtype=np.int32)
+    idx = np.full((B, Sq, 1, topk), -1, dtype=np.int32)   # -1 = empty slot
     for b in range(B):
         for s in range(Sq):
             hi = kv_len - Sq + s + 1
-            idx[b, s, 0] = np.sort(rng.choice(hi, size=min(topk, hi), replace=False))
+            n = min(topk, hi)
+            idx[b, s, 0, :n] = np.sort(rng.choice(hi, size=n, replace=False))
     return block_table, kv_lens, idx
 
 
