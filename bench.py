@@ -221,6 +221,202 @@ def cpu_baseline_bsa(ctx, seconds):
                       f"{el:.1f} s"}
 
 
+# ----------------------------------------------------------------------------
+# NSA selected attention
+# ----------------------------------------------------------------------------
+
+def bench_nsa(args):
+    import torch
+    import workloads as W
+    import top_selected_attention_amd as tsa
+
+    w = W.nsa_workload()
+    cu, q, k, v, do, topk = W.nsa_inputs()
+    sbs, G, D = w["sbs"], w["N1"] // w["N2"], w["D"]
+    scale = 1.0 / math.sqrt(D)
+    # effective (token, KV head, block) triples: blocks not wholly after the token
+    pos = np.arange(int(cu[-1])) - np.repeat(cu[:-1], np.diff(cu))
+    triples = int((topk.astype(np.int64) * sbs <= pos[:, None, None]).sum())
+    unit = float(triples) * G * sbs * D
+    fwd_flops, bwd_flops = 4.0 * unit, 10.0 * unit
+    dev = torch.device("cuda", 0)
+    plan = tsa.NsaPlan(q.to(dev), k.to(dev), v.to(dev), torch.from_numpy(topk).to(dev), cu, cu,
+                       sbs, scale, w["sparse_mode"])
+    plan.set_dout(do.to(dev))
+    st, ms_step, K = _timed_steps(args, plan, 2, 3)
+    fwd_ms = st[0] + st[1]
+    bwd_ms = st[2] + st[3] + st[4]
+    kern = {"nsa_fwd_kernel": (st[1], 4.0 * unit), "nsa_dq_kernel": (st[3], 6.0 * unit),
+            "nsa_dkdv_kernel": (st[4], 8.0 * unit)}
+    dom = max(kern, key=lambda n: kern[n][0])
+    dms, dfl = kern[dom]
+    achieved = dfl / (dms * 1e-3) / 1e12
+    gathered = triples * sbs * D * 2 * 2      # K and V rows brought to the CUs per pass
+    value = (fwd_flops + bwd_flops) / (ms_step * 1e-3) / 1e12
+    res = {
+        "metric": "effective TFLOP/s on selected blocks (fwd, bwd) and % of bf16 MFMA peak",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w["dtype"], "data": "synthetic",
+        "config": {"workload": w["name"], "layout": "TND", "seqlens": w["seqlens"],
+                   "N1": w["N1"], "N2": w["N2"], "D": D, "sbs": sbs, "sbc": w["sbc"],
+                   "sparse_mode": w["sparse_mode"], "effective_triples": triples},
+        "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "fwd_tflops": round(fwd_flops / (fwd_ms * 1e-3) / 1e12, 2),
+        "bwd_tflops": round(bwd_flops / (bwd_ms * 1e-3) / 1e12, 2),
+        "stage_ms": dict(zip(["fwd_lists", "fwd_attention", "bwd_lists", "bwd_dq", "bwd_dkdv"],
+                             [round(x, 4) for x in st])),
+        "fwd_gathered_GBps": round(gathered / (st[1] * 1e-3) / 1e9, 1),
+        "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": _traffic(dom, ["nsa.hip", "tsa_device.h"], None)},
+    }
+    return res, (w, cu, q, k, v, do, topk, scale, sbs, G, D)
+
+
+def cpu_baseline_nsa(ctx, seconds):
+    import oracle
+    w, cu, q, k, v, do, topk, scale, sbs, G, D = ctx
+    qn, kn, vn, don = (t.float().numpy() for t in (q, k, v, do))
+    T = int(cu[-1])
+    done, flops = 0, 0.0
+    t0 = time.perf_counter()
+    step = 97                                   # tokens spread over all sequences
+    for t in list(range(0, T, step)):
+        out, _ = oracle.nsa_fwd(qn, kn, vn, topk, cu, cu, sbs, scale, 2, tokens=[t])
+        oracle.nsa_bwd(qn, kn, vn, np.nan_to_num(out), don, topk, cu, cu, sbs, scale, 2,
+                       tokens=[t])
+        b = int(np.searchsorted(cu, t, side="right") - 1)
+        p_ = t - int(cu[b])
+        eff = int((topk[t].astype(np.int64) * sbs <= p_).sum())
+        flops += 14.0 * eff * G * sbs * D
+        done += 1
+        if time.perf_counter() - t0 > seconds:
+            break
+    el = time.perf_counter() - t0
+    return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": _threads(),
+            "kind": "oracle",
+            "sample": f"{done} tokens (every {step}th, both KV heads, fwd + bwd, float64) of "
+                      f"{w['name']}, {el:.1f} s"}
+
+
+# ----------------------------------------------------------------------------
+# Paged sparse flash attention decode
+# ----------------------------------------------------------------------------
+
+def _sfa_bytes(idx, kv_lens, B, Sq, N1, D, Dr, Dv):
+    """Algorithmic HBM bytes: per sequence the union of its tokens' selected rows
+    (key row + rope row; the value row is the key row), plus Q, q_rope, O, LSE,
+    indices and the page-table entries read."""
+    rows = 0
+    for b in range(B):
+        sel = idx[b].reshape(-1)
+        sel = sel[(sel >= 0) & (sel < kv_lens[b])]
+        rows += np.unique(sel).size
+    per_tok = N1 * (D + Dr) * 2 + N1 * Dv * 2 + N1 * 4 + idx.shape[-1] * 4 * 2
+    return rows * (D + Dr) * 2 + B * Sq * per_tok
+
+
+def bench_sfa(args):
+    import torch
+    import workloads as W
+    import top_selected_attention_amd as tsa
+
+    w = W.sfa_workload()
+    q, qr, kc, krc, bt, kv_lens, idx = W.sfa_inputs()
+    scale = 1.0 / math.sqrt(w["D"] + w["Dr"])
+    dev = torch.device("cuda", 0)
+    kcd = kc.to(dev)
+    plan = tsa.SfaPlan(q.to(dev), qr.to(dev), kcd, krc.to(dev), kcd, torch.from_numpy(bt).to(dev),
+                       torch.from_numpy(kv_lens).to(dev), torch.from_numpy(idx).to(dev), scale, 3)
+    nbytes = _sfa_bytes(idx, kv_lens, w["B"], w["Sq"], w["N1"], w["D"], w["Dr"], w["D"])
+    flops = 2.0 * w["B"] * w["Sq"] * w["N1"] * w["topk"] * ((w["D"] + w["Dr"]) + w["D"])
+    K = args.steps
+    for _ in range(args.warmup):
+        plan.fwd()
+    torch.cuda.synchronize()
+    evs = [_events(4) for _ in range(K)]
+    arrs = [_ev_array(e) for e in evs]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(K):
+        plan.a.n_events, plan.a.events = 2, ctypes.cast(arrs[i], ctypes.POINTER(ctypes.c_void_p))
+        plan.fwd()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - wall0) * 1e3 / K
+    plan.a.n_events = 0
+    split_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / K
+    comb_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / K
+    gbs = nbytes / (ms_step * 1e-3) / 1e9
+    kgbs = nbytes / (split_ms * 1e-3) / 1e9
+    res = {
+        "metric": "GB/s of algorithmic HBM bytes (paged top-k gather) and % of HBM peak",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w["dtype"], "data": "synthetic",
+        "config": {"workload": w["name"], "B": w["B"], "Sq": w["Sq"], "N1": w["N1"], "N2": 1,
+                   "D": w["D"], "Dr": w["Dr"], "page": w["page"], "kv_len": w["kv_len"],
+                   "topk": w["topk"]},
+        "pct_of_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
+        "effective_tflops": round(flops / (ms_step * 1e-3) / 1e12, 2),
+        "stage_ms": {"split_attention": round(split_ms, 4), "combine": round(comb_ms, 4)},
+        "algorithmic_bytes": int(nbytes),
+        "roofline": {"kernel": "sfa_split_kernel", "bound": "hbm", "achieved": round(kgbs, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(kgbs / PEAK_HBM_GBS, 4),
+                     "traffic": _traffic("sfa_split_kernel", ["sfa.hip", "tsa_device.h"], None)},
+    }
+    return res, (w, q, qr, kc, krc, bt, kv_lens, idx, scale, nbytes)
+
+
+def cpu_baseline_sfa(ctx, seconds):
+    import oracle
+    w, q, qr, kc, krc, bt, kv_lens, idx, scale, nbytes = ctx
+    qn, qrn = q.float().numpy(), qr.float().numpy()
+    kcn, krcn = kc.float().numpy(), krc.float().numpy()
+    tokens = [(b, s) for b in range(w["B"]) for s in range(w["Sq"])]
+    done = 0
+    t0 = time.perf_counter()
+    for tkn in tokens:
+        oracle.sfa_fwd(qn, qrn, kcn, krcn, kcn, bt, kv_lens, idx, scale, 3, tokens=[tkn])
+        done += 1
+        if time.perf_counter() - t0 > seconds:
+            break
+    el = time.perf_counter() - t0
+    per_tok = nbytes / len(tokens)
+    return {"value": round(per_tok * done / el / 1e9, 4), "unit": "GB/s", "cores": _threads(),
+            "kind": "oracle",
+            "sample": f"{done} of {len(tokens)} decode tokens (float64) of {w['name']}, {el:.1f} s"}
+
+
+def _timed_steps(args, plan, nf, nb):
+    """Warm up, then time K fwd+bwd steps with per-stage events; returns
+    (stage ms list [fwd stages..., bwd stages...], wall ms per step, K)."""
+    import torch
+    K = args.steps
+    for _ in range(args.warmup):
+        plan.fwd()
+        plan.bwd()
+    torch.cuda.synchronize()
+    fev = [_events(2 * nf) for _ in range(K)]
+    bev = [_events(2 * nb) for _ in range(K)]
+    farr = [_ev_array(e) for e in fev]
+    barr = [_ev_array(e) for e in bev]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(K):
+        plan.fa.n_events, plan.fa.events = nf, ctypes.cast(farr[i], ctypes.POINTER(ctypes.c_void_p))
+        plan.ba.n_events, plan.ba.events = nb, ctypes.cast(barr[i], ctypes.POINTER(ctypes.c_void_p))
+        plan.fwd()
+        plan.bwd()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - wall0) * 1e3 / K
+    plan.fa.n_events = plan.ba.n_events = 0
+    st = [sum(e[2 * j].elapsed_time(e[2 * j + 1]) for e in fev) / K for j in range(nf)]
+    st += [sum(e[2 * j].elapsed_time(e[2 * j + 1]) for e in bev) / K for j in range(nb)]
+    return st, ms_step, K
+
+
 def _threads():
     try:
         from threadpoolctl import threadpool_info
@@ -244,9 +440,14 @@ def main():
         res, ctx = bench_bsa(args)
         if args.cpu_seconds > 0:
             res["cpu_baseline"] = cpu_baseline_bsa(ctx, args.cpu_seconds)
+    elif args.workload == "nsa_varlen":
+        res, ctx = bench_nsa(args)
+        if args.cpu_seconds > 0:
+            res["cpu_baseline"] = cpu_baseline_nsa(ctx, args.cpu_seconds)
     else:
-        import bench_other
-        res = bench_other.run(args)
+        res, ctx = bench_sfa(args)
+        if args.cpu_seconds > 0:
+            res["cpu_baseline"] = cpu_baseline_sfa(ctx, args.cpu_seconds)
     print(json.dumps(res), flush=True)
 
 

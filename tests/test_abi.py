@@ -1,0 +1,179 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, its
+struct sizes match the binding, and host-side validation rejects bad
+arguments before touching the device (no kernels are launched here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "top_selected_attention.h")
+
+
+@pytest.fixture(scope="module")
+def tsa():
+    import top_selected_attention_amd as t
+    return t
+
+
+def _declared():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"TSA_API\s+[\w\s\*]+?\b(\w+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported(tsa):
+    names = _declared()
+    assert len(names) >= 17
+    for n in names:
+        assert hasattr(tsa.lib, n), n
+    assert set(names) == set(tsa._abi.EXPORTS)
+
+
+def test_struct_sizes_match(tsa):
+    for i, s in enumerate(tsa._abi.ARG_STRUCTS):
+        assert tsa.lib.tsa_args_sizeof(i) == ctypes.sizeof(s)
+    assert tsa.lib.tsa_args_sizeof(99) == 0
+
+
+def test_status_strings(tsa):
+    for code in range(7):
+        assert tsa.lib.tsa_status_string(code)
+    assert b"unknown" in tsa.lib.tsa_status_string(42)
+
+
+def _bsa(tsa, **kw):
+    a = dict(dtype=0, q_layout=0, kv_layout=0, B=2, N1=4, N2=2, Sq=1000, Skv=900, D=128,
+             block_q=128, block_kv=64, sparse_mode=0, scale=0.088, validate=0, block_mask=8,
+             q=8, k=8, v=8, out=8, lse=8)
+    a.update(kw)
+    return tsa._abi.BsaFwdArgs(**a)
+
+
+def _size(tsa, fn, args):
+    n = ctypes.c_size_t()
+    return fn(ctypes.byref(args), ctypes.byref(n)), n.value
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), 0),
+    (dict(D=64), 2),                       # headdim must be 128
+    (dict(N1=3, N2=2), 2),                 # N1 % N2 != 0
+    (dict(q_layout=1), 3),                 # TND: documented, not built
+    (dict(q_layout=7), 2),
+    (dict(sparse_mode=1), 2),
+    (dict(dtype=5), 2),
+    (dict(block_q=0), 2),
+    (dict(q=0), 1),
+    (dict(block_mask=0), 1),
+    (dict(scale=float("nan")), 2),
+    (dict(Sq=0), 0),                       # empty query: valid
+])
+def test_bsa_validation(tsa, kw, status):
+    s, n = _size(tsa, tsa.lib.bsa_fwd_workspace_size, _bsa(tsa, **kw))
+    assert s == status
+    if s == 0:
+        assert n > 0
+
+
+def test_bsa_workspace_too_small_is_rejected_before_launch(tsa):
+    a = _bsa(tsa)
+    s, n = _size(tsa, tsa.lib.bsa_fwd_workspace_size, a)
+    assert s == 0
+    assert tsa.lib.bsa_fwd(ctypes.byref(a), ctypes.c_void_p(8), n - 1, None) == 4
+    assert tsa.lib.bsa_fwd(ctypes.byref(a), None, n, None) == 4
+    assert tsa.lib.bsa_fwd(None, None, 0, None) == 1
+
+
+def test_bsa_bwd_validation(tsa):
+    a = tsa._abi.BsaBwdArgs(dtype=0, q_layout=0, kv_layout=0, B=1, N1=2, N2=2, Sq=256, Skv=256,
+                            D=128, block_q=128, block_kv=128, sparse_mode=2, scale=0.1,
+                            block_mask=8, q=8, k=8, v=8, out=8, dout=8, lse=8, dq=8, dk=8, dv=8)
+    assert _size(tsa, tsa.lib.bsa_bwd_workspace_size, a)[0] == 0
+    a.dk = 0
+    assert _size(tsa, tsa.lib.bsa_bwd_workspace_size, a)[0] == 1
+
+
+def _nsa(tsa, seqlens=(256, 512), **kw):
+    cu = (ctypes.c_int32 * (len(seqlens) + 1))(0, *[sum(seqlens[:i + 1]) for i in range(len(seqlens))])
+    T = sum(seqlens)
+    a = dict(dtype=0, layout=1, B=len(seqlens), T=T, Tk=T, N1=32, N2=2, D=128, Dv=128,
+             cu_seqlens_q=ctypes.cast(cu, ctypes.POINTER(ctypes.c_int32)),
+             cu_seqlens_kv=ctypes.cast(cu, ctypes.POINTER(ctypes.c_int32)),
+             sbs=64, sbc=4, sparse_mode=2, scale=0.088, validate=0, topk=8, q=8, k=8, v=8,
+             out=8, lse=8)
+    a.update(kw)
+    args = tsa._abi.NsaFwdArgs(**a)
+    args._keep = cu
+    return args
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), 0),
+    (dict(layout=0), 3),                   # BNSD: only TND is supported
+    (dict(sbs=8), 2),                      # block size a multiple of 16
+    (dict(sbs=144), 2),                    # at most 128
+    (dict(sbc=0), 2),
+    (dict(sbc=129), 2),
+    (dict(sbs=128, sbc=65), 2),            # product above 8K
+    (dict(sparse_mode=1), 2),
+    (dict(N1=31), 2),                      # N1 % N2
+    (dict(N1=128, N2=2), 2),               # G = 64 > 32
+    (dict(Dv=64), 3),                      # Dv != D not built
+    (dict(T=100), 2),                      # cu_seqlens_q[B] != T
+    (dict(topk=0), 1),
+])
+def test_nsa_validation(tsa, kw, status):
+    assert _size(tsa, tsa.lib.nsa_select_fwd_workspace_size, _nsa(tsa, **kw))[0] == status
+
+
+def test_nsa_sequence_constraints(tsa):
+    # a KV sequence shorter than sbs * sbc, and one not a multiple of sbs
+    assert _size(tsa, tsa.lib.nsa_select_fwd_workspace_size, _nsa(tsa, seqlens=(192, 512)))[0] == 2
+    assert _size(tsa, tsa.lib.nsa_select_fwd_workspace_size, _nsa(tsa, seqlens=(300, 512)))[0] == 2
+    nb = ctypes.c_int32()
+    assert tsa.lib.nsa_compact_blocks_total(ctypes.byref(_nsa(tsa)), ctypes.byref(nb)) == 0
+    assert nb.value == (256 + 512) // 64
+
+
+def _sfa(tsa, **kw):
+    a = dict(dtype=0, q_layout=2, B=32, Sq=4, N1=64, N2=1, D=512, Dr=64, Dv=512,
+             num_pages=16384, page_size=128, max_pages=512, topk=2048, sparse_block_size=1,
+             sparse_mode=3, scale=1 / 24, validate=0, q=8, q_rope=8, key_cache=16,
+             key_rope_cache=8, value_cache=16, block_table=8, kv_lens=8, topk_indices=8, out=8,
+             lse=8)
+    a.update(kw)
+    return tsa._abi.SfaArgs(**a)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), 0),
+    (dict(N1=48), 2),                      # N1 a power of two
+    (dict(N1=256), 2),
+    (dict(N2=2, N1=64), 3),                # one KV head only
+    (dict(D=256), 2),
+    (dict(Dr=32), 2),
+    (dict(page_size=8), 2),
+    (dict(page_size=2048), 2),
+    (dict(sparse_block_size=3), 2),        # must divide the page size
+    (dict(sparse_mode=2), 2),
+    (dict(value_cache=24), 3),             # separate value cache: not built
+    (dict(q_layout=1), 3),
+    (dict(kv_lens=0), 1),
+])
+def test_sfa_validation(tsa, kw, status):
+    assert _size(tsa, tsa.lib.sfa_paged_fwd_workspace_size, _sfa(tsa, **kw))[0] == status
+
+
+def test_import_fails_loudly_without_library(tmp_path):
+    """The binding has no fallback: without libtsa.so the import raises."""
+    import shutil
+    import subprocess
+    import sys
+    pkg = tmp_path / "top_selected_attention_amd"
+    shutil.copytree(os.path.join(ROOT, "top_selected_attention_amd"), pkg,
+                    ignore=shutil.ignore_patterns("*.so", "_build", "__pycache__"))
+    r = subprocess.run([sys.executable, "-c", "import top_selected_attention_amd"],
+                       cwd=tmp_path, capture_output=True, text=True)
+    assert r.returncode != 0 and "libtsa.so" in r.stderr
