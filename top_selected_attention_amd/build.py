@@ -25,6 +25,9 @@ COMMON = [
     f"--offload-arch={ARCH}",
     # packed fp32 VALU forms stay off: the compiler's own float code only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in VGPRs: the kernels touch them with VALU (softmax,
+    # scaling), and AGPR-resident accumulators cost a move per element
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", CSRC, "-I", INCLUDE,
 ]
 

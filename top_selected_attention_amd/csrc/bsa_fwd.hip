@@ -3,7 +3,7 @@
 // natural-log LSE of each row.
 //
 // One workgroup per (b, n1, Q block) slice of up to 128 query rows; each wave
-// owns 64 query rows.  The Q block's selected KV blocks are walked in 64-key
+// owns 32 query rows.  The Q block's selected KV blocks are walked in 64-key
 // chunks: K and V of a chunk are one contiguous slab of BNSD memory (the
 // gather is a base-pointer jump), moved by direct global -> LDS loads into a
 // double buffer while the previous chunk computes.
@@ -28,7 +28,7 @@ template <class E, int NW>
 __global__ __launch_bounds__(NW * 64) void bsa_fwd_kernel(BsaParams p, int qsub, int n_items) {
   typedef typename E::T T;
   typedef typename E::V8 V8;
-  constexpr int NT = NW * 64;
+  constexpr int NR = NW * 32;  // query rows per workgroup (32 per wave)
   __shared__ __attribute__((aligned(1024))) char lds_k[2][kTileB];
   __shared__ __attribute__((aligned(1024))) char lds_v[2][kTileB];
 
@@ -42,27 +42,25 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_kernel(BsaParams p, int qsub,
   const int bn = t1 / p.QB;  // b * N1 + n1
   const int n1 = bn % p.N1, b = bn / p.N1;
   const int n2 = n1 / p.G;
-  const int row_lo = qb * p.bq + qs * NT;
+  const int row_lo = qb * p.bq + qs * NR;
   const int row_hi = min((qb + 1) * p.bq, p.Sq);
   if (row_lo >= row_hi) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5;
-  const int wrow0 = row_lo + wid * 64;
+  const int wrow0 = row_lo + wid * 32;
+  const int qrow = wrow0 + l32;  // this lane's query column
 
   const T* qh = (const T*)p.q + (long)bn * p.Sq * kD;
   const T* kh = (const T*)p.k + ((long)b * p.N2 + n2) * p.Skv * kD;
   const T* vh = (const T*)p.v + ((long)b * p.N2 + n2) * p.Skv * kD;
 
-  V8 qreg[2][8];
+  // Q^T as the B operand of S^T = K Q^T: lane holds query l32, d = 16*ds + 8*h .. +7
+  V8 qreg[8];
 #pragma unroll
-  for (int qt = 0; qt < 2; qt++) {
-    const int row = wrow0 + qt * 32 + l32;
-#pragma unroll
-    for (int ds = 0; ds < 8; ds++)
-      qreg[qt][ds] = row < row_hi ? as_v8<V8>(ld16(qh + (long)row * kD + ds * 16 + 8 * h))
-                                  : zero_v8<V8>();
-  }
+  for (int ds = 0; ds < 8; ds++)
+    qreg[ds] = qrow < row_hi ? as_v8<V8>(ld16(qh + (long)qrow * kD + ds * 16 + 8 * h))
+                             : zero_v8<V8>();
 
   const int tile_row = bn * p.QB + qb;
   const int e0 = p.row_ptr[tile_row], e1 = p.row_ptr[tile_row + 1];
@@ -86,7 +84,6 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_kernel(BsaParams p, int qsub,
     }
     return i;
   };
-
   // Direct global -> LDS loads (no registers) into the swizzled layout.  Keys
   // past the chunk's end re-read its last key (finite data; their scores are
   // masked, so P = 0 exactly there).
@@ -96,15 +93,16 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_kernel(BsaParams p, int qsub,
     stage_tile64<NW>((const char*)vh, lds_v[buf], row_of);
   };
 
-  float m[2] = {-INFINITY, -INFINITY};
-  float lsum[2] = {0.f, 0.f};
-  f32x16 o[2][4];
+  // Online softmax state of this lane's query, base 2.  The reference m only
+  // moves when a chunk's max exceeds it by more than kLazy (so P <= 2^kLazy);
+  // O and l are rescaled only then, by a wave-uniform branch.
+  constexpr float kLazy = 8.f;
+  float m = -INFINITY, lsum = 0.f;
+  f32x16 o[4];
 #pragma unroll
-  for (int qt = 0; qt < 2; qt++)
+  for (int dt = 0; dt < 4; dt++)
 #pragma unroll
-    for (int dt = 0; dt < 4; dt++)
-#pragma unroll
-      for (int j = 0; j < 16; j++) o[qt][dt][j] = 0.f;
+    for (int j = 0; j < 16; j++) o[dt][j] = 0.f;
 
   int i = next_valid(0);
   if (i < nchunks) {
@@ -127,74 +125,61 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_kernel(BsaParams p, int qsub,
     const char* Kb = lds_k[buf];
     const char* Vb = lds_v[buf];
 
-    // S^T = K Q^T over the chunk: 64 keys x 64 queries per wave.
-    f32x16 st[2][2];
+    // S^T = K Q^T: 64 keys x 32 queries (two 32x32 tiles)
+    f32x16 st[2];
 #pragma unroll
     for (int kt = 0; kt < 2; kt++)
 #pragma unroll
-      for (int qt = 0; qt < 2; qt++)
-#pragma unroll
-        for (int j = 0; j < 16; j++) st[kt][qt][j] = 0.f;
+      for (int j = 0; j < 16; j++) st[kt][j] = 0.f;
 #pragma unroll
     for (int ds = 0; ds < 8; ds++) {
-      const V8 a0 = tile_read16<V8>(Kb, l32, 2 * ds + h);
-      const V8 a1 = tile_read16<V8>(Kb, 32 + l32, 2 * ds + h);
-      st[0][0] = E::mfma32(a0, qreg[0][ds], st[0][0]);
-      st[0][1] = E::mfma32(a0, qreg[1][ds], st[0][1]);
-      st[1][0] = E::mfma32(a1, qreg[0][ds], st[1][0]);
-      st[1][1] = E::mfma32(a1, qreg[1][ds], st[1][1]);
+      st[0] = E::mfma32(tile_read16<V8>(Kb, l32, 2 * ds + h), qreg[ds], st[0]);
+      st[1] = E::mfma32(tile_read16<V8>(Kb, 32 + l32, 2 * ds + h), qreg[ds], st[1]);
     }
-
-    // Online softmax, base 2.  Element j of a lane is key 8*(j/4) + 4*h + j%4.
-#pragma unroll
-    for (int qt = 0; qt < 2; qt++) {
-      const int qrow = wrow0 + qt * 32 + l32;
-      float mx = -INFINITY;
+    // element j of tile kt is key ks + kt*32 + 8*(j/4) + 4*h + j%4; a whole
+    // chunk at or below every row of this wave needs no mask
+    const bool full = (ke - ks == kKC) && (!p.causal || ke - 1 <= wrow0);
+    if (!full) {
 #pragma unroll
       for (int kt = 0; kt < 2; kt++)
 #pragma unroll
         for (int j = 0; j < 16; j++) {
           const int key = ks + kt * 32 + 8 * (j >> 2) + 4 * h + (j & 3);
           const bool ok = key < ke && (!p.causal || key <= qrow);
-          const float s = ok ? st[kt][qt][j] * sl2 : -INFINITY;
-          st[kt][qt][j] = s;
-          mx = fmaxf(mx, s);
+          st[kt][j] = ok ? st[kt][j] : -INFINITY;
         }
-      mx = wave_max_half_swap(mx);
-      const float m_new = fmaxf(m[qt], mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = fast_exp2(m[qt] - m_use);
-      m[qt] = m_new;
-      lsum[qt] *= alpha;
+    }
+    float mx = fmaxf(st[0][0], st[1][0]);
+#pragma unroll
+    for (int j = 1; j < 16; j++) mx = fmaxf(mx, fmaxf(st[0][j], st[1][j]));
+    mx = wave_max_half_swap(mx) * sl2;
+    if (__builtin_amdgcn_ballot_w64(mx > m + kLazy)) {
+      const float m_new = fmaxf(m, mx);
+      const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m - m_new);
+      m = m_new;
+      lsum *= alpha;
 #pragma unroll
       for (int dt = 0; dt < 4; dt++)
 #pragma unroll
-        for (int j = 0; j < 16; j++) o[qt][dt][j] *= alpha;
-#pragma unroll
-      for (int kt = 0; kt < 2; kt++)
-#pragma unroll
-        for (int j = 0; j < 16; j++) {
-          const float pv = fast_exp2(st[kt][qt][j] - m_use);
-          lsum[qt] += pv;
-          st[kt][qt][j] = pv;
-        }
+        for (int j = 0; j < 16; j++) o[dt][j] *= alpha;
     }
-
-    // O^T += V^T P^T, 16 keys per step.
+    // P^T = exp2(S^T * scale*log2e - m), fed back as the B operand of PV
+    const float mneg = m == -INFINITY ? 0.f : -m;
+    V8 pb[4];
 #pragma unroll
-    for (int k4 = 0; k4 < 4; k4++) {
-      V8 pb[2];
+    for (int kt = 0; kt < 2; kt++)
 #pragma unroll
-      for (int qt = 0; qt < 2; qt++)
-#pragma unroll
-        for (int e = 0; e < 8; e++) pb[qt][e] = E::from_f32(st[k4 >> 1][qt][8 * (k4 & 1) + e]);
-#pragma unroll
-      for (int dt = 0; dt < 4; dt++) {
-        const V8 a = tile_read_tr<V8>(Vb, k4, dt);
-        o[0][dt] = E::mfma32(a, pb[0], o[0][dt]);
-        o[1][dt] = E::mfma32(a, pb[1], o[1][dt]);
+      for (int j = 0; j < 16; j++) {
+        const float pv = fast_exp2(__builtin_fmaf(st[kt][j], sl2, mneg));
+        lsum += pv;
+        pb[2 * kt + (j >> 3)][j & 7] = E::from_f32(pv);
       }
-    }
+    // O^T += V^T P^T, 16 keys per step
+#pragma unroll
+    for (int k4 = 0; k4 < 4; k4++)
+#pragma unroll
+      for (int dt = 0; dt < 4; dt++)
+        o[dt] = E::mfma32(tile_read_tr<V8>(Vb, k4, dt), pb[k4], o[dt]);
 
     wait_vm();
     __syncthreads();
@@ -203,41 +188,43 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_kernel(BsaParams p, int qsub,
   }
 
   // Epilogue: O = O^T / l, LSE = (m + log2 l) * ln 2.
+  const float lt = lsum + __shfl_xor(lsum, 32);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  if (qrow < row_hi) {
+    T* orow = (T*)p.out + ((long)bn * p.Sq + qrow) * kD;
 #pragma unroll
-  for (int qt = 0; qt < 2; qt++) {
-    const float lt = lsum[qt] + __shfl_xor(lsum[qt], 32);
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    const int row = wrow0 + qt * 32 + l32;
-    if (row < row_hi) {
-      T* orow = (T*)p.out + ((long)bn * p.Sq + row) * kD;
+    for (int dt = 0; dt < 4; dt++)
 #pragma unroll
-      for (int dt = 0; dt < 4; dt++)
-#pragma unroll
-        for (int jj = 0; jj < 4; jj++) {
-          const int d0 = dt * 32 + 8 * jj + 4 * h;
-          *reinterpret_cast<uint2*>(orow + d0) =
-              pack4<E>(o[qt][dt][4 * jj] * inv, o[qt][dt][4 * jj + 1] * inv,
-                       o[qt][dt][4 * jj + 2] * inv, o[qt][dt][4 * jj + 3] * inv);
-        }
-      if (h == 0) p.lse[(long)bn * p.Sq + row] = lt > 0.f ? (m[qt] + log2f(lt)) * kLn2 : -INFINITY;
-    }
+      for (int jj = 0; jj < 4; jj++) {
+        const int d0 = dt * 32 + 8 * jj + 4 * h;
+        *reinterpret_cast<uint2*>(orow + d0) =
+            pack4<E>(o[dt][4 * jj] * inv, o[dt][4 * jj + 1] * inv, o[dt][4 * jj + 2] * inv,
+                     o[dt][4 * jj + 3] * inv);
+      }
+    if (h == 0) p.lse[(long)bn * p.Sq + qrow] = lt > 0.f ? (m + log2f(lt)) * kLn2 : -INFINITY;
   }
 }
 
 template <class E, int NW>
 static hipError_t launch_fwd_t(const BsaParams& p, hipStream_t st) {
-  const int qsub = (p.bq + NW * 64 - 1) / (NW * 64);
+  const int qsub = (p.bq + NW * 32 - 1) / (NW * 32);
   const int n_items = p.B * p.N1 * p.QB * qsub;
   const int grid = 8 * ((n_items + 7) / 8);
   hipLaunchKernelGGL((bsa_fwd_kernel<E, NW>), dim3(grid), dim3(NW * 64), 0, st, p, qsub, n_items);
   return hipGetLastError();
 }
 
+template <class E>
+static hipError_t launch_fwd_e(const BsaParams& p, hipStream_t st) {
+  // 32 query rows per wave: up to 4 waves cover a 128-row Q block slice
+  if (p.bq <= 32) return launch_fwd_t<E, 1>(p, st);
+  if (p.bq <= 64) return launch_fwd_t<E, 2>(p, st);
+  return launch_fwd_t<E, 4>(p, st);
+}
+
 hipError_t launch_bsa_fwd(const BsaParams& p, int fp16, hipStream_t st) {
   if (p.B * p.N1 * p.QB == 0) return hipSuccess;
-  const bool one = p.bq <= 64;
-  if (fp16) return one ? launch_fwd_t<FP16, 1>(p, st) : launch_fwd_t<FP16, 2>(p, st);
-  return one ? launch_fwd_t<BF16, 1>(p, st) : launch_fwd_t<BF16, 2>(p, st);
+  return fp16 ? launch_fwd_e<FP16>(p, st) : launch_fwd_e<BF16>(p, st);
 }
 
 }  // namespace tsa
