@@ -28,14 +28,15 @@ constexpr int kTileB = 64 * kD * 2;  // one 64-row chunk of a [rows][128] 16-bit
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// dQ (+ softmax_grad).  Each wave owns 64 query rows: two 32-query columns of
-// the transposed products S^T = K Q^T and dP^T = V dO^T, and dQ^T += K^T dS^T.
+// dQ (+ softmax_grad).  Each wave owns 32 query rows: per 32-key half of a
+// chunk it forms S^T = K Q^T and dP^T = V dO^T, dS^T = P^T (dP^T - D), and
+// accumulates dQ^T += K^T dS^T.
 // ---------------------------------------------------------------------------
 template <class E, int NW>
 __global__ __launch_bounds__(NW * 64) void bsa_dq_kernel(BsaParams p, int qsub, int n_items) {
   typedef typename E::T T;
   typedef typename E::V8 V8;
-  constexpr int NT = NW * 64;
+  constexpr int NR = NW * 32;
   __shared__ __attribute__((aligned(1024))) char lds_k[2][kTileB];
   __shared__ __attribute__((aligned(1024))) char lds_v[2][kTileB];
 
@@ -47,43 +48,42 @@ __global__ __launch_bounds__(NW * 64) void bsa_dq_kernel(BsaParams p, int qsub, 
   const int bn = t1 / p.QB;
   const int n1 = bn % p.N1, b = bn / p.N1;
   const int n2 = n1 / p.G;
-  const int row_lo = qb * p.bq + qs * NT;
+  const int row_lo = qb * p.bq + qs * NR;
   const int row_hi = min((qb + 1) * p.bq, p.Sq);
   if (row_lo >= row_hi) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5;
-  const int wrow0 = row_lo + wid * 64;
+  const int wrow0 = row_lo + wid * 32;
+  const int qrow = wrow0 + l32;
+  const bool row_ok = qrow < row_hi;
 
   const long qoff = (long)bn * p.Sq * kD;
-  const T* qh = (const T*)p.q + qoff;
-  const T* oh = (const T*)p.o + qoff;
-  const T* doh = (const T*)p.dout + qoff;
   const T* kh = (const T*)p.k + ((long)b * p.N2 + n2) * p.Skv * kD;
   const T* vh = (const T*)p.v + ((long)b * p.N2 + n2) * p.Skv * kD;
 
-  // Stationary operands: Q^T and dO^T columns of this lane's two queries, and
-  // per-query softmax_grad (computed here from O and dO) and LSE (base 2).
-  V8 qreg[2][8], doreg[2][8];
-  float dlt[2], lse2[2];
-#pragma unroll
-  for (int qt = 0; qt < 2; qt++) {
-    const int row = wrow0 + qt * 32 + l32;
-    const bool ok = row < row_hi;
+  // Stationary operands of this lane's query: Q^T and dO^T columns;
+  // softmax_grad D = rowsum(dO * O) formed here and stored; LSE (base 2).
+  V8 qreg[8], doreg[8];
+  float dlt, lse2;
+  {
+    const T* qr = (const T*)p.q + qoff + (long)qrow * kD;
+    const T* orr = (const T*)p.o + qoff + (long)qrow * kD;
+    const T* dor = (const T*)p.dout + qoff + (long)qrow * kD;
     float acc = 0.f;
 #pragma unroll
     for (int ds = 0; ds < 8; ds++) {
-      const long off = (long)row * kD + ds * 16 + 8 * h;
-      qreg[qt][ds] = ok ? as_v8<V8>(ld16(qh + off)) : zero_v8<V8>();
-      doreg[qt][ds] = ok ? as_v8<V8>(ld16(doh + off)) : zero_v8<V8>();
-      const V8 ov = ok ? as_v8<V8>(ld16(oh + off)) : zero_v8<V8>();
+      const int off = ds * 16 + 8 * h;
+      qreg[ds] = row_ok ? as_v8<V8>(ld16(qr + off)) : zero_v8<V8>();
+      doreg[ds] = row_ok ? as_v8<V8>(ld16(dor + off)) : zero_v8<V8>();
+      const V8 ov = row_ok ? as_v8<V8>(ld16(orr + off)) : zero_v8<V8>();
 #pragma unroll
-      for (int e = 0; e < 8; e++) acc += E::to_f32(doreg[qt][ds][e]) * E::to_f32(ov[e]);
+      for (int e = 0; e < 8; e++) acc += E::to_f32(doreg[ds][e]) * E::to_f32(ov[e]);
     }
     acc += __shfl_xor(acc, 32);
-    dlt[qt] = acc;
-    lse2[qt] = ok ? p.lse[(long)bn * p.Sq + row] * kLog2e : 0.f;
-    if (ok && h == 0) p.delta[(long)bn * p.Sq + row] = acc;
+    dlt = acc;
+    lse2 = row_ok ? p.lse[(long)bn * p.Sq + qrow] * kLog2e : 0.f;
+    if (row_ok && h == 0) p.delta[(long)bn * p.Sq + qrow] = acc;
   }
 
   const int e0 = p.row_ptr[bn * p.QB + qb], e1 = p.row_ptr[bn * p.QB + qb + 1];
@@ -110,13 +110,12 @@ __global__ __launch_bounds__(NW * 64) void bsa_dq_kernel(BsaParams p, int qsub, 
     stage_tile64<NW>((const char*)vh, lds_v[buf], row_of);
   };
 
-  f32x16 dq[2][4];
+  f32x16 dq[4];
 #pragma unroll
-  for (int qt = 0; qt < 2; qt++)
+  for (int dt = 0; dt < 4; dt++)
 #pragma unroll
-    for (int dt = 0; dt < 4; dt++)
-#pragma unroll
-      for (int j = 0; j < 16; j++) dq[qt][dt][j] = 0.f;
+    for (int j = 0; j < 16; j++) dq[dt][j] = 0.f;
+  const float lneg = -lse2;
 
   int i = next_valid(0);
   if (i < nchunks) {
@@ -138,49 +137,36 @@ __global__ __launch_bounds__(NW * 64) void bsa_dq_kernel(BsaParams p, int qsub, 
     }
     const char* Kb = lds_k[buf];
     const char* Vb = lds_v[buf];
+    const bool full = (ke - ks == 64) && wrow0 + 32 <= row_hi && (!p.causal || ke - 1 <= wrow0);
 #pragma unroll
     for (int kt = 0; kt < 2; kt++) {
-      f32x16 st[2], dpt[2];
+      f32x16 st, dpt;
 #pragma unroll
-      for (int qt = 0; qt < 2; qt++)
-#pragma unroll
-        for (int j = 0; j < 16; j++) st[qt][j] = dpt[qt][j] = 0.f;
+      for (int j = 0; j < 16; j++) st[j] = dpt[j] = 0.f;
 #pragma unroll
       for (int ds = 0; ds < 8; ds++) {
-        const V8 ak = tile_read16<V8>(Kb, kt * 32 + l32, 2 * ds + h);
-        const V8 av = tile_read16<V8>(Vb, kt * 32 + l32, 2 * ds + h);
-        st[0] = E::mfma32(ak, qreg[0][ds], st[0]);
-        st[1] = E::mfma32(ak, qreg[1][ds], st[1]);
-        dpt[0] = E::mfma32(av, doreg[0][ds], dpt[0]);
-        dpt[1] = E::mfma32(av, doreg[1][ds], dpt[1]);
+        st = E::mfma32(tile_read16<V8>(Kb, kt * 32 + l32, 2 * ds + h), qreg[ds], st);
+        dpt = E::mfma32(tile_read16<V8>(Vb, kt * 32 + l32, 2 * ds + h), doreg[ds], dpt);
       }
-      // dS^T = P^T * (dP^T - softmax_grad), P^T = exp2(S^T * scale*log2e - LSE2)
+      // dS^T = P^T * (dP^T - D), P^T = exp2(S^T * scale*log2e - LSE2);
+      // element j is key ks + kt*32 + 8*(j/4) + 4*h + j%4
+      V8 bs[2];
 #pragma unroll
-      for (int qt = 0; qt < 2; qt++) {
-        const int qrow = wrow0 + qt * 32 + l32;
-#pragma unroll
-        for (int j = 0; j < 16; j++) {
+      for (int j = 0; j < 16; j++) {
+        float pv = fast_exp2(__builtin_fmaf(st[j], sl2, lneg));
+        if (!full) {
           const int key = ks + kt * 32 + 8 * (j >> 2) + 4 * h + (j & 3);
-          const bool ok = key < ke && qrow < row_hi && (!p.causal || key <= qrow);
-          const float pv = ok ? fast_exp2(st[qt][j] * sl2 - lse2[qt]) : 0.f;
-          st[qt][j] = pv * (dpt[qt][j] - dlt[qt]);
+          const bool ok = key < ke && row_ok && (!p.causal || key <= qrow);
+          pv = ok ? pv : 0.f;
         }
+        bs[j >> 3][j & 7] = E::from_f32(pv * (dpt[j] - dlt));
       }
       // dQ^T += K^T dS^T over the tile's 32 keys (two 16-key steps)
 #pragma unroll
-      for (int k2 = 0; k2 < 2; k2++) {
-        V8 bs[2];
+      for (int k2 = 0; k2 < 2; k2++)
 #pragma unroll
-        for (int qt = 0; qt < 2; qt++)
-#pragma unroll
-          for (int e = 0; e < 8; e++) bs[qt][e] = E::from_f32(st[qt][8 * k2 + e]);
-#pragma unroll
-        for (int dt = 0; dt < 4; dt++) {
-          const V8 a = tile_read_tr<V8>(Kb, kt * 2 + k2, dt);
-          dq[0][dt] = E::mfma32(a, bs[0], dq[0][dt]);
-          dq[1][dt] = E::mfma32(a, bs[1], dq[1][dt]);
-        }
-      }
+        for (int dt = 0; dt < 4; dt++)
+          dq[dt] = E::mfma32(tile_read_tr<V8>(Kb, kt * 2 + k2, dt), bs[k2], dq[dt]);
     }
     wait_vm();
     __syncthreads();
@@ -188,21 +174,17 @@ __global__ __launch_bounds__(NW * 64) void bsa_dq_kernel(BsaParams p, int qsub, 
     i = inext;
   }
 
+  if (row_ok) {
+    T* drow = (T*)p.out + qoff + (long)qrow * kD;
 #pragma unroll
-  for (int qt = 0; qt < 2; qt++) {
-    const int row = wrow0 + qt * 32 + l32;
-    if (row < row_hi) {
-      T* drow = (T*)p.out + qoff + (long)row * kD;
+    for (int dt = 0; dt < 4; dt++)
 #pragma unroll
-      for (int dt = 0; dt < 4; dt++)
-#pragma unroll
-        for (int jj = 0; jj < 4; jj++) {
-          const int d0 = dt * 32 + 8 * jj + 4 * h;
-          *reinterpret_cast<uint2*>(drow + d0) =
-              pack4<E>(dq[qt][dt][4 * jj] * p.scale, dq[qt][dt][4 * jj + 1] * p.scale,
-                       dq[qt][dt][4 * jj + 2] * p.scale, dq[qt][dt][4 * jj + 3] * p.scale);
-        }
-    }
+      for (int jj = 0; jj < 4; jj++) {
+        const int d0 = dt * 32 + 8 * jj + 4 * h;
+        *reinterpret_cast<uint2*>(drow + d0) =
+            pack4<E>(dq[dt][4 * jj] * p.scale, dq[dt][4 * jj + 1] * p.scale,
+                     dq[dt][4 * jj + 2] * p.scale, dq[dt][4 * jj + 3] * p.scale);
+      }
   }
 }
 
@@ -219,10 +201,11 @@ __global__ __launch_bounds__(NW * 64) void bsa_dkdv_kernel(BsaParams p, int ksub
   typedef typename E::T T;
   typedef typename E::V8 V8;
   constexpr int NK = NW * 32;  // keys per workgroup
-  __shared__ __attribute__((aligned(1024))) char lds_q[2][kTileB];
-  __shared__ __attribute__((aligned(1024))) char lds_do[2][kTileB];
-  __shared__ float lds_lse[2][64];
-  __shared__ float lds_dlt[2][64];
+  constexpr int NS = 3;        // pipeline stages: chunks i+1 and i+2 load while i computes
+  __shared__ __attribute__((aligned(1024))) char lds_q[NS][kTileB];
+  __shared__ __attribute__((aligned(1024))) char lds_do[NS][kTileB];
+  __shared__ float lds_lse[NS][64];
+  __shared__ float lds_dlt[NS][64];
 
   const int item = xcd_remap(blockIdx.x, n_items);
   if (item < 0) return;
@@ -294,46 +277,56 @@ __global__ __launch_bounds__(NW * 64) void bsa_dkdv_kernel(BsaParams p, int ksub
 #pragma unroll
     for (int j = 0; j < 16; j++) dvt[dt][j] = dkt[dt][j] = 0.f;
 
-  int i = next_valid(0);
-  if (i < nchunks) {
+  // Loads per wave per chunk (they retire in order): the Q and dO slices,
+  // plus LSE and softmax_grad rows for wave 0.
+  constexpr int kLoads = 2 * (16 / NW);
+  const int i0 = next_valid(0);
+  const int i1 = i0 < nchunks ? next_valid(i0 + 1) : nchunks;
+  if (i0 < nchunks) {
     int n1, qs, qe;
-    chunk_range(i, n1, qs, qe);
+    chunk_range(i0, n1, qs, qe);
     load_chunk(n1, qs, qe, 0);
   }
-  wait_vm();
+  if (i1 < nchunks) {
+    int n1, qs, qe;
+    chunk_range(i1, n1, qs, qe);
+    load_chunk(n1, qs, qe, 1);
+    if (wid == 0) wait_vm_le<kLoads + 2>(); else wait_vm_le<kLoads>();
+  } else {
+    wait_vm();
+  }
   __syncthreads();
   int buf = 0;
+  int i = i0, inext = i1;
   while (i < nchunks) {
     int n1, qs, qe;
     chunk_range(i, n1, qs, qe);
-    const int inext = next_valid(i + 1);
-    if (inext < nchunks) {
+    const int inext2 = inext < nchunks ? next_valid(inext + 1) : nchunks;
+    if (inext2 < nchunks) {
       int n1b, qs2, qe2;
-      chunk_range(inext, n1b, qs2, qe2);
-      load_chunk(n1b, qs2, qe2, buf ^ 1);
+      chunk_range(inext2, n1b, qs2, qe2);
+      load_chunk(n1b, qs2, qe2, buf == 0 ? 2 : buf - 1);
     }
     const char* Qb = lds_q[buf];
     const char* Db = lds_do[buf];
 
-    f32x16 s[2], dp[2];
-#pragma unroll
-    for (int qt = 0; qt < 2; qt++)
-#pragma unroll
-      for (int j = 0; j < 16; j++) s[qt][j] = dp[qt][j] = 0.f;
-#pragma unroll
-    for (int ds = 0; ds < 8; ds++) {
-#pragma unroll
-      for (int qt = 0; qt < 2; qt++) {
-        const V8 aq = tile_read16<V8>(Qb, qt * 32 + l32, 2 * ds + h);
-        const V8 ad = tile_read16<V8>(Db, qt * 32 + l32, 2 * ds + h);
-        s[qt] = E::mfma32(aq, kreg[ds], s[qt]);
-        dp[qt] = E::mfma32(ad, vreg[ds], dp[qt]);
-      }
-    }
-    // rows of the accumulators are queries: element j of lane l is query
-    // qt*32 + 8*(j/4) + 4*h + j%4, column key l%32
+    // a chunk whose every query row is valid and at or after every key of
+    // this wave needs no mask
+    const bool full = (qe - qs == 64) && key_lo + wid * 32 + 32 <= key_hi &&
+                      (!p.causal || qs >= key_lo + wid * 32 + 31);
 #pragma unroll
     for (int qt = 0; qt < 2; qt++) {
+      // S = Q K^T and dP = dO V^T for 32 queries (rows) x this wave's 32 keys
+      f32x16 s, dp;
+#pragma unroll
+      for (int j = 0; j < 16; j++) s[j] = dp[j] = 0.f;
+#pragma unroll
+      for (int ds = 0; ds < 8; ds++) {
+        s = E::mfma32(tile_read16<V8>(Qb, qt * 32 + l32, 2 * ds + h), kreg[ds], s);
+        dp = E::mfma32(tile_read16<V8>(Db, qt * 32 + l32, 2 * ds + h), vreg[ds], dp);
+      }
+      // element j of a lane is query qt*32 + 8*(j/4) + 4*h + j%4, column key l32
+      V8 bp[2], bd[2];
 #pragma unroll
       for (int j4 = 0; j4 < 4; j4++) {
         const int rbase = qt * 32 + 8 * j4 + 4 * h;
@@ -344,35 +337,34 @@ __global__ __launch_bounds__(NW * 64) void bsa_dkdv_kernel(BsaParams p, int ksub
 #pragma unroll
         for (int jj = 0; jj < 4; jj++) {
           const int j = 4 * j4 + jj;
-          const int q = qs + rbase + jj;
-          const bool ok = key_ok && q < qe && (!p.causal || mykey <= q);
-          const float pv = ok ? fast_exp2(s[qt][j] * sl2 - lv[jj] * kLog2e) : 0.f;
-          s[qt][j] = pv;
-          dp[qt][j] = pv * (dp[qt][j] - dv[jj]);
+          float pr = fast_exp2(__builtin_fmaf(s[j], sl2, -lv[jj] * kLog2e));
+          if (!full) {
+            const int q = qs + rbase + jj;
+            const bool ok = key_ok && q < qe && (!p.causal || mykey <= q);
+            pr = ok ? pr : 0.f;
+          }
+          bp[j >> 3][j & 7] = E::from_f32(pr);
+          bd[j >> 3][j & 7] = E::from_f32(pr * (dp[j] - dv[jj]));
         }
       }
+      // dV^T += dO^T P ; dK^T += Q^T dS  (16 queries per step)
+#pragma unroll
+      for (int k2 = 0; k2 < 2; k2++)
+#pragma unroll
+        for (int dt = 0; dt < 4; dt++) {
+          dvt[dt] = E::mfma32(tile_read_tr<V8>(Db, qt * 2 + k2, dt), bp[k2], dvt[dt]);
+          dkt[dt] = E::mfma32(tile_read_tr<V8>(Qb, qt * 2 + k2, dt), bd[k2], dkt[dt]);
+        }
     }
-    // dV^T += dO^T P ; dK^T += Q^T dS  (16 queries per step)
-#pragma unroll
-    for (int k4 = 0; k4 < 4; k4++) {
-      V8 bp, bd;
-#pragma unroll
-      for (int e = 0; e < 8; e++) {
-        bp[e] = E::from_f32(s[k4 >> 1][8 * (k4 & 1) + e]);
-        bd[e] = E::from_f32(dp[k4 >> 1][8 * (k4 & 1) + e]);
-      }
-#pragma unroll
-      for (int dt = 0; dt < 4; dt++) {
-        const V8 ado = tile_read_tr<V8>(Db, k4, dt);
-        const V8 aq = tile_read_tr<V8>(Qb, k4, dt);
-        dvt[dt] = E::mfma32(ado, bp, dvt[dt]);
-        dkt[dt] = E::mfma32(aq, bd, dkt[dt]);
-      }
+    if (inext2 < nchunks) {
+      if (wid == 0) wait_vm_le<kLoads + 2>(); else wait_vm_le<kLoads>();
+    } else {
+      wait_vm();
     }
-    wait_vm();
     __syncthreads();
-    buf ^= 1;
+    buf = buf == NS - 1 ? 0 : buf + 1;
     i = inext;
+    inext = inext2;
   }
 
   if (key_ok) {
@@ -394,7 +386,7 @@ __global__ __launch_bounds__(NW * 64) void bsa_dkdv_kernel(BsaParams p, int ksub
 
 template <class E, int NW>
 static hipError_t launch_dq_t(const BsaParams& p, hipStream_t st) {
-  const int qsub = (p.bq + NW * 64 - 1) / (NW * 64);
+  const int qsub = (p.bq + NW * 32 - 1) / (NW * 32);
   const int n_items = p.B * p.N1 * p.QB * qsub;
   if (n_items == 0) return hipSuccess;
   hipLaunchKernelGGL((bsa_dq_kernel<E, NW>), dim3(8 * ((n_items + 7) / 8)), dim3(NW * 64), 0, st,
@@ -415,7 +407,9 @@ static hipError_t launch_dkdv_t(const BsaParams& p, hipStream_t st) {
 template <class E>
 static hipError_t launch_bwd_t(const BsaParams& p, hipStream_t st, void* const* ev, int n_ev) {
   hipError_t e = mark_event(ev, n_ev, 1, 0, st);
-  if (e == hipSuccess) e = p.bq <= 64 ? launch_dq_t<E, 1>(p, st) : launch_dq_t<E, 2>(p, st);
+  if (e == hipSuccess)
+    e = p.bq <= 32 ? launch_dq_t<E, 1>(p, st)
+                   : (p.bq <= 64 ? launch_dq_t<E, 2>(p, st) : launch_dq_t<E, 4>(p, st));
   if (e == hipSuccess) e = mark_event(ev, n_ev, 1, 1, st);
   if (e == hipSuccess) e = mark_event(ev, n_ev, 2, 0, st);
   if (e == hipSuccess)

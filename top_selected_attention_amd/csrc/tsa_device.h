@@ -108,6 +108,13 @@ __device__ __forceinline__ int swz(int r) {
 // Waits for this wave's outstanding vector-memory loads (including direct
 // global -> LDS loads) to land.
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Waits until at most N of this wave's vector-memory operations are still in
+// flight (they complete in issue order): the older stages of a multi-stage
+// pipeline have landed while the newest N loads may still be pending.
+template <int N>
+__device__ __forceinline__ void wait_vm_le() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 template <typename V8>
 __device__ __forceinline__ V8 zero_v8() {
