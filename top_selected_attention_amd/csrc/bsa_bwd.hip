@@ -17,6 +17,8 @@
 // double-buffered, swizzled LDS with direct global -> LDS loads, keep the
 // stationary operand in registers, and feed accumulator tiles straight back
 // into the next MFMA as operands (see tsa_device.h).
+#include <type_traits>
+
 #include "tsa_device.h"
 #include "tsa_internal.h"
 
@@ -149,18 +151,26 @@ __global__ __launch_bounds__(NW * 64) void bsa_dq_kernel(BsaParams p, int qsub, 
         dpt = E::mfma32(tile_read16<V8>(Vb, kt * 32 + l32, 2 * ds + h), doreg[ds], dpt);
       }
       // dS^T = P^T * (dP^T - D), P^T = exp2(S^T * scale*log2e - LSE2);
-      // element j is key ks + kt*32 + 8*(j/4) + 4*h + j%4
+      // element j is key ks + kt*32 + 8*(j/4) + 4*h + j%4.  Outside a full
+      // chunk, key offsets above this lane's limit are masked (two copies of
+      // the loop so the full path carries no compare).
       V8 bs[2];
-#pragma unroll
-      for (int j = 0; j < 16; j++) {
-        float pv = fast_exp2(__builtin_fmaf(st[j], sl2, lneg));
-        if (!full) {
-          const int key = ks + kt * 32 + 8 * (j >> 2) + 4 * h + (j & 3);
-          const bool ok = key < ke && row_ok && (!p.causal || key <= qrow);
-          pv = ok ? pv : 0.f;
+      auto form_ds = [&](auto masked) {
+        int lim = 0;
+        if (masked) {
+          lim = ke - 1 - ks;
+          if (p.causal) lim = min(lim, qrow - ks);
+          lim = row_ok ? lim - 4 * h : -1000000;
         }
-        bs[j >> 3][j & 7] = E::from_f32(pv * (dpt[j] - dlt));
-      }
+#pragma unroll
+        for (int j = 0; j < 16; j++) {
+          float pv = fast_exp2(__builtin_fmaf(st[j], sl2, lneg));
+          if (masked) pv = (kt * 32 + 8 * (j >> 2) + (j & 3)) <= lim ? pv : 0.f;
+          bs[j >> 3][j & 7] = E::from_f32(pv * (dpt[j] - dlt));
+        }
+      };
+      if (full) form_ds(std::false_type());
+      else form_ds(std::true_type());
       // dQ^T += K^T dS^T over the tile's 32 keys (two 16-key steps)
 #pragma unroll
       for (int k2 = 0; k2 < 2; k2++)
@@ -325,8 +335,9 @@ __global__ __launch_bounds__(NW * 64) void bsa_dkdv_kernel(BsaParams p, int ksub
         s = E::mfma32(tile_read16<V8>(Qb, qt * 32 + l32, 2 * ds + h), kreg[ds], s);
         dp = E::mfma32(tile_read16<V8>(Db, qt * 32 + l32, 2 * ds + h), vreg[ds], dp);
       }
+      sched_mfma_lds<16, 1, 4>();
       // element j of a lane is query qt*32 + 8*(j/4) + 4*h + j%4, column key l32
-      V8 bp[2], bd[2];
+      float pr[16], dd[16];
 #pragma unroll
       for (int j4 = 0; j4 < 4; j4++) {
         const int rbase = qt * 32 + 8 * j4 + 4 * h;
@@ -337,15 +348,25 @@ __global__ __launch_bounds__(NW * 64) void bsa_dkdv_kernel(BsaParams p, int ksub
 #pragma unroll
         for (int jj = 0; jj < 4; jj++) {
           const int j = 4 * j4 + jj;
-          float pr = fast_exp2(__builtin_fmaf(s[j], sl2, -lv[jj] * kLog2e));
-          if (!full) {
-            const int q = qs + rbase + jj;
-            const bool ok = key_ok && q < qe && (!p.causal || mykey <= q);
-            pr = ok ? pr : 0.f;
-          }
-          bp[j >> 3][j & 7] = E::from_f32(pr);
-          bd[j >> 3][j & 7] = E::from_f32(pr * (dp[j] - dv[jj]));
+          pr[j] = fast_exp2(__builtin_fmaf(s[j], sl2, -lv[jj] * kLog2e));
+          dd[j] = dp[j] - dv[jj];
         }
+      }
+      if (!full) {
+        // row offsets (without this lane's 4*h) must lie in [lo, hi]
+        const int lo = (p.causal ? mykey - qs : 0) - 4 * h;
+        const int hi = key_ok ? qe - qs - 1 - 4 * h : -1000000;
+#pragma unroll
+        for (int j = 0; j < 16; j++) {
+          const int off = qt * 32 + 8 * (j >> 2) + (j & 3);
+          pr[j] = (off >= lo && off <= hi) ? pr[j] : 0.f;
+        }
+      }
+      V8 bp[2], bd[2];
+#pragma unroll
+      for (int j = 0; j < 16; j++) {
+        bp[j >> 3][j & 7] = E::from_f32(pr[j]);
+        bd[j >> 3][j & 7] = E::from_f32(pr[j] * dd[j]);
       }
       // dV^T += dO^T P ; dK^T += Q^T dS  (16 queries per step)
 #pragma unroll
@@ -355,6 +376,7 @@ __global__ __launch_bounds__(NW * 64) void bsa_dkdv_kernel(BsaParams p, int ksub
           dvt[dt] = E::mfma32(tile_read_tr<V8>(Db, qt * 2 + k2, dt), bp[k2], dvt[dt]);
           dkt[dt] = E::mfma32(tile_read_tr<V8>(Qb, qt * 2 + k2, dt), bd[k2], dkt[dt]);
         }
+      sched_mfma_lds<16, 2, 4>();
     }
     if (inext2 < nchunks) {
       if (wid == 0) wait_vm_le<kLoads + 2>(); else wait_vm_le<kLoads>();

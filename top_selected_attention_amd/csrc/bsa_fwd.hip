@@ -136,18 +136,21 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_kernel(BsaParams p, int qsub,
       st[0] = E::mfma32(tile_read16<V8>(Kb, l32, 2 * ds + h), qreg[ds], st[0]);
       st[1] = E::mfma32(tile_read16<V8>(Kb, 32 + l32, 2 * ds + h), qreg[ds], st[1]);
     }
-    // element j of tile kt is key ks + kt*32 + 8*(j/4) + 4*h + j%4; a whole
-    // chunk at or below every row of this wave needs no mask
+    sched_mfma_lds<16, 1, 4>();
+    // Element j of tile kt is key ks + kt*32 + 8*(j/4) + 4*h + j%4.  A chunk
+    // wholly inside [0, ke) and at or below every row of this wave needs no
+    // mask; otherwise key offsets above this lane's limit are masked (the
+    // offset without the lane's 4*h is a compile-time constant per element).
     const bool full = (ke - ks == kKC) && (!p.causal || ke - 1 <= wrow0);
     if (!full) {
+      int lim = ke - 1 - ks;
+      if (p.causal) lim = min(lim, qrow - ks);
+      lim -= 4 * h;
 #pragma unroll
       for (int kt = 0; kt < 2; kt++)
 #pragma unroll
-        for (int j = 0; j < 16; j++) {
-          const int key = ks + kt * 32 + 8 * (j >> 2) + 4 * h + (j & 3);
-          const bool ok = key < ke && (!p.causal || key <= qrow);
-          st[kt][j] = ok ? st[kt][j] : -INFINITY;
-        }
+        for (int j = 0; j < 16; j++)
+          st[kt][j] = (kt * 32 + 8 * (j >> 2) + (j & 3)) <= lim ? st[kt][j] : -INFINITY;
     }
     float mx = fmaxf(st[0][0], st[1][0]);
 #pragma unroll
@@ -180,6 +183,7 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_kernel(BsaParams p, int qsub,
 #pragma unroll
       for (int dt = 0; dt < 4; dt++)
         o[dt] = E::mfma32(tile_read_tr<V8>(Vb, k4, dt), pb[k4], o[dt]);
+    sched_mfma_lds<16, 2, 4>();
 
     wait_vm();
     __syncthreads();

@@ -177,6 +177,20 @@ __device__ __forceinline__ V8 tile_read_tr(const char* tile, int k16, int dt) {
                               tile + r1 * 256 + ((c ^ swz(r1)) << 4) + b8);
 }
 
+// Scheduling hint for a stage of NM MFMAs fed by LDS reads: AHEAD reads are
+// issued first, then each MFMA is followed by RPM more reads, so the LDS
+// latency of later operands hides behind earlier MFMAs.  (Place it after the
+// stage's code, in the same basic block.)
+template <int NM, int RPM, int AHEAD>
+__device__ __forceinline__ void sched_mfma_lds() {
+  __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
+#pragma unroll
+  for (int u = 0; u < NM; u++) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);
+  }
+}
+
 // XCD-aware workgroup -> work-item remap.  Workgroups are dispatched to the 8
 // XCDs round-robin (workgroup w runs on XCD w % 8).  Giving XCD x the
 // contiguous range [x * per, (x + 1) * per) of the work order keeps the work
