@@ -199,23 +199,31 @@ __global__ __launch_bounds__(NW * 64) void bsa_dq_kernel(BsaParams p, int qsub, 
 }
 
 // ---------------------------------------------------------------------------
-// dK / dV.  Each wave owns 32 keys of the KV block and keeps their K and V as
-// MFMA B operands.  Per 64-query chunk of a selecting Q block:
+// dK / dV.  Each wave owns 32 keys of the KV block.  The block's K rows stay
+// in LDS for the whole walk (read as the B operand of S); each wave keeps its
+// V rows as the B operand of dP in registers.  Per 32-query chunk of a
+// selecting Q block (double-buffered in LDS):
 //   S = Q K^T and dP = dO V^T (queries x keys, lanes on key columns),
 //   P = exp2(S * scale*log2e - LSE2), dS = P * (dP - softmax_grad),
 //   dV^T += dO^T P and dK^T += Q^T dS, with dO^T / Q^T read from the staged
 //   natural-layout tiles by transpose reads.
+// Small chunks keep two workgroups' LDS within a CU and the live registers
+// under 256, so two waves share each SIMD.
 // ---------------------------------------------------------------------------
+// Two waves per SIMD (register budget 256; a few spills are cheaper than
+// running one wave per SIMD).
 template <class E, int NW>
-__global__ __launch_bounds__(NW * 64) void bsa_dkdv_kernel(BsaParams p, int ksub, int n_items) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void bsa_dkdv_kernel(BsaParams p, int ksub, int n_items) {
   typedef typename E::T T;
   typedef typename E::V8 V8;
-  constexpr int NK = NW * 32;  // keys per workgroup
-  constexpr int NS = 3;        // pipeline stages: chunks i+1 and i+2 load while i computes
-  __shared__ __attribute__((aligned(1024))) char lds_q[NS][kTileB];
-  __shared__ __attribute__((aligned(1024))) char lds_do[NS][kTileB];
-  __shared__ float lds_lse[NS][64];
-  __shared__ float lds_dlt[NS][64];
+  constexpr int NK = NW * 32;       // keys per workgroup
+  constexpr int kQC = 32;           // queries per chunk
+  constexpr int kQTile = kQC * kD * 2;
+  __shared__ __attribute__((aligned(1024))) char lds_k[NK * kD * 2];
+  __shared__ __attribute__((aligned(1024))) char lds_q[2][kQTile];
+  __shared__ __attribute__((aligned(1024))) char lds_do[2][kQTile];
+  __shared__ float lds_lse[2][64];
+  __shared__ float lds_dlt[2][64];
 
   const int item = xcd_remap(blockIdx.x, n_items);
   if (item < 0) return;
@@ -232,24 +240,33 @@ __global__ __launch_bounds__(NW * 64) void bsa_dkdv_kernel(BsaParams p, int ksub
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5;
-  const int mykey = key_lo + wid * 32 + l32;
+  const int wkey0 = key_lo + wid * 32;
+  const int mykey = wkey0 + l32;
   const bool key_ok = mykey < key_hi;
 
   const long kvoff = (long)bh * p.Skv * kD;
   const T* kh = (const T*)p.k + kvoff;
   const T* vh = (const T*)p.v + kvoff;
 
-  V8 kreg[8], vreg[8];
+  // K rows of the workgroup into LDS (rows past key_hi re-read the last key)
+  {
+    const int sub = lane >> 4, pc = lane & 15;
 #pragma unroll
-  for (int ds = 0; ds < 8; ds++) {
-    const long off = (long)mykey * kD + ds * 16 + 8 * h;
-    kreg[ds] = key_ok ? as_v8<V8>(ld16(kh + off)) : zero_v8<V8>();
-    vreg[ds] = key_ok ? as_v8<V8>(ld16(vh + off)) : zero_v8<V8>();
+    for (int u = 0; u < NK / 4 / NW; u++) {
+      const int inst = wid * (NK / 4 / NW) + u;
+      const int r = inst * 4 + sub;
+      const long key = min(key_lo + r, key_hi - 1);
+      g2lds16((const char*)(kh + key * kD) + ((pc ^ swz(r)) << 4), lds_k + inst * 1024);
+    }
   }
+  V8 vreg[8];
+#pragma unroll
+  for (int ds = 0; ds < 8; ds++)
+    vreg[ds] = key_ok ? as_v8<V8>(ld16(vh + (long)mykey * kD + ds * 16 + 8 * h)) : zero_v8<V8>();
 
   const int c = bh * p.KB + kb;
   const int e0 = p.rev_ptr[c], e1 = p.rev_ptr[c + 1];
-  const int cpq = (p.bq + 63) / 64;
+  const int cpq = (p.bq + kQC - 1) / kQC;
   const int nchunks = (e1 - e0) * cpq;
   const float sl2 = p.scale * kLog2e;
 
@@ -258,8 +275,8 @@ __global__ __launch_bounds__(NW * 64) void bsa_dkdv_kernel(BsaParams p, int ksub
     const int id = p.rev[e0 + i / cpq];
     const int g = id / p.QB, qb = id % p.QB;
     n1 = n2 * p.G + g;
-    qs = qb * p.bq + (i % cpq) * 64;
-    qe = min(min(qs + 64, (qb + 1) * p.bq), p.Sq);
+    qs = qb * p.bq + (i % cpq) * kQC;
+    qe = min(min(qs + kQC, (qb + 1) * p.bq), p.Sq);
   };
   auto next_valid = [&](int i) {
     for (; i < nchunks; i++) {
@@ -269,12 +286,22 @@ __global__ __launch_bounds__(NW * 64) void bsa_dkdv_kernel(BsaParams p, int ksub
     }
     return i;
   };
+  // 32 rows of Q and of dO (8 KB each) plus their LSE / softmax_grad
   auto load_chunk = [&](int n1, int qs, int qe, int buf) {
     const long hoff = ((long)b * p.N1 + n1) * p.Sq;
-    auto row_of = [&](int r) { return min(qs + r, qe - 1); };
-    stage_tile64<NW>((const char*)((const T*)p.q + hoff * kD), lds_q[buf], row_of);
-    stage_tile64<NW>((const char*)((const T*)p.dout + hoff * kD), lds_do[buf], row_of);
+    const int sub = lane >> 4, pc = lane & 15;
+#pragma unroll
+    for (int u = 0; u < 8 / NW; u++) {
+      const int inst = wid * (8 / NW) + u;
+      const int r = inst * 4 + sub;
+      const long row = hoff + min(qs + r, qe - 1);
+      g2lds16((const char*)((const T*)p.q + row * kD) + ((pc ^ swz(r)) << 4), lds_q[buf] + inst * 1024);
+      g2lds16((const char*)((const T*)p.dout + row * kD) + ((pc ^ swz(r)) << 4),
+              lds_do[buf] + inst * 1024);
+    }
     if (wid == 0) {
+      // a direct LDS load writes lane l's dword at base + 4*l for all 64
+      // lanes: the arrays hold 64 entries; entries past 32 are never read
       const long r = hoff + min(qs + lane, qe - 1);
       g2lds4(p.lse + r, lds_lse[buf]);
       g2lds4(p.delta + r, lds_dlt[buf]);
@@ -287,60 +314,57 @@ __global__ __launch_bounds__(NW * 64) void bsa_dkdv_kernel(BsaParams p, int ksub
 #pragma unroll
     for (int j = 0; j < 16; j++) dvt[dt][j] = dkt[dt][j] = 0.f;
 
-  // Loads per wave per chunk (they retire in order): the Q and dO slices,
-  // plus LSE and softmax_grad rows for wave 0.
-  constexpr int kLoads = 2 * (16 / NW);
-  const int i0 = next_valid(0);
-  const int i1 = i0 < nchunks ? next_valid(i0 + 1) : nchunks;
-  if (i0 < nchunks) {
+  int i = next_valid(0);
+  if (i < nchunks) {
     int n1, qs, qe;
-    chunk_range(i0, n1, qs, qe);
+    chunk_range(i, n1, qs, qe);
     load_chunk(n1, qs, qe, 0);
   }
-  if (i1 < nchunks) {
-    int n1, qs, qe;
-    chunk_range(i1, n1, qs, qe);
-    load_chunk(n1, qs, qe, 1);
-    if (wid == 0) wait_vm_le<kLoads + 2>(); else wait_vm_le<kLoads>();
-  } else {
-    wait_vm();
-  }
+  wait_vm();
   __syncthreads();
   int buf = 0;
-  int i = i0, inext = i1;
   while (i < nchunks) {
     int n1, qs, qe;
     chunk_range(i, n1, qs, qe);
-    const int inext2 = inext < nchunks ? next_valid(inext + 1) : nchunks;
-    if (inext2 < nchunks) {
+    const int inext = next_valid(i + 1);
+    if (inext < nchunks) {
       int n1b, qs2, qe2;
-      chunk_range(inext2, n1b, qs2, qe2);
-      load_chunk(n1b, qs2, qe2, buf == 0 ? 2 : buf - 1);
+      chunk_range(inext, n1b, qs2, qe2);
+      load_chunk(n1b, qs2, qe2, buf ^ 1);
     }
     const char* Qb = lds_q[buf];
     const char* Db = lds_do[buf];
 
+    // S = Q K^T and dP = dO V^T for 32 queries (rows) x this wave's 32 keys
+    f32x16 s, dp;
+#pragma unroll
+    for (int j = 0; j < 16; j++) s[j] = dp[j] = 0.f;
+#pragma unroll
+    for (int ds = 0; ds < 8; ds++) {
+      s = E::mfma32(tile_read16<V8>(Qb, l32, 2 * ds + h), tile_read16<V8>(lds_k, wid * 32 + l32, 2 * ds + h), s);
+      dp = E::mfma32(tile_read16<V8>(Db, l32, 2 * ds + h), vreg[ds], dp);
+    }
+    // three LDS reads feed two MFMAs per step
+    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+#pragma unroll
+    for (int u = 0; u < 8; u++) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+    }
     // a chunk whose every query row is valid and at or after every key of
     // this wave needs no mask
-    const bool full = (qe - qs == 64) && key_lo + wid * 32 + 32 <= key_hi &&
-                      (!p.causal || qs >= key_lo + wid * 32 + 31);
-#pragma unroll
-    for (int qt = 0; qt < 2; qt++) {
-      // S = Q K^T and dP = dO V^T for 32 queries (rows) x this wave's 32 keys
-      f32x16 s, dp;
-#pragma unroll
-      for (int j = 0; j < 16; j++) s[j] = dp[j] = 0.f;
-#pragma unroll
-      for (int ds = 0; ds < 8; ds++) {
-        s = E::mfma32(tile_read16<V8>(Qb, qt * 32 + l32, 2 * ds + h), kreg[ds], s);
-        dp = E::mfma32(tile_read16<V8>(Db, qt * 32 + l32, 2 * ds + h), vreg[ds], dp);
+    const bool full = (qe - qs == kQC) && wkey0 + 32 <= key_hi && (!p.causal || qs >= wkey0 + 31);
+    // element j of a lane is query 8*(j/4) + 4*h + j%4 of the chunk, column key l32
+    V8 bp[2], bd[2];
+    auto form = [&](auto masked) {
+      int lo = 0, hi = 0;
+      if (masked) {
+        lo = (p.causal ? mykey - qs : 0) - 4 * h;
+        hi = key_ok ? qe - qs - 1 - 4 * h : -1000000;
       }
-      sched_mfma_lds<16, 1, 4>();
-      // element j of a lane is query qt*32 + 8*(j/4) + 4*h + j%4, column key l32
-      float pr[16], dd[16];
 #pragma unroll
       for (int j4 = 0; j4 < 4; j4++) {
-        const int rbase = qt * 32 + 8 * j4 + 4 * h;
+        const int rbase = 8 * j4 + 4 * h;
         const float4 lse4 = *reinterpret_cast<const float4*>(&lds_lse[buf][rbase]);
         const float4 dl4 = *reinterpret_cast<const float4*>(&lds_dlt[buf][rbase]);
         const float lv[4] = {lse4.x, lse4.y, lse4.z, lse4.w};
@@ -348,45 +372,31 @@ __global__ __launch_bounds__(NW * 64) void bsa_dkdv_kernel(BsaParams p, int ksub
 #pragma unroll
         for (int jj = 0; jj < 4; jj++) {
           const int j = 4 * j4 + jj;
-          pr[j] = fast_exp2(__builtin_fmaf(s[j], sl2, -lv[jj] * kLog2e));
-          dd[j] = dp[j] - dv[jj];
+          float pr = fast_exp2(__builtin_fmaf(s[j], sl2, -lv[jj] * kLog2e));
+          if (masked) {
+            const int off = 8 * j4 + jj;
+            pr = (off >= lo && off <= hi) ? pr : 0.f;
+          }
+          bp[j >> 3][j & 7] = E::from_f32(pr);
+          bd[j >> 3][j & 7] = E::from_f32(pr * (dp[j] - dv[jj]));
         }
       }
-      if (!full) {
-        // row offsets (without this lane's 4*h) must lie in [lo, hi]
-        const int lo = (p.causal ? mykey - qs : 0) - 4 * h;
-        const int hi = key_ok ? qe - qs - 1 - 4 * h : -1000000;
+    };
+    if (full) form(std::false_type());
+    else form(std::true_type());
+    // dV^T += dO^T P ; dK^T += Q^T dS  (16 queries per step)
 #pragma unroll
-        for (int j = 0; j < 16; j++) {
-          const int off = qt * 32 + 8 * (j >> 2) + (j & 3);
-          pr[j] = (off >= lo && off <= hi) ? pr[j] : 0.f;
-        }
+    for (int k2 = 0; k2 < 2; k2++)
+#pragma unroll
+      for (int dt = 0; dt < 4; dt++) {
+        dvt[dt] = E::mfma32(tile_read_tr<V8>(Db, k2, dt), bp[k2], dvt[dt]);
+        dkt[dt] = E::mfma32(tile_read_tr<V8>(Qb, k2, dt), bd[k2], dkt[dt]);
       }
-      V8 bp[2], bd[2];
-#pragma unroll
-      for (int j = 0; j < 16; j++) {
-        bp[j >> 3][j & 7] = E::from_f32(pr[j]);
-        bd[j >> 3][j & 7] = E::from_f32(pr[j] * dd[j]);
-      }
-      // dV^T += dO^T P ; dK^T += Q^T dS  (16 queries per step)
-#pragma unroll
-      for (int k2 = 0; k2 < 2; k2++)
-#pragma unroll
-        for (int dt = 0; dt < 4; dt++) {
-          dvt[dt] = E::mfma32(tile_read_tr<V8>(Db, qt * 2 + k2, dt), bp[k2], dvt[dt]);
-          dkt[dt] = E::mfma32(tile_read_tr<V8>(Qb, qt * 2 + k2, dt), bd[k2], dkt[dt]);
-        }
-      sched_mfma_lds<16, 2, 4>();
-    }
-    if (inext2 < nchunks) {
-      if (wid == 0) wait_vm_le<kLoads + 2>(); else wait_vm_le<kLoads>();
-    } else {
-      wait_vm();
-    }
+    sched_mfma_lds<16, 2, 4>();
+    wait_vm();
     __syncthreads();
-    buf = buf == NS - 1 ? 0 : buf + 1;
+    buf ^= 1;
     i = inext;
-    inext = inext2;
   }
 
   if (key_ok) {
