@@ -207,6 +207,10 @@ struct NsaWs {
   int* rev;
   int* bad;
   float* delta;
+  int* seg_off;
+  int* seg_sums;
+  float* part;
+  int max_segments;
 };
 
 template <class A>
@@ -226,6 +230,10 @@ size_t nsa_carve(const A* a, void* ws, NsaWs* out, bool with_delta) {
   w.rev = c.take<int>(R * a->sbc);
   w.bad = c.take<int>(1);
   w.delta = with_delta ? c.take<float>((long)a->T * a->N1) : nullptr;
+  w.max_segments = with_delta ? nsa_max_segments(R * a->sbc, RR) : 0;
+  w.seg_off = with_delta ? c.take<int>(RR + 1) : nullptr;
+  w.seg_sums = with_delta ? c.take<int>(scan_sums_len(RR)) : nullptr;
+  w.part = with_delta ? c.take<float>((long)w.max_segments * 2 * a->sbs * a->D) : nullptr;
   if (out) *out = w;
   return c.off + kAlign;
 }
@@ -606,6 +614,7 @@ int nsa_select_bwd(const nsa_select_bwd_args* a, void* ws, size_t ws_bytes, void
   p.row_ptr = w.row_ptr; p.col = w.col; p.rev_ptr = w.rev_ptr; p.rev = w.rev;
   p.T = a->T; p.Tk = a->Tk; p.N1 = a->N1; p.N2 = a->N2; p.G = a->N1 / a->N2; p.D = a->D;
   p.scale = a->scale;
+  p.seg_off = w.seg_off; p.seg_sums = w.seg_sums; p.part = w.part; p.max_segments = w.max_segments;
   return hip_status(launch_nsa_bwd(p, a->dtype == TSA_FP16, st, tm.ev, tm.n));
 }
 

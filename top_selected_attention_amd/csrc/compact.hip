@@ -108,6 +108,16 @@ __global__ __launch_bounds__(kScanThreads) void scan_add(int* data, int n, const
 
 int scan_sums_len(long n) { return (int)((n + kScanTile - 1) / kScanTile) + 1; }
 
+__global__ void put_total(int* data, long n, const int* total) { data[n] = total[0]; }
+
+hipError_t exclusive_scan_total(int* data, long n, int* sums, hipStream_t st) {
+  hipError_t e = exclusive_scan(data, n, sums, st);
+  if (e != hipSuccess) return e;
+  const int nt = (int)((n + kScanTile - 1) / kScanTile);
+  hipLaunchKernelGGL(put_total, dim3(1), dim3(1), 0, st, data, n, sums + nt);
+  return hipGetLastError();
+}
+
 hipError_t exclusive_scan(int* data, long n, int* sums, hipStream_t st) {
   int nt = (int)((n + kScanTile - 1) / kScanTile);
   if (nt == 0) {
@@ -322,6 +332,37 @@ __global__ __launch_bounds__(256) void nsa_row_fill(const int* topk, NsaGeom g, 
   }
 }
 
+// Wave-parallel fill for rows of at most 64 slots: P lanes (a power of two
+// >= sbc) per row, 64 / P rows per wave; lane i of a row ranks slot i against
+// the row's other slots, fetched by lane shuffles.
+__global__ __launch_bounds__(256) void nsa_row_fill_wave(const int* topk, NsaGeom g,
+                                                         const int* row_ptr, int* col, int P) {
+  const int lane = threadIdx.x & 63;
+  const long wave = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int rpw = 64 / P;
+  const long r = wave * rpw + lane / P;
+  const int i = lane % P;
+  const bool live = r < (long)g.T * g.N2;
+  int v = -1;
+  bool keep = false;
+  if (live && i < g.sbc) {
+    const int t = (int)(r / g.N2);
+    const int b = seq_of(g.cu_q, g.B, t);
+    const int pos = t - g.cu_q[b];
+    const int nblk = g.blk_off[b + 1] - g.blk_off[b];
+    v = topk[r * g.sbc + i];
+    keep = nsa_keep(v, pos, nblk, g.sbs, g.causal);
+  }
+  const int base_lane = (lane / P) * P;
+  int rank = 0;
+  for (int j = 0; j < g.sbc; j++) {
+    const int vj = __shfl(v, base_lane + j);
+    const int kj = __shfl((int)keep, base_lane + j);
+    rank += kj && (vj < v || (vj == v && j < i));
+  }
+  if (live && keep) col[row_ptr[r] + rank] = v;
+}
+
 // Occurrences of block id in a sorted row.
 __device__ __forceinline__ int count_in_sorted(const int* a, int n, int id) {
   int lo = 0, hi = n;
@@ -331,41 +372,44 @@ __device__ __forceinline__ int count_in_sorted(const int* a, int n, int id) {
   return c;
 }
 
-// One wave per (n2, global block): lanes walk the tokens of the block's
-// sequence; pass 0 counts, pass 1 writes token ids in ascending order.
+// One 256-thread workgroup per (n2, global block): threads walk the tokens of
+// the block's sequence, 256 at a time; pass 0 counts, pass 1 writes token ids
+// in ascending order (a block-wide scan of the per-token counts places them).
 template <int PASS>
 __global__ __launch_bounds__(256) void nsa_rev(NsaGeom g, const int* row_ptr, const int* col,
                                                int* rev_cnt, const int* rev_ptr, int* rev) {
-  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (wave >= g.N2 * g.NB) return;
-  const int n2 = wave / g.NB, gb = wave % g.NB;
+  const int r = blockIdx.x;
+  if (r >= g.N2 * g.NB) return;
+  const int n2 = r / g.NB, gb = r % g.NB;
   const int b = seq_of(g.blk_off, g.B, gb);
   const int id = gb - g.blk_off[b];
   const int t0 = g.cu_q[b], t1 = g.cu_q[b + 1];
   // under causal mode tokens before the block's first key cannot keep it
   const int tstart = g.causal ? max(t0, t0 + id * g.sbs) : t0;
-  int out = PASS ? rev_ptr[wave] : 0;
+  int out = PASS ? rev_ptr[r] : 0;
   int total = 0;
-  for (int tb = tstart; tb < t1; tb += 64) {
-    const int t = tb + lane;
+  for (int tb = tstart; tb < t1; tb += 256) {
+    const int t = tb + threadIdx.x;
     int c = 0;
     if (t < t1) {
-      const long r = (long)t * g.N2 + n2;
-      c = count_in_sorted(col + row_ptr[r], row_ptr[r + 1] - row_ptr[r], id);
+      const long rr = (long)t * g.N2 + n2;
+      const int a0 = row_ptr[rr], a1 = row_ptr[rr + 1];
+      // rows are short and sorted: count matches with independent loads
+      for (int x = a0; x < a1; x++) c += col[x] == id;
     }
     if (PASS) {
-      int incl = wave_incl_scan(c);
-      int pos = out + incl - c;
-      for (int k = 0; k < c; k++) rev[pos + k] = t;
-      out += __shfl(incl, 63);
+      int tot;
+      const int ex = block_excl_scan(c, &tot);
+      for (int k = 0; k < c; k++) rev[out + ex + k] = t;
+      out += tot;
     } else {
       total += c;
     }
   }
   if (!PASS) {
-    for (int o = 32; o > 0; o >>= 1) total += __shfl_xor(total, o);
-    if (lane == 0) rev_cnt[wave] = total;
+    int tot;
+    block_excl_scan(total, &tot);
+    if (threadIdx.x == 0) rev_cnt[r] = tot;
   }
 }
 
@@ -402,10 +446,18 @@ hipError_t launch_nsa_compact(const int* topk, const NsaGeom& g, int* cnt_scan, 
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(copy_ptr, dim3((unsigned)((rows + 256) / 256)), dim3(256), 0, st, cnt_scan,
                      rows, sums + (rows + kScanTile - 1) / kScanTile, row_ptr);
-  hipLaunchKernelGGL(nsa_row_fill, dim3(rb), dim3(256), 0, st, topk, g, row_ptr, col);
+  if (g.sbc <= 64) {
+    int P = 1;
+    while (P < g.sbc) P <<= 1;
+    const long waves = (rows + 64 / P - 1) / (64 / P);
+    hipLaunchKernelGGL(nsa_row_fill_wave, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, topk,
+                       g, row_ptr, col, P);
+  } else {
+    hipLaunchKernelGGL(nsa_row_fill, dim3(rb), dim3(256), 0, st, topk, g, row_ptr, col);
+  }
   // reverse: counts -> scan -> fill
   const long rrows = (long)g.N2 * g.NB;
-  const unsigned wb = (unsigned)((rrows + 3) / 4);
+  const unsigned wb = (unsigned)rrows;
   hipLaunchKernelGGL(nsa_rev<0>, dim3(wb), dim3(256), 0, st, g, row_ptr, col, rev_scan,
                      (const int*)nullptr, (int*)nullptr);
   e = exclusive_scan(rev_scan, rrows, sums, st);

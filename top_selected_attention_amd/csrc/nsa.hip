@@ -13,6 +13,8 @@
 // MFMA).  The selected blocks are walked in 32-key chunks that the wave stages
 // into its own LDS region (direct global -> LDS loads) -- no workgroup
 // barrier; the other waves on the SIMD cover the load latency.
+#include <algorithm>
+
 #include "tsa_device.h"
 #include "tsa_internal.h"
 
@@ -274,14 +276,33 @@ __global__ __launch_bounds__(256) void nsa_dq_kernel(NsaParams p, int n_items) {
 }
 
 // ---------------------------------------------------------------------------
-// dK / dV: one workgroup per (KV head, selected block); each wave owns 32 of
-// the block's keys.  The tokens that selected the block are walked in chunks
-// of 64 query rows (64 / G tokens x G heads): S = Q K^T, dP = dO V^T,
-// P = exp2(S*scale*log2e - LSE2), dS = P (dP - softmax_grad),
-// dV^T += dO^T P, dK^T += Q^T dS.
+// dK / dV.  The tokens that selected a (KV head, block) -- its reverse list --
+// are cut into segments of at most kSegEntries listings, so a block that
+// thousands of tokens selected is shared by many workgroups.  A workgroup
+// walks its segments' tokens in chunks of 64 query rows (64 / G tokens x G
+// heads); each wave owns 32 of the block's keys:
+//   S = Q K^T, dP = dO V^T, P = exp2(S*scale*log2e - LSE2),
+//   dS = P (dP - softmax_grad), dV^T += dO^T P, dK^T += Q^T dS,
+// and writes fp32 partial dK/dV of its segment.  A reduction kernel then sums
+// each block's segments in segment order: no atomics, a fixed summation
+// order, bit-identical reruns.
 // ---------------------------------------------------------------------------
+constexpr int kSegEntries = 256;
+
+int nsa_max_segments(long total_entries, long nblocks) {
+  return (int)(nblocks + (total_entries + kSegEntries - 1) / kSegEntries);
+}
+
+__global__ void nsa_seg_count(const int* rev_ptr, int nblocks, int* seg_cnt) {
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  if (r >= nblocks) return;
+  const int len = rev_ptr[r + 1] - rev_ptr[r];
+  seg_cnt[r] = max(1, (len + kSegEntries - 1) / kSegEntries);
+}
+
 template <class E, int NW>
-__global__ __launch_bounds__(NW * 64) void nsa_dkdv_kernel(NsaParams p, int n_items) {
+__global__ __launch_bounds__(NW * 64) void nsa_dkdv_seg_kernel(NsaParams p, const int* seg_off,
+                                                               int nblocks, float* part) {
   typedef typename E::T T;
   typedef typename E::V8 V8;
   constexpr int kTileB = 64 * kD * 2;
@@ -290,150 +311,201 @@ __global__ __launch_bounds__(NW * 64) void nsa_dkdv_kernel(NsaParams p, int n_it
   __shared__ float lds_lse[2][64];
   __shared__ float lds_dlt[2][64];
   __shared__ int lds_pos[2][64];
+  __shared__ int lds_tok[kSegEntries];  // the segment's token ids
 
-  const int item = xcd_remap(blockIdx.x, n_items);
-  if (item < 0) return;
   const NsaGeom& g = p.g;
-  const int n2 = item / g.NB, gb = item % g.NB;
-  const int b = seq_of_dev(g.blk_off, g.B, gb);
-  const int blk = gb - g.blk_off[b];
-  const int kv0 = g.cu_kv[b], q0 = g.cu_q[b];
-  const int skv = g.cu_kv[b + 1] - kv0;
-  const int sbs = g.sbs;
+  const int total = seg_off[nblocks];
+  // contiguous segment ranges per workgroup (XCD-remapped: an XCD's
+  // workgroups hold neighbouring segments, which share K/V and tokens)
+  const int w = xcd_remap(blockIdx.x, gridDim.x);
+  const int per = (total + gridDim.x - 1) / gridDim.x;
+  const int s_lo = w < 0 ? total : w * per;
+  const int s_hi = min(s_lo + per, total);
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5;
-  const int key_lo = blk * sbs;
-  const int key_hi = min((blk + 1) * sbs, skv);
-  const int mykey = key_lo + wid * 32 + l32;  // position in the sequence
-  const bool key_ok = mykey < key_hi;
   const int G = p.G;
-  const int tpc = 64 / G;                     // tokens per 64-row chunk
-
-  const long krow = ((long)(kv0 + mykey) * p.N2 + n2) * kD;
-  V8 kreg[8], vreg[8];
-#pragma unroll
-  for (int ds = 0; ds < 8; ds++) {
-    const long off = krow + ds * 16 + 8 * h;
-    kreg[ds] = key_ok ? as_v8<V8>(ld16((const T*)p.k + off)) : zero_v8<V8>();
-    vreg[ds] = key_ok ? as_v8<V8>(ld16((const T*)p.v + off)) : zero_v8<V8>();
-  }
-
-  const int rr = n2 * g.NB + gb;
-  const int e0 = p.rev_ptr[rr], e1 = p.rev_ptr[rr + 1];
-  const int nchunks = (e1 - e0 + tpc - 1) / tpc;
+  const int tpc = 64 / G;
+  const int sbs = g.sbs;
   const float sl2 = p.scale * kLog2e;
 
-  // chunk row r -> (token entry e0 + c*tpc + r/G, head r%G); rows past the
-  // chunk's tokens re-read its last valid row and are masked
-  auto row_of = [&](int c, int r) {
-    const int nt = min(tpc, e1 - e0 - c * tpc);
-    const int tk = min(r / G, nt - 1);
-    const int gg = (r / G < nt && r < tpc * G) ? r % G : G - 1;
-    const int t = p.rev[e0 + c * tpc + tk];
-    return (long)t * p.N1 + n2 * G + gg;
-  };
-  auto load_chunk = [&](int c, int buf) {
-    const int sub = lane >> 4, pc = lane & 15;
-#pragma unroll
-    for (int u = 0; u < 16 / NW; u++) {
-      const int inst = wid * (16 / NW) + u;
-      const int r = inst * 4 + sub;
-      const long qrw = row_of(c, r);
-      g2lds16((const char*)((const T*)p.q + qrw * kD) + ((pc ^ swz(r)) << 4), lds_q[buf] + inst * 1024);
-      g2lds16((const char*)((const T*)p.dout + qrw * kD) + ((pc ^ swz(r)) << 4),
-              lds_do[buf] + inst * 1024);
+  for (int sg = s_lo; sg < s_hi; sg++) {
+    // segment -> block (largest r with seg_off[r] <= sg)
+    int lo = 0, hi = nblocks - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (seg_off[mid] <= sg) lo = mid; else hi = mid - 1;
     }
-    if (wid == 0) {
-      const long qrw = row_of(c, lane);
-      g2lds4(p.lse + qrw, lds_lse[buf]);
-      g2lds4(p.delta + qrw, lds_dlt[buf]);
-      const int nt = min(tpc, e1 - e0 - c * tpc);
-      const bool valid = lane / G < nt && lane < tpc * G;
-      // position of the row's token, or -1 for padding rows (always masked)
-      lds_pos[buf][lane] = valid ? p.rev[e0 + c * tpc + lane / G] - q0 : -1;
-    }
-  };
+    const int r = lo;
+    const int k = sg - seg_off[r];
+    const int n2 = r / g.NB, gb = r % g.NB;
+    const int b = seq_of_dev(g.blk_off, g.B, gb);
+    const int blk = gb - g.blk_off[b];
+    const int kv0 = g.cu_kv[b], q0 = g.cu_q[b];
+    const int skv = g.cu_kv[b + 1] - kv0;
+    const int key_lo = blk * sbs;
+    const int key_hi = min((blk + 1) * sbs, skv);
+    const int mykey = key_lo + wid * 32 + l32;
+    const bool key_ok = mykey < key_hi;
+    const int e0 = p.rev_ptr[r] + k * kSegEntries;
+    const int e1 = min(e0 + kSegEntries, p.rev_ptr[r + 1]);
 
-  f32x16 dvt[4], dkt[4];
+    const long krow = ((long)(kv0 + min(mykey, key_hi - 1)) * p.N2 + n2) * kD;
+    V8 kreg[8], vreg[8];
 #pragma unroll
-  for (int dt = 0; dt < 4; dt++)
-#pragma unroll
-    for (int j = 0; j < 16; j++) dvt[dt][j] = dkt[dt][j] = 0.f;
-
-  if (nchunks > 0) load_chunk(0, 0);
-  wait_vm();
-  __syncthreads();
-  int buf = 0;
-  for (int c = 0; c < nchunks; c++) {
-    if (c + 1 < nchunks) load_chunk(c + 1, buf ^ 1);
-    const char* Qb = lds_q[buf];
-    const char* Db = lds_do[buf];
-    f32x16 s[2], dp[2];
-#pragma unroll
-    for (int qt = 0; qt < 2; qt++)
-#pragma unroll
-      for (int j = 0; j < 16; j++) s[qt][j] = dp[qt][j] = 0.f;
-#pragma unroll
-    for (int ds = 0; ds < 8; ds++)
-#pragma unroll
-      for (int qt = 0; qt < 2; qt++) {
-        s[qt] = E::mfma32(tile_read16<V8>(Qb, qt * 32 + l32, 2 * ds + h), kreg[ds], s[qt]);
-        dp[qt] = E::mfma32(tile_read16<V8>(Db, qt * 32 + l32, 2 * ds + h), vreg[ds], dp[qt]);
-      }
-#pragma unroll
-    for (int qt = 0; qt < 2; qt++)
-#pragma unroll
-      for (int j4 = 0; j4 < 4; j4++) {
-        const int rbase = qt * 32 + 8 * j4 + 4 * h;
-        const float4 lse4 = *reinterpret_cast<const float4*>(&lds_lse[buf][rbase]);
-        const float4 dl4 = *reinterpret_cast<const float4*>(&lds_dlt[buf][rbase]);
-        const int4 ps4 = *reinterpret_cast<const int4*>(&lds_pos[buf][rbase]);
-        const float lv[4] = {lse4.x, lse4.y, lse4.z, lse4.w};
-        const float dv[4] = {dl4.x, dl4.y, dl4.z, dl4.w};
-        const int pv4[4] = {ps4.x, ps4.y, ps4.z, ps4.w};
-#pragma unroll
-        for (int jj = 0; jj < 4; jj++) {
-          const int j = 4 * j4 + jj;
-          const bool ok = key_ok && pv4[jj] >= 0 && (!g.causal || mykey <= pv4[jj]);
-          const float pr = ok ? fast_exp2(s[qt][j] * sl2 - lv[jj] * kLog2e) : 0.f;
-          s[qt][j] = pr;
-          dp[qt][j] = pr * (dp[qt][j] - dv[jj]);
-        }
-      }
-#pragma unroll
-    for (int k4 = 0; k4 < 4; k4++) {
-      V8 bp, bd;
-#pragma unroll
-      for (int e = 0; e < 8; e++) {
-        bp[e] = E::from_f32(s[k4 >> 1][8 * (k4 & 1) + e]);
-        bd[e] = E::from_f32(dp[k4 >> 1][8 * (k4 & 1) + e]);
-      }
-#pragma unroll
-      for (int dt = 0; dt < 4; dt++) {
-        dvt[dt] = E::mfma32(tile_read_tr<V8>(Db, k4, dt), bp, dvt[dt]);
-        dkt[dt] = E::mfma32(tile_read_tr<V8>(Qb, k4, dt), bd, dkt[dt]);
-      }
+    for (int ds = 0; ds < 8; ds++) {
+      const long off = krow + ds * 16 + 8 * h;
+      kreg[ds] = key_ok ? as_v8<V8>(ld16((const T*)p.k + off)) : zero_v8<V8>();
+      vreg[ds] = key_ok ? as_v8<V8>(ld16((const T*)p.v + off)) : zero_v8<V8>();
     }
-    wait_vm();
+    const int nchunks = (e1 - e0 + tpc - 1) / tpc;
+    // the segment's token ids into LDS once, so chunk addresses need no
+    // dependent global load
+    for (int x = tid; x < e1 - e0; x += NW * 64) lds_tok[x] = p.rev[e0 + x];
     __syncthreads();
-    buf ^= 1;
-  }
 
-  if (key_ok) {
-    T* dkr = (T*)p.dk + krow;
-    T* dvr = (T*)p.dv + krow;
+    // chunk row r -> (entry c*tpc + r/G of the segment, head r%G); rows past
+    // the chunk's tokens re-read its last valid row and are masked
+    auto row_of = [&](int c, int rr) {
+      const int nt = min(tpc, e1 - e0 - c * tpc);
+      const int tk = min(rr / G, nt - 1);
+      const int gg = (rr / G < nt && rr < tpc * G) ? rr % G : G - 1;
+      const int t = lds_tok[c * tpc + tk];
+      return (long)t * p.N1 + n2 * G + gg;
+    };
+    auto load_chunk = [&](int c, int buf) {
+      const int sub = lane >> 4, pc = lane & 15;
+#pragma unroll
+      for (int u = 0; u < 16 / NW; u++) {
+        const int inst = wid * (16 / NW) + u;
+        const int rr = inst * 4 + sub;
+        const long qrw = row_of(c, rr);
+        g2lds16((const char*)((const T*)p.q + qrw * kD) + ((pc ^ swz(rr)) << 4),
+                lds_q[buf] + inst * 1024);
+        g2lds16((const char*)((const T*)p.dout + qrw * kD) + ((pc ^ swz(rr)) << 4),
+                lds_do[buf] + inst * 1024);
+      }
+      if (wid == 0) {
+        const long qrw = row_of(c, lane);
+        g2lds4(p.lse + qrw, lds_lse[buf]);
+        g2lds4(p.delta + qrw, lds_dlt[buf]);
+        const int nt = min(tpc, e1 - e0 - c * tpc);
+        const bool valid = lane / G < nt && lane < tpc * G;
+        // position of the row's token, or -1 for padding rows (always masked)
+        lds_pos[buf][lane] = valid ? lds_tok[c * tpc + lane / G] - q0 : -1;
+      }
+    };
+
+    f32x16 dvt[4], dkt[4];
 #pragma unroll
     for (int dt = 0; dt < 4; dt++)
 #pragma unroll
-      for (int jj = 0; jj < 4; jj++) {
-        const int d0 = dt * 32 + 8 * jj + 4 * h;
-        *reinterpret_cast<uint2*>(dkr + d0) =
-            pack4<E>(dkt[dt][4 * jj] * p.scale, dkt[dt][4 * jj + 1] * p.scale,
-                     dkt[dt][4 * jj + 2] * p.scale, dkt[dt][4 * jj + 3] * p.scale);
-        *reinterpret_cast<uint2*>(dvr + d0) =
-            pack4<E>(dvt[dt][4 * jj], dvt[dt][4 * jj + 1], dvt[dt][4 * jj + 2], dvt[dt][4 * jj + 3]);
+      for (int j = 0; j < 16; j++) dvt[dt][j] = dkt[dt][j] = 0.f;
+
+    if (nchunks > 0) load_chunk(0, 0);
+    wait_vm();
+    __syncthreads();
+    int buf = 0;
+    for (int c = 0; c < nchunks; c++) {
+      if (c + 1 < nchunks) load_chunk(c + 1, buf ^ 1);
+      const char* Qb = lds_q[buf];
+      const char* Db = lds_do[buf];
+#pragma unroll
+      for (int qt = 0; qt < 2; qt++) {
+        f32x16 sc, dp;
+#pragma unroll
+        for (int j = 0; j < 16; j++) sc[j] = dp[j] = 0.f;
+#pragma unroll
+        for (int ds = 0; ds < 8; ds++) {
+          sc = E::mfma32(tile_read16<V8>(Qb, qt * 32 + l32, 2 * ds + h), kreg[ds], sc);
+          dp = E::mfma32(tile_read16<V8>(Db, qt * 32 + l32, 2 * ds + h), vreg[ds], dp);
+        }
+        V8 bp[2], bd[2];
+#pragma unroll
+        for (int j4 = 0; j4 < 4; j4++) {
+          const int rbase = qt * 32 + 8 * j4 + 4 * h;
+          const float4 lse4 = *reinterpret_cast<const float4*>(&lds_lse[buf][rbase]);
+          const float4 dl4 = *reinterpret_cast<const float4*>(&lds_dlt[buf][rbase]);
+          const int4 ps4 = *reinterpret_cast<const int4*>(&lds_pos[buf][rbase]);
+          const float lv[4] = {lse4.x, lse4.y, lse4.z, lse4.w};
+          const float dv[4] = {dl4.x, dl4.y, dl4.z, dl4.w};
+          const int pv4[4] = {ps4.x, ps4.y, ps4.z, ps4.w};
+#pragma unroll
+          for (int jj = 0; jj < 4; jj++) {
+            const int j = 4 * j4 + jj;
+            // a valid row (pos >= 0) at or after this key (causal) keeps it
+            const int need = g.causal ? mykey : 0;
+            const bool ok = key_ok && pv4[jj] >= need;
+            float pr = fast_exp2(__builtin_fmaf(sc[j], sl2, -lv[jj] * kLog2e));
+            pr = ok ? pr : 0.f;
+            bp[j >> 3][j & 7] = E::from_f32(pr);
+            bd[j >> 3][j & 7] = E::from_f32(pr * (dp[j] - dv[jj]));
+          }
+        }
+#pragma unroll
+        for (int k2 = 0; k2 < 2; k2++)
+#pragma unroll
+          for (int dt = 0; dt < 4; dt++) {
+            dvt[dt] = E::mfma32(tile_read_tr<V8>(Db, qt * 2 + k2, dt), bp[k2], dvt[dt]);
+            dkt[dt] = E::mfma32(tile_read_tr<V8>(Qb, qt * 2 + k2, dt), bd[k2], dkt[dt]);
+          }
       }
+      wait_vm();
+      __syncthreads();
+      buf ^= 1;
+    }
+
+    // fp32 partials of this segment: [segment][key within block][d], dK then dV
+    if (key_ok) {
+      float* pk = part + ((long)sg * 2 * sbs + (mykey - key_lo)) * kD;
+      float* pv = pk + (long)sbs * kD;
+#pragma unroll
+      for (int dt = 0; dt < 4; dt++)
+#pragma unroll
+        for (int jj = 0; jj < 4; jj++) {
+          const int d0 = dt * 32 + 8 * jj + 4 * h;
+          *reinterpret_cast<float4*>(pk + d0) =
+              make_float4(dkt[dt][4 * jj], dkt[dt][4 * jj + 1], dkt[dt][4 * jj + 2], dkt[dt][4 * jj + 3]);
+          *reinterpret_cast<float4*>(pv + d0) =
+              make_float4(dvt[dt][4 * jj], dvt[dt][4 * jj + 1], dvt[dt][4 * jj + 2], dvt[dt][4 * jj + 3]);
+        }
+    }
+    __syncthreads();  // the next segment reuses the LDS buffers
   }
+}
+
+// dK = scale * sum of a block's segment partials, dV = their sum, in segment
+// order; one thread per (block, key, 4 columns).
+template <class E>
+__global__ __launch_bounds__(256) void nsa_dkdv_reduce(NsaParams p, const int* seg_off, int nblocks,
+                                                       const float* part) {
+  const NsaGeom& g = p.g;
+  const int sbs = g.sbs;
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  const long per_block = (long)sbs * (kD / 4);
+  if (i >= (long)nblocks * per_block) return;
+  const int r = (int)(i / per_block);
+  const int key = (int)(i % per_block) / (kD / 4);
+  const int d0 = 4 * ((int)(i % per_block) % (kD / 4));
+  const int n2 = r / g.NB, gb = r % g.NB;
+  const int b = seq_of_dev(g.blk_off, g.B, gb);
+  const int blk = gb - g.blk_off[b];
+  const int kv0 = g.cu_kv[b];
+  const int skv = g.cu_kv[b + 1] - kv0;
+  const int kpos = blk * sbs + key;
+  if (kpos >= skv) return;
+  float4 ak = make_float4(0.f, 0.f, 0.f, 0.f), av = ak;
+  for (int sg = seg_off[r]; sg < seg_off[r + 1]; sg++) {
+    const float* pk = part + ((long)sg * 2 * sbs + key) * kD + d0;
+    const float4 x = *reinterpret_cast<const float4*>(pk);
+    const float4 y = *reinterpret_cast<const float4*>(pk + (long)sbs * kD);
+    ak.x += x.x; ak.y += x.y; ak.z += x.z; ak.w += x.w;
+    av.x += y.x; av.y += y.y; av.z += y.z; av.w += y.w;
+  }
+  const long orow = ((long)(kv0 + kpos) * p.N2 + n2) * kD + d0;
+  typedef typename E::T T;
+  *reinterpret_cast<uint2*>((T*)p.dk + orow) =
+      pack4<E>(ak.x * p.scale, ak.y * p.scale, ak.z * p.scale, ak.w * p.scale);
+  *reinterpret_cast<uint2*>((T*)p.dv + orow) = pack4<E>(av.x, av.y, av.z, av.w);
 }
 
 template <class E>
@@ -464,15 +536,30 @@ static hipError_t bwd_t(const NsaParams& p, hipStream_t st, void* const* ev, int
   if (e == hipSuccess) e = mark_event(ev, n_ev, 2, 0, st);
   const int nb = p.N2 * p.g.NB;
   if (e == hipSuccess && nb > 0) {
+    // segment table: counts, then their exclusive scan (total at the end)
+    hipLaunchKernelGGL(nsa_seg_count, dim3((nb + 255) / 256), dim3(256), 0, st, p.rev_ptr, nb,
+                       p.seg_off);
+    e = exclusive_scan_total(p.seg_off, nb, p.seg_sums, st);
+  }
+  if (e == hipSuccess && nb > 0) {
     const int nw = (p.g.sbs + 31) / 32;  // 1..4 waves, 32 keys each
-    const dim3 grid(8 * ((nb + 7) / 8));
+    const int grid = 8 * ((std::min(p.max_segments, 2048) + 7) / 8);
     if (nw <= 1)
-      hipLaunchKernelGGL((nsa_dkdv_kernel<E, 1>), grid, dim3(64), 0, st, p, nb);
+      hipLaunchKernelGGL((nsa_dkdv_seg_kernel<E, 1>), dim3(grid), dim3(64), 0, st, p, p.seg_off, nb,
+                         p.part);
     else if (nw <= 2)
-      hipLaunchKernelGGL((nsa_dkdv_kernel<E, 2>), grid, dim3(128), 0, st, p, nb);
+      hipLaunchKernelGGL((nsa_dkdv_seg_kernel<E, 2>), dim3(grid), dim3(128), 0, st, p, p.seg_off,
+                         nb, p.part);
     else
-      hipLaunchKernelGGL((nsa_dkdv_kernel<E, 4>), grid, dim3(256), 0, st, p, nb);
+      hipLaunchKernelGGL((nsa_dkdv_seg_kernel<E, 4>), dim3(grid), dim3(256), 0, st, p, p.seg_off,
+                         nb, p.part);
     e = hipGetLastError();
+    if (e == hipSuccess) {
+      const long n = (long)nb * p.g.sbs * (kD / 4);
+      hipLaunchKernelGGL((nsa_dkdv_reduce<E>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                         p, p.seg_off, nb, (const float*)p.part);
+      e = hipGetLastError();
+    }
   }
   if (e == hipSuccess) e = mark_event(ev, n_ev, 2, 1, st);
   return e;

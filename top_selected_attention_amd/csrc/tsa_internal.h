@@ -15,6 +15,8 @@ inline hipError_t mark_event(void* const* ev, int n, int stage, int end, hipStre
 // ----- scans and lists -----------------------------------------------------
 int scan_sums_len(long n);
 hipError_t exclusive_scan(int* data, long n, int* sums, hipStream_t st);
+// Exclusive scan of data[0..n) in place, with the total written to data[n].
+hipError_t exclusive_scan_total(int* data, long n, int* sums, hipStream_t st);
 
 long bsa_compact_parts_len(int B, int N1, int N2, int QB, int KB);
 hipError_t launch_bsa_compact(const uint8_t* mask, int B, int N1, int N2, int QB, int KB,
@@ -79,7 +81,14 @@ struct NsaParams {
   NsaGeom g;
   int T, Tk, N1, N2, G, D;
   float scale;
+  // backward dK/dV segments (workspace)
+  int* seg_off;        // [N2*NB + 1] exclusive scan of segments per block
+  int* seg_sums;       // scan scratch
+  float* part;         // [max_segments][2][sbs][D] fp32 partial dK, dV
+  int max_segments;
 };
+
+int nsa_max_segments(long total_entries, long nblocks);
 
 hipError_t launch_nsa_fwd(const NsaParams& p, int fp16, hipStream_t st);
 hipError_t launch_nsa_bwd(const NsaParams& p, int fp16, hipStream_t st, void* const* ev, int n_ev);
