@@ -13,12 +13,14 @@
 // so one gathered 1 KB row feeds both the scores and P V.
 //
 // Split kernel: one workgroup per (decode token, split of its selected keys,
-// group of 64 query heads); 4 waves x 16 heads.  Selected rows are gathered 32
+// group of 64 query heads); 8 waves = 2 groups of 32 heads x 4 quarters of
+// the 512 output columns.  Selected rows are gathered 32
 // at a time by direct global -> LDS loads (a 1 KB key row per instruction,
-// plus its 128-byte rope row) into a double buffer.  On 16x16x32 MFMA, per
-// wave: S^T (32 keys x 16 heads) = K Q^T over 576 dims (Q^T held in
-// registers), online softmax along the keys (lanes own heads), and
-// O^T (512 x 16) += V^T P^T with V^T read from the same key tile by LDS
+// plus its 128-byte rope row) into a three-stage ring.  On 16x16x32 MFMA, per
+// wave: a partial S^T (32 keys x 32 heads) = K Q^T over its quarter of the
+// 576 dims (Q^T slice held in registers), the partials of a head group summed
+// through LDS, online softmax along the keys (lanes own heads), and
+// O^T (128 x 32) += V^T P^T with V^T read from the same key tile by LDS
 // transpose reads.  With one split the kernel writes the output; otherwise it
 // writes normalised fp32 partials and their base-2 LSE, and the combine kernel
 // merges them: LSE = logsumexp_s LSE_s, O = sum_s exp(LSE_s - LSE) O_s.
@@ -35,6 +37,7 @@ constexpr int kDr = 64;           // rope dim
 constexpr int kKeys = 32;         // keys per chunk
 constexpr int kMainB = kKeys * kDv * 2;   // 32 KB
 constexpr int kRopeB = kKeys * kDr * 2;   // 4 KB
+constexpr int kTab = 2048;                // slots resolved into LDS at a time
 
 // 1 KB rows (64 16-byte pieces): piece c of row r at c ^ swz1k(r).  16 rows
 // reading one piece hit 16 distinct bank groups, and transpose reads of 8
@@ -48,12 +51,15 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 }  // namespace
 
 template <class E>
-__global__ __launch_bounds__(256) void sfa_split_kernel(SfaParams p, int n_items, int hgroups,
+__global__ __launch_bounds__(512) void sfa_split_kernel(SfaParams p, int n_items, int hgroups,
                                                         int per_split) {
   typedef typename E::T T;
   typedef typename E::V8 V8;
-  __shared__ __attribute__((aligned(1024))) char lds_main[2][kMainB];
-  __shared__ __attribute__((aligned(1024))) char lds_rope[2][kRopeB];
+  constexpr int NS = 3;  // gather ring: chunks c+1, c+2 in flight while c computes
+  __shared__ __attribute__((aligned(1024))) char lds_main[NS][kMainB];
+  __shared__ __attribute__((aligned(1024))) char lds_rope[NS][kRopeB];
+  __shared__ __attribute__((aligned(16))) char lds_xs[8 * 4 * 64 * 16];  // partial score tiles
+  __shared__ int lds_tab[kTab];
 
   const int item = xcd_remap(blockIdx.x, n_items);
   if (item < 0) return;
@@ -64,179 +70,252 @@ __global__ __launch_bounds__(256) void sfa_split_kernel(SfaParams p, int n_items
   const int b = tk / p.Sq, s = tk % p.Sq;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
+  // wave = (32-head group h2, quarter qd): the quarter selects 128 of the 512
+  // output columns and a quarter of the 576-dim score contraction (main dims
+  // 128*qd .. +127, and rope dims 32*qd .. +31 for qd < 2); the four waves of
+  // a head group sum their partial scores in the same fixed order, so all
+  // four hold identical scores and softmax state.
+  const int h2 = wid & 1, qd = wid >> 1;
 
   const int kv_len = p.kv_lens[b];
   const int qpos = kv_len - p.Sq + s;
   const int total = p.topk_n * p.sbs;
   const int slot_lo = sp * per_split;
   const int slot_hi = min(slot_lo + per_split, total);
-  const int nchunks = slot_hi > slot_lo ? (slot_hi - slot_lo + kKeys - 1) / kKeys : 0;
 
-  const int head = hg * 64 + wid * 16 + l16;
-  const bool head_ok = head < p.N1;
+  const int hbase = hg * 64 + h2 * 32;  // heads hbase + 16*hh + l16, hh = 0, 1
   const int* topk = p.topk + (long)tk * p.topk_n;  // N2 = 1
   const int* btab = p.block_table + (long)b * p.max_pages;
   const float sl2 = p.scale * kLog2e;
 
-  // Q^T as the B operand: lane (g, head) holds d = 32*ks + 8*g .. +7
-  V8 qreg[18];
-  {
-    const T* qr = (const T*)p.q + ((long)tk * p.N1 + (head_ok ? head : 0)) * kDv;
-    const T* qrr = (const T*)p.q_rope + ((long)tk * p.N1 + (head_ok ? head : 0)) * kDr;
+  // Q^T slices as B operands: lane (g, head) holds dims 32*ks + 8*g .. +7
+  V8 qm[2][4], qrp[2];
 #pragma unroll
-    for (int ks = 0; ks < 16; ks++)
-      qreg[ks] = head_ok ? as_v8<V8>(ld16(qr + 32 * ks + 8 * g)) : zero_v8<V8>();
+  for (int hh = 0; hh < 2; hh++) {
+    const int head = hbase + 16 * hh + l16;
+    const bool ok = head < p.N1;
+    const T* qr = (const T*)p.q + ((long)tk * p.N1 + (ok ? head : 0)) * kDv + 128 * qd;
 #pragma unroll
-    for (int ks = 0; ks < 2; ks++)
-      qreg[16 + ks] = head_ok ? as_v8<V8>(ld16(qrr + 32 * ks + 8 * g)) : zero_v8<V8>();
+    for (int ks = 0; ks < 4; ks++)
+      qm[hh][ks] = ok ? as_v8<V8>(ld16(qr + 32 * ks + 8 * g)) : zero_v8<V8>();
+    const T* qrr = (const T*)p.q_rope + ((long)tk * p.N1 + (ok ? head : 0)) * kDr + 32 * (qd & 1);
+    qrp[hh] = ok && qd < 2 ? as_v8<V8>(ld16(qrr + 8 * g)) : zero_v8<V8>();
   }
 
-  // Row addresses of chunk c: lanes 0..31 resolve slot -> position -> page
-  // -> physical row; returns the validity mask (bit r = key r is kept).
-  // Invalid slots re-read the chunk's first valid row (finite data, P = 0).
-  auto resolve = [&](int c, int& rowidx) -> unsigned {
-    const int slot = slot_lo + c * kKeys + (lane & 31);
-    bool ok = lane < 32 && slot < slot_hi;
-    int pos = 0;
-    if (ok) {
-      const int id = topk[slot / p.sbs];
-      pos = id * p.sbs + slot % p.sbs;
-      ok = id >= 0 && pos < kv_len && (!p.causal || pos <= qpos);
+  // Physical cache rows of a run of up to kTab slots, resolved once into LDS
+  // (slot -> selected block id -> position -> page -> row; -1 = dropped), so
+  // the gather loop never waits on the index and page-table loads.
+  auto fill_table = [&](int seg_lo, int seg_n) {
+    constexpr int R = kTab / 512;
+    int id[R];
+#pragma unroll
+    for (int i = 0; i < R; i++) {
+      const int t = tid + 512 * i;
+      id[i] = t < seg_n ? topk[(seg_lo + t) / p.sbs] : -1;
     }
-    int lp = min(max(pos / p.page, 0), p.max_pages - 1);
-    int phys = ok ? min(max(btab[lp], 0), p.num_pages - 1) : 0;
-    rowidx = phys * p.page + (ok ? pos % p.page : 0);
-    const unsigned long long bal = __ballot(ok);
-    const unsigned mask = (unsigned)(bal & 0xffffffffull);
+    int lp[R], pos[R];
+    bool ok[R];
+#pragma unroll
+    for (int i = 0; i < R; i++) {
+      const int t = tid + 512 * i;
+      pos[i] = id[i] * p.sbs + (seg_lo + t) % p.sbs;
+      ok[i] = t < seg_n && id[i] >= 0 && pos[i] < kv_len && (!p.causal || pos[i] <= qpos);
+      lp[i] = ok[i] ? min(pos[i] / p.page, p.max_pages - 1) : 0;
+    }
+    int phys[R];
+#pragma unroll
+    for (int i = 0; i < R; i++) phys[i] = ok[i] ? btab[lp[i]] : 0;
+#pragma unroll
+    for (int i = 0; i < R; i++) {
+      const int t = tid + 512 * i;
+      if (t < kTab)
+        lds_tab[t] = ok[i] ? min(max(phys[i], 0), p.num_pages - 1) * p.page + pos[i] % p.page : -1;
+    }
+  };
+  // Row of key (lane & 31) of chunk c of the table and the chunk's validity
+  // mask (bit r = key r kept).  Dropped keys re-read the chunk's first kept
+  // row (finite data, P = 0).
+  auto chunk_rows = [&](int c, int seg_n, int& rowidx) -> unsigned {
+    const int t = c * kKeys + (lane & 31);
+    const int r = t < seg_n ? lds_tab[t] : -1;
+    const bool ok = lane < 32 && r >= 0;
+    const unsigned mask = (unsigned)(__ballot(ok) & 0xffffffffull);
     const int first = mask ? __builtin_ctz(mask) : 0;
-    const int frow = __shfl(rowidx, first);
-    if (!ok) rowidx = frow;
+    const int frow = __shfl(r, first);
+    rowidx = ok ? r : max(frow, 0);
     return mask;
   };
+  // 8 waves x 4 one-KB key rows, and waves 0..3 one 1-KB slice of 8 rope rows
   auto load_chunk = [&](int rowidx, int buf) {
     const char* kc = (const char*)p.kc;
     const char* krc = (const char*)p.krc;
 #pragma unroll
-    for (int u = 0; u < 8; u++) {
-      const int r = wid * 8 + u;                 // one 1 KB row per instruction
+    for (int u = 0; u < 4; u++) {
+      const int r = wid * 4 + u;
       const int ri = __shfl(rowidx, r);
-      g2lds16(kc + (long)ri * (kDv * 2) + ((lane ^ swz1k(r)) << 4), lds_main[buf] + r * 1024);
+      g2lds16_async(kc + (long)ri * (kDv * 2) + ((lane ^ swz1k(r)) << 4), lds_main[buf] + r * 1024);
     }
-    {
-      const int r = wid * 8 + (lane >> 3);        // 8 rope rows per instruction
+    if (wid < 4) {
+      const int r = wid * 8 + (lane >> 3);
       const int ri = __shfl(rowidx, r);
-      g2lds16(krc + (long)ri * (kDr * 2) + (((lane & 7) ^ swzr(r)) << 4),
-              lds_rope[buf] + wid * 1024);
+      g2lds16_async(krc + (long)ri * (kDr * 2) + (((lane & 7) ^ swzr(r)) << 4), lds_rope[buf] + wid * 1024);
     }
   };
+  // wait until only the newest NS - 2 chunks' loads (4 key rows, plus a rope
+  // slice for waves 0..3, per chunk) are in flight
+  auto wait_keep_newest = [&]() {
+    if (wid < 4) wait_vm_le<5 * (NS - 2)>(); else wait_vm_le<4 * (NS - 2)>();
+  };
 
-  float m = -INFINITY, lsum = 0.f;
-  f32x4_t o[32];
+  constexpr float kLazy = 8.f;
+  float m[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
+  f32x4_t o[8][2];  // O^T tiles: rows d = 128*qd + 16*dt + 4*g + j, column head 16*hh + l16
 #pragma unroll
-  for (int dt = 0; dt < 32; dt++) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int dt = 0; dt < 8; dt++)
+#pragma unroll
+    for (int hh = 0; hh < 2; hh++) o[dt][hh] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  int rowidx;
-  unsigned mask_cur = 0, mask_next = 0;
-  if (nchunks > 0) {
-    mask_cur = resolve(0, rowidx);
-    load_chunk(rowidx, 0);
-  }
-  wait_vm();
-  __syncthreads();
-  int buf = 0;
-  for (int c = 0; c < nchunks; c++) {
-    if (c + 1 < nchunks) {
-      mask_next = resolve(c + 1, rowidx);
-      load_chunk(rowidx, buf ^ 1);
-    }
-    if (mask_cur) {
-      const char* Mt = lds_main[buf];
-      const char* Rt = lds_rope[buf];
-      f32x4_t st[2];
-#pragma unroll
-      for (int kt = 0; kt < 2; kt++) {
-        st[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        const int r = kt * 16 + l16;
-#pragma unroll
-        for (int ks = 0; ks < 16; ks++) {
-          const int c16 = 4 * ks + g;
-          const V8 a = lds_read16<V8>(Mt + r * 1024 + ((c16 ^ swz1k(r)) << 4));
-          st[kt] = E::mfma16(a, qreg[ks], st[kt]);
-        }
-#pragma unroll
-        for (int ks = 0; ks < 2; ks++) {
-          const int c8 = 4 * ks + g;
-          const V8 a = lds_read16<V8>(Rt + r * 128 + ((c8 ^ swzr(r)) << 4));
-          st[kt] = E::mfma16(a, qreg[16 + ks], st[kt]);
-        }
-      }
-      // element j of tile kt is key kt*16 + 4*g + j, column = this lane's head
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < 2; kt++)
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-          const int key = kt * 16 + 4 * g + j;
-          const float v = ((mask_cur >> key) & 1u) ? st[kt][j] * sl2 : -INFINITY;
-          st[kt][j] = v;
-          mx = fmaxf(mx, v);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m, mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = fast_exp2(m - m_use);
-      m = m_new;
-      lsum *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < 32; dt++) o[dt] *= alpha;
-      V8 pb;
-#pragma unroll
-      for (int kt = 0; kt < 2; kt++)
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-          const float pv = fast_exp2(st[kt][j] - m_use);
-          lsum += pv;
-          pb[4 * kt + j] = E::from_f32(pv);
-        }
-      // O^T += V^T P^T: V^T rows d = 16*dt + l16, keys {4g..4g+3, 16+4g..16+4g+3}
-      const int r0 = 4 * g + (l16 >> 2), r1 = r0 + 16;
-      const int cq = l16 & 3;
-#pragma unroll
-      for (int dt = 0; dt < 32; dt++) {
-        const int c16 = 2 * dt + (cq >> 1);
-        const int b8 = 8 * (cq & 1);
-        const V8 a = lds_read_tr_pair<V8>(Mt + r0 * 1024 + ((c16 ^ swz1k(r0)) << 4) + b8,
-                                          Mt + r1 * 1024 + ((c16 ^ swz1k(r1)) << 4) + b8);
-        o[dt] = E::mfma16(a, pb, o[dt]);
-      }
-    }
-    wait_vm();
+  for (int seg_lo = slot_lo; seg_lo < slot_hi; seg_lo += kTab) {
+    const int seg_n = min(kTab, slot_hi - seg_lo);
+    const int nchunks = (seg_n + kKeys - 1) / kKeys;
+    __syncthreads();  // the previous segment's table and tiles are no longer read
+    fill_table(seg_lo, seg_n);
     __syncthreads();
-    buf ^= 1;
-    mask_cur = mask_next;
+    int rowidx;
+#pragma unroll
+    for (int c = 0; c < NS - 1; c++)
+      if (c < nchunks) {
+        chunk_rows(c, seg_n, rowidx);
+        load_chunk(rowidx, c);
+      }
+    if (nchunks >= NS - 1) wait_keep_newest(); else wait_vm();
+    __syncthreads();
+    int buf = 0;
+    for (int c = 0; c < nchunks; c++) {
+      const bool issue = c + NS - 1 < nchunks;
+      if (issue) {
+        chunk_rows(c + NS - 1, seg_n, rowidx);
+        load_chunk(rowidx, buf == 0 ? NS - 1 : buf - 1);  // (buf + NS - 1) % NS
+      }
+      int unused;
+      const unsigned mcur = chunk_rows(c, seg_n, unused);
+      // uniform across the workgroup: every wave reads the same table entries
+      if (mcur) {
+        const char* Mt = lds_main[buf];
+        const char* Rt = lds_rope[buf];
+        // partial S^T tiles (16 keys x 16 heads) over this wave's quarter:
+        // element j of st[kt][hh] is key 16*kt + 4*g + j, head 16*hh + l16
+        f32x4_t st[2][2];
+#pragma unroll
+        for (int kt = 0; kt < 2; kt++) {
+          st[kt][0] = st[kt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          const int r = kt * 16 + l16;
+#pragma unroll
+          for (int ks = 0; ks < 4; ks++) {
+            const int c16 = 16 * qd + 4 * ks + g;  // 16-byte piece of dims 128*qd + 32*ks + 8*g
+            const V8 a = lds_read16<V8>(Mt + r * 1024 + ((c16 ^ swz1k(r)) << 4));
+            st[kt][0] = E::mfma16(a, qm[0][ks], st[kt][0]);
+            st[kt][1] = E::mfma16(a, qm[1][ks], st[kt][1]);
+          }
+          if (qd < 2) {
+            const int c8 = 4 * qd + g;
+            const V8 a = lds_read16<V8>(Rt + r * 128 + ((c8 ^ swzr(r)) << 4));
+            st[kt][0] = E::mfma16(a, qrp[0], st[kt][0]);
+            st[kt][1] = E::mfma16(a, qrp[1], st[kt][1]);
+          }
+        }
+        char* xs = lds_xs + lane * 16;
+#pragma unroll
+        for (int t = 0; t < 4; t++)
+          *reinterpret_cast<f32x4_t*>(xs + (wid * 4 + t) * 1024) = st[t >> 1][t & 1];
+        __syncthreads();
+        // S = ((p0 + p1) + p2) + p3 over the head group's quarters, in that order
+#pragma unroll
+        for (int t = 0; t < 4; t++) {
+          f32x4_t acc = *reinterpret_cast<const f32x4_t*>(xs + (h2 * 4 + t) * 1024);
+#pragma unroll
+          for (int q = 1; q < 4; q++)
+            acc += *reinterpret_cast<const f32x4_t*>(xs + ((2 * q + h2) * 4 + t) * 1024);
+          st[t >> 1][t & 1] = acc;
+        }
+        V8 pb[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; hh++) {
+          float mx = -INFINITY;
+#pragma unroll
+          for (int kt = 0; kt < 2; kt++)
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+              const int key = kt * 16 + 4 * g + j;
+              const float v = ((mcur >> key) & 1u) ? st[kt][hh][j] : -INFINITY;
+              st[kt][hh][j] = v;
+              mx = fmaxf(mx, v);
+            }
+          mx = fmaxf(mx, __shfl_xor(mx, 16));
+          mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+          if (__builtin_amdgcn_ballot_w64(mx > m[hh] + kLazy)) {
+            const float m_new = fmaxf(m[hh], mx);
+            const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m[hh] - m_new);
+            m[hh] = m_new;
+            lsum[hh] *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < 8; dt++) o[dt][hh] *= alpha;
+          }
+          const float mneg = m[hh] == -INFINITY ? 0.f : -m[hh];
+#pragma unroll
+          for (int kt = 0; kt < 2; kt++)
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+              const float pv = fast_exp2(__builtin_fmaf(st[kt][hh][j], sl2, mneg));
+              lsum[hh] += pv;
+              pb[hh][4 * kt + j] = E::from_f32(pv);
+            }
+        }
+        // O^T += V^T P^T: V^T rows d = 128*qd + 16*dt + l16, keys
+        // {4g..4g+3, 16+4g..16+4g+3} (the key order of pb)
+        const int r0 = 4 * g + (l16 >> 2), r1 = r0 + 16;
+        const int cq = l16 & 3;
+#pragma unroll
+        for (int dt = 0; dt < 8; dt++) {
+          const int c16 = 16 * qd + 2 * dt + (cq >> 1);
+          const int b8 = 8 * (cq & 1);
+          const V8 a = lds_read_tr_pair<V8>(Mt + r0 * 1024 + ((c16 ^ swz1k(r0)) << 4) + b8,
+                                            Mt + r1 * 1024 + ((c16 ^ swz1k(r1)) << 4) + b8);
+          o[dt][0] = E::mfma16(a, pb[0], o[dt][0]);
+          o[dt][1] = E::mfma16(a, pb[1], o[dt][1]);
+        }
+      }
+      if (issue) wait_keep_newest(); else wait_vm();
+      __syncthreads();
+      buf = buf == NS - 1 ? 0 : buf + 1;
+    }
   }
 
-  float lt = lsum + __shfl_xor(lsum, 16);
-  lt += __shfl_xor(lt, 32);
-  if (!head_ok) return;
-  const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  // element j of o[dt] is d = 16*dt + 4*g + j
-  if (p.splits == 1) {
-    T* orow = (T*)p.out + ((long)tk * p.N1 + head) * kDv;
 #pragma unroll
-    for (int dt = 0; dt < 32; dt++)
-      *reinterpret_cast<uint2*>(orow + 16 * dt + 4 * g) =
-          pack4<E>(o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv);
-    if (g == 0 && p.lse) p.lse[(long)tk * p.N1 + head] = lt > 0.f ? (m + log2f(lt)) * kLn2 : -INFINITY;
-  } else {
-    const long pr = ((long)tk * p.splits + sp) * p.N1 + head;
-    float* po = p.part_o + pr * kDv;
+  for (int hh = 0; hh < 2; hh++) {
+    const int head = hbase + 16 * hh + l16;
+    float lt = lsum[hh] + __shfl_xor(lsum[hh], 16);
+    lt += __shfl_xor(lt, 32);
+    if (head >= p.N1) continue;
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    // element j of o[dt][hh] is d = 128*qd + 16*dt + 4*g + j
+    if (p.splits == 1) {
+      T* orow = (T*)p.out + ((long)tk * p.N1 + head) * kDv + 128 * qd;
 #pragma unroll
-    for (int dt = 0; dt < 32; dt++)
-      *reinterpret_cast<float4*>(po + 16 * dt + 4 * g) =
-          make_float4(o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv);
-    if (g == 0) p.part_lse[pr] = lt > 0.f ? m + log2f(lt) : -INFINITY;
+      for (int dt = 0; dt < 8; dt++)
+        *reinterpret_cast<uint2*>(orow + 16 * dt + 4 * g) =
+            pack4<E>(o[dt][hh][0] * inv, o[dt][hh][1] * inv, o[dt][hh][2] * inv, o[dt][hh][3] * inv);
+      if (g == 0 && qd == 0 && p.lse)
+        p.lse[(long)tk * p.N1 + head] = lt > 0.f ? (m[hh] + log2f(lt)) * kLn2 : -INFINITY;
+    } else {
+      const long pr = ((long)tk * p.splits + sp) * p.N1 + head;
+      float* po = p.part_o + pr * kDv + 128 * qd;
+#pragma unroll
+      for (int dt = 0; dt < 8; dt++)
+        *reinterpret_cast<float4*>(po + 16 * dt + 4 * g) =
+            make_float4(o[dt][hh][0] * inv, o[dt][hh][1] * inv, o[dt][hh][2] * inv, o[dt][hh][3] * inv);
+      if (g == 0 && qd == 0) p.part_lse[pr] = lt > 0.f ? m[hh] + log2f(lt) : -INFINITY;
+    }
   }
 }
 
@@ -301,8 +380,8 @@ int sfa_splits(const SfaParams& p) {
   const long wgs = tokens * hgroups;
   const int total = p.topk_n * p.sbs;
   if (wgs == 0) return 1;
-  // aim for >= 512 workgroups (two per CU), at least 4 chunks per split
-  long s = (512 + wgs - 1) / wgs;
+  // aim for >= 256 workgroups (one resident per CU), at least 4 chunks per split
+  long s = (256 + wgs - 1) / wgs;
   const long max_s = (total + 4 * kKeys - 1) / (4 * kKeys);
   if (s > max_s) s = max_s;
   if (s < 1) s = 1;
@@ -326,7 +405,7 @@ static hipError_t sfa_t(const SfaParams& p, hipStream_t st, void* const* ev, int
   const long n_items = tokens * p.splits * hgroups;
   hipError_t e = mark_event(ev, n_ev, 0, 0, st);
   if (e == hipSuccess) {
-    hipLaunchKernelGGL((sfa_split_kernel<E>), dim3((unsigned)(8 * ((n_items + 7) / 8))), dim3(256),
+    hipLaunchKernelGGL((sfa_split_kernel<E>), dim3((unsigned)(8 * ((n_items + 7) / 8))), dim3(512),
                        0, st, p, (int)n_items, hgroups, per_split);
     e = hipGetLastError();
   }

@@ -135,6 +135,24 @@ __device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
 __device__ __forceinline__ void g2lds16(const void* g, void* lds_base) {
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
 }
+// g2lds16 issued from inline assembly, so the compiler's wait-count pass does
+// not see an LDS write in flight: it then places no "wait for every vector
+// load" before later LDS reads, and a ring of several stages can stay in
+// flight across the reads of an older stage.  The caller owns the ordering:
+// an explicit vmcnt wait plus a barrier before any wave reads the bytes, and
+// before the buffer is filled again.  M0 is saved and restored around the
+// load (the address is read when the instruction issues).
+__device__ __forceinline__ void g2lds16_async(const void* g, void* lds_base) {
+  const unsigned l = __builtin_amdgcn_readfirstlane(
+      (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)lds_base);
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0\n\ts_nop 0"
+      : "=&s"(saved)
+      : "v"(g), "s"(l)
+      : "memory");
+}
 // Same with 4 bytes per lane (lane l's dword lands at lds_base + 4*l).
 __device__ __forceinline__ void g2lds4(const void* g, void* lds_base) {
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_base, 4, 0, 0);
