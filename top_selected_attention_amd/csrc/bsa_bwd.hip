@@ -89,12 +89,13 @@ __global__ __launch_bounds__(NW * 64) void bsa_dq_kernel(BsaParams p, int qsub, 
   }
 
   const int e0 = p.row_ptr[bn * p.QB + qb], e1 = p.row_ptr[bn * p.QB + qb + 1];
+  ListWindow colw(p.col, e0, e1);
   const int cpb = (p.bkv + 63) / 64;
   const int nchunks = (e1 - e0) * cpb;
   const float sl2 = p.scale * kLog2e;
 
   auto chunk_range = [&](int i, int& ks, int& ke) {
-    const int kb = p.col[e0 + i / cpb];
+    const int kb = colw(e0 + i / cpb);
     ks = kb * p.bkv + (i % cpb) * 64;
     ke = min(min(ks + 64, (kb + 1) * p.bkv), p.Skv);
   };
@@ -266,13 +267,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 
   const int c = bh * p.KB + kb;
   const int e0 = p.rev_ptr[c], e1 = p.rev_ptr[c + 1];
+  ListWindow revw(p.rev, e0, e1);
   const int cpq = (p.bq + kQC - 1) / kQC;
   const int nchunks = (e1 - e0) * cpq;
   const float sl2 = p.scale * kLog2e;
 
   // Chunk i: query rows [qs, qe) of query head n1 (entry id g*QB + qb).
   auto chunk_range = [&](int i, int& n1, int& qs, int& qe) {
-    const int id = p.rev[e0 + i / cpq];
+    const int id = revw(e0 + i / cpq);
     const int g = id / p.QB, qb = id % p.QB;
     n1 = n2 * p.G + g;
     qs = qb * p.bq + (i % cpq) * kQC;

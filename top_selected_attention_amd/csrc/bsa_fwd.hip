@@ -64,6 +64,7 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_kernel(BsaParams p, int qsub,
 
   const int tile_row = bn * p.QB + qb;
   const int e0 = p.row_ptr[tile_row], e1 = p.row_ptr[tile_row + 1];
+  ListWindow colw(p.col, e0, e1);
   const int cpb = (p.bkv + kKC - 1) / kKC;
   const int nchunks = (e1 - e0) * cpb;
   const float sl2 = p.scale * kLog2e;
@@ -72,7 +73,7 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_kernel(BsaParams p, int qsub,
   // are empty (ragged tail) or wholly after the slice's last row under causal
   // mode are skipped; the test is uniform across the workgroup.
   auto chunk_range = [&](int i, int& ks, int& ke) {
-    const int kb = p.col[e0 + i / cpb];
+    const int kb = colw(e0 + i / cpb);
     ks = kb * p.bkv + (i % cpb) * kKC;
     ke = min(min(ks + kKC, (kb + 1) * p.bkv), p.Skv);
   };

@@ -82,6 +82,7 @@ __global__ __launch_bounds__(256) void nsa_fwd_kernel(NsaParams p, int n_items) 
 
   const long row = (long)t * p.N2 + n2;
   const int e0 = p.row_ptr[row], e1 = p.row_ptr[row + 1];
+  ListWindow colw(p.col, e0, e1);
   const int sbs = g.sbs;
   const int cpb = (sbs + kChunk - 1) / kChunk;
   const int nchunks = (e1 - e0) * cpb;
@@ -98,7 +99,7 @@ __global__ __launch_bounds__(256) void nsa_fwd_kernel(NsaParams p, int n_items) 
     for (int j = 0; j < 16; j++) o[dt][j] = 0.f;
 
   for (int i = 0; i < nchunks; i++) {
-    const int blk = p.col[e0 + i / cpb];
+    const int blk = colw(e0 + i / cpb);
     const int ks = blk * sbs + (i % cpb) * kChunk;     // key position in the sequence
     const int ke = min(ks + kChunk, (blk + 1) * sbs);
     if (g.causal && ks > pos) continue;                // wholly after the token
@@ -211,6 +212,7 @@ __global__ __launch_bounds__(256) void nsa_dq_kernel(NsaParams p, int n_items) {
 
   const long row = (long)t * p.N2 + n2;
   const int e0 = p.row_ptr[row], e1 = p.row_ptr[row + 1];
+  ListWindow colw(p.col, e0, e1);
   const int sbs = g.sbs;
   const int cpb = (sbs + kChunk - 1) / kChunk;
   const int nchunks = (e1 - e0) * cpb;
@@ -226,7 +228,7 @@ __global__ __launch_bounds__(256) void nsa_dq_kernel(NsaParams p, int n_items) {
     for (int j = 0; j < 16; j++) dq[dt][j] = 0.f;
 
   for (int i = 0; i < nchunks; i++) {
-    const int blk = p.col[e0 + i / cpb];
+    const int blk = colw(e0 + i / cpb);
     const int ks = blk * sbs + (i % cpb) * kChunk;
     const int ke = min(ks + kChunk, (blk + 1) * sbs);
     if (g.causal && ks > pos) continue;

@@ -59,7 +59,8 @@ __global__ __launch_bounds__(512) void sfa_split_kernel(SfaParams p, int n_items
   __shared__ __attribute__((aligned(1024))) char lds_main[NS][kMainB];
   __shared__ __attribute__((aligned(1024))) char lds_rope[NS][kRopeB];
   __shared__ __attribute__((aligned(16))) char lds_xs[8 * 4 * 64 * 16];  // partial score tiles
-  __shared__ int lds_tab[kTab];
+  __shared__ __attribute__((aligned(16))) int lds_tab[kTab];
+  __shared__ unsigned lds_cmask[kTab / kKeys];
 
   const int item = xcd_remap(blockIdx.x, n_items);
   if (item < 0) return;
@@ -68,7 +69,8 @@ __global__ __launch_bounds__(512) void sfa_split_kernel(SfaParams p, int n_items
   const int sp = (item / hgroups) % p.splits;
   const int tk = item / (hgroups * p.splits);
   const int b = tk / p.Sq, s = tk % p.Sq;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
   // wave = (32-head group h2, quarter qd): the quarter selects 128 of the 512
   // output columns and a quarter of the 576-dim score contraction (main dims
@@ -103,8 +105,11 @@ __global__ __launch_bounds__(512) void sfa_split_kernel(SfaParams p, int n_items
   }
 
   // Physical cache rows of a run of up to kTab slots, resolved once into LDS
-  // (slot -> selected block id -> position -> page -> row; -1 = dropped), so
-  // the gather loop never waits on the index and page-table loads.
+  // (slot -> selected block id -> position -> page -> row), with one
+  // validity mask per 32-slot chunk (bit r = key r kept), so the gather loop
+  // never waits on index or page-table loads.  A dropped slot holds its
+  // chunk's first kept row (finite data, P = 0), or row 0 in a chunk with
+  // none (never read: such chunks are skipped).
   auto fill_table = [&](int seg_lo, int seg_n) {
     constexpr int R = kTab / 512;
     int id[R];
@@ -127,38 +132,32 @@ __global__ __launch_bounds__(512) void sfa_split_kernel(SfaParams p, int n_items
     for (int i = 0; i < R; i++) phys[i] = ok[i] ? btab[lp[i]] : 0;
 #pragma unroll
     for (int i = 0; i < R; i++) {
-      const int t = tid + 512 * i;
-      if (t < kTab)
-        lds_tab[t] = ok[i] ? min(max(phys[i], 0), p.num_pages - 1) * p.page + pos[i] % p.page : -1;
+      const int t = tid + 512 * i;  // lanes 0..31 and 32..63 each cover one chunk
+      const int row = ok[i] ? min(max(phys[i], 0), p.num_pages - 1) * p.page + pos[i] % p.page : 0;
+      const unsigned long long bal = __ballot(ok[i]);
+      const unsigned half = lane < 32 ? (unsigned)bal : (unsigned)(bal >> 32);
+      const int first = (half ? __builtin_ctz(half) : 0) + (lane & 32);
+      const int frow = __shfl(row, first);
+      lds_tab[t] = ok[i] ? row : (half ? frow : 0);
+      if ((lane & 31) == 0) lds_cmask[t >> 5] = half;
     }
   };
-  // Row of key (lane & 31) of chunk c of the table and the chunk's validity
-  // mask (bit r = key r kept).  Dropped keys re-read the chunk's first kept
-  // row (finite data, P = 0).
-  auto chunk_rows = [&](int c, int seg_n, int& rowidx) -> unsigned {
-    const int t = c * kKeys + (lane & 31);
-    const int r = t < seg_n ? lds_tab[t] : -1;
-    const bool ok = lane < 32 && r >= 0;
-    const unsigned mask = (unsigned)(__ballot(ok) & 0xffffffffull);
-    const int first = mask ? __builtin_ctz(mask) : 0;
-    const int frow = __shfl(r, first);
-    rowidx = ok ? r : max(frow, 0);
-    return mask;
-  };
   // 8 waves x 4 one-KB key rows, and waves 0..3 one 1-KB slice of 8 rope rows
-  auto load_chunk = [&](int rowidx, int buf) {
+  auto load_chunk = [&](int c, int buf) {
     const char* kc = (const char*)p.kc;
     const char* krc = (const char*)p.krc;
+    const int* tb = lds_tab + c * kKeys;
+    const int4 rm = *reinterpret_cast<const int4*>(tb + wid * 4);  // same for all lanes
+    const int rms[4] = {rm.x, rm.y, rm.z, rm.w};
 #pragma unroll
     for (int u = 0; u < 4; u++) {
       const int r = wid * 4 + u;
-      const int ri = __shfl(rowidx, r);
-      g2lds16_async(kc + (long)ri * (kDv * 2) + ((lane ^ swz1k(r)) << 4), lds_main[buf] + r * 1024);
+      g2lds16(kc + (long)rms[u] * (kDv * 2) + ((lane ^ swz1k(r)) << 4), lds_main[buf] + r * 1024);
     }
     if (wid < 4) {
       const int r = wid * 8 + (lane >> 3);
-      const int ri = __shfl(rowidx, r);
-      g2lds16_async(krc + (long)ri * (kDr * 2) + (((lane & 7) ^ swzr(r)) << 4), lds_rope[buf] + wid * 1024);
+      g2lds16(krc + (long)tb[r] * (kDr * 2) + (((lane & 7) ^ swzr(r)) << 4),
+                    lds_rope[buf] + wid * 1024);
     }
   };
   // wait until only the newest NS - 2 chunks' loads (4 key rows, plus a rope
@@ -181,47 +180,45 @@ __global__ __launch_bounds__(512) void sfa_split_kernel(SfaParams p, int n_items
     __syncthreads();  // the previous segment's table and tiles are no longer read
     fill_table(seg_lo, seg_n);
     __syncthreads();
-    int rowidx;
 #pragma unroll
     for (int c = 0; c < NS - 1; c++)
-      if (c < nchunks) {
-        chunk_rows(c, seg_n, rowidx);
-        load_chunk(rowidx, c);
-      }
+      if (c < nchunks) load_chunk(c, c);
     if (nchunks >= NS - 1) wait_keep_newest(); else wait_vm();
     __syncthreads();
     int buf = 0;
     for (int c = 0; c < nchunks; c++) {
       const bool issue = c + NS - 1 < nchunks;
-      if (issue) {
-        chunk_rows(c + NS - 1, seg_n, rowidx);
-        load_chunk(rowidx, buf == 0 ? NS - 1 : buf - 1);  // (buf + NS - 1) % NS
-      }
-      int unused;
-      const unsigned mcur = chunk_rows(c, seg_n, unused);
-      // uniform across the workgroup: every wave reads the same table entries
+      if (issue) load_chunk(c + NS - 1, buf == 0 ? NS - 1 : buf - 1);  // (buf + NS - 1) % NS
+      // the same for every wave of the workgroup
+      const unsigned mcur = __builtin_amdgcn_readfirstlane(lds_cmask[c]);
       if (mcur) {
         const char* Mt = lds_main[buf];
         const char* Rt = lds_rope[buf];
         // partial S^T tiles (16 keys x 16 heads) over this wave's quarter:
         // element j of st[kt][hh] is key 16*kt + 4*g + j, head 16*hh + l16
         f32x4_t st[2][2];
+        V8 ka[2][5];  // all A operands of the chunk's scores, read before the MFMAs
 #pragma unroll
         for (int kt = 0; kt < 2; kt++) {
-          st[kt][0] = st[kt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
           const int r = kt * 16 + l16;
 #pragma unroll
           for (int ks = 0; ks < 4; ks++) {
             const int c16 = 16 * qd + 4 * ks + g;  // 16-byte piece of dims 128*qd + 32*ks + 8*g
-            const V8 a = lds_read16<V8>(Mt + r * 1024 + ((c16 ^ swz1k(r)) << 4));
-            st[kt][0] = E::mfma16(a, qm[0][ks], st[kt][0]);
-            st[kt][1] = E::mfma16(a, qm[1][ks], st[kt][1]);
+            ka[kt][ks] = lds_read16<V8>(Mt + r * 1024 + ((c16 ^ swz1k(r)) << 4));
+          }
+          if (qd < 2) ka[kt][4] = lds_read16<V8>(Rt + r * 128 + (((4 * qd + g) ^ swzr(r)) << 4));
+        }
+#pragma unroll
+        for (int kt = 0; kt < 2; kt++) {
+          st[kt][0] = st[kt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < 4; ks++) {
+            st[kt][0] = E::mfma16(ka[kt][ks], qm[0][ks], st[kt][0]);
+            st[kt][1] = E::mfma16(ka[kt][ks], qm[1][ks], st[kt][1]);
           }
           if (qd < 2) {
-            const int c8 = 4 * qd + g;
-            const V8 a = lds_read16<V8>(Rt + r * 128 + ((c8 ^ swzr(r)) << 4));
-            st[kt][0] = E::mfma16(a, qrp[0], st[kt][0]);
-            st[kt][1] = E::mfma16(a, qrp[1], st[kt][1]);
+            st[kt][0] = E::mfma16(ka[kt][4], qrp[0], st[kt][0]);
+            st[kt][1] = E::mfma16(ka[kt][4], qrp[1], st[kt][1]);
           }
         }
         char* xs = lds_xs + lane * 16;
@@ -251,8 +248,7 @@ __global__ __launch_bounds__(512) void sfa_split_kernel(SfaParams p, int n_items
               st[kt][hh][j] = v;
               mx = fmaxf(mx, v);
             }
-          mx = fmaxf(mx, __shfl_xor(mx, 16));
-          mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+          mx = max_xor16_32(mx) * sl2;
           if (__builtin_amdgcn_ballot_w64(mx > m[hh] + kLazy)) {
             const float m_new = fmaxf(m[hh], mx);
             const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m[hh] - m_new);

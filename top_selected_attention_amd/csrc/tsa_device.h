@@ -92,6 +92,18 @@ __device__ __forceinline__ float wave_max_half_swap(float x) {
   return fmaxf(x, __shfl_xor(x, 32));
 }
 
+// Max over lanes l and l ^ 32, and over l, l ^ 16, l ^ 32, l ^ 48, on the
+// VALU lane-swap instructions (a swap of 16-lane rows 1, 3 with 0, 2, and of
+// the two 32-lane halves) instead of LDS-routed shuffles.
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor16_32(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return max_xor32(fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // XOR swizzle of the 16 16-byte pieces of a 256-byte LDS row (one K, V, Q or
@@ -132,17 +144,16 @@ __device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
 
 // Direct global -> LDS copy of 16 bytes per lane: lane l's bytes land at
 // lds_base + 16*l.  lds_base must be the same for every lane of the wave.
+//
+// Issued from inline assembly, so the compiler's wait-count pass does not see
+// an LDS write in flight: it then inserts no "wait for every vector load"
+// before later LDS reads, and a pipeline stage can stay in flight across the
+// reads of an older stage.  The caller owns the ordering: an explicit vmcnt
+// wait (wait_vm / wait_vm_le) by the issuing wave, then a barrier when other
+// waves read the bytes, before any read; and the same before a buffer is
+// filled again.  The global address is read when the instruction issues; M0
+// (the LDS base) is saved and restored around it.
 __device__ __forceinline__ void g2lds16(const void* g, void* lds_base) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
-}
-// g2lds16 issued from inline assembly, so the compiler's wait-count pass does
-// not see an LDS write in flight: it then places no "wait for every vector
-// load" before later LDS reads, and a ring of several stages can stay in
-// flight across the reads of an older stage.  The caller owns the ordering:
-// an explicit vmcnt wait plus a barrier before any wave reads the bytes, and
-// before the buffer is filled again.  M0 is saved and restored around the
-// load (the address is read when the instruction issues).
-__device__ __forceinline__ void g2lds16_async(const void* g, void* lds_base) {
   const unsigned l = __builtin_amdgcn_readfirstlane(
       (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)lds_base);
   unsigned saved;
@@ -155,8 +166,40 @@ __device__ __forceinline__ void g2lds16_async(const void* g, void* lds_base) {
 }
 // Same with 4 bytes per lane (lane l's dword lands at lds_base + 4*l).
 __device__ __forceinline__ void g2lds4(const void* g, void* lds_base) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_base, 4, 0, 0);
+  const unsigned l = __builtin_amdgcn_readfirstlane(
+      (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)lds_base);
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+      "global_load_lds_dword %1, off\n\ts_mov_b32 m0, %0\n\ts_nop 0"
+      : "=&s"(saved)
+      : "v"(g), "s"(l)
+      : "memory");
 }
+
+// Wave-uniform lookups into an int32 list (e.g. the column ids of one row of
+// a compacted block mask): 64 consecutive entries are held one per lane and
+// read back with readlane, so a loop over the list issues no global load per
+// step; a lookup outside the held run refills it from there.  Lookups must
+// be wave-uniform.
+struct ListWindow {
+  const int* list;
+  int base, hi, val;
+  __device__ __forceinline__ ListWindow(const int* l, int lo, int hi_) : list(l), base(lo), hi(hi_) {
+    fill();
+  }
+  __device__ __forceinline__ void fill() {
+    const int e = base + (int)(threadIdx.x & 63);
+    val = e < hi ? list[e] : 0;
+  }
+  __device__ __forceinline__ int operator()(int idx) {
+    if ((unsigned)(idx - base) >= 64u) {
+      base = idx;
+      fill();
+    }
+    return __builtin_amdgcn_readlane(val, idx - base);
+  }
+};
 
 // Stages rows [0, 64) of a 64 x 256-byte tile into swizzled LDS.  Row r of
 // the tile is global row row_of(r) (the caller clamps it into range).  The
