@@ -44,6 +44,14 @@ def parse():
                              "sfa_decode"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample (0 = skip)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain copy kernel of known size (HBM counter calibration)")
+    ap.add_argument("--ingest-copy", metavar="DIR",
+                    help="read the copy kernel's FETCH_SIZE / WRITE_SIZE runs (DIR/fetch, "
+                         "DIR/write) into profiles/traffic.json (no GPU needed)")
+    ap.add_argument("--ingest", metavar="DIR",
+                    help="summarise rocprofv3 runs of --workload (DIR/trace, DIR/bench.json, "
+                         "DIR/fetch, DIR/write) into profiles/ (no GPU needed)")
     return ap.parse_args()
 
 
@@ -60,24 +68,38 @@ def _ev_array(evs):
     return arr
 
 
-def _src_hash(*names):
+# Sources that decide each kernel's memory traffic: a counter summary taken
+# before any of them changed no longer describes the kernel.
+KERNEL_SOURCES = {
+    "bsa_fwd_kernel": ["bsa_fwd.hip"],
+    "bsa_dq_kernel": ["bsa_bwd.hip"],
+    "bsa_dkdv_kernel": ["bsa_bwd.hip"],
+    "nsa_fwd_kernel": ["nsa.hip"],
+    "nsa_dq_kernel": ["nsa.hip"],
+    "nsa_dkdv_seg_kernel": ["nsa.hip"],
+    "sfa_split_kernel": ["sfa.hip"],
+}
+COMMON_SOURCES = ["tsa_device.h", "tsa_internal.h"]
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def _src_hash(kernel):
     h = hashlib.sha256()
-    for n in names:
+    for n in KERNEL_SOURCES[kernel] + COMMON_SOURCES:
         with open(os.path.join(ROOT, "top_selected_attention_amd", "csrc", n), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def _traffic(kernel, src_files, units_per_launch):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None when absent or when the kernel source changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
-    if not os.path.exists(path):
+def _traffic(workload, kernel):
+    """HBM bytes per launch of ``kernel`` on ``workload`` from the committed
+    rocprofv3 counter summary (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or
+    None when absent or when the kernel's sources changed since it was taken."""
+    if not os.path.exists(TRAFFIC_JSON):
         return None
-    with open(path) as f:
-        t = json.load(f)
-    ent = t.get(kernel)
-    if not ent or ent.get("src_hash") != _src_hash(*src_files):
+    with open(TRAFFIC_JSON) as f:
+        ent = json.load(f).get(workload, {}).get(kernel)
+    if not ent or kernel not in KERNEL_SOURCES or ent.get("src_hash") != _src_hash(kernel):
         return None
     return ent.get("bytes_per_launch")
 
@@ -161,9 +183,6 @@ def bench_bsa(args):
     dom = max(kern, key=lambda n: kern[n][0])
     dms, dfl = kern[dom]
     achieved = dfl / (dms * 1e-3) / 1e12
-    files = {"bsa_fwd_kernel": ["bsa_fwd.hip", "tsa_device.h"],
-             "bsa_dq_kernel": ["bsa_bwd.hip", "tsa_device.h"],
-             "bsa_dkdv_kernel": ["bsa_bwd.hip", "tsa_device.h"]}[dom]
     value = (fwd_flops + bwd_flops) / (ms_step * 1e-3) / 1e12
     res = {
         "metric": "effective TFLOP/s on selected blocks (fwd, bwd) and % of bf16 MFMA peak",
@@ -187,7 +206,7 @@ def bench_bsa(args):
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": _traffic(dom, files, None)},
+                     "traffic": _traffic(w["name"], dom)},
     }
     return res, (w, q, k, v, do, mask, scale, unit)
 
@@ -243,11 +262,12 @@ def bench_nsa(args):
     plan = tsa.NsaPlan(q.to(dev), k.to(dev), v.to(dev), torch.from_numpy(topk).to(dev), cu, cu,
                        sbs, scale, w["sparse_mode"])
     plan.set_dout(do.to(dev))
-    st, ms_step, K = _timed_steps(args, plan, 2, 3)
+    st, ms_step, K = _timed_steps(args, plan, 2, 4)
     fwd_ms = st[0] + st[1]
-    bwd_ms = st[2] + st[3] + st[4]
+    bwd_ms = st[2] + st[3] + st[4] + st[5]
+    # dK/dV: the partial kernel does the 4 GEMMs; the reduction is a separate stage
     kern = {"nsa_fwd_kernel": (st[1], 4.0 * unit), "nsa_dq_kernel": (st[3], 6.0 * unit),
-            "nsa_dkdv_kernel": (st[4], 8.0 * unit)}
+            "nsa_dkdv_seg_kernel": (st[4], 8.0 * unit)}
     dom = max(kern, key=lambda n: kern[n][0])
     dms, dfl = kern[dom]
     achieved = dfl / (dms * 1e-3) / 1e12
@@ -264,13 +284,13 @@ def bench_nsa(args):
         "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "fwd_tflops": round(fwd_flops / (fwd_ms * 1e-3) / 1e12, 2),
         "bwd_tflops": round(bwd_flops / (bwd_ms * 1e-3) / 1e12, 2),
-        "stage_ms": dict(zip(["fwd_lists", "fwd_attention", "bwd_lists", "bwd_dq", "bwd_dkdv"],
-                             [round(x, 4) for x in st])),
+        "stage_ms": dict(zip(["fwd_lists", "fwd_attention", "bwd_lists", "bwd_dq", "bwd_dkdv",
+                              "bwd_dkdv_reduce"], [round(x, 4) for x in st])),
         "fwd_gathered_GBps": round(gathered / (st[1] * 1e-3) / 1e9, 1),
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": _traffic(dom, ["nsa.hip", "tsa_device.h"], None)},
+                     "traffic": _traffic(w["name"], dom)},
     }
     return res, (w, cu, q, k, v, do, topk, scale, sbs, G, D)
 
@@ -364,7 +384,7 @@ def bench_sfa(args):
         "algorithmic_bytes": int(nbytes),
         "roofline": {"kernel": "sfa_split_kernel", "bound": "hbm", "achieved": round(kgbs, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(kgbs / PEAK_HBM_GBS, 4),
-                     "traffic": _traffic("sfa_split_kernel", ["sfa.hip", "tsa_device.h"], None)},
+                     "traffic": _traffic(w["name"], "sfa_split_kernel")},
     }
     return res, (w, q, qr, kc, krc, bt, kv_lens, idx, scale, nbytes)
 
@@ -417,6 +437,170 @@ def _timed_steps(args, plan, nf, nb):
     return st, ms_step, K
 
 
+# ----------------------------------------------------------------------------
+# rocprofv3 summaries under profiles/
+# ----------------------------------------------------------------------------
+
+COPY_BYTES = 256 << 20   # the calibration kernel reads and writes this many bytes per launch
+
+
+def copy_calibration():
+    """Three launches of a plain elementwise copy (torch.neg, float32) that
+    read COPY_BYTES and write COPY_BYTES each: what FETCH_SIZE / WRITE_SIZE
+    report for a kernel of known HBM traffic."""
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": COPY_BYTES, "launches": 3}), flush=True)
+
+
+def _csv_rows(d, suffix):
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True)):
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    return rows
+
+
+def _short(name):
+    """'void tsa::bsa_dkdv_kernel<tsa::BF16, 4>(...)' -> 'bsa_dkdv_kernel'."""
+    n = name.split("(")[0].replace("void ", "").strip().split("<")[0]
+    return n.split("::")[-1]
+
+
+def _counter_means(d, counter, match=None):
+    """Kernel short name (or the kernels whose full name contains ``match``)
+    -> mean counter value per dispatch, in the counter's unit (KiB)."""
+    acc = {}
+    for r in _csv_rows(d, "counter_collection.csv"):
+        if r.get("Counter_Name") != counter:
+            continue
+        name = r["Kernel_Name"]
+        if match is not None:
+            if match not in name:
+                continue
+            key = match
+        else:
+            key = _short(name)
+        acc.setdefault(key, []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def _load_traffic():
+    if os.path.exists(TRAFFIC_JSON):
+        with open(TRAFFIC_JSON) as f:
+            return json.load(f)
+    return {}
+
+
+def _save_traffic(t):
+    with open(TRAFFIC_JSON, "w") as f:
+        json.dump(t, f, indent=1, sort_keys=True)
+        f.write("\n")
+
+
+def ingest_copy(d):
+    """FETCH_SIZE / WRITE_SIZE calibration factors from the copy kernel's
+    counter runs under d/fetch and d/write."""
+    fk = _counter_means(os.path.join(d, "fetch"), "FETCH_SIZE", "neg_kernel")["neg_kernel"]
+    wk = _counter_means(os.path.join(d, "write"), "WRITE_SIZE", "neg_kernel")["neg_kernel"]
+    t = _load_traffic()
+    t["_calibration"] = {
+        "copy_bytes": COPY_BYTES, "fetch_kib": round(fk, 1), "write_kib": round(wk, 1),
+        "fetch_factor": COPY_BYTES / (fk * 1024.0), "write_factor": COPY_BYTES / (wk * 1024.0)}
+    _save_traffic(t)
+    print(json.dumps(t["_calibration"]))
+
+
+def ingest(d, workload):
+    """Writes profiles/<dominant kernel>_<workload>.md from the kernel trace
+    under d/trace (with the bench line the traced run printed, d/bench.json)
+    and the counter runs under d/fetch, d/write; records each library
+    kernel's calibrated HBM bytes per launch in profiles/traffic.json."""
+    tr = {}
+    for r in _csv_rows(os.path.join(d, "trace"), "kernel_trace.csv"):
+        name = r["Kernel_Name"]
+        if "tsa::" not in name:
+            continue
+        us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        tr.setdefault(_short(name), []).append(us)
+    bench = None
+    with open(os.path.join(d, "bench.json")) as f:
+        for line in f:
+            if line.startswith("{"):
+                bench = json.loads(line)
+    fetch = _counter_means(os.path.join(d, "fetch"), "FETCH_SIZE")
+    write = _counter_means(os.path.join(d, "write"), "WRITE_SIZE")
+    t = _load_traffic()
+    cal = t["_calibration"]
+    total = sum(sum(v) for v in tr.values())
+    dom = bench["roofline"]["kernel"]
+    entries = t.setdefault(workload, {})
+    lines = []
+    for k in sorted(tr, key=lambda k: -sum(tr[k])):
+        v = tr[k]
+        fb = fetch.get(k, 0.0) * 1024 * cal["fetch_factor"]
+        wb = write.get(k, 0.0) * 1024 * cal["write_factor"]
+        lines.append(f"| `{k}` | {len(v)} | {sum(v) / len(v):.1f} | {min(v):.1f} | {max(v):.1f} | "
+                     f"{100 * sum(v) / total:.1f} | {fetch.get(k, 0.0):.0f} | {write.get(k, 0.0):.0f} | "
+                     f"{(fb + wb) / 1e6:.2f} |")
+        if k in KERNEL_SOURCES:
+            entries[k] = {"src_hash": _src_hash(k), "fetch_kib": round(fetch.get(k, 0.0), 1),
+                          "write_kib": round(write.get(k, 0.0), 1),
+                          "bytes_per_launch": int(round(fb + wb)),
+                          "avg_us_kernel_trace": round(sum(v) / len(v), 1)}
+    _save_traffic(t)
+    rl = bench["roofline"]
+    cmd = (f"python3 bench.py --workload {workload} --steps 5 --warmup 2 --cpu-seconds 0")
+    pcmd = (f"python3 bench.py --workload {workload} --steps 2 --warmup 1 --cpu-seconds 0")
+    out = [
+        f"# {dom} on {workload}: rocprofv3 kernel trace and HBM counters",
+        "",
+        f"Workload: `{json.dumps(bench['config'])}`.",
+        "",
+        "Commands (repository root, one MI355X; `cd /tmp && export TMPDIR=/tmp` first, then back):",
+        "",
+        "```",
+        f"rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof/{workload}/trace -o run -- {cmd} > gpurun_out/prof/{workload}/bench.json",
+        f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/prof/{workload}/fetch -o run -- {pcmd}",
+        f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof/{workload}/write -o run -- {pcmd}",
+        "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/prof/copy/fetch -o run -- python3 bench.py --copy-calibration",
+        "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof/copy/write -o run -- python3 bench.py --copy-calibration",
+        "python3 bench.py --ingest-copy gpurun_out/prof/copy",
+        f"python3 bench.py --ingest gpurun_out/prof/{workload} --workload {workload}",
+        "```",
+        "",
+        "Kernel trace: every call of the traced run (warm-up included).  FETCH / WRITE: mean "
+        "KiB per dispatch from the two counter runs; HBM MB = FETCH x "
+        f"{cal['fetch_factor']:.4f} + WRITE x {cal['write_factor']:.4f} (the factors make a "
+        f"plain copy of {COPY_BYTES >> 20} MiB read as {COPY_BYTES >> 20} MiB each way: it "
+        f"reads {cal['fetch_kib']:.0f} / {cal['write_kib']:.0f} KiB).",
+        "",
+        "| kernel | calls | avg (us) | min (us) | max (us) | % of library GPU time | FETCH (KiB) | WRITE (KiB) | HBM MB / launch |",
+        "|---|---|---|---|---|---|---|---|---|",
+    ] + lines + [
+        "",
+        f"bench.py's own HIP-event stage times in the traced run (ms): `{json.dumps(bench['stage_ms'])}`.",
+        "",
+        f"Dominant kernel `{dom}`: {rl['achieved']} {rl['unit']} by the bench's events "
+        f"(roofline fraction {rl['frac']} of {rl['peak']} {rl['unit']}); its kernel-trace average "
+        f"above is the duration to compare.",
+        "",
+        f"Bench line of the traced run: value {bench['value']} {bench['unit']}, "
+        f"{bench['ms_per_step']} ms per step.",
+        "",
+    ]
+    path = os.path.join(ROOT, "profiles", f"{dom}_{workload}.md")
+    with open(path, "w") as f:
+        f.write("\n".join(out))
+    print(path)
+
+
 def _threads():
     try:
         from threadpoolctl import threadpool_info
@@ -427,6 +611,12 @@ def _threads():
 
 def main():
     args = parse()
+    if args.ingest_copy:
+        ingest_copy(args.ingest_copy)
+        return
+    if args.ingest:
+        ingest(args.ingest, args.workload)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
               "the path shards by KV head / batch with no exchange, so per-GPU throughput "
@@ -436,6 +626,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.workload in CFG_OF:
         res, ctx = bench_bsa(args)
         if args.cpu_seconds > 0:

@@ -31,7 +31,8 @@
  * Every args struct ends with reuse_lists, n_events and events.  Stages
  * that can be timed, per entry point: bsa_fwd 0 = lists, 1 = attention;
  * bsa_bwd 0 = lists, 1 = dQ (with softmax_grad), 2 = dK/dV; nsa_select_fwd
- * 0 = lists, 1 = attention; nsa_select_bwd 0 = lists, 1 = dQ, 2 = dK/dV;
+ * 0 = lists, 1 = attention; nsa_select_bwd 0 = lists, 1 = dQ, 2 = dK/dV
+ * fp32 partials (segment table + partial kernel), 3 = their reduction;
  * sfa_paged_fwd 0 = split attention, 1 = split combine.  A stage that a call
  * skips records both of its events back to back.
  *

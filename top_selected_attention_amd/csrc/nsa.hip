@@ -556,14 +556,16 @@ static hipError_t bwd_t(const NsaParams& p, hipStream_t st, void* const* ev, int
       hipLaunchKernelGGL((nsa_dkdv_seg_kernel<E, 4>), dim3(grid), dim3(256), 0, st, p, p.seg_off,
                          nb, p.part);
     e = hipGetLastError();
-    if (e == hipSuccess) {
-      const long n = (long)nb * p.g.sbs * (kD / 4);
-      hipLaunchKernelGGL((nsa_dkdv_reduce<E>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
-                         p, p.seg_off, nb, (const float*)p.part);
-      e = hipGetLastError();
-    }
   }
   if (e == hipSuccess) e = mark_event(ev, n_ev, 2, 1, st);
+  if (e == hipSuccess) e = mark_event(ev, n_ev, 3, 0, st);
+  if (e == hipSuccess && nb > 0) {
+    const long n = (long)nb * p.g.sbs * (kD / 4);
+    hipLaunchKernelGGL((nsa_dkdv_reduce<E>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                       p, p.seg_off, nb, (const float*)p.part);
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess) e = mark_event(ev, n_ev, 3, 1, st);
   return e;
 }
 
