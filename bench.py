@@ -37,8 +37,10 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    # enough untimed steps for the GPU clocks to settle (timing right after a
+    # cold start reads several percent slow)
+    ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--workload", default="bsa_causal_8k",
                     choices=["bsa_causal_8k", "bsa_small", "bsa_window_128k", "nsa_varlen",
                              "sfa_decode"])

@@ -91,21 +91,20 @@ __global__ __launch_bounds__(NW * 64) void bsa_dq_kernel(BsaParams p, int qsub, 
   const int e0 = p.row_ptr[bn * p.QB + qb], e1 = p.row_ptr[bn * p.QB + qb + 1];
   ListWindow colw(p.col, e0, e1);
   const int cpb = (p.bkv + 63) / 64;
-  const int nchunks = (e1 - e0) * cpb;
   const float sl2 = p.scale * kLog2e;
 
-  auto chunk_range = [&](int i, int& ks, int& ke) {
-    const int kb = colw(e0 + i / cpb);
-    ks = kb * p.bkv + (i % cpb) * 64;
+  auto chunk_range = [&](ChunkPos c, int& ks, int& ke) {
+    const int kb = colw(c.e);
+    ks = kb * p.bkv + c.s * 64;
     ke = min(min(ks + 64, (kb + 1) * p.bkv), p.Skv);
   };
-  auto next_valid = [&](int i) {
-    for (; i < nchunks; i++) {
+  auto next_valid = [&](ChunkPos c) {
+    for (; c.e < e1; c = chunk_advance(c, cpb)) {
       int ks, ke;
-      chunk_range(i, ks, ke);
+      chunk_range(c, ks, ke);
       if (ks < ke && !(p.causal && ks > row_hi - 1)) break;
     }
-    return i;
+    return c;
   };
   auto load_chunk = [&](int ks, int ke, int buf) {
     auto row_of = [&](int r) { return min(ks + r, ke - 1); };
@@ -120,8 +119,8 @@ __global__ __launch_bounds__(NW * 64) void bsa_dq_kernel(BsaParams p, int qsub, 
     for (int j = 0; j < 16; j++) dq[dt][j] = 0.f;
   const float lneg = -lse2;
 
-  int i = next_valid(0);
-  if (i < nchunks) {
+  ChunkPos i = next_valid(ChunkPos{e0, 0});
+  if (i.e < e1) {
     int ks, ke;
     chunk_range(i, ks, ke);
     load_chunk(ks, ke, 0);
@@ -129,11 +128,11 @@ __global__ __launch_bounds__(NW * 64) void bsa_dq_kernel(BsaParams p, int qsub, 
   wait_vm();
   __syncthreads();
   int buf = 0;
-  while (i < nchunks) {
+  while (i.e < e1) {
     int ks, ke;
     chunk_range(i, ks, ke);
-    const int inext = next_valid(i + 1);
-    if (inext < nchunks) {
+    const ChunkPos inext = next_valid(chunk_advance(i, cpb));
+    if (inext.e < e1) {
       int ks2, ke2;
       chunk_range(inext, ks2, ke2);
       load_chunk(ks2, ke2, buf ^ 1);
@@ -269,29 +268,34 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int e0 = p.rev_ptr[c], e1 = p.rev_ptr[c + 1];
   ListWindow revw(p.rev, e0, e1);
   const int cpq = (p.bq + kQC - 1) / kQC;
-  const int nchunks = (e1 - e0) * cpq;
   const float sl2 = p.scale * kLog2e;
 
-  // Chunk i: query rows [qs, qe) of query head n1 (entry id g*QB + qb).
-  auto chunk_range = [&](int i, int& n1, int& qs, int& qe) {
-    const int id = revw(e0 + i / cpq);
-    const int g = id / p.QB, qb = id % p.QB;
+  // Chunk (e, s): query rows [qs, qe) (sub-chunk s) of query head n1, for
+  // reverse-list entry id g*QB + qb.
+  auto chunk_range = [&](ChunkPos c, int& n1, int& qs, int& qe) {
+    const int id = revw(c.e);
+    const int g = p.G > 1 ? id / p.QB : 0, qb = id - g * p.QB;
     n1 = n2 * p.G + g;
-    qs = qb * p.bq + (i % cpq) * kQC;
+    qs = qb * p.bq + c.s * kQC;
     qe = min(min(qs + kQC, (qb + 1) * p.bq), p.Sq);
   };
-  auto next_valid = [&](int i) {
-    for (; i < nchunks; i++) {
+  auto next_valid = [&](ChunkPos c) {
+    for (; c.e < e1; c = chunk_advance(c, cpq)) {
       int n1, qs, qe;
-      chunk_range(i, n1, qs, qe);
+      chunk_range(c, n1, qs, qe);
       if (qs < qe && !(p.causal && qe - 1 < key_lo)) break;
     }
-    return i;
+    return c;
   };
   // 32 rows of Q and of dO (8 KB each) plus their LSE / softmax_grad
   auto load_chunk = [&](int n1, int qs, int qe, int buf) {
     const long hoff = ((long)b * p.N1 + n1) * p.Sq;
-    const int sub = lane >> 4, pc = lane & 15;
+    // The per-lane address terms are rebuilt here from an opaque copy of the
+    // lane id: hoisted out of the loop they would be spilled, and a scratch
+    // reload between two direct loads waits for the first to land.
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int sub = ln >> 4, pc = ln & 15;
 #pragma unroll
     for (int u = 0; u < 8 / NW; u++) {
       const int inst = wid * (8 / NW) + u;
@@ -304,7 +308,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     if (wid == 0) {
       // a direct LDS load writes lane l's dword at base + 4*l for all 64
       // lanes: the arrays hold 64 entries; entries past 32 are never read
-      const long r = hoff + min(qs + lane, qe - 1);
+      const long r = hoff + min(qs + ln, qe - 1);
       g2lds4(p.lse + r, lds_lse[buf]);
       g2lds4(p.delta + r, lds_dlt[buf]);
     }
@@ -316,8 +320,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
     for (int j = 0; j < 16; j++) dvt[dt][j] = dkt[dt][j] = 0.f;
 
-  int i = next_valid(0);
-  if (i < nchunks) {
+  ChunkPos i = next_valid(ChunkPos{e0, 0});
+  if (i.e < e1) {
     int n1, qs, qe;
     chunk_range(i, n1, qs, qe);
     load_chunk(n1, qs, qe, 0);
@@ -325,11 +329,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   wait_vm();
   __syncthreads();
   int buf = 0;
-  while (i < nchunks) {
+  while (i.e < e1) {
+    // Lane-derived terms of this iteration come from an opaque copy of the
+    // lane id, so they are recomputed here rather than kept (and spilled)
+    // across iterations.
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int l32i = ln & 31, hi = ln >> 5;
     int n1, qs, qe;
     chunk_range(i, n1, qs, qe);
-    const int inext = next_valid(i + 1);
-    if (inext < nchunks) {
+    const ChunkPos inext = next_valid(chunk_advance(i, cpq));
+    if (inext.e < e1) {
       int n1b, qs2, qe2;
       chunk_range(inext, n1b, qs2, qe2);
       load_chunk(n1b, qs2, qe2, buf ^ 1);
@@ -343,8 +353,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     for (int j = 0; j < 16; j++) s[j] = dp[j] = 0.f;
 #pragma unroll
     for (int ds = 0; ds < 8; ds++) {
-      s = E::mfma32(tile_read16<V8>(Qb, l32, 2 * ds + h), tile_read16<V8>(lds_k, wid * 32 + l32, 2 * ds + h), s);
-      dp = E::mfma32(tile_read16<V8>(Db, l32, 2 * ds + h), vreg[ds], dp);
+      s = E::mfma32(tile_read16<V8>(Qb, l32i, 2 * ds + hi),
+                    tile_read16<V8>(lds_k, wid * 32 + l32i, 2 * ds + hi), s);
+      dp = E::mfma32(tile_read16<V8>(Db, l32i, 2 * ds + hi), vreg[ds], dp);
     }
     // three LDS reads feed two MFMAs per step
     __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
@@ -359,14 +370,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     // element j of a lane is query 8*(j/4) + 4*h + j%4 of the chunk, column key l32
     V8 bp[2], bd[2];
     auto form = [&](auto masked) {
-      int lo = 0, hi = 0;
+      int lo = 0, up = 0;
       if (masked) {
-        lo = (p.causal ? mykey - qs : 0) - 4 * h;
-        hi = key_ok ? qe - qs - 1 - 4 * h : -1000000;
+        lo = (p.causal ? wkey0 + l32i - qs : 0) - 4 * hi;
+        up = wkey0 + l32i < key_hi ? qe - qs - 1 - 4 * hi : -1000000;
       }
 #pragma unroll
       for (int j4 = 0; j4 < 4; j4++) {
-        const int rbase = 8 * j4 + 4 * h;
+        const int rbase = 8 * j4 + 4 * hi;
         const float4 lse4 = *reinterpret_cast<const float4*>(&lds_lse[buf][rbase]);
         const float4 dl4 = *reinterpret_cast<const float4*>(&lds_dlt[buf][rbase]);
         const float lv[4] = {lse4.x, lse4.y, lse4.z, lse4.w};
@@ -377,7 +388,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
           float pr = fast_exp2(__builtin_fmaf(s[j], sl2, -lv[jj] * kLog2e));
           if (masked) {
             const int off = 8 * j4 + jj;
-            pr = (off >= lo && off <= hi) ? pr : 0.f;
+            pr = (off >= lo && off <= up) ? pr : 0.f;
           }
           bp[j >> 3][j & 7] = E::from_f32(pr);
           bd[j >> 3][j & 7] = E::from_f32(pr * (dp[j] - dv[jj]));
@@ -391,8 +402,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     for (int k2 = 0; k2 < 2; k2++)
 #pragma unroll
       for (int dt = 0; dt < 4; dt++) {
-        dvt[dt] = E::mfma32(tile_read_tr<V8>(Db, k2, dt), bp[k2], dvt[dt]);
-        dkt[dt] = E::mfma32(tile_read_tr<V8>(Qb, k2, dt), bd[k2], dkt[dt]);
+        dvt[dt] = E::mfma32(tile_read_tr<V8>(Db, k2, dt, ln), bp[k2], dvt[dt]);
+        dkt[dt] = E::mfma32(tile_read_tr<V8>(Qb, k2, dt, ln), bd[k2], dkt[dt]);
       }
     sched_mfma_lds<16, 2, 4>();
     wait_vm();

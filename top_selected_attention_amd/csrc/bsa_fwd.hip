@@ -66,24 +66,23 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_kernel(BsaParams p, int qsub,
   const int e0 = p.row_ptr[tile_row], e1 = p.row_ptr[tile_row + 1];
   ListWindow colw(p.col, e0, e1);
   const int cpb = (p.bkv + kKC - 1) / kKC;
-  const int nchunks = (e1 - e0) * cpb;
   const float sl2 = p.scale * kLog2e;
 
-  // Chunk i covers keys [ks, ke) of KV block col[e0 + i / cpb].  Chunks that
+  // Chunk (e, s) covers keys [ks, ke) of KV block col[e], sub-chunk s.  Chunks that
   // are empty (ragged tail) or wholly after the slice's last row under causal
   // mode are skipped; the test is uniform across the workgroup.
-  auto chunk_range = [&](int i, int& ks, int& ke) {
-    const int kb = colw(e0 + i / cpb);
-    ks = kb * p.bkv + (i % cpb) * kKC;
+  auto chunk_range = [&](ChunkPos c, int& ks, int& ke) {
+    const int kb = colw(c.e);
+    ks = kb * p.bkv + c.s * kKC;
     ke = min(min(ks + kKC, (kb + 1) * p.bkv), p.Skv);
   };
-  auto next_valid = [&](int i) {
-    for (; i < nchunks; i++) {
+  auto next_valid = [&](ChunkPos c) {
+    for (; c.e < e1; c = chunk_advance(c, cpb)) {
       int ks, ke;
-      chunk_range(i, ks, ke);
+      chunk_range(c, ks, ke);
       if (ks < ke && !(p.causal && ks > row_hi - 1)) break;
     }
-    return i;
+    return c;
   };
   // Direct global -> LDS loads (no registers) into the swizzled layout.  Keys
   // past the chunk's end re-read its last key (finite data; their scores are
@@ -105,8 +104,8 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_kernel(BsaParams p, int qsub,
 #pragma unroll
     for (int j = 0; j < 16; j++) o[dt][j] = 0.f;
 
-  int i = next_valid(0);
-  if (i < nchunks) {
+  ChunkPos i = next_valid(ChunkPos{e0, 0});
+  if (i.e < e1) {
     int ks, ke;
     chunk_range(i, ks, ke);
     load_chunk(ks, ke, 0);
@@ -114,11 +113,11 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_kernel(BsaParams p, int qsub,
   wait_vm();
   __syncthreads();
   int buf = 0;
-  while (i < nchunks) {
+  while (i.e < e1) {
     int ks, ke;
     chunk_range(i, ks, ke);
-    const int inext = next_valid(i + 1);
-    if (inext < nchunks) {
+    const ChunkPos inext = next_valid(chunk_advance(i, cpb));
+    if (inext.e < e1) {
       int ks2, ke2;
       chunk_range(inext, ks2, ke2);
       load_chunk(ks2, ke2, buf ^ 1);

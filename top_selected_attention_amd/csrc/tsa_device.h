@@ -177,6 +177,19 @@ __device__ __forceinline__ void g2lds4(const void* g, void* lds_base) {
       : "memory");
 }
 
+// Position in a walk over the chunks of a block list: entry e of the list
+// and sub-chunk s of that entry (advanced by counting, with no division).
+struct ChunkPos {
+  int e, s;
+};
+__device__ __forceinline__ ChunkPos chunk_advance(ChunkPos c, int per_entry) {
+  if (++c.s == per_entry) {
+    c.s = 0;
+    ++c.e;
+  }
+  return c;
+}
+
 // Wave-uniform lookups into an int32 list (e.g. the column ids of one row of
 // a compacted block mask): 64 consecutive entries are held one per lane and
 // read back with readlane, so a loop over the list issues no global load per
@@ -227,8 +240,8 @@ __device__ __forceinline__ V8 tile_read16(const char* tile, int r, int c) {
 // (h = l/32), the row order that a 32x32 accumulator's elements 8*k2..8*k2+7
 // have in their row index (8*(j/4) + 4*h + j%4).
 template <typename V8>
-__device__ __forceinline__ V8 tile_read_tr(const char* tile, int k16, int dt) {
-  const int lane = threadIdx.x & 63;
+__device__ __forceinline__ V8 tile_read_tr(const char* tile, int k16, int dt,
+                                          int lane = threadIdx.x & 63) {
   const int g16 = lane >> 4, i16 = lane & 15, h = lane >> 5;
   const int r0 = k16 * 16 + 4 * h + (i16 >> 2);
   const int r1 = r0 + 8;
