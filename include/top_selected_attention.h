@@ -114,8 +114,10 @@ typedef struct {
   const void* v;            /* DEVICE */
   void* out;                /* DEVICE, written */
   float* lse;               /* DEVICE, written */
-  int32_t reuse_lists;      /* 1: the workspace holds this call's lists from an earlier call
-                               with the same mask/indices and workspace; skip building them */
+  int32_t reuse_lists;      /* 0: build the forward and reverse lists in the workspace;
+                               1: they are there from an earlier bsa_fwd / bsa_bwd call with
+                               the same mask and shapes on this workspace; skip building them;
+                               other values: TSA_ERR_INVALID */
   int32_t n_events;         /* number of stages to time (0 = off) */
   void* const* events;      /* HOST array of 2*n_events hipEvent_t: events[2i] / [2i+1] are
                                recorded on `stream` before / after stage i (see each entry) */
@@ -153,8 +155,9 @@ typedef struct {
   void* dq;                 /* DEVICE, written */
   void* dk;                 /* DEVICE, written */
   void* dv;                 /* DEVICE, written */
-  int32_t reuse_lists;      /* 1: the workspace holds this call's lists from an earlier call
-                               with the same mask/indices and workspace; skip building them */
+  int32_t reuse_lists;      /* 0: build the lists; 1: they are there from an earlier bsa_fwd /
+                               bsa_bwd call with the same mask and shapes on this workspace
+                               (bsa_fwd builds both directions); other values: TSA_ERR_INVALID */
   int32_t n_events;         /* number of stages to time (0 = off) */
   void* const* events;      /* HOST array of 2*n_events hipEvent_t: events[2i] / [2i+1] are
                                recorded on `stream` before / after stage i (see each entry) */
@@ -222,8 +225,9 @@ typedef struct {
   const void* v;            /* DEVICE */
   void* out;                /* DEVICE, written */
   float* lse;               /* DEVICE, written */
-  int32_t reuse_lists;      /* 1: the workspace holds this call's lists from an earlier call
-                               with the same mask/indices and workspace; skip building them */
+  int32_t reuse_lists;      /* 0: build the per-row lists (the reverse lists are left to the
+                               backward); 1: they are there from an earlier call with the same
+                               indices on this workspace; other values: TSA_ERR_INVALID */
   int32_t n_events;         /* number of stages to time (0 = off) */
   void* const* events;      /* HOST array of 2*n_events hipEvent_t: events[2i] / [2i+1] are
                                recorded on `stream` before / after stage i (see each entry) */
@@ -255,8 +259,12 @@ typedef struct {
   void* dq;                 /* DEVICE, written [T, N1, D] */
   void* dk;                 /* DEVICE, written [Tk, N2, D] */
   void* dv;                 /* DEVICE, written [Tk, N2, Dv] */
-  int32_t reuse_lists;      /* 1: the workspace holds this call's lists from an earlier call
-                               with the same mask/indices and workspace; skip building them */
+  int32_t reuse_lists;      /* 0: build per-row and reverse lists; 1: both are there from an
+                               earlier nsa_select_bwd call with the same indices on this
+                               workspace; 2: the per-row lists are there from an earlier
+                               nsa_select_fwd call with the same indices and cu_seqlens on this
+                               workspace (its size being this call's): build only the reverse
+                               lists; other values: TSA_ERR_INVALID */
   int32_t n_events;         /* number of stages to time (0 = off) */
   void* const* events;      /* HOST array of 2*n_events hipEvent_t: events[2i] / [2i+1] are
                                recorded on `stream` before / after stage i (see each entry) */
@@ -329,8 +337,7 @@ typedef struct {
   const int32_t* topk_indices;  /* DEVICE */
   void* out;                /* DEVICE, written */
   float* lse;               /* DEVICE, written, or NULL */
-  int32_t reuse_lists;      /* 1: the workspace holds this call's lists from an earlier call
-                               with the same mask/indices and workspace; skip building them */
+  int32_t reuse_lists;      /* unused (no lists); keep 0 */
   int32_t n_events;         /* number of stages to time (0 = off) */
   void* const* events;      /* HOST array of 2*n_events hipEvent_t: events[2i] / [2i+1] are
                                recorded on `stream` before / after stage i (see each entry) */

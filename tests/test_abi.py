@@ -69,6 +69,8 @@ def _size(tsa, fn, args):
     (dict(block_mask=0), 1),
     (dict(scale=float("nan")), 2),
     (dict(Sq=0), 0),                       # empty query: valid
+    (dict(reuse_lists=1), 0),
+    (dict(reuse_lists=2), 2),              # BSA has no partial-reuse mode
 ])
 def test_bsa_validation(tsa, kw, status):
     s, n = _size(tsa, tsa.lib.bsa_fwd_workspace_size, _bsa(tsa, **kw))
@@ -123,9 +125,21 @@ def _nsa(tsa, seqlens=(256, 512), **kw):
     (dict(Dv=64), 3),                      # Dv != D not built
     (dict(T=100), 2),                      # cu_seqlens_q[B] != T
     (dict(topk=0), 1),
+    (dict(reuse_lists=1), 0),
+    (dict(reuse_lists=2), 2),              # the forward has no partial-reuse mode
 ])
 def test_nsa_validation(tsa, kw, status):
     assert _size(tsa, tsa.lib.nsa_select_fwd_workspace_size, _nsa(tsa, **kw))[0] == status
+
+
+@pytest.mark.parametrize("reuse,status", [(0, 0), (1, 0), (2, 0), (3, 2), (-1, 2)])
+def test_nsa_bwd_reuse_modes(tsa, reuse, status):
+    f = _nsa(tsa)
+    fields = {n: getattr(f, n) for n, _ in f._fields_ if n not in ("out", "lse", "events")}
+    fields.update(out=8, dout=8, lse=8, dq=8, dk=8, dv=8, reuse_lists=reuse)
+    b = tsa._abi.NsaBwdArgs(**fields)
+    b._keep = f._keep
+    assert _size(tsa, tsa.lib.nsa_select_bwd_workspace_size, b)[0] == status
 
 
 def test_nsa_sequence_constraints(tsa):

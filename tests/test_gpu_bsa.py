@@ -282,3 +282,21 @@ def test_unselected_blocks_are_never_read(mode):
     assert torch.equal(r1[3][:, :, sel], r2[3][:, :, sel])
     assert torch.equal(r1[4][:, :, sel], r2[4][:, :, sel])
     assert (r2[3][:, :, ~sel] == 0).all() and (r2[4][:, :, ~sel] == 0).all()
+
+
+def test_bwd_reusing_forward_lists_matches_fresh_lists():
+    """A backward that reuses the lists the forward built in the shared
+    workspace equals, bit for bit, one that builds them itself."""
+    w, q, k, v, do, mask, scale = W.bsa_inputs(2)
+    tsa = _tsa()
+    qd, kd, vd, dod, md = _dev(q, k, v, do, torch.from_numpy(mask))
+    plan = tsa.BsaPlan(qd, kd, vd, md, w["bq"], w["bkv"], scale, 0)
+    plan.set_dout(dod)
+    out, lse = plan.fwd()
+    g1 = [t.clone() for t in plan.bwd()]            # reuses the forward's lists
+    fresh = tsa.BsaPlan(qd, kd, vd, md, w["bq"], w["bkv"], scale, 0)
+    fresh.set_out(out, lse)
+    g2 = fresh.bwd(dod)                             # builds its own lists
+    torch.cuda.synchronize()
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)

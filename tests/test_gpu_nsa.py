@@ -188,3 +188,18 @@ def test_validate_reports_out_of_range_ids():
         tsa.nsa_select_fwd(q.to(dev), k.to(dev), v.to(dev), torch.from_numpy(topk).to(dev),
                            cu, cu, 32, 0.1, 2, validate=True)
     assert ei.value.status == 6
+
+
+def test_bwd_reusing_forward_lists_matches_fresh_lists():
+    """A backward that reuses the forward's per-row lists (building only the
+    reverse lists) equals, bit for bit, one that builds every list itself."""
+    tsa = _tsa()
+    cu, q, k, v, do, topk = _case([512, 1024], 32, 2, 64, 8, 93)
+    out, lse, dq, dk, dv = _run(cu, q, k, v, do, topk, 64, 0.088, 2)
+    dev = torch.device("cuda")
+    plan = tsa.NsaPlan(q.to(dev), k.to(dev), v.to(dev), torch.from_numpy(topk).to(dev), cu, cu, 64,
+                       0.088, 2)
+    plan.set_out(out, lse)
+    dq2, dk2, dv2 = plan.bwd(do.to(dev))          # no forward on this plan: builds all lists
+    torch.cuda.synchronize()
+    assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)

@@ -109,6 +109,9 @@ class BsaPlan:
         nb = ctypes.c_size_t()
         _abi.call(lib.bsa_fwd_workspace_size, ctypes.byref(self.fa), ctypes.byref(nb))
         self.ws_fwd = _workspace(nb.value, dev)
+        # fwd() builds the block lists (both directions) in the workspace; the
+        # backward then shares that workspace and reuses them
+        self._lists = False
         self.backward = backward
         if backward:
             self.dout = None
@@ -124,8 +127,10 @@ class BsaPlan:
                 dq=self.dq.data_ptr(), dk=self.dk.data_ptr(), dv=self.dv.data_ptr())
 
     def fwd(self):
+        self.fa.reuse_lists = 0
         _abi.call(lib.bsa_fwd, ctypes.byref(self.fa), _ptr(self.ws_fwd),
                   ctypes.c_size_t(self.ws_fwd.numel()), _stream())
+        self._lists = True
         return self.out, self.lse
 
     def set_dout(self, dout):
@@ -134,7 +139,10 @@ class BsaPlan:
         self.ba.dout = dout.data_ptr()
         nb = ctypes.c_size_t()
         _abi.call(lib.bsa_bwd_workspace_size, ctypes.byref(self.ba), ctypes.byref(nb))
-        self.ws_bwd = _workspace(nb.value, self.q.device)
+        if nb.value > self.ws_fwd.numel():
+            self.ws_fwd = _workspace(nb.value, self.q.device)
+            self._lists = False
+        self.ws_bwd = self.ws_fwd
 
     def set_out(self, out, lse):
         """Use an externally produced forward output / LSE in the backward."""
@@ -148,8 +156,10 @@ class BsaPlan:
             self.set_dout(dout)
         if self.dout is None:
             raise ValueError("bwd needs dout")
+        self.ba.reuse_lists = 1 if self._lists else 0
         _abi.call(lib.bsa_bwd, ctypes.byref(self.ba), _ptr(self.ws_bwd),
                   ctypes.c_size_t(self.ws_bwd.numel()), _stream())
+        self._lists = True
         return self.dq, self.dk, self.dv
 
 
@@ -230,6 +240,9 @@ class NsaPlan:
         nb = ctypes.c_size_t()
         _abi.call(lib.nsa_select_fwd_workspace_size, ctypes.byref(self.fa), ctypes.byref(nb))
         self.ws_fwd = _workspace(nb.value, dev)
+        # fwd() builds the per-row lists in the workspace; the backward shares
+        # it and adds only the reverse lists
+        self._lists = False
         if backward:
             self.dout = None
             self.dq = torch.empty_like(q)
@@ -240,8 +253,10 @@ class NsaPlan:
                                       dv=self.dv.data_ptr(), **common)
 
     def fwd(self):
+        self.fa.reuse_lists = 0
         _abi.call(lib.nsa_select_fwd, ctypes.byref(self.fa), _ptr(self.ws_fwd),
                   ctypes.c_size_t(self.ws_fwd.numel()), _stream())
+        self._lists = True
         return self.out, self.lse
 
     def set_dout(self, dout):
@@ -250,7 +265,10 @@ class NsaPlan:
         self.ba.dout = dout.data_ptr()
         nb = ctypes.c_size_t()
         _abi.call(lib.nsa_select_bwd_workspace_size, ctypes.byref(self.ba), ctypes.byref(nb))
-        self.ws_bwd = _workspace(nb.value, self.q.device)
+        if nb.value > self.ws_fwd.numel():
+            self.ws_fwd = _workspace(nb.value, self.q.device)
+            self._lists = False
+        self.ws_bwd = self.ws_fwd
 
     def set_out(self, out, lse):
         _check(out, "out", self.q.dtype, self.out.shape)
@@ -263,6 +281,7 @@ class NsaPlan:
             self.set_dout(dout)
         if self.dout is None:
             raise ValueError("bwd needs dout")
+        self.ba.reuse_lists = 2 if self._lists else 0
         _abi.call(lib.nsa_select_bwd, ctypes.byref(self.ba), _ptr(self.ws_bwd),
                   ctypes.c_size_t(self.ws_bwd.numel()), _stream())
         return self.dq, self.dk, self.dv

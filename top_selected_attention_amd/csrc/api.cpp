@@ -113,6 +113,7 @@ size_t bsa_carve(const A* a, void* ws, BsaWs* out, bool with_delta) {
 
 int check_bsa_fwd(const bsa_fwd_args* a) {
   if (!a) return TSA_ERR_NULL;
+  if (a->reuse_lists != 0 && a->reuse_lists != 1) return TSA_ERR_INVALID;
   int s = check_bsa_common(a->dtype, a->q_layout, a->kv_layout, a->B, a->N1, a->N2, a->Sq, a->Skv,
                            a->D, a->block_q, a->block_kv, a->sparse_mode, a->scale);
   if (s) return s;
@@ -124,6 +125,7 @@ int check_bsa_fwd(const bsa_fwd_args* a) {
 
 int check_bsa_bwd(const bsa_bwd_args* a) {
   if (!a) return TSA_ERR_NULL;
+  if (a->reuse_lists != 0 && a->reuse_lists != 1) return TSA_ERR_INVALID;
   int s = check_bsa_common(a->dtype, a->q_layout, a->kv_layout, a->B, a->N1, a->N2, a->Sq, a->Skv,
                            a->D, a->block_q, a->block_kv, a->sparse_mode, a->scale);
   if (s) return s;
@@ -280,9 +282,11 @@ void nsa_geom(const A* a, const NsaWs& w, NsaGeom* g) {
   g->NB = nsa_blocks_total(a->cu_seqlens_kv, a->B, a->sbs);
 }
 
+enum NsaListParts { kNsaForward = 1, kNsaReverse = 2, kNsaAll = 3 };
+
 template <class A>
-int nsa_lists(const A* a, const NsaWs& w, const NsaGeom& g, hipStream_t st) {
-  if (a->validate) {
+int nsa_lists(const A* a, const NsaWs& w, const NsaGeom& g, int parts, hipStream_t st) {
+  if (a->validate && (parts & kNsaForward)) {
     hipError_t e = hipMemsetAsync(w.bad, 0, sizeof(int), st);
     if (e == hipSuccess) e = launch_nsa_check(a->topk, g, w.bad, st);
     int bad = 0;
@@ -291,8 +295,12 @@ int nsa_lists(const A* a, const NsaWs& w, const NsaGeom& g, hipStream_t st) {
     if (e != hipSuccess) return TSA_ERR_HIP;
     if (bad) return TSA_ERR_DATA;
   }
-  return hip_status(launch_nsa_compact(a->topk, g, w.cnt, w.sums, w.row_ptr, w.col, w.rcnt,
-                                       w.rev_ptr, w.rev, st));
+  hipError_t e = hipSuccess;
+  if (parts & kNsaForward)
+    e = launch_nsa_forward_lists(a->topk, g, w.cnt, w.sums, w.row_ptr, w.col, st);
+  if (e == hipSuccess && (parts & kNsaReverse))
+    e = launch_nsa_reverse_lists(g, w.row_ptr, w.col, w.sums, w.rcnt, w.rev_ptr, w.rev, st);
+  return hip_status(e);
 }
 
 // ---------------------------------------------------------------------------
@@ -534,10 +542,11 @@ int nsa_compact(const nsa_select_fwd_args* a, int32_t* row_ptr, int32_t* col, in
   NsaGeom g;
   s = nsa_setup(a, w, &g, st);
   if (s) return s;
-  return nsa_lists(a, w, g, st);
+  return nsa_lists(a, w, g, kNsaAll, st);
 }
 
 int nsa_select_fwd_workspace_size(const nsa_select_fwd_args* a, size_t* bytes) {
+  if (a && a->reuse_lists != 0 && a->reuse_lists != 1) return TSA_ERR_INVALID;
   return nsa_compact_workspace_size(a, bytes);
 }
 
@@ -555,9 +564,11 @@ int nsa_select_fwd(const nsa_select_fwd_args* a, void* ws, size_t ws_bytes, void
   const StageTimer tm = timer_of(a, st);
   if (tm.mark(0, 0) != hipSuccess) return TSA_ERR_HIP;
   if (!a->reuse_lists) {
+    // the forward needs only the per-row lists; the reverse lists are left
+    // to the backward (reuse_lists = 2 there)
     s = nsa_setup(a, w, &p.g, st);
     if (s) return s;
-    s = nsa_lists(a, w, p.g, st);
+    s = nsa_lists(a, w, p.g, kNsaForward, st);
     if (s) return s;
   } else {
     nsa_geom(a, w, &p.g);
@@ -577,6 +588,7 @@ int nsa_select_bwd_workspace_size(const nsa_select_bwd_args* a, size_t* bytes) {
   if (!bytes) return TSA_ERR_NULL;
   int s = check_nsa(a);
   if (s) return s;
+  if (a->reuse_lists < 0 || a->reuse_lists > 2) return TSA_ERR_INVALID;
   if (a->T > 0 && (!a->out || !a->dout || !a->lse || !a->dq)) return TSA_ERR_NULL;
   if (a->Tk > 0 && (!a->dk || !a->dv)) return TSA_ERR_NULL;
   *bytes = nsa_carve(a, nullptr, nullptr, true);
@@ -595,11 +607,11 @@ int nsa_select_bwd(const nsa_select_bwd_args* a, void* ws, size_t ws_bytes, void
   std::memset(&p, 0, sizeof(p));
   const StageTimer tm = timer_of(a, st);
   if (tm.mark(0, 0) != hipSuccess) return TSA_ERR_HIP;
-  if (!a->reuse_lists) {
+  if (a->reuse_lists == 0) {
     s = nsa_setup(a, w, &p.g, st);
     if (s) return s;
     if (a->T > 0) {
-      s = nsa_lists(a, w, p.g, st);
+      s = nsa_lists(a, w, p.g, kNsaAll, st);
       if (s) return s;
     } else {
       if (hipMemsetAsync(w.rev_ptr, 0, sizeof(int) * ((long)a->N2 * p.g.NB + 1), st) != hipSuccess)
@@ -607,6 +619,10 @@ int nsa_select_bwd(const nsa_select_bwd_args* a, void* ws, size_t ws_bytes, void
     }
   } else {
     nsa_geom(a, w, &p.g);
+    if (a->reuse_lists == 2 && a->T > 0) {
+      s = nsa_lists(a, w, p.g, kNsaReverse, st);
+      if (s) return s;
+    }
   }
   if (tm.mark(0, 1) != hipSuccess) return TSA_ERR_HIP;
   p.q = a->q; p.k = a->k; p.v = a->v; p.o = a->out; p.dout = a->dout; p.lse = (float*)a->lse;

@@ -435,9 +435,8 @@ hipError_t launch_nsa_check(const int* topk, const NsaGeom& g, int* bad, hipStre
   return hipGetLastError();
 }
 
-hipError_t launch_nsa_compact(const int* topk, const NsaGeom& g, int* cnt_scan, int* sums,
-                              int* row_ptr, int* col, int* rev_scan, int* rev_ptr, int* rev,
-                              hipStream_t st) {
+hipError_t launch_nsa_forward_lists(const int* topk, const NsaGeom& g, int* cnt_scan, int* sums,
+                                    int* row_ptr, int* col, hipStream_t st) {
   const long rows = (long)g.T * g.N2;
   const unsigned rb = (unsigned)((rows + 255) / 256);
   // forward: counts -> scan -> fill
@@ -455,18 +454,33 @@ hipError_t launch_nsa_compact(const int* topk, const NsaGeom& g, int* cnt_scan, 
   } else {
     hipLaunchKernelGGL(nsa_row_fill, dim3(rb), dim3(256), 0, st, topk, g, row_ptr, col);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_nsa_reverse_lists(const NsaGeom& g, const int* row_ptr, const int* col,
+                                    int* sums, int* rev_scan, int* rev_ptr, int* rev,
+                                    hipStream_t st) {
   // reverse: counts -> scan -> fill
   const long rrows = (long)g.N2 * g.NB;
+  if (rrows == 0) return hipMemsetAsync(rev_ptr, 0, sizeof(int), st);
   const unsigned wb = (unsigned)rrows;
   hipLaunchKernelGGL(nsa_rev<0>, dim3(wb), dim3(256), 0, st, g, row_ptr, col, rev_scan,
                      (const int*)nullptr, (int*)nullptr);
-  e = exclusive_scan(rev_scan, rrows, sums, st);
+  hipError_t e = exclusive_scan(rev_scan, rrows, sums, st);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(copy_ptr, dim3((unsigned)((rrows + 256) / 256)), dim3(256), 0, st, rev_scan,
                      rrows, sums + (rrows + kScanTile - 1) / kScanTile, rev_ptr);
   hipLaunchKernelGGL(nsa_rev<1>, dim3(wb), dim3(256), 0, st, g, row_ptr, col, (int*)nullptr,
                      (const int*)rev_ptr, rev);
   return hipGetLastError();
+}
+
+hipError_t launch_nsa_compact(const int* topk, const NsaGeom& g, int* cnt_scan, int* sums,
+                              int* row_ptr, int* col, int* rev_scan, int* rev_ptr, int* rev,
+                              hipStream_t st) {
+  hipError_t e = launch_nsa_forward_lists(topk, g, cnt_scan, sums, row_ptr, col, st);
+  if (e == hipSuccess) e = launch_nsa_reverse_lists(g, row_ptr, col, sums, rev_scan, rev_ptr, rev, st);
+  return e;
 }
 
 }  // namespace tsa

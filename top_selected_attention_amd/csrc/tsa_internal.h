@@ -34,6 +34,13 @@ struct NsaGeom {
 hipError_t launch_nsa_compact(const int* topk, const NsaGeom& g, int* cnt_scan, int* sums,
                               int* row_ptr, int* col, int* rev_scan, int* rev_ptr, int* rev,
                               hipStream_t st);
+// The two halves of launch_nsa_compact: per-row sorted lists, then the
+// reverse lists built from them.
+hipError_t launch_nsa_forward_lists(const int* topk, const NsaGeom& g, int* cnt_scan, int* sums,
+                                    int* row_ptr, int* col, hipStream_t st);
+hipError_t launch_nsa_reverse_lists(const NsaGeom& g, const int* row_ptr, const int* col,
+                                    int* sums, int* rev_scan, int* rev_ptr, int* rev,
+                                    hipStream_t st);
 hipError_t launch_nsa_check(const int* topk, const NsaGeom& g, int* bad, hipStream_t st);
 
 // ----- block-sparse attention ---------------------------------------------
