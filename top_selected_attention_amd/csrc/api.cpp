@@ -207,6 +207,11 @@ struct NsaWs {
   int* rcnt;
   int* rev_ptr;
   int* rev;
+  int* ekey;      // per forward entry: reverse key and token id
+  int* etok;
+  int* rhist;     // reverse-list sort: (key, tile) counters and their scan sums
+  int* rsums;
+  NsaRevSort rs;
   int* bad;
   float* delta;
   int* seg_off;
@@ -230,6 +235,12 @@ size_t nsa_carve(const A* a, void* ws, NsaWs* out, bool with_delta) {
   w.rcnt = c.take<int>(RR);
   w.rev_ptr = c.take<int>(RR + 1);
   w.rev = c.take<int>(R * a->sbc);
+  w.rs = nsa_rev_sort_plan(R * a->sbc, RR);
+  w.ekey = c.take<int>(R * a->sbc);
+  w.etok = c.take<int>(R * a->sbc);
+  const long nh = w.rs.usable ? (long)w.rs.NK * w.rs.n_tiles : 0;
+  w.rhist = c.take<int>(nh);
+  w.rsums = c.take<int>(w.rs.usable ? scan_sums_len(nh) : 0);
   w.bad = c.take<int>(1);
   w.delta = with_delta ? c.take<float>((long)a->T * a->N1) : nullptr;
   w.max_segments = with_delta ? nsa_max_segments(R * a->sbc, RR) : 0;
@@ -297,9 +308,10 @@ int nsa_lists(const A* a, const NsaWs& w, const NsaGeom& g, int parts, hipStream
   }
   hipError_t e = hipSuccess;
   if (parts & kNsaForward)
-    e = launch_nsa_forward_lists(a->topk, g, w.cnt, w.sums, w.row_ptr, w.col, st);
+    e = launch_nsa_forward_lists(a->topk, g, w.cnt, w.sums, w.row_ptr, w.col, w.ekey, w.etok, st);
   if (e == hipSuccess && (parts & kNsaReverse))
-    e = launch_nsa_reverse_lists(g, w.row_ptr, w.col, w.sums, w.rcnt, w.rev_ptr, w.rev, st);
+    e = launch_nsa_reverse_lists(g, w.row_ptr, w.col, w.sums, w.rcnt, w.rev_ptr, w.rev, w.ekey,
+                                 w.etok, w.rs, w.rhist, w.rsums, st);
   return hip_status(e);
 }
 

@@ -311,10 +311,11 @@ __global__ __launch_bounds__(256) void nsa_row_count(const int* topk, NsaGeom g,
 // One thread per (t, n2) row: each kept slot goes to its rank among the kept
 // slots ordered by (id, slot).
 __global__ __launch_bounds__(256) void nsa_row_fill(const int* topk, NsaGeom g, const int* row_ptr,
-                                                    int* col) {
+                                                    int* col, int* ekey, int* etok) {
   const long r = (long)blockIdx.x * 256 + threadIdx.x;
   if (r >= (long)g.T * g.N2) return;
   const int t = (int)(r / g.N2);
+  const int n2 = (int)(r - (long)t * g.N2);
   const int b = seq_of(g.cu_q, g.B, t);
   const int pos = t - g.cu_q[b];
   const int nblk = g.blk_off[b + 1] - g.blk_off[b];
@@ -329,6 +330,10 @@ __global__ __launch_bounds__(256) void nsa_row_fill(const int* topk, NsaGeom g, 
       if (nsa_keep(vj, pos, nblk, g.sbs, g.causal) && (vj < vi || (vj == vi && j < i))) rank++;
     }
     col[base + rank] = vi;
+    if (ekey) {
+      ekey[base + rank] = n2 * g.NB + g.blk_off[b] + vi;
+      etok[base + rank] = t;
+    }
   }
 }
 
@@ -336,22 +341,25 @@ __global__ __launch_bounds__(256) void nsa_row_fill(const int* topk, NsaGeom g, 
 // >= sbc) per row, 64 / P rows per wave; lane i of a row ranks slot i against
 // the row's other slots, fetched by lane shuffles.
 __global__ __launch_bounds__(256) void nsa_row_fill_wave(const int* topk, NsaGeom g,
-                                                         const int* row_ptr, int* col, int P) {
+                                                         const int* row_ptr, int* col, int* ekey,
+                                                         int* etok, int P) {
   const int lane = threadIdx.x & 63;
   const long wave = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int rpw = 64 / P;
   const long r = wave * rpw + lane / P;
   const int i = lane % P;
   const bool live = r < (long)g.T * g.N2;
-  int v = -1;
+  int v = -1, t = 0, key = 0;
   bool keep = false;
   if (live && i < g.sbc) {
-    const int t = (int)(r / g.N2);
+    t = (int)(r / g.N2);
+    const int n2 = (int)(r - (long)t * g.N2);
     const int b = seq_of(g.cu_q, g.B, t);
     const int pos = t - g.cu_q[b];
     const int nblk = g.blk_off[b + 1] - g.blk_off[b];
     v = topk[r * g.sbc + i];
     keep = nsa_keep(v, pos, nblk, g.sbs, g.causal);
+    key = n2 * g.NB + g.blk_off[b] + v;
   }
   const int base_lane = (lane / P) * P;
   int rank = 0;
@@ -360,7 +368,14 @@ __global__ __launch_bounds__(256) void nsa_row_fill_wave(const int* topk, NsaGeo
     const int kj = __shfl((int)keep, base_lane + j);
     rank += kj && (vj < v || (vj == v && j < i));
   }
-  if (live && keep) col[row_ptr[r] + rank] = v;
+  if (live && keep) {
+    const int e = row_ptr[r] + rank;
+    col[e] = v;
+    if (ekey) {
+      ekey[e] = key;
+      etok[e] = t;
+    }
+  }
 }
 
 // Occurrences of block id in a sorted row.
@@ -413,6 +428,69 @@ __global__ __launch_bounds__(256) void nsa_rev(NsaGeom g, const int* row_ptr, co
   }
 }
 
+// Reverse lists as a stable counting sort of the forward entries by their
+// reverse key (n2 * NB + global block): entries in forward order are cut
+// into tiles of `rounds` x 64; nsa_rev_hist counts each tile's keys,
+// an exclusive scan over (key, tile) in key-major order gives every tile its
+// first output slot per key, and nsa_rev_place writes the token ids.  Within
+// a wave, lanes holding the same key (found with one ballot per key bit)
+// are ranked by lane, and rounds run in order, so each list comes out in
+// forward-entry order: tokens ascending, a listed duplicate twice.
+__device__ __forceinline__ unsigned long long key_peers(int key, int bits, bool valid) {
+  unsigned long long m = __ballot(valid);
+  for (int b = 0; b < bits; b++) {
+    const bool bit = (key >> b) & 1;
+    const unsigned long long bb = __ballot(bit);
+    m &= bit ? bb : ~bb;
+  }
+  return m;
+}
+
+__global__ __launch_bounds__(64) void nsa_rev_hist(const int* n_entries, const int* ekey, int NK,
+                                                   int bits, int rounds, int n_tiles, int* hist) {
+  extern __shared__ int cnt[];
+  const int lane = threadIdx.x, tile = blockIdx.x;
+  const int E = n_entries[0];
+  for (int k = lane; k < NK; k += 64) cnt[k] = 0;
+  const long e0 = (long)tile * rounds * 64;
+  for (int rd = 0; rd < rounds && e0 + rd * 64 < E; rd++) {
+    const long e = e0 + rd * 64 + lane;
+    const bool valid = e < E;
+    const int key = valid ? ekey[e] : 0;
+    const unsigned long long m = key_peers(key, bits, valid);
+    if (valid && lane == __ffsll((long long)m) - 1) cnt[key] += __popcll(m);
+  }
+  for (int k = lane; k < NK; k += 64) hist[(long)k * n_tiles + tile] = cnt[k];
+}
+
+__global__ __launch_bounds__(64) void nsa_rev_place(const int* n_entries, const int* ekey,
+                                                    const int* etok, int NK, int bits, int rounds,
+                                                    int n_tiles, const int* hist, int* rev) {
+  extern __shared__ int cnt[];
+  const int lane = threadIdx.x, tile = blockIdx.x;
+  const int E = n_entries[0];
+  const long e0 = (long)tile * rounds * 64;
+  if (e0 >= E) return;
+  for (int k = lane; k < NK; k += 64) cnt[k] = hist[(long)k * n_tiles + tile];
+  const unsigned long long below = (1ull << lane) - 1;
+  for (int rd = 0; rd < rounds && e0 + rd * 64 < E; rd++) {
+    const long e = e0 + rd * 64 + lane;
+    const bool valid = e < E;
+    const int key = valid ? ekey[e] : 0;
+    const unsigned long long m = key_peers(key, bits, valid);
+    const int at = valid ? cnt[key] + __popcll(m & below) : 0;
+    if (valid) rev[at] = etok[e];
+    if (valid && lane == __ffsll((long long)m) - 1) cnt[key] += __popcll(m);
+  }
+}
+
+__global__ void nsa_rev_ptr(const int* n_entries, const int* hist, int NK, int n_tiles,
+                            int* rev_ptr) {
+  const long k = (long)blockIdx.x * 256 + threadIdx.x;
+  if (k < NK) rev_ptr[k] = hist[k * n_tiles];
+  if (k == NK) rev_ptr[k] = n_entries[0];
+}
+
 // Data check for validate = 1: counts ids outside [0, nblk).
 __global__ __launch_bounds__(256) void nsa_check_ids(const int* topk, NsaGeom g, int* bad) {
   const long r = (long)blockIdx.x * 256 + threadIdx.x;
@@ -436,7 +514,8 @@ hipError_t launch_nsa_check(const int* topk, const NsaGeom& g, int* bad, hipStre
 }
 
 hipError_t launch_nsa_forward_lists(const int* topk, const NsaGeom& g, int* cnt_scan, int* sums,
-                                    int* row_ptr, int* col, hipStream_t st) {
+                                    int* row_ptr, int* col, int* ekey, int* etok,
+                                    hipStream_t st) {
   const long rows = (long)g.T * g.N2;
   const unsigned rb = (unsigned)((rows + 255) / 256);
   // forward: counts -> scan -> fill
@@ -450,19 +529,47 @@ hipError_t launch_nsa_forward_lists(const int* topk, const NsaGeom& g, int* cnt_
     while (P < g.sbc) P <<= 1;
     const long waves = (rows + 64 / P - 1) / (64 / P);
     hipLaunchKernelGGL(nsa_row_fill_wave, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, topk,
-                       g, row_ptr, col, P);
+                       g, row_ptr, col, ekey, etok, P);
   } else {
-    hipLaunchKernelGGL(nsa_row_fill, dim3(rb), dim3(256), 0, st, topk, g, row_ptr, col);
+    hipLaunchKernelGGL(nsa_row_fill, dim3(rb), dim3(256), 0, st, topk, g, row_ptr, col, ekey, etok);
   }
   return hipGetLastError();
 }
 
+NsaRevSort nsa_rev_sort_plan(long max_entries, long n_keys) {
+  NsaRevSort r;
+  r.NK = (int)n_keys;
+  r.bits = 1;
+  while ((1L << r.bits) < n_keys) r.bits++;
+  r.rounds = 16;
+  // key-major (key, tile) counters: at most 8M of them
+  while ((max_entries + 64L * r.rounds - 1) / (64L * r.rounds) * n_keys > (8L << 20)) r.rounds *= 2;
+  r.n_tiles = (int)((max_entries + 64L * r.rounds - 1) / (64L * r.rounds));
+  if (r.n_tiles < 1) r.n_tiles = 1;
+  r.usable = n_keys >= 1 && n_keys <= kNsaRevMaxKeys;
+  return r;
+}
+
 hipError_t launch_nsa_reverse_lists(const NsaGeom& g, const int* row_ptr, const int* col,
                                     int* sums, int* rev_scan, int* rev_ptr, int* rev,
-                                    hipStream_t st) {
+                                    const int* ekey, const int* etok, const NsaRevSort& rs,
+                                    int* hist, int* hsums, hipStream_t st) {
   // reverse: counts -> scan -> fill
   const long rrows = (long)g.N2 * g.NB;
   if (rrows == 0) return hipMemsetAsync(rev_ptr, 0, sizeof(int), st);
+  if (ekey && rs.usable) {
+    const int* n_entries = row_ptr + (long)g.T * g.N2;
+    const size_t lds = sizeof(int) * rs.NK;
+    hipLaunchKernelGGL(nsa_rev_hist, dim3(rs.n_tiles), dim3(64), lds, st, n_entries, ekey, rs.NK,
+                       rs.bits, rs.rounds, rs.n_tiles, hist);
+    hipError_t e = exclusive_scan(hist, (long)rs.NK * rs.n_tiles, hsums, st);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(nsa_rev_place, dim3(rs.n_tiles), dim3(64), lds, st, n_entries, ekey, etok,
+                       rs.NK, rs.bits, rs.rounds, rs.n_tiles, (const int*)hist, rev);
+    hipLaunchKernelGGL(nsa_rev_ptr, dim3((unsigned)((rs.NK + 1 + 255) / 256)), dim3(256), 0, st,
+                       n_entries, (const int*)hist, rs.NK, rs.n_tiles, rev_ptr);
+    return hipGetLastError();
+  }
   const unsigned wb = (unsigned)rrows;
   hipLaunchKernelGGL(nsa_rev<0>, dim3(wb), dim3(256), 0, st, g, row_ptr, col, rev_scan,
                      (const int*)nullptr, (int*)nullptr);
@@ -475,12 +582,5 @@ hipError_t launch_nsa_reverse_lists(const NsaGeom& g, const int* row_ptr, const 
   return hipGetLastError();
 }
 
-hipError_t launch_nsa_compact(const int* topk, const NsaGeom& g, int* cnt_scan, int* sums,
-                              int* row_ptr, int* col, int* rev_scan, int* rev_ptr, int* rev,
-                              hipStream_t st) {
-  hipError_t e = launch_nsa_forward_lists(topk, g, cnt_scan, sums, row_ptr, col, st);
-  if (e == hipSuccess) e = launch_nsa_reverse_lists(g, row_ptr, col, sums, rev_scan, rev_ptr, rev, st);
-  return e;
-}
 
 }  // namespace tsa

@@ -31,16 +31,25 @@ struct NsaGeom {
   int B, T, N2, sbc, sbs, causal, NB;
 };
 
-hipError_t launch_nsa_compact(const int* topk, const NsaGeom& g, int* cnt_scan, int* sums,
-                              int* row_ptr, int* col, int* rev_scan, int* rev_ptr, int* rev,
-                              hipStream_t st);
-// The two halves of launch_nsa_compact: per-row sorted lists, then the
-// reverse lists built from them.
+
+// NSA list building.  Forward: per-row sorted lists (row_ptr, col), plus
+// each entry's reverse key n2*NB + global block and token id when ekey is
+// given.  Reverse: per (n2, block) ascending token lists, by a stable
+// counting sort of those entries when the key count allows (rs.usable),
+// else by a per-list scan of the forward rows.
+constexpr int kNsaRevMaxKeys = 16384;  // LDS counters of one sort tile (64 KB)
+struct NsaRevSort {
+  int NK, bits, rounds, n_tiles;
+  bool usable;
+};
+NsaRevSort nsa_rev_sort_plan(long max_entries, long n_keys);
 hipError_t launch_nsa_forward_lists(const int* topk, const NsaGeom& g, int* cnt_scan, int* sums,
-                                    int* row_ptr, int* col, hipStream_t st);
+                                    int* row_ptr, int* col, int* ekey, int* etok,
+                                    hipStream_t st);
 hipError_t launch_nsa_reverse_lists(const NsaGeom& g, const int* row_ptr, const int* col,
                                     int* sums, int* rev_scan, int* rev_ptr, int* rev,
-                                    hipStream_t st);
+                                    const int* ekey, const int* etok, const NsaRevSort& rs,
+                                    int* hist, int* hsums, hipStream_t st);
 hipError_t launch_nsa_check(const int* topk, const NsaGeom& g, int* bad, hipStream_t st);
 
 // ----- block-sparse attention ---------------------------------------------
