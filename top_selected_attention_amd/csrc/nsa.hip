@@ -291,6 +291,13 @@ __global__ __launch_bounds__(256) void nsa_dq_kernel(NsaParams p, int n_items) {
 // ---------------------------------------------------------------------------
 constexpr int kSegEntries = 256;
 
+// Workgroups of the dK/dV partial kernel: about three resident per CU on
+// 256 CUs, a multiple of the 8 XCDs, never more than the segments.
+int nsa_dkdv_grid(const NsaParams& p) {
+  const int g = std::min(kNsaDkdvMaxGrid, std::max(1, p.max_segments));
+  return 8 * ((g + 7) / 8);
+}
+
 int nsa_max_segments(long total_entries, long nblocks) {
   return (int)(nblocks + (total_entries + kSegEntries - 1) / kSegEntries);
 }
@@ -302,33 +309,74 @@ __global__ void nsa_seg_count(const int* rev_ptr, int nblocks, int* seg_cnt) {
   seg_cnt[r] = max(1, (len + kSegEntries - 1) / kSegEntries);
 }
 
+// Static balance of segments over `grid` workgroups: workgroup w takes the
+// segments whose first listing lies in [w*E/grid, (w+1)*E/grid) of the E
+// listings of all reverse lists (an empty list's one segment counts at its
+// position).  One thread per (KV head, block) writes the first segment of
+// every workgroup whose range starts among its segments.
+__global__ void nsa_seg_bounds(const int* rev_ptr, const int* seg_off, int nblocks, int grid,
+                               int* wg_first) {
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  if (r >= nblocks) return;
+  const long E = max(rev_ptr[nblocks], 1);
+  const int total = seg_off[nblocks];
+  auto wg_of = [&](long start) { return (int)min((long)grid - 1, start * grid / E); };
+  int w_prev = -1;
+  if (r > 0) {
+    const int nprev = seg_off[r] - seg_off[r - 1];
+    w_prev = wg_of(rev_ptr[r - 1] + (long)kSegEntries * (nprev - 1));
+  }
+  const int nseg = seg_off[r + 1] - seg_off[r];
+  for (int k = 0; k < nseg; k++) {
+    const int w = wg_of(rev_ptr[r] + (long)kSegEntries * k);
+    for (int x = w_prev + 1; x <= w; x++) wg_first[x] = seg_off[r] + k;
+    w_prev = w;
+  }
+  if (r == nblocks - 1)
+    for (int x = w_prev + 1; x <= grid; x++) wg_first[x] = total;
+}
+
 template <class E, int NW>
-__global__ __launch_bounds__(NW * 64) void nsa_dkdv_seg_kernel(NsaParams p, const int* seg_off,
-                                                               int nblocks, float* part) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void nsa_dkdv_seg_kernel(NsaParams p, const int* wg_first, int nblocks, float* part) {
   typedef typename E::T T;
   typedef typename E::V8 V8;
-  constexpr int kTileB = 64 * kD * 2;
-  __shared__ __attribute__((aligned(1024))) char lds_q[2][kTileB];
-  __shared__ __attribute__((aligned(1024))) char lds_do[2][kTileB];
+  constexpr int kQC = 32;                  // query rows per chunk
+  constexpr int kQTile = kQC * kD * 2;
+  __shared__ __attribute__((aligned(1024))) char lds_k[NW * 32 * kD * 2];
+  __shared__ __attribute__((aligned(1024))) char lds_q[2][kQTile];
+  __shared__ __attribute__((aligned(1024))) char lds_do[2][kQTile];
+  // a direct LDS load writes all 64 lanes' dwords: rows 32..63 are never read
   __shared__ float lds_lse[2][64];
   __shared__ float lds_dlt[2][64];
   __shared__ int lds_pos[2][64];
   __shared__ int lds_tok[kSegEntries];  // the segment's token ids
 
   const NsaGeom& g = p.g;
-  const int total = seg_off[nblocks];
-  // contiguous segment ranges per workgroup (XCD-remapped: an XCD's
-  // workgroups hold neighbouring segments, which share K/V and tokens)
+  const int* seg_off = p.seg_off;
+  // balanced contiguous segment ranges (XCD-remapped: an XCD's workgroups
+  // hold neighbouring segments, which share K/V and tokens)
   const int w = xcd_remap(blockIdx.x, gridDim.x);
-  const int per = (total + gridDim.x - 1) / gridDim.x;
-  const int s_lo = w < 0 ? total : w * per;
-  const int s_hi = min(s_lo + per, total);
+  if (w < 0) return;
+  const int s_lo = wg_first[w], s_hi = wg_first[w + 1];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5;
   const int G = p.G;
-  const int tpc = 64 / G;
+  const int tpc = max(1, kQC / G);  // tokens per chunk (G <= 32)
   const int sbs = g.sbs;
   const float sl2 = p.scale * kLog2e;
+  // chunk row -> (token of the chunk, head): shifts when G is a power of two
+  const bool gpow2 = (G & (G - 1)) == 0;
+  const int gsh = __builtin_ctz(G);
+  auto div_g = [&](int x, int& qq, int& rr) {
+    if (gpow2) {
+      qq = x >> gsh;
+      rr = x & (G - 1);
+    } else {
+      qq = x / G;
+      rr = x - qq * G;
+    }
+  };
 
   for (int sg = s_lo; sg < s_hi; sg++) {
     // segment -> block (largest r with seg_off[r] <= sg)
@@ -346,18 +394,31 @@ __global__ __launch_bounds__(NW * 64) void nsa_dkdv_seg_kernel(NsaParams p, cons
     const int skv = g.cu_kv[b + 1] - kv0;
     const int key_lo = blk * sbs;
     const int key_hi = min((blk + 1) * sbs, skv);
-    const int mykey = key_lo + wid * 32 + l32;
-    const bool key_ok = mykey < key_hi;
+    const int wkey0 = key_lo + wid * 32;
     const int e0 = p.rev_ptr[r] + k * kSegEntries;
     const int e1 = min(e0 + kSegEntries, p.rev_ptr[r + 1]);
 
-    const long krow = ((long)(kv0 + min(mykey, key_hi - 1)) * p.N2 + n2) * kD;
-    V8 kreg[8], vreg[8];
+    // K rows of the block into LDS (rows past key_hi re-read the last key);
+    // V rows of this wave's keys as the B operand of dP in registers
+    {
+      const int sub = lane >> 4, pc = lane & 15;
 #pragma unroll
-    for (int ds = 0; ds < 8; ds++) {
-      const long off = krow + ds * 16 + 8 * h;
-      kreg[ds] = key_ok ? as_v8<V8>(ld16((const T*)p.k + off)) : zero_v8<V8>();
-      vreg[ds] = key_ok ? as_v8<V8>(ld16((const T*)p.v + off)) : zero_v8<V8>();
+      for (int u = 0; u < 8; u++) {
+        const int inst = wid * 8 + u;
+        const int rr = inst * 4 + sub;
+        const long key = kv0 + min(key_lo + rr, key_hi - 1);
+        g2lds16((const char*)((const T*)p.k + (key * p.N2 + n2) * kD) + ((pc ^ swz(rr)) << 4),
+                lds_k + inst * 1024);
+      }
+    }
+    V8 vreg[8];
+    {
+      const int mykey = wkey0 + l32;
+      const long vrow = ((long)(kv0 + min(mykey, key_hi - 1)) * p.N2 + n2) * kD;
+#pragma unroll
+      for (int ds = 0; ds < 8; ds++)
+        vreg[ds] = mykey < key_hi ? as_v8<V8>(ld16((const T*)p.v + vrow + ds * 16 + 8 * h))
+                                  : zero_v8<V8>();
     }
     const int nchunks = (e1 - e0 + tpc - 1) / tpc;
     // the segment's token ids into LDS once, so chunk addresses need no
@@ -365,35 +426,45 @@ __global__ __launch_bounds__(NW * 64) void nsa_dkdv_seg_kernel(NsaParams p, cons
     for (int x = tid; x < e1 - e0; x += NW * 64) lds_tok[x] = p.rev[e0 + x];
     __syncthreads();
 
-    // chunk row r -> (entry c*tpc + r/G of the segment, head r%G); rows past
-    // the chunk's tokens re-read its last valid row and are masked
-    auto row_of = [&](int c, int rr) {
-      const int nt = min(tpc, e1 - e0 - c * tpc);
-      const int tk = min(rr / G, nt - 1);
-      const int gg = (rr / G < nt && rr < tpc * G) ? rr % G : G - 1;
-      const int t = lds_tok[c * tpc + tk];
-      return (long)t * p.N1 + n2 * G + gg;
-    };
+    // chunk row rr -> (entry c*tpc + rr/G of the segment, head rr%G); rows
+    // past the chunk's tokens re-read its last valid row and are masked.
+    // The token ids of all of a wave's rows are read from LDS first, then
+    // the direct loads are issued.
     auto load_chunk = [&](int c, int buf) {
-      const int sub = lane >> 4, pc = lane & 15;
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int sub = ln >> 4, pc = ln & 15;
+      const int nt = min(tpc, e1 - e0 - c * tpc);
+      constexpr int U = 8 / NW;
+      int tok[U], gh[U];
 #pragma unroll
-      for (int u = 0; u < 16 / NW; u++) {
-        const int inst = wid * (16 / NW) + u;
+      for (int u = 0; u < U; u++) {
+        const int rr = (wid * U + u) * 4 + sub;
+        int tq, tr;
+        div_g(rr, tq, tr);
+        gh[u] = (tq < nt && rr < tpc * G) ? tr : G - 1;
+        tok[u] = lds_tok[c * tpc + min(tq, nt - 1)];
+      }
+#pragma unroll
+      for (int u = 0; u < U; u++) {
+        const int inst = wid * U + u;
         const int rr = inst * 4 + sub;
-        const long qrw = row_of(c, rr);
+        const long qrw = (long)tok[u] * p.N1 + n2 * G + gh[u];
         g2lds16((const char*)((const T*)p.q + qrw * kD) + ((pc ^ swz(rr)) << 4),
                 lds_q[buf] + inst * 1024);
         g2lds16((const char*)((const T*)p.dout + qrw * kD) + ((pc ^ swz(rr)) << 4),
                 lds_do[buf] + inst * 1024);
       }
       if (wid == 0) {
-        const long qrw = row_of(c, lane);
+        int tq, tr;
+        div_g(ln & 31, tq, tr);
+        const bool valid = ln < kQC && tq < nt && ln < tpc * G;
+        const int t = lds_tok[c * tpc + min(tq, nt - 1)];
+        const long qrw = (long)t * p.N1 + n2 * G + (valid ? tr : G - 1);
         g2lds4(p.lse + qrw, lds_lse[buf]);
         g2lds4(p.delta + qrw, lds_dlt[buf]);
-        const int nt = min(tpc, e1 - e0 - c * tpc);
-        const bool valid = lane / G < nt && lane < tpc * G;
         // position of the row's token, or -1 for padding rows (always masked)
-        lds_pos[buf][lane] = valid ? lds_tok[c * tpc + lane / G] - q0 : -1;
+        lds_pos[buf][ln] = valid ? t - q0 : -1;
       }
     };
 
@@ -409,55 +480,64 @@ __global__ __launch_bounds__(NW * 64) void nsa_dkdv_seg_kernel(NsaParams p, cons
     int buf = 0;
     for (int c = 0; c < nchunks; c++) {
       if (c + 1 < nchunks) load_chunk(c + 1, buf ^ 1);
+      // lane terms of this iteration from an opaque lane id (not kept, and
+      // spilled, across iterations)
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int l32i = ln & 31, hi2 = ln >> 5;
       const char* Qb = lds_q[buf];
       const char* Db = lds_do[buf];
+      // S = Q K^T and dP = dO V^T: 32 rows x this wave's 32 keys
+      f32x16 sc, dp;
 #pragma unroll
-      for (int qt = 0; qt < 2; qt++) {
-        f32x16 sc, dp;
+      for (int j = 0; j < 16; j++) sc[j] = dp[j] = 0.f;
 #pragma unroll
-        for (int j = 0; j < 16; j++) sc[j] = dp[j] = 0.f;
-#pragma unroll
-        for (int ds = 0; ds < 8; ds++) {
-          sc = E::mfma32(tile_read16<V8>(Qb, qt * 32 + l32, 2 * ds + h), kreg[ds], sc);
-          dp = E::mfma32(tile_read16<V8>(Db, qt * 32 + l32, 2 * ds + h), vreg[ds], dp);
-        }
-        V8 bp[2], bd[2];
-#pragma unroll
-        for (int j4 = 0; j4 < 4; j4++) {
-          const int rbase = qt * 32 + 8 * j4 + 4 * h;
-          const float4 lse4 = *reinterpret_cast<const float4*>(&lds_lse[buf][rbase]);
-          const float4 dl4 = *reinterpret_cast<const float4*>(&lds_dlt[buf][rbase]);
-          const int4 ps4 = *reinterpret_cast<const int4*>(&lds_pos[buf][rbase]);
-          const float lv[4] = {lse4.x, lse4.y, lse4.z, lse4.w};
-          const float dv[4] = {dl4.x, dl4.y, dl4.z, dl4.w};
-          const int pv4[4] = {ps4.x, ps4.y, ps4.z, ps4.w};
-#pragma unroll
-          for (int jj = 0; jj < 4; jj++) {
-            const int j = 4 * j4 + jj;
-            // a valid row (pos >= 0) at or after this key (causal) keeps it
-            const int need = g.causal ? mykey : 0;
-            const bool ok = key_ok && pv4[jj] >= need;
-            float pr = fast_exp2(__builtin_fmaf(sc[j], sl2, -lv[jj] * kLog2e));
-            pr = ok ? pr : 0.f;
-            bp[j >> 3][j & 7] = E::from_f32(pr);
-            bd[j >> 3][j & 7] = E::from_f32(pr * (dp[j] - dv[jj]));
-          }
-        }
-#pragma unroll
-        for (int k2 = 0; k2 < 2; k2++)
-#pragma unroll
-          for (int dt = 0; dt < 4; dt++) {
-            dvt[dt] = E::mfma32(tile_read_tr<V8>(Db, qt * 2 + k2, dt), bp[k2], dvt[dt]);
-            dkt[dt] = E::mfma32(tile_read_tr<V8>(Qb, qt * 2 + k2, dt), bd[k2], dkt[dt]);
-          }
+      for (int ds = 0; ds < 8; ds++) {
+        sc = E::mfma32(tile_read16<V8>(Qb, l32i, 2 * ds + hi2),
+                       tile_read16<V8>(lds_k, wid * 32 + l32i, 2 * ds + hi2), sc);
+        dp = E::mfma32(tile_read16<V8>(Db, l32i, 2 * ds + hi2), vreg[ds], dp);
       }
+      // element j of a lane is row 8*(j/4) + 4*h + j%4 of the chunk, column key l32
+      const int mykey = wkey0 + l32i;
+      const int need = g.causal ? mykey : 0;
+      const bool key_ok = mykey < key_hi;
+      V8 bp[2], bd[2];
+#pragma unroll
+      for (int j4 = 0; j4 < 4; j4++) {
+        const int rbase = 8 * j4 + 4 * hi2;
+        const float4 lse4 = *reinterpret_cast<const float4*>(&lds_lse[buf][rbase]);
+        const float4 dl4 = *reinterpret_cast<const float4*>(&lds_dlt[buf][rbase]);
+        const int4 ps4 = *reinterpret_cast<const int4*>(&lds_pos[buf][rbase]);
+        const float lv[4] = {lse4.x, lse4.y, lse4.z, lse4.w};
+        const float dv[4] = {dl4.x, dl4.y, dl4.z, dl4.w};
+        const int pv4[4] = {ps4.x, ps4.y, ps4.z, ps4.w};
+#pragma unroll
+        for (int jj = 0; jj < 4; jj++) {
+          const int j = 4 * j4 + jj;
+          // a valid row (pos >= 0) at or after this key (causal) keeps it
+          const bool ok = key_ok && pv4[jj] >= need;
+          float pr = fast_exp2(__builtin_fmaf(sc[j], sl2, -lv[jj] * kLog2e));
+          pr = ok ? pr : 0.f;
+          bp[j >> 3][j & 7] = E::from_f32(pr);
+          bd[j >> 3][j & 7] = E::from_f32(pr * (dp[j] - dv[jj]));
+        }
+      }
+      // dV^T += dO^T P ; dK^T += Q^T dS  (16 rows per step)
+#pragma unroll
+      for (int k2 = 0; k2 < 2; k2++)
+#pragma unroll
+        for (int dt = 0; dt < 4; dt++) {
+          dvt[dt] = E::mfma32(tile_read_tr<V8>(Db, k2, dt, ln), bp[k2], dvt[dt]);
+          dkt[dt] = E::mfma32(tile_read_tr<V8>(Qb, k2, dt, ln), bd[k2], dkt[dt]);
+        }
       wait_vm();
       __syncthreads();
       buf ^= 1;
     }
 
     // fp32 partials of this segment: [segment][key within block][d], dK then dV
-    if (key_ok) {
+    const int mykey = wkey0 + l32;
+    if (mykey < key_hi) {
       float* pk = part + ((long)sg * 2 * sbs + (mykey - key_lo)) * kD;
       float* pv = pk + (long)sbs * kD;
 #pragma unroll
@@ -545,15 +625,17 @@ static hipError_t bwd_t(const NsaParams& p, hipStream_t st, void* const* ev, int
   }
   if (e == hipSuccess && nb > 0) {
     const int nw = (p.g.sbs + 31) / 32;  // 1..4 waves, 32 keys each
-    const int grid = 8 * ((std::min(p.max_segments, 2048) + 7) / 8);
+    const int grid = nsa_dkdv_grid(p);
+    hipLaunchKernelGGL(nsa_seg_bounds, dim3((nb + 255) / 256), dim3(256), 0, st, p.rev_ptr,
+                       p.seg_off, nb, grid, p.wg_first);
     if (nw <= 1)
-      hipLaunchKernelGGL((nsa_dkdv_seg_kernel<E, 1>), dim3(grid), dim3(64), 0, st, p, p.seg_off, nb,
-                         p.part);
+      hipLaunchKernelGGL((nsa_dkdv_seg_kernel<E, 1>), dim3(grid), dim3(64), 0, st, p, p.wg_first,
+                         nb, p.part);
     else if (nw <= 2)
-      hipLaunchKernelGGL((nsa_dkdv_seg_kernel<E, 2>), dim3(grid), dim3(128), 0, st, p, p.seg_off,
+      hipLaunchKernelGGL((nsa_dkdv_seg_kernel<E, 2>), dim3(grid), dim3(128), 0, st, p, p.wg_first,
                          nb, p.part);
     else
-      hipLaunchKernelGGL((nsa_dkdv_seg_kernel<E, 4>), dim3(grid), dim3(256), 0, st, p, p.seg_off,
+      hipLaunchKernelGGL((nsa_dkdv_seg_kernel<E, 4>), dim3(grid), dim3(256), 0, st, p, p.wg_first,
                          nb, p.part);
     e = hipGetLastError();
   }

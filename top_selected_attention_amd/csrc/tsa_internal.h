@@ -101,10 +101,13 @@ struct NsaParams {
   int* seg_off;        // [N2*NB + 1] exclusive scan of segments per block
   int* seg_sums;       // scan scratch
   float* part;         // [max_segments][2][sbs][D] fp32 partial dK, dV
+  int* wg_first;       // [grid + 1] first segment of each dK/dV workgroup
   int max_segments;
 };
 
 int nsa_max_segments(long total_entries, long nblocks);
+constexpr int kNsaDkdvMaxGrid = 768;
+int nsa_dkdv_grid(const NsaParams& p);
 
 hipError_t launch_nsa_fwd(const NsaParams& p, int fp16, hipStream_t st);
 hipError_t launch_nsa_bwd(const NsaParams& p, int fp16, hipStream_t st, void* const* ev, int n_ev);
