@@ -7,12 +7,13 @@
 // which the dK/dV kernel does by walking, per KV block, the tokens that
 // selected it (reverse list) -- one owner per output row, no atomics.
 //
-// Forward and dQ: one wave per (token, KV head).  Its G query heads are the
-// query columns of a 32-wide MFMA tile (G <= 32; columns past G are padding:
-// the work is bound by gathering K/V, at ~16 FLOP per gathered byte, not by
-// MFMA).  The selected blocks are walked in 32-key chunks that the wave stages
-// into its own LDS region (direct global -> LDS loads) -- no workgroup
-// barrier; the other waves on the SIMD cover the load latency.
+// Forward and dQ: one wave per (token, KV head), walking the selected blocks
+// in 32-key chunks through its own LDS region -- no workgroup barrier.  The
+// work is bound by gathering K/V (about 16 FLOP per gathered byte, nearly all
+// of it served by L2), not by MFMA.  Head groups of up to 16 query heads use
+// 16x16x32 MFMA with the group's heads as the 16 columns, and stage the next
+// chunk in registers while the current one computes; larger groups (up to
+// 32) use a 32-wide tile staged by direct global -> LDS loads.
 #include <algorithm>
 
 #include "tsa_device.h"
@@ -45,6 +46,20 @@ __device__ __forceinline__ void stage32_wave(char* tile, RowPtr rowptr) {
     const int r = inst * 4 + sub;
     g2lds16(rowptr(r) + ((pc ^ swz(r)) << 4), tile + inst * 1024);
   }
+}
+
+// Per-wave 32-key tile of the 16-head kernels: key k sits in row
+// 16*(k/16) + 2*(k%8) + (k/8)%2, rows 272 bytes apart (one 16-byte bank group
+// further per row).  Stores of whole rows, reads of one piece from 16
+// consecutive keys, and transposed reads of 32 bytes from 8 consecutive keys
+// then all touch distinct banks, and every lane's addresses are one base plus
+// compile-time offsets (no per-access address registers).
+constexpr int kPitch = 272;
+constexpr int kTile16 = kChunk * kPitch;
+__device__ __forceinline__ int key_row(int k) { return (k & 16) | ((k & 7) << 1) | ((k >> 3) & 1); }
+// Row of key 4*u + s (0 <= s < 4) is key_row(4*u) + 2*s.
+__device__ __forceinline__ constexpr int key_row4(int u) {
+  return 16 * (u >> 2) + 8 * (u & 1) + ((u >> 1) & 1);
 }
 }  // namespace
 
@@ -169,6 +184,184 @@ __global__ __launch_bounds__(256) void nsa_fwd_kernel(NsaParams p, int n_items) 
 }
 
 // ---------------------------------------------------------------------------
+// Forward for head groups of up to 16 query heads: one wave per (token, KV
+// head) on 16x16x32 MFMA (the group's heads are the 16 columns).  The next
+// chunk's K and V rows are loaded into registers while the current chunk
+// computes, each quarter-wave reading one whole 256-byte row (L1 tag lookups,
+// not bytes, limit a gather whose 16 lanes touch 16 rows).  K is written to
+// the wave's LDS tile and read back as the A operand of S^T = K Q^T; V then
+// overwrites it and is read back transposed as the A operand of
+// O^T += V^T P^T.  One 8.5 KB tile per wave and at most 168 VGPRs keep three
+// waves on each SIMD.
+// ---------------------------------------------------------------------------
+template <class E>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
+void nsa_fwd16_kernel(NsaParams p, int n_items) {
+  typedef typename E::T T;
+  typedef typename E::V8 V8;
+  typedef float f32x4_t __attribute__((ext_vector_type(4)));
+  __shared__ __attribute__((aligned(1024))) char lds[4][kTile16];  // per wave: K, then V
+
+  const int item = xcd_remap(blockIdx.x, n_items);
+  if (item < 0) return;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int l16 = lane & 15, gq = lane >> 4;
+  // unit order: KV-head-major, tokens ascending (a sequence's K/V stay hot)
+  const int unit = item * 4 + wid;
+  if (unit >= p.T * p.N2) return;
+  const int n2 = unit / p.T, t = unit % p.T;
+  const NsaGeom& g = p.g;
+  const int b = seq_of_dev(g.cu_q, g.B, t);
+  const int pos = t - g.cu_q[b];
+  const int kv0 = g.cu_kv[b];
+  const int G = p.G;
+  char* Tl = lds[wid];
+
+  // Q^T as the B operand: lane (head l16, quarter gq) holds dims 32*ks + 8*gq .. +7
+  const bool col_ok = l16 < G;
+  V8 qreg[4];
+  {
+    const T* qrow = (const T*)p.q + ((long)t * p.N1 + n2 * G + (col_ok ? l16 : 0)) * kD;
+#pragma unroll
+    for (int ks = 0; ks < 4; ks++)
+      qreg[ks] = col_ok ? as_v8<V8>(ld16(qrow + 32 * ks + 8 * gq)) : zero_v8<V8>();
+  }
+
+  const long row = (long)t * p.N2 + n2;
+  const int e0 = p.row_ptr[row], e1 = p.row_ptr[row + 1];
+  const ShortList blocks(p.col + e0, e1 - e0);  // sbc <= 128 entries
+  const int sbs = g.sbs;
+  const int cpb = (sbs + kChunk - 1) / kChunk;
+  const float sl2 = p.scale * kLog2e;
+  const long kstride = (long)p.N2 * kD;  // elements between consecutive tokens of one KV head
+  const T* kbase = (const T*)p.k + ((long)kv0 * p.N2 + n2) * kD;
+  const T* vbase = (const T*)p.v + ((long)kv0 * p.N2 + n2) * kD;
+
+  auto chunk_range = [&](ChunkPos c, int& ks, int& ke) {
+    const int blk = blocks(c.e - e0);
+    ks = blk * sbs + c.s * kChunk;
+    ke = min(ks + kChunk, (blk + 1) * sbs);
+  };
+  auto next_valid = [&](ChunkPos c) {
+    for (; c.e < e1; c = chunk_advance(c, cpb)) {
+      int ks, ke;
+      chunk_range(c, ks, ke);
+      if (!(g.causal && ks > pos)) break;  // wholly after the token: skipped
+    }
+    return c;
+  };
+  // K and V chunks as 32 x 256-byte tiles, 8 16-byte pieces per lane (row
+  // 4*u + lane/16, piece lane%16): every quarter-wave reads one whole row.
+  // Keys past the chunk's end re-read its last key.
+  const int rstride = p.N2 * kD;  // elements between consecutive tokens of one KV head
+  auto load = [&](const T* base, ChunkPos c, uint4 (&r8)[8]) {
+    int ks, ke;
+    chunk_range(c, ks, ke);
+    const T* cb = base + (long)ks * kstride + 8 * (lane & 15);
+    const int last = ke - 1 - ks;  // rows past it re-read the chunk's last key
+#pragma unroll
+    for (int u = 0; u < 8; u++) r8[u] = ld16(cb + min(4 * u + (lane >> 4), last) * rstride);
+  };
+  // tile bases: row stores (key 4*u + gq, piece l16), A-operand reads (key
+  // 16*kt + l16, piece 4*q4 + gq), transposed reads (keys 4*gq + l16/4 and
+  // +16, bytes 32*dt + 8*(l16%4) ..)
+  char* const Tw = Tl + 2 * gq * kPitch + 16 * l16;
+  char* const Tr = Tl + key_row(l16) * kPitch + 16 * gq;
+  char* const Tt = Tl + key_row(4 * gq + (l16 >> 2)) * kPitch + 8 * (l16 & 3);
+  auto to_lds = [&](const uint4 (&r8)[8]) {
+#pragma unroll
+    for (int u = 0; u < 8; u++) *reinterpret_cast<uint4*>(Tw + key_row4(u) * kPitch) = r8[u];
+  };
+
+  constexpr float kLazy = 8.f;
+  float m = -INFINITY, lsum = 0.f;
+  f32x4_t o[8];  // O^T tiles: d = 16*dt + 4*gq + j, column head l16
+#pragma unroll
+  for (int dt = 0; dt < 8; dt++) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  uint4 kr[8], vr[8];
+  // One step per chunk c, whose K and V loads are in flight; nx is the next
+  // chunk (c itself after the last one, so the loads stay unconditional).
+  // The wave's one LDS tile holds K, then V: LDS operations of a wave run in
+  // order, so V's stores follow the S reads of K.
+  auto step = [&](ChunkPos c, ChunkPos nx) {
+    int ks, ke;
+    chunk_range(c, ks, ke);
+    to_lds(kr);
+    load(kbase, nx, kr);
+    // S^T tiles: element j of st[kt] is key ks + 16*kt + 4*gq + j, column head
+    // l16; A operand = key row 16*kt + l16, dims 32*q4 + 8*gq ..
+    f32x4_t st[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; kt++) {
+      st[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int q4 = 0; q4 < 4; q4++)
+        st[kt] = E::mfma16(lds_read16<V8>(Tr + kt * 16 * kPitch + 64 * q4), qreg[q4], st[kt]);
+    }
+    to_lds(vr);
+    load(vbase, nx, vr);
+    const int lim = min(ke - 1, g.causal ? pos : 0x7fffffff) - ks;  // last kept key offset
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; kt++)
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const float v = (16 * kt + 4 * gq + j) <= lim ? st[kt][j] : -INFINITY;
+        st[kt][j] = v;
+        mx = fmaxf(mx, v);
+      }
+    mx = max_xor16_32(mx) * sl2;
+    if (__builtin_amdgcn_ballot_w64(mx > m + kLazy)) {
+      const float m_new = fmaxf(m, mx);
+      const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m - m_new);
+      m = m_new;
+      lsum *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 8; dt++) o[dt] *= alpha;
+    }
+    const float mneg = m == -INFINITY ? 0.f : -m;
+    V8 pb;
+#pragma unroll
+    for (int kt = 0; kt < 2; kt++)
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const float pv = fast_exp2(__builtin_fmaf(st[kt][j], sl2, mneg));
+        lsum += pv;
+        pb[4 * kt + j] = E::from_f32(pv);
+      }
+    // O^T += V^T P^T: V^T rows d = 16*dt + l16, keys {4gq..4gq+3, 16+4gq..16+4gq+3}
+#pragma unroll
+    for (int dt = 0; dt < 8; dt++)
+      o[dt] = E::mfma16(lds_read_tr_pair<V8>(Tt + 32 * dt, Tt + 16 * kPitch + 32 * dt), pb, o[dt]);
+  };
+
+  ChunkPos c = next_valid(ChunkPos{e0, 0});
+  if (c.e < e1) {
+    load(kbase, c, kr);
+    load(vbase, c, vr);
+  }
+  while (c.e < e1) {
+    const ChunkPos nx = next_valid(chunk_advance(c, cpb));
+    step(c, nx.e < e1 ? nx : c);
+    c = nx;
+  }
+
+  float lt = lsum + __shfl_xor(lsum, 16);
+  lt += __shfl_xor(lt, 32);
+  if (col_ok) {
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const long orow = (long)t * p.N1 + n2 * G + l16;
+    T* op = (T*)p.out + orow * kD;
+#pragma unroll
+    for (int dt = 0; dt < 8; dt++)
+      *reinterpret_cast<uint2*>(op + 16 * dt + 4 * gq) =
+          pack4<E>(o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv);
+    if (gq == 0) p.lse[orow] = lt > 0.f ? (m + log2f(lt)) * kLn2 : -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // dQ (+ softmax_grad): one wave per (token, KV head)
 // ---------------------------------------------------------------------------
 template <class E>
@@ -274,6 +467,167 @@ __global__ __launch_bounds__(256) void nsa_dq_kernel(NsaParams p, int n_items) {
             pack4<E>(dq[dt][4 * jj] * p.scale, dq[dt][4 * jj + 1] * p.scale,
                      dq[dt][4 * jj + 2] * p.scale, dq[dt][4 * jj + 3] * p.scale);
       }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ for head groups of up to 16 query heads, on 16x16x32 MFMA with the same
+// register-staged gather and single LDS tile as the 16-head forward:
+// dP^T = V dO^T from the V tile, then K replaces it for S^T = K Q^T,
+// dS^T = P^T (dP^T - softmax_grad), and dQ^T += K^T dS^T with K^T read
+// transposed from the tile.
+// ---------------------------------------------------------------------------
+template <class E>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
+void nsa_dq16_kernel(NsaParams p, int n_items) {
+  typedef typename E::T T;
+  typedef typename E::V8 V8;
+  typedef float f32x4_t __attribute__((ext_vector_type(4)));
+  __shared__ __attribute__((aligned(1024))) char lds[4][kTile16];  // per wave: V, then K
+
+  const int item = xcd_remap(blockIdx.x, n_items);
+  if (item < 0) return;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int l16 = lane & 15, gq = lane >> 4;
+  const int unit = item * 4 + wid;
+  if (unit >= p.T * p.N2) return;
+  const int n2 = unit / p.T, t = unit % p.T;
+  const NsaGeom& g = p.g;
+  const int b = seq_of_dev(g.cu_q, g.B, t);
+  const int pos = t - g.cu_q[b];
+  const int kv0 = g.cu_kv[b];
+  const int G = p.G;
+  char* Tl = lds[wid];
+
+  // Q^T and dO^T as B operands: lane (head l16, quarter gq) holds dims
+  // 32*ks + 8*gq .. +7; softmax_grad = rowsum(dO * O) of head l16.
+  const bool col_ok = l16 < G;
+  const long qr = (long)t * p.N1 + n2 * G + (col_ok ? l16 : 0);
+  V8 qreg[4], doreg[4];
+  float acc = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < 4; ks++) {
+    const long off = qr * kD + 32 * ks + 8 * gq;
+    qreg[ks] = col_ok ? as_v8<V8>(ld16((const T*)p.q + off)) : zero_v8<V8>();
+    doreg[ks] = col_ok ? as_v8<V8>(ld16((const T*)p.dout + off)) : zero_v8<V8>();
+    const V8 ov = col_ok ? as_v8<V8>(ld16((const T*)p.o + off)) : zero_v8<V8>();
+#pragma unroll
+    for (int e = 0; e < 8; e++) acc += E::to_f32(doreg[ks][e]) * E::to_f32(ov[e]);
+  }
+  acc += __shfl_xor(acc, 16);
+  acc += __shfl_xor(acc, 32);
+  const float dlt = acc;
+  const float lse2 = col_ok ? p.lse[qr] * kLog2e : 0.f;
+  if (col_ok && gq == 0) p.delta[qr] = dlt;
+
+  const long row = (long)t * p.N2 + n2;
+  const int e0 = p.row_ptr[row], e1 = p.row_ptr[row + 1];
+  const ShortList blocks(p.col + e0, e1 - e0);  // sbc <= 128 entries
+  const int sbs = g.sbs;
+  const int cpb = (sbs + kChunk - 1) / kChunk;
+  const float sl2 = p.scale * kLog2e;
+  const long kstride = (long)p.N2 * kD;
+  const T* kbase = (const T*)p.k + ((long)kv0 * p.N2 + n2) * kD;
+  const T* vbase = (const T*)p.v + ((long)kv0 * p.N2 + n2) * kD;
+
+  auto chunk_range = [&](ChunkPos c, int& ks, int& ke) {
+    const int blk = blocks(c.e - e0);
+    ks = blk * sbs + c.s * kChunk;
+    ke = min(ks + kChunk, (blk + 1) * sbs);
+  };
+  auto next_valid = [&](ChunkPos c) {
+    for (; c.e < e1; c = chunk_advance(c, cpb)) {
+      int ks, ke;
+      chunk_range(c, ks, ke);
+      if (!(g.causal && ks > pos)) break;
+    }
+    return c;
+  };
+  const int rstride = p.N2 * kD;
+  auto load = [&](const T* base, ChunkPos c, uint4 (&r8)[8]) {
+    int ks, ke;
+    chunk_range(c, ks, ke);
+    const T* cb = base + (long)ks * kstride + 8 * (lane & 15);
+    const int last = ke - 1 - ks;
+#pragma unroll
+    for (int u = 0; u < 8; u++) r8[u] = ld16(cb + min(4 * u + (lane >> 4), last) * rstride);
+  };
+  // tile bases: row stores (key 4*u + gq, piece l16), A-operand reads (key
+  // 16*kt + l16, piece 4*q4 + gq), transposed reads (keys 4*gq + l16/4 and
+  // +16, bytes 32*dt + 8*(l16%4) ..)
+  char* const Tw = Tl + 2 * gq * kPitch + 16 * l16;
+  char* const Tr = Tl + key_row(l16) * kPitch + 16 * gq;
+  char* const Tt = Tl + key_row(4 * gq + (l16 >> 2)) * kPitch + 8 * (l16 & 3);
+  auto to_lds = [&](const uint4 (&r8)[8]) {
+#pragma unroll
+    for (int u = 0; u < 8; u++) *reinterpret_cast<uint4*>(Tw + key_row4(u) * kPitch) = r8[u];
+  };
+
+  f32x4_t dq[8];  // dQ^T tiles: d = 16*dt + 4*gq + j, column head l16
+#pragma unroll
+  for (int dt = 0; dt < 8; dt++) dq[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  uint4 kr[8], vr[8];
+  // One step per chunk c, whose K and V loads are in flight; nx is the next
+  // chunk (c itself after the last one).  The wave's one LDS tile holds V,
+  // then K (a wave's LDS operations run in order).
+  auto step = [&](ChunkPos c, ChunkPos nx) {
+    int ks, ke;
+    chunk_range(c, ks, ke);
+    // element j of st[kt] / dpt[kt]: key ks + 16*kt + 4*gq + j, column head l16
+    f32x4_t st[2], dpt[2];
+    to_lds(vr);
+    load(vbase, nx, vr);
+#pragma unroll
+    for (int kt = 0; kt < 2; kt++) {
+      dpt[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int q4 = 0; q4 < 4; q4++)
+        dpt[kt] = E::mfma16(lds_read16<V8>(Tr + kt * 16 * kPitch + 64 * q4), doreg[q4], dpt[kt]);
+    }
+    to_lds(kr);
+    load(kbase, nx, kr);
+#pragma unroll
+    for (int kt = 0; kt < 2; kt++) {
+      st[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int q4 = 0; q4 < 4; q4++)
+        st[kt] = E::mfma16(lds_read16<V8>(Tr + kt * 16 * kPitch + 64 * q4), qreg[q4], st[kt]);
+    }
+    const int lim = min(ke - 1, g.causal ? pos : 0x7fffffff) - ks;  // last kept key offset
+    V8 bs;
+#pragma unroll
+    for (int kt = 0; kt < 2; kt++)
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const bool ok = col_ok && (16 * kt + 4 * gq + j) <= lim;
+        const float pv = ok ? fast_exp2(__builtin_fmaf(st[kt][j], sl2, -lse2)) : 0.f;
+        bs[4 * kt + j] = E::from_f32(pv * (dpt[kt][j] - dlt));
+      }
+    // dQ^T += K^T dS^T: K^T rows d = 16*dt + l16, keys {4gq..4gq+3, 16+4gq..16+4gq+3}
+#pragma unroll
+    for (int dt = 0; dt < 8; dt++)
+      dq[dt] = E::mfma16(lds_read_tr_pair<V8>(Tt + 32 * dt, Tt + 16 * kPitch + 32 * dt), bs, dq[dt]);
+  };
+
+  ChunkPos c = next_valid(ChunkPos{e0, 0});
+  if (c.e < e1) {
+    load(vbase, c, vr);
+    load(kbase, c, kr);
+  }
+  while (c.e < e1) {
+    const ChunkPos nx = next_valid(chunk_advance(c, cpb));
+    step(c, nx.e < e1 ? nx : c);
+    c = nx;
+  }
+
+  if (col_ok) {
+    T* dp = (T*)p.out + qr * kD;
+#pragma unroll
+    for (int dt = 0; dt < 8; dt++)
+      *reinterpret_cast<uint2*>(dp + 16 * dt + 4 * gq) =
+          pack4<E>(dq[dt][0] * p.scale, dq[dt][1] * p.scale, dq[dt][2] * p.scale,
+                   dq[dt][3] * p.scale);
   }
 }
 
@@ -595,8 +949,12 @@ static hipError_t fwd_t(const NsaParams& p, hipStream_t st) {
   const int units = p.T * p.N2;
   const int n_items = (units + 3) / 4;
   if (n_items == 0) return hipSuccess;
-  hipLaunchKernelGGL((nsa_fwd_kernel<E>), dim3(8 * ((n_items + 7) / 8)), dim3(256), 0, st, p,
-                     n_items);
+  if (p.G <= 16)
+    hipLaunchKernelGGL((nsa_fwd16_kernel<E>), dim3(8 * ((n_items + 7) / 8)), dim3(256), 0, st, p,
+                       n_items);
+  else
+    hipLaunchKernelGGL((nsa_fwd_kernel<E>), dim3(8 * ((n_items + 7) / 8)), dim3(256), 0, st, p,
+                       n_items);
   return hipGetLastError();
 }
 
@@ -610,8 +968,12 @@ static hipError_t bwd_t(const NsaParams& p, hipStream_t st, void* const* ev, int
   const int units = p.T * p.N2;
   const int n_items = (units + 3) / 4;
   if (e == hipSuccess && n_items > 0) {
-    hipLaunchKernelGGL((nsa_dq_kernel<E>), dim3(8 * ((n_items + 7) / 8)), dim3(256), 0, st, p,
-                       n_items);
+    if (p.G <= 16)
+      hipLaunchKernelGGL((nsa_dq16_kernel<E>), dim3(8 * ((n_items + 7) / 8)), dim3(256), 0, st,
+                         p, n_items);
+    else
+      hipLaunchKernelGGL((nsa_dq_kernel<E>), dim3(8 * ((n_items + 7) / 8)), dim3(256), 0, st, p,
+                         n_items);
     e = hipGetLastError();
   }
   if (e == hipSuccess) e = mark_event(ev, n_ev, 1, 1, st);
