@@ -42,12 +42,13 @@ __global__ __launch_bounds__(NW * 64) void bsa_dq_kernel(BsaParams p, int qsub, 
   __shared__ __attribute__((aligned(1024))) char lds_k[2][kTileB];
   __shared__ __attribute__((aligned(1024))) char lds_v[2][kTileB];
 
-  const int item = xcd_remap(blockIdx.x, n_items);
-  if (item < 0) return;
+  const int item = blockIdx.x;
+  if (item >= n_items) return;
+  // work order as in the forward: Q blocks descending, heads interleaved
   const int qs = item % qsub;
   const int t1 = item / qsub;
-  const int qb = p.QB - 1 - (t1 % p.QB);
-  const int bn = t1 / p.QB;
+  const int qb = p.QB - 1 - t1 / (p.B * p.N1);
+  const int bn = t1 % (p.B * p.N1);
   const int n1 = bn % p.N1, b = bn / p.N1;
   const int n2 = n1 / p.G;
   const int row_lo = qb * p.bq + qs * NR;
@@ -231,14 +232,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   __shared__ float lds_lse[2][64];
   __shared__ float lds_dlt[2][64];
 
-  const int item = xcd_remap(blockIdx.x, n_items);
-  if (item < 0) return;
-  // Work order: head-major, KV blocks ascending (under causal-shaped masks the
-  // first blocks have the longest reverse lists).
+  const int item = blockIdx.x;
+  if (item >= n_items) return;
+  // Work order: KV blocks ascending (under causal-shaped masks the first
+  // blocks have the longest reverse lists), all heads of one KV block next to
+  // each other, dealt round-robin over the XCDs in launch order.
   const int ksl = item % ksub;
   const int t1 = item / ksub;
-  const int kb = t1 % p.KB;
-  const int bh = t1 / p.KB;  // b * N2 + n2
+  const int kb = t1 / (p.B * p.N2);
+  const int bh = t1 % (p.B * p.N2);  // b * N2 + n2
   const int n2 = bh % p.N2, b = bh / p.N2;
   const int key_lo = kb * p.bkv + ksl * NK;
   const int key_hi = min((kb + 1) * p.bkv, p.Skv);

@@ -32,14 +32,17 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_kernel(BsaParams p, int qsub,
   __shared__ __attribute__((aligned(1024))) char lds_k[2][kTileB];
   __shared__ __attribute__((aligned(1024))) char lds_v[2][kTileB];
 
-  const int item = xcd_remap(blockIdx.x, n_items);
-  if (item < 0) return;
-  // Work order: head-major, and within a head the last Q block first (the
-  // longest lists under causal-shaped masks start first).
+  const int item = blockIdx.x;
+  if (item >= n_items) return;
+  // Work order: Q blocks from the last to the first, all heads of one Q block
+  // next to each other.  Workgroups go to the 8 XCDs round-robin in launch
+  // order, so every XCD starts with the longest lists of causal-shaped masks
+  // (and holds the same 1/8 of the heads throughout); a head-major order left
+  // each XCD's last head's long lists for the end.
   const int qs = item % qsub;
   const int t1 = item / qsub;
-  const int qb = p.QB - 1 - (t1 % p.QB);
-  const int bn = t1 / p.QB;  // b * N1 + n1
+  const int qb = p.QB - 1 - t1 / (p.B * p.N1);
+  const int bn = t1 % (p.B * p.N1);  // b * N1 + n1
   const int n1 = bn % p.N1, b = bn / p.N1;
   const int n2 = n1 / p.G;
   const int row_lo = qb * p.bq + qs * NR;

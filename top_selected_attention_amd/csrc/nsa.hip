@@ -72,11 +72,14 @@ __global__ __launch_bounds__(256) void nsa_fwd_kernel(NsaParams p, int n_items) 
   typedef typename E::V8 V8;
   __shared__ __attribute__((aligned(1024))) char lds[4][2][kWaveTile];  // per wave: K, V
 
-  const int item = xcd_remap(blockIdx.x, n_items);
-  if (item < 0) return;
+  const int item = blockIdx.x;
+  if (item >= n_items) return;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int l32 = lane & 31, h = lane >> 5;
-  // unit order: KV-head-major, tokens ascending (a sequence's K/V stay hot)
+  // unit order: KV-head-major, tokens ascending; workgroups are dealt to the
+  // 8 XCDs round-robin, so each XCD holds an even share of every stretch of
+  // tokens (and of their unequal list lengths) while the K/V of the
+  // sequences in progress stay in L2
   const int unit = item * 4 + wid;
   if (unit >= p.T * p.N2) return;
   const int n2 = unit / p.T, t = unit % p.T;
@@ -202,11 +205,14 @@ void nsa_fwd16_kernel(NsaParams p, int n_items) {
   typedef float f32x4_t __attribute__((ext_vector_type(4)));
   __shared__ __attribute__((aligned(1024))) char lds[4][kTile16];  // per wave: K, then V
 
-  const int item = xcd_remap(blockIdx.x, n_items);
-  if (item < 0) return;
+  const int item = blockIdx.x;
+  if (item >= n_items) return;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int l16 = lane & 15, gq = lane >> 4;
-  // unit order: KV-head-major, tokens ascending (a sequence's K/V stay hot)
+  // unit order: KV-head-major, tokens ascending; workgroups are dealt to the
+  // 8 XCDs round-robin, so each XCD holds an even share of every stretch of
+  // tokens (and of their unequal list lengths) while the K/V of the
+  // sequences in progress stay in L2
   const int unit = item * 4 + wid;
   if (unit >= p.T * p.N2) return;
   const int n2 = unit / p.T, t = unit % p.T;
@@ -370,8 +376,8 @@ __global__ __launch_bounds__(256) void nsa_dq_kernel(NsaParams p, int n_items) {
   typedef typename E::V8 V8;
   __shared__ __attribute__((aligned(1024))) char lds[4][2][kWaveTile];
 
-  const int item = xcd_remap(blockIdx.x, n_items);
-  if (item < 0) return;
+  const int item = blockIdx.x;
+  if (item >= n_items) return;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int l32 = lane & 31, h = lane >> 5;
   const int unit = item * 4 + wid;
@@ -485,8 +491,8 @@ void nsa_dq16_kernel(NsaParams p, int n_items) {
   typedef float f32x4_t __attribute__((ext_vector_type(4)));
   __shared__ __attribute__((aligned(1024))) char lds[4][kTile16];  // per wave: V, then K
 
-  const int item = xcd_remap(blockIdx.x, n_items);
-  if (item < 0) return;
+  const int item = blockIdx.x;
+  if (item >= n_items) return;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int l16 = lane & 15, gq = lane >> 4;
   const int unit = item * 4 + wid;
