@@ -90,6 +90,8 @@ struct BsaWs {
   int* col;
   int* rev_ptr;
   int* rev;
+  int* order_q;
+  int* order_kv;
   float* delta;
 };
 
@@ -106,6 +108,8 @@ size_t bsa_carve(const A* a, void* ws, BsaWs* out, bool with_delta) {
   w.col = c.take<int>(R * KB);
   w.rev_ptr = c.take<int>(C + 1);
   w.rev = c.take<int>(R * KB);
+  w.order_q = c.take<int>(R);
+  w.order_kv = c.take<int>(C);
   w.delta = with_delta ? c.take<float>((long)a->B * a->N1 * a->Sq) : nullptr;
   if (out) *out = w;
   return c.off + kAlign;
@@ -475,11 +479,14 @@ int bsa_fwd(const bsa_fwd_args* a, void* ws, size_t ws_bytes, void* stream) {
                              w.row_ptr, w.col, w.rev_ptr, w.rev, st);
     else
       e = hipMemsetAsync(w.row_ptr, 0, sizeof(int) * ((long)a->B * a->N1 * p.QB + 1), st);
+    if (e == hipSuccess)
+      e = launch_tile_order(w.row_ptr, a->B * a->N1 * p.QB, w.order_q, w.rev_ptr,
+                            p.KB > 0 ? a->B * a->N2 * p.KB : 0, w.order_kv, st);
   }
   if (e == hipSuccess) e = tm.mark(0, 1);
   if (e != hipSuccess) return TSA_ERR_HIP;
   p.q = a->q; p.k = a->k; p.v = a->v; p.out = a->out; p.lse = a->lse;
-  p.row_ptr = w.row_ptr; p.col = w.col;
+  p.row_ptr = w.row_ptr; p.col = w.col; p.order_q = w.order_q;
   e = tm.mark(1, 0);
   if (e == hipSuccess) e = launch_bsa_fwd(p, a->dtype == TSA_FP16, st);
   if (e == hipSuccess) e = tm.mark(1, 1);
@@ -515,12 +522,15 @@ int bsa_bwd(const bsa_bwd_args* a, void* ws, size_t ws_bytes, void* stream) {
       e = hipMemsetAsync(w.row_ptr, 0, sizeof(int) * (R + 1), st);
       if (e == hipSuccess) e = hipMemsetAsync(w.rev_ptr, 0, sizeof(int) * (C + 1), st);
     }
+    if (e == hipSuccess)
+      e = launch_tile_order(w.row_ptr, (int)R, w.order_q, w.rev_ptr, (int)C, w.order_kv, st);
   }
   if (e == hipSuccess) e = tm.mark(0, 1);
   if (e != hipSuccess) return TSA_ERR_HIP;
   p.q = a->q; p.k = a->k; p.v = a->v; p.o = a->out; p.dout = a->dout; p.lse = (float*)a->lse;
   p.out = a->dq; p.dk = a->dk; p.dv = a->dv; p.delta = w.delta;
   p.row_ptr = w.row_ptr; p.col = w.col; p.rev_ptr = w.rev_ptr; p.rev = w.rev;
+  p.order_q = w.order_q; p.order_kv = w.order_kv;
   return hip_status(launch_bsa_bwd(p, a->dtype == TSA_FP16, st, tm.ev, tm.n));
 }
 

@@ -44,11 +44,11 @@ __global__ __launch_bounds__(NW * 64) void bsa_dq_kernel(BsaParams p, int qsub, 
 
   const int item = blockIdx.x;
   if (item >= n_items) return;
-  // work order as in the forward: Q blocks descending, heads interleaved
+  // work order as in the forward: Q tiles by list length, longest first
   const int qs = item % qsub;
-  const int t1 = item / qsub;
-  const int qb = p.QB - 1 - t1 / (p.B * p.N1);
-  const int bn = t1 % (p.B * p.N1);
+  const int tile = p.order_q[item / qsub];
+  const int qb = tile % p.QB;
+  const int bn = tile / p.QB;
   const int n1 = bn % p.N1, b = bn / p.N1;
   const int n2 = n1 / p.G;
   const int row_lo = qb * p.bq + qs * NR;
@@ -234,13 +234,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 
   const int item = blockIdx.x;
   if (item >= n_items) return;
-  // Work order: KV blocks ascending (under causal-shaped masks the first
-  // blocks have the longest reverse lists), all heads of one KV block next to
-  // each other, dealt round-robin over the XCDs in launch order.
+  // Work order: KV tiles by reverse-list length, longest first
+  // (p.order_kv), dealt round-robin over the XCDs in launch order.
   const int ksl = item % ksub;
-  const int t1 = item / ksub;
-  const int kb = t1 / (p.B * p.N2);
-  const int bh = t1 % (p.B * p.N2);  // b * N2 + n2
+  const int tile = p.order_kv[item / ksub];
+  const int kb = tile % p.KB;
+  const int bh = tile / p.KB;  // b * N2 + n2
   const int n2 = bh % p.N2, b = bh / p.N2;
   const int key_lo = kb * p.bkv + ksl * NK;
   const int key_hi = min((kb + 1) * p.bkv, p.Skv);

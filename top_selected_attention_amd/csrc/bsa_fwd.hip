@@ -34,15 +34,15 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_kernel(BsaParams p, int qsub,
 
   const int item = blockIdx.x;
   if (item >= n_items) return;
-  // Work order: Q blocks from the last to the first, all heads of one Q block
-  // next to each other.  Workgroups go to the 8 XCDs round-robin in launch
-  // order, so every XCD starts with the longest lists of causal-shaped masks
-  // (and holds the same 1/8 of the heads throughout); a head-major order left
-  // each XCD's last head's long lists for the end.
+  // Work order: Q tiles by list length, longest first (p.order_q).
+  // Workgroups go to the 8 XCDs round-robin in launch order, so every XCD
+  // starts with its share of the longest lists and the short ones fill the
+  // end; a head-major order left each XCD's last head's long lists for the
+  // end.
   const int qs = item % qsub;
-  const int t1 = item / qsub;
-  const int qb = p.QB - 1 - t1 / (p.B * p.N1);
-  const int bn = t1 % (p.B * p.N1);  // b * N1 + n1
+  const int tile = p.order_q[item / qsub];
+  const int qb = tile % p.QB;
+  const int bn = tile / p.QB;  // b * N1 + n1
   const int n1 = bn % p.N1, b = bn / p.N1;
   const int n2 = n1 / p.G;
   const int row_lo = qb * p.bq + qs * NR;

@@ -276,6 +276,63 @@ hipError_t launch_bsa_compact(const uint8_t* mask, int B, int N1, int N2, int QB
 }
 
 // ---------------------------------------------------------------------------
+// Work order of the attention kernels: tiles by list length, longest first
+// (ties in any order), so that the workgroups dealt out last are the short
+// ones.  A counting sort in LDS: one workgroup per list set (workgroup 0 the
+// forward lists, 1 the reverse lists); lengths of kOrderBins - 1 and more
+// share the first bucket.  order[k] is the tile of rank k.  The order decides
+// only which workgroup starts when, never a result.
+// ---------------------------------------------------------------------------
+constexpr int kOrderBins = 2048;
+
+__global__ __launch_bounds__(1024) void tile_order(const int* ptr_a, int n_a, int* ord_a,
+                                                   const int* ptr_b, int n_b, int* ord_b) {
+  const int* ptr = blockIdx.x ? ptr_b : ptr_a;
+  const int n = blockIdx.x ? n_b : n_a;
+  int* ord = blockIdx.x ? ord_b : ord_a;
+  __shared__ int cnt[kOrderBins];
+  __shared__ int wsum[16];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  auto bucket = [&](int i) { return kOrderBins - 1 - min(ptr[i + 1] - ptr[i], kOrderBins - 1); };
+  for (int i = tid; i < kOrderBins; i += 1024) cnt[i] = 0;
+  __syncthreads();
+  for (int i = tid; i < n; i += 1024) atomicAdd(&cnt[bucket(i)], 1);
+  __syncthreads();
+  // exclusive scan over the buckets: thread t owns buckets 2t and 2t + 1
+  const int c0 = cnt[2 * tid], c1 = cnt[2 * tid + 1];
+  int v = c0 + c1;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(v, d);
+    if (lane >= d) v += y;
+  }
+  if (lane == 63) wsum[w] = v;
+  __syncthreads();
+  if (w == 0) {
+    int x = lane < 16 ? wsum[lane] : 0;
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) {
+      const int y = __shfl_up(x, d);
+      if (lane >= d) x += y;
+    }
+    if (lane < 16) wsum[lane] = x;
+  }
+  __syncthreads();
+  const int base = (w ? wsum[w - 1] : 0) + v - c0 - c1;
+  cnt[2 * tid] = base;
+  cnt[2 * tid + 1] = base + c0;
+  __syncthreads();
+  for (int i = tid; i < n; i += 1024) ord[atomicAdd(&cnt[bucket(i)], 1)] = i;
+}
+
+hipError_t launch_tile_order(const int* row_ptr, int n_rows, int* order_rows, const int* rev_ptr,
+                             int n_cols, int* order_cols, hipStream_t st) {
+  hipLaunchKernelGGL(tile_order, dim3(2), dim3(1024), 0, st, row_ptr, n_rows, order_rows, rev_ptr,
+                     n_cols, order_cols);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // NSA topk_indices -> forward / reverse CSR.
 // ---------------------------------------------------------------------------
 

@@ -19,6 +19,10 @@ hipError_t exclusive_scan(int* data, long n, int* sums, hipStream_t st);
 hipError_t exclusive_scan_total(int* data, long n, int* sums, hipStream_t st);
 
 long bsa_compact_parts_len(int B, int N1, int N2, int QB, int KB);
+// order_rows / order_cols: the n_rows forward and n_cols reverse lists' tile
+// ids by list length, longest first (the attention kernels' work order).
+hipError_t launch_tile_order(const int* row_ptr, int n_rows, int* order_rows, const int* rev_ptr,
+                             int n_cols, int* order_cols, hipStream_t st);
 hipError_t launch_bsa_compact(const uint8_t* mask, int B, int N1, int N2, int QB, int KB,
                               int* parts, int* sums, int* row_ptr, int* col, int* rev_ptr,
                               int* rev, hipStream_t st);
@@ -68,6 +72,8 @@ struct BsaParams {
   const int* col;
   const int* rev_ptr;
   const int* rev;
+  const int* order_q;   // Q tiles (b*N1 + n1)*QB + qb, longest list first
+  const int* order_kv;  // KV tiles (b*N2 + n2)*KB + kb, longest list first
   int B, N1, N2, G, Sq, Skv, D;
   int bq, bkv, QB, KB;
   int causal;
