@@ -221,7 +221,6 @@ struct NsaWs {
   int* seg_off;
   int* seg_sums;
   float* part;
-  int* wg_first;
   int max_segments;
 };
 
@@ -252,7 +251,6 @@ size_t nsa_carve(const A* a, void* ws, NsaWs* out, bool with_delta) {
   w.seg_off = with_delta ? c.take<int>(RR + 1) : nullptr;
   w.seg_sums = with_delta ? c.take<int>(scan_sums_len(RR)) : nullptr;
   w.part = with_delta ? c.take<float>((long)w.max_segments * 2 * a->sbs * a->D) : nullptr;
-  w.wg_first = with_delta ? c.take<int>(kNsaDkdvMaxGrid + 8 + 1) : nullptr;
   if (out) *out = w;
   return c.off + kAlign;
 }
@@ -655,7 +653,6 @@ int nsa_select_bwd(const nsa_select_bwd_args* a, void* ws, size_t ws_bytes, void
   p.T = a->T; p.Tk = a->Tk; p.N1 = a->N1; p.N2 = a->N2; p.G = a->N1 / a->N2; p.D = a->D;
   p.scale = a->scale;
   p.seg_off = w.seg_off; p.seg_sums = w.seg_sums; p.part = w.part; p.max_segments = w.max_segments;
-  p.wg_first = w.wg_first;
   return hip_status(launch_nsa_bwd(p, a->dtype == TSA_FP16, st, tm.ev, tm.n));
 }
 

@@ -641,7 +641,7 @@ void nsa_dq16_kernel(NsaParams p, int n_items) {
 // dK / dV.  The tokens that selected a (KV head, block) -- its reverse list --
 // are cut into segments of at most kSegEntries listings, so a block that
 // thousands of tokens selected is shared by many workgroups.  A workgroup
-// walks its segments' tokens in chunks of 64 query rows (64 / G tokens x G
+// walks its segments' tokens in chunks of 32 query rows (32 / G tokens x G
 // heads); each wave owns 32 of the block's keys:
 //   S = Q K^T, dP = dO V^T, P = exp2(S*scale*log2e - LSE2),
 //   dS = P (dP - softmax_grad), dV^T += dO^T P, dK^T += Q^T dS,
@@ -669,36 +669,9 @@ __global__ void nsa_seg_count(const int* rev_ptr, int nblocks, int* seg_cnt) {
   seg_cnt[r] = max(1, (len + kSegEntries - 1) / kSegEntries);
 }
 
-// Static balance of segments over `grid` workgroups: workgroup w takes the
-// segments whose first listing lies in [w*E/grid, (w+1)*E/grid) of the E
-// listings of all reverse lists (an empty list's one segment counts at its
-// position).  One thread per (KV head, block) writes the first segment of
-// every workgroup whose range starts among its segments.
-__global__ void nsa_seg_bounds(const int* rev_ptr, const int* seg_off, int nblocks, int grid,
-                               int* wg_first) {
-  const int r = blockIdx.x * 256 + threadIdx.x;
-  if (r >= nblocks) return;
-  const long E = max(rev_ptr[nblocks], 1);
-  const int total = seg_off[nblocks];
-  auto wg_of = [&](long start) { return (int)min((long)grid - 1, start * grid / E); };
-  int w_prev = -1;
-  if (r > 0) {
-    const int nprev = seg_off[r] - seg_off[r - 1];
-    w_prev = wg_of(rev_ptr[r - 1] + (long)kSegEntries * (nprev - 1));
-  }
-  const int nseg = seg_off[r + 1] - seg_off[r];
-  for (int k = 0; k < nseg; k++) {
-    const int w = wg_of(rev_ptr[r] + (long)kSegEntries * k);
-    for (int x = w_prev + 1; x <= w; x++) wg_first[x] = seg_off[r] + k;
-    w_prev = w;
-  }
-  if (r == nblocks - 1)
-    for (int x = w_prev + 1; x <= grid; x++) wg_first[x] = total;
-}
-
 template <class E, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
-void nsa_dkdv_seg_kernel(NsaParams p, const int* wg_first, int nblocks, float* part) {
+void nsa_dkdv_seg_kernel(NsaParams p, int nblocks, float* part) {
   typedef typename E::T T;
   typedef typename E::V8 V8;
   constexpr int kQC = 32;                  // query rows per chunk
@@ -714,11 +687,13 @@ void nsa_dkdv_seg_kernel(NsaParams p, const int* wg_first, int nblocks, float* p
 
   const NsaGeom& g = p.g;
   const int* seg_off = p.seg_off;
-  // balanced contiguous segment ranges (XCD-remapped: an XCD's workgroups
-  // hold neighbouring segments, which share K/V and tokens)
-  const int w = xcd_remap(blockIdx.x, gridDim.x);
-  if (w < 0) return;
-  const int s_lo = wg_first[w], s_hi = wg_first[w + 1];
+  // Segments are dealt round-robin (workgroup w takes w, w + grid, ...), so
+  // all workgroups move through the (KV head, sequence, block) order
+  // together: the Q and dO rows in use at any time are those of one stretch
+  // of sequences, which stay in MALL, rather than of every sequence and head
+  // at once.
+  const int w = blockIdx.x;
+  const int nseg = seg_off[nblocks];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5;
   const int G = p.G;
@@ -738,7 +713,7 @@ void nsa_dkdv_seg_kernel(NsaParams p, const int* wg_first, int nblocks, float* p
     }
   };
 
-  for (int sg = s_lo; sg < s_hi; sg++) {
+  for (int sg = w; sg < nseg; sg += gridDim.x) {
     // segment -> block (largest r with seg_off[r] <= sg)
     int lo = 0, hi = nblocks - 1;
     while (lo < hi) {
@@ -994,17 +969,15 @@ static hipError_t bwd_t(const NsaParams& p, hipStream_t st, void* const* ev, int
   if (e == hipSuccess && nb > 0) {
     const int nw = (p.g.sbs + 31) / 32;  // 1..4 waves, 32 keys each
     const int grid = nsa_dkdv_grid(p);
-    hipLaunchKernelGGL(nsa_seg_bounds, dim3((nb + 255) / 256), dim3(256), 0, st, p.rev_ptr,
-                       p.seg_off, nb, grid, p.wg_first);
     if (nw <= 1)
-      hipLaunchKernelGGL((nsa_dkdv_seg_kernel<E, 1>), dim3(grid), dim3(64), 0, st, p, p.wg_first,
-                         nb, p.part);
+      hipLaunchKernelGGL((nsa_dkdv_seg_kernel<E, 1>), dim3(grid), dim3(64), 0, st, p, nb,
+                         p.part);
     else if (nw <= 2)
-      hipLaunchKernelGGL((nsa_dkdv_seg_kernel<E, 2>), dim3(grid), dim3(128), 0, st, p, p.wg_first,
-                         nb, p.part);
+      hipLaunchKernelGGL((nsa_dkdv_seg_kernel<E, 2>), dim3(grid), dim3(128), 0, st, p, nb,
+                         p.part);
     else
-      hipLaunchKernelGGL((nsa_dkdv_seg_kernel<E, 4>), dim3(grid), dim3(256), 0, st, p, p.wg_first,
-                         nb, p.part);
+      hipLaunchKernelGGL((nsa_dkdv_seg_kernel<E, 4>), dim3(grid), dim3(256), 0, st, p, nb,
+                         p.part);
     e = hipGetLastError();
   }
   if (e == hipSuccess) e = mark_event(ev, n_ev, 2, 1, st);

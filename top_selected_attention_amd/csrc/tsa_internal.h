@@ -107,7 +107,6 @@ struct NsaParams {
   int* seg_off;        // [N2*NB + 1] exclusive scan of segments per block
   int* seg_sums;       // scan scratch
   float* part;         // [max_segments][2][sbs][D] fp32 partial dK, dV
-  int* wg_first;       // [grid + 1] first segment of each dK/dV workgroup
   int max_segments;
 };
 
