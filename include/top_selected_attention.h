@@ -86,10 +86,20 @@ TSA_API size_t tsa_args_sizeof(int which);
  * row selects.  Also writes LSE = row max + ln(row sum of exp), fp32 (natural
  * log), which the backward uses.
  *
- * Layout: BNSD only (the page's constraints section: only BNSD is supported).
- *   q [B, N1, Sq, D], k [B, N2, Skv, D], v [B, N2, Skv, D], out like q,
- *   lse fp32 [B, N1, Sq].  D must be 128 (constraints section: headdim=128).
- *   N1 % N2 == 0 (constraints section); query head n1 reads KV head n1/(N1/N2).
+ * Layouts (the page's layout section lists TND and BNSD for qInputLayout
+ * and kvInputLayout; its constraints build only BNSD, both are built here,
+ * with q and k/v in the same layout, else TSA_ERR_UNSUPPORTED):
+ *   BNSD: q [B, N1, Sq, D], k [B, N2, Skv, D], v [B, N2, Skv, D], out like q,
+ *     lse fp32 [B, N1, Sq].
+ *   TND (varlen): q [T, N1, D], k [Tk, N2, D], v [Tk, N2, D], out like q,
+ *     lse fp32 [T, N1]; cu_seqlens_q / cu_seqlens_kv are HOST int32 [B+1]
+ *     prefix sums from 0 (T = cu_seqlens_q[B], Tk = cu_seqlens_kv[B]; the
+ *     layout section makes the sequence lengths mandatory with TND).  Sq and
+ *     Skv are then the longest query / key sequence: they size the mask, and
+ *     each sequence's own length bounds its rows (mask entries of blocks past
+ *     a sequence's end are ignored).  Causal positions are within a sequence.
+ *   D must be 128 (constraints section: headdim=128).  N1 % N2 == 0
+ *   (constraints section); query head n1 reads KV head n1/(N1/N2).
  * block_mask: u8 DEVICE [B, N1, ceil(Sq/block_q), ceil(Skv/block_kv)],
  *   non-zero = the Q block attends to that KV block (blockShapeX = block_q
  *   rows, blockShapeY = block_kv keys; function description).  Tail blocks of
@@ -101,8 +111,8 @@ TSA_API size_t tsa_args_sizeof(int which);
  * ------------------------------------------------------------------------ */
 typedef struct {
   int32_t dtype;            /* TSA_BF16 or TSA_FP16 (q, k, v, out, dout, dq, dk, dv) */
-  int32_t q_layout;         /* TSA_LAYOUT_BNSD */
-  int32_t kv_layout;        /* TSA_LAYOUT_BNSD */
+  int32_t q_layout;         /* TSA_LAYOUT_BNSD or TSA_LAYOUT_TND */
+  int32_t kv_layout;        /* the same as q_layout */
   int32_t B, N1, N2, Sq, Skv, D;
   int32_t block_q, block_kv;
   int32_t sparse_mode;      /* 0 or 2 */
@@ -121,6 +131,8 @@ typedef struct {
   int32_t n_events;         /* number of stages to time (0 = off) */
   void* const* events;      /* HOST array of 2*n_events hipEvent_t: events[2i] / [2i+1] are
                                recorded on `stream` before / after stage i (see each entry) */
+  const int32_t* cu_seqlens_q;  /* TND only: HOST [B+1] (ignored for BNSD) */
+  const int32_t* cu_seqlens_kv; /* TND only: HOST [B+1] */
 } bsa_fwd_args;
 
 TSA_API int bsa_fwd_workspace_size(const bsa_fwd_args* args, size_t* bytes);
@@ -161,6 +173,8 @@ typedef struct {
   int32_t n_events;         /* number of stages to time (0 = off) */
   void* const* events;      /* HOST array of 2*n_events hipEvent_t: events[2i] / [2i+1] are
                                recorded on `stream` before / after stage i (see each entry) */
+  const int32_t* cu_seqlens_q;  /* TND only: HOST [B+1] (ignored for BNSD) */
+  const int32_t* cu_seqlens_kv; /* TND only: HOST [B+1] */
 } bsa_bwd_args;
 
 TSA_API int bsa_bwd_workspace_size(const bsa_bwd_args* args, size_t* bytes);

@@ -33,6 +33,8 @@ from .attention import (  # noqa: F401
     attend_bwd,
     bsa_fwd,
     bsa_bwd,
+    bsa_fwd_tnd,
+    bsa_bwd_tnd,
     bsa_keys,
     nsa_fwd,
     nsa_bwd,

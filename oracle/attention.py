@@ -172,6 +172,74 @@ def bsa_bwd(q, k, v, out, dout, mask, block_q, block_kv, scale, sparse_mode=0,
     return dq, dk, dv
 
 
+def _tnd_tiles(cu_q, N1, block_q, q_tiles):
+    B = len(cu_q) - 1
+    if q_tiles is not None:
+        return [tuple(int(x) for x in t) for t in q_tiles]
+    return [(b, n, qb) for b in range(B) for n in range(N1)
+            for qb in range(-(-(int(cu_q[b + 1]) - int(cu_q[b])) // block_q))]
+
+
+def bsa_fwd_tnd(q, k, v, mask, cu_seqlens_q, cu_seqlens_kv, block_q, block_kv, scale,
+                sparse_mode=0, q_tiles=None):
+    """Block-sparse attention forward, TND (variable-length sequences).
+
+    "aclnnBlockSparseAttentionGrad", layout section: TND rows are the tokens
+    of all sequences back to back, sequence b holding rows cu[b] .. cu[b+1]-1
+    (the actual sequence lengths are mandatory with TND).  q [T, N1, D],
+    k [Tk, N2, D], v [Tk, N2, Dv]; mask [B, N1, QB, KB] with QB / KB the block
+    counts of the longest sequences: sequence b reads the entries of its own
+    blocks only.  Block positions and the causal test are within a sequence.
+    Returns (out [T, N1, Dv], lse [T, N1]); rows outside ``q_tiles`` (a list
+    of (b, n1, qb), default all) are NaN.
+    """
+    cu_q, cu_k = np.asarray(cu_seqlens_q), np.asarray(cu_seqlens_kv)
+    T, N1, _ = q.shape
+    N2, Dv = k.shape[1], v.shape[2]
+    G = N1 // N2
+    out = np.full((T, N1, Dv), np.nan)
+    lse = np.full((T, N1), np.nan)
+    for b, n1, qb in _tnd_tiles(cu_q, N1, block_q, q_tiles):
+        q0, sq = int(cu_q[b]), int(cu_q[b + 1] - cu_q[b])
+        k0, skv = int(cu_k[b]), int(cu_k[b + 1] - cu_k[b])
+        rows = np.arange(qb * block_q, min((qb + 1) * block_q, sq))
+        keys = bsa_keys(mask[b, n1, qb, :-(-skv // block_kv)], block_kv, skv)
+        n2 = n1 // G
+        o, l, _ = attend_fwd(q[q0 + rows, n1], k[k0 + keys, n2], v[k0 + keys, n2],
+                             _bsa_allowed(rows, keys, sparse_mode), scale)
+        out[q0 + rows, n1] = o
+        lse[q0 + rows, n1] = l
+    return out, lse
+
+
+def bsa_bwd_tnd(q, k, v, out, dout, mask, cu_seqlens_q, cu_seqlens_kv, block_q, block_kv,
+                scale, sparse_mode=0, q_tiles=None):
+    """Block-sparse attention backward, TND: the backward chain of the
+    formula section per (sequence, head, Q block), with each selected key's
+    gradient added back to its row.  Returns (dq, dk, dv); as ``bsa_bwd`` for
+    ``q_tiles`` (dq NaN outside them, dk / dv their contributions only)."""
+    cu_q, cu_k = np.asarray(cu_seqlens_q), np.asarray(cu_seqlens_kv)
+    T, N1, D = q.shape
+    Tk, N2, Dv = v.shape
+    G = N1 // N2
+    dq = np.full((T, N1, D), np.nan)
+    dk = np.zeros((Tk, N2, D))
+    dv = np.zeros((Tk, N2, Dv))
+    for b, n1, qb in _tnd_tiles(cu_q, N1, block_q, q_tiles):
+        q0, sq = int(cu_q[b]), int(cu_q[b + 1] - cu_q[b])
+        k0, skv = int(cu_k[b]), int(cu_k[b + 1] - cu_k[b])
+        rows = np.arange(qb * block_q, min((qb + 1) * block_q, sq))
+        keys = bsa_keys(mask[b, n1, qb, :-(-skv // block_kv)], block_kv, skv)
+        n2 = n1 // G
+        g_q, g_k, g_v = attend_bwd(q[q0 + rows, n1], k[k0 + keys, n2], v[k0 + keys, n2],
+                                   _bsa_allowed(rows, keys, sparse_mode),
+                                   out[q0 + rows, n1], dout[q0 + rows, n1], scale)
+        dq[q0 + rows, n1] = g_q
+        np.add.at(dk[:, n2], k0 + keys, g_k)
+        np.add.at(dv[:, n2], k0 + keys, g_v)
+    return dq, dk, dv
+
+
 # --------------------------------------------------------------------------
 # NSA selected attention (topk_indices), TND layout.
 # --------------------------------------------------------------------------

@@ -60,7 +60,7 @@ def _size(tsa, fn, args):
     (dict(), 0),
     (dict(D=64), 2),                       # headdim must be 128
     (dict(N1=3, N2=2), 2),                 # N1 % N2 != 0
-    (dict(q_layout=1), 3),                 # TND: documented, not built
+    (dict(q_layout=1), 3),                 # q TND with k/v BNSD: mixed layouts not built
     (dict(q_layout=7), 2),
     (dict(sparse_mode=1), 2),
     (dict(dtype=5), 2),
@@ -77,6 +77,34 @@ def test_bsa_validation(tsa, kw, status):
     assert s == status
     if s == 0:
         assert n > 0
+
+
+def _cu(*vals):
+    return (ctypes.c_int32 * len(vals))(*vals)
+
+
+@pytest.mark.parametrize("cq,ck,status", [
+    ((0, 1000, 1700), (0, 900, 1500), 0),   # varlen, each sequence within Sq / Skv
+    ((0, 1001, 1700), (0, 900, 1500), 2),   # a query sequence longer than Sq
+    ((0, 1000, 1700), (0, 901, 1500), 2),   # a key sequence longer than Skv
+    ((1, 1000, 1700), (0, 900, 1500), 2),   # prefix sums must start at 0
+    ((0, 1000, 900), (0, 900, 1500), 2),    # and not decrease
+    ((0, 0, 0), (0, 0, 0), 0),              # every sequence empty: valid
+    (None, (0, 900, 1500), 1),              # TND needs both arrays
+])
+def test_bsa_tnd_validation(tsa, cq, ck, status):
+    a = _bsa(tsa, q_layout=1, kv_layout=1)
+    a.cu_seqlens_q = _cu(*cq) if cq else None
+    a.cu_seqlens_kv = _cu(*ck)
+    s, n = _size(tsa, tsa.lib.bsa_fwd_workspace_size, a)
+    assert s == status
+    if s == 0:
+        assert n > 0
+    b = tsa._abi.BsaBwdArgs(dtype=0, q_layout=1, kv_layout=1, B=2, N1=4, N2=2, Sq=1000,
+                            Skv=900, D=128, block_q=128, block_kv=64, sparse_mode=2, scale=0.1,
+                            block_mask=8, q=8, k=8, v=8, out=8, dout=8, lse=8, dq=8, dk=8, dv=8)
+    b.cu_seqlens_q, b.cu_seqlens_kv = a.cu_seqlens_q, a.cu_seqlens_kv
+    assert _size(tsa, tsa.lib.bsa_bwd_workspace_size, b)[0] == status
 
 
 def test_bsa_workspace_too_small_is_rejected_before_launch(tsa):

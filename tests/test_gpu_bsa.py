@@ -300,3 +300,57 @@ def test_bwd_reusing_forward_lists_matches_fresh_lists():
     torch.cuda.synchronize()
     for a, b in zip(g1, g2):
         assert torch.equal(a, b)
+
+
+# ----------------------------------------------------------------------------
+# TND (variable-length sequences)
+# ----------------------------------------------------------------------------
+
+def _tnd_case(lens_q, lens_kv, N1, N2, bq, bkv, mode, dtype, seed, p=0.5):
+    """Ragged sequences; the mask is padded to the longest sequence and holds
+    random entries past each sequence's end too (they must be ignored)."""
+    tsa = _tsa()
+    dt = "bf16" if dtype == torch.bfloat16 else "fp16"
+    cq = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int32)
+    ck = np.concatenate([[0], np.cumsum(lens_kv)]).astype(np.int32)
+    T, Tk, B = int(cq[-1]), int(ck[-1]), len(lens_q)
+    Sq, Skv = max(lens_q), max(lens_kv)
+    q = W.normal((T, N1, 128), seed + 1, dt)
+    k = W.normal((Tk, N2, 128), seed + 2, dt)
+    v = W.normal((Tk, N2, 128), seed + 3, dt)
+    do = W.normal((T, N1, 128), seed + 4, dt)
+    QB, KB = -(-Sq // bq), -(-Skv // bkv)
+    mask = (np.random.default_rng(seed).random((B, N1, QB, KB)) < p).astype(np.uint8)
+    for i in range(min(QB, KB)):
+        mask[:, :, i, i] = 1
+    scale = 1 / math.sqrt(128)
+    qd, kd, vd, dod = _dev(q, k, v, do)
+    plan = tsa.BsaPlan(qd, kd, vd, torch.from_numpy(mask).cuda(), bq, bkv, scale, mode,
+                       cu_seqlens_q=cq, cu_seqlens_kv=ck)
+    out, lse = plan.fwd()
+    dq, dk, dv = plan.bwd(dod)
+    torch.cuda.synchronize()
+    qn, kn, vn, don = _np(q), _np(k), _np(v), _np(do)
+    ro, rl = oracle.bsa_fwd_tnd(qn, kn, vn, mask, cq, ck, bq, bkv, scale, mode)
+    _close(out, ro, OUT_TOL, "out")
+    _lse_close(lse, rl)
+    rdq, rdk, rdv = oracle.bsa_bwd_tnd(qn, kn, vn, _np(out), don, mask, cq, ck, bq, bkv, scale,
+                                       mode)
+    _close(dq, rdq, GRAD_TOL, "dq")
+    _close(dk, rdk, GRAD_TOL, "dk")
+    _close(dv, rdv, GRAD_TOL, "dv")
+
+
+@pytest.mark.parametrize("mode", [0, 2])
+@pytest.mark.parametrize("lens_q,lens_kv,N1,N2,bq,bkv", [
+    ([200, 512, 77], [200, 512, 77], 4, 2, 64, 64),      # GQA, tails in every sequence
+    ([300, 1000, 129], [300, 1000, 129], 2, 2, 128, 128),
+    ([64, 0, 100], [64, 0, 100], 2, 1, 32, 48),          # an empty sequence, odd block size
+    ([100, 300], [250, 180], 4, 4, 64, 32),              # query and key lengths differ
+])
+def test_tnd_varlen_fwd_bwd(lens_q, lens_kv, N1, N2, bq, bkv, mode):
+    _tnd_case(lens_q, lens_kv, N1, N2, bq, bkv, mode, torch.bfloat16, 500)
+
+
+def test_tnd_varlen_fp16():
+    _tnd_case([130, 257], [130, 257], 2, 2, 64, 64, 2, torch.float16, 510)

@@ -141,6 +141,90 @@ def test_sfa_page_table_permutation_is_invisible():
 # Finite differences of L = sum(dO * O)
 # ----------------------------------------------------------------------------
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_bsa_tnd_all_blocks_equals_dense_attention_per_sequence(causal):
+    """TND varlen with every mask entry set (also past each sequence's end,
+    which must be ignored): each sequence equals dense attention over its own
+    rows, with causality counted from the sequence start."""
+    r = _rng(2)
+    lens, N1, N2, D, bq, bkv = [13, 40, 27], 4, 2, 16, 8, 8
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    T = int(cu[-1])
+    q = r.standard_normal((T, N1, D))
+    k = r.standard_normal((T, N2, D))
+    v = r.standard_normal((T, N2, D))
+    do = r.standard_normal((T, N1, D))
+    scale = 1 / math.sqrt(D)
+    mask = np.ones((3, N1, 5, 5), np.uint8)
+    mode = 2 if causal else 0
+    out, lse = oracle.bsa_fwd_tnd(q, k, v, mask, cu, cu, bq, bkv, scale, mode)
+    dq, dk, dv = oracle.bsa_bwd_tnd(q, k, v, out, do, mask, cu, cu, bq, bkv, scale, mode)
+    for b in range(3):
+        sl = slice(cu[b], cu[b + 1])
+        qt, kt, vt, ref = _dense_torch(q[sl].transpose(1, 0, 2), k[sl].transpose(1, 0, 2),
+                                       v[sl].transpose(1, 0, 2), scale, causal, N1 // N2)
+        np.testing.assert_allclose(out[sl], ref.detach().numpy().transpose(1, 0, 2), rtol=0,
+                                   atol=1e-12)
+        ref.backward(torch.tensor(do[sl].transpose(1, 0, 2)))
+        for mine, theirs in ((dq[sl], qt.grad), (dk[sl], kt.grad), (dv[sl], vt.grad)):
+            t = theirs.numpy().transpose(1, 0, 2)
+            assert np.abs(mine - t).max() <= 1e-10 * np.abs(t).max()
+    assert np.all(np.isfinite(lse))
+
+
+@pytest.mark.parametrize("mode", [0, 2])
+def test_bsa_tnd_equal_lengths_equals_bnsd(mode):
+    """TND with B equal-length sequences is the BNSD problem with its axes
+    moved: the same numbers, bit for bit."""
+    r = _rng(3)
+    B, N1, N2, S, D, bq, bkv = 3, 4, 2, 24, 8, 8, 4
+    q = r.standard_normal((B, N1, S, D))
+    k = r.standard_normal((B, N2, S, D))
+    v = r.standard_normal((B, N2, S, D))
+    do = r.standard_normal((B, N1, S, D))
+    mask = W.mask_random(r, B, N1, 3, 6, 0.5)
+    cu = np.arange(B + 1) * S
+    tnd = lambda x: x.transpose(0, 2, 1, 3).reshape(B * S, x.shape[1], D)  # noqa: E731
+    o, l = oracle.bsa_fwd(q, k, v, mask, bq, bkv, 0.4, mode)
+    ot, lt = oracle.bsa_fwd_tnd(tnd(q), tnd(k), tnd(v), mask, cu, cu, bq, bkv, 0.4, mode)
+    assert np.array_equal(tnd(o), ot) and np.array_equal(l.transpose(0, 2, 1).reshape(B * S, N1), lt)
+    g = oracle.bsa_bwd(q, k, v, o, do, mask, bq, bkv, 0.4, mode)
+    gt = oracle.bsa_bwd_tnd(tnd(q), tnd(k), tnd(v), ot, tnd(do), mask, cu, cu, bq, bkv, 0.4, mode)
+    for a, b_ in zip(g, gt):
+        assert np.array_equal(tnd(a), b_)
+
+
+@pytest.mark.parametrize("mode", [0, 2])
+def test_bsa_tnd_finite_differences_and_sequence_isolation(mode):
+    r = _rng(4)
+    lens, N1, N2, D, bq, bkv = [9, 16], 2, 1, 8, 4, 4
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    T = int(cu[-1])
+    a = dict(q=r.standard_normal((T, N1, D)), k=r.standard_normal((T, N2, D)),
+             v=r.standard_normal((T, N2, D)))
+    do = r.standard_normal((T, N1, D))
+    mask = W.mask_random(r, 2, N1, 4, 4, 0.5)
+    scale = 0.41
+
+    def loss():
+        o, _ = oracle.bsa_fwd_tnd(a["q"], a["k"], a["v"], mask, cu, cu, bq, bkv, scale, mode)
+        return float((do * o).sum())
+
+    o, _ = oracle.bsa_fwd_tnd(a["q"], a["k"], a["v"], mask, cu, cu, bq, bkv, scale, mode)
+    g = oracle.bsa_bwd_tnd(a["q"], a["k"], a["v"], o, do, mask, cu, cu, bq, bkv, scale, mode)
+    _fd_check(loss, a, ["q", "k", "v"], list(g))
+    # another sequence's K/V never enters sequence 0's results
+    k2, v2 = a["k"].copy(), a["v"].copy()
+    k2[cu[1]:] += 5.0
+    v2[cu[1]:] -= 3.0
+    o2, _ = oracle.bsa_fwd_tnd(a["q"], k2, v2, mask, cu, cu, bq, bkv, scale, mode)
+    g2 = oracle.bsa_bwd_tnd(a["q"], k2, v2, o2, do, mask, cu, cu, bq, bkv, scale, mode)
+    s0 = slice(0, cu[1])
+    assert np.array_equal(o[s0], o2[s0])
+    for x, y in zip(g, g2):
+        assert np.array_equal(x[s0], y[s0])
+
+
 def _fd_check(f, args, idx_names, grads, n_probe=12, h=1e-6, seed=0):
     r = _rng(seed)
     for name, g in zip(idx_names, grads):

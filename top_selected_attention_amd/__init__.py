@@ -78,34 +78,57 @@ def _ceil(a, b):
 class BsaPlan:
     """Forward and backward of block-sparse attention for fixed tensors.
 
-    q [B, N1, Sq, 128], k/v [B, N2, Skv, 128] (bf16 or fp16, BNSD),
-    block_mask u8 [B, N1, ceil(Sq/block_q), ceil(Skv/block_kv)].
-    ``fwd()`` writes ``self.out`` / ``self.lse``; ``bwd(dout)`` writes
-    ``self.dq`` / ``self.dk`` / ``self.dv``.
+    BNSD: q [B, N1, Sq, 128], k/v [B, N2, Skv, 128]; TND (varlen, when
+    cu_seqlens_q / cu_seqlens_kv are given as host B+1 prefix sums):
+    q [T, N1, 128], k/v [Tk, N2, 128], with Sq / Skv the longest sequences.
+    bf16 or fp16; block_mask u8 [B, N1, ceil(Sq/block_q), ceil(Skv/block_kv)].
+    ``fwd()`` writes ``self.out`` / ``self.lse`` (LSE [B, N1, Sq] or
+    [T, N1]); ``bwd(dout)`` writes ``self.dq`` / ``self.dk`` / ``self.dv``.
     """
 
     def __init__(self, q, k, v, block_mask, block_q, block_kv, scale=None, sparse_mode=0,
-                 backward=True):
+                 backward=True, cu_seqlens_q=None, cu_seqlens_kv=None):
         _check(q, "q"), _check(k, "k", q.dtype), _check(v, "v", q.dtype)
-        if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
-            raise ValueError("q, k, v must be BNSD with k and v of one shape")
-        B, N1, Sq, D = q.shape
-        _, N2, Skv, _ = k.shape
-        if k.shape[0] != B or k.shape[3] != D:
-            raise ValueError("q and k disagree in B or D")
+        tnd = cu_seqlens_q is not None or cu_seqlens_kv is not None
+        if tnd:
+            if cu_seqlens_q is None or cu_seqlens_kv is None:
+                raise ValueError("TND needs both cu_seqlens_q and cu_seqlens_kv")
+            if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape:
+                raise ValueError("q, k, v must be TND with k and v of one shape")
+            self.cu_q, self.cu_kv = _host_i32(cu_seqlens_q), _host_i32(cu_seqlens_kv)
+            B = self.cu_q.numel() - 1
+            if self.cu_kv.numel() != B + 1:
+                raise ValueError("cu_seqlens_q and cu_seqlens_kv differ in length")
+            T, N1, D = q.shape
+            Tk, N2, _ = k.shape
+            if int(self.cu_q[-1]) != T or int(self.cu_kv[-1]) != Tk or k.shape[2] != D:
+                raise ValueError("cu_seqlens do not match q / k")
+            Sq = int((self.cu_q[1:] - self.cu_q[:-1]).max()) if B > 0 else 0
+            Skv = int((self.cu_kv[1:] - self.cu_kv[:-1]).max()) if B > 0 else 0
+            lse_shape, layout = (T, N1), LAYOUT_TND
+            seq = dict(cu_seqlens_q=ctypes.cast(self.cu_q.data_ptr(), ctypes.POINTER(ctypes.c_int32)),
+                       cu_seqlens_kv=ctypes.cast(self.cu_kv.data_ptr(), ctypes.POINTER(ctypes.c_int32)))
+        else:
+            if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+                raise ValueError("q, k, v must be BNSD with k and v of one shape")
+            B, N1, Sq, D = q.shape
+            _, N2, Skv, _ = k.shape
+            if k.shape[0] != B or k.shape[3] != D:
+                raise ValueError("q and k disagree in B or D")
+            lse_shape, layout, seq = (B, N1, Sq), LAYOUT_BNSD, {}
         QB, KB = _ceil(Sq, block_q), _ceil(Skv, block_kv)
         _check(block_mask, "block_mask", torch.uint8, (B, N1, QB, KB))
         self.q, self.k, self.v, self.mask = q, k, v, block_mask
         self.scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
         dev = q.device
         self.out = torch.empty_like(q)
-        self.lse = torch.empty((B, N1, Sq), dtype=torch.float32, device=dev)
+        self.lse = torch.empty(lse_shape, dtype=torch.float32, device=dev)
         self.fa = _abi.BsaFwdArgs(
-            dtype=_dtype_code(q), q_layout=LAYOUT_BNSD, kv_layout=LAYOUT_BNSD,
+            dtype=_dtype_code(q), q_layout=layout, kv_layout=layout,
             B=B, N1=N1, N2=N2, Sq=Sq, Skv=Skv, D=D, block_q=block_q, block_kv=block_kv,
             sparse_mode=sparse_mode, scale=self.scale, validate=0,
             block_mask=block_mask.data_ptr(), q=q.data_ptr(), k=k.data_ptr(), v=v.data_ptr(),
-            out=self.out.data_ptr(), lse=self.lse.data_ptr())
+            out=self.out.data_ptr(), lse=self.lse.data_ptr(), **seq)
         nb = ctypes.c_size_t()
         _abi.call(lib.bsa_fwd_workspace_size, ctypes.byref(self.fa), ctypes.byref(nb))
         self.ws_fwd = _workspace(nb.value, dev)
@@ -119,12 +142,12 @@ class BsaPlan:
             self.dk = torch.empty_like(k)
             self.dv = torch.empty_like(v)
             self.ba = _abi.BsaBwdArgs(
-                dtype=_dtype_code(q), q_layout=LAYOUT_BNSD, kv_layout=LAYOUT_BNSD,
+                dtype=_dtype_code(q), q_layout=layout, kv_layout=layout,
                 B=B, N1=N1, N2=N2, Sq=Sq, Skv=Skv, D=D, block_q=block_q, block_kv=block_kv,
                 sparse_mode=sparse_mode, scale=self.scale, validate=0,
                 block_mask=block_mask.data_ptr(), q=q.data_ptr(), k=k.data_ptr(),
                 v=v.data_ptr(), out=self.out.data_ptr(), dout=0, lse=self.lse.data_ptr(),
-                dq=self.dq.data_ptr(), dk=self.dk.data_ptr(), dv=self.dv.data_ptr())
+                dq=self.dq.data_ptr(), dk=self.dk.data_ptr(), dv=self.dv.data_ptr(), **seq)
 
     def fwd(self):
         self.fa.reuse_lists = 0
@@ -163,15 +186,19 @@ class BsaPlan:
         return self.dq, self.dk, self.dv
 
 
-def bsa_fwd(q, k, v, block_mask, block_q, block_kv, scale=None, sparse_mode=0):
-    """Block-sparse attention forward: returns (out, lse)."""
-    plan = BsaPlan(q, k, v, block_mask, block_q, block_kv, scale, sparse_mode, backward=False)
+def bsa_fwd(q, k, v, block_mask, block_q, block_kv, scale=None, sparse_mode=0,
+            cu_seqlens_q=None, cu_seqlens_kv=None):
+    """Block-sparse attention forward (BNSD, or TND with cu_seqlens): returns (out, lse)."""
+    plan = BsaPlan(q, k, v, block_mask, block_q, block_kv, scale, sparse_mode, backward=False,
+                   cu_seqlens_q=cu_seqlens_q, cu_seqlens_kv=cu_seqlens_kv)
     return plan.fwd()
 
 
-def bsa_bwd(q, k, v, out, dout, lse, block_mask, block_q, block_kv, scale=None, sparse_mode=0):
-    """Block-sparse attention backward: returns (dq, dk, dv)."""
-    plan = BsaPlan(q, k, v, block_mask, block_q, block_kv, scale, sparse_mode, backward=True)
+def bsa_bwd(q, k, v, out, dout, lse, block_mask, block_q, block_kv, scale=None, sparse_mode=0,
+            cu_seqlens_q=None, cu_seqlens_kv=None):
+    """Block-sparse attention backward (BNSD, or TND with cu_seqlens): returns (dq, dk, dv)."""
+    plan = BsaPlan(q, k, v, block_mask, block_q, block_kv, scale, sparse_mode, backward=True,
+                   cu_seqlens_q=cu_seqlens_q, cu_seqlens_kv=cu_seqlens_kv)
     plan.set_out(out, lse)
     return plan.bwd(dout)
 

@@ -39,7 +39,7 @@ class BsaFwdArgs(ctypes.Structure):
         ("scale", c_float), ("validate", c_int32),
         ("block_mask", c_void_p), ("q", c_void_p), ("k", c_void_p), ("v", c_void_p),
         ("out", c_void_p), ("lse", c_void_p),
-    ] + TRAIL
+    ] + TRAIL + [("cu_seqlens_q", POINTER(c_int32)), ("cu_seqlens_kv", POINTER(c_int32))]
 
 
 class BsaBwdArgs(ctypes.Structure):
@@ -51,7 +51,7 @@ class BsaBwdArgs(ctypes.Structure):
         ("block_mask", c_void_p), ("q", c_void_p), ("k", c_void_p), ("v", c_void_p),
         ("out", c_void_p), ("dout", c_void_p), ("lse", c_void_p),
         ("dq", c_void_p), ("dk", c_void_p), ("dv", c_void_p),
-    ] + TRAIL
+    ] + TRAIL + [("cu_seqlens_q", POINTER(c_int32)), ("cu_seqlens_kv", POINTER(c_int32))]
 
 
 _NSA_COMMON = [

@@ -63,12 +63,13 @@ StageTimer timer_of(const A* a, hipStream_t st) {
 int check_bsa_common(int dtype, int ql, int kl, int B, int N1, int N2, int Sq, int Skv, int D,
                      int bq, int bkv, int mode, float scale) {
   if (dtype != TSA_BF16 && dtype != TSA_FP16) return TSA_ERR_INVALID;
-  // "aclnnBlockSparseAttentionGrad", constraints: only BNSD is supported
-  // (TND is a documented layout, not built here).
+  // "aclnnBlockSparseAttentionGrad", layout section: qInputLayout and
+  // kvInputLayout are TND or BNSD (the operator itself builds only BNSD, per
+  // its constraints; both are built here, q and k/v in the same layout).
   if ((ql != TSA_LAYOUT_BNSD && ql != TSA_LAYOUT_TND) ||
       (kl != TSA_LAYOUT_BNSD && kl != TSA_LAYOUT_TND))
     return TSA_ERR_INVALID;
-  if (ql != TSA_LAYOUT_BNSD || kl != TSA_LAYOUT_BNSD) return TSA_ERR_UNSUPPORTED;
+  if (ql != kl) return TSA_ERR_UNSUPPORTED;
   if (B < 0 || Sq < 0 || Skv < 0 || N1 < 1 || N2 < 1) return TSA_ERR_INVALID;
   // constraints: N1 >= N2 and N1 % N2 == 0
   if (N1 % N2 != 0) return TSA_ERR_INVALID;
@@ -83,7 +84,37 @@ int check_bsa_common(int dtype, int ql, int kl, int B, int N1, int N2, int Sq, i
   return TSA_OK;
 }
 
+// TND: host prefix sums cu_seqlens_q / _kv [B+1] from 0 (the layout
+// section: actualSeqLengths are mandatory with TND); every sequence at most
+// Sq / Skv long (those give the mask's padded block counts).
+template <class A>
+int check_bsa_tnd(const A* a) {
+  if (a->q_layout != TSA_LAYOUT_TND) return TSA_OK;
+  if (!a->cu_seqlens_q || !a->cu_seqlens_kv) return TSA_ERR_NULL;
+  const int32_t* cq = a->cu_seqlens_q;
+  const int32_t* ck = a->cu_seqlens_kv;
+  if (cq[0] != 0 || ck[0] != 0) return TSA_ERR_INVALID;
+  for (int b = 0; b < a->B; b++) {
+    const long sq = (long)cq[b + 1] - cq[b], sk = (long)ck[b + 1] - ck[b];
+    if (sq < 0 || sk < 0 || sq > a->Sq || sk > a->Skv) return TSA_ERR_INVALID;
+  }
+  if (!fits_i32((long)cq[a->B] * a->N1 * a->D) || !fits_i32((long)ck[a->B] * a->N2 * a->D))
+    return TSA_ERR_INVALID;
+  return TSA_OK;
+}
+
+// Query / key rows the call touches (TND: the tokens; BNSD: B*Sq, B*Skv).
+template <class A>
+long bsa_q_rows(const A* a) {
+  return a->q_layout == TSA_LAYOUT_TND ? (long)a->cu_seqlens_q[a->B] : (long)a->B * a->Sq;
+}
+template <class A>
+long bsa_kv_rows(const A* a) {
+  return a->q_layout == TSA_LAYOUT_TND ? (long)a->cu_seqlens_kv[a->B] : (long)a->B * a->Skv;
+}
+
 struct BsaWs {
+  int* meta;     // TND: cu_q [B+1], cu_kv [B+1]
   int* parts;
   int* sums;
   int* row_ptr;
@@ -102,6 +133,7 @@ size_t bsa_carve(const A* a, void* ws, BsaWs* out, bool with_delta) {
   const long nparts = bsa_compact_parts_len(a->B, a->N1, a->N2, QB, KB);
   Carver c(ws);
   BsaWs w;
+  w.meta = c.take<int>(2 * ((long)a->B + 1));
   w.parts = c.take<int>(nparts);
   w.sums = c.take<int>(scan_sums_len(nparts));
   w.row_ptr = c.take<int>(R + 1);
@@ -121,9 +153,11 @@ int check_bsa_fwd(const bsa_fwd_args* a) {
   int s = check_bsa_common(a->dtype, a->q_layout, a->kv_layout, a->B, a->N1, a->N2, a->Sq, a->Skv,
                            a->D, a->block_q, a->block_kv, a->sparse_mode, a->scale);
   if (s) return s;
-  const bool empty = (long)a->B * a->Sq == 0;
+  s = check_bsa_tnd(a);
+  if (s) return s;
+  const bool empty = bsa_q_rows(a) == 0;
   if (!empty && (!a->q || !a->out || !a->lse || !a->block_mask)) return TSA_ERR_NULL;
-  if (!empty && a->Skv > 0 && (!a->k || !a->v)) return TSA_ERR_NULL;
+  if (!empty && bsa_kv_rows(a) > 0 && (!a->k || !a->v)) return TSA_ERR_NULL;
   return TSA_OK;
 }
 
@@ -133,11 +167,31 @@ int check_bsa_bwd(const bsa_bwd_args* a) {
   int s = check_bsa_common(a->dtype, a->q_layout, a->kv_layout, a->B, a->N1, a->N2, a->Sq, a->Skv,
                            a->D, a->block_q, a->block_kv, a->sparse_mode, a->scale);
   if (s) return s;
-  const bool empty_q = (long)a->B * a->Sq == 0, empty_k = (long)a->B * a->Skv == 0;
+  s = check_bsa_tnd(a);
+  if (s) return s;
+  const bool empty_q = bsa_q_rows(a) == 0, empty_k = bsa_kv_rows(a) == 0;
   if (!empty_q && (!a->q || !a->out || !a->dout || !a->lse || !a->dq || !a->block_mask))
     return TSA_ERR_NULL;
   if (!empty_k && (!a->k || !a->v || !a->dk || !a->dv)) return TSA_ERR_NULL;
   return TSA_OK;
+}
+
+// TND: uploads cu_seqlens into the workspace and points the kernels at them.
+template <class A>
+hipError_t bsa_upload_seqlens(const A* a, const BsaWs& w, BsaParams* p, hipStream_t st) {
+  if (a->q_layout != TSA_LAYOUT_TND) return hipSuccess;
+  const int n = a->B + 1;
+  int* host = new int[2 * n];
+  for (int b = 0; b < n; b++) {
+    host[b] = a->cu_seqlens_q[b];
+    host[n + b] = a->cu_seqlens_kv[b];
+  }
+  hipError_t e = hipMemcpyAsync(w.meta, host, sizeof(int) * 2 * n, hipMemcpyHostToDevice, st);
+  // the copy from pageable memory is staged before hipMemcpyAsync returns
+  delete[] host;
+  p->cu_q = w.meta;
+  p->cu_kv = w.meta + n;
+  return e;
 }
 
 BsaParams bsa_params(int B, int N1, int N2, int Sq, int Skv, int bq, int bkv, int mode,
@@ -463,14 +517,15 @@ int bsa_fwd(const bsa_fwd_args* a, void* ws, size_t ws_bytes, void* stream) {
   int s = bsa_fwd_workspace_size(a, &need);
   if (s) return s;
   if (!ws || ws_bytes < need) return TSA_ERR_WORKSPACE;
-  if ((long)a->B * a->Sq == 0) return TSA_OK;
+  if (bsa_q_rows(a) == 0) return TSA_OK;
   hipStream_t st = (hipStream_t)stream;
   BsaWs w;
   bsa_carve(a, ws, &w, false);
   BsaParams p = bsa_params(a->B, a->N1, a->N2, a->Sq, a->Skv, a->block_q, a->block_kv,
                            a->sparse_mode, a->scale);
   const StageTimer tm = timer_of(a, st);
-  hipError_t e = tm.mark(0, 0);
+  hipError_t e = bsa_upload_seqlens(a, w, &p, st);
+  if (e == hipSuccess) e = tm.mark(0, 0);
   if (e == hipSuccess && !a->reuse_lists) {
     if (p.KB > 0)
       e = launch_bsa_compact(a->block_mask, a->B, a->N1, a->N2, p.QB, p.KB, w.parts, w.sums,
@@ -511,7 +566,8 @@ int bsa_bwd(const bsa_bwd_args* a, void* ws, size_t ws_bytes, void* stream) {
                            a->sparse_mode, a->scale);
   const long R = (long)a->B * a->N1 * p.QB, C = (long)a->B * a->N2 * p.KB;
   const StageTimer tm = timer_of(a, st);
-  hipError_t e = tm.mark(0, 0);
+  hipError_t e = bsa_upload_seqlens(a, w, &p, st);
+  if (e == hipSuccess) e = tm.mark(0, 0);
   if (e == hipSuccess && !a->reuse_lists) {
     if (R > 0 && C > 0) {
       e = launch_bsa_compact(a->block_mask, a->B, a->N1, a->N2, p.QB, p.KB, w.parts, w.sums,

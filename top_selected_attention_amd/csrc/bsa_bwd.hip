@@ -51,8 +51,11 @@ __global__ __launch_bounds__(NW * 64) void bsa_dq_kernel(BsaParams p, int qsub, 
   const int bn = tile / p.QB;
   const int n1 = bn % p.N1, b = bn / p.N1;
   const int n2 = n1 / p.G;
+  const BsaRowMap qm = bsa_rows(p.cu_q, b, p.N1, p.Sq, kD);
+  const BsaRowMap km = bsa_rows(p.cu_kv, b, p.N2, p.Skv, kD);
+  const BsaRowMap sm = bsa_rows(p.cu_q, b, p.N1, p.Sq, 1);
   const int row_lo = qb * p.bq + qs * NR;
-  const int row_hi = min((qb + 1) * p.bq, p.Sq);
+  const int row_hi = min((qb + 1) * p.bq, qm.len);
   if (row_lo >= row_hi) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -61,18 +64,19 @@ __global__ __launch_bounds__(NW * 64) void bsa_dq_kernel(BsaParams p, int qsub, 
   const int qrow = wrow0 + l32;
   const bool row_ok = qrow < row_hi;
 
-  const long qoff = (long)bn * p.Sq * kD;
-  const T* kh = (const T*)p.k + ((long)b * p.N2 + n2) * p.Skv * kD;
-  const T* vh = (const T*)p.v + ((long)b * p.N2 + n2) * p.Skv * kD;
+  const long qoff = qm.at(n1, qrow);  // this lane's query row
+  const T* kh = (const T*)p.k + km.at(n2, 0);
+  const T* vh = (const T*)p.v + km.at(n2, 0);
+  const long krow_bytes = (long)km.row * 2;
 
   // Stationary operands of this lane's query: Q^T and dO^T columns;
   // softmax_grad D = rowsum(dO * O) formed here and stored; LSE (base 2).
   V8 qreg[8], doreg[8];
   float dlt, lse2;
   {
-    const T* qr = (const T*)p.q + qoff + (long)qrow * kD;
-    const T* orr = (const T*)p.o + qoff + (long)qrow * kD;
-    const T* dor = (const T*)p.dout + qoff + (long)qrow * kD;
+    const T* qr = (const T*)p.q + qoff;
+    const T* orr = (const T*)p.o + qoff;
+    const T* dor = (const T*)p.dout + qoff;
     float acc = 0.f;
 #pragma unroll
     for (int ds = 0; ds < 8; ds++) {
@@ -85,8 +89,8 @@ __global__ __launch_bounds__(NW * 64) void bsa_dq_kernel(BsaParams p, int qsub, 
     }
     acc += __shfl_xor(acc, 32);
     dlt = acc;
-    lse2 = row_ok ? p.lse[(long)bn * p.Sq + qrow] * kLog2e : 0.f;
-    if (row_ok && h == 0) p.delta[(long)bn * p.Sq + qrow] = acc;
+    lse2 = row_ok ? p.lse[sm.at(n1, qrow)] * kLog2e : 0.f;
+    if (row_ok && h == 0) p.delta[sm.at(n1, qrow)] = acc;
   }
 
   const int e0 = p.row_ptr[bn * p.QB + qb], e1 = p.row_ptr[bn * p.QB + qb + 1];
@@ -97,7 +101,7 @@ __global__ __launch_bounds__(NW * 64) void bsa_dq_kernel(BsaParams p, int qsub, 
   auto chunk_range = [&](ChunkPos c, int& ks, int& ke) {
     const int kb = colw(c.e);
     ks = kb * p.bkv + c.s * 64;
-    ke = min(min(ks + 64, (kb + 1) * p.bkv), p.Skv);
+    ke = min(min(ks + 64, (kb + 1) * p.bkv), km.len);
   };
   auto next_valid = [&](ChunkPos c) {
     for (; c.e < e1; c = chunk_advance(c, cpb)) {
@@ -109,8 +113,8 @@ __global__ __launch_bounds__(NW * 64) void bsa_dq_kernel(BsaParams p, int qsub, 
   };
   auto load_chunk = [&](int ks, int ke, int buf) {
     auto row_of = [&](int r) { return min(ks + r, ke - 1); };
-    stage_tile64<NW>((const char*)kh, lds_k[buf], row_of);
-    stage_tile64<NW>((const char*)vh, lds_v[buf], row_of);
+    stage_tile64<NW>((const char*)kh, krow_bytes, lds_k[buf], row_of);
+    stage_tile64<NW>((const char*)vh, krow_bytes, lds_v[buf], row_of);
   };
 
   f32x16 dq[4];
@@ -192,7 +196,7 @@ __global__ __launch_bounds__(NW * 64) void bsa_dq_kernel(BsaParams p, int qsub, 
   }
 
   if (row_ok) {
-    T* drow = (T*)p.out + qoff + (long)qrow * kD;
+    T* drow = (T*)p.out + qoff;
 #pragma unroll
     for (int dt = 0; dt < 4; dt++)
 #pragma unroll
@@ -241,8 +245,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int kb = tile % p.KB;
   const int bh = tile / p.KB;  // b * N2 + n2
   const int n2 = bh % p.N2, b = bh / p.N2;
+  // rows of this sequence (BNSD: one per batch entry; TND: cu_q / cu_kv)
+  const BsaRowMap qm = bsa_rows(p.cu_q, b, p.N1, p.Sq, kD);
+  const BsaRowMap km = bsa_rows(p.cu_kv, b, p.N2, p.Skv, kD);
+  const BsaRowMap sm = bsa_rows(p.cu_q, b, p.N1, p.Sq, 1);
   const int key_lo = kb * p.bkv + ksl * NK;
-  const int key_hi = min((kb + 1) * p.bkv, p.Skv);
+  const int key_hi = min((kb + 1) * p.bkv, km.len);
   if (key_lo >= key_hi) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -251,7 +259,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int mykey = wkey0 + l32;
   const bool key_ok = mykey < key_hi;
 
-  const long kvoff = (long)bh * p.Skv * kD;
+  const long kvoff = km.at(n2, 0);
   const T* kh = (const T*)p.k + kvoff;
   const T* vh = (const T*)p.v + kvoff;
 
@@ -263,13 +271,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
       const int inst = wid * (NK / 4 / NW) + u;
       const int r = inst * 4 + sub;
       const long key = min(key_lo + r, key_hi - 1);
-      g2lds16((const char*)(kh + key * kD) + ((pc ^ swz(r)) << 4), lds_k + inst * 1024);
+      g2lds16((const char*)(kh + key * km.row) + ((pc ^ swz(r)) << 4), lds_k + inst * 1024);
     }
   }
   V8 vreg[8];
 #pragma unroll
   for (int ds = 0; ds < 8; ds++)
-    vreg[ds] = key_ok ? as_v8<V8>(ld16(vh + (long)mykey * kD + ds * 16 + 8 * h)) : zero_v8<V8>();
+    vreg[ds] = key_ok ? as_v8<V8>(ld16(vh + (long)mykey * km.row + ds * 16 + 8 * h)) : zero_v8<V8>();
 
   const int c = bh * p.KB + kb;
   const int e0 = p.rev_ptr[c], e1 = p.rev_ptr[c + 1];
@@ -284,7 +292,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     const int g = p.G > 1 ? id / p.QB : 0, qb = id - g * p.QB;
     n1 = n2 * p.G + g;
     qs = qb * p.bq + c.s * kQC;
-    qe = min(min(qs + kQC, (qb + 1) * p.bq), p.Sq);
+    qe = min(min(qs + kQC, (qb + 1) * p.bq), qm.len);
   };
   auto next_valid = [&](ChunkPos c) {
     for (; c.e < e1; c = chunk_advance(c, cpq)) {
@@ -296,7 +304,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   };
   // 32 rows of Q and of dO (8 KB each) plus their LSE / softmax_grad
   auto load_chunk = [&](int n1, int qs, int qe, int buf) {
-    const long hoff = ((long)b * p.N1 + n1) * p.Sq;
+    const long qoff = qm.at(n1, 0), soff = sm.at(n1, 0);
     // The per-lane address terms are rebuilt here from an opaque copy of the
     // lane id: hoisted out of the loop they would be spilled, and a scratch
     // reload between two direct loads waits for the first to land.
@@ -307,15 +315,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     for (int u = 0; u < 8 / NW; u++) {
       const int inst = wid * (8 / NW) + u;
       const int r = inst * 4 + sub;
-      const long row = hoff + min(qs + r, qe - 1);
-      g2lds16((const char*)((const T*)p.q + row * kD) + ((pc ^ swz(r)) << 4), lds_q[buf] + inst * 1024);
-      g2lds16((const char*)((const T*)p.dout + row * kD) + ((pc ^ swz(r)) << 4),
+      const long row = qoff + (long)min(qs + r, qe - 1) * qm.row;
+      g2lds16((const char*)((const T*)p.q + row) + ((pc ^ swz(r)) << 4), lds_q[buf] + inst * 1024);
+      g2lds16((const char*)((const T*)p.dout + row) + ((pc ^ swz(r)) << 4),
               lds_do[buf] + inst * 1024);
     }
     if (wid == 0) {
       // a direct LDS load writes lane l's dword at base + 4*l for all 64
       // lanes: the arrays hold 64 entries; entries past 32 are never read
-      const long r = hoff + min(qs + ln, qe - 1);
+      const long r = soff + (long)min(qs + ln, qe - 1) * sm.row;
       g2lds4(p.lse + r, lds_lse[buf]);
       g2lds4(p.delta + r, lds_dlt[buf]);
     }
@@ -425,8 +433,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   }
 
   if (key_ok) {
-    T* dkrow = (T*)p.dk + kvoff + (long)mykey * kD;
-    T* dvrow = (T*)p.dv + kvoff + (long)mykey * kD;
+    T* dkrow = (T*)p.dk + kvoff + (long)mykey * km.row;
+    T* dvrow = (T*)p.dv + kvoff + (long)mykey * km.row;
 #pragma unroll
     for (int dt = 0; dt < 4; dt++)
 #pragma unroll

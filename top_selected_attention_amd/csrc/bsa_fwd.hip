@@ -45,8 +45,12 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_kernel(BsaParams p, int qsub,
   const int bn = tile / p.QB;  // b * N1 + n1
   const int n1 = bn % p.N1, b = bn / p.N1;
   const int n2 = n1 / p.G;
+  // rows of this sequence (BNSD: one per batch entry; TND: cu_q / cu_kv)
+  const BsaRowMap qm = bsa_rows(p.cu_q, b, p.N1, p.Sq, kD);
+  const BsaRowMap km = bsa_rows(p.cu_kv, b, p.N2, p.Skv, kD);
+  const BsaRowMap sm = bsa_rows(p.cu_q, b, p.N1, p.Sq, 1);
   const int row_lo = qb * p.bq + qs * NR;
-  const int row_hi = min((qb + 1) * p.bq, p.Sq);
+  const int row_hi = min((qb + 1) * p.bq, qm.len);
   if (row_lo >= row_hi) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -54,15 +58,16 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_kernel(BsaParams p, int qsub,
   const int wrow0 = row_lo + wid * 32;
   const int qrow = wrow0 + l32;  // this lane's query column
 
-  const T* qh = (const T*)p.q + (long)bn * p.Sq * kD;
-  const T* kh = (const T*)p.k + ((long)b * p.N2 + n2) * p.Skv * kD;
-  const T* vh = (const T*)p.v + ((long)b * p.N2 + n2) * p.Skv * kD;
+  const T* qh = (const T*)p.q + qm.at(n1, 0);
+  const T* kh = (const T*)p.k + km.at(n2, 0);
+  const T* vh = (const T*)p.v + km.at(n2, 0);
+  const long krow_bytes = (long)km.row * 2;
 
   // Q^T as the B operand of S^T = K Q^T: lane holds query l32, d = 16*ds + 8*h .. +7
   V8 qreg[8];
 #pragma unroll
   for (int ds = 0; ds < 8; ds++)
-    qreg[ds] = qrow < row_hi ? as_v8<V8>(ld16(qh + (long)qrow * kD + ds * 16 + 8 * h))
+    qreg[ds] = qrow < row_hi ? as_v8<V8>(ld16(qh + (long)qrow * qm.row + ds * 16 + 8 * h))
                              : zero_v8<V8>();
 
   const int tile_row = bn * p.QB + qb;
@@ -77,7 +82,7 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_kernel(BsaParams p, int qsub,
   auto chunk_range = [&](ChunkPos c, int& ks, int& ke) {
     const int kb = colw(c.e);
     ks = kb * p.bkv + c.s * kKC;
-    ke = min(min(ks + kKC, (kb + 1) * p.bkv), p.Skv);
+    ke = min(min(ks + kKC, (kb + 1) * p.bkv), km.len);
   };
   auto next_valid = [&](ChunkPos c) {
     for (; c.e < e1; c = chunk_advance(c, cpb)) {
@@ -92,8 +97,8 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_kernel(BsaParams p, int qsub,
   // masked, so P = 0 exactly there).
   auto load_chunk = [&](int ks, int ke, int buf) {
     auto row_of = [&](int r) { return min(ks + r, ke - 1); };
-    stage_tile64<NW>((const char*)kh, lds_k[buf], row_of);
-    stage_tile64<NW>((const char*)vh, lds_v[buf], row_of);
+    stage_tile64<NW>((const char*)kh, krow_bytes, lds_k[buf], row_of);
+    stage_tile64<NW>((const char*)vh, krow_bytes, lds_v[buf], row_of);
   };
 
   // Online softmax state of this lane's query, base 2.  The reference m only
@@ -198,7 +203,7 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_kernel(BsaParams p, int qsub,
   const float lt = lsum + __shfl_xor(lsum, 32);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   if (qrow < row_hi) {
-    T* orow = (T*)p.out + ((long)bn * p.Sq + qrow) * kD;
+    T* orow = (T*)p.out + qm.at(n1, qrow);
 #pragma unroll
     for (int dt = 0; dt < 4; dt++)
 #pragma unroll
@@ -208,7 +213,7 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_kernel(BsaParams p, int qsub,
             pack4<E>(o[dt][4 * jj] * inv, o[dt][4 * jj + 1] * inv, o[dt][4 * jj + 2] * inv,
                      o[dt][4 * jj + 3] * inv);
       }
-    if (h == 0) p.lse[(long)bn * p.Sq + qrow] = lt > 0.f ? (m + log2f(lt)) * kLn2 : -INFINITY;
+    if (h == 0) p.lse[sm.at(n1, qrow)] = lt > 0.f ? (m + log2f(lt)) * kLn2 : -INFINITY;
   }
 }
 

@@ -233,17 +233,19 @@ struct ListWindow {
 };
 
 // Stages rows [0, 64) of a 64 x 256-byte tile into swizzled LDS.  Row r of
-// the tile is global row row_of(r) (the caller clamps it into range).  The
-// NW waves of the workgroup split the 16 1-KB slices.
+// the tile is the 256 bytes at gbase + row_of(r) * row_bytes (the caller
+// clamps row_of into range).  The NW waves of the workgroup split the 16
+// 1-KB slices.
 template <int NW, class RowFn>
-__device__ __forceinline__ void stage_tile64(const char* gbase, char* lds_tile, RowFn row_of) {
+__device__ __forceinline__ void stage_tile64(const char* gbase, long row_bytes, char* lds_tile,
+                                             RowFn row_of) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int sub = lane >> 4, pc = lane & 15;
 #pragma unroll
   for (int u = 0; u < 16 / NW; u++) {
     const int inst = wid * (16 / NW) + u;
     const int r = inst * 4 + sub;
-    g2lds16(gbase + (long)row_of(r) * 256 + ((pc ^ swz(r)) << 4), lds_tile + inst * 1024);
+    g2lds16(gbase + (long)row_of(r) * row_bytes + ((pc ^ swz(r)) << 4), lds_tile + inst * 1024);
   }
 }
 

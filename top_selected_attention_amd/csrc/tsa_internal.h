@@ -74,11 +74,33 @@ struct BsaParams {
   const int* rev;
   const int* order_q;   // Q tiles (b*N1 + n1)*QB + qb, longest list first
   const int* order_kv;  // KV tiles (b*N2 + n2)*KB + kb, longest list first
-  int B, N1, N2, G, Sq, Skv, D;
+  const int* cu_q;      // TND: [B+1] query prefix sums (device); null for BNSD
+  const int* cu_kv;     // TND: [B+1] key prefix sums (device)
+  int B, N1, N2, G, Sq, Skv, D;  // TND: Sq, Skv are the longest sequences
   int bq, bkv, QB, KB;
   int causal;
   float scale;
 };
+
+// Where the rows of one sequence b live in a BSA tensor: row r of head n is
+// element at(n, r).  BNSD: a head's rows are contiguous, S rows per head;
+// TND: rows are tokens of the sequence, the N heads of a token adjacent.
+// `elems` is the elements per row of one head (D for Q/K/V/O and their
+// gradients, 1 for the fp32 per-row LSE and softmax_grad).
+struct BsaRowMap {
+  long base;  // element offset of row 0 of head 0
+  long head;  // elements between heads
+  int row;    // elements between rows
+  int len;    // rows of the sequence
+  __device__ __forceinline__ long at(int n, int r) const { return base + n * head + (long)r * row; }
+};
+__device__ __forceinline__ BsaRowMap bsa_rows(const int* cu, int b, int N, int S, int elems) {
+  if (cu) {
+    const int s0 = cu[b];
+    return BsaRowMap{(long)s0 * N * elems, elems, N * elems, cu[b + 1] - s0};
+  }
+  return BsaRowMap{(long)b * N * S * elems, (long)S * elems, elems, S};
+}
 
 hipError_t launch_bsa_fwd(const BsaParams& p, int fp16, hipStream_t st);
 // ev / n_ev: caller timing events (stage 1 = dQ, stage 2 = dK/dV), may be null.
