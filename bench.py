@@ -11,9 +11,10 @@ Prints ONE JSON line.  ``value`` is effective TFLOP/s counted on the
 selected blocks only (forward 4*rows*keys*D per selected block pair,
 backward 2.5x that), i.e. algorithmic FLOPs / measured step time.
 
-Other workloads (``--workload``): bsa_small, bsa_window_128k, nsa_varlen
-(forward + backward) and sfa_decode (forward; value in GB/s of algorithmic
-gathered bytes).
+Other workloads (``--workload``): bsa_small, bsa_window_128k, bsa_tnd_varlen
+(block-sparse in TND layout over sequences of 2048, 4096, 8192, 2048 tokens,
+16 query / 4 KV heads), nsa_varlen (forward + backward) and sfa_decode
+(forward; value in GB/s of algorithmic gathered bytes).
 """
 
 import argparse
@@ -42,8 +43,8 @@ def parse():
     # cold start reads several percent slow)
     ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--workload", default="bsa_causal_8k",
-                    choices=["bsa_causal_8k", "bsa_small", "bsa_window_128k", "nsa_varlen",
-                             "sfa_decode"])
+                    choices=["bsa_causal_8k", "bsa_small", "bsa_window_128k", "bsa_tnd_varlen",
+                             "nsa_varlen", "sfa_decode"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -209,6 +210,92 @@ def cpu_baseline_bsa(ctx, seconds):
     return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": _threads(),
             "kind": "oracle",
             "sample": f"{done} of {len(order)} Q blocks (fwd + bwd, float64) of {w['name']}, "
+                      f"{el:.1f} s"}
+
+
+def _tnd_pair_flops(mask, seqlens, bq, bkv, D=128):
+    """Sum over sequences of their selected pairs' rows * keys * D (each
+    sequence's own blocks only)."""
+    total = 0.0
+    for b, L in enumerate(seqlens):
+        QB, KB = -(-L // bq), -(-L // bkv)
+        total += _pair_flops(mask[b:b + 1, :, :QB, :KB], bq, bkv, L, L, D)
+    return total
+
+
+def bench_bsa_tnd(args):
+    import torch
+    import workloads as W
+    import top_selected_attention_amd as tsa
+
+    w = W.bsa_tnd_workload()
+    cu, q, k, v, do, mask = W.bsa_tnd_inputs()
+    bq, bkv, scale = w["bq"], w["bkv"], 1.0 / math.sqrt(w["D"])
+    unit = _tnd_pair_flops(mask, w["seqlens"], bq, bkv)
+    fwd_flops, bwd_flops = 4.0 * unit, 10.0 * unit
+    dev = torch.device("cuda", 0)
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
+    plan = tsa.BsaPlan(qd, kd, vd, torch.from_numpy(mask).to(dev), bq, bkv, scale, 0,
+                       cu_seqlens_q=cu, cu_seqlens_kv=cu)
+    plan.set_dout(dod)
+    stl, ms_step, K, ms_ev = _timed_steps(args, plan, 2, 3)
+    st = dict(zip(["fwd_lists", "fwd_attention", "bwd_lists", "bwd_dq", "bwd_dkdv"], stl))
+    fwd_ms = st["fwd_lists"] + st["fwd_attention"]
+    bwd_ms = st["bwd_lists"] + st["bwd_dq"] + st["bwd_dkdv"]
+    kern = {"bsa_fwd_kernel": (st["fwd_attention"], 4.0 * unit),
+            "bsa_dq_kernel": (st["bwd_dq"], 6.0 * unit),
+            "bsa_dkdv_kernel": (st["bwd_dkdv"], 8.0 * unit)}
+    dom = max(kern, key=lambda n: kern[n][0])
+    dms, dfl = kern[dom]
+    achieved = dfl / (dms * 1e-3) / 1e12
+    value = (fwd_flops + bwd_flops) / (ms_step * 1e-3) / 1e12
+    res = {
+        "metric": "effective TFLOP/s on selected blocks (fwd, bwd) and % of bf16 MFMA peak",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w["dtype"], "data": "synthetic",
+        "config": {"workload": w["name"], "layout": "TND", "seqlens": w["seqlens"],
+                   "N1": w["N1"], "N2": w["N2"], "D": w["D"], "block": f"{bq}x{bkv}",
+                   "selected_pairs": int((mask != 0).sum()), "sparse_mode": 0},
+        "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "fwd_tflops": round(fwd_flops / (fwd_ms * 1e-3) / 1e12, 2),
+        "bwd_tflops": round(bwd_flops / (bwd_ms * 1e-3) / 1e12, 2),
+        "stage_ms": {k_: round(v_, 4) for k_, v_ in st.items()},
+        "ms_per_step_instrumented": round(ms_ev, 4),
+        "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": _traffic(w["name"], dom)},
+    }
+    return res, (w, cu, q, k, v, do, mask, scale)
+
+
+def cpu_baseline_bsa_tnd(ctx, seconds):
+    """Oracle (float64 numpy) fwd + bwd on a bounded sample of Q tiles."""
+    import oracle
+    w, cu, q, k, v, do, mask, scale = ctx
+    bq, bkv = w["bq"], w["bkv"]
+    qn, kn, vn, don = (t.float().numpy() for t in (q, k, v, do))
+    tiles = [(b, n, qb) for b, L in enumerate(w["seqlens"]) for n in range(w["N1"])
+             for qb in range(-(-L // bq))]
+    done, flops = 0, 0.0
+    t0 = time.perf_counter()
+    for tile in tiles:
+        b, n, qb = tile
+        out, _ = oracle.bsa_fwd_tnd(qn, kn, vn, mask, cu, cu, bq, bkv, scale, 0, q_tiles=[tile])
+        oracle.bsa_bwd_tnd(qn, kn, vn, np.nan_to_num(out), don, mask, cu, cu, bq, bkv, scale, 0,
+                           q_tiles=[tile])
+        L = w["seqlens"][b]
+        rows = min(bq, L - qb * bq)
+        keys = oracle.bsa_keys(mask[b, n, qb, :-(-L // bkv)], bkv, L).size
+        flops += 14.0 * rows * keys * w["D"]
+        done += 1
+        if time.perf_counter() - t0 > seconds:
+            break
+    el = time.perf_counter() - t0
+    return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": _threads(),
+            "kind": "oracle",
+            "sample": f"{done} of {len(tiles)} Q tiles (fwd + bwd, float64) of {w['name']}, "
                       f"{el:.1f} s"}
 
 
@@ -549,7 +636,8 @@ def ingest(d, workload):
                           "avg_us_kernel_trace": round(sum(v) / len(v), 1)}
     _save_traffic(t)
     rl = bench["roofline"]
-    cmd = (f"python3 bench.py --workload {workload} --steps 5 --warmup 2 --cpu-seconds 0")
+    cmd = (f"python3 bench.py --workload {workload} --steps {bench['steps']} "
+           f"--warmup {bench['warmup']} --cpu-seconds 0")
     pcmd = (f"python3 bench.py --workload {workload} --steps 2 --warmup 1 --cpu-seconds 0")
     out = [
         f"# {dom} on {workload}: rocprofv3 kernel trace and HBM counters",
@@ -626,6 +714,10 @@ def main():
         res, ctx = bench_bsa(args)
         if args.cpu_seconds > 0:
             res["cpu_baseline"] = cpu_baseline_bsa(ctx, args.cpu_seconds)
+    elif args.workload == "bsa_tnd_varlen":
+        res, ctx = bench_bsa_tnd(args)
+        if args.cpu_seconds > 0:
+            res["cpu_baseline"] = cpu_baseline_bsa_tnd(ctx, args.cpu_seconds)
     elif args.workload == "nsa_varlen":
         res, ctx = bench_nsa(args)
         if args.cpu_seconds > 0:

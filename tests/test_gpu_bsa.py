@@ -354,3 +354,43 @@ def test_tnd_varlen_fwd_bwd(lens_q, lens_kv, N1, N2, bq, bkv, mode):
 
 def test_tnd_varlen_fp16():
     _tnd_case([130, 257], [130, 257], 2, 2, 64, 64, 2, torch.float16, 510)
+
+
+def test_tnd_varlen_workload_sampled():
+    """The full TND workload (sequences of 2048, 4096, 8192, 2048 tokens, 16
+    query / 4 KV heads, 128x128 blocks) in the timed launch configuration:
+    out / LSE / dQ on sampled Q blocks; dK / dV on sampled KV blocks of a KV
+    head, with every Q block of its 4 query heads that selected them."""
+    tsa = _tsa()
+    w = W.bsa_tnd_workload()
+    cu, q, k, v, do, mask = W.bsa_tnd_inputs()
+    bq, bkv, scale = w["bq"], w["bkv"], 1 / math.sqrt(128)
+    qd, kd, vd, dod = _dev(q, k, v, do)
+    plan = tsa.BsaPlan(qd, kd, vd, torch.from_numpy(mask).cuda(), bq, bkv, scale, 0,
+                       cu_seqlens_q=cu, cu_seqlens_kv=cu)
+    out, lse = plan.fwd()
+    dq, dk, dv = plan.bwd(dod)
+    torch.cuda.synchronize()
+    G = w["N1"] // w["N2"]
+    tiles = set()
+    qrows = np.zeros((int(cu[-1]), w["N1"]), bool)
+    kv_rows = np.zeros((int(cu[-1]), w["N2"]), bool)
+    for b, n2, kb in [(0, 0, 0), (2, 3, 0), (2, 3, 63), (1, 1, 17)]:
+        kv_rows[cu[b] + kb * bkv:cu[b] + (kb + 1) * bkv, n2] = True
+        for n1 in range(n2 * G, (n2 + 1) * G):
+            for qb in np.nonzero(mask[b, n1, :, kb])[0]:
+                tiles.add((b, n1, int(qb)))
+    for b, n1, qb in [(0, 0, 0), (2, 15, 63), (3, 5, 15), (1, 9, 31)]:
+        tiles.add((b, n1, qb))
+    tiles = sorted(tiles)
+    for b, n1, qb in tiles:
+        qrows[cu[b] + qb * bq:cu[b] + (qb + 1) * bq, n1] = True
+    qn, kn, vn, don = _np(q), _np(k), _np(v), _np(do)
+    ro, rl = oracle.bsa_fwd_tnd(qn, kn, vn, mask, cu, cu, bq, bkv, scale, 0, q_tiles=tiles)
+    _close(out, ro, OUT_TOL, "out", qrows)
+    _lse_close(lse, rl, qrows)
+    rdq, rdk, rdv = oracle.bsa_bwd_tnd(qn, kn, vn, _np(out), don, mask, cu, cu, bq, bkv, scale, 0,
+                                       q_tiles=tiles)
+    _close(dq, rdq, GRAD_TOL, "dq", qrows)
+    _close(dk, rdk, GRAD_TOL, "dk", kv_rows)
+    _close(dv, rdv, GRAD_TOL, "dv", kv_rows)

@@ -169,6 +169,36 @@ def bsa_inputs(cfg):
     return w, q, k, v, do, mask, 1.0 / math.sqrt(D)
 
 
+def bsa_tnd_workload():
+    return dict(name="bsa_tnd_varlen", seqlens=[2048, 4096, 8192, 2048], N1=16, N2=4, D=128,
+                dtype="bf16", bq=128, bkv=128, p=0.25)
+
+
+def bsa_tnd_inputs(seqlens=None, N1=16, N2=4, bq=128, bkv=128, p=0.25, seed_base=60,
+                   dtype="bf16"):
+    """(cu_seqlens int32 [B+1], q [T,N1,D], k [T,N2,D], v [T,N2,D], dout, mask).
+
+    Per sequence a causal-shaped block mask: KV block kb <= Q block qb, the
+    diagonal kept, every other such block kept i.i.d. with p.  The mask is
+    padded to the longest sequence ([B, N1, QB, KB]) and zero past each
+    sequence's own blocks."""
+    w = bsa_tnd_workload()
+    seqlens = w["seqlens"] if seqlens is None else seqlens
+    T, D = int(sum(seqlens)), 128
+    cu = np.concatenate([[0], np.cumsum(seqlens)]).astype(np.int32)
+    q = normal((T, N1, D), seed_base + 1, dtype)
+    k = normal((T, N2, D), seed_base + 2, dtype)
+    v = normal((T, N2, D), seed_base + 3, dtype)
+    do = normal((T, N1, D), seed_base + 4, dtype)
+    QB, KB = -(-max(seqlens) // bq), -(-max(seqlens) // bkv)
+    mask = mask_random(np.random.default_rng(1000 + seed_base // 10), len(seqlens), N1, QB, KB,
+                       p, causal=True)
+    for b, L in enumerate(seqlens):
+        mask[b, :, -(-L // bq):, :] = 0
+        mask[b, :, :, -(-L // bkv):] = 0
+    return cu, q, k, v, do, mask
+
+
 def nsa_workload():
     return dict(name="nsa_varlen", seqlens=[2048, 4096, 8192, 2048], N1=32, N2=2, D=128,
                 dtype="bf16", sbs=64, sbc=16, sparse_mode=2)
