@@ -106,6 +106,34 @@ __global__ __launch_bounds__(kScanThreads) void scan_add(int* data, int n, const
     if (base + i < n) data[base + i] += add;
 }
 
+// Up to kScanSmallTiles tiles: one workgroup scans them in order with a
+// carry, in one launch instead of three (sums[t] = offset of tile t,
+// sums[nt] = total, as the three-pass path leaves them).
+constexpr int kScanSmallTiles = 4;
+__global__ __launch_bounds__(kScanThreads) void scan_small(int* data, int n, int nt, int* sums) {
+  int carry = 0;
+  for (int t = 0; t < nt; t++) {
+    const int base = t * kScanTile + threadIdx.x * kScanPer;
+    int v[kScanPer];
+    int s = 0;
+#pragma unroll
+    for (int i = 0; i < kScanPer; i++) {
+      v[i] = (base + i < n) ? data[base + i] : 0;
+      s += v[i];
+    }
+    int total;
+    int ex = carry + block_excl_scan(s, &total);
+#pragma unroll
+    for (int i = 0; i < kScanPer; i++) {
+      if (base + i < n) data[base + i] = ex;
+      ex += v[i];
+    }
+    if (threadIdx.x == 0) sums[t] = carry;
+    carry += total;
+  }
+  if (threadIdx.x == 0) sums[nt] = carry;
+}
+
 int scan_sums_len(long n) { return (int)((n + kScanTile - 1) / kScanTile) + 1; }
 
 __global__ void put_total(int* data, long n, const int* total) { data[n] = total[0]; }
@@ -122,6 +150,10 @@ hipError_t exclusive_scan(int* data, long n, int* sums, hipStream_t st) {
   int nt = (int)((n + kScanTile - 1) / kScanTile);
   if (nt == 0) {
     hipLaunchKernelGGL(scan_sums, dim3(1), dim3(kScanThreads), 0, st, sums, 0);
+    return hipGetLastError();
+  }
+  if (nt <= kScanSmallTiles) {
+    hipLaunchKernelGGL(scan_small, dim3(1), dim3(kScanThreads), 0, st, data, (int)n, nt, sums);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(scan_tiles, dim3(nt), dim3(kScanThreads), 0, st, data, (int)n, sums);
