@@ -124,6 +124,11 @@ struct BsaWs {
   int* order_q;
   int* order_kv;
   float* delta;
+  // backward dK/dV segments
+  int* seg_off;
+  int* part_off;
+  int* seg_meta;
+  float* part;
 };
 
 template <class A>
@@ -142,7 +147,14 @@ size_t bsa_carve(const A* a, void* ws, BsaWs* out, bool with_delta) {
   w.rev = c.take<int>(R * KB);
   w.order_q = c.take<int>(R);
   w.order_kv = c.take<int>(C);
+  // the dK/dV segment plan is made with the lists (forward or backward), so
+  // the forward's workspace layout holds it too
+  const BsaDkdvShape ds = bsa_dkdv_shape(a->B, a->N1, a->N2, QB, KB, a->block_kv);
+  w.seg_off = c.take<int>(ds.n_items + 1);
+  w.part_off = c.take<int>(ds.n_items + 1);
+  w.seg_meta = c.take<int>(1);
   w.delta = with_delta ? c.take<float>((long)a->B * a->N1 * a->Sq) : nullptr;
+  w.part = with_delta ? c.take<float>(ds.max_parts * 2 * ds.nk * 128) : nullptr;
   if (out) *out = w;
   return c.off + kAlign;
 }
@@ -174,6 +186,19 @@ int check_bsa_bwd(const bsa_bwd_args* a) {
     return TSA_ERR_NULL;
   if (!empty_k && (!a->k || !a->v || !a->dk || !a->dv)) return TSA_ERR_NULL;
   return TSA_OK;
+}
+
+// The dK/dV segment plan's outputs in the workspace (none without KV blocks).
+template <class A>
+BsaSegPlan seg_plan(const A* a, const BsaWs& w, const BsaParams& p) {
+  const BsaDkdvShape ds = bsa_dkdv_shape(a->B, a->N1, a->N2, p.QB, p.KB, a->block_kv);
+  BsaSegPlan sp{nullptr, nullptr, nullptr, ds.ksub, (int)ds.n_items};
+  if (p.KB > 0) {
+    sp.seg_off = w.seg_off;
+    sp.part_off = w.part_off;
+    sp.seg_meta = w.seg_meta;
+  }
+  return sp;
 }
 
 // TND: uploads cu_seqlens into the workspace and points the kernels at them.
@@ -534,7 +559,8 @@ int bsa_fwd(const bsa_fwd_args* a, void* ws, size_t ws_bytes, void* stream) {
       e = hipMemsetAsync(w.row_ptr, 0, sizeof(int) * ((long)a->B * a->N1 * p.QB + 1), st);
     if (e == hipSuccess)
       e = launch_tile_order(w.row_ptr, a->B * a->N1 * p.QB, w.order_q, w.rev_ptr,
-                            p.KB > 0 ? a->B * a->N2 * p.KB : 0, w.order_kv, st);
+                            p.KB > 0 ? a->B * a->N2 * p.KB : 0, w.order_kv, seg_plan(a, w, p),
+                            st);
   }
   if (e == hipSuccess) e = tm.mark(0, 1);
   if (e != hipSuccess) return TSA_ERR_HIP;
@@ -577,7 +603,8 @@ int bsa_bwd(const bsa_bwd_args* a, void* ws, size_t ws_bytes, void* stream) {
       if (e == hipSuccess) e = hipMemsetAsync(w.rev_ptr, 0, sizeof(int) * (C + 1), st);
     }
     if (e == hipSuccess)
-      e = launch_tile_order(w.row_ptr, (int)R, w.order_q, w.rev_ptr, (int)C, w.order_kv, st);
+      e = launch_tile_order(w.row_ptr, (int)R, w.order_q, w.rev_ptr, (int)C, w.order_kv,
+                            seg_plan(a, w, p), st);
   }
   if (e == hipSuccess) e = tm.mark(0, 1);
   if (e != hipSuccess) return TSA_ERR_HIP;
@@ -585,6 +612,7 @@ int bsa_bwd(const bsa_bwd_args* a, void* ws, size_t ws_bytes, void* stream) {
   p.out = a->dq; p.dk = a->dk; p.dv = a->dv; p.delta = w.delta;
   p.row_ptr = w.row_ptr; p.col = w.col; p.rev_ptr = w.rev_ptr; p.rev = w.rev;
   p.order_q = w.order_q; p.order_kv = w.order_kv;
+  p.seg_off = w.seg_off; p.part_off = w.part_off; p.seg_meta = w.seg_meta; p.part = w.part;
   return hip_status(launch_bsa_bwd(p, a->dtype == TSA_FP16, st, tm.ev, tm.n));
 }
 

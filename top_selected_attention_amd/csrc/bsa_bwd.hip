@@ -19,6 +19,8 @@
 // into the next MFMA as operands (see tsa_device.h).
 #include <type_traits>
 
+#include <algorithm>
+
 #include "tsa_device.h"
 #include "tsa_internal.h"
 
@@ -236,12 +238,24 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   __shared__ float lds_lse[2][64];
   __shared__ float lds_dlt[2][64];
 
-  const int item = blockIdx.x;
-  if (item >= n_items) return;
-  // Work order: KV tiles by reverse-list length, longest first
-  // (p.order_kv), dealt round-robin over the XCDs in launch order.
-  const int ksl = item % ksub;
-  const int tile = p.order_kv[item / ksub];
+  // One workgroup per segment: segment sg belongs to work item rank (the
+  // largest r with seg_off[r] <= sg), items in the order of p.order_kv
+  // (KV tiles by reverse-list length, longest first), dealt round-robin over
+  // the XCDs in launch order.
+  const int sg = blockIdx.x;
+  if (sg >= p.seg_off[n_items]) return;
+  int rank = 0;
+  {
+    int hi = n_items - 1;
+    while (rank < hi) {
+      const int mid = (rank + hi + 1) >> 1;
+      if (p.seg_off[mid] <= sg) rank = mid; else hi = mid - 1;
+    }
+  }
+  const int kseg = sg - p.seg_off[rank];
+  const int nseg = p.seg_off[rank + 1] - p.seg_off[rank];
+  const int ksl = rank % ksub;
+  const int tile = p.order_kv[rank / ksub];
   const int kb = tile % p.KB;
   const int bh = tile / p.KB;  // b * N2 + n2
   const int n2 = bh % p.N2, b = bh / p.N2;
@@ -279,8 +293,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   for (int ds = 0; ds < 8; ds++)
     vreg[ds] = key_ok ? as_v8<V8>(ld16(vh + (long)mykey * km.row + ds * 16 + 8 * h)) : zero_v8<V8>();
 
+  // this segment's entries of the KV tile's reverse list
   const int c = bh * p.KB + kb;
-  const int e0 = p.rev_ptr[c], e1 = p.rev_ptr[c + 1];
+  const int seg_len = p.seg_meta[0];
+  const int e0 = p.rev_ptr[c] + kseg * seg_len;
+  const int e1 = min(e0 + seg_len, p.rev_ptr[c + 1]);
   ListWindow revw(p.rev, e0, e1);
   const int cpq = (p.bq + kQC - 1) / kQC;
   const float sl2 = p.scale * kLog2e;
@@ -432,7 +449,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     i = inext;
   }
 
-  if (key_ok) {
+  if (key_ok && nseg == 1) {
     T* dkrow = (T*)p.dk + kvoff + (long)mykey * km.row;
     T* dvrow = (T*)p.dv + kvoff + (long)mykey * km.row;
 #pragma unroll
@@ -446,6 +463,57 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         *reinterpret_cast<uint2*>(dvrow + d0) =
             pack4<E>(dvt[dt][4 * jj], dvt[dt][4 * jj + 1], dvt[dt][4 * jj + 2], dvt[dt][4 * jj + 3]);
       }
+  } else if (key_ok) {
+    // fp32 partials of a split item: [slot][dK, dV][key of the item][d]
+    float* pk = p.part + ((long)(p.part_off[rank] + kseg) * 2 * NK + (mykey - key_lo)) * kD;
+    float* pv = pk + (long)NK * kD;
+#pragma unroll
+    for (int dt = 0; dt < 4; dt++)
+#pragma unroll
+      for (int jj = 0; jj < 4; jj++) {
+        const int d0 = dt * 32 + 8 * jj + 4 * h;
+        *reinterpret_cast<float4*>(pk + d0) =
+            make_float4(dkt[dt][4 * jj], dkt[dt][4 * jj + 1], dkt[dt][4 * jj + 2], dkt[dt][4 * jj + 3]);
+        *reinterpret_cast<float4*>(pv + d0) =
+            make_float4(dvt[dt][4 * jj], dvt[dt][4 * jj + 1], dvt[dt][4 * jj + 2], dvt[dt][4 * jj + 3]);
+      }
+  }
+}
+
+// Sums the segments' fp32 partials of each split dK/dV work item in segment
+// order (fixed order: bit-identical reruns) and writes dK (times scale) and
+// dV.  One workgroup per work item; items with one segment wrote their rows
+// themselves.
+template <class E, int NW>
+__global__ __launch_bounds__(256) void bsa_dkdv_reduce(BsaParams p, int ksub, int n_items) {
+  typedef typename E::T T;
+  constexpr int NK = NW * 32;
+  const int rank = blockIdx.x;
+  if (rank >= n_items) return;
+  const int nseg = p.seg_off[rank + 1] - p.seg_off[rank];
+  if (nseg <= 1) return;
+  const int ksl = rank % ksub;
+  const int tile = p.order_kv[rank / ksub];
+  const int kb = tile % p.KB, bh = tile / p.KB;
+  const int n2 = bh % p.N2, b = bh / p.N2;
+  const BsaRowMap km = bsa_rows(p.cu_kv, b, p.N2, p.Skv, kD);
+  const int key_lo = kb * p.bkv + ksl * NK;
+  const int key_hi = min((kb + 1) * p.bkv, km.len);
+  const float* base = p.part + (long)p.part_off[rank] * 2 * NK * kD;
+  for (int i = threadIdx.x; i < 2 * NK * (kD / 4); i += 256) {
+    const int which = i / (NK * (kD / 4));  // 0 dK, 1 dV
+    const int kk = (i / (kD / 4)) % NK, d4 = i % (kD / 4);
+    const int key = key_lo + kk;
+    if (key >= key_hi) continue;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int sgi = 0; sgi < nseg; sgi++) {
+      const float4 x = *reinterpret_cast<const float4*>(
+          base + ((long)sgi * 2 * NK + which * NK + kk) * kD + 4 * d4);
+      acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
+    }
+    const float sc = which ? 1.f : p.scale;
+    T* dst = (T*)(which ? p.dv : p.dk) + km.at(n2, key) + 4 * d4;
+    *reinterpret_cast<uint2*>(dst) = pack4<E>(acc.x * sc, acc.y * sc, acc.z * sc, acc.w * sc);
   }
 }
 
@@ -464,9 +532,24 @@ static hipError_t launch_dkdv_t(const BsaParams& p, hipStream_t st) {
   const int ksub = (p.bkv + NW * 32 - 1) / (NW * 32);
   const int n_items = p.B * p.N2 * p.KB * ksub;
   if (n_items == 0) return hipSuccess;
-  hipLaunchKernelGGL((bsa_dkdv_kernel<E, NW>), dim3(8 * ((n_items + 7) / 8)), dim3(NW * 64), 0,
+  // the segment plan was made with the lists (launch_tile_order); at most
+  // n_items + kBsaMaxParts segments, the surplus workgroups exit
+  hipLaunchKernelGGL((bsa_dkdv_kernel<E, NW>), dim3(n_items + kBsaMaxParts), dim3(NW * 64), 0,
                      st, p, ksub, n_items);
+  hipLaunchKernelGGL((bsa_dkdv_reduce<E, NW>), dim3(n_items), dim3(256), 0, st, p, ksub, n_items);
   return hipGetLastError();
+}
+
+BsaDkdvShape bsa_dkdv_shape(int B, int N1, int N2, int QB, int KB, int bkv) {
+  BsaDkdvShape s;
+  const int nw = bkv <= 32 ? 1 : (bkv <= 64 ? 2 : 4);  // as launch_bwd_t picks
+  s.nk = 32 * nw;
+  s.ksub = (bkv + s.nk - 1) / s.nk;
+  s.n_items = (long)B * N2 * KB * s.ksub;
+  // partial slots: fewer than kBsaMaxParts, and fewer than twice the
+  // entries of all items (R * KB bounds the reverse-list entries)
+  s.max_parts = std::max(1L, std::min((long)kBsaMaxParts, 2L * B * N1 * QB * KB * s.ksub));
+  return s;
 }
 
 template <class E>

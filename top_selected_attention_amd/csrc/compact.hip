@@ -25,39 +25,6 @@ constexpr int kScanThreads = 1024;
 constexpr int kScanPer = 4;
 constexpr int kScanTile = kScanThreads * kScanPer;
 
-__device__ __forceinline__ int wave_incl_scan(int x) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
-  return x;
-}
-
-// Block-wide exclusive scan of one value per thread; returns the exclusive
-// prefix, *total gets the block sum.
-__device__ __forceinline__ int block_excl_scan(int x, int* total) {
-  __shared__ int wsum[kScanThreads / 64];
-  __shared__ int tot;
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int nw = blockDim.x >> 6;
-  const int incl = wave_incl_scan(x);
-  if (lane == 63) wsum[wid] = incl;
-  __syncthreads();
-  if (wid == 0) {
-    const int v = lane < nw ? wsum[lane] : 0;
-    const int vi = wave_incl_scan(v);
-    if (lane < nw) wsum[lane] = vi - v;
-    if (lane == nw - 1) tot = vi;
-  }
-  __syncthreads();
-  const int excl = wsum[wid] + incl - x;
-  *total = tot;
-  __syncthreads();  // wsum / tot are reused by the next call
-  return excl;
-}
-
 // ptr[i] = scanned[i] for i < n, ptr[n] = *total.
 __global__ void copy_ptr(const int* scanned, long n, const int* total, int* ptr) {
   const long i = (long)blockIdx.x * 256 + threadIdx.x;
@@ -317,8 +284,49 @@ hipError_t launch_bsa_compact(const uint8_t* mask, int B, int N1, int N2, int QB
 // ---------------------------------------------------------------------------
 constexpr int kOrderBins = 2048;
 
+// Segment plan of the BSA dK/dV work items, made by the workgroup that
+// ordered the KV tiles.  The segment length S = max(1, ceil(E * ksub /
+// kBsaDkdvSlots)) for E reverse-list entries in all keeps every segment
+// within one workgroup slot's fair share of the work, so a KV block that
+// many Q blocks selected no longer sets the kernel's length.  Work item r
+// (KV tile order[r / ksub], key split r % ksub) with L entries gets
+// max(1, ceil(L / S)) segments, and fp32 partial slots only when it has more
+// than one: fewer than 2 * kBsaDkdvSlots slots in all (each split item has
+// L > S, so ceil(L / S) < 2 L / S).  Writes exclusive prefix sums with their
+// totals at [n_items].
+__device__ void bsa_seg_plan(const int* rev_ptr, int n_tiles, const int* order, int ksub,
+                             int n_items, int* seg_off, int* part_off, int* seg_meta) {
+  const long E = rev_ptr[n_tiles];
+  const int S = (int)max(1L, (E * ksub + kBsaDkdvSlots - 1) / kBsaDkdvSlots);
+  if (threadIdx.x == 0) seg_meta[0] = S;
+  int carry_s = 0, carry_p = 0;
+  for (int base = 0; base < n_items; base += blockDim.x) {
+    const int r = base + threadIdx.x;
+    int ns = 0;
+    if (r < n_items) {
+      const int tile = order[r / ksub];
+      ns = max(1, (rev_ptr[tile + 1] - rev_ptr[tile] + S - 1) / S);
+    }
+    const int np = ns > 1 ? ns : 0;
+    int ts, tp;
+    const int es = block_excl_scan(ns, &ts);
+    const int ep = block_excl_scan(np, &tp);
+    if (r < n_items) {
+      seg_off[r] = carry_s + es;
+      part_off[r] = carry_p + ep;
+    }
+    carry_s += ts;
+    carry_p += tp;
+  }
+  if (threadIdx.x == 0) {
+    seg_off[n_items] = carry_s;
+    part_off[n_items] = carry_p;
+  }
+}
+
 __global__ __launch_bounds__(1024) void tile_order(const int* ptr_a, int n_a, int* ord_a,
-                                                   const int* ptr_b, int n_b, int* ord_b) {
+                                                   const int* ptr_b, int n_b, int* ord_b,
+                                                   BsaSegPlan plan) {
   const int* ptr = blockIdx.x ? ptr_b : ptr_a;
   const int n = blockIdx.x ? n_b : n_a;
   int* ord = blockIdx.x ? ord_b : ord_a;
@@ -355,12 +363,17 @@ __global__ __launch_bounds__(1024) void tile_order(const int* ptr_a, int n_a, in
   cnt[2 * tid + 1] = base + c0;
   __syncthreads();
   for (int i = tid; i < n; i += 1024) ord[atomicAdd(&cnt[bucket(i)], 1)] = i;
+  if (blockIdx.x == 1 && plan.seg_off) {
+    __syncthreads();  // this workgroup's order writes are visible to all its threads
+    bsa_seg_plan(ptr_b, n_b, ord_b, plan.ksub, plan.n_items, plan.seg_off, plan.part_off,
+                 plan.seg_meta);
+  }
 }
 
 hipError_t launch_tile_order(const int* row_ptr, int n_rows, int* order_rows, const int* rev_ptr,
-                             int n_cols, int* order_cols, hipStream_t st) {
+                             int n_cols, int* order_cols, const BsaSegPlan& plan, hipStream_t st) {
   hipLaunchKernelGGL(tile_order, dim3(2), dim3(1024), 0, st, row_ptr, n_rows, order_rows, rev_ptr,
-                     n_cols, order_cols);
+                     n_cols, order_cols, plan);
   return hipGetLastError();
 }
 

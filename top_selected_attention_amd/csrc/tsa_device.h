@@ -285,6 +285,40 @@ __device__ __forceinline__ void sched_mfma_lds() {
   }
 }
 
+// Inclusive scan over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+// Block-wide exclusive scan of one value per thread; returns the exclusive
+// prefix, *total gets the block sum.
+__device__ __forceinline__ int block_excl_scan(int x, int* total) {
+  __shared__ int wsum[16];  // up to 1024 threads
+  __shared__ int tot;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  const int incl = wave_incl_scan(x);
+  if (lane == 63) wsum[wid] = incl;
+  __syncthreads();
+  if (wid == 0) {
+    const int v = lane < nw ? wsum[lane] : 0;
+    const int vi = wave_incl_scan(v);
+    if (lane < nw) wsum[lane] = vi - v;
+    if (lane == nw - 1) tot = vi;
+  }
+  __syncthreads();
+  const int excl = wsum[wid] + incl - x;
+  *total = tot;
+  __syncthreads();  // wsum / tot are reused by the next call
+  return excl;
+}
+
 // XCD-aware workgroup -> work-item remap.  Workgroups are dispatched to the 8
 // XCDs round-robin (workgroup w runs on XCD w % 8).  Giving XCD x the
 // contiguous range [x * per, (x + 1) * per) of the work order keeps the work

@@ -19,10 +19,18 @@ hipError_t exclusive_scan(int* data, long n, int* sums, hipStream_t st);
 hipError_t exclusive_scan_total(int* data, long n, int* sums, hipStream_t st);
 
 long bsa_compact_parts_len(int B, int N1, int N2, int QB, int KB);
+// Segment plan of the dK/dV work items (see BsaParams); seg_off null: none.
+struct BsaSegPlan {
+  int* seg_off;
+  int* part_off;
+  int* seg_meta;
+  int ksub, n_items;
+};
 // order_rows / order_cols: the n_rows forward and n_cols reverse lists' tile
-// ids by list length, longest first (the attention kernels' work order).
+// ids by list length, longest first (the attention kernels' work order);
+// with plan.seg_off set, also the dK/dV segment plan over order_cols.
 hipError_t launch_tile_order(const int* row_ptr, int n_rows, int* order_rows, const int* rev_ptr,
-                             int n_cols, int* order_cols, hipStream_t st);
+                             int n_cols, int* order_cols, const BsaSegPlan& plan, hipStream_t st);
 hipError_t launch_bsa_compact(const uint8_t* mask, int B, int N1, int N2, int QB, int KB,
                               int* parts, int* sums, int* row_ptr, int* col, int* rev_ptr,
                               int* rev, hipStream_t st);
@@ -80,7 +88,27 @@ struct BsaParams {
   int bq, bkv, QB, KB;
   int causal;
   float scale;
+  // backward dK/dV segments (workspace): work item r (in order_kv order) has
+  // seg_off[r+1] - seg_off[r] segments of at most seg_meta[0] reverse-list
+  // entries; a split item's segments write fp32 partials from slot
+  // part_off[r] on, which a reduction sums in segment order.
+  int* seg_off;        // [n_items + 1]
+  int* part_off;       // [n_items + 1]
+  int* seg_meta;       // [1]
+  float* part;         // [kBsaMaxParts][2][keys per item][D]
 };
+
+// Workgroup slots the dK/dV segment length is sized for (two 4-wave
+// workgroups on each of 256 CUs), and the partial slots that bound implies.
+constexpr int kBsaDkdvSlots = 512;
+constexpr int kBsaMaxParts = 2 * kBsaDkdvSlots;
+// dK/dV work items of a backward: keys per item, key splits per KV tile,
+// item count, and the fp32 partial slots (2 x nk x D floats each) to reserve.
+struct BsaDkdvShape {
+  int nk, ksub;
+  long n_items, max_parts;
+};
+BsaDkdvShape bsa_dkdv_shape(int B, int N1, int N2, int QB, int KB, int bkv);
 
 // Where the rows of one sequence b live in a BSA tensor: row r of head n is
 // element at(n, r).  BNSD: a head's rows are contiguous, S rows per head;
