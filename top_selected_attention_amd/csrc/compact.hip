@@ -275,14 +275,19 @@ hipError_t launch_bsa_compact(const uint8_t* mask, int B, int N1, int N2, int QB
 }
 
 // ---------------------------------------------------------------------------
-// Work order of the attention kernels: tiles by list length, longest first
-// (ties in any order), so that the workgroups dealt out last are the short
-// ones.  A counting sort in LDS: one workgroup per list set (workgroup 0 the
-// forward lists, 1 the reverse lists); lengths of kOrderBins - 1 and more
+// Work order of the attention kernels: tiles by list length, longest first,
+// equal lengths in tile order (head-major), so that the workgroups dealt out
+// last are the short ones while tiles of one head that cost the same stay
+// together (their K/V or Q/dO stay in cache).  A stable counting sort in
+// LDS, one workgroup per list set (workgroup 0 the forward lists, 1 the
+// reverse lists): each wave counts the buckets of its contiguous segment of
+// tiles, a bucket-major scan over (bucket, wave) gives every wave its slots,
+// and each wave places its tiles in index order, ranking equal buckets among
+// the 64 lanes of a step with ballots.  Lengths of kOrderBins - 1 and more
 // share the first bucket.  order[k] is the tile of rank k.  The order decides
 // only which workgroup starts when, never a result.
 // ---------------------------------------------------------------------------
-constexpr int kOrderBins = 2048;
+constexpr int kOrderBins = 256;
 
 // Segment plan of the BSA dK/dV work items, made by the workgroup that
 // ordered the KV tiles.  The segment length S = max(1, ceil(E * ksub /
@@ -330,39 +335,49 @@ __global__ __launch_bounds__(1024) void tile_order(const int* ptr_a, int n_a, in
   const int* ptr = blockIdx.x ? ptr_b : ptr_a;
   const int n = blockIdx.x ? n_b : n_a;
   int* ord = blockIdx.x ? ord_b : ord_a;
-  __shared__ int cnt[kOrderBins];
-  __shared__ int wsum[16];
+  __shared__ int cnt[16][kOrderBins];  // [wave][bucket]
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   auto bucket = [&](int i) { return kOrderBins - 1 - min(ptr[i + 1] - ptr[i], kOrderBins - 1); };
-  for (int i = tid; i < kOrderBins; i += 1024) cnt[i] = 0;
+  const int seg = (n + 15) / 16;
+  const int lo = min(w * seg, n), hi = min(lo + seg, n);
+  for (int i = tid; i < 16 * kOrderBins; i += 1024) (&cnt[0][0])[i] = 0;
   __syncthreads();
-  for (int i = tid; i < n; i += 1024) atomicAdd(&cnt[bucket(i)], 1);
+  for (int i = lo + lane; i < hi; i += 64) atomicAdd(&cnt[w][bucket(i)], 1);
   __syncthreads();
-  // exclusive scan over the buckets: thread t owns buckets 2t and 2t + 1
-  const int c0 = cnt[2 * tid], c1 = cnt[2 * tid + 1];
-  int v = c0 + c1;
+  // exclusive scan in (bucket, wave) order: thread t owns flat entries
+  // 4t .. 4t+3, entry f = bucket * 16 + wave
+  int v[4], sum = 0;
 #pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_up(v, d);
-    if (lane >= d) v += y;
+  for (int j = 0; j < 4; j++) {
+    const int f = 4 * tid + j;
+    v[j] = cnt[f & 15][f >> 4];
+    sum += v[j];
   }
-  if (lane == 63) wsum[w] = v;
-  __syncthreads();
-  if (w == 0) {
-    int x = lane < 16 ? wsum[lane] : 0;
+  int total;
+  int ex = block_excl_scan(sum, &total);
 #pragma unroll
-    for (int d = 1; d < 16; d <<= 1) {
-      const int y = __shfl_up(x, d);
-      if (lane >= d) x += y;
+  for (int j = 0; j < 4; j++) {
+    const int f = 4 * tid + j;
+    cnt[f & 15][f >> 4] = ex;
+    ex += v[j];
+  }
+  __syncthreads();
+  // each wave places its segment in index order, 64 tiles a step
+  for (int base = lo; base < hi; base += 64) {
+    const int i = base + lane;
+    const bool valid = i < hi;
+    const int bk = valid ? bucket(i) : -1;
+    unsigned long long todo = __ballot(valid);
+    while (todo) {
+      const int leader = __builtin_ctzll(todo);
+      const int lb = __shfl(bk, leader);
+      const unsigned long long peers = __ballot(bk == lb) & todo;
+      const int start = cnt[w][lb];  // read by every lane before the leader's update
+      if (bk == lb && valid) ord[start + __popcll(peers & ((1ull << lane) - 1))] = i;
+      if (lane == leader) cnt[w][lb] = start + __popcll(peers);
+      todo &= ~peers;
     }
-    if (lane < 16) wsum[lane] = x;
   }
-  __syncthreads();
-  const int base = (w ? wsum[w - 1] : 0) + v - c0 - c1;
-  cnt[2 * tid] = base;
-  cnt[2 * tid + 1] = base + c0;
-  __syncthreads();
-  for (int i = tid; i < n; i += 1024) ord[atomicAdd(&cnt[bucket(i)], 1)] = i;
   if (blockIdx.x == 1 && plan.seg_off) {
     __syncthreads();  // this workgroup's order writes are visible to all its threads
     bsa_seg_plan(ptr_b, n_b, ord_b, plan.ksub, plan.n_items, plan.seg_off, plan.part_off,
