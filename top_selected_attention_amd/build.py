@@ -1,4 +1,5 @@
-"""Builds the HIP library (libtsa.so) for gfx950 with hipcc, in-tree.
+"""Builds the HIP library (libtsa.so) for gfx950 with hipcc, in-tree, and
+beside it the measured-peaks library (peaks/libtsa_peaks.so).
 
 Usage: python top_selected_attention_amd/build.py  (or build() from Python; running it as
 a file does not import the package, which needs the library to exist).
@@ -18,6 +19,8 @@ INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_NAME = "libtsa.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
+PEAKS_SRC = os.path.join(HERE, "peaks", "peaks.hip")
+PEAKS_LIB = os.path.join(HERE, "peaks", "libtsa_peaks.so")
 
 ARCH = "gfx950"
 COMMON = [
@@ -57,17 +60,24 @@ def build(verbose=True):
     with concurrent.futures.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
         futs = [ex.submit(_compile, s, os.path.join(BUILD_DIR, os.path.basename(s) + ".o"))
                 for s in srcs]
+        pfut = ex.submit(_compile, PEAKS_SRC, os.path.join(BUILD_DIR, "peaks.hip.o"))
         for f in futs:
             objs.append(f.result())
-    tmp = LIB_PATH + ".tmp"
+        pobj = pfut.result()
+    _link(objs, LIB_PATH)
+    _link([pobj], PEAKS_LIB)
+    if verbose:
+        print(f"built {LIB_PATH} from {len(srcs)} sources, and {PEAKS_LIB}")
+    return LIB_PATH
+
+
+def _link(objs, out):
+    tmp = out + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB_PATH)
-    if verbose:
-        print(f"built {LIB_PATH} from {len(srcs)} sources")
-    return LIB_PATH
+        raise RuntimeError(f"link of {os.path.basename(out)} failed:\n{r.stderr}")
+    os.replace(tmp, out)
 
 
 if __name__ == "__main__":
