@@ -23,6 +23,13 @@ Conventions that the pages leave open, and the reading taken here:
   from the start of each sequence; mode 3 (rightDownCausal, sparse flash
   attention) places decode token s of Sq at position kv_len - Sq + s.
 * The LSE is the natural log of the softmax denominator plus the row max.
+* ``atten_mask`` of block-sparse attention (the Mask operand of the formula
+  section; its format is not given): u8, element (b, n1, i, j) non-zero =
+  the score of query position i and key position j is excluded, zero = kept;
+  shape [Sq, Skv] (every batch entry and head) or [B or 1, N1 or 1, Sq, Skv]
+  (size-1 axes broadcast).  It only removes entries of the selected blocks;
+  with sparse_mode 2 both exclusions apply.  Positions are within a sequence
+  in TND.
 
 Parity status: attend_fwd / attend_bwd, bsa_*, nsa_* and sfa_fwd are pinned by
 the tests in ``tests/test_oracle_pins.py`` (dense special cases against an
@@ -110,18 +117,38 @@ def _bsa_tiles(B, N1, QB, q_tiles):
     return [tuple(int(x) for x in t) for t in q_tiles]
 
 
-def _bsa_allowed(rows, keys, sparse_mode):
+def _am_slice(atten_mask, b, n1):
+    """The [Sq, Skv] plane of ``atten_mask`` that query head n1 of batch entry
+    b reads (None when there is no element mask)."""
+    if atten_mask is None:
+        return None
+    am = np.asarray(atten_mask)
+    if am.ndim == 2:
+        return am
+    if am.ndim != 4:
+        raise ValueError("atten_mask must be [Sq, Skv] or [B|1, N1|1, Sq, Skv]")
+    return am[b if am.shape[0] > 1 else 0, n1 if am.shape[1] > 1 else 0]
+
+
+def _bsa_allowed(rows, keys, sparse_mode, am=None):
+    """Which (row, key) scores of a Q block's selected keys enter the softmax:
+    every one, less the causal exclusions (sparse_mode 2) and the entries
+    ``am`` (an [Sq, Skv] plane of atten_mask) marks non-zero."""
     allowed = np.ones((len(rows), len(keys)), dtype=bool)
     if sparse_mode == 2:
         allowed &= keys[None, :] <= rows[:, None]
+    if am is not None:
+        allowed &= am[np.ix_(rows, keys)] == 0
     return allowed
 
 
-def bsa_fwd(q, k, v, mask, block_q, block_kv, scale, sparse_mode=0, q_tiles=None):
+def bsa_fwd(q, k, v, mask, block_q, block_kv, scale, sparse_mode=0, q_tiles=None,
+            atten_mask=None):
     """Block-sparse attention forward, BNSD.
 
     q [B, N1, Sq, D], k [B, N2, Skv, D], v [B, N2, Skv, Dv],
-    mask [B, N1, ceil(Sq/block_q), ceil(Skv/block_kv)] (non-zero = keep).
+    mask [B, N1, ceil(Sq/block_q), ceil(Skv/block_kv)] (non-zero = keep),
+    atten_mask None or as in the module docstring (non-zero = excluded).
     Returns (out [B, N1, Sq, Dv], lse [B, N1, Sq]); rows of Q blocks outside
     ``q_tiles`` (a list of (b, n1, qb), default all) are NaN.
     """
@@ -136,14 +163,15 @@ def bsa_fwd(q, k, v, mask, block_q, block_kv, scale, sparse_mode=0, q_tiles=None
         keys = bsa_keys(mask[b, n1, qb], block_kv, Skv)
         n2 = n1 // G
         o, l, _ = attend_fwd(q[b, n1, rows], k[b, n2, keys], v[b, n2, keys],
-                             _bsa_allowed(rows, keys, sparse_mode), scale)
+                             _bsa_allowed(rows, keys, sparse_mode, _am_slice(atten_mask, b, n1)),
+                             scale)
         out[b, n1, rows] = o
         lse[b, n1, rows] = l
     return out, lse
 
 
 def bsa_bwd(q, k, v, out, dout, mask, block_q, block_kv, scale, sparse_mode=0,
-            q_tiles=None):
+            q_tiles=None, atten_mask=None):
     """Block-sparse attention backward, BNSD.
 
     Returns (dq, dk, dv).  dq rows of Q blocks outside ``q_tiles`` are NaN;
@@ -164,7 +192,8 @@ def bsa_bwd(q, k, v, out, dout, mask, block_q, block_kv, scale, sparse_mode=0,
         keys = bsa_keys(mask[b, n1, qb], block_kv, Skv)
         n2 = n1 // G
         g_q, g_k, g_v = attend_bwd(q[b, n1, rows], k[b, n2, keys], v[b, n2, keys],
-                                   _bsa_allowed(rows, keys, sparse_mode),
+                                   _bsa_allowed(rows, keys, sparse_mode,
+                                                _am_slice(atten_mask, b, n1)),
                                    out[b, n1, rows], dout[b, n1, rows], scale)
         dq[b, n1, rows] = g_q
         np.add.at(dk[b, n2], keys, g_k)
@@ -181,7 +210,7 @@ def _tnd_tiles(cu_q, N1, block_q, q_tiles):
 
 
 def bsa_fwd_tnd(q, k, v, mask, cu_seqlens_q, cu_seqlens_kv, block_q, block_kv, scale,
-                sparse_mode=0, q_tiles=None):
+                sparse_mode=0, q_tiles=None, atten_mask=None):
     """Block-sparse attention forward, TND (variable-length sequences).
 
     "aclnnBlockSparseAttentionGrad", layout section: TND rows are the tokens
@@ -189,7 +218,8 @@ def bsa_fwd_tnd(q, k, v, mask, cu_seqlens_q, cu_seqlens_kv, block_q, block_kv, s
     (the actual sequence lengths are mandatory with TND).  q [T, N1, D],
     k [Tk, N2, D], v [Tk, N2, Dv]; mask [B, N1, QB, KB] with QB / KB the block
     counts of the longest sequences: sequence b reads the entries of its own
-    blocks only.  Block positions and the causal test are within a sequence.
+    blocks only.  Block positions, the causal test and atten_mask positions
+    ([Sq, Skv] planes of the longest lengths) are within a sequence.
     Returns (out [T, N1, Dv], lse [T, N1]); rows outside ``q_tiles`` (a list
     of (b, n1, qb), default all) are NaN.
     """
@@ -206,14 +236,15 @@ def bsa_fwd_tnd(q, k, v, mask, cu_seqlens_q, cu_seqlens_kv, block_q, block_kv, s
         keys = bsa_keys(mask[b, n1, qb, :-(-skv // block_kv)], block_kv, skv)
         n2 = n1 // G
         o, l, _ = attend_fwd(q[q0 + rows, n1], k[k0 + keys, n2], v[k0 + keys, n2],
-                             _bsa_allowed(rows, keys, sparse_mode), scale)
+                             _bsa_allowed(rows, keys, sparse_mode, _am_slice(atten_mask, b, n1)),
+                             scale)
         out[q0 + rows, n1] = o
         lse[q0 + rows, n1] = l
     return out, lse
 
 
 def bsa_bwd_tnd(q, k, v, out, dout, mask, cu_seqlens_q, cu_seqlens_kv, block_q, block_kv,
-                scale, sparse_mode=0, q_tiles=None):
+                scale, sparse_mode=0, q_tiles=None, atten_mask=None):
     """Block-sparse attention backward, TND: the backward chain of the
     formula section per (sequence, head, Q block), with each selected key's
     gradient added back to its row.  Returns (dq, dk, dv); as ``bsa_bwd`` for
@@ -232,7 +263,8 @@ def bsa_bwd_tnd(q, k, v, out, dout, mask, cu_seqlens_q, cu_seqlens_kv, block_q, 
         keys = bsa_keys(mask[b, n1, qb, :-(-skv // block_kv)], block_kv, skv)
         n2 = n1 // G
         g_q, g_k, g_v = attend_bwd(q[q0 + rows, n1], k[k0 + keys, n2], v[k0 + keys, n2],
-                                   _bsa_allowed(rows, keys, sparse_mode),
+                                   _bsa_allowed(rows, keys, sparse_mode,
+                                                _am_slice(atten_mask, b, n1)),
                                    out[q0 + rows, n1], dout[q0 + rows, n1], scale)
         dq[q0 + rows, n1] = g_q
         np.add.at(dk[:, n2], k0 + keys, g_k)

@@ -138,6 +138,160 @@ def test_sfa_page_table_permutation_is_invisible():
 
 
 # ----------------------------------------------------------------------------
+# atten_mask (element mask inside the selected blocks; non-zero = excluded)
+# ----------------------------------------------------------------------------
+
+def _atten_mask(r, shape, p=0.35):
+    """Random exclusions that keep the diagonal, so no row is empty."""
+    am = (r.random(shape) < p).astype(np.uint8)
+    S = min(shape[-2], shape[-1])
+    idx = np.arange(S)
+    am[..., idx, idx] = 0
+    return am
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bsa_atten_mask_all_blocks_equals_dense_masked_attention(causal):
+    """Every block selected, a per-head atten_mask: torch's dense attention
+    with the same (inverted: True = take part) boolean mask, float64 autograd."""
+    r = _rng(21)
+    N1, N2, S, D, bq, bkv = 4, 2, 36, 16, 8, 8     # ragged: 36 = 4.5 blocks
+    G = N1 // N2
+    q = r.standard_normal((1, N1, S, D))
+    k = r.standard_normal((1, N2, S, D))
+    v = r.standard_normal((1, N2, S, D))
+    do = r.standard_normal((1, N1, S, D))
+    am = _atten_mask(r, (1, N1, S, S))
+    scale = 1 / math.sqrt(D)
+    mask = np.ones((1, N1, 5, 5), np.uint8)
+    mode = 2 if causal else 0
+    out, lse = oracle.bsa_fwd(q, k, v, mask, bq, bkv, scale, mode, atten_mask=am)
+    keep = torch.tensor(am[0] == 0)
+    if causal:
+        keep &= torch.ones(S, S, dtype=torch.bool).tril()
+    qt = torch.tensor(q[0], requires_grad=True)
+    kt = torch.tensor(k[0], requires_grad=True)
+    vt = torch.tensor(v[0], requires_grad=True)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        qt[None], kt.repeat_interleave(G, 0)[None], vt.repeat_interleave(G, 0)[None],
+        attn_mask=keep[None], scale=scale)[0]
+    np.testing.assert_allclose(out[0], ref.detach().numpy(), rtol=0, atol=1e-12)
+    sc = scale * torch.tensor(q[0]) @ torch.tensor(k[0]).repeat_interleave(G, 0).transpose(1, 2)
+    np.testing.assert_allclose(lse[0], torch.logsumexp(sc.masked_fill(~keep, -math.inf), -1).numpy(),
+                               rtol=0, atol=1e-12)
+    ref.backward(torch.tensor(do[0]))
+    dq, dk, dv = oracle.bsa_bwd(q, k, v, out, do, mask, bq, bkv, scale, mode, atten_mask=am)
+    for mine, theirs in ((dq[0], qt.grad), (dk[0], kt.grad), (dv[0], vt.grad)):
+        t = theirs.numpy()
+        assert np.abs(mine - t).max() <= 1e-10 * np.abs(t).max()
+
+
+def test_bsa_atten_mask_upper_triangle_is_causal_mode():
+    """atten_mask = the strict upper triangle under sparse_mode 0 is
+    sparse_mode 2 (top-left causal), bit for bit."""
+    r = _rng(22)
+    B, N1, N2, S, D, bq, bkv = 2, 2, 1, 20, 8, 8, 4
+    q = r.standard_normal((B, N1, S, D))
+    k = r.standard_normal((B, N2, S, D))
+    v = r.standard_normal((B, N2, S, D))
+    do = r.standard_normal((B, N1, S, D))
+    mask = W.mask_random(r, B, N1, 3, 5, 0.6)
+    tri = np.triu(np.ones((S, S), np.uint8), 1)
+    o0, l0 = oracle.bsa_fwd(q, k, v, mask, bq, bkv, 0.3, 0, atten_mask=tri)
+    o2, l2 = oracle.bsa_fwd(q, k, v, mask, bq, bkv, 0.3, 2)
+    assert np.array_equal(o0, o2, equal_nan=True) and np.array_equal(l0, l2, equal_nan=True)
+    g0 = oracle.bsa_bwd(q, k, v, o0, do, mask, bq, bkv, 0.3, 0, atten_mask=tri)
+    g2 = oracle.bsa_bwd(q, k, v, o2, do, mask, bq, bkv, 0.3, 2)
+    for a, b_ in zip(g0, g2):
+        assert np.array_equal(a, b_, equal_nan=True)
+
+
+def test_bsa_atten_mask_over_a_whole_block_deselects_it():
+    """Excluding every entry of one (Q block, KV block) pair with atten_mask
+    gives the result of clearing that pair in the block mask."""
+    r = _rng(23)
+    B, N1, N2, S, D, bq, bkv = 1, 2, 2, 24, 8, 8, 8
+    q = r.standard_normal((B, N1, S, D))
+    k = r.standard_normal((B, N2, S, D))
+    v = r.standard_normal((B, N2, S, D))
+    do = r.standard_normal((B, N1, S, D))
+    mask = np.ones((B, N1, 3, 3), np.uint8)
+    am = np.zeros((B, N1, S, S), np.uint8)
+    am[0, 1, 8:16, 16:24] = 1          # head 1, Q block 1, KV block 2
+    cleared = mask.copy()
+    cleared[0, 1, 1, 2] = 0
+    oa, la = oracle.bsa_fwd(q, k, v, mask, bq, bkv, 0.35, 0, atten_mask=am)
+    ob, lb = oracle.bsa_fwd(q, k, v, cleared, bq, bkv, 0.35, 0)
+    np.testing.assert_allclose(oa, ob, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(la, lb, rtol=0, atol=1e-12)
+    ga = oracle.bsa_bwd(q, k, v, oa, do, mask, bq, bkv, 0.35, 0, atten_mask=am)
+    gb = oracle.bsa_bwd(q, k, v, ob, do, cleared, bq, bkv, 0.35, 0)
+    for a, b_ in zip(ga, gb):
+        np.testing.assert_allclose(a, b_, rtol=0, atol=1e-12)
+
+
+def test_bsa_atten_mask_broadcast_forms_agree():
+    """[Sq, Skv], [1, 1, Sq, Skv] and its expansion to [B, N1, Sq, Skv] are
+    the same mask."""
+    r = _rng(24)
+    B, N1, N2, S, D, bq, bkv = 2, 2, 2, 16, 8, 8, 8
+    q = r.standard_normal((B, N1, S, D))
+    k = r.standard_normal((B, N2, S, D))
+    v = r.standard_normal((B, N2, S, D))
+    mask = W.mask_random(r, B, N1, 2, 2, 0.7)
+    am2 = _atten_mask(r, (S, S))
+    outs = [oracle.bsa_fwd(q, k, v, mask, bq, bkv, 0.3, 0, atten_mask=a)
+            for a in (am2, am2[None, None], np.broadcast_to(am2, (B, N1, S, S)).copy())]
+    for o, l in outs[1:]:
+        assert np.array_equal(o, outs[0][0], equal_nan=True)
+        assert np.array_equal(l, outs[0][1], equal_nan=True)
+
+
+@pytest.mark.parametrize("mode", [0, 2])
+def test_bsa_atten_mask_finite_differences(mode):
+    r = _rng(25)
+    B, N1, N2, S, D, bq, bkv = 1, 2, 1, 16, 8, 4, 4
+    a = dict(q=r.standard_normal((B, N1, S, D)), k=r.standard_normal((B, N2, S, D)),
+             v=r.standard_normal((B, N2, S, D)))
+    do = r.standard_normal((B, N1, S, D))
+    mask = W.mask_random(r, B, N1, 4, 4, 0.6)
+    am = _atten_mask(r, (B, N1, S, S), 0.5)
+    scale = 0.37
+
+    def loss():
+        o, _ = oracle.bsa_fwd(a["q"], a["k"], a["v"], mask, bq, bkv, scale, mode, atten_mask=am)
+        return float(np.nansum(do * o))
+
+    o, _ = oracle.bsa_fwd(a["q"], a["k"], a["v"], mask, bq, bkv, scale, mode, atten_mask=am)
+    g = oracle.bsa_bwd(a["q"], a["k"], a["v"], o, do, mask, bq, bkv, scale, mode, atten_mask=am)
+    _fd_check(loss, a, ["q", "k", "v"], list(g))
+
+
+def test_bsa_tnd_atten_mask_equal_lengths_equals_bnsd():
+    """TND with equal lengths and a per-(b, n1) atten_mask is the BNSD
+    problem: element positions count from each sequence's start."""
+    r = _rng(26)
+    B, N1, N2, S, D, bq, bkv = 3, 2, 1, 16, 8, 8, 4
+    q = r.standard_normal((B, N1, S, D))
+    k = r.standard_normal((B, N2, S, D))
+    v = r.standard_normal((B, N2, S, D))
+    do = r.standard_normal((B, N1, S, D))
+    mask = W.mask_random(r, B, N1, 2, 4, 0.6)
+    am = _atten_mask(r, (B, N1, S, S))
+    cu = np.arange(B + 1) * S
+    tnd = lambda x: x.transpose(0, 2, 1, 3).reshape(B * S, x.shape[1], D)  # noqa: E731
+    o, l = oracle.bsa_fwd(q, k, v, mask, bq, bkv, 0.4, 0, atten_mask=am)
+    ot, lt = oracle.bsa_fwd_tnd(tnd(q), tnd(k), tnd(v), mask, cu, cu, bq, bkv, 0.4, 0,
+                                atten_mask=am)
+    assert np.array_equal(tnd(o), ot) and np.array_equal(l.transpose(0, 2, 1).reshape(B * S, N1), lt)
+    g = oracle.bsa_bwd(q, k, v, o, do, mask, bq, bkv, 0.4, 0, atten_mask=am)
+    gt = oracle.bsa_bwd_tnd(tnd(q), tnd(k), tnd(v), ot, tnd(do), mask, cu, cu, bq, bkv, 0.4, 0,
+                            atten_mask=am)
+    for a_, b_ in zip(g, gt):
+        assert np.array_equal(tnd(a_), b_)
+
+
+# ----------------------------------------------------------------------------
 # Finite differences of L = sum(dO * O)
 # ----------------------------------------------------------------------------
 
