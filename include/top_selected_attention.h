@@ -106,6 +106,17 @@ TSA_API size_t tsa_args_sizeof(int which);
  *   a ragged Sq / Skv are partial.
  * sparse_mode: 0 = the selected blocks in full; 2 = additionally causal,
  *   key position j <= query position i (top-left aligned).
+ * atten_mask (optional; the formula's Mask operand, whose format the page
+ *   does not give): u8 DEVICE, element (b, n1, i, j) at
+ *   atten_mask[b*atten_mask_stride_b + n1*atten_mask_stride_n + i*Skv + j]
+ *   for query position i < Sq and key position j < Skv (within the sequence
+ *   for TND); non-zero = that score is excluded, zero = kept.  Strides are in
+ *   elements, >= 0 (0 = one plane shared by every batch entry / head), else
+ *   TSA_ERR_INVALID; the caller guarantees every addressed element is in its
+ *   allocation.  It only excludes entries of the selected blocks and adds to
+ *   the causal exclusions of sparse_mode 2; a row left with no key gets
+ *   Out = 0 and LSE = -inf.  NULL = no element mask (strides ignored).
+ * scale: finite and > 0.
  * block_q, block_kv: 1..65536 (any size; partial tiles are masked).
  * A Q block that selects nothing gets Out = 0 and LSE = -inf.
  * ------------------------------------------------------------------------ */
@@ -116,7 +127,7 @@ typedef struct {
   int32_t B, N1, N2, Sq, Skv, D;
   int32_t block_q, block_kv;
   int32_t sparse_mode;      /* 0 or 2 */
-  float scale;              /* typically 1/sqrt(D) */
+  float scale;              /* > 0, typically 1/sqrt(D) */
   int32_t validate;         /* reserved for BSA (masks cannot hold bad data); 0 */
   const uint8_t* block_mask;/* DEVICE */
   const void* q;            /* DEVICE */
@@ -133,6 +144,9 @@ typedef struct {
                                recorded on `stream` before / after stage i (see each entry) */
   const int32_t* cu_seqlens_q;  /* TND only: HOST [B+1] (ignored for BNSD) */
   const int32_t* cu_seqlens_kv; /* TND only: HOST [B+1] */
+  const uint8_t* atten_mask;    /* DEVICE or NULL: element exclusions (see above) */
+  int64_t atten_mask_stride_b;  /* elements between batch entries' [Sq, Skv] planes; 0 = shared */
+  int64_t atten_mask_stride_n;  /* elements between query heads' planes; 0 = shared */
 } bsa_fwd_args;
 
 TSA_API int bsa_fwd_workspace_size(const bsa_fwd_args* args, size_t* bytes);
@@ -175,6 +189,9 @@ typedef struct {
                                recorded on `stream` before / after stage i (see each entry) */
   const int32_t* cu_seqlens_q;  /* TND only: HOST [B+1] (ignored for BNSD) */
   const int32_t* cu_seqlens_kv; /* TND only: HOST [B+1] */
+  const uint8_t* atten_mask;    /* DEVICE or NULL: the forward's atten_mask */
+  int64_t atten_mask_stride_b;
+  int64_t atten_mask_stride_n;
 } bsa_bwd_args;
 
 TSA_API int bsa_bwd_workspace_size(const bsa_bwd_args* args, size_t* bytes);
@@ -231,7 +248,7 @@ typedef struct {
   const int32_t* cu_seqlens_kv;  /* HOST [B+1] */
   int32_t sbs, sbc;
   int32_t sparse_mode;      /* 0 or 2 */
-  float scale;
+  float scale;              /* finite, > 0 */
   int32_t validate;
   const int32_t* topk;      /* DEVICE [T, N2, sbc] */
   const void* q;            /* DEVICE */
@@ -339,7 +356,7 @@ typedef struct {
   int32_t topk;
   int32_t sparse_block_size;
   int32_t sparse_mode;      /* 0 or 3 */
-  float scale;
+  float scale;              /* finite, > 0 */
   int32_t validate;
   const void* q;            /* DEVICE */
   const void* q_rope;       /* DEVICE */

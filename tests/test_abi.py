@@ -68,6 +68,13 @@ def _size(tsa, fn, args):
     (dict(q=0), 1),
     (dict(block_mask=0), 1),
     (dict(scale=float("nan")), 2),
+    (dict(scale=0.0), 2),                  # scale must be positive
+    (dict(scale=-0.1), 2),
+    (dict(atten_mask=8), 0),               # atten_mask with shared planes
+    (dict(atten_mask=8, atten_mask_stride_b=900000, atten_mask_stride_n=0), 0),
+    (dict(atten_mask=8, atten_mask_stride_b=-1), 2),   # strides must be >= 0
+    (dict(atten_mask=8, atten_mask_stride_n=-900000), 2),
+    (dict(atten_mask=0, atten_mask_stride_n=-1), 0),    # no mask: strides ignored
     (dict(Sq=0), 0),                       # empty query: valid
     (dict(reuse_lists=1), 0),
     (dict(reuse_lists=2), 2),              # BSA has no partial-reuse mode
@@ -120,6 +127,10 @@ def test_bsa_bwd_validation(tsa):
     a = tsa._abi.BsaBwdArgs(dtype=0, q_layout=0, kv_layout=0, B=1, N1=2, N2=2, Sq=256, Skv=256,
                             D=128, block_q=128, block_kv=128, sparse_mode=2, scale=0.1,
                             block_mask=8, q=8, k=8, v=8, out=8, dout=8, lse=8, dq=8, dk=8, dv=8)
+    assert _size(tsa, tsa.lib.bsa_bwd_workspace_size, a)[0] == 0
+    a.atten_mask, a.atten_mask_stride_b = 8, -5
+    assert _size(tsa, tsa.lib.bsa_bwd_workspace_size, a)[0] == 2
+    a.atten_mask_stride_b = 0
     assert _size(tsa, tsa.lib.bsa_bwd_workspace_size, a)[0] == 0
     a.dk = 0
     assert _size(tsa, tsa.lib.bsa_bwd_workspace_size, a)[0] == 1

@@ -82,12 +82,14 @@ class BsaPlan:
     cu_seqlens_q / cu_seqlens_kv are given as host B+1 prefix sums):
     q [T, N1, 128], k/v [Tk, N2, 128], with Sq / Skv the longest sequences.
     bf16 or fp16; block_mask u8 [B, N1, ceil(Sq/block_q), ceil(Skv/block_kv)].
-    ``fwd()`` writes ``self.out`` / ``self.lse`` (LSE [B, N1, Sq] or
+    atten_mask (optional): u8 or bool, [Sq, Skv] or [B|1, N1|1, Sq, Skv]
+    (size-1 or stride-0 axes shared), rows contiguous; non-zero / True = that
+    score is excluded.  ``fwd()`` writes ``self.out`` / ``self.lse`` (LSE [B, N1, Sq] or
     [T, N1]); ``bwd(dout)`` writes ``self.dq`` / ``self.dk`` / ``self.dv``.
     """
 
     def __init__(self, q, k, v, block_mask, block_q, block_kv, scale=None, sparse_mode=0,
-                 backward=True, cu_seqlens_q=None, cu_seqlens_kv=None):
+                 backward=True, cu_seqlens_q=None, cu_seqlens_kv=None, atten_mask=None):
         _check(q, "q"), _check(k, "k", q.dtype), _check(v, "v", q.dtype)
         tnd = cu_seqlens_q is not None or cu_seqlens_kv is not None
         if tnd:
@@ -118,6 +120,8 @@ class BsaPlan:
             lse_shape, layout, seq = (B, N1, Sq), LAYOUT_BNSD, {}
         QB, KB = _ceil(Sq, block_q), _ceil(Skv, block_kv)
         _check(block_mask, "block_mask", torch.uint8, (B, N1, QB, KB))
+        seq.update(_atten_mask_fields(atten_mask, B, N1, Sq, Skv))
+        self.atten_mask = atten_mask
         self.q, self.k, self.v, self.mask = q, k, v, block_mask
         self.scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
         dev = q.device
@@ -186,19 +190,40 @@ class BsaPlan:
         return self.dq, self.dk, self.dv
 
 
+def _atten_mask_fields(am, B, N1, Sq, Skv):
+    """Pointer and plane strides of an atten_mask tensor (see BsaPlan)."""
+    if am is None:
+        return {}
+    if not isinstance(am, torch.Tensor) or not am.is_cuda:
+        raise ValueError("atten_mask must be a device tensor")
+    if am.dtype not in (torch.uint8, torch.bool):
+        raise TypeError(f"atten_mask must be uint8 or bool, got {am.dtype}")
+    if am.dim() == 2:
+        am = am[None, None]
+    if am.dim() != 4 or tuple(am.shape[2:]) != (Sq, Skv) or am.shape[0] not in (1, B) \
+            or am.shape[1] not in (1, N1):
+        raise ValueError(f"atten_mask must be [Sq, Skv] or [B|1, N1|1, Sq, Skv] with "
+                         f"Sq={Sq}, Skv={Skv}, got {tuple(am.shape)}")
+    if Sq * Skv > 0 and ((Skv > 1 and am.stride(3) != 1) or (Sq > 1 and am.stride(2) != Skv)):
+        raise ValueError("atten_mask rows must be contiguous, Skv elements apart")
+    sb = am.stride(0) if am.shape[0] > 1 else 0
+    sn = am.stride(1) if am.shape[1] > 1 else 0
+    return dict(atten_mask=am.data_ptr(), atten_mask_stride_b=sb, atten_mask_stride_n=sn)
+
+
 def bsa_fwd(q, k, v, block_mask, block_q, block_kv, scale=None, sparse_mode=0,
-            cu_seqlens_q=None, cu_seqlens_kv=None):
+            cu_seqlens_q=None, cu_seqlens_kv=None, atten_mask=None):
     """Block-sparse attention forward (BNSD, or TND with cu_seqlens): returns (out, lse)."""
     plan = BsaPlan(q, k, v, block_mask, block_q, block_kv, scale, sparse_mode, backward=False,
-                   cu_seqlens_q=cu_seqlens_q, cu_seqlens_kv=cu_seqlens_kv)
+                   cu_seqlens_q=cu_seqlens_q, cu_seqlens_kv=cu_seqlens_kv, atten_mask=atten_mask)
     return plan.fwd()
 
 
 def bsa_bwd(q, k, v, out, dout, lse, block_mask, block_q, block_kv, scale=None, sparse_mode=0,
-            cu_seqlens_q=None, cu_seqlens_kv=None):
+            cu_seqlens_q=None, cu_seqlens_kv=None, atten_mask=None):
     """Block-sparse attention backward (BNSD, or TND with cu_seqlens): returns (dq, dk, dv)."""
     plan = BsaPlan(q, k, v, block_mask, block_q, block_kv, scale, sparse_mode, backward=True,
-                   cu_seqlens_q=cu_seqlens_q, cu_seqlens_kv=cu_seqlens_kv)
+                   cu_seqlens_q=cu_seqlens_q, cu_seqlens_kv=cu_seqlens_kv, atten_mask=atten_mask)
     plan.set_out(out, lse)
     return plan.bwd(dout)
 

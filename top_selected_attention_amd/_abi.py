@@ -1,7 +1,7 @@
 """ctypes mirror of include/top_selected_attention.h (structs, codes, signatures)."""
 
 import ctypes
-from ctypes import POINTER, c_float, c_int, c_int32, c_size_t, c_void_p, c_char_p
+from ctypes import POINTER, c_float, c_int, c_int32, c_int64, c_size_t, c_void_p, c_char_p
 
 BF16, FP16 = 0, 1
 LAYOUT_BNSD, LAYOUT_TND, LAYOUT_BSND = 0, 1, 2
@@ -39,7 +39,9 @@ class BsaFwdArgs(ctypes.Structure):
         ("scale", c_float), ("validate", c_int32),
         ("block_mask", c_void_p), ("q", c_void_p), ("k", c_void_p), ("v", c_void_p),
         ("out", c_void_p), ("lse", c_void_p),
-    ] + TRAIL + [("cu_seqlens_q", POINTER(c_int32)), ("cu_seqlens_kv", POINTER(c_int32))]
+    ] + TRAIL + [("cu_seqlens_q", POINTER(c_int32)), ("cu_seqlens_kv", POINTER(c_int32)),
+                 ("atten_mask", c_void_p), ("atten_mask_stride_b", c_int64),
+                 ("atten_mask_stride_n", c_int64)]
 
 
 class BsaBwdArgs(ctypes.Structure):
@@ -51,7 +53,9 @@ class BsaBwdArgs(ctypes.Structure):
         ("block_mask", c_void_p), ("q", c_void_p), ("k", c_void_p), ("v", c_void_p),
         ("out", c_void_p), ("dout", c_void_p), ("lse", c_void_p),
         ("dq", c_void_p), ("dk", c_void_p), ("dv", c_void_p),
-    ] + TRAIL + [("cu_seqlens_q", POINTER(c_int32)), ("cu_seqlens_kv", POINTER(c_int32))]
+    ] + TRAIL + [("cu_seqlens_q", POINTER(c_int32)), ("cu_seqlens_kv", POINTER(c_int32)),
+                 ("atten_mask", c_void_p), ("atten_mask_stride_b", c_int64),
+                 ("atten_mask_stride_n", c_int64)]
 
 
 _NSA_COMMON = [

@@ -77,7 +77,8 @@ int check_bsa_common(int dtype, int ql, int kl, int B, int N1, int N2, int Sq, i
   if (D != 128) return TSA_ERR_INVALID;
   if (bq < 1 || bkv < 1 || bq > 65536 || bkv > 65536) return TSA_ERR_INVALID;
   if (mode != 0 && mode != 2) return TSA_ERR_INVALID;
-  if (!std::isfinite(scale)) return TSA_ERR_INVALID;
+  // a positive scale: the kernels take the row max of the unscaled scores
+  if (!std::isfinite(scale) || !(scale > 0.f)) return TSA_ERR_INVALID;
   const long QB = cdiv(Sq, bq), KB = cdiv(Skv, bkv);
   if (!fits_i32((long)B * N1 * QB * KB) || !fits_i32((long)B * N1 * QB + 1)) return TSA_ERR_INVALID;
   if (!fits_i32(QB * bq) || !fits_i32(KB * bkv)) return TSA_ERR_INVALID;
@@ -167,6 +168,8 @@ int check_bsa_fwd(const bsa_fwd_args* a) {
   if (s) return s;
   s = check_bsa_tnd(a);
   if (s) return s;
+  if (a->atten_mask && (a->atten_mask_stride_b < 0 || a->atten_mask_stride_n < 0))
+    return TSA_ERR_INVALID;
   const bool empty = bsa_q_rows(a) == 0;
   if (!empty && (!a->q || !a->out || !a->lse || !a->block_mask)) return TSA_ERR_NULL;
   if (!empty && bsa_kv_rows(a) > 0 && (!a->k || !a->v)) return TSA_ERR_NULL;
@@ -181,6 +184,8 @@ int check_bsa_bwd(const bsa_bwd_args* a) {
   if (s) return s;
   s = check_bsa_tnd(a);
   if (s) return s;
+  if (a->atten_mask && (a->atten_mask_stride_b < 0 || a->atten_mask_stride_n < 0))
+    return TSA_ERR_INVALID;
   const bool empty_q = bsa_q_rows(a) == 0, empty_k = bsa_kv_rows(a) == 0;
   if (!empty_q && (!a->q || !a->out || !a->dout || !a->lse || !a->dq || !a->block_mask))
     return TSA_ERR_NULL;
@@ -219,6 +224,18 @@ hipError_t bsa_upload_seqlens(const A* a, const BsaWs& w, BsaParams* p, hipStrea
   return e;
 }
 
+// atten_mask fields of the kernel parameters.
+template <class A>
+void bsa_set_atten_mask(const A* a, BsaParams* p) {
+  p->am = a->atten_mask;
+  if (!p->am) return;
+  p->am_sb = (long)a->atten_mask_stride_b;
+  p->am_sn = (long)a->atten_mask_stride_n;
+  p->am_pitch = a->Skv;
+  p->am_al4 = (((uintptr_t)p->am | (uintptr_t)p->am_sb | (uintptr_t)p->am_sn |
+                (uintptr_t)a->Skv | (uintptr_t)a->block_kv) & 3) == 0;
+}
+
 BsaParams bsa_params(int B, int N1, int N2, int Sq, int Skv, int bq, int bkv, int mode,
                      float scale) {
   BsaParams p;
@@ -255,7 +272,7 @@ int check_nsa(const A* a) {
   if (a->sbc < 1 || a->sbc > 128 || a->sbs * a->sbc > 8192) return TSA_ERR_INVALID;
   // constraints: sparseMode 0 or 2.
   if (a->sparse_mode != 0 && a->sparse_mode != 2) return TSA_ERR_INVALID;
-  if (!std::isfinite(a->scale)) return TSA_ERR_INVALID;
+  if (!std::isfinite(a->scale) || !(a->scale > 0.f)) return TSA_ERR_INVALID;
   if (!a->cu_seqlens_q || !a->cu_seqlens_kv) return TSA_ERR_NULL;
   const int32_t* cq = a->cu_seqlens_q;
   const int32_t* ck = a->cu_seqlens_kv;
@@ -422,7 +439,7 @@ int check_sfa(const sfa_paged_fwd_args* a) {
   if (a->sparse_block_size < 1 || a->page_size % a->sparse_block_size != 0) return TSA_ERR_INVALID;
   if (a->sparse_mode != 0 && a->sparse_mode != 3) return TSA_ERR_INVALID;
   if (a->topk < 1 || a->max_pages < 1 || a->num_pages < 1) return TSA_ERR_INVALID;
-  if (!std::isfinite(a->scale)) return TSA_ERR_INVALID;
+  if (!std::isfinite(a->scale) || !(a->scale > 0.f)) return TSA_ERR_INVALID;
   if (!fits_i32((long)a->num_pages * a->page_size) || !fits_i32((long)a->B * a->max_pages))
     return TSA_ERR_INVALID;
   if ((long)a->B * a->Sq > 0 &&
@@ -566,6 +583,7 @@ int bsa_fwd(const bsa_fwd_args* a, void* ws, size_t ws_bytes, void* stream) {
   if (e != hipSuccess) return TSA_ERR_HIP;
   p.q = a->q; p.k = a->k; p.v = a->v; p.out = a->out; p.lse = a->lse;
   p.row_ptr = w.row_ptr; p.col = w.col; p.order_q = w.order_q;
+  bsa_set_atten_mask(a, &p);
   e = tm.mark(1, 0);
   if (e == hipSuccess) e = launch_bsa_fwd(p, a->dtype == TSA_FP16, st);
   if (e == hipSuccess) e = tm.mark(1, 1);
@@ -613,6 +631,7 @@ int bsa_bwd(const bsa_bwd_args* a, void* ws, size_t ws_bytes, void* stream) {
   p.row_ptr = w.row_ptr; p.col = w.col; p.rev_ptr = w.rev_ptr; p.rev = w.rev;
   p.order_q = w.order_q; p.order_kv = w.order_kv;
   p.seg_off = w.seg_off; p.part_off = w.part_off; p.seg_meta = w.seg_meta; p.part = w.part;
+  bsa_set_atten_mask(a, &p);
   return hip_status(launch_bsa_bwd(p, a->dtype == TSA_FP16, st, tm.ev, tm.n));
 }
 

@@ -36,7 +36,8 @@ constexpr int kTileB = 64 * kD * 2;  // one 64-row chunk of a [rows][128] 16-bit
 // chunk it forms S^T = K Q^T and dP^T = V dO^T, dS^T = P^T (dP^T - D), and
 // accumulates dQ^T += K^T dS^T.
 // ---------------------------------------------------------------------------
-template <class E, int NW>
+// AM (both kernels): an element mask (atten_mask) is given.
+template <class E, int NW, bool AM>
 __global__ __launch_bounds__(NW * 64) void bsa_dq_kernel(BsaParams p, int qsub, int n_items) {
   typedef typename E::T T;
   typedef typename E::V8 V8;
@@ -95,6 +96,9 @@ __global__ __launch_bounds__(NW * 64) void bsa_dq_kernel(BsaParams p, int qsub, 
     if (row_ok && h == 0) p.delta[sm.at(n1, qrow)] = acc;
   }
 
+  const unsigned char* amrow = nullptr;
+  if constexpr (AM) amrow = p.am + b * p.am_sb + n1 * p.am_sn + (long)qrow * p.am_pitch;
+
   const int e0 = p.row_ptr[bn * p.QB + qb], e1 = p.row_ptr[bn * p.QB + qb + 1];
   ListWindow colw(p.col, e0, e1);
   const int cpb = (p.bkv + 63) / 64;
@@ -146,7 +150,11 @@ __global__ __launch_bounds__(NW * 64) void bsa_dq_kernel(BsaParams p, int qsub, 
     }
     const char* Kb = lds_k[buf];
     const char* Vb = lds_v[buf];
-    const bool full = (ke - ks == 64) && wrow0 + 32 <= row_hi && (!p.causal || ke - 1 <= wrow0);
+    const bool full =
+        !AM && (ke - ks == 64) && wrow0 + 32 <= row_hi && (!p.causal || ke - 1 <= wrow0);
+    // atten_mask keep bits of this lane's row: bit 16*kt + j for element j of tile kt
+    uint32_t keep = 0xffffffffu;
+    if constexpr (AM) keep = row_ok ? am_keep_row(amrow + ks, ke - ks, h, p.am_al4) : 0u;
 #pragma unroll
     for (int kt = 0; kt < 2; kt++) {
       f32x16 st, dpt;
@@ -176,7 +184,9 @@ __global__ __launch_bounds__(NW * 64) void bsa_dq_kernel(BsaParams p, int qsub, 
 #pragma unroll
         for (int j = 0; j < 16; j++) {
           float pv = fast_exp2(__builtin_fmaf(st[j], sl2, lneg));
-          if (masked) pv = (kt * 32 + 8 * (j >> 2) + (j & 3)) <= lim ? pv : 0.f;
+          if (masked)
+            pv = ((kt * 32 + 8 * (j >> 2) + (j & 3)) <= lim && ((keep >> (16 * kt + j)) & 1u))
+                     ? pv : 0.f;
           bs[j >> 3][j & 7] = E::from_f32(pv * (dpt[j] - dlt));
         }
       };
@@ -225,7 +235,7 @@ __global__ __launch_bounds__(NW * 64) void bsa_dq_kernel(BsaParams p, int qsub, 
 // ---------------------------------------------------------------------------
 // Two waves per SIMD (register budget 256; a few spills are cheaper than
 // running one wave per SIMD).
-template <class E, int NW>
+template <class E, int NW, bool AM>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void bsa_dkdv_kernel(BsaParams p, int ksub, int n_items) {
   typedef typename E::T T;
   typedef typename E::V8 V8;
@@ -401,7 +411,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     __builtin_amdgcn_s_setprio(0);
     // a chunk whose every query row is valid and at or after every key of
     // this wave needs no mask
-    const bool full = (qe - qs == kQC) && wkey0 + 32 <= key_hi && (!p.causal || qs >= wkey0 + 31);
+    const bool full =
+        !AM && (qe - qs == kQC) && wkey0 + 32 <= key_hi && (!p.causal || qs >= wkey0 + 31);
+    // atten_mask keep bits of this lane's key column: bit j for element j
+    uint32_t keep = 0xffffffffu;
+    if constexpr (AM) {
+      const int key = wkey0 + l32i;
+      keep = key < key_hi ? am_keep_col(p.am + b * p.am_sb + n1 * p.am_sn + (long)qs * p.am_pitch +
+                                            key, p.am_pitch, qe - qs, hi)
+                          : 0u;
+    }
     // element j of a lane is query 8*(j/4) + 4*h + j%4 of the chunk, column key l32
     V8 bp[2], bd[2];
     auto form = [&](auto masked) {
@@ -423,7 +442,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
           float pr = fast_exp2(__builtin_fmaf(s[j], sl2, -lv[jj] * kLog2e));
           if (masked) {
             const int off = 8 * j4 + jj;
-            pr = (off >= lo && off <= up) ? pr : 0.f;
+            pr = (off >= lo && off <= up && ((keep >> j) & 1u)) ? pr : 0.f;
           }
           bp[j >> 3][j & 7] = E::from_f32(pr);
           bd[j >> 3][j & 7] = E::from_f32(pr * (dp[j] - dv[jj]));
@@ -522,8 +541,12 @@ static hipError_t launch_dq_t(const BsaParams& p, hipStream_t st) {
   const int qsub = (p.bq + NW * 32 - 1) / (NW * 32);
   const int n_items = p.B * p.N1 * p.QB * qsub;
   if (n_items == 0) return hipSuccess;
-  hipLaunchKernelGGL((bsa_dq_kernel<E, NW>), dim3(8 * ((n_items + 7) / 8)), dim3(NW * 64), 0, st,
-                     p, qsub, n_items);
+  if (p.am)
+    hipLaunchKernelGGL((bsa_dq_kernel<E, NW, true>), dim3(8 * ((n_items + 7) / 8)), dim3(NW * 64),
+                       0, st, p, qsub, n_items);
+  else
+    hipLaunchKernelGGL((bsa_dq_kernel<E, NW, false>), dim3(8 * ((n_items + 7) / 8)), dim3(NW * 64),
+                       0, st, p, qsub, n_items);
   return hipGetLastError();
 }
 
@@ -534,8 +557,12 @@ static hipError_t launch_dkdv_t(const BsaParams& p, hipStream_t st) {
   if (n_items == 0) return hipSuccess;
   // the segment plan was made with the lists (launch_tile_order); at most
   // n_items + kBsaMaxParts segments, the surplus workgroups exit
-  hipLaunchKernelGGL((bsa_dkdv_kernel<E, NW>), dim3(n_items + kBsaMaxParts), dim3(NW * 64), 0,
-                     st, p, ksub, n_items);
+  if (p.am)
+    hipLaunchKernelGGL((bsa_dkdv_kernel<E, NW, true>), dim3(n_items + kBsaMaxParts), dim3(NW * 64),
+                       0, st, p, ksub, n_items);
+  else
+    hipLaunchKernelGGL((bsa_dkdv_kernel<E, NW, false>), dim3(n_items + kBsaMaxParts),
+                       dim3(NW * 64), 0, st, p, ksub, n_items);
   hipLaunchKernelGGL((bsa_dkdv_reduce<E, NW>), dim3(n_items), dim3(256), 0, st, p, ksub, n_items);
   return hipGetLastError();
 }

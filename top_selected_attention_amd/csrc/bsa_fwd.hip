@@ -1,6 +1,6 @@
 // Block-sparse attention forward ("aclnnBlockSparseAttentionGrad", formula
-// section): Out = Softmax(Mask(scale * Q K_sparse^T)) V_sparse, plus the
-// natural-log LSE of each row.
+// section): Out = Softmax(Mask(scale * Q K_sparse^T, atten_mask)) V_sparse,
+// plus the natural-log LSE of each row.
 //
 // One workgroup per (b, n1, Q block) slice of up to 128 query rows; each wave
 // owns 32 query rows.  The Q block's selected KV blocks are walked in 64-key
@@ -24,7 +24,8 @@ constexpr int kD = 128;        // head dim (the page's constraint: headdim = 128
 constexpr int kKC = 64;        // keys per chunk
 constexpr int kTileB = kKC * kD * 2;  // bytes per staged K or V chunk
 
-template <class E, int NW>
+// AM: an element mask (atten_mask) is given; its entries are read per chunk.
+template <class E, int NW, bool AM>
 __global__ __launch_bounds__(NW * 64) void bsa_fwd_kernel(BsaParams p, int qsub, int n_items) {
   typedef typename E::T T;
   typedef typename E::V8 V8;
@@ -69,6 +70,10 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_kernel(BsaParams p, int qsub,
   for (int ds = 0; ds < 8; ds++)
     qreg[ds] = qrow < row_hi ? as_v8<V8>(ld16(qh + (long)qrow * qm.row + ds * 16 + 8 * h))
                              : zero_v8<V8>();
+
+  // this lane's atten_mask row (positions within the sequence)
+  const unsigned char* amrow = nullptr;
+  if constexpr (AM) amrow = p.am + b * p.am_sb + n1 * p.am_sn + (long)qrow * p.am_pitch;
 
   const int tile_row = bn * p.QB + qb;
   const int e0 = p.row_ptr[tile_row], e1 = p.row_ptr[tile_row + 1];
@@ -149,16 +154,20 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_kernel(BsaParams p, int qsub,
     // wholly inside [0, ke) and at or below every row of this wave needs no
     // mask; otherwise key offsets above this lane's limit are masked (the
     // offset without the lane's 4*h is a compile-time constant per element).
-    const bool full = (ke - ks == kKC) && (!p.causal || ke - 1 <= wrow0);
+    // An atten_mask clears element j of tile kt where keep bit 16*kt + j is 0.
+    const bool full = !AM && (ke - ks == kKC) && (!p.causal || ke - 1 <= wrow0);
     if (!full) {
       int lim = ke - 1 - ks;
       if (p.causal) lim = min(lim, qrow - ks);
       lim -= 4 * h;
+      uint32_t keep = 0xffffffffu;
+      if constexpr (AM) keep = qrow < row_hi ? am_keep_row(amrow + ks, ke - ks, h, p.am_al4) : 0u;
 #pragma unroll
       for (int kt = 0; kt < 2; kt++)
 #pragma unroll
         for (int j = 0; j < 16; j++)
-          st[kt][j] = (kt * 32 + 8 * (j >> 2) + (j & 3)) <= lim ? st[kt][j] : -INFINITY;
+          st[kt][j] = ((kt * 32 + 8 * (j >> 2) + (j & 3)) <= lim && ((keep >> (16 * kt + j)) & 1u))
+                          ? st[kt][j] : -INFINITY;
     }
     float mx = fmaxf(st[0][0], st[1][0]);
 #pragma unroll
@@ -222,7 +231,12 @@ static hipError_t launch_fwd_t(const BsaParams& p, hipStream_t st) {
   const int qsub = (p.bq + NW * 32 - 1) / (NW * 32);
   const int n_items = p.B * p.N1 * p.QB * qsub;
   const int grid = 8 * ((n_items + 7) / 8);
-  hipLaunchKernelGGL((bsa_fwd_kernel<E, NW>), dim3(grid), dim3(NW * 64), 0, st, p, qsub, n_items);
+  if (p.am)
+    hipLaunchKernelGGL((bsa_fwd_kernel<E, NW, true>), dim3(grid), dim3(NW * 64), 0, st, p, qsub,
+                       n_items);
+  else
+    hipLaunchKernelGGL((bsa_fwd_kernel<E, NW, false>), dim3(grid), dim3(NW * 64), 0, st, p, qsub,
+                       n_items);
   return hipGetLastError();
 }
 

@@ -330,4 +330,50 @@ __device__ __forceinline__ int xcd_remap(int w, int n_items, int n_xcd = 8) {
   return item < n_items ? item : -1;
 }
 
+// ---------------------------------------------------------------------------
+// Element masks (u8, non-zero = excluded) inside a 64-key chunk.
+// ---------------------------------------------------------------------------
+
+// Keep bits of one query row over the keys a lane holds in a 64-key chunk
+// when keys run along the accumulator's rows: bit 4*c + i stands for key
+// offset 8*c + 4*h + i (c = 0..7, i = 0..3) and is set when that entry is
+// zero.  `row` points at the chunk's first key in the mask row; offsets at or
+// past n are not read and come out cleared.  al4: row and chunk starts are
+// 4-byte aligned and rows end on a 4-byte boundary, so four keys load as
+// one dword that stays inside the row.
+__device__ __forceinline__ uint32_t am_keep_row(const unsigned char* row, int n, int h, int al4) {
+  uint32_t keep = 0;
+#pragma unroll
+  for (int c = 0; c < 8; c++) {
+    const int o = 8 * c + 4 * h;
+    if (o >= n) continue;
+    uint32_t w = 0;
+    if (al4) {
+      w = *reinterpret_cast<const uint32_t*>(row + o);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; i++) w |= (uint32_t)(o + i < n ? row[o + i] : 1) << (8 * i);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+      keep |= (uint32_t)(((w >> (8 * i)) & 0xffu) == 0 && o + i < n) << (4 * c + i);
+  }
+  return keep;
+}
+
+// Keep bits of one key column over the 16 queries a lane holds in a 32-query
+// chunk when queries run along the accumulator's rows: bit j stands for
+// query offset 8*(j/4) + 4*h + j%4.  `col` points at the chunk's first query
+// row in the key's column; rows are `pitch` bytes apart; offsets at or past n
+// are not read and come out cleared.
+__device__ __forceinline__ uint32_t am_keep_col(const unsigned char* col, long pitch, int n, int h) {
+  uint32_t keep = 0;
+#pragma unroll
+  for (int j = 0; j < 16; j++) {
+    const int o = 8 * (j >> 2) + 4 * h + (j & 3);
+    if (o < n && col[(long)o * pitch] == 0) keep |= 1u << j;
+  }
+  return keep;
+}
+
 }  // namespace tsa

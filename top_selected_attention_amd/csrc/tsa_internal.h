@@ -88,6 +88,12 @@ struct BsaParams {
   int bq, bkv, QB, KB;
   int causal;
   float scale;
+  // atten_mask: element (b, n1, i, j) at am[b*am_sb + n1*am_sn + i*am_pitch + j],
+  // non-zero = excluded; null = none.  am_al4: every row start and every
+  // chunk start is 4-byte aligned, so 4 keys load as one dword.
+  const unsigned char* am;
+  long am_sb, am_sn;
+  int am_pitch, am_al4;
   // backward dK/dV segments (workspace): work item r (in order_kv order) has
   // seg_off[r+1] - seg_off[r] segments of at most seg_meta[0] reverse-list
   // entries; a split item's segments write fp32 partials from slot
