@@ -40,5 +40,6 @@ from .attention import (  # noqa: F401
     nsa_bwd,
     nsa_keys,
     sfa_fwd,
+    sfa_fwd_tnd,
 )
 from .compaction import bsa_compact, nsa_compact  # noqa: F401

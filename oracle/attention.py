@@ -374,6 +374,41 @@ def nsa_bwd(q, k, v, out, dout, topk, cu_seqlens_q, cu_seqlens_kv, sbs, scale,
 # Sparse flash attention over a paged (PA_ND) shared KV cache, inference.
 # --------------------------------------------------------------------------
 
+def _sfa_token(q_t, qr_t, topk_t, block_row, kv_len, qpos, key_cache, key_rope_cache,
+               value_cache, scale, sparse_mode, sparse_block_size):
+    """One decode token's selected-key attention, all query heads: q_t
+    [N1, D], qr_t [N1, Dr], topk_t [N2, K]; block_row the sequence's page
+    table row; qpos the token's position (rightDownCausal).  Returns (out
+    [N1, Dv], lse [N1])."""
+    page, N2 = key_cache.shape[1], key_cache.shape[2]
+    N1 = q_t.shape[0]
+    G = N1 // N2
+    out = np.zeros((N1, value_cache.shape[3]))
+    lse = np.zeros(N1)
+    for n2 in range(N2):
+        ids = np.asarray(topk_t[n2]).astype(np.int64)
+        ids = ids[ids >= 0]
+        if np.any(ids * sparse_block_size >= kv_len):
+            raise ValueError("selected id beyond kv_len")
+        pos = (ids[:, None] * sparse_block_size
+               + np.arange(sparse_block_size)[None, :]).reshape(-1)
+        pos = pos[pos < kv_len]
+        phys = np.asarray(block_row)[pos // page]
+        row = pos % page
+        keys = np.concatenate([_f64(key_cache[phys, row, n2]),
+                               _f64(key_rope_cache[phys, row, n2])], axis=1)
+        vals = _f64(value_cache[phys, row, n2])
+        heads = slice(n2 * G, (n2 + 1) * G)
+        qcat = np.concatenate([_f64(q_t[heads]), _f64(qr_t[heads])], axis=1)
+        allowed = np.ones((G, len(pos)), dtype=bool)
+        if sparse_mode == 3:
+            allowed &= (pos <= qpos)[None, :]
+        o, l, _ = attend_fwd(qcat, keys, vals, allowed, scale)
+        out[heads] = o
+        lse[heads] = l
+    return out, lse
+
+
 def sfa_fwd(q, q_rope, key_cache, key_rope_cache, value_cache, block_table, kv_lens,
             topk, scale, sparse_mode=3, sparse_block_size=1, tokens=None):
     """Sparse flash attention forward over selected tokens of a paged cache.
@@ -394,33 +429,41 @@ def sfa_fwd(q, q_rope, key_cache, key_rope_cache, value_cache, block_table, kv_l
     Returns (out [B, Sq, N1, Dv], lse [B, Sq, N1]).
     """
     B, Sq, N1, _ = q.shape
-    page, N2, Dv = key_cache.shape[1], key_cache.shape[2], value_cache.shape[3]
-    G = N1 // N2
+    Dv = value_cache.shape[3]
     out = np.full((B, Sq, N1, Dv), np.nan)
     lse = np.full((B, Sq, N1), np.nan)
     units = [(b, s) for b in range(B) for s in range(Sq)] if tokens is None else tokens
     for b, s in units:
         kv_len = int(kv_lens[b])
-        qpos = kv_len - Sq + s
-        for n2 in range(N2):
-            ids = np.asarray(topk[b, s, n2]).astype(np.int64)
-            ids = ids[ids >= 0]
-            if np.any(ids * sparse_block_size >= kv_len):
-                raise ValueError("selected id beyond kv_len")
-            pos = (ids[:, None] * sparse_block_size
-                   + np.arange(sparse_block_size)[None, :]).reshape(-1)
-            pos = pos[pos < kv_len]
-            phys = np.asarray(block_table[b])[pos // page]
-            row = pos % page
-            keys = np.concatenate([_f64(key_cache[phys, row, n2]),
-                                   _f64(key_rope_cache[phys, row, n2])], axis=1)
-            vals = _f64(value_cache[phys, row, n2])
-            heads = slice(n2 * G, (n2 + 1) * G)
-            qcat = np.concatenate([_f64(q[b, s, heads]), _f64(q_rope[b, s, heads])], axis=1)
-            allowed = np.ones((G, len(pos)), dtype=bool)
-            if sparse_mode == 3:
-                allowed &= (pos <= qpos)[None, :]
-            o, l, _ = attend_fwd(qcat, keys, vals, allowed, scale)
-            out[b, s, heads] = o
-            lse[b, s, heads] = l
+        out[b, s], lse[b, s] = _sfa_token(q[b, s], q_rope[b, s], topk[b, s], block_table[b],
+                                          kv_len, kv_len - Sq + s, key_cache, key_rope_cache,
+                                          value_cache, scale, sparse_mode, sparse_block_size)
+    return out, lse
+
+
+def sfa_fwd_tnd(q, q_rope, key_cache, key_rope_cache, value_cache, block_table, kv_lens,
+                topk, cu_seqlens_q, scale, sparse_mode=3, sparse_block_size=1, tokens=None):
+    """Sparse flash attention forward with TND queries.
+
+    "SparseAttnSharedkvMetadata", parameter list: layout_q may be TND, with
+    cu_seqlens_q the B+1 prefix sums of each batch entry's query tokens.
+    Sequence b's Sq_b = cu[b+1] - cu[b] decode tokens are rows cu[b] ..
+    cu[b+1]-1; under rightDownCausal its token s sits at kv_len - Sq_b + s.
+    q [T, N1, D], q_rope [T, N1, Dr], topk [T, N2, K]; caches, block_table and
+    kv_lens as in ``sfa_fwd``.  ``tokens``: optional list of global rows t.
+    Returns (out [T, N1, Dv], lse [T, N1]); rows not computed are NaN.
+    """
+    cu = np.asarray(cu_seqlens_q)
+    T, N1, _ = q.shape
+    Dv = value_cache.shape[3]
+    out = np.full((T, N1, Dv), np.nan)
+    lse = np.full((T, N1), np.nan)
+    rows = range(T) if tokens is None else tokens
+    for t in rows:
+        b = int(np.searchsorted(cu, t, side="right")) - 1
+        sq_b = int(cu[b + 1] - cu[b])
+        kv_len = int(kv_lens[b])
+        out[t], lse[t] = _sfa_token(q[t], q_rope[t], topk[t], block_table[b], kv_len,
+                                    kv_len - sq_b + (t - int(cu[b])), key_cache, key_rope_cache,
+                                    value_cache, scale, sparse_mode, sparse_block_size)
     return out, lse

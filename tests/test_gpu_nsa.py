@@ -203,3 +203,40 @@ def test_bwd_reusing_forward_lists_matches_fresh_lists():
     dq2, dk2, dv2 = plan.bwd(do.to(dev))          # no forward on this plan: builds all lists
     torch.cuda.synchronize()
     assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
+
+
+@pytest.mark.parametrize("seqlens,N1,N2,sbs,sbc", [
+    ([8192], 4, 2, 64, 128),          # the largest selection: sbs * sbc = 8K keys per token
+    ([2048, 2304], 8, 2, 16, 128),    # the most blocks (128) of the smallest size
+    ([2048, 4096], 4, 1, 128, 16),    # the largest block size with many blocks
+])
+def test_selection_size_limits_sampled(seqlens, N1, N2, sbs, sbc):
+    """Block size / count at the operator's limits (block size <= 128, count
+    <= 128, product <= 8K): out / LSE / dQ on sampled tokens, dK / dV on the
+    last two blocks of each sequence with every token that selected them."""
+    cu, q, k, v, do, topk = _case(seqlens, N1, N2, sbs, sbc, 110)
+    scale = 1 / math.sqrt(128)
+    out, lse, dq, dk, dv = _run(cu, q, k, v, do, topk, sbs, scale, 2)
+    T = int(cu[-1])
+    toks = sorted(set([0, 1, sbs - 1, sbs, T - 1] + [int(c) for c in cu[1:-1]] +
+                      list(range(37, T, 409))))
+    qn, kn, vn, don, on = _np(q), _np(k), _np(v), _np(do), _np(out)
+    ro, rl = oracle.nsa_fwd(qn, kn, vn, topk, cu, cu, sbs, scale, 2, tokens=toks)
+    _close(out, ro, OUT_TOL, "out", rows=toks)
+    _lse_close(lse, rl, rows=toks)
+    _, _, rvp, rv, nb = oracle.nsa_compact(topk, cu, cu, sbs, 2)
+    sel, rows = set(toks), np.zeros(T, bool)
+    first = 0                                   # global id of each sequence's first block
+    for b, n in enumerate(seqlens):
+        nblk = n // sbs
+        for blk in (nblk - 2, nblk - 1):
+            for n2 in range(N2):
+                r = n2 * nb + first + blk
+                sel.update(rv[rvp[r]:rvp[r + 1]].tolist())
+            rows[int(cu[b]) + blk * sbs:int(cu[b]) + (blk + 1) * sbs] = True
+        first += nblk
+    rdq, rdk, rdv = oracle.nsa_bwd(qn, kn, vn, on, don, topk, cu, cu, sbs, scale, 2,
+                                   tokens=sorted(sel))
+    _close(dq, rdq, GRAD_TOL, "dq", rows=toks)
+    _close(dk, rdk, GRAD_TOL, "dk", rows=rows)
+    _close(dv, rdv, GRAD_TOL, "dv", rows=rows)

@@ -118,6 +118,65 @@ def test_sfa_identity_pages_all_tokens_equals_dense_mqa():
         np.testing.assert_allclose(out[b], ref.numpy().transpose(1, 0, 2), atol=1e-12, rtol=0)
 
 
+def test_sfa_tnd_ragged_queries_equal_dense_mqa_per_sequence():
+    """TND queries (1, 3 and 2 decode tokens per sequence), every position
+    selected: each sequence is dense MQA with its own rightDownCausal offset
+    kv_len - Sq_b (torch, float64)."""
+    r = _rng(31)
+    lens, N1, D, Dr, page = [1, 3, 2], 4, 16, 8, 8
+    kv_lens = np.array([24, 16, 20])
+    B = len(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    T = int(cu[-1])
+    q, qr = r.standard_normal((T, N1, D)), r.standard_normal((T, N1, Dr))
+    pages = [-(-int(n) // page) for n in kv_lens]
+    P = sum(pages)
+    kc, krc = r.standard_normal((P, page, 1, D)), r.standard_normal((P, page, 1, Dr))
+    bt = np.zeros((B, max(pages)), np.int64)
+    perm = r.permutation(P)
+    off = 0
+    for b in range(B):
+        bt[b, :pages[b]] = perm[off:off + pages[b]]
+        off += pages[b]
+    K = int(kv_lens.max())
+    topk = np.full((T, 1, K), -1)
+    for b in range(B):
+        topk[cu[b]:cu[b + 1], 0, :kv_lens[b]] = np.arange(kv_lens[b])
+    scale = 1 / math.sqrt(D + Dr)
+    out, lse = oracle.sfa_fwd_tnd(q, qr, kc, krc, kc, bt, kv_lens, topk, cu, scale, 3)
+    for b in range(B):
+        n, sq = int(kv_lens[b]), lens[b]
+        keys = kc[bt[b, :pages[b]]].reshape(-1, D)[:n]
+        kro = krc[bt[b, :pages[b]]].reshape(-1, Dr)[:n]
+        sl = slice(cu[b], cu[b + 1])
+        qcat = torch.tensor(np.concatenate([q[sl], qr[sl]], -1)).transpose(0, 1)  # [N1, sq, .]
+        kcat = torch.tensor(np.concatenate([keys, kro], -1))[None].expand(N1, -1, -1)
+        vals = torch.tensor(keys)[None].expand(N1, -1, -1)
+        allowed = torch.arange(n)[None, :] <= (n - sq + torch.arange(sq))[:, None]
+        ref = torch.nn.functional.scaled_dot_product_attention(qcat, kcat, vals, attn_mask=allowed,
+                                                               scale=scale)
+        np.testing.assert_allclose(out[sl], ref.numpy().transpose(1, 0, 2), atol=1e-12, rtol=0)
+    assert np.all(np.isfinite(lse))
+
+
+def test_sfa_tnd_equal_lengths_equals_bsnd():
+    r = _rng(32)
+    B, Sq, N1, D, Dr, page, kv_len = 3, 2, 2, 8, 4, 4, 16
+    q, qr = r.standard_normal((B, Sq, N1, D)), r.standard_normal((B, Sq, N1, Dr))
+    P = B * kv_len // page
+    kc, krc = r.standard_normal((P, page, 1, D)), r.standard_normal((P, page, 1, Dr))
+    bt = r.permutation(P).reshape(B, kv_len // page)
+    kv_lens = np.array([16, 11, 14])
+    topk = np.stack([np.stack([np.sort(r.choice(kv_lens[b] - 1, 5, replace=False))
+                               for s in range(Sq)]) for b in range(B)])[:, :, None, :]
+    o, l = oracle.sfa_fwd(q, qr, kc, krc, kc, bt, kv_lens, topk, 0.3, 3)
+    cu = np.arange(B + 1) * Sq
+    ot, lt = oracle.sfa_fwd_tnd(q.reshape(B * Sq, N1, D), qr.reshape(B * Sq, N1, Dr), kc, krc,
+                                kc, bt, kv_lens, topk.reshape(B * Sq, 1, -1), cu, 0.3, 3)
+    assert np.array_equal(o.reshape(B * Sq, N1, D), ot)
+    assert np.array_equal(l.reshape(B * Sq, N1), lt)
+
+
 def test_sfa_page_table_permutation_is_invisible():
     """Moving pages around the physical cache (and the table with them) changes nothing."""
     r = _rng(4)
