@@ -330,7 +330,13 @@ TSA_API int nsa_compact(const nsa_select_fwd_args* args, int32_t* row_ptr, int32
  * head, PA_ND paged KV, seqused_kv = active KV length per batch, mask mode
  * 3 = rightDownCausal.
  *
- * q [B, Sq, N1, D], q_rope [B, Sq, N1, Dr] (BSND);
+ * q [B, Sq, N1, D], q_rope [B, Sq, N1, Dr] (BSND), or with q_layout TND
+ *   ("SparseAttnSharedkvMetadata": layout_q BSND or TND, cu_seqlens_q the
+ *   B+1 prefix sums of each entry's query tokens) q [T, N1, D], q_rope
+ *   [T, N1, Dr], rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 belonging to
+ *   entry b; Sq is then ignored and entry b's Sq_b = cu[b+1] - cu[b] sets
+ *   its causal offset; topk_indices [T, N2, topk], out [T, N1, Dv], lse
+ *   [T, N1].
  * key_cache [num_pages, page_size, N2, D], key_rope_cache [num_pages,
  *   page_size, N2, Dr], value_cache [num_pages, page_size, N2, Dv] (PA_ND);
  *   value_cache must equal key_cache (shared KV: V is the key row; a
@@ -342,7 +348,7 @@ TSA_API int nsa_compact(const nsa_select_fwd_args* args, int32_t* row_ptr, int32
  * sparse_block_size: divides page_size (reading of the constraint that ties
  *   it to block_size: a selected block never straddles a page); 1..page_size.
  * sparse_mode: 0 = no mask; 3 = rightDownCausal (token s of Sq sits at
- *   position kv_len - Sq + s; later keys are masked).
+ *   position kv_len - Sq + s, Sq_b for TND; later keys are masked).
  * out [B, Sq, N1, Dv]; lse fp32 [B, Sq, N1] (may be NULL).
  * validate = 1: checks ids, kv_lens and page ids on the device, synchronises
  *   `stream`, TSA_ERR_DATA on a bad value; with validate = 0 positions at or
@@ -350,7 +356,7 @@ TSA_API int nsa_compact(const nsa_select_fwd_args* args, int32_t* row_ptr, int32
  * ------------------------------------------------------------------------ */
 typedef struct {
   int32_t dtype;
-  int32_t q_layout;         /* TSA_LAYOUT_BSND */
+  int32_t q_layout;         /* TSA_LAYOUT_BSND or TSA_LAYOUT_TND */
   int32_t B, Sq, N1, N2, D, Dr, Dv;
   int32_t num_pages, page_size, max_pages;
   int32_t topk;
@@ -372,6 +378,8 @@ typedef struct {
   int32_t n_events;         /* number of stages to time (0 = off) */
   void* const* events;      /* HOST array of 2*n_events hipEvent_t: events[2i] / [2i+1] are
                                recorded on `stream` before / after stage i (see each entry) */
+  int32_t T;                    /* TND: total query tokens (== cu_seqlens_q[B]) */
+  const int32_t* cu_seqlens_q;  /* TND: HOST [B+1] prefix sums from 0 (ignored for BSND) */
 } sfa_paged_fwd_args;
 
 TSA_API int sfa_paged_fwd_workspace_size(const sfa_paged_fwd_args* args, size_t* bytes);

@@ -200,6 +200,22 @@ def _sfa(tsa, **kw):
     return tsa._abi.SfaArgs(**a)
 
 
+@pytest.mark.parametrize("cq,T,status", [
+    ((0, 4, 9, 9), 9, 0),                  # ragged query counts, an empty entry
+    ((0, 0, 0, 0), 0, 0),                  # no queries: valid
+    ((1, 4, 9, 9), 9, 2),                  # prefix sums start at 0
+    ((0, 4, 3, 9), 9, 2),                  # and do not decrease
+    ((0, 4, 9, 9), 10, 2),                 # and end at T
+])
+def test_sfa_tnd_validation(tsa, cq, T, status):
+    a = _sfa(tsa, q_layout=1, B=3, Sq=0, T=T)
+    a.cu_seqlens_q = (ctypes.c_int32 * 4)(*cq)
+    s, n = _size(tsa, tsa.lib.sfa_paged_fwd_workspace_size, a)
+    assert s == status
+    if s == 0:
+        assert n > 0
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(), 0),
     (dict(N1=48), 2),                      # N1 a power of two
@@ -212,7 +228,8 @@ def _sfa(tsa, **kw):
     (dict(sparse_block_size=3), 2),        # must divide the page size
     (dict(sparse_mode=2), 2),
     (dict(value_cache=24), 3),             # separate value cache: not built
-    (dict(q_layout=1), 3),
+    (dict(q_layout=1), 1),                 # TND queries need cu_seqlens_q
+    (dict(scale=0.0), 2),
     (dict(kv_lens=0), 1),
 ])
 def test_sfa_validation(tsa, kw, status):

@@ -108,3 +108,71 @@ def test_sfa_validate_reports_bad_ids():
     with pytest.raises(tsa.TsaError) as ei:
         _run(q, qr, kc, krc, bt, kv_lens, idx, 0.04, 3, validate=True)
     assert ei.value.status == 6
+
+
+def _tnd_inputs(lens, kv_lens, N1, page, K, seed, dtype="bf16"):
+    """TND decode queries: entry b has lens[b] tokens; each selects up to K
+    distinct positions of [0, kv_len - lens[b] + s] (rightDownCausal), -1 in
+    the slots left over; pages are a random permutation."""
+    rng = np.random.default_rng(seed)
+    B, T = len(lens), int(sum(lens))
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    pages = [-(-int(n) // page) for n in kv_lens]
+    P = sum(pages) + 2
+    perm = rng.permutation(P)
+    bt = np.zeros((B, max(pages)), np.int32)
+    off = 0
+    for b in range(B):
+        bt[b, :pages[b]] = perm[off:off + pages[b]]
+        off += pages[b]
+    idx = np.full((T, 1, K), -1, np.int32)
+    for b in range(B):
+        for s in range(lens[b]):
+            hi = int(kv_lens[b]) - lens[b] + s + 1
+            n = min(K, hi)
+            idx[cu[b] + s, 0, :n] = np.sort(rng.choice(hi, size=n, replace=False))
+    q = W.normal((T, N1, 512), seed + 1, dtype)
+    qr = W.normal((T, N1, 64), seed + 2, dtype)
+    kc = W.normal((P, page, 1, 512), seed + 3, dtype)
+    krc = W.normal((P, page, 1, 64), seed + 4, dtype)
+    return cu, q, qr, kc, krc, bt, np.asarray(kv_lens, np.int32), idx
+
+
+@pytest.mark.parametrize("lens,kv_lens,N1,page,K", [
+    ([1, 4, 0, 2, 3], [300, 900, 200, 513, 640], 64, 32, 256),   # ragged, an empty entry
+    ([2, 1], [130, 4100], 16, 128, 2048),                          # many splits, 16 heads
+])
+def test_sfa_tnd_ragged_queries(lens, kv_lens, N1, page, K):
+    tsa = _tsa()
+    cu, q, qr, kc, krc, bt, kvl, idx = _tnd_inputs(lens, kv_lens, N1, page, K, 90)
+    scale = 1 / math.sqrt(576)
+    d = torch.device("cuda")
+    kcd = kc.to(d)
+    out, lse = tsa.sfa_paged_fwd(q.to(d), qr.to(d), kcd, krc.to(d), kcd, torch.from_numpy(bt).to(d),
+                                 torch.from_numpy(kvl).to(d), torch.from_numpy(idx).to(d), scale,
+                                 3, cu_seqlens_q=cu)
+    torch.cuda.synchronize()
+    ro, rl = oracle.sfa_fwd_tnd(_np(q), _np(qr), _np(kc), _np(krc), _np(kc), bt, kvl, idx, cu,
+                                scale, 3)
+    o, l = _np(out), _np(lse)
+    assert np.isfinite(o).all()
+    err, sc = np.abs(o - ro).max(), np.abs(ro).max()
+    assert err <= OUT_TOL * sc, f"out: {err:.3e} vs {OUT_TOL} * {sc:.3e}"
+    assert np.abs(l - rl).max() <= LSE_TOL * max(1.0, np.abs(rl).max())
+
+
+def test_sfa_tnd_equal_lengths_is_bsnd_bitwise():
+    tsa = _tsa()
+    q, qr, kc, krc, bt, kv_lens, idx = W.sfa_inputs(B=3, Sq=2, N1=64, page=64, kv_len=1500,
+                                                    topk=512, seed_base=95)
+    d = torch.device("cuda")
+    kcd, krcd = kc.to(d), krc.to(d)
+    btd, kvd = torch.from_numpy(bt).to(d), torch.from_numpy(kv_lens).to(d)
+    o1, l1 = tsa.sfa_paged_fwd(q.to(d), qr.to(d), kcd, krcd, kcd, btd, kvd,
+                               torch.from_numpy(idx).to(d), 0.04, 3)
+    cu = np.arange(4, dtype=np.int32) * 2
+    o2, l2 = tsa.sfa_paged_fwd(q.reshape(6, 64, 512).to(d), qr.reshape(6, 64, 64).to(d), kcd, krcd,
+                               kcd, btd, kvd, torch.from_numpy(idx.reshape(6, 1, -1)).to(d), 0.04,
+                               3, cu_seqlens_q=cu)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.reshape(6, 64, 512), o2) and torch.equal(l1.reshape(6, 64), l2)

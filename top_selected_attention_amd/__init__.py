@@ -393,36 +393,53 @@ class SfaPlan:
     q [B, Sq, N1, 512], q_rope [B, Sq, N1, 64] (BSND); key_cache [P, page, 1, 512],
     key_rope_cache [P, page, 1, 64], value_cache [P, page, 1, 512] (may be key_cache);
     block_table int32 [B, max_pages]; kv_lens int32 [B]; topk_indices int32
-    [B, Sq, 1, K] (-1 = empty).
+    [B, Sq, 1, K] (-1 = empty).  With cu_seqlens_q (host B+1 prefix sums) the
+    queries are TND: q [T, N1, 512], q_rope [T, N1, 64], topk_indices
+    [T, 1, K], out [T, N1, 512], lse [T, N1].
     """
 
     def __init__(self, q, q_rope, key_cache, key_rope_cache, value_cache, block_table, kv_lens,
-                 topk_indices, scale=None, sparse_mode=3, sparse_block_size=1, validate=False):
+                 topk_indices, scale=None, sparse_mode=3, sparse_block_size=1, validate=False,
+                 cu_seqlens_q=None):
         for t, n in ((q, "q"), (q_rope, "q_rope"), (key_cache, "key_cache"),
                      (key_rope_cache, "key_rope_cache"), (value_cache, "value_cache")):
             _check(t, n, q.dtype)
-        B, Sq, N1, D = q.shape
         P, page, N2, _ = key_cache.shape
-        Dr, Dv = q_rope.shape[3], value_cache.shape[3]
+        Dv = value_cache.shape[3]
+        K = topk_indices.shape[-1]
+        extra = {}
+        if cu_seqlens_q is not None:
+            self.cu_q = _host_i32(cu_seqlens_q)
+            B = self.cu_q.numel() - 1
+            T, N1, D = q.shape
+            Sq, Dr = 0, q_rope.shape[2]
+            if int(self.cu_q[-1]) != T:
+                raise ValueError("cu_seqlens_q does not match q")
+            tok_shape, layout = (T,), LAYOUT_TND
+            extra = dict(T=T, cu_seqlens_q=ctypes.cast(self.cu_q.data_ptr(),
+                                                       ctypes.POINTER(ctypes.c_int32)))
+        else:
+            B, Sq, N1, D = q.shape
+            Dr = q_rope.shape[3]
+            tok_shape, layout = (B, Sq), LAYOUT_BSND
         _check(block_table, "block_table", torch.int32)
         _check(kv_lens, "kv_lens", torch.int32, (B,))
-        K = topk_indices.shape[-1]
-        _check(topk_indices, "topk_indices", torch.int32, (B, Sq, N2, K))
+        _check(topk_indices, "topk_indices", torch.int32, tok_shape + (N2, K))
         self.keep = (q, q_rope, key_cache, key_rope_cache, value_cache, block_table, kv_lens,
                      topk_indices)
         self.scale = 1.0 / math.sqrt(D + Dr) if scale is None else float(scale)
         dev = q.device
-        self.out = torch.empty((B, Sq, N1, Dv), dtype=q.dtype, device=dev)
-        self.lse = torch.empty((B, Sq, N1), dtype=torch.float32, device=dev)
+        self.out = torch.empty(tok_shape + (N1, Dv), dtype=q.dtype, device=dev)
+        self.lse = torch.empty(tok_shape + (N1,), dtype=torch.float32, device=dev)
         self.a = _abi.SfaArgs(
-            dtype=_dtype_code(q), q_layout=LAYOUT_BSND, B=B, Sq=Sq, N1=N1, N2=N2, D=D, Dr=Dr,
+            dtype=_dtype_code(q), q_layout=layout, B=B, Sq=Sq, N1=N1, N2=N2, D=D, Dr=Dr,
             Dv=Dv, num_pages=P, page_size=page, max_pages=block_table.shape[1], topk=K,
             sparse_block_size=sparse_block_size, sparse_mode=sparse_mode, scale=self.scale,
             validate=int(bool(validate)), q=q.data_ptr(), q_rope=q_rope.data_ptr(),
             key_cache=key_cache.data_ptr(), key_rope_cache=key_rope_cache.data_ptr(),
             value_cache=value_cache.data_ptr(), block_table=block_table.data_ptr(),
             kv_lens=kv_lens.data_ptr(), topk_indices=topk_indices.data_ptr(),
-            out=self.out.data_ptr(), lse=self.lse.data_ptr())
+            out=self.out.data_ptr(), lse=self.lse.data_ptr(), **extra)
         nb = ctypes.c_size_t()
         _abi.call(lib.sfa_paged_fwd_workspace_size, ctypes.byref(self.a), ctypes.byref(nb))
         self.ws = _workspace(nb.value, dev)
@@ -434,7 +451,10 @@ class SfaPlan:
 
 
 def sfa_paged_fwd(q, q_rope, key_cache, key_rope_cache, value_cache, block_table, kv_lens,
-                  topk_indices, scale=None, sparse_mode=3, sparse_block_size=1, validate=False):
-    """Paged sparse flash attention forward: returns (out, lse)."""
+                  topk_indices, scale=None, sparse_mode=3, sparse_block_size=1, validate=False,
+                  cu_seqlens_q=None):
+    """Paged sparse flash attention forward (BSND, or TND queries with
+    cu_seqlens_q): returns (out, lse)."""
     return SfaPlan(q, q_rope, key_cache, key_rope_cache, value_cache, block_table, kv_lens,
-                   topk_indices, scale, sparse_mode, sparse_block_size, validate).fwd()
+                   topk_indices, scale, sparse_mode, sparse_block_size, validate,
+                   cu_seqlens_q).fwd()

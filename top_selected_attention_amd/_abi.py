@@ -90,7 +90,7 @@ class SfaArgs(ctypes.Structure):
         ("key_rope_cache", c_void_p), ("value_cache", c_void_p),
         ("block_table", c_void_p), ("kv_lens", c_void_p), ("topk_indices", c_void_p),
         ("out", c_void_p), ("lse", c_void_p),
-    ] + TRAIL
+    ] + TRAIL + [("T", c_int32), ("cu_seqlens_q", POINTER(c_int32))]
 
 
 ARG_STRUCTS = [BsaFwdArgs, BsaBwdArgs, NsaFwdArgs, NsaBwdArgs, SfaArgs]

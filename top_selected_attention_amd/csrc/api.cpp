@@ -419,12 +419,25 @@ int nsa_lists(const A* a, const NsaWs& w, const NsaGeom& g, int parts, hipStream
 // Sparse flash attention
 // ---------------------------------------------------------------------------
 
+// Decode tokens of an SFA call: B * Sq (BSND) or T (TND).
+long sfa_tokens(const sfa_paged_fwd_args* a) {
+  return a->q_layout == TSA_LAYOUT_TND ? (long)a->T : (long)a->B * a->Sq;
+}
+
 int check_sfa(const sfa_paged_fwd_args* a) {
   if (!a) return TSA_ERR_NULL;
   if (a->dtype != TSA_BF16 && a->dtype != TSA_FP16) return TSA_ERR_INVALID;
-  if (a->q_layout == TSA_LAYOUT_TND) return TSA_ERR_UNSUPPORTED;
-  if (a->q_layout != TSA_LAYOUT_BSND) return TSA_ERR_INVALID;
+  // "SparseAttnSharedkvMetadata", parameter list: layout_q BSND or TND
+  // (cu_seqlens_q prefix sums for TND).
+  if (a->q_layout != TSA_LAYOUT_BSND && a->q_layout != TSA_LAYOUT_TND) return TSA_ERR_INVALID;
   if (a->B < 0 || a->Sq < 0) return TSA_ERR_INVALID;
+  if (a->q_layout == TSA_LAYOUT_TND) {
+    if (!a->cu_seqlens_q) return TSA_ERR_NULL;
+    if (a->T < 0 || a->cu_seqlens_q[0] != 0 || a->cu_seqlens_q[a->B] != a->T)
+      return TSA_ERR_INVALID;
+    for (int b = 0; b < a->B; b++)
+      if (a->cu_seqlens_q[b + 1] < a->cu_seqlens_q[b]) return TSA_ERR_INVALID;
+  }
   // "aclnnSparseFlashAttention", constraints: N1 in {1, 2, 4, ..., 128}.
   if (a->N1 < 1 || a->N1 > 128 || (a->N1 & (a->N1 - 1))) return TSA_ERR_INVALID;
   if (a->N2 < 1 || a->N1 % a->N2 != 0) return TSA_ERR_INVALID;
@@ -442,7 +455,9 @@ int check_sfa(const sfa_paged_fwd_args* a) {
   if (!std::isfinite(a->scale) || !(a->scale > 0.f)) return TSA_ERR_INVALID;
   if (!fits_i32((long)a->num_pages * a->page_size) || !fits_i32((long)a->B * a->max_pages))
     return TSA_ERR_INVALID;
-  if ((long)a->B * a->Sq > 0 &&
+  if (!fits_i32(sfa_tokens(a) * a->N1 * a->D) || !fits_i32(sfa_tokens(a) * a->topk))
+    return TSA_ERR_INVALID;
+  if (sfa_tokens(a) > 0 &&
       (!a->q || !a->q_rope || !a->key_cache || !a->key_rope_cache || !a->value_cache ||
        !a->block_table || !a->kv_lens || !a->topk_indices || !a->out))
     return TSA_ERR_NULL;
@@ -459,6 +474,7 @@ SfaParams sfa_params(const sfa_paged_fwd_args* a) {
   p.vc = a->value_cache; p.block_table = a->block_table; p.kv_lens = a->kv_lens;
   p.topk = a->topk_indices; p.out = a->out; p.lse = a->lse;
   p.B = a->B; p.Sq = a->Sq; p.N1 = a->N1; p.N2 = a->N2; p.D = a->D; p.Dr = a->Dr; p.Dv = a->Dv;
+  p.ntok = sfa_tokens(a);
   p.num_pages = a->num_pages; p.page = a->page_size; p.max_pages = a->max_pages;
   p.topk_n = a->topk; p.sbs = a->sparse_block_size;
   p.causal = a->sparse_mode == 3;
@@ -469,15 +485,18 @@ SfaParams sfa_params(const sfa_paged_fwd_args* a) {
 
 size_t sfa_carve(const SfaParams& p, void* ws, SfaParams* out) {
   Carver c(ws);
-  const long tok = (long)p.B * p.Sq;
+  const long tok = p.ntok;
   float* po = c.take<float>(tok * p.splits * p.N1 * p.Dv);
   float* pl = c.take<float>(tok * p.splits * p.N1);
   int* bad = c.take<int>(1);
+  int* cu = c.take<int>(p.B + 1);   // TND query prefix sums, uploaded per call
   if (out) {
     *out = p;
     out->part_o = po;
     out->part_lse = pl;
     out->bad = bad;
+    out->cu_q = nullptr;
+    out->cu_dev = cu;
   }
   return c.off + kAlign;
 }
@@ -774,10 +793,17 @@ int sfa_paged_fwd(const sfa_paged_fwd_args* a, void* ws, size_t ws_bytes, void* 
   int s = sfa_paged_fwd_workspace_size(a, &need);
   if (s) return s;
   if (!ws || ws_bytes < need) return TSA_ERR_WORKSPACE;
-  if ((long)a->B * a->Sq == 0) return TSA_OK;
+  if (sfa_tokens(a) == 0) return TSA_OK;
   hipStream_t st = (hipStream_t)stream;
   SfaParams p;
   sfa_carve(sfa_params(a), ws, &p);
+  if (a->q_layout == TSA_LAYOUT_TND) {
+    // the copy from pageable memory is staged before hipMemcpyAsync returns
+    if (hipMemcpyAsync(p.cu_dev, a->cu_seqlens_q, sizeof(int) * (a->B + 1),
+                       hipMemcpyHostToDevice, st) != hipSuccess)
+      return TSA_ERR_HIP;
+    p.cu_q = p.cu_dev;
+  }
   if (a->validate) {
     hipError_t e = hipMemsetAsync(p.bad, 0, sizeof(int), st);
     if (e == hipSuccess) e = launch_sfa_check(p, st);

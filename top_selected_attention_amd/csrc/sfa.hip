@@ -48,6 +48,26 @@ __device__ __forceinline__ int swz1k(int r) { return ((r & 7) << 1) | ((r >> 3) 
 __device__ __forceinline__ int swzr(int r) { return (r >> 1) & 7; }
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// Batch entry b, index s within it and query count sq of decode token tk:
+// BSND has Sq tokens per entry; TND entry b holds rows cu_q[b] .. cu_q[b+1]-1
+// (the largest b with cu_q[b] <= tk, which skips empty entries).
+__device__ __forceinline__ void sfa_token(const SfaParams& p, int tk, int& b, int& s, int& sq) {
+  if (!p.cu_q) {
+    b = tk / p.Sq;
+    s = tk - b * p.Sq;
+    sq = p.Sq;
+    return;
+  }
+  int lo = 0, hi = p.B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (p.cu_q[mid] <= tk) lo = mid; else hi = mid - 1;
+  }
+  b = lo;
+  s = tk - p.cu_q[b];
+  sq = p.cu_q[b + 1] - p.cu_q[b];
+}
 }  // namespace
 
 template <class E>
@@ -68,7 +88,8 @@ __global__ __launch_bounds__(512) void sfa_split_kernel(SfaParams p, int n_items
   const int hg = item % hgroups;
   const int sp = (item / hgroups) % p.splits;
   const int tk = item / (hgroups * p.splits);
-  const int b = tk / p.Sq, s = tk % p.Sq;
+  int b, s, sq;
+  sfa_token(p, tk, b, s, sq);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
@@ -80,7 +101,7 @@ __global__ __launch_bounds__(512) void sfa_split_kernel(SfaParams p, int n_items
   const int h2 = wid & 1, qd = wid >> 1;
 
   const int kv_len = p.kv_lens[b];
-  const int qpos = kv_len - p.Sq + s;
+  const int qpos = kv_len - sq + s;
   const int total = p.topk_n * p.sbs;
   const int slot_lo = sp * per_split;
   const int slot_hi = min(slot_lo + per_split, total);
@@ -321,7 +342,7 @@ __global__ __launch_bounds__(256) void sfa_combine_kernel(SfaParams p) {
   typedef typename E::T T;
   const long w = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const long ntok = (long)p.B * p.Sq;
+  const long ntok = p.ntok;
   if (w >= ntok * p.N1) return;
   const long tk = w / p.N1;
   const int head = (int)(w % p.N1);
@@ -352,10 +373,11 @@ __global__ __launch_bounds__(256) void sfa_combine_kernel(SfaParams p) {
 // validate = 1: ids, kv_lens and the pages they reach must be in range.
 __global__ void sfa_check_kernel(SfaParams p) {
   const long i = (long)blockIdx.x * 256 + threadIdx.x;
-  const long ntok = (long)p.B * p.Sq;
+  const long ntok = p.ntok;
   if (i >= ntok * p.topk_n) return;
   const long tk = i / p.topk_n;
-  const int b = (int)(tk / p.Sq);
+  int b, s, sq;
+  sfa_token(p, (int)tk, b, s, sq);
   const int kv_len = p.kv_lens[b];
   bool bad = kv_len < 0 || kv_len > p.max_pages * p.page;
   const int id = p.topk[i];
@@ -371,7 +393,7 @@ __global__ void sfa_check_kernel(SfaParams p) {
 }
 
 int sfa_splits(const SfaParams& p) {
-  const long tokens = (long)p.B * p.Sq;
+  const long tokens = p.ntok;
   const int hgroups = (p.N1 + 63) / 64;
   const long wgs = tokens * hgroups;
   const int total = p.topk_n * p.sbs;
@@ -386,7 +408,7 @@ int sfa_splits(const SfaParams& p) {
 }
 
 hipError_t launch_sfa_check(const SfaParams& p, hipStream_t st) {
-  const long n = (long)p.B * p.Sq * p.topk_n;
+  const long n = p.ntok * p.topk_n;
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(sfa_check_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p);
   return hipGetLastError();
@@ -394,7 +416,7 @@ hipError_t launch_sfa_check(const SfaParams& p, hipStream_t st) {
 
 template <class E>
 static hipError_t sfa_t(const SfaParams& p, hipStream_t st, void* const* ev, int n_ev) {
-  const long tokens = (long)p.B * p.Sq;
+  const long tokens = p.ntok;
   const int hgroups = (p.N1 + 63) / 64;
   const int total = p.topk_n * p.sbs;
   const int per_split = ((total + p.splits - 1) / p.splits + kKeys - 1) / kKeys * kKeys;

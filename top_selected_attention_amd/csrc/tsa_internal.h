@@ -185,10 +185,13 @@ struct SfaParams {
   const int* topk;
   void* out;
   float* lse;          // may be null
-  float* part_o;       // split partials [B*Sq, splits, N1, Dv] fp32
-  float* part_lse;     // [B*Sq, splits, N1]
+  float* part_o;       // split partials [ntok, splits, N1, Dv] fp32
+  float* part_lse;     // [ntok, splits, N1]
   int* bad;            // validate flag (may be null)
   int B, Sq, N1, N2, D, Dr, Dv;
+  long ntok;           // decode tokens: B * Sq (BSND) or T (TND)
+  const int* cu_q;     // TND: [B+1] query prefix sums (device); null for BSND
+  int* cu_dev;         // workspace slot the TND prefix sums are uploaded to
   int num_pages, page, max_pages, topk_n, sbs;
   int causal;
   int splits;
