@@ -702,8 +702,9 @@ def ingest(d, workload):
     _save_traffic(t)
     rl = bench["roofline"]
     cmd = (f"python3 bench.py --workload {workload} --steps {bench['steps']} "
-           f"--warmup {bench['warmup']} --cpu-seconds 0")
-    pcmd = (f"python3 bench.py --workload {workload} --steps 2 --warmup 1 --cpu-seconds 0")
+           f"--warmup {bench['warmup']} --cpu-seconds 0 --no-peaks")
+    pcmd = (f"python3 bench.py --workload {workload} --steps 2 --warmup 1 --cpu-seconds 0 "
+            f"--no-peaks")
     out = [
         f"# {dom} on {workload}: rocprofv3 kernel trace and HBM counters",
         "",
