@@ -41,5 +41,6 @@ from .attention import (  # noqa: F401
     nsa_keys,
     sfa_fwd,
     sfa_fwd_tnd,
+    sfa_sharedkv_fwd,
 )
 from .compaction import bsa_compact, nsa_compact  # noqa: F401

@@ -31,7 +31,8 @@ Conventions that the pages leave open, and the reading taken here:
   with sparse_mode 2 both exclusions apply.  Positions are within a sequence
   in TND.
 
-Parity status: attend_fwd / attend_bwd, bsa_*, nsa_* and sfa_fwd are pinned by
+Parity status: attend_fwd / attend_bwd, bsa_*, nsa_*, sfa_fwd, sfa_fwd_tnd and
+sfa_sharedkv_fwd are pinned by
 the tests in ``tests/test_oracle_pins.py`` (dense special cases against an
 independent torch autograd attention, finite differences, closed forms,
 invariants and cross-path equalities).  The empty-row convention is unpinned.
@@ -466,4 +467,68 @@ def sfa_fwd_tnd(q, q_rope, key_cache, key_rope_cache, value_cache, block_table, 
         out[t], lse[t] = _sfa_token(q[t], q_rope[t], topk[t], block_table[b], kv_len,
                                     kv_len - sq_b + (t - int(cu[b])), key_cache, key_rope_cache,
                                     value_cache, scale, sparse_mode, sparse_block_size)
+    return out, lse
+
+
+def sfa_sharedkv_fwd(q, q_rope, cu_seqlens_q, kv_lens, scale, ori=None, cmp=None,
+                     win_left=127, win_right=0, cmp_ratio=4, tokens=None):
+    """Shared-KV sparse decode over two key sets in one softmax.
+
+    "SparseAttnSharedkvMetadata", parameter list: the query attends to the
+    original KV (ori_kv) under mask mode 4, a band of ori_win_left past and
+    ori_win_right future tokens around its own position, and to cmp_topk
+    selected entries of a compressed KV (cmp_kv, ori_kv compressed by
+    cmp_ratio) under mask mode 3, rightDownCausal; both caches are PageAttention
+    paged with one KV head (has_ori_kv / has_cmp_kv say which are given).  The
+    score and value rules are those of "aclnnSparseFlashAttention" (formulas):
+    score = scale * (q.k + q_rope.k_rope), value = the key's 512-wide row.
+
+    Readings: the two key sets share one softmax (one normalisation); query
+    token s of entry b (Sq_b tokens) sits at p = kv_len_b - Sq_b + s in the
+    original sequence; the band is [p - win_left, p + win_right] clipped to
+    [0, kv_len_b); the compressed sequence holds cmp_len_b = kv_len_b //
+    cmp_ratio entries and rightDownCausal lets compressed id c through iff
+    c <= cmp_len_b - Sq_b + s.
+
+    q [T, N1, D], q_rope [T, N1, Dr] (TND rows; cu_seqlens_q [B+1] prefix
+    sums); kv_lens [B] (seqused_kv).  ori = (key_cache [P, page, 1, D],
+    key_rope_cache [P, page, 1, Dr], block_table [B, max_pages]) or None;
+    cmp = (key_cache, key_rope_cache, block_table, topk [T, 1, K] compressed
+    ids, -1 = empty) or None.  ``tokens``: optional list of rows t.
+    Returns (out [T, N1, D], lse [T, N1]); rows not computed are NaN.
+    """
+    cu = np.asarray(cu_seqlens_q)
+    T, N1, D = q.shape
+    out = np.full((T, N1, D), np.nan)
+    lse = np.full((T, N1), np.nan)
+    for t in (range(T) if tokens is None else tokens):
+        b = int(np.searchsorted(cu, t, side="right")) - 1
+        sq_b, s = int(cu[b + 1] - cu[b]), t - int(cu[b])
+        kv_len = int(kv_lens[b])
+        keys, vals = [], []
+        if ori is not None:
+            kc, krc, bt = ori
+            page = kc.shape[1]
+            p = kv_len - sq_b + s
+            pos = np.arange(max(0, p - win_left), min(kv_len, p + win_right + 1))
+            phys, row = np.asarray(bt[b])[pos // page], pos % page
+            keys.append(np.concatenate([_f64(kc[phys, row, 0]), _f64(krc[phys, row, 0])], 1))
+            vals.append(_f64(kc[phys, row, 0]))
+        if cmp is not None:
+            kc, krc, bt, topk = cmp
+            page = kc.shape[1]
+            cmp_len = kv_len // cmp_ratio
+            ids = np.asarray(topk[t, 0]).astype(np.int64)
+            ids = ids[ids >= 0]
+            if np.any(ids >= cmp_len):
+                raise ValueError("compressed id beyond cmp_len")
+            ids = ids[ids <= cmp_len - sq_b + s]
+            phys, row = np.asarray(bt[b])[ids // page], ids % page
+            keys.append(np.concatenate([_f64(kc[phys, row, 0]), _f64(krc[phys, row, 0])], 1))
+            vals.append(_f64(kc[phys, row, 0]))
+        kmat = np.concatenate(keys) if keys else np.zeros((0, D + q_rope.shape[2]))
+        vmat = np.concatenate(vals) if vals else np.zeros((0, D))
+        qcat = np.concatenate([_f64(q[t]), _f64(q_rope[t])], axis=1)
+        o, l, _ = attend_fwd(qcat, kmat, vmat, np.ones((N1, len(kmat)), bool), scale)
+        out[t], lse[t] = o, l
     return out, lse

@@ -197,6 +197,107 @@ def test_sfa_page_table_permutation_is_invisible():
 
 
 # ----------------------------------------------------------------------------
+# Shared-KV two-branch decode (band over the original KV + compressed top-k)
+# ----------------------------------------------------------------------------
+
+def _skv_small(seed=40, lens=(1, 3, 2), kv_lens=(40, 70, 9), cmp_ratio=4, K=6):
+    x = W.sfa_sharedkv_inputs(lens=lens, kv_lens=kv_lens, N1=4, D=16, Dr=8, page=8,
+                              cmp_ratio=cmp_ratio, cmp_topk=K, seed_base=seed, dtype="fp32")
+    cu, q, qr, kvl, ori, cmp = x
+    f = lambda t: t.double().numpy() if isinstance(t, torch.Tensor) else t  # noqa: E731
+    return (cu, f(q), f(qr), kvl, tuple(f(t) for t in ori), tuple(f(t) for t in cmp))
+
+
+def _rows(kc, krc, bt, pos):
+    page = kc.shape[1]
+    phys, row = bt[pos // page], pos % page
+    return np.concatenate([kc[phys, row, 0], krc[phys, row, 0]], 1), kc[phys, row, 0]
+
+
+def test_sfa_sharedkv_equals_dense_attention_over_the_union():
+    """Each token's keys gathered straight from the caches (band rows, then
+    the compressed rows it may see) and run through torch's attention equal
+    the oracle; with win_left = 3 the band is shorter than most sequences."""
+    cu, q, qr, kvl, ori, cmp = _skv_small()
+    scale = 0.21
+    out, lse = oracle.sfa_sharedkv_fwd(q, qr, cu, kvl, scale, ori=ori, cmp=cmp, win_left=3,
+                                       cmp_ratio=4)
+    for b in range(len(kvl)):
+        sq, n = int(cu[b + 1] - cu[b]), int(kvl[b])
+        for s in range(sq):
+            t = int(cu[b]) + s
+            p = n - sq + s
+            band = np.arange(max(0, p - 3), p + 1)
+            ids = cmp[3][t, 0]
+            ids = ids[(ids >= 0) & (ids <= n // 4 - sq + s)]
+            k1, v1 = _rows(ori[0], ori[1], ori[2][b], band)
+            k2, v2 = _rows(cmp[0], cmp[1], cmp[2][b], ids)
+            kk, vv = torch.tensor(np.concatenate([k1, k2])), torch.tensor(np.concatenate([v1, v2]))
+            qq = torch.tensor(np.concatenate([q[t], qr[t]], 1))
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                qq[:, None], kk[None].expand(4, -1, -1), vv[None].expand(4, -1, -1),
+                scale=scale)[:, 0]
+            np.testing.assert_allclose(out[t], ref.numpy(), rtol=0, atol=1e-12)
+            np.testing.assert_allclose(lse[t], torch.logsumexp(scale * qq @ kk.T, -1).numpy(),
+                                       rtol=0, atol=1e-12)
+
+
+def test_sfa_sharedkv_band_alone_is_sfa_over_the_window():
+    """Without the compressed branch the decode is the pinned SFA path with
+    the window positions as its selection (rightDownCausal)."""
+    cu, q, qr, kvl, ori, cmp = _skv_small(41)
+    o1, l1 = oracle.sfa_sharedkv_fwd(q, qr, cu, kvl, 0.3, ori=ori, cmp=None, win_left=127)
+    T = q.shape[0]
+    idx = np.full((T, 1, 128), -1)
+    for b in range(len(kvl)):
+        sq, n = int(cu[b + 1] - cu[b]), int(kvl[b])
+        for s in range(sq):
+            p = n - sq + s
+            pos = np.arange(max(0, p - 127), p + 1)
+            idx[cu[b] + s, 0, :len(pos)] = pos
+    o2, l2 = oracle.sfa_fwd_tnd(q, qr, ori[0], ori[1], ori[0], ori[2], kvl, idx, cu, 0.3, 3)
+    np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l1, l2, rtol=0, atol=1e-12)
+
+
+def test_sfa_sharedkv_branches_merge_by_lse():
+    """One softmax over both key sets is the LSE-weighted merge of the two
+    single-branch results: LSE = logaddexp(LSE_ori, LSE_cmp) and
+    O = exp(LSE_ori - LSE) O_ori + exp(LSE_cmp - LSE) O_cmp."""
+    cu, q, qr, kvl, ori, cmp = _skv_small(42, kv_lens=(64, 128, 40), cmp_ratio=4, K=10)
+    ob, lb = oracle.sfa_sharedkv_fwd(q, qr, cu, kvl, 0.25, ori=ori, cmp=cmp, win_left=7)
+    oo, lo = oracle.sfa_sharedkv_fwd(q, qr, cu, kvl, 0.25, ori=ori, cmp=None, win_left=7)
+    oc, lc = oracle.sfa_sharedkv_fwd(q, qr, cu, kvl, 0.25, ori=None, cmp=cmp, win_left=7)
+    lse = np.logaddexp(lo, lc)
+    np.testing.assert_allclose(lb, lse, rtol=0, atol=1e-12)
+    merged = np.exp(lo - lse)[..., None] * oo + np.exp(lc - lse)[..., None] * oc
+    np.testing.assert_allclose(ob, merged, rtol=0, atol=1e-12)
+
+
+def test_sfa_sharedkv_compressed_alone_all_ids_is_dense_causal_mqa():
+    """Without the band, selecting every compressed id is dense MQA over the
+    compressed sequence with the rightDownCausal offset cmp_len - Sq_b."""
+    lens, kvl = (2, 3), (48, 64)
+    cu, q, qr, kv, ori, cmp = _skv_small(43, lens=lens, kv_lens=kvl, cmp_ratio=4, K=16)
+    kc, krc, bt, _ = cmp
+    T = q.shape[0]
+    idx = np.full((T, 1, 16), -1)
+    for b in range(2):
+        idx[cu[b]:cu[b + 1], 0, :kvl[b] // 4] = np.arange(kvl[b] // 4)
+    out, _ = oracle.sfa_sharedkv_fwd(q, qr, cu, kv, 0.2, ori=None, cmp=(kc, krc, bt, idx))
+    for b in range(2):
+        n, sq = kvl[b] // 4, lens[b]
+        k, v = _rows(kc, krc, bt[b], np.arange(n))
+        sl = slice(cu[b], cu[b + 1])
+        qq = torch.tensor(np.concatenate([q[sl], qr[sl]], -1)).transpose(0, 1)   # [N1, sq, .]
+        allowed = torch.arange(n)[None, :] <= (n - sq + torch.arange(sq))[:, None]
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            qq, torch.tensor(k)[None].expand(4, -1, -1), torch.tensor(v)[None].expand(4, -1, -1),
+            attn_mask=allowed, scale=0.2)
+        np.testing.assert_allclose(out[sl], ref.numpy().transpose(1, 0, 2), rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------
 # atten_mask (element mask inside the selected blocks; non-zero = excluded)
 # ----------------------------------------------------------------------------
 

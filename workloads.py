@@ -31,7 +31,7 @@ import math
 import numpy as np
 import torch
 
-DTYPES = {"bf16": torch.bfloat16, "fp16": torch.float16}
+DTYPES = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}
 
 
 def normal(shape, seed, dtype="bf16"):
@@ -221,6 +221,62 @@ def nsa_inputs(seqlens=None, N1=32, N2=2, D=128, sbs=64, sbc=16, seed_base=30, d
 def sfa_workload():
     return dict(name="sfa_decode", B=32, Sq=4, N1=64, N2=1, D=512, Dr=64, dtype="bf16",
                 page=128, kv_len=65536, topk=2048)
+
+
+def sfa_sharedkv_workload():
+    return dict(name="sfa_sharedkv_decode", B=32, Sq=4, N1=64, N2=1, D=512, Dr=64, dtype="bf16",
+                page=128, kv_len=65536, win_left=127, win_right=0, cmp_ratio=4, cmp_topk=512)
+
+
+def _paged_table(rng, lens, page, extra=0):
+    """block_table int32 [B, max_pages]: entry b's logical pages on a random
+    permutation of the physical pages (extra unused pages at the end)."""
+    pages = [-(-int(n) // page) for n in lens]
+    perm = rng.permutation(sum(pages) + extra)
+    bt = np.zeros((len(lens), max(max(pages), 1)), np.int32)
+    off = 0
+    for b, n in enumerate(pages):
+        bt[b, :n] = perm[off:off + n]
+        off += n
+    return bt, sum(pages) + extra
+
+
+def sfa_sharedkv_inputs(lens=None, kv_lens=None, N1=64, D=512, Dr=64, page=128, cmp_ratio=4,
+                        cmp_topk=512, seed_base=120, dtype="bf16", extra_pages=0):
+    """TND decode queries for the two-branch shared-KV decode.
+
+    lens: query tokens per batch entry (default 32 entries of 4); kv_lens: the
+    original KV length per entry (default 65536).  The original cache holds
+    kv_len rows per entry and the compressed cache kv_len // cmp_ratio, both
+    paged on random page permutations.  Each query token selects min(cmp_topk,
+    n) distinct sorted compressed ids uniformly from the n = cmp_len - Sq_b + s
+    + 1 it may see (rightDownCausal), -1 in the slots left.
+    Returns (cu int32 [B+1], q [T, N1, D], q_rope [T, N1, Dr], kv_lens int32
+    [B], (ori_kc, ori_krc, ori_bt), (cmp_kc, cmp_krc, cmp_bt, cmp_idx int32
+    [T, 1, cmp_topk]))."""
+    w = sfa_sharedkv_workload()
+    lens = [w["Sq"]] * w["B"] if lens is None else list(lens)
+    kv_lens = np.asarray([w["kv_len"]] * len(lens) if kv_lens is None else kv_lens, np.int32)
+    rng = np.random.default_rng(1000 + seed_base // 10)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    cmp_lens = kv_lens // cmp_ratio
+    ori_bt, P = _paged_table(rng, kv_lens, page, extra_pages)
+    cmp_bt, Pc = _paged_table(rng, cmp_lens, page, extra_pages)
+    idx = np.full((T, 1, cmp_topk), -1, np.int32)
+    for b, n_q in enumerate(lens):
+        for s in range(n_q):
+            n = int(cmp_lens[b]) - n_q + s + 1
+            if n > 0:
+                idx[cu[b] + s, 0, :min(cmp_topk, n)] = np.sort(
+                    rng.choice(n, size=min(cmp_topk, n), replace=False))
+    q = normal((T, N1, D), seed_base + 1, dtype)
+    q_rope = normal((T, N1, Dr), seed_base + 2, dtype)
+    ori = (normal((P, page, 1, D), seed_base + 3, dtype), normal((P, page, 1, Dr), seed_base + 4, dtype),
+           ori_bt)
+    cmp = (normal((Pc, page, 1, D), seed_base + 5, dtype),
+           normal((Pc, page, 1, Dr), seed_base + 6, dtype), cmp_bt, idx)
+    return cu, q, q_rope, kv_lens, ori, cmp
 
 
 def sfa_inputs(B=32, Sq=4, N1=64, D=512, Dr=64, page=128, kv_len=65536, topk=2048,
