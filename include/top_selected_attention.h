@@ -73,8 +73,8 @@ enum { TSA_LAYOUT_BNSD = 0, TSA_LAYOUT_TND = 1, TSA_LAYOUT_BSND = 2 };
 TSA_API const char* tsa_status_string(int status);
 
 /* sizeof of each argument struct, for binding checks: which = 0 bsa_fwd,
- * 1 bsa_bwd, 2 nsa_select_fwd, 3 nsa_select_bwd, 4 sfa_paged_fwd;
- * returns 0 for an unknown value. */
+ * 1 bsa_bwd, 2 nsa_select_fwd, 3 nsa_select_bwd, 4 sfa_paged_fwd,
+ * 5 sfa_sharedkv_fwd; returns 0 for an unknown value. */
 TSA_API size_t tsa_args_sizeof(int which);
 
 /* ------------------------------------------------------------------------
@@ -385,6 +385,72 @@ typedef struct {
 TSA_API int sfa_paged_fwd_workspace_size(const sfa_paged_fwd_args* args, size_t* bytes);
 TSA_API int sfa_paged_fwd(const sfa_paged_fwd_args* args, void* workspace, size_t workspace_bytes,
                   void* stream);
+
+/* ------------------------------------------------------------------------
+ * Shared-KV two-branch sparse decode ("SparseAttnSharedkvMetadata",
+ * parameter list; scores and values as in "aclnnSparseFlashAttention").
+ *
+ * Each decode token attends, in one softmax, to
+ *   - the original KV (ori_kv, has_ori_kv = 1) under mask mode 4, a band of
+ *     ori_win_left past and ori_win_right future positions around its own
+ *     position p = seqused_kv[b] - Sq_b + s, clipped to [0, seqused_kv[b]);
+ *   - cmp_topk selected entries of the compressed KV (cmp_kv, has_cmp_kv =
+ *     1; the original compressed by cmp_ratio, so entry b holds
+ *     seqused_kv[b] / cmp_ratio entries) under mask mode 3, rightDownCausal:
+ *     compressed id c is kept iff c <= cmp_len - Sq_b + s.
+ * score = scale * (q . k + q_rope . k_rope); the value is the key's 512-wide
+ * row (shared KV); one KV head (num_heads_kv = 1).  Both caches are PA_ND:
+ * key cache [pages, page_size, 1, 512], rope cache [pages, page_size, 1, 64],
+ * block table int32 [B, max_pages] (DEVICE).
+ * q [B, Sq, N1, 512], q_rope [B, Sq, N1, 64] (BSND) or [T, N1, ...] (TND
+ * with HOST cu_seqlens_q [B+1]); cmp_topk_indices int32 DEVICE [tokens, 1,
+ * cmp_topk] (-1 = empty); out like q with 512 columns; lse fp32 [tokens, N1]
+ * (may be NULL).  A token with no kept key gets Out = 0, LSE = -inf.
+ *
+ * A metadata kernel first writes the task list in the workspace: each
+ * token's slots (the band padded to a multiple of 32, then the top-k slots)
+ * are cut into per-workgroup slot ranges of near-equal kept-key weight; the
+ * split kernel takes its range from that list and the combine kernel merges
+ * the ranges by LSE.  Stages: 0 = task list, 1 = split attention, 2 =
+ * combine.
+ * Constraints: N1 a power of two <= 128; D 512, Dr 64; page sizes multiples
+ * of 16 <= 1024; cmp_ratio 4 or 128 (the parameter list's range);
+ * ori_win_left, ori_win_right >= 0 with their band <= 4096 slots;
+ * cmp_topk >= 1; at least one branch; scale finite and > 0.  Ids at or past
+ * the compressed length are skipped.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  int32_t dtype;
+  int32_t q_layout;             /* TSA_LAYOUT_BSND or TSA_LAYOUT_TND */
+  int32_t B, Sq, T, N1, N2, D, Dr;
+  float scale;
+  const void* q;                /* DEVICE */
+  const void* q_rope;           /* DEVICE */
+  const int32_t* cu_seqlens_q;  /* TND: HOST [B+1] */
+  const int32_t* seqused_kv;    /* DEVICE [B]: original KV tokens of each entry */
+  int32_t has_ori_kv, has_cmp_kv;
+  int32_t ori_win_left, ori_win_right;   /* 127, 0 */
+  int32_t ori_num_pages, ori_page_size, ori_max_pages;
+  const void* ori_key_cache;             /* DEVICE */
+  const void* ori_key_rope_cache;        /* DEVICE */
+  const int32_t* ori_block_table;        /* DEVICE */
+  int32_t cmp_ratio;                     /* 4 or 128 */
+  int32_t cmp_topk;
+  int32_t cmp_num_pages, cmp_page_size, cmp_max_pages;
+  const void* cmp_key_cache;             /* DEVICE */
+  const void* cmp_key_rope_cache;        /* DEVICE */
+  const int32_t* cmp_block_table;        /* DEVICE */
+  const int32_t* cmp_topk_indices;       /* DEVICE */
+  void* out;                    /* DEVICE, written */
+  float* lse;                   /* DEVICE, written, or NULL */
+  int32_t reuse_lists;          /* unused; keep 0 */
+  int32_t n_events;             /* number of stages to time (0 = off) */
+  void* const* events;          /* HOST array of 2*n_events hipEvent_t (see above) */
+} sfa_sharedkv_fwd_args;
+
+TSA_API int sfa_sharedkv_fwd_workspace_size(const sfa_sharedkv_fwd_args* args, size_t* bytes);
+TSA_API int sfa_sharedkv_fwd(const sfa_sharedkv_fwd_args* args, void* workspace,
+                             size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

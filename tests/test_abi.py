@@ -247,3 +247,52 @@ def test_import_fails_loudly_without_library(tmp_path):
     r = subprocess.run([sys.executable, "-c", "import top_selected_attention_amd"],
                        cwd=tmp_path, capture_output=True, text=True)
     assert r.returncode != 0 and "libtsa.so" in r.stderr
+
+
+def _skv(tsa, **kw):
+    a = dict(dtype=0, q_layout=2, B=32, Sq=4, N1=64, N2=1, D=512, Dr=64, scale=1 / 24, q=8,
+             q_rope=8, seqused_kv=8, has_ori_kv=1, has_cmp_kv=1, ori_win_left=127,
+             ori_win_right=0, ori_num_pages=16384, ori_page_size=128, ori_max_pages=512,
+             ori_key_cache=8, ori_key_rope_cache=8, ori_block_table=8, cmp_ratio=4,
+             cmp_topk=512, cmp_num_pages=4096, cmp_page_size=128, cmp_max_pages=128,
+             cmp_key_cache=8, cmp_key_rope_cache=8, cmp_block_table=8, cmp_topk_indices=8,
+             out=8, lse=8)
+    a.update(kw)
+    return tsa._abi.SfaSharedkvArgs(**a)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), 0),
+    (dict(N1=48), 2),                          # N1 a power of two
+    (dict(N2=2), 3),                           # one KV head
+    (dict(D=256), 2),
+    (dict(has_ori_kv=0, has_cmp_kv=0), 2),     # at least one branch
+    (dict(has_ori_kv=2), 2),
+    (dict(cmp_ratio=8), 2),                    # 4 or 128
+    (dict(cmp_ratio=128), 0),
+    (dict(cmp_topk=0), 2),
+    (dict(ori_win_left=-1), 2),
+    (dict(ori_win_left=4000, ori_win_right=100), 2),   # band of at most 4096 slots
+    (dict(ori_page_size=8), 2),
+    (dict(cmp_page_size=2048), 2),
+    (dict(scale=0.0), 2),
+    (dict(q=0), 1),
+    (dict(cmp_topk_indices=0), 1),
+    (dict(has_cmp_kv=0, cmp_key_cache=0, cmp_topk_indices=0, cmp_ratio=0), 0),
+    (dict(has_ori_kv=0, ori_key_cache=0, ori_block_table=0, ori_win_left=-5), 0),
+    (dict(q_layout=1, T=128), 1),              # TND needs cu_seqlens_q
+    (dict(B=0), 0),                            # no tokens
+])
+def test_sfa_sharedkv_validation(tsa, kw, status):
+    s, n = _size(tsa, tsa.lib.sfa_sharedkv_fwd_workspace_size, _skv(tsa, **kw))
+    assert s == status
+    if s == 0:
+        assert n > 0
+
+
+def test_sfa_sharedkv_workspace_too_small_is_rejected_before_launch(tsa):
+    a = _skv(tsa)
+    s, n = _size(tsa, tsa.lib.sfa_sharedkv_fwd_workspace_size, a)
+    assert s == 0
+    assert tsa.lib.sfa_sharedkv_fwd(ctypes.byref(a), ctypes.c_void_p(8), n - 1, None) == 4
+

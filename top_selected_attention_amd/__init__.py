@@ -458,3 +458,81 @@ def sfa_paged_fwd(q, q_rope, key_cache, key_rope_cache, value_cache, block_table
     return SfaPlan(q, q_rope, key_cache, key_rope_cache, value_cache, block_table, kv_lens,
                    topk_indices, scale, sparse_mode, sparse_block_size, validate,
                    cu_seqlens_q).fwd()
+
+
+class SfaSharedkvPlan:
+    """Shared-KV two-branch sparse decode for fixed tensors: a band of
+    win_left past / win_right future tokens over the original paged KV plus
+    cmp_topk selected entries of a compressed paged KV, in one softmax.
+
+    q [B, Sq, N1, 512] / q_rope [B, Sq, N1, 64] (BSND), or [T, N1, ...] with
+    host cu_seqlens_q (TND); seqused_kv int32 [B]; ori = (key_cache [P, page,
+    1, 512], key_rope_cache [P, page, 1, 64], block_table int32 [B, max_pages])
+    or None; cmp = (key_cache, key_rope_cache, block_table, topk int32
+    [tokens, 1, K]) or None.  ``fwd()`` returns (out, lse).
+    """
+
+    def __init__(self, q, q_rope, seqused_kv, ori=None, cmp=None, scale=None, win_left=127,
+                 win_right=0, cmp_ratio=4, cu_seqlens_q=None):
+        _check(q, "q"), _check(q_rope, "q_rope", q.dtype)
+        extra = {}
+        if cu_seqlens_q is not None:
+            self.cu_q = _host_i32(cu_seqlens_q)
+            B = self.cu_q.numel() - 1
+            T, N1, D = q.shape
+            Sq, Dr = 0, q_rope.shape[2]
+            if int(self.cu_q[-1]) != T:
+                raise ValueError("cu_seqlens_q does not match q")
+            tok_shape, layout = (T,), LAYOUT_TND
+            extra = dict(T=T, cu_seqlens_q=ctypes.cast(self.cu_q.data_ptr(),
+                                                       ctypes.POINTER(ctypes.c_int32)))
+        else:
+            B, Sq, N1, D = q.shape
+            Dr = q_rope.shape[3]
+            tok_shape, layout = (B, Sq), LAYOUT_BSND
+        _check(seqused_kv, "seqused_kv", torch.int32, (B,))
+        if ori is not None:
+            okc, okrc, obt = ori
+            _check(okc, "ori key_cache", q.dtype), _check(okrc, "ori key_rope_cache", q.dtype)
+            _check(obt, "ori block_table", torch.int32)
+            extra.update(has_ori_kv=1, ori_win_left=win_left, ori_win_right=win_right,
+                         ori_num_pages=okc.shape[0], ori_page_size=okc.shape[1],
+                         ori_max_pages=obt.shape[1], ori_key_cache=okc.data_ptr(),
+                         ori_key_rope_cache=okrc.data_ptr(), ori_block_table=obt.data_ptr())
+        if cmp is not None:
+            ckc, ckrc, cbt, idx = cmp
+            _check(ckc, "cmp key_cache", q.dtype), _check(ckrc, "cmp key_rope_cache", q.dtype)
+            _check(cbt, "cmp block_table", torch.int32)
+            K = idx.shape[-1]
+            _check(idx, "cmp topk", torch.int32, tok_shape + (1, K))
+            extra.update(has_cmp_kv=1, cmp_ratio=cmp_ratio, cmp_topk=K,
+                         cmp_num_pages=ckc.shape[0], cmp_page_size=ckc.shape[1],
+                         cmp_max_pages=cbt.shape[1], cmp_key_cache=ckc.data_ptr(),
+                         cmp_key_rope_cache=ckrc.data_ptr(), cmp_block_table=cbt.data_ptr(),
+                         cmp_topk_indices=idx.data_ptr())
+        self.keep = (q, q_rope, seqused_kv, ori, cmp)
+        self.scale = 1.0 / math.sqrt(D + Dr) if scale is None else float(scale)
+        dev = q.device
+        self.out = torch.empty(tok_shape + (N1, D), dtype=q.dtype, device=dev)
+        self.lse = torch.empty(tok_shape + (N1,), dtype=torch.float32, device=dev)
+        self.a = _abi.SfaSharedkvArgs(
+            dtype=_dtype_code(q), q_layout=layout, B=B, Sq=Sq, N1=N1, N2=1, D=D, Dr=Dr,
+            scale=self.scale, q=q.data_ptr(), q_rope=q_rope.data_ptr(),
+            seqused_kv=seqused_kv.data_ptr(), out=self.out.data_ptr(), lse=self.lse.data_ptr(),
+            **extra)
+        nb = ctypes.c_size_t()
+        _abi.call(lib.sfa_sharedkv_fwd_workspace_size, ctypes.byref(self.a), ctypes.byref(nb))
+        self.ws = _workspace(nb.value, dev)
+
+    def fwd(self):
+        _abi.call(lib.sfa_sharedkv_fwd, ctypes.byref(self.a), _ptr(self.ws),
+                  ctypes.c_size_t(self.ws.numel()), _stream())
+        return self.out, self.lse
+
+
+def sfa_sharedkv_fwd(q, q_rope, seqused_kv, ori=None, cmp=None, scale=None, win_left=127,
+                     win_right=0, cmp_ratio=4, cu_seqlens_q=None):
+    """Shared-KV two-branch sparse decode: returns (out, lse)."""
+    return SfaSharedkvPlan(q, q_rope, seqused_kv, ori, cmp, scale, win_left, win_right,
+                           cmp_ratio, cu_seqlens_q).fwd()
+

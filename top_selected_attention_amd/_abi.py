@@ -18,6 +18,7 @@ EXPORTS = [
     "nsa_select_fwd_workspace_size", "nsa_select_fwd", "nsa_select_bwd_workspace_size",
     "nsa_select_bwd", "nsa_compact_blocks_total", "nsa_compact_workspace_size", "nsa_compact",
     "sfa_paged_fwd_workspace_size", "sfa_paged_fwd",
+    "sfa_sharedkv_fwd_workspace_size", "sfa_sharedkv_fwd",
 ]
 
 
@@ -93,7 +94,26 @@ class SfaArgs(ctypes.Structure):
     ] + TRAIL + [("T", c_int32), ("cu_seqlens_q", POINTER(c_int32))]
 
 
-ARG_STRUCTS = [BsaFwdArgs, BsaBwdArgs, NsaFwdArgs, NsaBwdArgs, SfaArgs]
+class SfaSharedkvArgs(ctypes.Structure):
+    _fields_ = [
+        ("dtype", c_int32), ("q_layout", c_int32), ("B", c_int32), ("Sq", c_int32),
+        ("T", c_int32), ("N1", c_int32), ("N2", c_int32), ("D", c_int32), ("Dr", c_int32),
+        ("scale", c_float), ("q", c_void_p), ("q_rope", c_void_p),
+        ("cu_seqlens_q", POINTER(c_int32)), ("seqused_kv", c_void_p),
+        ("has_ori_kv", c_int32), ("has_cmp_kv", c_int32),
+        ("ori_win_left", c_int32), ("ori_win_right", c_int32),
+        ("ori_num_pages", c_int32), ("ori_page_size", c_int32), ("ori_max_pages", c_int32),
+        ("ori_key_cache", c_void_p), ("ori_key_rope_cache", c_void_p),
+        ("ori_block_table", c_void_p),
+        ("cmp_ratio", c_int32), ("cmp_topk", c_int32),
+        ("cmp_num_pages", c_int32), ("cmp_page_size", c_int32), ("cmp_max_pages", c_int32),
+        ("cmp_key_cache", c_void_p), ("cmp_key_rope_cache", c_void_p),
+        ("cmp_block_table", c_void_p), ("cmp_topk_indices", c_void_p),
+        ("out", c_void_p), ("lse", c_void_p),
+    ] + TRAIL
+
+
+ARG_STRUCTS = [BsaFwdArgs, BsaBwdArgs, NsaFwdArgs, NsaBwdArgs, SfaArgs, SfaSharedkvArgs]
 
 _lib = None
 
@@ -117,6 +137,7 @@ def load(path):
         "nsa_compact_blocks_total": [P, P], "nsa_compact_workspace_size": [P, P],
         "nsa_compact": [P, P, P, P, P, P, c_size_t, P],
         "sfa_paged_fwd_workspace_size": [P, P], "sfa_paged_fwd": [P, P, c_size_t, P],
+        "sfa_sharedkv_fwd_workspace_size": [P, P], "sfa_sharedkv_fwd": [P, P, c_size_t, P],
     }
     for name, args in sig.items():
         f = getattr(lib, name)

@@ -483,6 +483,117 @@ SfaParams sfa_params(const sfa_paged_fwd_args* a) {
   return p;
 }
 
+// ----- shared-KV two-branch decode --------------------------------------------
+
+long skv_tokens(const sfa_sharedkv_fwd_args* a) {
+  return a->q_layout == TSA_LAYOUT_TND ? (long)a->T : (long)a->B * a->Sq;
+}
+
+bool skv_page_ok(int page, int pages, int max_pages) {
+  return page >= 16 && page <= 1024 && page % 16 == 0 && pages >= 1 && max_pages >= 1 &&
+         fits_i32((long)pages * page);
+}
+
+int check_sfa_sharedkv(const sfa_sharedkv_fwd_args* a) {
+  if (!a) return TSA_ERR_NULL;
+  if (a->dtype != TSA_BF16 && a->dtype != TSA_FP16) return TSA_ERR_INVALID;
+  if (a->q_layout != TSA_LAYOUT_BSND && a->q_layout != TSA_LAYOUT_TND) return TSA_ERR_INVALID;
+  if (a->B < 0 || a->Sq < 0) return TSA_ERR_INVALID;
+  if (a->q_layout == TSA_LAYOUT_TND) {
+    if (!a->cu_seqlens_q) return TSA_ERR_NULL;
+    if (a->T < 0 || a->cu_seqlens_q[0] != 0 || a->cu_seqlens_q[a->B] != a->T)
+      return TSA_ERR_INVALID;
+    for (int b = 0; b < a->B; b++)
+      if (a->cu_seqlens_q[b + 1] < a->cu_seqlens_q[b]) return TSA_ERR_INVALID;
+  }
+  // "SparseAttnSharedkvMetadata", parameter list: num_heads_kv 1; the SFA
+  // constraints: N1 a power of two <= 128, D 512, Dr 64.
+  if (a->N1 < 1 || a->N1 > 128 || (a->N1 & (a->N1 - 1))) return TSA_ERR_INVALID;
+  if (a->N2 != 1) return TSA_ERR_UNSUPPORTED;
+  if (a->D != 512 || a->Dr != 64) return TSA_ERR_INVALID;
+  if (!std::isfinite(a->scale) || !(a->scale > 0.f)) return TSA_ERR_INVALID;
+  if ((a->has_ori_kv != 0 && a->has_ori_kv != 1) || (a->has_cmp_kv != 0 && a->has_cmp_kv != 1) ||
+      !(a->has_ori_kv || a->has_cmp_kv))
+    return TSA_ERR_INVALID;
+  if (a->has_ori_kv) {
+    if (a->ori_win_left < 0 || a->ori_win_right < 0 ||
+        (long)a->ori_win_left + a->ori_win_right + 1 > 4096)
+      return TSA_ERR_INVALID;
+    if (!skv_page_ok(a->ori_page_size, a->ori_num_pages, a->ori_max_pages)) return TSA_ERR_INVALID;
+  }
+  if (a->has_cmp_kv) {
+    // cmp_ratio: the parameter list's range, 4 or 128
+    if (a->cmp_ratio != 4 && a->cmp_ratio != 128) return TSA_ERR_INVALID;
+    if (a->cmp_topk < 1) return TSA_ERR_INVALID;
+    if (!skv_page_ok(a->cmp_page_size, a->cmp_num_pages, a->cmp_max_pages)) return TSA_ERR_INVALID;
+  }
+  const long tok = skv_tokens(a);
+  if (!fits_i32(tok * a->N1 * a->D) || !fits_i32(tok * (a->has_cmp_kv ? a->cmp_topk : 1)) ||
+      !fits_i32((long)a->B * (a->has_ori_kv ? a->ori_max_pages : 1)) ||
+      !fits_i32((long)a->B * (a->has_cmp_kv ? a->cmp_max_pages : 1)))
+    return TSA_ERR_INVALID;
+  if (tok > 0) {
+    if (!a->q || !a->q_rope || !a->out || !a->seqused_kv) return TSA_ERR_NULL;
+    if (a->has_ori_kv && (!a->ori_key_cache || !a->ori_key_rope_cache || !a->ori_block_table))
+      return TSA_ERR_NULL;
+    if (a->has_cmp_kv && (!a->cmp_key_cache || !a->cmp_key_rope_cache || !a->cmp_block_table ||
+                          !a->cmp_topk_indices))
+      return TSA_ERR_NULL;
+  }
+  return TSA_OK;
+}
+
+SfaParams skv_params(const sfa_sharedkv_fwd_args* a) {
+  SfaParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.q = a->q; p.q_rope = a->q_rope; p.out = a->out; p.lse = a->lse;
+  p.kv_lens = a->seqused_kv;
+  p.B = a->B; p.Sq = a->Sq; p.N1 = a->N1; p.N2 = 1; p.D = a->D; p.Dr = a->Dr; p.Dv = a->D;
+  p.ntok = skv_tokens(a);
+  p.sbs = 1;
+  p.causal = 1;  // top-k slots: rightDownCausal in compressed positions
+  p.scale = a->scale;
+  if (a->has_ori_kv) {
+    p.kc = a->ori_key_cache; p.krc = a->ori_key_rope_cache; p.vc = a->ori_key_cache;
+    p.block_table = a->ori_block_table;
+    p.num_pages = a->ori_num_pages; p.page = a->ori_page_size; p.max_pages = a->ori_max_pages;
+    p.win_left = a->ori_win_left;
+    p.win_len = a->ori_win_left + a->ori_win_right + 1;
+    p.win_pad = (p.win_len + 31) / 32 * 32;
+  }
+  p.cmp_ratio = 1;
+  if (a->has_cmp_kv) {
+    p.ckc = a->cmp_key_cache; p.ckrc = a->cmp_key_rope_cache; p.cbt = a->cmp_block_table;
+    p.c_num_pages = a->cmp_num_pages; p.c_page = a->cmp_page_size;
+    p.c_max_pages = a->cmp_max_pages; p.cmp_ratio = a->cmp_ratio;
+    p.topk = a->cmp_topk_indices; p.topk_n = a->cmp_topk;
+    if (!a->has_ori_kv) {  // no band: the one cache fields point at the compressed cache
+      p.kc = p.ckc; p.krc = p.ckrc; p.vc = p.ckc; p.block_table = p.cbt;
+      p.num_pages = p.c_num_pages; p.page = p.c_page; p.max_pages = p.c_max_pages;
+    }
+  }
+  p.splits = sfa_splits(p);
+  return p;
+}
+
+size_t skv_carve(const SfaParams& p, void* ws, SfaParams* out) {
+  Carver c(ws);
+  const long tok = p.ntok;
+  float* po = c.take<float>(tok * p.splits * p.N1 * p.Dv);
+  float* pl = c.take<float>(tok * p.splits * p.N1);
+  int* cu = c.take<int>(p.B + 1);
+  int* task = c.take<int>(2 * tok * p.splits);
+  if (out) {
+    *out = p;
+    out->part_o = po;
+    out->part_lse = pl;
+    out->cu_q = nullptr;
+    out->cu_dev = cu;
+    out->task = task;
+  }
+  return c.off + kAlign;
+}
+
 size_t sfa_carve(const SfaParams& p, void* ws, SfaParams* out) {
   Carver c(ws);
   const long tok = p.ntok;
@@ -528,6 +639,7 @@ size_t tsa_args_sizeof(int which) {
     case 2: return sizeof(nsa_select_fwd_args);
     case 3: return sizeof(nsa_select_bwd_args);
     case 4: return sizeof(sfa_paged_fwd_args);
+    case 5: return sizeof(sfa_sharedkv_fwd_args);
     default: return 0;
   }
 }
@@ -815,6 +927,36 @@ int sfa_paged_fwd(const sfa_paged_fwd_args* a, void* ws, size_t ws_bytes, void* 
   }
   const StageTimer tm = timer_of(a, st);
   return hip_status(launch_sfa_fwd(p, a->dtype == TSA_FP16, st, tm.ev, tm.n));
+}
+
+// ----- shared-KV two-branch decode -------------------------------------------
+
+int sfa_sharedkv_fwd_workspace_size(const sfa_sharedkv_fwd_args* a, size_t* bytes) {
+  if (!bytes) return TSA_ERR_NULL;
+  int s = check_sfa_sharedkv(a);
+  if (s) return s;
+  *bytes = skv_carve(skv_params(a), nullptr, nullptr);
+  return TSA_OK;
+}
+
+int sfa_sharedkv_fwd(const sfa_sharedkv_fwd_args* a, void* ws, size_t ws_bytes, void* stream) {
+  size_t need;
+  int s = sfa_sharedkv_fwd_workspace_size(a, &need);
+  if (s) return s;
+  if (!ws || ws_bytes < need) return TSA_ERR_WORKSPACE;
+  if (skv_tokens(a) == 0) return TSA_OK;
+  hipStream_t st = (hipStream_t)stream;
+  SfaParams p;
+  skv_carve(skv_params(a), ws, &p);
+  if (a->q_layout == TSA_LAYOUT_TND) {
+    // the copy from pageable memory is staged before hipMemcpyAsync returns
+    if (hipMemcpyAsync(p.cu_dev, a->cu_seqlens_q, sizeof(int) * (a->B + 1),
+                       hipMemcpyHostToDevice, st) != hipSuccess)
+      return TSA_ERR_HIP;
+    p.cu_q = p.cu_dev;
+  }
+  const StageTimer tm = timer_of(a, st);
+  return hip_status(launch_sfa_sharedkv(p, a->dtype == TSA_FP16, st, tm.ev, tm.n));
 }
 
 }  // extern "C"

@@ -102,9 +102,22 @@ __global__ __launch_bounds__(512) void sfa_split_kernel(SfaParams p, int n_items
 
   const int kv_len = p.kv_lens[b];
   const int qpos = kv_len - sq + s;
-  const int total = p.topk_n * p.sbs;
-  const int slot_lo = sp * per_split;
-  const int slot_hi = min(slot_lo + per_split, total);
+  const int total = sfa_total_slots(p);
+  int slot_lo = sp * per_split;
+  int slot_hi = min(slot_lo + per_split, total);
+  if (p.task) {
+    slot_lo = p.task[2 * (tk * p.splits + sp)];
+    slot_hi = p.task[2 * (tk * p.splits + sp) + 1];
+  }
+  // the top-k slots' cache, length and causal bound: the compressed cache in
+  // the shared-KV decode, else the one cache
+  const bool skv = p.ckc != nullptr;
+  const int t_len = skv ? kv_len / p.cmp_ratio : kv_len;
+  const int t_qpos = skv ? t_len - sq + s : qpos;
+  const int t_page = skv ? p.c_page : p.page;
+  const int t_maxp = skv ? p.c_max_pages : p.max_pages;
+  const int t_nump = skv ? p.c_num_pages : p.num_pages;
+  const int* t_btab = skv ? p.cbt + (long)b * p.c_max_pages : p.block_table + (long)b * p.max_pages;
 
   const int hbase = hg * 64 + h2 * 32;  // heads hbase + 16*hh + l16, hh = 0, 1
   const int* topk = p.topk + (long)tk * p.topk_n;  // N2 = 1
@@ -134,27 +147,40 @@ __global__ __launch_bounds__(512) void sfa_split_kernel(SfaParams p, int n_items
   auto fill_table = [&](int seg_lo, int seg_n) {
     constexpr int R = kTab / 512;
     int id[R];
+    bool band[R];
 #pragma unroll
     for (int i = 0; i < R; i++) {
       const int t = tid + 512 * i;
-      id[i] = t < seg_n ? topk[(seg_lo + t) / p.sbs] : -1;
+      const int gs = seg_lo + t;  // slot of the token
+      band[i] = gs < p.win_pad;
+      id[i] = t >= seg_n ? -1 : (band[i] ? 0 : topk[(gs - p.win_pad) / p.sbs]);
     }
-    int lp[R], pos[R];
+    int lp[R], pos[R], pg[R];
     bool ok[R];
 #pragma unroll
     for (int i = 0; i < R; i++) {
       const int t = tid + 512 * i;
-      pos[i] = id[i] * p.sbs + (seg_lo + t) % p.sbs;
-      ok[i] = t < seg_n && id[i] >= 0 && pos[i] < kv_len && (!p.causal || pos[i] <= qpos);
-      lp[i] = ok[i] ? min(pos[i] / p.page, p.max_pages - 1) : 0;
+      const int gs = seg_lo + t;
+      if (band[i]) {
+        pos[i] = qpos - p.win_left + gs;
+        ok[i] = t < seg_n && gs < p.win_len && pos[i] >= 0 && pos[i] < kv_len;
+        pg[i] = p.page;
+        lp[i] = ok[i] ? min(pos[i] / p.page, p.max_pages - 1) : 0;
+      } else {
+        pos[i] = id[i] * p.sbs + (gs - p.win_pad) % p.sbs;
+        ok[i] = t < seg_n && id[i] >= 0 && pos[i] < t_len && (!p.causal || pos[i] <= t_qpos);
+        pg[i] = t_page;
+        lp[i] = ok[i] ? min(pos[i] / t_page, t_maxp - 1) : 0;
+      }
     }
     int phys[R];
 #pragma unroll
-    for (int i = 0; i < R; i++) phys[i] = ok[i] ? btab[lp[i]] : 0;
+    for (int i = 0; i < R; i++) phys[i] = ok[i] ? (band[i] ? btab[lp[i]] : t_btab[lp[i]]) : 0;
 #pragma unroll
     for (int i = 0; i < R; i++) {
       const int t = tid + 512 * i;  // lanes 0..31 and 32..63 each cover one chunk
-      const int row = ok[i] ? min(max(phys[i], 0), p.num_pages - 1) * p.page + pos[i] % p.page : 0;
+      const int np = band[i] ? p.num_pages : t_nump;
+      const int row = ok[i] ? min(max(phys[i], 0), np - 1) * pg[i] + pos[i] % pg[i] : 0;
       const unsigned long long bal = __ballot(ok[i]);
       const unsigned half = lane < 32 ? (unsigned)bal : (unsigned)(bal >> 32);
       const int first = (half ? __builtin_ctz(half) : 0) + (lane & 32);
@@ -163,10 +189,13 @@ __global__ __launch_bounds__(512) void sfa_split_kernel(SfaParams p, int n_items
       if ((lane & 31) == 0) lds_cmask[t >> 5] = half;
     }
   };
-  // 8 waves x 4 one-KB key rows, and waves 0..3 one 1-KB slice of 8 rope rows
+  // 8 waves x 4 one-KB key rows, and waves 0..3 one 1-KB slice of 8 rope rows;
+  // a chunk past the band reads the top-k slots' cache
+  int seg_base = 0;  // first slot of the segment being gathered
   auto load_chunk = [&](int c, int buf) {
-    const char* kc = (const char*)p.kc;
-    const char* krc = (const char*)p.krc;
+    const bool tk_cache = skv && seg_base + c * kKeys >= p.win_pad;
+    const char* kc = (const char*)(tk_cache ? p.ckc : p.kc);
+    const char* krc = (const char*)(tk_cache ? p.ckrc : p.krc);
     const int* tb = lds_tab + c * kKeys;
     const int4 rm = *reinterpret_cast<const int4*>(tb + wid * 4);  // same for all lanes
     const int rms[4] = {rm.x, rm.y, rm.z, rm.w};
@@ -199,6 +228,7 @@ __global__ __launch_bounds__(512) void sfa_split_kernel(SfaParams p, int n_items
     const int seg_n = min(kTab, slot_hi - seg_lo);
     const int nchunks = (seg_n + kKeys - 1) / kKeys;
     __syncthreads();  // the previous segment's table and tiles are no longer read
+    seg_base = seg_lo;
     fill_table(seg_lo, seg_n);
     __syncthreads();
 #pragma unroll
@@ -396,7 +426,7 @@ int sfa_splits(const SfaParams& p) {
   const long tokens = p.ntok;
   const int hgroups = (p.N1 + 63) / 64;
   const long wgs = tokens * hgroups;
-  const int total = p.topk_n * p.sbs;
+  const int total = sfa_total_slots(p);
   if (wgs == 0) return 1;
   // aim for >= 256 workgroups (one resident per CU), at least 4 chunks per split
   long s = (256 + wgs - 1) / wgs;
@@ -418,7 +448,7 @@ template <class E>
 static hipError_t sfa_t(const SfaParams& p, hipStream_t st, void* const* ev, int n_ev) {
   const long tokens = p.ntok;
   const int hgroups = (p.N1 + 63) / 64;
-  const int total = p.topk_n * p.sbs;
+  const int total = sfa_total_slots(p);
   const int per_split = ((total + p.splits - 1) / p.splits + kKeys - 1) / kKeys * kKeys;
   const long n_items = tokens * p.splits * hgroups;
   hipError_t e = mark_event(ev, n_ev, 0, 0, st);
@@ -436,6 +466,86 @@ static hipError_t sfa_t(const SfaParams& p, hipStream_t st, void* const* ev, int
     e = hipGetLastError();
   }
   if (e == hipSuccess) e = mark_event(ev, n_ev, 1, 1, st);
+  return e;
+}
+
+// Shared-KV task list ("SparseAttnSharedkvMetadata": a per-core list of
+// attention tasks with their start and end points): one wave per decode
+// token.  Each 32-slot chunk of the token's slots weighs its kept keys plus a
+// fixed cost for the gather and barrier it always takes; the chunks are cut
+// into p.splits contiguous ranges of near-equal weight (split k starts at the
+// first chunk whose inclusive weight prefix exceeds k / splits of the total)
+// and written as slot ranges, so each split workgroup gets a similar number
+// of kept keys whatever the band clipping and empty top-k slots.
+__global__ __launch_bounds__(256) void sfa_task_kernel(SfaParams p) {
+  constexpr int kChunkCost = 4;
+  const long tk = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (tk >= p.ntok) return;
+  int b, s, sq;
+  sfa_token(p, (int)tk, b, s, sq);
+  const int kv_len = p.kv_lens[b];
+  const int qpos = kv_len - sq + s;
+  const int t_len = kv_len / p.cmp_ratio;
+  const int t_qpos = t_len - sq + s;
+  const int total = sfa_total_slots(p);
+  const int nch = (total + kKeys - 1) / kKeys;
+  const int* topk = p.topk + tk * p.topk_n;
+  auto weight = [&](int c) {
+    if (c >= nch) return 0;
+    const int lo = c * kKeys, hi = min(lo + kKeys, total);
+    int kept = 0;
+    if (lo < p.win_pad) {  // band slots i keep position qpos - win_left + i in [0, kv_len)
+      const int a = max(lo, p.win_left - qpos);
+      const int e = min(min(hi, p.win_len), kv_len - qpos + p.win_left);
+      kept = max(0, e - a);
+    } else {
+      for (int j = lo; j < hi; j++) {
+        const int id = topk[(j - p.win_pad) / p.sbs];
+        const int pos = id * p.sbs + (j - p.win_pad) % p.sbs;
+        kept += id >= 0 && pos < t_len && pos <= t_qpos;
+      }
+    }
+    return kept + kChunkCost;
+  };
+  long wsum = 0;
+  for (int c0 = 0; c0 < nch; c0 += 64) {
+    int w = weight(c0 + lane);
+    for (int o = 32; o > 0; o >>= 1) w += __shfl_xor(w, o);
+    wsum += w;
+  }
+  int cnt = 0;  // lane k: chunks whose inclusive prefix * splits <= k * wsum
+  long carry = 0;
+  for (int c0 = 0; c0 < nch; c0 += 64) {
+    const int c = c0 + lane;
+    long incl = wave_incl_scan(weight(c)) + carry;
+    for (int k = 1; k < p.splits; k++) {
+      const unsigned long long bal = __ballot(c < nch && incl * p.splits <= (long)k * wsum);
+      if (lane == k) cnt += __popcll(bal);
+    }
+    carry = __shfl(incl, 63);
+  }
+  const int nxt = __shfl(cnt, (lane + 1) & 63);
+  if (lane < p.splits) {
+    const int clo = lane == 0 ? 0 : cnt;
+    const int chi = lane + 1 == p.splits ? nch : nxt;
+    int* t = p.task + 2 * (tk * p.splits + lane);
+    t[0] = min(clo * kKeys, total);
+    t[1] = min(max(chi, clo) * kKeys, total);
+  }
+}
+
+hipError_t launch_sfa_sharedkv(const SfaParams& p, int fp16, hipStream_t st, void* const* ev,
+                               int n_ev) {
+  hipError_t e = mark_event(ev, n_ev, 0, 0, st);
+  if (e == hipSuccess) {
+    hipLaunchKernelGGL(sfa_task_kernel, dim3((unsigned)((p.ntok + 3) / 4)), dim3(256), 0, st, p);
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess) e = mark_event(ev, n_ev, 0, 1, st);
+  // the split / combine stages are timed as stages 1 and 2
+  void* const* ev2 = n_ev > 1 ? ev + 2 : nullptr;
+  if (e == hipSuccess) e = fp16 ? sfa_t<FP16>(p, st, ev2, n_ev - 1) : sfa_t<BF16>(p, st, ev2, n_ev - 1);
   return e;
 }
 

@@ -196,9 +196,30 @@ struct SfaParams {
   int causal;
   int splits;
   float scale;
+  // Shared-KV two-branch decode (null ckc: plain SFA).  A token's slots
+  // [0, win_pad) are the band over the cache above (kc, block_table, page):
+  // slot i is position qpos - win_left + i, kept for i < win_len inside
+  // [0, kv_len); slots [win_pad, win_pad + topk_n) are topk's compressed ids
+  // in the compressed cache (ckc / ckrc / cbt), kv_len / cmp_ratio entries,
+  // rightDownCausal in compressed positions.  win_pad is a multiple of 32,
+  // so no 32-slot chunk mixes the two caches.
+  int win_pad, win_len, win_left;
+  const void* ckc;
+  const void* ckrc;
+  const int* cbt;
+  int c_page, c_max_pages, c_num_pages, cmp_ratio;
+  // Slot range [task[2i], task[2i+1]) of split i = tk * splits + sp, or null
+  // for equal slot ranges.
+  int* task;
 };
 
 int sfa_splits(const SfaParams& p);
+// slots per decode token: the band (padded) plus the top-k entries
+__host__ __device__ inline int sfa_total_slots(const SfaParams& p) { return p.win_pad + p.topk_n * p.sbs; }
+// The shared-KV task list (metadata kernel), then the split and combine
+// kernels: stage 0 = task list, 1 = split attention, 2 = combine.
+hipError_t launch_sfa_sharedkv(const SfaParams& p, int fp16, hipStream_t st, void* const* ev,
+                               int n_ev);
 // stage 0 = split attention, stage 1 = combine
 hipError_t launch_sfa_fwd(const SfaParams& p, int fp16, hipStream_t st, void* const* ev, int n_ev);
 hipError_t launch_sfa_check(const SfaParams& p, hipStream_t st);
