@@ -44,7 +44,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--workload", default="bsa_causal_8k",
                     choices=["bsa_causal_8k", "bsa_small", "bsa_window_128k", "bsa_tnd_varlen",
-                             "nsa_varlen", "sfa_decode"])
+                             "nsa_varlen", "sfa_decode", "sfa_sharedkv_decode"])
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the measured GEMM / copy peaks reported beside the published ones")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -408,6 +408,40 @@ def _sfa_bytes(idx, kv_lens, B, Sq, N1, D, Dr, Dv):
     return rows * (D + Dr) * 2 + B * Sq * per_tok
 
 
+def _time_forward(plan, n_stages, args):
+    """Warm-up, K plain forward calls timed by the wall clock between
+    synchronisations (the throughput), then K more with events around each
+    stage on the library's stream, then five cache-cold calls.  Returns (ms
+    per plain step, ms per instrumented step, [mean ms of each stage], per-step
+    event ms, median cold ms)."""
+    import torch
+    K = args.steps
+    for _ in range(args.warmup):
+        plan.fwd()
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for _ in range(K):
+        plan.fwd()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - wall0) * 1e3 / K
+    # a second run of K steps with stage events (kept out of the throughput)
+    evs = [_events(2 * n_stages) for _ in range(K)]
+    arrs = [_ev_array(e) for e in evs]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(K):
+        plan.a.n_events = n_stages
+        plan.a.events = ctypes.cast(arrs[i], ctypes.POINTER(ctypes.c_void_p))
+        plan.fwd()
+    torch.cuda.synchronize()
+    ms_ev = (time.perf_counter() - wall0) * 1e3 / K
+    plan.a.n_events = 0
+    step_ms = [e[0].elapsed_time(e[2 * n_stages - 1]) for e in evs]
+    stages = [sum(e[2 * j].elapsed_time(e[2 * j + 1]) for e in evs) / K for j in range(n_stages)]
+    cold_ms = _cold_steps(plan.fwd)
+    return ms_step, ms_ev, stages, step_ms, cold_ms
+
+
 def bench_sfa(args):
     import torch
     import workloads as W
@@ -423,29 +457,7 @@ def bench_sfa(args):
     nbytes = _sfa_bytes(idx, kv_lens, w["B"], w["Sq"], w["N1"], w["D"], w["Dr"], w["D"])
     flops = 2.0 * w["B"] * w["Sq"] * w["N1"] * w["topk"] * ((w["D"] + w["Dr"]) + w["D"])
     K = args.steps
-    for _ in range(args.warmup):
-        plan.fwd()
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    for _ in range(K):
-        plan.fwd()
-    torch.cuda.synchronize()
-    ms_step = (time.perf_counter() - wall0) * 1e3 / K
-    # a second run of K steps with stage events (kept out of the throughput)
-    evs = [_events(4) for _ in range(K)]
-    arrs = [_ev_array(e) for e in evs]
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    for i in range(K):
-        plan.a.n_events, plan.a.events = 2, ctypes.cast(arrs[i], ctypes.POINTER(ctypes.c_void_p))
-        plan.fwd()
-    torch.cuda.synchronize()
-    ms_ev = (time.perf_counter() - wall0) * 1e3 / K
-    plan.a.n_events = 0
-    step_ms = [e[0].elapsed_time(e[3]) for e in evs]
-    cold_ms = _cold_steps(plan.fwd)
-    split_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / K
-    comb_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / K
+    ms_step, ms_ev, (split_ms, comb_ms), step_ms, cold_ms = _time_forward(plan, 2, args)
     gbs = nbytes / (ms_step * 1e-3) / 1e9
     kgbs = nbytes / (split_ms * 1e-3) / 1e9
     res = {
@@ -488,6 +500,109 @@ def cpu_baseline_sfa(ctx, seconds):
     return {"value": round(per_tok * done / el / 1e9, 4), "unit": "GB/s", "cores": _threads(),
             "kind": "oracle",
             "sample": f"{done} of {len(tokens)} decode tokens (float64) of {w['name']}, {el:.1f} s"}
+
+
+def _skv_bytes_and_keys(cu, kv_lens, idx, w):
+    """Algorithmic HBM bytes of the shared-KV decode: per sequence the union of
+    its tokens' band rows and the union of their kept compressed rows (key +
+    rope row each; the value row is the key row), plus per token Q, q_rope, O,
+    LSE, the top-k ids and one page-table entry per slot.  Also the kept keys
+    summed over tokens (for the FLOP count)."""
+    D, Dr, N1, K = w["D"], w["Dr"], w["N1"], w["cmp_topk"]
+    win = w["win_left"] + w["win_right"] + 1
+    rows, kept = 0, 0
+    for b in range(len(kv_lens)):
+        n, sq = int(kv_lens[b]), int(cu[b + 1] - cu[b])
+        cl = n // w["cmp_ratio"]
+        band, ids = set(), set()
+        for s in range(sq):
+            p = n - sq + s
+            pos = range(max(0, p - w["win_left"]), min(n, p + w["win_right"] + 1))
+            band.update(pos)
+            sel = idx[cu[b] + s, 0]
+            sel = sel[(sel >= 0) & (sel < cl) & (sel <= cl - sq + s)]
+            ids.update(sel.tolist())
+            kept += len(pos) + sel.size
+        rows += len(band) + len(ids)
+    T = int(cu[-1])
+    per_tok = N1 * (D + Dr) * 2 + N1 * D * 2 + N1 * 4 + K * 4 + (win + K) * 4
+    return rows * (D + Dr) * 2 + T * per_tok, kept
+
+
+def bench_sfa_skv(args):
+    import torch
+    import workloads as W
+    import top_selected_attention_amd as tsa
+
+    w = W.sfa_sharedkv_workload()
+    cu, q, qr, kv_lens, ori, cmp = W.sfa_sharedkv_inputs()
+    scale = 1.0 / math.sqrt(w["D"] + w["Dr"])
+    dev = torch.device("cuda", 0)
+    ori_d = tuple(torch.as_tensor(t).to(dev) for t in ori)
+    cmp_d = tuple(torch.as_tensor(t).to(dev) for t in cmp)
+    plan = tsa.SfaSharedkvPlan(q.to(dev), qr.to(dev), torch.from_numpy(kv_lens).to(dev), ori_d,
+                               cmp_d, scale, w["win_left"], w["win_right"], w["cmp_ratio"],
+                               cu_seqlens_q=cu)
+    nbytes, kept = _skv_bytes_and_keys(cu, kv_lens, cmp[3], w)
+    flops = 2.0 * w["N1"] * kept * ((w["D"] + w["Dr"]) + w["D"])
+    K = args.steps
+    ms_step, ms_ev, (task_ms, split_ms, comb_ms), step_ms, cold_ms = _time_forward(plan, 3, args)
+    # every layer of a decode step after the first reuses one task list
+    plan.metadata()
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for _ in range(K):
+        plan.fwd()
+    torch.cuda.synchronize()
+    ms_reuse = (time.perf_counter() - wall0) * 1e3 / K
+    gbs = nbytes / (ms_step * 1e-3) / 1e9
+    kgbs = nbytes / (split_ms * 1e-3) / 1e9
+    res = {
+        "metric": "GB/s of algorithmic HBM bytes (band + compressed top-k gather) and % of HBM "
+                  "peak",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w["dtype"], "data": "synthetic",
+        "config": {"workload": w["name"], "layout_q": "TND", "B": w["B"], "Sq": w["Sq"],
+                   "N1": w["N1"], "N2": 1, "D": w["D"], "Dr": w["Dr"], "page": w["page"],
+                   "kv_len": w["kv_len"], "win_left": w["win_left"], "win_right": w["win_right"],
+                   "cmp_ratio": w["cmp_ratio"], "cmp_topk": w["cmp_topk"]},
+        "pct_of_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
+        "effective_tflops": round(flops / (ms_step * 1e-3) / 1e12, 2),
+        "stage_ms": {"task_list": round(task_ms, 4), "split_attention": round(split_ms, 4),
+                     "combine": round(comb_ms, 4)},
+        "ms_per_step_reusing_task_list": round(ms_reuse, 4),
+        "ms_per_step_instrumented": round(ms_ev, 4),
+        "step_ms_events": _step_stats(step_ms),
+        "ms_per_step_cold": round(cold_ms, 4),
+        "algorithmic_bytes": int(nbytes),
+        "roofline": {"kernel": "sfa_split_kernel", "bound": "hbm", "achieved": round(kgbs, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(kgbs / PEAK_HBM_GBS, 4),
+                     "traffic": _traffic(w["name"], "sfa_split_kernel")},
+    }
+    return res, (w, cu, q, qr, kv_lens, ori, cmp, scale, nbytes)
+
+
+def cpu_baseline_sfa_skv(ctx, seconds):
+    import oracle
+    w, cu, q, qr, kv_lens, ori, cmp, scale, nbytes = ctx
+    f = lambda t: t.float().numpy() if hasattr(t, "float") else t  # noqa: E731
+    qn, qrn = q.float().numpy(), qr.float().numpy()
+    orin, cmpn = tuple(f(t) for t in ori), tuple(f(t) for t in cmp)
+    T = int(cu[-1])
+    done = 0
+    t0 = time.perf_counter()
+    for t in range(T):
+        oracle.sfa_sharedkv_fwd(qn, qrn, cu, kv_lens, scale, ori=orin, cmp=cmpn,
+                                win_left=w["win_left"], win_right=w["win_right"],
+                                cmp_ratio=w["cmp_ratio"], tokens=[t])
+        done += 1
+        if time.perf_counter() - t0 > seconds:
+            break
+    el = time.perf_counter() - t0
+    return {"value": round(nbytes / T * done / el / 1e9, 4), "unit": "GB/s", "cores": _threads(),
+            "kind": "oracle",
+            "sample": f"{done} of {T} decode tokens (float64) of {w['name']}, {el:.1f} s"}
 
 
 def _flush_buffer():
@@ -788,6 +903,10 @@ def main():
         res, ctx = bench_nsa(args)
         if args.cpu_seconds > 0:
             res["cpu_baseline"] = cpu_baseline_nsa(ctx, args.cpu_seconds)
+    elif args.workload == "sfa_sharedkv_decode":
+        res, ctx = bench_sfa_skv(args)
+        if args.cpu_seconds > 0:
+            res["cpu_baseline"] = cpu_baseline_sfa_skv(ctx, args.cpu_seconds)
     else:
         res, ctx = bench_sfa(args)
         if args.cpu_seconds > 0:

@@ -407,12 +407,19 @@ TSA_API int sfa_paged_fwd(const sfa_paged_fwd_args* args, void* workspace, size_
  * cmp_topk] (-1 = empty); out like q with 512 columns; lse fp32 [tokens, N1]
  * (may be NULL).  A token with no kept key gets Out = 0, LSE = -inf.
  *
- * A metadata kernel first writes the task list in the workspace: each
- * token's slots (the band padded to a multiple of 32, then the top-k slots)
- * are cut into per-workgroup slot ranges of near-equal kept-key weight; the
- * split kernel takes its range from that list and the combine kernel merges
- * the ranges by LSE.  Stages: 0 = task list, 1 = split attention, 2 =
- * combine.
+ * Task list (the metadata page's per-core list of tasks with their start
+ * and end points): sfa_sharedkv_metadata writes, into a caller buffer of
+ * sfa_sharedkv_metadata_size bytes, each token's batch entry and its slots
+ * (the band padded to a multiple of 32, then the top-k slots) cut into
+ * per-workgroup slot ranges of near-equal kept-key weight.  sfa_sharedkv_fwd
+ * takes such a list in `tasks` (DEVICE) and then uploads and computes
+ * nothing before the attention; with tasks == NULL it makes the list itself
+ * in its workspace first.  A list made for the same shapes, cu_seqlens_q,
+ * band and cmp_topk is valid for any ids and seqused_kv (those only steer
+ * the balance), so one list can serve every layer of a decode step.  The
+ * split kernel takes its range from the list and the combine kernel merges
+ * the ranges by LSE.  Stages: 0 = task list (recorded back to back when
+ * `tasks` is given), 1 = split attention, 2 = combine.
  * Constraints: N1 a power of two <= 128; D 512, Dr 64; page sizes multiples
  * of 16 <= 1024; cmp_ratio 4 or 128 (the parameter list's range);
  * ori_win_left, ori_win_right >= 0 with their band <= 4096 slots;
@@ -443,11 +450,20 @@ typedef struct {
   const int32_t* cmp_topk_indices;       /* DEVICE */
   void* out;                    /* DEVICE, written */
   float* lse;                   /* DEVICE, written, or NULL */
+  const void* tasks;            /* DEVICE task list from sfa_sharedkv_metadata, or NULL */
   int32_t reuse_lists;          /* unused; keep 0 */
   int32_t n_events;             /* number of stages to time (0 = off) */
   void* const* events;          /* HOST array of 2*n_events hipEvent_t (see above) */
 } sfa_sharedkv_fwd_args;
 
+/* Bytes of the task list of these arguments (validates them like the
+ * forward; `tasks` is not read). */
+TSA_API int sfa_sharedkv_metadata_size(const sfa_sharedkv_fwd_args* args, size_t* bytes);
+/* Writes the task list into `tasks` (DEVICE, at least the size above; owned
+ * by the caller), enqueued on `stream`; reads cu_seqlens_q (HOST, TND),
+ * seqused_kv and cmp_topk_indices (DEVICE). */
+TSA_API int sfa_sharedkv_metadata(const sfa_sharedkv_fwd_args* args, void* tasks,
+                                  size_t tasks_bytes, void* stream);
 TSA_API int sfa_sharedkv_fwd_workspace_size(const sfa_sharedkv_fwd_args* args, size_t* bytes);
 TSA_API int sfa_sharedkv_fwd(const sfa_sharedkv_fwd_args* args, void* workspace,
                              size_t workspace_bytes, void* stream);

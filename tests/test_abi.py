@@ -296,3 +296,16 @@ def test_sfa_sharedkv_workspace_too_small_is_rejected_before_launch(tsa):
     assert s == 0
     assert tsa.lib.sfa_sharedkv_fwd(ctypes.byref(a), ctypes.c_void_p(8), n - 1, None) == 4
 
+
+
+def test_sfa_sharedkv_metadata_size_and_buffer_checks(tsa):
+    a = _skv(tsa)
+    n = ctypes.c_size_t()
+    assert tsa.lib.sfa_sharedkv_metadata_size(ctypes.byref(a), ctypes.byref(n)) == 0
+    # 128 tokens: prefix sums (padded) + 4 ints of token entry + 2 per split range
+    assert n.value % 4 == 0 and n.value >= 4 * (36 + 128 * 4 + 128 * 2)
+    assert tsa.lib.sfa_sharedkv_metadata(ctypes.byref(a), ctypes.c_void_p(8), n.value - 4,
+                                         None) == 4
+    assert tsa.lib.sfa_sharedkv_metadata(ctypes.byref(a), None, n.value, None) == 4
+    bad = _skv(tsa, N1=48)
+    assert tsa.lib.sfa_sharedkv_metadata_size(ctypes.byref(bad), ctypes.byref(n)) == 2

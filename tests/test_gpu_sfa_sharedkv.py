@@ -112,3 +112,36 @@ def test_workload_full_size_sampled():
     rows = [0, 3, 29, 64, 101, 127]
     _run_case([w["Sq"]] * w["B"], [w["kv_len"]] * w["B"], w["N1"], w["page"], w["cmp_ratio"],
               w["cmp_topk"], 120, rows=rows)
+
+
+def test_task_list_made_once_serves_other_ids():
+    """A task list made by the metadata call for one set of compressed ids
+    serves a forward over other ids (another layer of the decode step): the
+    result matches the oracle for the new ids, and a fresh list gives the
+    same bits as the list made inside the forward."""
+    tsa = _tsa()
+    lens, kv_lens, N1, K = [1, 4, 0, 3], [900, 4000, 70, 2600], 64, 128
+    cu, q, qr, kvl, ori, cmp = W.sfa_sharedkv_inputs(lens=lens, kv_lens=kv_lens, N1=N1, page=64,
+                                                     cmp_ratio=4, cmp_topk=K, seed_base=190)
+    _, _, _, _, _, cmp2 = W.sfa_sharedkv_inputs(lens=lens, kv_lens=kv_lens, N1=N1, page=64,
+                                                cmp_ratio=4, cmp_topk=K, seed_base=200)
+    ori_d = tuple(_dev(t) for t in ori)
+    cmp_d = tuple(_dev(t) for t in cmp)
+    plan = tsa.SfaSharedkvPlan(_dev(q), _dev(qr), _dev(kvl), ori_d, cmp_d, 0.04,
+                               cu_seqlens_q=cu)
+    inline, _ = plan.fwd()
+    inline = inline.clone()
+    plan.metadata()
+    listed, _ = plan.fwd()
+    torch.cuda.synchronize()
+    assert torch.equal(inline, listed)
+    # the other layer's ids, copied into the same id tensor the plan points at
+    cmp_d[3].copy_(_dev(cmp2[3]))
+    out, lse = plan.fwd()
+    torch.cuda.synchronize()
+    f = lambda t: t.float().numpy() if isinstance(t, torch.Tensor) else t  # noqa: E731
+    ro, rl = oracle.sfa_sharedkv_fwd(_np(q), _np(qr), cu, kvl, 0.04, ori=tuple(f(t) for t in ori),
+                                     cmp=tuple(f(t) for t in cmp[:3]) + (cmp2[3],))
+    err, sc = np.abs(_np(out) - ro).max(), np.abs(ro).max()
+    assert err <= OUT_TOL * sc, f"out: {err:.3e} vs {OUT_TOL} * {sc:.3e}"
+    assert np.abs(_np(lse) - rl).max() <= LSE_TOL * max(1.0, np.abs(rl).max())

@@ -469,7 +469,9 @@ class SfaSharedkvPlan:
     host cu_seqlens_q (TND); seqused_kv int32 [B]; ori = (key_cache [P, page,
     1, 512], key_rope_cache [P, page, 1, 64], block_table int32 [B, max_pages])
     or None; cmp = (key_cache, key_rope_cache, block_table, topk int32
-    [tokens, 1, K]) or None.  ``fwd()`` returns (out, lse).
+    [tokens, 1, K]) or None.  ``fwd()`` returns (out, lse).  ``metadata()``
+    makes the task list once (``self.tasks``); later ``fwd()`` calls use it
+    and skip the list kernel, as every layer of a decode step may.
     """
 
     def __init__(self, q, q_rope, seqused_kv, ori=None, cmp=None, scale=None, win_left=127,
@@ -512,7 +514,7 @@ class SfaSharedkvPlan:
                          cmp_topk_indices=idx.data_ptr())
         self.keep = (q, q_rope, seqused_kv, ori, cmp)
         self.scale = 1.0 / math.sqrt(D + Dr) if scale is None else float(scale)
-        dev = q.device
+        dev = self.q_device = q.device
         self.out = torch.empty(tok_shape + (N1, D), dtype=q.dtype, device=dev)
         self.lse = torch.empty(tok_shape + (N1,), dtype=torch.float32, device=dev)
         self.a = _abi.SfaSharedkvArgs(
@@ -523,6 +525,19 @@ class SfaSharedkvPlan:
         nb = ctypes.c_size_t()
         _abi.call(lib.sfa_sharedkv_fwd_workspace_size, ctypes.byref(self.a), ctypes.byref(nb))
         self.ws = _workspace(nb.value, dev)
+        self.tasks = None
+
+    def metadata(self):
+        """Makes the task list (device) that later fwd() calls use."""
+        nb = ctypes.c_size_t()
+        _abi.call(lib.sfa_sharedkv_metadata_size, ctypes.byref(self.a), ctypes.byref(nb))
+        if self.tasks is None or self.tasks.numel() < nb.value:
+            self.tasks = _workspace(nb.value, self.q_device)
+        self.a.tasks = None
+        _abi.call(lib.sfa_sharedkv_metadata, ctypes.byref(self.a), _ptr(self.tasks),
+                  ctypes.c_size_t(self.tasks.numel()), _stream())
+        self.a.tasks = self.tasks.data_ptr()
+        return self.tasks
 
     def fwd(self):
         _abi.call(lib.sfa_sharedkv_fwd, ctypes.byref(self.a), _ptr(self.ws),

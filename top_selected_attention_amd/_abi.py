@@ -19,6 +19,7 @@ EXPORTS = [
     "nsa_select_bwd", "nsa_compact_blocks_total", "nsa_compact_workspace_size", "nsa_compact",
     "sfa_paged_fwd_workspace_size", "sfa_paged_fwd",
     "sfa_sharedkv_fwd_workspace_size", "sfa_sharedkv_fwd",
+    "sfa_sharedkv_metadata_size", "sfa_sharedkv_metadata",
 ]
 
 
@@ -109,7 +110,7 @@ class SfaSharedkvArgs(ctypes.Structure):
         ("cmp_num_pages", c_int32), ("cmp_page_size", c_int32), ("cmp_max_pages", c_int32),
         ("cmp_key_cache", c_void_p), ("cmp_key_rope_cache", c_void_p),
         ("cmp_block_table", c_void_p), ("cmp_topk_indices", c_void_p),
-        ("out", c_void_p), ("lse", c_void_p),
+        ("out", c_void_p), ("lse", c_void_p), ("tasks", c_void_p),
     ] + TRAIL
 
 
@@ -138,6 +139,7 @@ def load(path):
         "nsa_compact": [P, P, P, P, P, P, c_size_t, P],
         "sfa_paged_fwd_workspace_size": [P, P], "sfa_paged_fwd": [P, P, c_size_t, P],
         "sfa_sharedkv_fwd_workspace_size": [P, P], "sfa_sharedkv_fwd": [P, P, c_size_t, P],
+        "sfa_sharedkv_metadata_size": [P, P], "sfa_sharedkv_metadata": [P, P, c_size_t, P],
     }
     for name, args in sig.items():
         f = getattr(lib, name)

@@ -581,15 +581,14 @@ size_t skv_carve(const SfaParams& p, void* ws, SfaParams* out) {
   const long tok = p.ntok;
   float* po = c.take<float>(tok * p.splits * p.N1 * p.Dv);
   float* pl = c.take<float>(tok * p.splits * p.N1);
-  int* cu = c.take<int>(p.B + 1);
-  int* task = c.take<int>(2 * tok * p.splits);
+  int* buf = c.take<int>(skv_cu_ints(p.B) + skv_task_ints(tok, p.splits));
   if (out) {
     *out = p;
     out->part_o = po;
     out->part_lse = pl;
     out->cu_q = nullptr;
-    out->cu_dev = cu;
-    out->task = task;
+    out->cu_dev = buf;
+    out->task = buf + skv_cu_ints(p.B);
   }
   return c.off + kAlign;
 }
@@ -939,6 +938,41 @@ int sfa_sharedkv_fwd_workspace_size(const sfa_sharedkv_fwd_args* a, size_t* byte
   return TSA_OK;
 }
 
+int sfa_sharedkv_metadata_size(const sfa_sharedkv_fwd_args* a, size_t* bytes) {
+  if (!bytes) return TSA_ERR_NULL;
+  int s = check_sfa_sharedkv(a);
+  if (s) return s;
+  const SfaParams p = skv_params(a);
+  *bytes = sizeof(int) * (skv_cu_ints(p.B) + skv_task_ints(p.ntok, p.splits));
+  return TSA_OK;
+}
+
+// TND prefix sums into the task buffer (host -> device), pointed at by p->cu_q.
+static hipError_t skv_upload_cu(const sfa_sharedkv_fwd_args* a, SfaParams* p, hipStream_t st) {
+  if (a->q_layout != TSA_LAYOUT_TND) return hipSuccess;
+  // the copy from pageable memory is staged before hipMemcpyAsync returns
+  hipError_t e = hipMemcpyAsync(p->cu_dev, a->cu_seqlens_q, sizeof(int) * (a->B + 1),
+                                hipMemcpyHostToDevice, st);
+  p->cu_q = p->cu_dev;
+  return e;
+}
+
+int sfa_sharedkv_metadata(const sfa_sharedkv_fwd_args* a, void* tasks, size_t bytes,
+                          void* stream) {
+  size_t need;
+  int s = sfa_sharedkv_metadata_size(a, &need);
+  if (s) return s;
+  if (!tasks || bytes < need) return TSA_ERR_WORKSPACE;
+  if (skv_tokens(a) == 0) return TSA_OK;
+  hipStream_t st = (hipStream_t)stream;
+  SfaParams p = skv_params(a);
+  p.cu_dev = (int*)tasks;
+  p.task = (int*)tasks + skv_cu_ints(p.B);
+  hipError_t e = skv_upload_cu(a, &p, st);
+  if (e == hipSuccess) e = launch_sfa_task(p, st);
+  return hip_status(e);
+}
+
 int sfa_sharedkv_fwd(const sfa_sharedkv_fwd_args* a, void* ws, size_t ws_bytes, void* stream) {
   size_t need;
   int s = sfa_sharedkv_fwd_workspace_size(a, &need);
@@ -948,15 +982,17 @@ int sfa_sharedkv_fwd(const sfa_sharedkv_fwd_args* a, void* ws, size_t ws_bytes, 
   hipStream_t st = (hipStream_t)stream;
   SfaParams p;
   skv_carve(skv_params(a), ws, &p);
-  if (a->q_layout == TSA_LAYOUT_TND) {
-    // the copy from pageable memory is staged before hipMemcpyAsync returns
-    if (hipMemcpyAsync(p.cu_dev, a->cu_seqlens_q, sizeof(int) * (a->B + 1),
-                       hipMemcpyHostToDevice, st) != hipSuccess)
-      return TSA_ERR_HIP;
-    p.cu_q = p.cu_dev;
+  const bool have = a->tasks != nullptr;
+  if (have) {
+    // the list of an earlier sfa_sharedkv_metadata call: token entries and
+    // slot ranges; no upload, no list kernel
+    p.cu_dev = (int*)a->tasks;
+    p.task = (int*)a->tasks + skv_cu_ints(p.B);
+  } else if (skv_upload_cu(a, &p, st) != hipSuccess) {
+    return TSA_ERR_HIP;
   }
   const StageTimer tm = timer_of(a, st);
-  return hip_status(launch_sfa_sharedkv(p, a->dtype == TSA_FP16, st, tm.ev, tm.n));
+  return hip_status(launch_sfa_sharedkv(p, a->dtype == TSA_FP16, have, st, tm.ev, tm.n));
 }
 
 }  // extern "C"

@@ -89,7 +89,14 @@ __global__ __launch_bounds__(512) void sfa_split_kernel(SfaParams p, int n_items
   const int sp = (item / hgroups) % p.splits;
   const int tk = item / (hgroups * p.splits);
   int b, s, sq;
-  sfa_token(p, tk, b, s, sq);
+  if (p.task) {
+    const int4 ti = *reinterpret_cast<const int4*>(p.task + 4 * (long)tk);
+    b = ti.x;
+    s = ti.y;
+    sq = ti.z;
+  } else {
+    sfa_token(p, tk, b, s, sq);
+  }
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
@@ -106,8 +113,9 @@ __global__ __launch_bounds__(512) void sfa_split_kernel(SfaParams p, int n_items
   int slot_lo = sp * per_split;
   int slot_hi = min(slot_lo + per_split, total);
   if (p.task) {
-    slot_lo = p.task[2 * (tk * p.splits + sp)];
-    slot_hi = p.task[2 * (tk * p.splits + sp) + 1];
+    const int* rg = p.task + 4 * p.ntok + 2 * ((long)tk * p.splits + sp);
+    slot_lo = rg[0];
+    slot_hi = rg[1];
   }
   // the top-k slots' cache, length and causal bound: the compressed cache in
   // the shared-KV decode, else the one cache
@@ -482,8 +490,21 @@ __global__ __launch_bounds__(256) void sfa_task_kernel(SfaParams p) {
   const long tk = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (tk >= p.ntok) return;
+  // the token's batch entry: the largest b with cu_q[b] <= tk, i.e. the count
+  // of i in [1, B) with cu_q[i] <= tk, 64 prefix sums tested at a time
   int b, s, sq;
-  sfa_token(p, (int)tk, b, s, sq);
+  if (p.cu_q) {
+    b = 0;
+    for (int i0 = 1; i0 < p.B; i0 += 64) {
+      const int i = i0 + lane;
+      b += __popcll(__ballot(i < p.B && p.cu_q[i] <= tk));
+    }
+    s = (int)tk - p.cu_q[b];
+    sq = p.cu_q[b + 1] - p.cu_q[b];
+  } else {
+    sfa_token(p, (int)tk, b, s, sq);
+  }
+  if (lane == 0) *reinterpret_cast<int4*>(p.task + 4 * tk) = make_int4(b, s, sq, 0);
   const int kv_len = p.kv_lens[b];
   const int qpos = kv_len - sq + s;
   const int t_len = kv_len / p.cmp_ratio;
@@ -500,17 +521,24 @@ __global__ __launch_bounds__(256) void sfa_task_kernel(SfaParams p) {
       const int e = min(min(hi, p.win_len), kv_len - qpos + p.win_left);
       kept = max(0, e - a);
     } else {
-      for (int j = lo; j < hi; j++) {
-        const int id = topk[(j - p.win_pad) / p.sbs];
-        const int pos = id * p.sbs + (j - p.win_pad) % p.sbs;
-        kept += id >= 0 && pos < t_len && pos <= t_qpos;
+      // a fixed-length loop: the chunk's id loads issue back to back
+      int id[kKeys];
+#pragma unroll
+      for (int u = 0; u < kKeys; u++) id[u] = lo + u < hi ? topk[(lo + u - p.win_pad) / p.sbs] : -1;
+#pragma unroll
+      for (int u = 0; u < kKeys; u++) {
+        const int pos = id[u] * p.sbs + (lo + u - p.win_pad) % p.sbs;
+        kept += id[u] >= 0 && pos < t_len && pos <= t_qpos;
       }
     }
     return kept + kChunkCost;
   };
+  // one round of 64 chunks covers 2048 slots: the weights are kept from the
+  // total's pass when it is the only round
+  const int w0 = weight(lane);
   long wsum = 0;
   for (int c0 = 0; c0 < nch; c0 += 64) {
-    int w = weight(c0 + lane);
+    int w = c0 == 0 ? w0 : weight(c0 + lane);
     for (int o = 32; o > 0; o >>= 1) w += __shfl_xor(w, o);
     wsum += w;
   }
@@ -518,7 +546,7 @@ __global__ __launch_bounds__(256) void sfa_task_kernel(SfaParams p) {
   long carry = 0;
   for (int c0 = 0; c0 < nch; c0 += 64) {
     const int c = c0 + lane;
-    long incl = wave_incl_scan(weight(c)) + carry;
+    long incl = wave_incl_scan(c0 == 0 ? w0 : weight(c)) + carry;
     for (int k = 1; k < p.splits; k++) {
       const unsigned long long bal = __ballot(c < nch && incl * p.splits <= (long)k * wsum);
       if (lane == k) cnt += __popcll(bal);
@@ -529,19 +557,22 @@ __global__ __launch_bounds__(256) void sfa_task_kernel(SfaParams p) {
   if (lane < p.splits) {
     const int clo = lane == 0 ? 0 : cnt;
     const int chi = lane + 1 == p.splits ? nch : nxt;
-    int* t = p.task + 2 * (tk * p.splits + lane);
+    int* t = p.task + 4 * p.ntok + 2 * (tk * p.splits + lane);
     t[0] = min(clo * kKeys, total);
     t[1] = min(max(chi, clo) * kKeys, total);
   }
 }
 
-hipError_t launch_sfa_sharedkv(const SfaParams& p, int fp16, hipStream_t st, void* const* ev,
-                               int n_ev) {
+hipError_t launch_sfa_task(const SfaParams& p, hipStream_t st) {
+  if (p.ntok == 0) return hipSuccess;
+  hipLaunchKernelGGL(sfa_task_kernel, dim3((unsigned)((p.ntok + 3) / 4)), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_sfa_sharedkv(const SfaParams& p, int fp16, bool have_tasks, hipStream_t st,
+                               void* const* ev, int n_ev) {
   hipError_t e = mark_event(ev, n_ev, 0, 0, st);
-  if (e == hipSuccess) {
-    hipLaunchKernelGGL(sfa_task_kernel, dim3((unsigned)((p.ntok + 3) / 4)), dim3(256), 0, st, p);
-    e = hipGetLastError();
-  }
+  if (e == hipSuccess && !have_tasks) e = launch_sfa_task(p, st);
   if (e == hipSuccess) e = mark_event(ev, n_ev, 0, 1, st);
   // the split / combine stages are timed as stages 1 and 2
   void* const* ev2 = n_ev > 1 ? ev + 2 : nullptr;

@@ -208,18 +208,27 @@ struct SfaParams {
   const void* ckrc;
   const int* cbt;
   int c_page, c_max_pages, c_num_pages, cmp_ratio;
-  // Slot range [task[2i], task[2i+1]) of split i = tk * splits + sp, or null
-  // for equal slot ranges.
+  // Shared-KV task list, or null (plain SFA: equal slot ranges, the token's
+  // entry found from Sq / cu_q): per token {b, s, Sq_b, 0}, then per split
+  // i = tk * splits + sp its slot range [lo, hi).
   int* task;
 };
+
+// The task-list buffer of the shared-KV decode: the TND prefix sums (B+1,
+// padded to 4 ints), then the task list; sizes in ints.
+inline long skv_cu_ints(int B) { return ((long)B + 1 + 3) / 4 * 4; }
+inline long skv_task_ints(long ntok, int splits) { return ntok * 4 + ntok * splits * 2; }
 
 int sfa_splits(const SfaParams& p);
 // slots per decode token: the band (padded) plus the top-k entries
 __host__ __device__ inline int sfa_total_slots(const SfaParams& p) { return p.win_pad + p.topk_n * p.sbs; }
-// The shared-KV task list (metadata kernel), then the split and combine
-// kernels: stage 0 = task list, 1 = split attention, 2 = combine.
-hipError_t launch_sfa_sharedkv(const SfaParams& p, int fp16, hipStream_t st, void* const* ev,
-                               int n_ev);
+// The shared-KV task list (metadata kernel) into p.task.
+hipError_t launch_sfa_task(const SfaParams& p, hipStream_t st);
+// The split and combine kernels of the shared-KV decode, with the task list
+// made first unless `have_tasks`: stage 0 = task list, 1 = split attention,
+// 2 = combine.
+hipError_t launch_sfa_sharedkv(const SfaParams& p, int fp16, bool have_tasks, hipStream_t st,
+                               void* const* ev, int n_ev);
 // stage 0 = split attention, stage 1 = combine
 hipError_t launch_sfa_fwd(const SfaParams& p, int fp16, hipStream_t st, void* const* ev, int n_ev);
 hipError_t launch_sfa_check(const SfaParams& p, hipStream_t st);
