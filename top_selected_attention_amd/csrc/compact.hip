@@ -143,65 +143,69 @@ struct MaskTileGeom {
 };
 
 constexpr int kTileStride = 68;  // bytes per LDS tile row (odd dword count: conflict-free columns)
+constexpr int kMaskWaves = 4;    // waves per tile: each takes 16 of its rows / columns
 
+// The tile's 64 rows x 64 columns into LDS: thread t loads 16 columns
+// (quarter t / 64) of row t % 64; entries past the mask's edge read 0.
 __device__ __forceinline__ void load_mask_tile(const uint8_t* mask, const MaskTileGeom& g, int grp,
                                                int rt, int ct, uint8_t* tile) {
-  const int lane = threadIdx.x;
-  const int lrow = rt * 64 + lane;                  // row within group
+  const int r = threadIdx.x & 63, qtr = threadIdx.x >> 6;
+  const int lrow = rt * 64 + r;                     // row within group
   const long row = (long)grp * g.RG + lrow;
-  const int c0 = ct * 64;
-  const int nc = min(64, g.KB - c0);
-  uint8_t* dst = tile + lane * kTileStride;
-  if (lrow < g.RG) {
+  const int c0 = ct * 64 + 16 * qtr;
+  const int nc = max(0, min(16, g.KB - c0));
+  uint8_t* dst = tile + r * kTileStride + 16 * qtr;
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+  if (lrow < g.RG && nc > 0) {
     const uint8_t* src = mask + row * g.KB + c0;
     if ((g.KB & 15) == 0) {
-      for (int i = 0; i < nc; i += 16) {
-        uint4 u = *reinterpret_cast<const uint4*>(src + i);
-        uint32_t w[4] = {u.x, u.y, u.z, u.w};
-        for (int j = 0; j < 4; j++) *reinterpret_cast<uint32_t*>(dst + i + 4 * j) = w[j];
-      }
+      const uint4 u = *reinterpret_cast<const uint4*>(src);
+      w[0] = u.x; w[1] = u.y; w[2] = u.z; w[3] = u.w;
     } else {
-      for (int i = 0; i < nc; i++) dst[i] = src[i];
+      for (int i = 0; i < nc; i++) w[i >> 2] |= (uint32_t)src[i] << (8 * (i & 3));
     }
-    for (int i = nc; i < 64; i++) dst[i] = 0;
-  } else {
-    for (int i = 0; i < 64; i++) dst[i] = 0;
   }
+  for (int j = 0; j < 4; j++) *reinterpret_cast<uint32_t*>(dst + 4 * j) = w[j];
 }
 
-__global__ __launch_bounds__(64) void bsa_mask_count(const uint8_t* mask, MaskTileGeom g,
-                                                     int* parts) {
+__global__ __launch_bounds__(64 * kMaskWaves) void bsa_mask_count(const uint8_t* mask,
+                                                                  MaskTileGeom g, int* parts) {
   __shared__ uint8_t tile[64 * kTileStride];
+  __shared__ int rsum[kMaskWaves][64];
   const int ct = blockIdx.x % g.CT;
   const int rtg = blockIdx.x / g.CT;
   const int grp = rtg / g.RTG, rt = rtg % g.RTG;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   load_mask_tile(mask, g, grp, rt, ct, tile);
   __syncthreads();
-  // row counts within this column tile
+  // row counts within this column tile: wave w counts columns 16w .. 16w+15
   int rc = 0;
-  for (int c = 0; c < 64; c++) rc += tile[lane * kTileStride + c] != 0;
-  const int lrow = rt * 64 + lane;
-  if (lrow < g.RG) parts[((long)grp * g.RG + lrow) * g.CT + ct] = rc;
-  // column counts within this row tile
+  for (int c = 16 * w; c < 16 * w + 16; c++) rc += tile[lane * kTileStride + c] != 0;
+  rsum[w][lane] = rc;
+  // column counts within this row tile: wave w takes columns 16w .. 16w+15
   int myc = 0;
-  for (int c = 0; c < 64; c++) {
-    unsigned long long bits = __ballot(tile[lane * kTileStride + c] != 0);
+  for (int c = 16 * w; c < 16 * w + 16; c++) {
+    const unsigned long long bits = __ballot(tile[lane * kTileStride + c] != 0);
     if (lane == c) myc = __popcll(bits);
   }
   const int col = ct * 64 + lane;
-  if (col < g.KB) parts[(long)g.R * g.CT + ((long)grp * g.KB + col) * g.RTG + rt] = myc;
+  if (lane >= 16 * w && lane < 16 * w + 16 && col < g.KB)
+    parts[(long)g.R * g.CT + ((long)grp * g.KB + col) * g.RTG + rt] = myc;
+  __syncthreads();
+  const int lrow = rt * 64 + lane;
+  if (w == 0 && lrow < g.RG)
+    parts[((long)grp * g.RG + lrow) * g.CT + ct] = rsum[0][lane] + rsum[1][lane] + rsum[2][lane] +
+                                                   rsum[3][lane];
 }
 
-__global__ __launch_bounds__(64) void bsa_mask_fill(const uint8_t* mask, MaskTileGeom g,
-                                                    const int* scanned, const int* sums_total,
-                                                    int* row_ptr, int* col, int* rev_ptr,
-                                                    int* rev) {
+__global__ __launch_bounds__(64 * kMaskWaves) void bsa_mask_fill(
+    const uint8_t* mask, MaskTileGeom g, const int* scanned, const int* sums_total, int* row_ptr,
+    int* col, int* rev_ptr, int* rev) {
   __shared__ uint8_t tile[64 * kTileStride];
   const int ct = blockIdx.x % g.CT;
   const int rtg = blockIdx.x / g.CT;
   const int grp = rtg / g.RTG, rt = rtg % g.RTG;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   load_mask_tile(mask, g, grp, rt, ct, tile);
   __syncthreads();
   const long colpart0 = (long)g.R * g.CT;
@@ -209,31 +213,33 @@ __global__ __launch_bounds__(64) void bsa_mask_fill(const uint8_t* mask, MaskTil
   const int nnz = scanned[colpart0];
   const int lrow = rt * 64 + lane;
   const long row = (long)grp * g.RG + lrow;
+  // every wave forms the 64 row and 64 column bases (lane = row / column);
+  // wave 0 also writes the pointers
   int my_rbase = 0;
   if (lrow < g.RG) {
     my_rbase = scanned[row * g.CT + ct];
-    if (ct == 0) row_ptr[row] = my_rbase;
+    if (ct == 0 && w == 0) row_ptr[row] = my_rbase;
   }
   const int mycol = ct * 64 + lane;
   int my_cbase = 0;
   if (mycol < g.KB) {
     my_cbase = scanned[colpart0 + ((long)grp * g.KB + mycol) * g.RTG + rt] - nnz;
-    if (rt == 0) rev_ptr[(long)grp * g.KB + mycol] = my_cbase;
+    if (rt == 0 && w == 0) rev_ptr[(long)grp * g.KB + mycol] = my_cbase;
   }
-  if (blockIdx.x == 0 && lane == 0) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
     row_ptr[g.R] = nnz;
     rev_ptr[(long)g.groups * g.KB] = sums_total[0] - nnz;
   }
   const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  // forward entries: for each row of the tile, lanes are columns
-  for (int r = 0; r < 64; r++) {
+  // forward entries: wave w takes rows 16w .. 16w+15, lanes are columns
+  for (int r = 16 * w; r < 16 * w + 16; r++) {
     const bool bit = tile[r * kTileStride + lane] != 0;
     const unsigned long long bits = __ballot(bit);
     const int base = __shfl(my_rbase, r);
     if (bit) col[base + __popcll(bits & below)] = ct * 64 + lane;
   }
-  // reverse entries: for each column of the tile, lanes are rows
-  for (int c = 0; c < 64; c++) {
+  // reverse entries: wave w takes columns 16w .. 16w+15, lanes are rows
+  for (int c = 16 * w; c < 16 * w + 16; c++) {
     const bool bit = tile[lane * kTileStride + c] != 0;
     const unsigned long long bits = __ballot(bit);
     const int base = __shfl(my_cbase, c);
@@ -265,12 +271,12 @@ hipError_t launch_bsa_compact(const uint8_t* mask, int B, int N1, int N2, int QB
   MaskTileGeom g = mask_geom(B, N1, N2, QB, KB);
   const long nparts = bsa_compact_parts_len(B, N1, N2, QB, KB);
   const int ntiles = g.groups * g.RTG * g.CT;
-  hipLaunchKernelGGL(bsa_mask_count, dim3(ntiles), dim3(64), 0, st, mask, g, parts);
+  hipLaunchKernelGGL(bsa_mask_count, dim3(ntiles), dim3(64 * kMaskWaves), 0, st, mask, g, parts);
   hipError_t e = exclusive_scan(parts, nparts, sums, st);
   if (e != hipSuccess) return e;
   const int nt = (int)((nparts + kScanTile - 1) / kScanTile);
-  hipLaunchKernelGGL(bsa_mask_fill, dim3(ntiles), dim3(64), 0, st, mask, g, parts, sums + nt,
-                     row_ptr, col, rev_ptr, rev);
+  hipLaunchKernelGGL(bsa_mask_fill, dim3(ntiles), dim3(64 * kMaskWaves), 0, st, mask, g, parts,
+                     sums + nt, row_ptr, col, rev_ptr, rev);
   return hipGetLastError();
 }
 
@@ -362,21 +368,27 @@ __global__ __launch_bounds__(1024) void tile_order(const int* ptr_a, int n_a, in
     ex += v[j];
   }
   __syncthreads();
-  // each wave places its segment in index order, 64 tiles a step
+  // each wave places its segment in index order, 64 tiles a step: a lane's
+  // peers (the lanes of its bucket) are the AND over the bucket's 8 bits of
+  // the ballot of that bit or of its complement; its rank among them is the
+  // count of lower peers, and the lowest peer advances the bucket's slot
+  static_assert(kOrderBins == 256, "8 bucket bits");
+  const unsigned long long below = (1ull << lane) - 1;
   for (int base = lo; base < hi; base += 64) {
     const int i = base + lane;
     const bool valid = i < hi;
-    const int bk = valid ? bucket(i) : -1;
-    unsigned long long todo = __ballot(valid);
-    while (todo) {
-      const int leader = __builtin_ctzll(todo);
-      const int lb = __shfl(bk, leader);
-      const unsigned long long peers = __ballot(bk == lb) & todo;
-      const int start = cnt[w][lb];  // read by every lane before the leader's update
-      if (bk == lb && valid) ord[start + __popcll(peers & ((1ull << lane) - 1))] = i;
-      if (lane == leader) cnt[w][lb] = start + __popcll(peers);
-      todo &= ~peers;
+    const int bk = valid ? bucket(i) : 0;
+    unsigned long long peers = __ballot(valid);
+#pragma unroll
+    for (int bit = 0; bit < 8; bit++) {
+      const bool on = (bk >> bit) & 1;
+      const unsigned long long m = __ballot(valid && on);
+      peers &= on ? m : ~m;
     }
+    const int start = valid ? cnt[w][bk] : 0;  // every lane reads before any update
+    const int rank = __popcll(peers & below);
+    if (valid) ord[start + rank] = i;
+    if (valid && rank == 0) cnt[w][bk] = start + __popcll(peers);
   }
   if (blockIdx.x == 1 && plan.seg_off) {
     __syncthreads();  // this workgroup's order writes are visible to all its threads
