@@ -1,4 +1,5 @@
-/* Measured peaks of the chip: dense MFMA issue rate and HBM streaming rate.
+/* Measured peaks of the chip (dense MFMA issue rate, HBM streaming rate), and a
+ * register-fill test aid.
  *
  * A measurement aid that sits beside the attention library (libtsa_peaks.so,
  * built from the same tree): the attention kernels are compared against the
@@ -43,6 +44,13 @@ int tsa_peak_copy(const void* src, void* dst, size_t bytes, int n_blocks, void* 
  * 32-bit word it read to out[blk] (device, n_blocks words).  HBM traffic:
  * bytes.  Limits as for tsa_peak_copy. */
 int tsa_peak_read(const void* src, size_t bytes, int n_blocks, unsigned* out, void* stream);
+
+/* Test aid: 4096 workgroups of 256 threads, one wave per SIMD at 512
+ * registers each, write `pattern` into all 256 VGPRs and 256 AGPRs of their
+ * wave.  A kernel launched next on the same device that reads a register it
+ * never wrote then finds that pattern (say the bits of +inf or a NaN)
+ * instead of whatever earlier work left, so such reads show in results. */
+int tsa_fill_registers(unsigned pattern, void* stream);
 
 #ifdef __cplusplus
 }

@@ -21,8 +21,9 @@ def _lib():
 
 
 def test_exports_match_header():
-    names = re.findall(r"^int (tsa_peak_\w+)\(", open(HEADER).read(), re.M)
-    assert sorted(names) == ["tsa_peak_copy", "tsa_peak_mfma", "tsa_peak_read"]
+    names = re.findall(r"^int (tsa_\w+)\(", open(HEADER).read(), re.M)
+    assert sorted(names) == ["tsa_fill_registers", "tsa_peak_copy", "tsa_peak_mfma",
+                             "tsa_peak_read"]
     L = _lib()
     for n in names:
         assert hasattr(L, n), n

@@ -265,7 +265,11 @@ __global__ __launch_bounds__(512) void sfa_split_kernel(SfaParams p, int n_items
             const int c16 = 16 * qd + 4 * ks + g;  // 16-byte piece of dims 128*qd + 32*ks + 8*g
             ka[kt][ks] = lds_read16<V8>(Mt + r * 1024 + ((c16 ^ swz1k(r)) << 4));
           }
-          if (qd < 2) ka[kt][4] = lds_read16<V8>(Rt + r * 128 + (((4 * qd + g) ^ swzr(r)) << 4));
+          // waves without rope dims hold a zero operand: the compiler may issue the
+          // rope MFMA on every wave (with a zero Q operand there), and leftover
+          // register contents such as inf would turn its products into NaN
+          ka[kt][4] = qd < 2 ? lds_read16<V8>(Rt + r * 128 + (((4 * qd + g) ^ swzr(r)) << 4))
+                             : zero_v8<V8>();
         }
 #pragma unroll
         for (int kt = 0; kt < 2; kt++) {

@@ -25,7 +25,8 @@ def lib():
                                     ctypes.c_int, ctypes.c_void_p]
         L.tsa_peak_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
                                     ctypes.c_void_p, ctypes.c_void_p]
-        for f in (L.tsa_peak_mfma, L.tsa_peak_copy, L.tsa_peak_read):
+        L.tsa_fill_registers.argtypes = [ctypes.c_uint, ctypes.c_void_p]
+        for f in (L.tsa_peak_mfma, L.tsa_peak_copy, L.tsa_peak_read, L.tsa_fill_registers):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -65,6 +66,11 @@ def read(src, out, n_blocks=8192):
     _check(lib().tsa_peak_read(ctypes.c_void_p(src.data_ptr()), src.numel() * src.element_size(),
                                n_blocks, ctypes.c_void_p(out.data_ptr()), _stream()),
            "tsa_peak_read")
+
+
+def fill_registers(pattern):
+    """Writes ``pattern`` (32 bits) into every SIMD's registers (test aid)."""
+    _check(lib().tsa_fill_registers(pattern & 0xffffffff, _stream()), "tsa_fill_registers")
 
 
 def _timed(f, n):
