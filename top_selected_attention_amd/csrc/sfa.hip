@@ -98,8 +98,7 @@ __global__ __launch_bounds__(512) void sfa_split_kernel(SfaParams p, int n_items
     sfa_token(p, tk, b, s, sq);
   }
   const int tid = threadIdx.x, lane = tid & 63;
-  // wave-uniform (a scalar): branches on the wave's role skip their MFMAs outright
-  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wid = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
   // wave = (32-head group h2, quarter qd): the quarter selects 128 of the 512
   // output columns and a quarter of the 576-dim score contraction (main dims
