@@ -248,6 +248,39 @@ def test_bwd_bsa_causal_8k_sampled():
     _bwd_check(q, k, v, do, mask, bq, w["bkv"], scale, 0, q_tiles=sorted(tiles), kv_rows=kv_rows)
 
 
+def test_bsa_window_128k_sampled():
+    """The full 1x8x131072 window workload (8-block window + 24 random
+    earlier blocks per Q block) in the timed launch configuration: out / LSE
+    / dQ on sampled Q blocks; dK / dV on KV blocks 0, 512 and 1023 of two
+    heads, each with every Q block on its reverse list."""
+    w, q, k, v, do, mask, scale = W.bsa_inputs(5)
+    bq = w["bq"]
+    QB = w["S"] // bq
+    tiles = set()
+    kv_rows = np.zeros((w["B"], w["N2"], w["S"]), bool)
+    for b, n in [(0, 0), (0, 7)]:
+        for qb in (0, 511, QB - 1):
+            tiles.add((b, n, qb))
+        for kb in (0, 512, QB - 1):
+            kv_rows[b, n, kb * bq:(kb + 1) * bq] = True
+            for qb in np.nonzero(mask[b, n, :, kb])[0]:
+                tiles.add((b, n, int(qb)))
+    tiles = sorted(tiles)
+    out, lse, dq, dk, dv = _bwd_gpu(q, k, v, do, mask, bq, w["bkv"], scale, 0)
+    qn, kn, vn = _np(q), _np(k), _np(v)
+    ro, rl = oracle.bsa_fwd(qn, kn, vn, mask, bq, w["bkv"], scale, 0, q_tiles=tiles)
+    qrows = np.zeros(ro.shape[:3], bool)
+    for b, n, qb in tiles:
+        qrows[b, n, qb * bq:(qb + 1) * bq] = True
+    _close(out, ro, OUT_TOL, "out", qrows)
+    _lse_close(lse, rl, qrows)
+    rdq, rdk, rdv = oracle.bsa_bwd(qn, kn, vn, _np(out), _np(do), mask, bq, w["bkv"], scale, 0,
+                                   q_tiles=tiles)
+    _close(dq, rdq, GRAD_TOL, "dq", qrows)
+    _close(dk, rdk, GRAD_TOL, "dk", kv_rows)
+    _close(dv, rdv, GRAD_TOL, "dv", kv_rows)
+
+
 def test_bwd_deterministic_bitwise():
     """Two backward runs give bit-identical gradients (no atomics)."""
     w, q, k, v, do, mask, scale = W.bsa_inputs(2)
