@@ -871,6 +871,21 @@ def _threads():
         return 1
 
 
+def _host():
+    """The host the oracle baseline ran on: CPU model and the cores this
+    process may use."""
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "affinity_cores": len(os.sched_getaffinity(0))}
+
+
 def main():
     args = parse()
     if args.ingest_copy:
@@ -911,6 +926,8 @@ def main():
         res, ctx = bench_sfa(args)
         if args.cpu_seconds > 0:
             res["cpu_baseline"] = cpu_baseline_sfa(ctx, args.cpu_seconds)
+    if "cpu_baseline" in res:
+        res["cpu_baseline"].update(_host())
     if not args.no_peaks:
         res["measured_peaks"] = measured_peaks()
     print(json.dumps(res), flush=True)
