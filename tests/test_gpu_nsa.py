@@ -240,3 +240,22 @@ def test_selection_size_limits_sampled(seqlens, N1, N2, sbs, sbc):
     _close(dq, rdq, GRAD_TOL, "dq", rows=toks)
     _close(dk, rdk, GRAD_TOL, "dk", rows=rows)
     _close(dv, rdv, GRAD_TOL, "dv", rows=rows)
+
+
+def test_unselected_block_is_never_read():
+    """Noise in the K/V rows of a block no token selects on one KV head leaves
+    O, LSE and dQ bit-identical and that block's dK/dV exactly zero."""
+    cu, q, k, v, do, topk = _case([512, 384], 32, 2, 64, 4, 120)
+    blk, n2 = 3, 1                               # block 3 of the first sequence, KV head 1
+    t = topk[:, n2]
+    t[t == blk] = 0 if blk != 0 else 1          # every token that listed it lists block 0 instead
+    rows = slice(int(cu[0]) + blk * 64, int(cu[0]) + (blk + 1) * 64)
+    r1 = _run(cu, q, k, v, do, topk, 64, 0.088, 2)
+    k2, v2 = k.clone(), v.clone()
+    k2[rows, n2] = W.normal((64, 128), 97) * 50
+    v2[rows, n2] = W.normal((64, 128), 96) * 50
+    r2 = _run(cu, q, k2, v2, do, topk, 64, 0.088, 2)
+    for i in range(3):
+        assert torch.equal(r1[i], r2[i])
+    assert torch.equal(r1[3][:, 1 - n2], r2[3][:, 1 - n2])
+    assert (r2[3][rows, n2] == 0).all() and (r2[4][rows, n2] == 0).all()

@@ -176,3 +176,23 @@ def test_sfa_tnd_equal_lengths_is_bsnd_bitwise():
                                3, cu_seqlens_q=cu)
     torch.cuda.synchronize()
     assert torch.equal(o1.reshape(6, 64, 512), o2) and torch.equal(l1.reshape(6, 64), l2)
+
+
+def test_sfa_unselected_rows_are_never_read():
+    """Noise in cache rows that no decode token selects (and in unused pages)
+    leaves O and LSE bit-identical."""
+    q, qr, kc, krc, bt, kv_lens, idx = W.sfa_inputs(B=2, Sq=2, N1=64, page=32, kv_len=640,
+                                                    topk=96, seed_base=85, extra_pages=4)
+    scale = 1 / math.sqrt(576)
+    o1, l1 = _run(q, qr, kc, krc, bt, kv_lens, idx, scale, 3)
+    sel = np.zeros(kc.shape[0] * kc.shape[1], bool)
+    for b in range(idx.shape[0]):
+        ids = idx[b].reshape(-1)
+        ids = ids[ids >= 0]
+        sel[bt[b][ids // 32] * 32 + ids % 32] = True
+    kc2, krc2 = kc.clone(), krc.clone()
+    noise = ~torch.from_numpy(sel).reshape(kc.shape[0], kc.shape[1])
+    kc2[noise] = (W.normal(tuple(kc.shape), 95) * 50)[noise]
+    krc2[noise] = (W.normal(tuple(krc.shape), 94) * 50)[noise]
+    o2, l2 = _run(q, qr, kc2, krc2, bt, kv_lens, idx, scale, 3)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
