@@ -145,3 +145,12 @@ def test_task_list_made_once_serves_other_ids():
     err, sc = np.abs(_np(out) - ro).max(), np.abs(ro).max()
     assert err <= OUT_TOL * sc, f"out: {err:.3e} vs {OUT_TOL} * {sc:.3e}"
     assert np.abs(_np(lse) - rl).max() <= LSE_TOL * max(1.0, np.abs(rl).max())
+
+
+def test_tokens_before_the_sequence_start_see_nothing():
+    """More decode tokens than original KV rows: tokens whose position
+    kv_len - Sq_b + s is negative have no band rows and no compressed ids, and
+    get Out = 0 and LSE = -inf; the later ones see their short band."""
+    out, lse = _run_case([5, 2], [3, 300], 64, 16, 4, 8, 210)
+    assert torch.all(out[:2] == 0) and torch.all(torch.isneginf(lse[:2]))
+    assert torch.isfinite(lse[2:]).all()
