@@ -820,6 +820,8 @@ def ingest(d, workload):
            f"--warmup {bench['warmup']} --cpu-seconds 0 --no-peaks")
     pcmd = (f"python3 bench.py --workload {workload} --steps 2 --warmup 1 --cpu-seconds 0 "
             f"--no-peaks")
+    d = os.path.normpath(d)
+    cdir = os.path.join(os.path.dirname(d), "copy")   # the copy calibration beside it
     out = [
         f"# {dom} on {workload}: rocprofv3 kernel trace and HBM counters",
         "",
@@ -828,13 +830,13 @@ def ingest(d, workload):
         "Commands (repository root, one MI355X; `cd /tmp && export TMPDIR=/tmp` first, then back):",
         "",
         "```",
-        f"rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof/{workload}/trace -o run -- {cmd} > gpurun_out/prof/{workload}/bench.json",
-        f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/prof/{workload}/fetch -o run -- {pcmd}",
-        f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof/{workload}/write -o run -- {pcmd}",
-        "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/prof/copy/fetch -o run -- python3 bench.py --copy-calibration",
-        "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof/copy/write -o run -- python3 bench.py --copy-calibration",
-        "python3 bench.py --ingest-copy gpurun_out/prof/copy",
-        f"python3 bench.py --ingest gpurun_out/prof/{workload} --workload {workload}",
+        f"rocprofv3 --kernel-trace --stats --output-format csv -d {d}/trace -o run -- {cmd} > {d}/bench.json",
+        f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d}/fetch -o run -- {pcmd}",
+        f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}/write -o run -- {pcmd}",
+        f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {cdir}/fetch -o run -- python3 bench.py --copy-calibration",
+        f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {cdir}/write -o run -- python3 bench.py --copy-calibration",
+        f"python3 bench.py --ingest-copy {cdir}",
+        f"python3 bench.py --ingest {d} --workload {workload}",
         "```",
         "",
         "Kernel trace: every call of the traced run (warm-up included).  FETCH / WRITE: mean "
