@@ -450,7 +450,8 @@ typedef struct {
   const int32_t* cmp_topk_indices;       /* DEVICE */
   void* out;                    /* DEVICE, written */
   float* lse;                   /* DEVICE, written, or NULL */
-  const void* tasks;            /* DEVICE task list from sfa_sharedkv_metadata, or NULL */
+  const void* tasks;            /* DEVICE task list from sfa_sharedkv_metadata (16-byte
+                                   aligned, else TSA_ERR_INVALID), or NULL */
   int32_t reuse_lists;          /* unused; keep 0 */
   int32_t n_events;             /* number of stages to time (0 = off) */
   void* const* events;          /* HOST array of 2*n_events hipEvent_t (see above) */
@@ -459,9 +460,10 @@ typedef struct {
 /* Bytes of the task list of these arguments (validates them like the
  * forward; `tasks` is not read). */
 TSA_API int sfa_sharedkv_metadata_size(const sfa_sharedkv_fwd_args* args, size_t* bytes);
-/* Writes the task list into `tasks` (DEVICE, at least the size above; owned
- * by the caller), enqueued on `stream`; reads cu_seqlens_q (HOST, TND),
- * seqused_kv and cmp_topk_indices (DEVICE). */
+/* Writes the task list into `tasks` (DEVICE, 16-byte aligned, at least the
+ * size above; owned by the caller), enqueued on `stream`; reads cu_seqlens_q
+ * (HOST, TND), seqused_kv and cmp_topk_indices (DEVICE).  NULL or too small:
+ * TSA_ERR_WORKSPACE; misaligned: TSA_ERR_INVALID. */
 TSA_API int sfa_sharedkv_metadata(const sfa_sharedkv_fwd_args* args, void* tasks,
                                   size_t tasks_bytes, void* stream);
 TSA_API int sfa_sharedkv_fwd_workspace_size(const sfa_sharedkv_fwd_args* args, size_t* bytes);

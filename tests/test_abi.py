@@ -307,5 +307,11 @@ def test_sfa_sharedkv_metadata_size_and_buffer_checks(tsa):
     assert tsa.lib.sfa_sharedkv_metadata(ctypes.byref(a), ctypes.c_void_p(8), n.value - 4,
                                          None) == 4
     assert tsa.lib.sfa_sharedkv_metadata(ctypes.byref(a), None, n.value, None) == 4
+    # a task list off a 16-byte boundary is refused before any launch
+    assert tsa.lib.sfa_sharedkv_metadata(ctypes.byref(a), ctypes.c_void_p(8), n.value, None) == 2
+    w = ctypes.c_size_t()
+    assert tsa.lib.sfa_sharedkv_fwd_workspace_size(ctypes.byref(a), ctypes.byref(w)) == 0
+    a.tasks = 24
+    assert tsa.lib.sfa_sharedkv_fwd(ctypes.byref(a), ctypes.c_void_p(256), w.value, None) == 2
     bad = _skv(tsa, N1=48)
     assert tsa.lib.sfa_sharedkv_metadata_size(ctypes.byref(bad), ctypes.byref(n)) == 2

@@ -963,6 +963,7 @@ int sfa_sharedkv_metadata(const sfa_sharedkv_fwd_args* a, void* tasks, size_t by
   int s = sfa_sharedkv_metadata_size(a, &need);
   if (s) return s;
   if (!tasks || bytes < need) return TSA_ERR_WORKSPACE;
+  if ((uintptr_t)tasks % 16) return TSA_ERR_INVALID;  // the list holds 16-byte records
   if (skv_tokens(a) == 0) return TSA_OK;
   hipStream_t st = (hipStream_t)stream;
   SfaParams p = skv_params(a);
@@ -978,6 +979,7 @@ int sfa_sharedkv_fwd(const sfa_sharedkv_fwd_args* a, void* ws, size_t ws_bytes, 
   int s = sfa_sharedkv_fwd_workspace_size(a, &need);
   if (s) return s;
   if (!ws || ws_bytes < need) return TSA_ERR_WORKSPACE;
+  if (a->tasks && (uintptr_t)a->tasks % 16) return TSA_ERR_INVALID;
   if (skv_tokens(a) == 0) return TSA_OK;
   hipStream_t st = (hipStream_t)stream;
   SfaParams p;
