@@ -26,7 +26,11 @@
  *
  * Pointers marked DEVICE must be device memory of the current HIP device.
  * All tensors are dense and contiguous in the stated layout.  `stream` is a
- * hipStream_t (NULL = the null stream).
+ * hipStream_t (NULL = the null stream).  The kernels move rows in 16-byte
+ * pieces: the workspace and the DEVICE pointers of q, k, v, out, dout, dq,
+ * dk, dv, block_mask, q_rope and the key caches must be 16-byte aligned
+ * (fresh allocations are); a misaligned tensor gives TSA_ERR_INVALID, a
+ * misaligned workspace TSA_ERR_WORKSPACE.
  *
  * Every args struct ends with reuse_lists, n_events and events.  Stages
  * that can be timed, per entry point: bsa_fwd 0 = lists, 1 = attention;
@@ -61,7 +65,8 @@ typedef enum {
   TSA_ERR_NULL = 1,          /* a required pointer is NULL */
   TSA_ERR_INVALID = 2,       /* a value or shape violates a documented constraint */
   TSA_ERR_UNSUPPORTED = 3,   /* valid for the operator, not built in this library */
-  TSA_ERR_WORKSPACE = 4,     /* workspace NULL or smaller than XXX_workspace_size */
+  TSA_ERR_WORKSPACE = 4,     /* workspace NULL, smaller than XXX_workspace_size or
+                                not 16-byte aligned */
   TSA_ERR_HIP = 5,           /* a HIP launch or runtime call failed */
   TSA_ERR_DATA = 6           /* validate = 1 found bad data (ids out of range) */
 } tsa_status;

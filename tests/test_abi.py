@@ -45,8 +45,8 @@ def test_status_strings(tsa):
 
 def _bsa(tsa, **kw):
     a = dict(dtype=0, q_layout=0, kv_layout=0, B=2, N1=4, N2=2, Sq=1000, Skv=900, D=128,
-             block_q=128, block_kv=64, sparse_mode=0, scale=0.088, validate=0, block_mask=8,
-             q=8, k=8, v=8, out=8, lse=8)
+             block_q=128, block_kv=64, sparse_mode=0, scale=0.088, validate=0, block_mask=16,
+             q=16, k=16, v=16, out=16, lse=16)
     a.update(kw)
     return tsa._abi.BsaFwdArgs(**a)
 
@@ -67,6 +67,8 @@ def _size(tsa, fn, args):
     (dict(block_q=0), 2),
     (dict(q=0), 1),
     (dict(block_mask=0), 1),
+    (dict(q=24), 2),                       # device tensors 16-byte aligned
+    (dict(block_mask=8), 2),
     (dict(scale=float("nan")), 2),
     (dict(scale=0.0), 2),                  # scale must be positive
     (dict(scale=-0.1), 2),
@@ -109,7 +111,8 @@ def test_bsa_tnd_validation(tsa, cq, ck, status):
         assert n > 0
     b = tsa._abi.BsaBwdArgs(dtype=0, q_layout=1, kv_layout=1, B=2, N1=4, N2=2, Sq=1000,
                             Skv=900, D=128, block_q=128, block_kv=64, sparse_mode=2, scale=0.1,
-                            block_mask=8, q=8, k=8, v=8, out=8, dout=8, lse=8, dq=8, dk=8, dv=8)
+                            block_mask=16, q=16, k=16, v=16, out=16, dout=16, lse=16, dq=16,
+                            dk=16, dv=16)
     b.cu_seqlens_q, b.cu_seqlens_kv = a.cu_seqlens_q, a.cu_seqlens_kv
     assert _size(tsa, tsa.lib.bsa_bwd_workspace_size, b)[0] == status
 
@@ -126,7 +129,8 @@ def test_bsa_workspace_too_small_is_rejected_before_launch(tsa):
 def test_bsa_bwd_validation(tsa):
     a = tsa._abi.BsaBwdArgs(dtype=0, q_layout=0, kv_layout=0, B=1, N1=2, N2=2, Sq=256, Skv=256,
                             D=128, block_q=128, block_kv=128, sparse_mode=2, scale=0.1,
-                            block_mask=8, q=8, k=8, v=8, out=8, dout=8, lse=8, dq=8, dk=8, dv=8)
+                            block_mask=16, q=16, k=16, v=16, out=16, dout=16, lse=16, dq=16,
+                            dk=16, dv=16)
     assert _size(tsa, tsa.lib.bsa_bwd_workspace_size, a)[0] == 0
     a.atten_mask, a.atten_mask_stride_b = 8, -5
     assert _size(tsa, tsa.lib.bsa_bwd_workspace_size, a)[0] == 2
@@ -142,8 +146,8 @@ def _nsa(tsa, seqlens=(256, 512), **kw):
     a = dict(dtype=0, layout=1, B=len(seqlens), T=T, Tk=T, N1=32, N2=2, D=128, Dv=128,
              cu_seqlens_q=ctypes.cast(cu, ctypes.POINTER(ctypes.c_int32)),
              cu_seqlens_kv=ctypes.cast(cu, ctypes.POINTER(ctypes.c_int32)),
-             sbs=64, sbc=4, sparse_mode=2, scale=0.088, validate=0, topk=8, q=8, k=8, v=8,
-             out=8, lse=8)
+             sbs=64, sbc=4, sparse_mode=2, scale=0.088, validate=0, topk=16, q=16, k=16, v=16,
+             out=16, lse=16)
     a.update(kw)
     args = tsa._abi.NsaFwdArgs(**a)
     args._keep = cu
@@ -164,6 +168,7 @@ def _nsa(tsa, seqlens=(256, 512), **kw):
     (dict(Dv=64), 3),                      # Dv != D not built
     (dict(T=100), 2),                      # cu_seqlens_q[B] != T
     (dict(topk=0), 1),
+    (dict(v=40), 2),                       # device tensors 16-byte aligned
     (dict(reuse_lists=1), 0),
     (dict(reuse_lists=2), 2),              # the forward has no partial-reuse mode
 ])
@@ -171,11 +176,12 @@ def test_nsa_validation(tsa, kw, status):
     assert _size(tsa, tsa.lib.nsa_select_fwd_workspace_size, _nsa(tsa, **kw))[0] == status
 
 
-@pytest.mark.parametrize("reuse,status", [(0, 0), (1, 0), (2, 0), (3, 2), (-1, 2)])
-def test_nsa_bwd_reuse_modes(tsa, reuse, status):
+@pytest.mark.parametrize("reuse,status,dq", [(0, 0, 16), (1, 0, 16), (2, 0, 16), (3, 2, 16),
+                                             (-1, 2, 16), (0, 2, 20)])
+def test_nsa_bwd_reuse_modes(tsa, reuse, status, dq):
     f = _nsa(tsa)
     fields = {n: getattr(f, n) for n, _ in f._fields_ if n not in ("out", "lse", "events")}
-    fields.update(out=8, dout=8, lse=8, dq=8, dk=8, dv=8, reuse_lists=reuse)
+    fields.update(out=16, dout=16, lse=16, dq=dq, dk=16, dv=16, reuse_lists=reuse)
     b = tsa._abi.NsaBwdArgs(**fields)
     b._keep = f._keep
     assert _size(tsa, tsa.lib.nsa_select_bwd_workspace_size, b)[0] == status
@@ -193,9 +199,9 @@ def test_nsa_sequence_constraints(tsa):
 def _sfa(tsa, **kw):
     a = dict(dtype=0, q_layout=2, B=32, Sq=4, N1=64, N2=1, D=512, Dr=64, Dv=512,
              num_pages=16384, page_size=128, max_pages=512, topk=2048, sparse_block_size=1,
-             sparse_mode=3, scale=1 / 24, validate=0, q=8, q_rope=8, key_cache=16,
-             key_rope_cache=8, value_cache=16, block_table=8, kv_lens=8, topk_indices=8, out=8,
-             lse=8)
+             sparse_mode=3, scale=1 / 24, validate=0, q=16, q_rope=16, key_cache=16,
+             key_rope_cache=16, value_cache=16, block_table=16, kv_lens=16, topk_indices=16, out=16,
+             lse=16)
     a.update(kw)
     return tsa._abi.SfaArgs(**a)
 
@@ -228,6 +234,8 @@ def test_sfa_tnd_validation(tsa, cq, T, status):
     (dict(sparse_block_size=3), 2),        # must divide the page size
     (dict(sparse_mode=2), 2),
     (dict(value_cache=24), 3),             # separate value cache: not built
+    (dict(key_cache=24, value_cache=24), 2),   # caches 16-byte aligned
+    (dict(q_rope=40), 2),
     (dict(q_layout=1), 1),                 # TND queries need cu_seqlens_q
     (dict(scale=0.0), 2),
     (dict(kv_lens=0), 1),
@@ -250,13 +258,13 @@ def test_import_fails_loudly_without_library(tmp_path):
 
 
 def _skv(tsa, **kw):
-    a = dict(dtype=0, q_layout=2, B=32, Sq=4, N1=64, N2=1, D=512, Dr=64, scale=1 / 24, q=8,
-             q_rope=8, seqused_kv=8, has_ori_kv=1, has_cmp_kv=1, ori_win_left=127,
+    a = dict(dtype=0, q_layout=2, B=32, Sq=4, N1=64, N2=1, D=512, Dr=64, scale=1 / 24, q=16,
+             q_rope=16, seqused_kv=16, has_ori_kv=1, has_cmp_kv=1, ori_win_left=127,
              ori_win_right=0, ori_num_pages=16384, ori_page_size=128, ori_max_pages=512,
-             ori_key_cache=8, ori_key_rope_cache=8, ori_block_table=8, cmp_ratio=4,
+             ori_key_cache=16, ori_key_rope_cache=16, ori_block_table=16, cmp_ratio=4,
              cmp_topk=512, cmp_num_pages=4096, cmp_page_size=128, cmp_max_pages=128,
-             cmp_key_cache=8, cmp_key_rope_cache=8, cmp_block_table=8, cmp_topk_indices=8,
-             out=8, lse=8)
+             cmp_key_cache=16, cmp_key_rope_cache=16, cmp_block_table=16, cmp_topk_indices=16,
+             out=16, lse=16)
     a.update(kw)
     return tsa._abi.SfaSharedkvArgs(**a)
 
@@ -278,6 +286,8 @@ def _skv(tsa, **kw):
     (dict(scale=0.0), 2),
     (dict(q=0), 1),
     (dict(cmp_topk_indices=0), 1),
+    (dict(out=24), 2),                         # device tensors 16-byte aligned
+    (dict(cmp_key_rope_cache=8), 2),
     (dict(has_cmp_kv=0, cmp_key_cache=0, cmp_topk_indices=0, cmp_ratio=0), 0),
     (dict(has_ori_kv=0, ori_key_cache=0, ori_block_table=0, ori_win_left=-5), 0),
     (dict(q_layout=1, T=128), 1),              # TND needs cu_seqlens_q
@@ -295,6 +305,8 @@ def test_sfa_sharedkv_workspace_too_small_is_rejected_before_launch(tsa):
     s, n = _size(tsa, tsa.lib.sfa_sharedkv_fwd_workspace_size, a)
     assert s == 0
     assert tsa.lib.sfa_sharedkv_fwd(ctypes.byref(a), ctypes.c_void_p(8), n - 1, None) == 4
+    # large enough but not 16-byte aligned
+    assert tsa.lib.sfa_sharedkv_fwd(ctypes.byref(a), ctypes.c_void_p(24), n + 64, None) == 4
 
 
 

@@ -35,6 +35,9 @@ struct Carver {
 };
 
 inline long cdiv(long a, long b) { return (a + b - 1) / b; }
+// The kernels move tensor rows, caches and workspace buffers in 16-byte
+// pieces: such pointers must be 16-byte aligned (NULL passes).
+inline bool a16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 inline bool fits_i32(long x) { return x >= 0 && x <= 0x7fffffffL; }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? TSA_OK : TSA_ERR_HIP; }
@@ -173,6 +176,8 @@ int check_bsa_fwd(const bsa_fwd_args* a) {
   const bool empty = bsa_q_rows(a) == 0;
   if (!empty && (!a->q || !a->out || !a->lse || !a->block_mask)) return TSA_ERR_NULL;
   if (!empty && bsa_kv_rows(a) > 0 && (!a->k || !a->v)) return TSA_ERR_NULL;
+  if (!a16(a->q) || !a16(a->k) || !a16(a->v) || !a16(a->out) || !a16(a->block_mask))
+    return TSA_ERR_INVALID;
   return TSA_OK;
 }
 
@@ -190,6 +195,9 @@ int check_bsa_bwd(const bsa_bwd_args* a) {
   if (!empty_q && (!a->q || !a->out || !a->dout || !a->lse || !a->dq || !a->block_mask))
     return TSA_ERR_NULL;
   if (!empty_k && (!a->k || !a->v || !a->dk || !a->dv)) return TSA_ERR_NULL;
+  if (!a16(a->q) || !a16(a->k) || !a16(a->v) || !a16(a->out) || !a16(a->dout) || !a16(a->dq) ||
+      !a16(a->dk) || !a16(a->dv) || !a16(a->block_mask))
+    return TSA_ERR_INVALID;
   return TSA_OK;
 }
 
@@ -289,6 +297,7 @@ int check_nsa(const A* a) {
     return TSA_ERR_INVALID;
   if (a->T > 0 && (!a->q || !a->out || !a->lse || !a->topk)) return TSA_ERR_NULL;
   if (a->T > 0 && (!a->k || !a->v)) return TSA_ERR_NULL;
+  if (!a16(a->q) || !a16(a->k) || !a16(a->v) || !a16(a->out)) return TSA_ERR_INVALID;
   return TSA_OK;
 }
 
@@ -464,6 +473,9 @@ int check_sfa(const sfa_paged_fwd_args* a) {
   // Shared KV ("SparseAttnSharedkvMetadata": sharedkv): the value row is the
   // key row; a separate value cache is not built.
   if (a->value_cache != a->key_cache) return TSA_ERR_UNSUPPORTED;
+  if (!a16(a->q) || !a16(a->q_rope) || !a16(a->key_cache) || !a16(a->key_rope_cache) ||
+      !a16(a->out))
+    return TSA_ERR_INVALID;
   return TSA_OK;
 }
 
@@ -540,6 +552,9 @@ int check_sfa_sharedkv(const sfa_sharedkv_fwd_args* a) {
                           !a->cmp_topk_indices))
       return TSA_ERR_NULL;
   }
+  if (!a16(a->q) || !a16(a->q_rope) || !a16(a->out) || !a16(a->ori_key_cache) ||
+      !a16(a->ori_key_rope_cache) || !a16(a->cmp_key_cache) || !a16(a->cmp_key_rope_cache))
+    return TSA_ERR_INVALID;
   return TSA_OK;
 }
 
@@ -624,7 +639,7 @@ const char* tsa_status_string(int s) {
     case TSA_ERR_NULL: return "a required pointer is NULL";
     case TSA_ERR_INVALID: return "a value or shape violates a documented constraint";
     case TSA_ERR_UNSUPPORTED: return "valid for the operator but not built in this library";
-    case TSA_ERR_WORKSPACE: return "workspace missing or too small";
+    case TSA_ERR_WORKSPACE: return "workspace missing, too small or not 16-byte aligned";
     case TSA_ERR_HIP: return "a HIP launch or runtime call failed";
     case TSA_ERR_DATA: return "input data out of range (validate = 1)";
     default: return "unknown status";
@@ -669,7 +684,7 @@ int bsa_compact(const bsa_fwd_args* a, int32_t* row_ptr, int32_t* col, int32_t* 
   if (s) return s;
   if (!row_ptr || !col || !rev_ptr || !rev || (a->B * (long)a->Sq > 0 && !a->block_mask))
     return TSA_ERR_NULL;
-  if (!ws || ws_bytes < need) return TSA_ERR_WORKSPACE;
+  if (!ws || !a16(ws) || ws_bytes < need) return TSA_ERR_WORKSPACE;
   BsaWs w;
   bsa_carve(a, ws, &w, false);
   const int QB = (int)cdiv(a->Sq, a->block_q), KB = (int)cdiv(a->Skv, a->block_kv);
@@ -688,7 +703,7 @@ int bsa_fwd(const bsa_fwd_args* a, void* ws, size_t ws_bytes, void* stream) {
   size_t need;
   int s = bsa_fwd_workspace_size(a, &need);
   if (s) return s;
-  if (!ws || ws_bytes < need) return TSA_ERR_WORKSPACE;
+  if (!ws || !a16(ws) || ws_bytes < need) return TSA_ERR_WORKSPACE;
   if (bsa_q_rows(a) == 0) return TSA_OK;
   hipStream_t st = (hipStream_t)stream;
   BsaWs w;
@@ -732,7 +747,7 @@ int bsa_bwd(const bsa_bwd_args* a, void* ws, size_t ws_bytes, void* stream) {
   size_t need;
   int s = bsa_bwd_workspace_size(a, &need);
   if (s) return s;
-  if (!ws || ws_bytes < need) return TSA_ERR_WORKSPACE;
+  if (!ws || !a16(ws) || ws_bytes < need) return TSA_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   BsaWs w;
   bsa_carve(a, ws, &w, true);
@@ -789,7 +804,7 @@ int nsa_compact(const nsa_select_fwd_args* a, int32_t* row_ptr, int32_t* col, in
   int s = nsa_compact_workspace_size(a, &need);
   if (s) return s;
   if (!row_ptr || !col || !rev_ptr || !rev) return TSA_ERR_NULL;
-  if (!ws || ws_bytes < need) return TSA_ERR_WORKSPACE;
+  if (!ws || !a16(ws) || ws_bytes < need) return TSA_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   NsaWs w;
   nsa_carve(a, ws, &w, false);
@@ -809,7 +824,7 @@ int nsa_select_fwd(const nsa_select_fwd_args* a, void* ws, size_t ws_bytes, void
   size_t need;
   int s = nsa_select_fwd_workspace_size(a, &need);
   if (s) return s;
-  if (!ws || ws_bytes < need) return TSA_ERR_WORKSPACE;
+  if (!ws || !a16(ws) || ws_bytes < need) return TSA_ERR_WORKSPACE;
   if (a->T == 0) return TSA_OK;
   hipStream_t st = (hipStream_t)stream;
   NsaWs w;
@@ -846,6 +861,7 @@ int nsa_select_bwd_workspace_size(const nsa_select_bwd_args* a, size_t* bytes) {
   if (a->reuse_lists < 0 || a->reuse_lists > 2) return TSA_ERR_INVALID;
   if (a->T > 0 && (!a->out || !a->dout || !a->lse || !a->dq)) return TSA_ERR_NULL;
   if (a->Tk > 0 && (!a->dk || !a->dv)) return TSA_ERR_NULL;
+  if (!a16(a->dout) || !a16(a->dq) || !a16(a->dk) || !a16(a->dv)) return TSA_ERR_INVALID;
   *bytes = nsa_carve(a, nullptr, nullptr, true);
   return TSA_OK;
 }
@@ -854,7 +870,7 @@ int nsa_select_bwd(const nsa_select_bwd_args* a, void* ws, size_t ws_bytes, void
   size_t need;
   int s = nsa_select_bwd_workspace_size(a, &need);
   if (s) return s;
-  if (!ws || ws_bytes < need) return TSA_ERR_WORKSPACE;
+  if (!ws || !a16(ws) || ws_bytes < need) return TSA_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   NsaWs w;
   nsa_carve(a, ws, &w, true);
@@ -903,7 +919,7 @@ int sfa_paged_fwd(const sfa_paged_fwd_args* a, void* ws, size_t ws_bytes, void* 
   size_t need;
   int s = sfa_paged_fwd_workspace_size(a, &need);
   if (s) return s;
-  if (!ws || ws_bytes < need) return TSA_ERR_WORKSPACE;
+  if (!ws || !a16(ws) || ws_bytes < need) return TSA_ERR_WORKSPACE;
   if (sfa_tokens(a) == 0) return TSA_OK;
   hipStream_t st = (hipStream_t)stream;
   SfaParams p;
@@ -978,7 +994,7 @@ int sfa_sharedkv_fwd(const sfa_sharedkv_fwd_args* a, void* ws, size_t ws_bytes, 
   size_t need;
   int s = sfa_sharedkv_fwd_workspace_size(a, &need);
   if (s) return s;
-  if (!ws || ws_bytes < need) return TSA_ERR_WORKSPACE;
+  if (!ws || !a16(ws) || ws_bytes < need) return TSA_ERR_WORKSPACE;
   if (a->tasks && (uintptr_t)a->tasks % 16) return TSA_ERR_INVALID;
   if (skv_tokens(a) == 0) return TSA_OK;
   hipStream_t st = (hipStream_t)stream;
