@@ -311,7 +311,8 @@ TSA_API int nsa_select_bwd(const nsa_select_bwd_args* args, void* workspace, siz
                    void* stream);
 
 /* The lists of topk_indices, as the kernels use them.  Uses the shape fields,
- * cu_seqlens, sbs, sbc, sparse_mode and topk of args.  With R = T*N2 rows and
+ * cu_seqlens, sbs, sbc, sparse_mode and topk of args; q, k, v, out and lse
+ * are not read and may be NULL.  With R = T*N2 rows and
  * NB = sum_b ceil(Skv_b/sbs) blocks:
  *   row_ptr int32 DEVICE [R+1]; col int32 DEVICE [R*sbc]: per (t, n2) the
  *     block ids sorted ascending (mode 2: blocks wholly after t dropped);

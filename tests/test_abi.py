@@ -196,6 +196,15 @@ def test_nsa_sequence_constraints(tsa):
     assert nb.value == (256 + 512) // 64
 
 
+def test_nsa_list_calls_need_only_topk(tsa):
+    """The list calls read shapes, cu_seqlens and topk: NULL attention tensors
+    pass there and are refused by the forward."""
+    a = _nsa(tsa, q=0, k=0, v=0, out=0, lse=0)
+    assert _size(tsa, tsa.lib.nsa_compact_workspace_size, a)[0] == 0
+    assert _size(tsa, tsa.lib.nsa_select_fwd_workspace_size, a)[0] == 1
+    assert _size(tsa, tsa.lib.nsa_compact_workspace_size, _nsa(tsa, topk=0))[0] == 1
+
+
 def _sfa(tsa, **kw):
     a = dict(dtype=0, q_layout=2, B=32, Sq=4, N1=64, N2=1, D=512, Dr=64, Dv=512,
              num_pages=16384, page_size=128, max_pages=512, topk=2048, sparse_block_size=1,

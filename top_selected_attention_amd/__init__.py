@@ -365,8 +365,7 @@ def nsa_compact(topk, cu_seqlens_q, cu_seqlens_kv, N1, sbs, sparse_mode=2, valid
                         cu_seqlens_q=ctypes.cast(cu_q.data_ptr(), ctypes.POINTER(ctypes.c_int32)),
                         cu_seqlens_kv=ctypes.cast(cu_kv.data_ptr(), ctypes.POINTER(ctypes.c_int32)),
                         sbs=sbs, sbc=sbc, sparse_mode=sparse_mode, scale=1.0,
-                        validate=int(bool(validate)), topk=topk.data_ptr(), q=1, k=1, v=1, out=1,
-                        lse=1)
+                        validate=int(bool(validate)), topk=topk.data_ptr())
     nb = ctypes.c_size_t()
     _abi.call(lib.nsa_compact_workspace_size, ctypes.byref(a), ctypes.byref(nb))
     NB = ctypes.c_int32()

@@ -262,7 +262,7 @@ BsaParams bsa_params(int B, int N1, int N2, int Sq, int Skv, int bq, int bkv, in
 // ---------------------------------------------------------------------------
 
 template <class A>
-int check_nsa(const A* a) {
+int check_nsa(const A* a, bool tensors = true) {
   if (!a) return TSA_ERR_NULL;
   if (a->dtype != TSA_BF16 && a->dtype != TSA_FP16) return TSA_ERR_INVALID;
   // "aclnnNsaSelectedAttention", constraints: inputLayout supports only TND.
@@ -295,8 +295,9 @@ int check_nsa(const A* a) {
   if (cq[a->B] != a->T || ck[a->B] != a->Tk) return TSA_ERR_INVALID;
   if (!fits_i32((long)a->T * a->N2 * a->sbc) || !fits_i32((long)a->T * a->N1 * a->D))
     return TSA_ERR_INVALID;
-  if (a->T > 0 && (!a->q || !a->out || !a->lse || !a->topk)) return TSA_ERR_NULL;
-  if (a->T > 0 && (!a->k || !a->v)) return TSA_ERR_NULL;
+  if (a->T > 0 && !a->topk) return TSA_ERR_NULL;
+  if (!tensors) return TSA_OK;  // the list calls read only shapes and topk
+  if (a->T > 0 && (!a->q || !a->out || !a->lse || !a->k || !a->v)) return TSA_ERR_NULL;
   if (!a16(a->q) || !a16(a->k) || !a16(a->v) || !a16(a->out)) return TSA_ERR_INVALID;
   return TSA_OK;
 }
@@ -784,7 +785,7 @@ int bsa_bwd(const bsa_bwd_args* a, void* ws, size_t ws_bytes, void* stream) {
 
 int nsa_compact_blocks_total(const nsa_select_fwd_args* a, int32_t* nb) {
   if (!nb) return TSA_ERR_NULL;
-  int s = check_nsa(a);
+  int s = check_nsa(a, false);
   if (s) return s;
   *nb = nsa_blocks_total(a->cu_seqlens_kv, a->B, a->sbs);
   return TSA_OK;
@@ -792,7 +793,7 @@ int nsa_compact_blocks_total(const nsa_select_fwd_args* a, int32_t* nb) {
 
 int nsa_compact_workspace_size(const nsa_select_fwd_args* a, size_t* bytes) {
   if (!bytes) return TSA_ERR_NULL;
-  int s = check_nsa(a);
+  int s = check_nsa(a, false);
   if (s) return s;
   *bytes = nsa_carve(a, nullptr, nullptr, false);
   return TSA_OK;
@@ -816,8 +817,12 @@ int nsa_compact(const nsa_select_fwd_args* a, int32_t* row_ptr, int32_t* col, in
 }
 
 int nsa_select_fwd_workspace_size(const nsa_select_fwd_args* a, size_t* bytes) {
+  if (!bytes) return TSA_ERR_NULL;
   if (a && a->reuse_lists != 0 && a->reuse_lists != 1) return TSA_ERR_INVALID;
-  return nsa_compact_workspace_size(a, bytes);
+  int s = check_nsa(a);
+  if (s) return s;
+  *bytes = nsa_carve(a, nullptr, nullptr, false);
+  return TSA_OK;
 }
 
 int nsa_select_fwd(const nsa_select_fwd_args* a, void* ws, size_t ws_bytes, void* stream) {
