@@ -7,10 +7,14 @@ stream.  All arithmetic runs in the library's HIP kernels; there is no other
 execution path, and importing this package raises if the library is missing.
 
 Entry points (names as in the C ABI):
-  bsa_fwd, bsa_bwd, bsa_compact             block-sparse attention (BNSD)
+  bsa_fwd, bsa_bwd, bsa_compact             block-sparse attention (BNSD or
+                                             TND, optional atten_mask)
   nsa_select_fwd, nsa_select_bwd, nsa_compact   NSA selected attention (TND)
   sfa_paged_fwd                              sparse flash attention decode
-The ``*Plan`` classes pre-allocate outputs and workspace for repeated calls.
+  sfa_sharedkv_fwd                           shared-KV decode: band over the
+                                             original cache + compressed top-k
+The ``*Plan`` classes (BsaPlan, NsaPlan, SfaPlan, SfaSharedkvPlan)
+pre-allocate outputs and workspace for repeated calls.
 """
 
 import ctypes
