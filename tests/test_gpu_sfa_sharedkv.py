@@ -154,3 +154,9 @@ def test_tokens_before_the_sequence_start_see_nothing():
     out, lse = _run_case([5, 2], [3, 300], 64, 16, 4, 8, 210)
     assert torch.all(out[:2] == 0) and torch.all(torch.isneginf(lse[:2]))
     assert torch.isfinite(lse[2:]).all()
+
+
+@pytest.mark.parametrize("N1", [1, 2, 128])
+def test_head_count_limits(N1):
+    """N1 from 1 (one partly used head group) to 128 (two head groups)."""
+    _run_case([2, 3], [500, 2000], N1, 64, 4, 64, 220 + N1)
