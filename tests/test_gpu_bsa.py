@@ -449,3 +449,22 @@ def test_bwd_shared_block_long_reverse_lists(mode):
     b = _bwd_gpu(q, k, v, do, mask, bq, bq, 1 / math.sqrt(128), mode)
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+def test_misaligned_tensor_is_refused_before_launch():
+    """A contiguous view at an odd element offset is not 16-byte aligned: the
+    binding refuses it, and so does the C ABI (status 2) if called directly."""
+    import ctypes
+    tsa = _tsa()
+    B, N, S, D, bq = 1, 2, 256, 128, 128
+    n = B * N * S * D
+    base = torch.zeros(n + 8, dtype=torch.bfloat16, device="cuda")
+    q_bad = base[1:n + 1].view(B, N, S, D)                 # 2 bytes past a 16-byte boundary
+    k = torch.zeros(B, N, S, D, dtype=torch.bfloat16, device="cuda")
+    mask = torch.ones(B, N, S // bq, S // bq, dtype=torch.uint8, device="cuda")
+    with pytest.raises(ValueError, match="16-byte"):
+        tsa.bsa_fwd(q_bad, k, k, mask, bq, bq)
+    plan = tsa.BsaPlan(k, k, k, mask, bq, bq, 0.088, 0, backward=False)
+    plan.fa.q = q_bad.data_ptr()
+    n_ws = ctypes.c_size_t()
+    assert tsa.lib.bsa_fwd_workspace_size(ctypes.byref(plan.fa), ctypes.byref(n_ws)) == 2

@@ -45,7 +45,9 @@ def _dtype_code(t):
     raise TypeError(f"expected bfloat16 or float16, got {t.dtype}")
 
 
-def _check(t, name, dtype=None, shape=None):
+def _check(t, name, dtype=None, shape=None, align16=None):
+    """align16 (default: for 16-bit float tensors): the kernels move the
+    tensor in 16-byte pieces, so its address must be a multiple of 16."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if not t.is_cuda:
@@ -56,6 +58,11 @@ def _check(t, name, dtype=None, shape=None):
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if shape is not None and tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if align16 is None:
+        align16 = t.dtype in (torch.bfloat16, torch.float16)
+    if align16 and t.data_ptr() % 16:
+        raise ValueError(f"{name} must start at a 16-byte aligned address (a view at an "
+                         f"element offset is not): {t.data_ptr():#x}")
     return t
 
 
@@ -123,7 +130,7 @@ class BsaPlan:
                 raise ValueError("q and k disagree in B or D")
             lse_shape, layout, seq = (B, N1, Sq), LAYOUT_BNSD, {}
         QB, KB = _ceil(Sq, block_q), _ceil(Skv, block_kv)
-        _check(block_mask, "block_mask", torch.uint8, (B, N1, QB, KB))
+        _check(block_mask, "block_mask", torch.uint8, (B, N1, QB, KB), align16=True)
         seq.update(_atten_mask_fields(atten_mask, B, N1, Sq, Skv))
         self.atten_mask = atten_mask
         self.q, self.k, self.v, self.mask = q, k, v, block_mask
@@ -236,7 +243,8 @@ def bsa_compact(block_mask, N2, Sq, Skv, block_q, block_kv):
     """The forward / reverse CSR lists of a BlockSparseMask (int32 device tensors,
     entry arrays trimmed to their used length)."""
     B, N1, QB, KB = block_mask.shape
-    _check(block_mask, "block_mask", torch.uint8, (B, N1, _ceil(Sq, block_q), _ceil(Skv, block_kv)))
+    _check(block_mask, "block_mask", torch.uint8, (B, N1, _ceil(Sq, block_q), _ceil(Skv, block_kv)),
+           align16=True)
     dev = block_mask.device
     a = _abi.BsaFwdArgs(dtype=BF16, q_layout=LAYOUT_BNSD, kv_layout=LAYOUT_BNSD, B=B, N1=N1,
                         N2=N2, Sq=Sq, Skv=Skv, D=128, block_q=block_q, block_kv=block_kv,
