@@ -160,3 +160,16 @@ def test_tokens_before_the_sequence_start_see_nothing():
 def test_head_count_limits(N1):
     """N1 from 1 (one partly used head group) to 128 (two head groups)."""
     _run_case([2, 3], [500, 2000], N1, 64, 4, 64, 220 + N1)
+
+
+def test_no_tokens_at_all():
+    """Every entry without decode tokens: the calls launch nothing and return
+    empty outputs."""
+    tsa = _tsa()
+    cu, q, qr, kvl, ori, cmp = W.sfa_sharedkv_inputs(lens=[0, 0], kv_lens=[100, 300], N1=64,
+                                                     page=32, cmp_ratio=4, cmp_topk=16,
+                                                     seed_base=260)
+    out, lse = tsa.sfa_sharedkv_fwd(_dev(q), _dev(qr), _dev(kvl), tuple(_dev(t) for t in ori),
+                                    tuple(_dev(t) for t in cmp), 0.04, cu_seqlens_q=cu)
+    torch.cuda.synchronize()
+    assert tuple(out.shape) == (0, 64, 512) and tuple(lse.shape) == (0, 64)
