@@ -780,8 +780,9 @@ def ingest_copy(d):
 def ingest(d, workload):
     """Writes profiles/<dominant kernel>_<workload>.md from the kernel trace
     under d/trace (with the bench line the traced run printed, d/bench.json)
-    and the counter runs under d/fetch, d/write; records each library
-    kernel's calibrated HBM bytes per launch in profiles/traffic.json."""
+    and the counter runs under d/fetch, d/write (and, when present, the MFMA
+    counter run under d/mfma); records each library kernel's calibrated HBM
+    bytes per launch in profiles/traffic.json."""
     tr = {}
     for r in _csv_rows(os.path.join(d, "trace"), "kernel_trace.csv"):
         name = r["Kernel_Name"]
@@ -815,6 +816,16 @@ def ingest(d, workload):
                           "bytes_per_launch": int(round(fb + wb)),
                           "avg_us_kernel_trace": round(sum(v) / len(v), 1)}
     _save_traffic(t)
+    mdir = os.path.join(d, "mfma")
+    mlines = []
+    if os.path.isdir(mdir):
+        util = _counter_means(mdir, "MfmaUtil")
+        fbf = _counter_means(mdir, "MfmaFlopsBF16")
+        ffp = _counter_means(mdir, "MfmaFlopsF16")
+        for k in sorted(tr, key=lambda k: -sum(tr[k])):
+            fl = fbf.get(k, 0.0) + ffp.get(k, 0.0)
+            if fl > 0:
+                mlines.append(f"| `{k}` | {util.get(k, 0.0):.1f} | {fl / 1e9:.2f} |")
     rl = bench["roofline"]
     cmd = (f"python3 bench.py --workload {workload} --steps {bench['steps']} "
            f"--warmup {bench['warmup']} --cpu-seconds 0 --no-peaks")
@@ -833,6 +844,8 @@ def ingest(d, workload):
         f"rocprofv3 --kernel-trace --stats --output-format csv -d {d}/trace -o run -- {cmd} > {d}/bench.json",
         f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d}/fetch -o run -- {pcmd}",
         f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}/write -o run -- {pcmd}",
+    ] + ([f"rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 MfmaFlopsF16 --output-format csv -d {d}/mfma "
+          f"-o run -- {pcmd}"] if mlines else []) + [
         f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {cdir}/fetch -o run -- python3 bench.py --copy-calibration",
         f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {cdir}/write -o run -- python3 bench.py --copy-calibration",
         f"python3 bench.py --ingest-copy {cdir}",
@@ -859,6 +872,16 @@ def ingest(d, workload):
         f"{bench['ms_per_step']} ms per step.",
         "",
     ]
+    if mlines:
+        out += [
+            "MFMA counters (mean per dispatch): MfmaUtil = MFMA-busy cycles summed over the "
+            "SIMDs / (GPU-active cycles x SIMD count) x 100; MFMA GFLOP = the issued MFMA "
+            "operations (SQ_INSTS_VALU_MFMA_MOPS_BF16 + _F16, 512 FLOP each), masked and "
+            "padded work included.",
+            "",
+            "| kernel | MfmaUtil (%) | MFMA GFLOP / launch |",
+            "|---|---|---|",
+        ] + mlines + [""]
     path = os.path.join(ROOT, "profiles", f"{dom}_{workload}.md")
     with open(path, "w") as f:
         f.write("\n".join(out))
