@@ -196,6 +196,88 @@ def test_sfa_page_table_permutation_is_invisible():
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
+def _sdpa_over_positions(q_tok, qr_tok, kc, krc, bt_row, selected, scale):
+    """torch float64 attention of one decode token's heads over the cache
+    rows at the positions where ``selected`` (bool over positions) is true;
+    the value is the 512-wide key row (shared KV)."""
+    pos = np.nonzero(selected)[0]
+    page = kc.shape[1]
+    keys = np.concatenate([kc[bt_row[pos // page], pos % page, 0],
+                           krc[bt_row[pos // page], pos % page, 0]], -1)
+    vals = kc[bt_row[pos // page], pos % page, 0]
+    qq = torch.tensor(np.concatenate([q_tok, qr_tok], -1))             # [N1, D+Dr]
+    H = qq.shape[0]
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        qq[:, None], torch.tensor(keys)[None].expand(H, -1, -1),
+        torch.tensor(vals)[None].expand(H, -1, -1), scale=scale)[:, 0]
+    return ref.numpy(), torch.logsumexp(scale * qq @ torch.tensor(keys).T, -1).numpy()
+
+
+@pytest.mark.parametrize("mode", [0, 3])
+def test_sfa_sparse_blocks_equal_attention_over_the_blocks_positions(mode):
+    """"aclnnSparseFlashAttention", constraints section: an id selects a
+    sparse block of sparse_block_size consecutive positions.  Position p
+    belongs to the block p // sbs; the positions are marked from that
+    membership test (not by expanding ids), and torch attends over them:
+    the sequence's last block is partial (kv_len 30, sbs 4) and, under
+    rightDownCausal, the cut falls inside a selected block."""
+    r = _rng(33)
+    B, Sq, N1, D, Dr, page, sbs = 2, 3, 4, 16, 8, 8, 4
+    kv_lens = np.array([30, 21])
+    P = 12
+    q, qr = r.standard_normal((B, Sq, N1, D)), r.standard_normal((B, Sq, N1, Dr))
+    kc, krc = r.standard_normal((P, page, 1, D)), r.standard_normal((P, page, 1, Dr))
+    bt = r.permutation(P).reshape(B, 6)[:, :4]
+    K = 4
+    topk = np.full((B, Sq, 1, K), -1)
+    for b in range(B):
+        nblk = -(-int(kv_lens[b]) // sbs)
+        for s in range(Sq):
+            ids = r.choice(nblk - 1, 2, replace=False)
+            # the last (partial / causally cut) block first; slot 3 stays empty (-1)
+            topk[b, s, 0, :3] = [nblk - 1, ids[0], ids[1]]
+    scale = 1 / math.sqrt(D + Dr)
+    out, lse = oracle.sfa_fwd(q, qr, kc, krc, kc, bt, kv_lens, topk, scale, sparse_mode=mode,
+                              sparse_block_size=sbs)
+    for b in range(B):
+        n = int(kv_lens[b])
+        positions = np.arange(n)
+        for s in range(Sq):
+            chosen = set(int(i) for i in topk[b, s, 0] if i >= 0)
+            selected = np.array([(p // sbs) in chosen for p in positions])
+            if mode == 3:
+                selected &= positions <= n - Sq + s
+            ref, ref_lse = _sdpa_over_positions(q[b, s], qr[b, s], kc, krc, bt[b], selected, scale)
+            np.testing.assert_allclose(out[b, s], ref, rtol=0, atol=1e-12)
+            np.testing.assert_allclose(lse[b, s], ref_lse, rtol=0, atol=1e-12)
+
+
+def test_sfa_mode0_all_tokens_is_dense_mqa_without_a_mask():
+    """sparse_mode 0 masks nothing: with every position selected, each decode
+    token (even the earlier ones of Sq = 3, which rightDownCausal would cut)
+    is dense MQA over the whole sequence (torch, no attn_mask)."""
+    r = _rng(34)
+    B, Sq, N1, D, Dr, page, kv_len = 2, 3, 4, 16, 8, 8, 24
+    q, qr = r.standard_normal((B, Sq, N1, D)), r.standard_normal((B, Sq, N1, Dr))
+    P = B * kv_len // page
+    kc, krc = r.standard_normal((P, page, 1, D)), r.standard_normal((P, page, 1, Dr))
+    bt = r.permutation(P).reshape(B, kv_len // page)
+    kv_lens = np.full(B, kv_len)
+    topk = np.tile(np.arange(kv_len), (B, Sq, 1, 1))
+    scale = 1 / math.sqrt(D + Dr)
+    out, lse = oracle.sfa_fwd(q, qr, kc, krc, kc, bt, kv_lens, topk, scale, sparse_mode=0)
+    for b in range(B):
+        keys = kc[bt[b]].reshape(kv_len, D)
+        kro = krc[bt[b]].reshape(kv_len, Dr)
+        qcat = torch.tensor(np.concatenate([q[b], qr[b]], -1)).transpose(0, 1)   # [N1, Sq, D+Dr]
+        kcat = torch.tensor(np.concatenate([keys, kro], -1))[None].expand(N1, -1, -1)
+        vals = torch.tensor(keys)[None].expand(N1, -1, -1)
+        ref = torch.nn.functional.scaled_dot_product_attention(qcat, kcat, vals, scale=scale)
+        np.testing.assert_allclose(out[b], ref.numpy().transpose(1, 0, 2), atol=1e-12, rtol=0)
+        full = torch.logsumexp(scale * qcat @ kcat.transpose(1, 2), -1).numpy().T
+        np.testing.assert_allclose(lse[b], full, atol=1e-12, rtol=0)
+
+
 # ----------------------------------------------------------------------------
 # Shared-KV two-branch decode (band over the original KV + compressed top-k)
 # ----------------------------------------------------------------------------
@@ -240,6 +322,37 @@ def test_sfa_sharedkv_equals_dense_attention_over_the_union():
             np.testing.assert_allclose(out[t], ref.numpy(), rtol=0, atol=1e-12)
             np.testing.assert_allclose(lse[t], torch.logsumexp(scale * qq @ kk.T, -1).numpy(),
                                        rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("wl,wr", [(3, 2), (0, 5), (127, 1)])
+def test_sfa_sharedkv_band_with_future_tokens_equals_attention_over_it(wl, wr):
+    """"SparseAttnSharedkvMetadata", parameter list: mask mode 4 keeps
+    ori_win_left past and ori_win_right future original tokens around the
+    query's position p.  The band is marked per position by the offset test
+    -wl <= j - p <= wr (and 0 <= j < kv_len), not by a range; torch attends
+    over the marked rows.  Later decode tokens' bands reach past kv_len and
+    are clipped there."""
+    cu, q, qr, kvl, ori, cmp = _skv_small(44, lens=(1, 3, 2), kv_lens=(40, 70, 9))
+    scale = 0.23
+    out, lse = oracle.sfa_sharedkv_fwd(q, qr, cu, kvl, scale, ori=ori, cmp=None, win_left=wl,
+                                       win_right=wr)
+    for b in range(len(kvl)):
+        sq, n = int(cu[b + 1] - cu[b]), int(kvl[b])
+        j = np.arange(n)
+        for s in range(sq):
+            t = int(cu[b]) + s
+            p = n - sq + s
+            selected = (j - p >= -wl) & (j - p <= wr)
+            ref, ref_lse = _sdpa_over_positions(q[t], qr[t], ori[0], ori[1], ori[2][b], selected,
+                                                scale)
+            np.testing.assert_allclose(out[t], ref, rtol=0, atol=1e-12)
+            np.testing.assert_allclose(lse[t], ref_lse, rtol=0, atol=1e-12)
+    # the future half matters: entry 1's first token (p = kv_len - 3) has two
+    # future tokens, and a band without them differs
+    o0, _ = oracle.sfa_sharedkv_fwd(q, qr, cu, kvl, scale, ori=ori, cmp=None, win_left=wl,
+                                    win_right=0)
+    t1 = int(cu[1])
+    assert not np.allclose(o0[t1], out[t1])
 
 
 def test_sfa_sharedkv_band_alone_is_sfa_over_the_window():
