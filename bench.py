@@ -1,20 +1,25 @@
 #!/usr/bin/env python3
 """Throughput of the selected-block attention hot path on one MI355X.
 
-Default workload (``bsa_causal_8k``): block-sparse attention forward +
-backward, BNSD, B=2, N1=N2=16, S=8192, D=128, bf16, 128x128 blocks, causal
-block mask with the diagonal kept and every other block kept with p=0.25.
+Default workload (``bsa_window_128k``, the largest one-GPU configuration):
+block-sparse attention forward + backward, BNSD, B=1, N1=N2=8, S=131072,
+D=128, bf16, 128x128 blocks; each Q block selects its 8-block sliding
+window plus 24 distinct random earlier blocks (258,176 selected pairs).
 One step = the whole path over one batch: mask compaction + forward
-attention, then compaction + dQ (with softmax_grad) + dK/dV.
+attention, then dQ (with softmax_grad) + dK/dV reusing the lists.
 
 Prints ONE JSON line.  ``value`` is effective TFLOP/s counted on the
 selected blocks only (forward 4*rows*keys*D per selected block pair,
-backward 2.5x that), i.e. algorithmic FLOPs / measured step time.
+backward 2.5x that), i.e. algorithmic FLOPs / measured step time.  The same
+run then times the further workloads named by ``--also`` (by default
+bsa_causal_8k, nsa_varlen and sfa_decode) and reports them under
+``workloads``; only the main workload carries the oracle CPU baseline.
 
-Other workloads (``--workload``): bsa_small, bsa_window_128k, bsa_tnd_varlen
+Workloads (``--workload``): bsa_window_128k, bsa_causal_8k (B=2, N=16,
+S=8192, causal block mask with p=0.25), bsa_small, bsa_tnd_varlen
 (block-sparse in TND layout over sequences of 2048, 4096, 8192, 2048 tokens,
-16 query / 4 KV heads), nsa_varlen (forward + backward) and sfa_decode
-(forward; value in GB/s of algorithmic gathered bytes).
+16 query / 4 KV heads), nsa_varlen (forward + backward), sfa_decode and
+sfa_sharedkv_decode (forward; value in GB/s of algorithmic gathered bytes).
 """
 
 import argparse
@@ -42,9 +47,15 @@ def parse():
     # enough untimed steps for the GPU clocks to settle (timing right after a
     # cold start reads several percent slow)
     ap.add_argument("--warmup", type=int, default=1000)
-    ap.add_argument("--workload", default="bsa_causal_8k",
-                    choices=["bsa_causal_8k", "bsa_small", "bsa_window_128k", "bsa_tnd_varlen",
-                             "nsa_varlen", "sfa_decode", "sfa_sharedkv_decode"])
+    ap.add_argument("--workload", default="bsa_window_128k", choices=WORKLOADS)
+    ap.add_argument("--also", default="bsa_causal_8k,nsa_varlen,sfa_decode",
+                    help="comma-separated workloads timed after the main one in the same run "
+                         "(same steps and warm-up) and reported under 'workloads'; 'none' = "
+                         "only the main workload")
+    ap.add_argument("--settle-seconds", type=float, default=1.0,
+                    help="after the warm-up steps, further untimed steps until this much "
+                         "warm-up time has passed (the GPU clocks need about a second of load "
+                         "to settle); their count is reported as settle_steps")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the measured GEMM / copy peaks reported beside the published ones")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -58,6 +69,27 @@ def parse():
                     help="summarise rocprofv3 runs of --workload (DIR/trace, DIR/bench.json, "
                          "DIR/fetch, DIR/write) into profiles/ (no GPU needed)")
     return ap.parse_args()
+
+
+WORKLOADS = ["bsa_window_128k", "bsa_causal_8k", "bsa_small", "bsa_tnd_varlen", "nsa_varlen",
+             "sfa_decode", "sfa_sharedkv_decode"]
+
+
+def _warm(step, args):
+    """args.warmup untimed steps, then more until args.settle_seconds of
+    warm-up have passed.  Returns the number of the extra steps."""
+    import torch
+    t0 = time.perf_counter()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    extra = 0
+    while time.perf_counter() - t0 < args.settle_seconds:
+        for _ in range(8):
+            step()
+        extra += 8
+        torch.cuda.synchronize()
+    return extra
 
 
 def _events(n):
@@ -180,6 +212,7 @@ def bench_bsa(args):
         "ms_per_step_instrumented": round(ms_ev, 4),
         "step_ms_events": _step_stats(plan.step_ms),
         "ms_per_step_cold": round(plan.cold_ms, 4),
+        "settle_steps": plan.settle_steps,
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
@@ -195,8 +228,10 @@ def cpu_baseline_bsa(ctx, seconds):
     bq, bkv = w["bq"], w["bkv"]
     qn, kn, vn, don = (t.float().numpy() for t in (q, k, v, do))
     QB = mask.shape[2]
-    # longest-list-first order within head (0, 0), then the next heads
-    order = [(b, n, qb) for b in range(w["B"]) for n in range(w["N1"]) for qb in range(QB)]
+    # every 37th Q block in head-major order (37 is prime to the block counts),
+    # so the sample mixes heads, positions and list lengths like the workload
+    allt = [(b, n, qb) for b in range(w["B"]) for n in range(w["N1"]) for qb in range(QB)]
+    order = [allt[(i * 37) % len(allt)] for i in range(len(allt))]
     done, flops = 0, 0.0
     t0 = time.perf_counter()
     for tile in order:
@@ -213,8 +248,8 @@ def cpu_baseline_bsa(ctx, seconds):
     el = time.perf_counter() - t0
     return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": _threads(),
             "kind": "oracle",
-            "sample": f"{done} of {len(order)} Q blocks (fwd + bwd, float64) of {w['name']}, "
-                      f"{el:.1f} s"}
+            "sample": f"{done} of {len(order)} Q blocks (every 37th in head-major order; "
+                      f"fwd + bwd, float64) of {w['name']}, {el:.1f} s"}
 
 
 def _tnd_pair_flops(mask, seqlens, bq, bkv, D=128):
@@ -268,6 +303,7 @@ def bench_bsa_tnd(args):
         "ms_per_step_instrumented": round(ms_ev, 4),
         "step_ms_events": _step_stats(plan.step_ms),
         "ms_per_step_cold": round(plan.cold_ms, 4),
+        "settle_steps": plan.settle_steps,
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
@@ -320,8 +356,14 @@ def bench_nsa(args):
     scale = 1.0 / math.sqrt(D)
     # effective (token, KV head, block) triples: blocks not wholly after the token
     pos = np.arange(int(cu[-1])) - np.repeat(cu[:-1], np.diff(cu))
-    triples = int((topk.astype(np.int64) * sbs <= pos[:, None, None]).sum())
+    start = topk.astype(np.int64) * sbs
+    kept = start <= pos[:, None, None]
+    triples = int(kept.sum())
     unit = float(triples) * G * sbs * D
+    # the count above takes a token's own (diagonal) block in full, as the
+    # metric's definition does; the keys the causal mask leaves there number
+    # pos - start + 1, so the exact count of unmasked keys is a little lower
+    exact_keys = float(np.where(kept, np.minimum(sbs, pos[:, None, None] - start + 1), 0).sum())
     fwd_flops, bwd_flops = 4.0 * unit, 10.0 * unit
     dev = torch.device("cuda", 0)
     plan = tsa.NsaPlan(q.to(dev), k.to(dev), v.to(dev), torch.from_numpy(topk).to(dev), cu, cu,
@@ -347,7 +389,11 @@ def bench_nsa(args):
         "scaling": "weak", "vs_baseline": None, "dtype": w["dtype"], "data": "synthetic",
         "config": {"workload": w["name"], "layout": "TND", "seqlens": w["seqlens"],
                    "N1": w["N1"], "N2": w["N2"], "D": D, "sbs": sbs, "sbc": w["sbc"],
-                   "sparse_mode": w["sparse_mode"], "effective_triples": triples},
+                   "sparse_mode": w["sparse_mode"], "effective_triples": triples,
+                   "flop_count": "4*G*sbs*D per kept (token, KV head, block), the own block "
+                                 "in full; value_unmasked_keys counts only keys the causal "
+                                 "mask leaves"},
+        "value_unmasked_keys": round(value * exact_keys / (triples * sbs), 2),
         "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "fwd_tflops": round(fwd_flops / (fwd_ms * 1e-3) / 1e12, 2),
         "bwd_tflops": round(bwd_flops / (bwd_ms * 1e-3) / 1e12, 2),
@@ -356,6 +402,7 @@ def bench_nsa(args):
         "ms_per_step_instrumented": round(ms_ev, 4),
         "step_ms_events": _step_stats(plan.step_ms),
         "ms_per_step_cold": round(plan.cold_ms, 4),
+        "settle_steps": plan.settle_steps,
         "fwd_gathered_GBps": round(gathered / (st[1] * 1e-3) / 1e9, 1),
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -416,9 +463,7 @@ def _time_forward(plan, n_stages, args):
     event ms, median cold ms)."""
     import torch
     K = args.steps
-    for _ in range(args.warmup):
-        plan.fwd()
-    torch.cuda.synchronize()
+    plan.settle_steps = _warm(plan.fwd, args)
     wall0 = time.perf_counter()
     for _ in range(K):
         plan.fwd()
@@ -474,6 +519,7 @@ def bench_sfa(args):
         "ms_per_step_instrumented": round(ms_ev, 4),
         "step_ms_events": _step_stats(step_ms),
         "ms_per_step_cold": round(cold_ms, 4),
+        "settle_steps": plan.settle_steps,
         "algorithmic_bytes": int(nbytes),
         "roofline": {"kernel": "sfa_split_kernel", "bound": "hbm", "achieved": round(kgbs, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(kgbs / PEAK_HBM_GBS, 4),
@@ -575,6 +621,7 @@ def bench_sfa_skv(args):
         "ms_per_step_instrumented": round(ms_ev, 4),
         "step_ms_events": _step_stats(step_ms),
         "ms_per_step_cold": round(cold_ms, 4),
+        "settle_steps": plan.settle_steps,
         "algorithmic_bytes": int(nbytes),
         "roofline": {"kernel": "sfa_split_kernel", "bound": "hbm", "achieved": round(kgbs, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(kgbs / PEAK_HBM_GBS, 4),
@@ -660,10 +707,11 @@ def _timed_steps(args, plan, nf, nb):
     instrumented step)."""
     import torch
     K = args.steps
-    for _ in range(args.warmup):
+
+    def fb():
         plan.fwd()
         plan.bwd()
-    torch.cuda.synchronize()
+    plan.settle_steps = _warm(fb, args)
     wall0 = time.perf_counter()
     for _ in range(K):
         plan.fwd()
@@ -931,31 +979,55 @@ def main():
     if args.copy_calibration:
         copy_calibration()
         return
-    if args.workload in CFG_OF:
-        res, ctx = bench_bsa(args)
-        if args.cpu_seconds > 0:
-            res["cpu_baseline"] = cpu_baseline_bsa(ctx, args.cpu_seconds)
-    elif args.workload == "bsa_tnd_varlen":
-        res, ctx = bench_bsa_tnd(args)
-        if args.cpu_seconds > 0:
-            res["cpu_baseline"] = cpu_baseline_bsa_tnd(ctx, args.cpu_seconds)
-    elif args.workload == "nsa_varlen":
-        res, ctx = bench_nsa(args)
-        if args.cpu_seconds > 0:
-            res["cpu_baseline"] = cpu_baseline_nsa(ctx, args.cpu_seconds)
-    elif args.workload == "sfa_sharedkv_decode":
-        res, ctx = bench_sfa_skv(args)
-        if args.cpu_seconds > 0:
-            res["cpu_baseline"] = cpu_baseline_sfa_skv(ctx, args.cpu_seconds)
-    else:
-        res, ctx = bench_sfa(args)
-        if args.cpu_seconds > 0:
-            res["cpu_baseline"] = cpu_baseline_sfa(ctx, args.cpu_seconds)
-    if "cpu_baseline" in res:
+    res, ctx = run_workload(args.workload, args)
+    if args.cpu_seconds > 0:
+        res["cpu_baseline"] = CPU_BASELINE[_kind(args.workload)](ctx, args.cpu_seconds)
         res["cpu_baseline"].update(_host())
+    del ctx
+    also = [] if args.also in ("", "none") else [x for x in args.also.split(",") if x]
+    for name in also:
+        if name not in WORKLOADS:
+            print(f"unknown workload {name!r} in --also", file=sys.stderr)
+            sys.exit(2)
+    extra = {}
+    for name in also:
+        if name == args.workload:
+            continue
+        torch.cuda.empty_cache()
+        r, c = run_workload(name, args)
+        del c
+        extra[name] = {k_: r[k_] for k_ in EXTRA_KEYS if k_ in r}
+        print(f"# {name}: {r['value']} {r['unit']}", file=sys.stderr, flush=True)
+    if extra:
+        res["workloads"] = extra
     if not args.no_peaks:
         res["measured_peaks"] = measured_peaks()
     print(json.dumps(res), flush=True)
+
+
+# what the line carries for each further workload
+EXTRA_KEYS = ["metric", "value", "unit", "ms_per_step", "dtype", "config", "pct_of_bf16_peak",
+              "pct_of_hbm_peak", "fwd_tflops", "bwd_tflops", "effective_tflops", "stage_ms",
+              "ms_per_step_cold", "settle_steps", "roofline"]
+
+
+def _kind(name):
+    return "bsa" if name in CFG_OF else name
+
+
+BENCH = {"bsa": bench_bsa, "bsa_tnd_varlen": bench_bsa_tnd, "nsa_varlen": bench_nsa,
+         "sfa_decode": bench_sfa, "sfa_sharedkv_decode": bench_sfa_skv}
+CPU_BASELINE = {"bsa": cpu_baseline_bsa, "bsa_tnd_varlen": cpu_baseline_bsa_tnd,
+                "nsa_varlen": cpu_baseline_nsa, "sfa_decode": cpu_baseline_sfa,
+                "sfa_sharedkv_decode": cpu_baseline_sfa_skv}
+
+
+def run_workload(name, args):
+    """Times one workload; returns (bench line dict, context for the oracle baseline)."""
+    import argparse
+    a = argparse.Namespace(**vars(args))
+    a.workload = name
+    return BENCH[_kind(name)](a)
 
 
 if __name__ == "__main__":

@@ -51,6 +51,15 @@ struct StageTimer {
     if (!ev || stage >= n) return hipSuccess;
     return hipEventRecord((hipEvent_t)ev[2 * stage + end], st);
   }
+  // A call with no work still records every requested stage, back to back.
+  hipError_t skip_all(int stages) const {
+    hipError_t e = hipSuccess;
+    for (int i = 0; i < stages && e == hipSuccess; i++) {
+      e = mark(i, 0);
+      if (e == hipSuccess) e = mark(i, 1);
+    }
+    return e;
+  }
 };
 
 template <class A>
@@ -242,6 +251,26 @@ void bsa_set_atten_mask(const A* a, BsaParams* p) {
   p->am_pitch = a->Skv;
   p->am_al4 = (((uintptr_t)p->am | (uintptr_t)p->am_sb | (uintptr_t)p->am_sn |
                 (uintptr_t)a->Skv | (uintptr_t)a->block_kv) & 3) == 0;
+}
+
+// Builds the forward and reverse lists, the tile order and the dK/dV
+// segment plan in the workspace.  Without query or key rows every list is
+// empty (and the mask, which such a call need not pass, is not read).
+template <class A>
+hipError_t bsa_build_lists(const A* a, const BsaWs& w, const BsaParams& p, hipStream_t st) {
+  const long R = (long)a->B * a->N1 * p.QB, C = (long)a->B * a->N2 * p.KB;
+  hipError_t e;
+  if (R > 0 && C > 0 && bsa_q_rows(a) > 0 && bsa_kv_rows(a) > 0) {
+    e = launch_bsa_compact(a->block_mask, a->B, a->N1, a->N2, p.QB, p.KB, w.parts, w.sums,
+                           w.row_ptr, w.col, w.rev_ptr, w.rev, st);
+  } else {
+    e = hipMemsetAsync(w.row_ptr, 0, sizeof(int) * (R + 1), st);
+    if (e == hipSuccess) e = hipMemsetAsync(w.rev_ptr, 0, sizeof(int) * (C + 1), st);
+  }
+  if (e == hipSuccess)
+    e = launch_tile_order(w.row_ptr, (int)R, w.order_q, w.rev_ptr, (int)C, w.order_kv,
+                          seg_plan(a, w, p), st);
+  return e;
 }
 
 BsaParams bsa_params(int B, int N1, int N2, int Sq, int Skv, int bq, int bkv, int mode,
@@ -705,7 +734,6 @@ int bsa_fwd(const bsa_fwd_args* a, void* ws, size_t ws_bytes, void* stream) {
   int s = bsa_fwd_workspace_size(a, &need);
   if (s) return s;
   if (!ws || !a16(ws) || ws_bytes < need) return TSA_ERR_WORKSPACE;
-  if (bsa_q_rows(a) == 0) return TSA_OK;
   hipStream_t st = (hipStream_t)stream;
   BsaWs w;
   bsa_carve(a, ws, &w, false);
@@ -714,24 +742,16 @@ int bsa_fwd(const bsa_fwd_args* a, void* ws, size_t ws_bytes, void* stream) {
   const StageTimer tm = timer_of(a, st);
   hipError_t e = bsa_upload_seqlens(a, w, &p, st);
   if (e == hipSuccess) e = tm.mark(0, 0);
-  if (e == hipSuccess && !a->reuse_lists) {
-    if (p.KB > 0)
-      e = launch_bsa_compact(a->block_mask, a->B, a->N1, a->N2, p.QB, p.KB, w.parts, w.sums,
-                             w.row_ptr, w.col, w.rev_ptr, w.rev, st);
-    else
-      e = hipMemsetAsync(w.row_ptr, 0, sizeof(int) * ((long)a->B * a->N1 * p.QB + 1), st);
-    if (e == hipSuccess)
-      e = launch_tile_order(w.row_ptr, a->B * a->N1 * p.QB, w.order_q, w.rev_ptr,
-                            p.KB > 0 ? a->B * a->N2 * p.KB : 0, w.order_kv, seg_plan(a, w, p),
-                            st);
-  }
+  // the lists are built even with no query rows, so that a backward reusing
+  // this workspace finds valid (empty) lists
+  if (e == hipSuccess && !a->reuse_lists) e = bsa_build_lists(a, w, p, st);
   if (e == hipSuccess) e = tm.mark(0, 1);
   if (e != hipSuccess) return TSA_ERR_HIP;
   p.q = a->q; p.k = a->k; p.v = a->v; p.out = a->out; p.lse = a->lse;
   p.row_ptr = w.row_ptr; p.col = w.col; p.order_q = w.order_q;
   bsa_set_atten_mask(a, &p);
   e = tm.mark(1, 0);
-  if (e == hipSuccess) e = launch_bsa_fwd(p, a->dtype == TSA_FP16, st);
+  if (e == hipSuccess && bsa_q_rows(a) > 0) e = launch_bsa_fwd(p, a->dtype == TSA_FP16, st);
   if (e == hipSuccess) e = tm.mark(1, 1);
   return hip_status(e);
 }
@@ -754,22 +774,13 @@ int bsa_bwd(const bsa_bwd_args* a, void* ws, size_t ws_bytes, void* stream) {
   bsa_carve(a, ws, &w, true);
   BsaParams p = bsa_params(a->B, a->N1, a->N2, a->Sq, a->Skv, a->block_q, a->block_kv,
                            a->sparse_mode, a->scale);
-  const long R = (long)a->B * a->N1 * p.QB, C = (long)a->B * a->N2 * p.KB;
   const StageTimer tm = timer_of(a, st);
   hipError_t e = bsa_upload_seqlens(a, w, &p, st);
   if (e == hipSuccess) e = tm.mark(0, 0);
-  if (e == hipSuccess && !a->reuse_lists) {
-    if (R > 0 && C > 0) {
-      e = launch_bsa_compact(a->block_mask, a->B, a->N1, a->N2, p.QB, p.KB, w.parts, w.sums,
-                             w.row_ptr, w.col, w.rev_ptr, w.rev, st);
-    } else {
-      e = hipMemsetAsync(w.row_ptr, 0, sizeof(int) * (R + 1), st);
-      if (e == hipSuccess) e = hipMemsetAsync(w.rev_ptr, 0, sizeof(int) * (C + 1), st);
-    }
-    if (e == hipSuccess)
-      e = launch_tile_order(w.row_ptr, (int)R, w.order_q, w.rev_ptr, (int)C, w.order_kv,
-                            seg_plan(a, w, p), st);
-  }
+  // without query or key rows the lists are empty: they are written here
+  // whatever reuse_lists says, so no kernel reads lists a call never wrote
+  const bool rebuild = !a->reuse_lists || bsa_q_rows(a) == 0 || bsa_kv_rows(a) == 0;
+  if (e == hipSuccess && rebuild) e = bsa_build_lists(a, w, p, st);
   if (e == hipSuccess) e = tm.mark(0, 1);
   if (e != hipSuccess) return TSA_ERR_HIP;
   p.q = a->q; p.k = a->k; p.v = a->v; p.o = a->out; p.dout = a->dout; p.lse = (float*)a->lse;
@@ -830,8 +841,8 @@ int nsa_select_fwd(const nsa_select_fwd_args* a, void* ws, size_t ws_bytes, void
   int s = nsa_select_fwd_workspace_size(a, &need);
   if (s) return s;
   if (!ws || !a16(ws) || ws_bytes < need) return TSA_ERR_WORKSPACE;
-  if (a->T == 0) return TSA_OK;
   hipStream_t st = (hipStream_t)stream;
+  if (a->T == 0) return hip_status(timer_of(a, st).skip_all(2));
   NsaWs w;
   nsa_carve(a, ws, &w, false);
   NsaParams p;
@@ -883,7 +894,9 @@ int nsa_select_bwd(const nsa_select_bwd_args* a, void* ws, size_t ws_bytes, void
   std::memset(&p, 0, sizeof(p));
   const StageTimer tm = timer_of(a, st);
   if (tm.mark(0, 0) != hipSuccess) return TSA_ERR_HIP;
-  if (a->reuse_lists == 0) {
+  // with no tokens the lists are empty: they are written here whatever
+  // reuse_lists says (a forward without tokens leaves the workspace alone)
+  if (a->reuse_lists == 0 || a->T == 0) {
     s = nsa_setup(a, w, &p.g, st);
     if (s) return s;
     if (a->T > 0) {
@@ -925,8 +938,8 @@ int sfa_paged_fwd(const sfa_paged_fwd_args* a, void* ws, size_t ws_bytes, void* 
   int s = sfa_paged_fwd_workspace_size(a, &need);
   if (s) return s;
   if (!ws || !a16(ws) || ws_bytes < need) return TSA_ERR_WORKSPACE;
-  if (sfa_tokens(a) == 0) return TSA_OK;
   hipStream_t st = (hipStream_t)stream;
+  if (sfa_tokens(a) == 0) return hip_status(timer_of(a, st).skip_all(2));
   SfaParams p;
   sfa_carve(sfa_params(a), ws, &p);
   if (a->q_layout == TSA_LAYOUT_TND) {
@@ -1001,8 +1014,8 @@ int sfa_sharedkv_fwd(const sfa_sharedkv_fwd_args* a, void* ws, size_t ws_bytes, 
   if (s) return s;
   if (!ws || !a16(ws) || ws_bytes < need) return TSA_ERR_WORKSPACE;
   if (a->tasks && (uintptr_t)a->tasks % 16) return TSA_ERR_INVALID;
-  if (skv_tokens(a) == 0) return TSA_OK;
   hipStream_t st = (hipStream_t)stream;
+  if (skv_tokens(a) == 0) return hip_status(timer_of(a, st).skip_all(3));
   SfaParams p;
   skv_carve(skv_params(a), ws, &p);
   const bool have = a->tasks != nullptr;

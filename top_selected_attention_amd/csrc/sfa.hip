@@ -175,8 +175,11 @@ __global__ __launch_bounds__(512) void sfa_split_kernel(SfaParams p, int n_items
         pg[i] = p.page;
         lp[i] = ok[i] ? min(pos[i] / p.page, p.max_pages - 1) : 0;
       } else {
-        pos[i] = id[i] * p.sbs + (gs - p.win_pad) % p.sbs;
-        ok[i] = t < seg_n && id[i] >= 0 && pos[i] < t_len && (!p.causal || pos[i] <= t_qpos);
+        // the id is range-checked before it is scaled, so a huge id cannot
+        // wrap into a small position
+        const bool idok = id[i] >= 0 && id[i] <= (t_len - 1) / p.sbs;
+        pos[i] = idok ? id[i] * p.sbs + (gs - p.win_pad) % p.sbs : 0;
+        ok[i] = t < seg_n && idok && pos[i] < t_len && (!p.causal || pos[i] <= t_qpos);
         pg[i] = t_page;
         lp[i] = ok[i] ? min(pos[i] / t_page, t_maxp - 1) : 0;
       }
@@ -531,8 +534,9 @@ __global__ __launch_bounds__(256) void sfa_task_kernel(SfaParams p) {
       for (int u = 0; u < kKeys; u++) id[u] = lo + u < hi ? topk[(lo + u - p.win_pad) / p.sbs] : -1;
 #pragma unroll
       for (int u = 0; u < kKeys; u++) {
-        const int pos = id[u] * p.sbs + (lo + u - p.win_pad) % p.sbs;
-        kept += id[u] >= 0 && pos < t_len && pos <= t_qpos;
+        const bool idok = id[u] >= 0 && id[u] <= (t_len - 1) / p.sbs;
+        const int pos = idok ? id[u] * p.sbs + (lo + u - p.win_pad) % p.sbs : 0;
+        kept += idok && pos < t_len && pos <= t_qpos;
       }
     }
     return kept + kChunkCost;
