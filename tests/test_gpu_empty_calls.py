@@ -86,7 +86,7 @@ def test_bsa_zero_query_rows_then_reusing_backward_gives_zero_dk_dv(layout):
     ws = _ws(tsa.lib, tsa.lib.bsa_bwd_workspace_size, ba)
     evs, arr = _events(2)
     fa = A.BsaFwdArgs(out=out.data_ptr(), lse=lse.data_ptr(), **common)
-    fa.n_events, fa.events = 2, ctypes.cast(arr, ctypes.c_void_p)
+    fa.n_events, fa.events = 2, ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
     A.call(tsa.lib.bsa_fwd, ctypes.byref(fa), ctypes.c_void_p(ws.data_ptr()),
            ctypes.c_size_t(ws.numel()), _stream())
     _all_recorded(evs)
@@ -115,7 +115,7 @@ def test_bsa_backward_with_zero_rows_ignores_stale_lists():
                       dk=dk.data_ptr(), dv=dv.data_ptr())
     ws = _ws(tsa.lib, tsa.lib.bsa_bwd_workspace_size, ba)
     evs, arr = _events(3)
-    ba.reuse_lists, ba.n_events, ba.events = 1, 3, ctypes.cast(arr, ctypes.c_void_p)
+    ba.reuse_lists, ba.n_events, ba.events = 1, 3, ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
     A.call(tsa.lib.bsa_bwd, ctypes.byref(ba), ctypes.c_void_p(ws.data_ptr()),
            ctypes.c_size_t(ws.numel()), _stream())
     _all_recorded(evs)
@@ -146,7 +146,7 @@ def test_nsa_zero_tokens_then_reusing_backward_gives_zero_dk_dv():
     ws = _ws(tsa.lib, tsa.lib.nsa_select_bwd_workspace_size, ba)
     evs, arr = _events(2)
     fa = A.NsaFwdArgs(out=q.data_ptr(), lse=lse.data_ptr(), **common)
-    fa.n_events, fa.events = 2, ctypes.cast(arr, ctypes.c_void_p)
+    fa.n_events, fa.events = 2, ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
     A.call(tsa.lib.nsa_select_fwd, ctypes.byref(fa), ctypes.c_void_p(ws.data_ptr()),
            ctypes.c_size_t(ws.numel()), _stream())
     _all_recorded(evs)
@@ -175,7 +175,7 @@ def test_sfa_zero_tokens_records_its_events():
                   topk_indices=bt.data_ptr(), out=z.data_ptr(), lse=0)
     ws = _ws(tsa.lib, tsa.lib.sfa_paged_fwd_workspace_size, a)
     evs, arr = _events(2)
-    a.n_events, a.events = 2, ctypes.cast(arr, ctypes.c_void_p)
+    a.n_events, a.events = 2, ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
     A.call(tsa.lib.sfa_paged_fwd, ctypes.byref(a), ctypes.c_void_p(ws.data_ptr()),
            ctypes.c_size_t(ws.numel()), _stream())
     _all_recorded(evs)
@@ -191,7 +191,7 @@ def test_sfa_sharedkv_zero_tokens_records_its_events():
                                cmp=tuple(torch.as_tensor(t).cuda() for t in cmp),
                                cu_seqlens_q=cu)
     evs, arr = _events(3)
-    plan.a.n_events, plan.a.events = 3, ctypes.cast(arr, ctypes.c_void_p)
+    plan.a.n_events, plan.a.events = 3, ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
     plan.fwd()
     _all_recorded(evs)
     assert plan.out.numel() == 0
