@@ -20,7 +20,8 @@
  *
  * Ownership: the caller owns every buffer, including the workspace.  The
  * library never allocates or frees device memory and keeps no device state
- * besides its loaded code objects; calls are reentrant.  Device pointers are
+ * besides its loaded code objects (which hold the fixed scratch array of
+ * sfa_paged_fwd_noalloc); calls other than that one are reentrant.  Device pointers are
  * borrowed until the work enqueued on `stream` completes.  Host pointers
  * (marked HOST) are read during the call only.
  *
@@ -68,7 +69,8 @@ typedef enum {
   TSA_ERR_WORKSPACE = 4,     /* workspace NULL, smaller than XXX_workspace_size or
                                 not 16-byte aligned */
   TSA_ERR_HIP = 5,           /* a HIP launch or runtime call failed */
-  TSA_ERR_DATA = 6           /* validate = 1 found bad data (ids out of range) */
+  TSA_ERR_DATA = 6,          /* validate = 1 found bad data (ids out of range) */
+  TSA_ERR_SCRATCH = 7        /* a no-allocation call needs more than its fixed scratch */
 } tsa_status;
 
 enum { TSA_BF16 = 0, TSA_FP16 = 1 };
@@ -391,6 +393,22 @@ typedef struct {
 TSA_API int sfa_paged_fwd_workspace_size(const sfa_paged_fwd_args* args, size_t* bytes);
 TSA_API int sfa_paged_fwd(const sfa_paged_fwd_args* args, void* workspace, size_t workspace_bytes,
                   void* stream);
+
+/* sfa_paged_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * it takes its workspace from a fixed array of the library's own, one per
+ * GPU, that lives until the process ends, and calls no hipMalloc, hipFree
+ * or other allocating routine.  The caller still owns q, the caches, the
+ * tables, out and lse.  Same arguments, validation and results as
+ * sfa_paged_fwd; a call whose workspace would exceed
+ * sfa_paged_fwd_noalloc_max_bytes() (64 MiB: e.g. 128 decode tokens of 64
+ * heads with 2 splits need 32 MiB) returns TSA_ERR_SCRATCH before any launch.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (other streams, other threads) race and must be serialised by the
+ * caller.  The array keeps the last call's partial results; nothing in it
+ * has to start at zero. */
+TSA_API size_t sfa_paged_fwd_noalloc_max_bytes(void);
+TSA_API int sfa_paged_fwd_noalloc(const sfa_paged_fwd_args* args, void* stream);
 
 /* ------------------------------------------------------------------------
  * Shared-KV two-branch sparse decode ("SparseAttnSharedkvMetadata",

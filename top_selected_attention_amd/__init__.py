@@ -460,6 +460,13 @@ class SfaPlan:
                   ctypes.c_size_t(self.ws.numel()), _stream())
         return self.out, self.lse
 
+    def fwd_noalloc(self):
+        """The same forward through sfa_paged_fwd_noalloc: the library's fixed
+        per-GPU scratch instead of this plan's workspace (for callers that
+        cannot allocate; overlapping calls on one GPU race)."""
+        _abi.call(lib.sfa_paged_fwd_noalloc, ctypes.byref(self.a), _stream())
+        return self.out, self.lse
+
 
 def sfa_paged_fwd(q, q_rope, key_cache, key_rope_cache, value_cache, block_table, kv_lens,
                   topk_indices, scale=None, sparse_mode=3, sparse_block_size=1, validate=False,

@@ -8,7 +8,7 @@ LAYOUT_BNSD, LAYOUT_TND, LAYOUT_BSND = 0, 1, 2
 
 STATUS = {
     0: "TSA_OK", 1: "TSA_ERR_NULL", 2: "TSA_ERR_INVALID", 3: "TSA_ERR_UNSUPPORTED",
-    4: "TSA_ERR_WORKSPACE", 5: "TSA_ERR_HIP", 6: "TSA_ERR_DATA",
+    4: "TSA_ERR_WORKSPACE", 5: "TSA_ERR_HIP", 6: "TSA_ERR_DATA", 7: "TSA_ERR_SCRATCH",
 }
 
 EXPORTS = [
@@ -18,6 +18,7 @@ EXPORTS = [
     "nsa_select_fwd_workspace_size", "nsa_select_fwd", "nsa_select_bwd_workspace_size",
     "nsa_select_bwd", "nsa_compact_blocks_total", "nsa_compact_workspace_size", "nsa_compact",
     "sfa_paged_fwd_workspace_size", "sfa_paged_fwd",
+    "sfa_paged_fwd_noalloc_max_bytes", "sfa_paged_fwd_noalloc",
     "sfa_sharedkv_fwd_workspace_size", "sfa_sharedkv_fwd",
     "sfa_sharedkv_metadata_size", "sfa_sharedkv_metadata",
 ]
@@ -138,6 +139,7 @@ def load(path):
         "nsa_compact_blocks_total": [P, P], "nsa_compact_workspace_size": [P, P],
         "nsa_compact": [P, P, P, P, P, P, c_size_t, P],
         "sfa_paged_fwd_workspace_size": [P, P], "sfa_paged_fwd": [P, P, c_size_t, P],
+        "sfa_paged_fwd_noalloc": [P, P],
         "sfa_sharedkv_fwd_workspace_size": [P, P], "sfa_sharedkv_fwd": [P, P, c_size_t, P],
         "sfa_sharedkv_metadata_size": [P, P], "sfa_sharedkv_metadata": [P, P, c_size_t, P],
     }
@@ -145,6 +147,8 @@ def load(path):
         f = getattr(lib, name)
         f.restype = c_int
         f.argtypes = args
+    lib.sfa_paged_fwd_noalloc_max_bytes.restype = c_size_t
+    lib.sfa_paged_fwd_noalloc_max_bytes.argtypes = []
     for i, s in enumerate(ARG_STRUCTS):
         n = lib.tsa_args_sizeof(i)
         if n != ctypes.sizeof(s):

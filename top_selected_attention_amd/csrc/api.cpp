@@ -9,6 +9,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/top_selected_attention.h"
 #include "tsa_internal.h"
@@ -656,6 +657,33 @@ size_t sfa_carve(const SfaParams& p, void* ws, SfaParams* out) {
   return c.off + kAlign;
 }
 
+// ----- fixed scratch for the entry point that allocates nothing -------------
+
+// Every GPU the library runs on holds its own copy of this array until the
+// process ends.  In host code its name is only a stand-in: the device address
+// comes from hipGetSymbolAddress, taken once per device.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The current device's scratch address (looked up on the first call on that
+// device, with it current).
+int scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return TSA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return TSA_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return TSA_OK;
+}
+
 }  // namespace
 
 // ===========================================================================
@@ -672,6 +700,8 @@ const char* tsa_status_string(int s) {
     case TSA_ERR_WORKSPACE: return "workspace missing, too small or not 16-byte aligned";
     case TSA_ERR_HIP: return "a HIP launch or runtime call failed";
     case TSA_ERR_DATA: return "input data out of range (validate = 1)";
+    case TSA_ERR_SCRATCH:
+      return "the call needs more scratch than the fixed no-allocation maximum (64 MiB)";
     default: return "unknown status";
   }
 }
@@ -950,7 +980,7 @@ int sfa_paged_fwd(const sfa_paged_fwd_args* a, void* ws, size_t ws_bytes, void* 
     p.cu_q = p.cu_dev;
   }
   if (a->validate) {
-    hipError_t e = hipMemsetAsync(p.bad, 0, sizeof(int), st);
+    hipError_t e = launch_fill_i32(p.bad, 1, 0, st);
     if (e == hipSuccess) e = launch_sfa_check(p, st);
     int bad = 0;
     if (e == hipSuccess) e = hipMemcpyAsync(&bad, p.bad, sizeof(int), hipMemcpyDeviceToHost, st);
@@ -960,6 +990,21 @@ int sfa_paged_fwd(const sfa_paged_fwd_args* a, void* ws, size_t ws_bytes, void* 
   }
   const StageTimer tm = timer_of(a, st);
   return hip_status(launch_sfa_fwd(p, a->dtype == TSA_FP16, st, tm.ev, tm.n));
+}
+
+size_t sfa_paged_fwd_noalloc_max_bytes(void) { return kScratchBytes; }
+
+int sfa_paged_fwd_noalloc(const sfa_paged_fwd_args* a, void* stream) {
+  size_t need;
+  int s = sfa_paged_fwd_workspace_size(a, &need);
+  if (s) return s;
+  if (need > kScratchBytes) return TSA_ERR_SCRATCH;
+  void* ptr = nullptr;
+  s = scratch_of_current_device(&ptr);
+  if (s) return s;
+  // the split partials are written in full before the combine reads them,
+  // so nothing in the scratch needs clearing between calls
+  return sfa_paged_fwd(a, ptr, kScratchBytes, stream);
 }
 
 // ----- shared-KV two-branch decode -------------------------------------------

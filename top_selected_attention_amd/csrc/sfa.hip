@@ -452,6 +452,18 @@ int sfa_splits(const SfaParams& p) {
   return (int)s;
 }
 
+// Sets n ints to v (a kernel, not a memset node, so callers may capture it).
+__global__ void fill_i32_kernel(int* p, int n, int v) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+hipError_t launch_fill_i32(int* p, int n, int v, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_i32_kernel, dim3((n + 255) / 256), dim3(256), 0, st, p, n, v);
+  return hipGetLastError();
+}
+
 hipError_t launch_sfa_check(const SfaParams& p, hipStream_t st) {
   const long n = p.ntok * p.topk_n;
   if (n == 0) return hipSuccess;

@@ -232,5 +232,6 @@ hipError_t launch_sfa_sharedkv(const SfaParams& p, int fp16, bool have_tasks, hi
 // stage 0 = split attention, stage 1 = combine
 hipError_t launch_sfa_fwd(const SfaParams& p, int fp16, hipStream_t st, void* const* ev, int n_ev);
 hipError_t launch_sfa_check(const SfaParams& p, hipStream_t st);
+hipError_t launch_fill_i32(int* p, int n, int v, hipStream_t st);
 
 }  // namespace tsa
