@@ -24,6 +24,9 @@ Sources (the pages are CANN operator documents and one news page):
   64-wide rope part.
 * "SparseAttnSharedkvMetadata" (news page), parameter list: cu_seqlens as B+1
   prefix sums, seqused_kv, rightDownCausal mask mode 3.
+* "aclnnFusedFloydAttentionGrad", formula section: scores as the sum of two
+  products batched over different sequence axes, one softmax, and its
+  backward chain (module ``floyd``).
 
 Parity status per function is stated in each module's header.
 """
@@ -44,3 +47,4 @@ from .attention import (  # noqa: F401
     sfa_sharedkv_fwd,
 )
 from .compaction import bsa_compact, nsa_compact  # noqa: F401
+from .floyd import floyd_fwd, floyd_bwd  # noqa: F401

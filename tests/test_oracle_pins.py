@@ -945,3 +945,110 @@ def test_workload_closed_form_counts():
     own = (np.arange(topk.shape[0]) - np.repeat(cu[:-1], np.diff(cu))) // 64
     assert np.all(np.sort(topk, -1)[..., 1:] != np.sort(topk, -1)[..., :-1])
     assert np.all((topk == own[:, None, None]).any(-1))
+
+
+# ----------------------------------------------------------------------------
+# FloydAttention (two batched score products, one softmax)
+# ----------------------------------------------------------------------------
+
+def _floyd_inputs(seed, B=1, H=2, N=5, M=6, K=7, D=4):
+    r = _rng(seed)
+    return (r.standard_normal((B, H, N, M, D)), r.standard_normal((B, H, N, K, D)),
+            r.standard_normal((B, H, N, K, D)), r.standard_normal((B, H, M, K, D)),
+            r.standard_normal((B, H, M, K, D)), r.standard_normal((B, H, N, M, D)))
+
+
+def _sdpa_grads(q, k, v, do, scale):
+    """Dense attention of q [R, D] over k, v [J, D] (torch float64, autograd)."""
+    qt, kt, vt = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    out = torch.nn.functional.scaled_dot_product_attention(qt[None], kt[None], vt[None],
+                                                           scale=scale)[0]
+    out.backward(torch.tensor(do))
+    lse = torch.logsumexp(scale * qt.detach() @ kt.detach().T, -1)
+    return out.detach().numpy(), lse.numpy(), qt.grad.numpy(), kt.grad.numpy(), vt.grad.numpy()
+
+
+def test_floyd_first_branch_alone_is_attention_batched_over_n():
+    """With key2 = value2 = 0 every (b, h, n) is dense attention of the M
+    query rows q[b,h,n] over key1 / value1 [b,h,n] (torch, autograd)."""
+    q, k1, v1, k2, v2, dy = _floyd_inputs(60)
+    k2[:] = 0.0
+    v2[:] = 0.0
+    scale = 0.37
+    y, lse = oracle.floyd_fwd(q, k1, v1, k2, v2, scale)
+    dq, dk1, dv1, _, _ = oracle.floyd_bwd(q, k1, v1, k2, v2, y, dy, scale)
+    for b in range(q.shape[0]):
+        for h in range(q.shape[1]):
+            for n in range(q.shape[2]):
+                o, l_, gq, gk, gv = _sdpa_grads(q[b, h, n], k1[b, h, n], v1[b, h, n],
+                                                dy[b, h, n], scale)
+                for mine, ref in ((y, o), (lse, l_), (dq, gq), (dk1, gk), (dv1, gv)):
+                    np.testing.assert_allclose(mine[b, h, n], ref, rtol=0, atol=1e-12)
+
+
+def test_floyd_second_branch_alone_is_attention_batched_over_m():
+    """With key1 = value1 = 0 every (b, h, m) is dense attention of the N
+    query rows q[b,h,:,m] over key2 / value2 [b,h,m] (the second sequence
+    axis as the batch axis)."""
+    q, k1, v1, k2, v2, dy = _floyd_inputs(61)
+    k1[:] = 0.0
+    v1[:] = 0.0
+    scale = 0.41
+    y, lse = oracle.floyd_fwd(q, k1, v1, k2, v2, scale)
+    dq, _, _, dk2, dv2 = oracle.floyd_bwd(q, k1, v1, k2, v2, y, dy, scale)
+    for b in range(q.shape[0]):
+        for h in range(q.shape[1]):
+            for m in range(q.shape[3]):
+                o, l_, gq, gk, gv = _sdpa_grads(q[b, h, :, m], k2[b, h, m], v2[b, h, m],
+                                                dy[b, h, :, m], scale)
+                np.testing.assert_allclose(y[b, h, :, m], o, rtol=0, atol=1e-12)
+                np.testing.assert_allclose(lse[b, h, :, m], l_, rtol=0, atol=1e-12)
+                np.testing.assert_allclose(dq[b, h, :, m], gq, rtol=0, atol=1e-12)
+                np.testing.assert_allclose(dk2[b, h, m], gk, rtol=0, atol=1e-12)
+                np.testing.assert_allclose(dv2[b, h, m], gv, rtol=0, atol=1e-12)
+
+
+def test_floyd_finite_differences():
+    """Central differences of L = sum(dY * Y) for all five inputs, both
+    branches live, N != M != K."""
+    q, k1, v1, k2, v2, dy = _floyd_inputs(62, B=1, H=2, N=3, M=4, K=5, D=3)
+    scale = 0.5
+    args = dict(q=q, k1=k1, v1=v1, k2=k2, v2=v2)
+    y, _ = oracle.floyd_fwd(q, k1, v1, k2, v2, scale)
+    grads = oracle.floyd_bwd(q, k1, v1, k2, v2, y, dy, scale)
+    f = lambda: float((oracle.floyd_fwd(**args, scale=scale)[0] * dy).sum())  # noqa: E731
+    _fd_check(f, args, ["q", "k1", "v1", "k2", "v2"], grads, n_probe=10)
+
+
+def test_floyd_transpose_symmetry():
+    """Swapping the two sequence axes of the query together with the two
+    key/value pairs transposes every result (an axis mix-up fails this)."""
+    q, k1, v1, k2, v2, dy = _floyd_inputs(63, N=4, M=6, K=5)
+    scale = 0.3
+    y, lse = oracle.floyd_fwd(q, k1, v1, k2, v2, scale)
+    g = oracle.floyd_bwd(q, k1, v1, k2, v2, y, dy, scale)
+    qt, dyt = np.swapaxes(q, 2, 3).copy(), np.swapaxes(dy, 2, 3).copy()
+    yt, lset = oracle.floyd_fwd(qt, k2, v2, k1, v1, scale)
+    gt = oracle.floyd_bwd(qt, k2, v2, k1, v1, yt, dyt, scale)
+    np.testing.assert_allclose(yt, np.swapaxes(y, 2, 3), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lset, np.swapaxes(lse, 2, 3), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(gt[0], np.swapaxes(g[0], 2, 3), rtol=0, atol=1e-12)
+    for a, b_ in ((gt[1], g[3]), (gt[2], g[4]), (gt[3], g[1]), (gt[4], g[2])):
+        np.testing.assert_allclose(a, b_, rtol=0, atol=1e-12)
+
+
+def test_floyd_constant_values_and_probability_rows():
+    """value1 rows all a and value2 rows all c give Y = a + c and zero dQ,
+    dK1, dK2 (dP - softmax_grad vanishes); the recomputed P has unit rows
+    (exp(S - LSE) summed over k)."""
+    q, k1, v1, k2, v2, dy = _floyd_inputs(64)
+    a, c = _rng(65).standard_normal(4), _rng(66).standard_normal(4)
+    v1[:] = a
+    v2[:] = c
+    y, lse = oracle.floyd_fwd(q, k1, v1, k2, v2, 0.6)
+    np.testing.assert_allclose(y, np.broadcast_to(a + c, y.shape), rtol=0, atol=1e-12)
+    dq, dk1, _, dk2, _ = oracle.floyd_bwd(q, k1, v1, k2, v2, y, dy, 0.6)
+    for gr in (dq, dk1, dk2):
+        assert np.abs(gr).max() < 1e-12
+    s = 0.6 * (np.einsum("bhnmd,bhnkd->bhnmk", q, k1) + np.einsum("bhnmd,bhmkd->bhnmk", q, k2))
+    np.testing.assert_allclose(np.exp(s - lse[..., None]).sum(-1), 1.0, rtol=0, atol=1e-12)
