@@ -68,13 +68,16 @@ def test_bsa_all_blocks_equals_dense_attention(causal, N1, N2):
         assert np.abs(mine - t).max() <= 1e-10 * np.abs(t).max()
 
 
-def test_nsa_all_blocks_equals_dense_attention():
+@pytest.mark.parametrize("D,Dv", [(8, 8), (12, 8)])
+def test_nsa_all_blocks_equals_dense_attention(D, Dv):
+    """Every block selected is dense causal attention (torch, autograd),
+    with value heads as wide as or narrower than the query/key heads."""
     r = _rng(2)
-    seqlens, N1, N2, D, sbs = [16, 24], 4, 2, 8, 4
+    seqlens, N1, N2, sbs = [16, 24], 4, 2, 4
     cu = np.array([0, 16, 40])
     T = 40
-    q, k, v = r.standard_normal((T, N1, D)), r.standard_normal((T, N2, D)), r.standard_normal((T, N2, D))
-    do = r.standard_normal((T, N1, D))
+    q, k, v = r.standard_normal((T, N1, D)), r.standard_normal((T, N2, D)), r.standard_normal((T, N2, Dv))
+    do = r.standard_normal((T, N1, Dv))
     scale = 0.3
     # every token selects every block of its sequence (sbc = blocks of the longest; the
     # shorter sequence lists its 4 blocks; use one topk width per call -> two calls)
@@ -689,14 +692,15 @@ def test_bsa_finite_differences_gqa(mode):
 
 
 @pytest.mark.parametrize("mode", [0, 2])
-def test_nsa_finite_differences(mode):
+@pytest.mark.parametrize("Dv", [8, 5])
+def test_nsa_finite_differences(mode, Dv):
     r = _rng(6)
     seqlens, N1, N2, D, sbs, sbc = [12, 8], 4, 2, 8, 4, 2
     cu = np.array([0, 12, 20])
     T = 20
     a = dict(q=r.standard_normal((T, N1, D)), k=r.standard_normal((T, N2, D)),
-             v=r.standard_normal((T, N2, D)))
-    do = r.standard_normal((T, N1, D))
+             v=r.standard_normal((T, N2, Dv)))
+    do = r.standard_normal((T, N1, Dv))
     topk = W.nsa_topk_causal(r, seqlens, N2, sbs, sbc)
 
     def loss():

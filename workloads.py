@@ -204,16 +204,19 @@ def nsa_workload():
                 dtype="bf16", sbs=64, sbc=16, sparse_mode=2)
 
 
-def nsa_inputs(seqlens=None, N1=32, N2=2, D=128, sbs=64, sbc=16, seed_base=30, dtype="bf16"):
-    """(cu_seqlens int32 [B+1], q [T,N1,D], k [T,N2,D], v [T,N2,D], dout, topk)."""
+def nsa_inputs(seqlens=None, N1=32, N2=2, D=128, sbs=64, sbc=16, seed_base=30, dtype="bf16",
+               Dv=None):
+    """(cu_seqlens int32 [B+1], q [T,N1,D], k [T,N2,D], v [T,N2,Dv], dout [T,N1,Dv], topk);
+    Dv defaults to D."""
     w = nsa_workload()
     seqlens = w["seqlens"] if seqlens is None else seqlens
+    Dv = D if Dv is None else Dv
     T = int(sum(seqlens))
     cu = np.concatenate([[0], np.cumsum(seqlens)]).astype(np.int32)
     q = normal((T, N1, D), seed_base + 1, dtype)
     k = normal((T, N2, D), seed_base + 2, dtype)
-    v = normal((T, N2, D), seed_base + 3, dtype)
-    do = normal((T, N1, D), seed_base + 4, dtype)
+    v = normal((T, N2, Dv), seed_base + 3, dtype)
+    do = normal((T, N1, Dv), seed_base + 4, dtype)
     topk = nsa_topk_causal(np.random.default_rng(1000 + seed_base // 10), seqlens, N2, sbs, sbc)
     return cu, q, k, v, do, topk
 
