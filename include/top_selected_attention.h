@@ -229,7 +229,10 @@ TSA_API int bsa_compact(const bsa_fwd_args* args, int32_t* row_ptr, int32_t* col
  * its source row (deterministic, no atomics).
  *
  * Layout TND only (constraints section): q [T, N1, D], k [Tk, N2, D],
- * v [Tk, N2, Dv], out [T, N1, Dv], lse fp32 [T, N1].  D = Dv = 128.
+ * v [Tk, N2, Dv], out [T, N1, Dv], lse fp32 [T, N1].  Dv = 128 and D = 128
+ *   or 192 (the constraints section fixes the query/key and the value head
+ *   dims to two values its extraction lost; read as 192 and 128, and the
+ *   equal pair 128 / 128 is built too); other values: TSA_ERR_UNSUPPORTED.
  * cu_seqlens_q / cu_seqlens_kv: HOST int32 [B+1] prefix sums starting at 0
  *   ("SparseAttnSharedkvMetadata", parameter list: cu_seqlens are B+1 prefix
  *   sums); cu_seqlens_q[B] == T, cu_seqlens_kv[B] == Tk.

@@ -165,7 +165,9 @@ def _nsa(tsa, seqlens=(256, 512), **kw):
     (dict(sparse_mode=1), 2),
     (dict(N1=31), 2),                      # N1 % N2
     (dict(N1=128, N2=2), 2),               # G = 64 > 32
-    (dict(Dv=64), 3),                      # Dv != D not built
+    (dict(Dv=64), 3),                      # value heads other than 128 not built
+    (dict(D=192), 0),                      # 192-dim query/key over 128-dim values
+    (dict(D=64), 3),                       # other query/key dims not built
     (dict(T=100), 2),                      # cu_seqlens_q[B] != T
     (dict(topk=0), 1),
     (dict(v=40), 2),                       # device tensors 16-byte aligned

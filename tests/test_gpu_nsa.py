@@ -122,6 +122,62 @@ def test_fwd_bwd_small(seqlens, N1, N2, sbs, sbc, mode):
     _close(dv, rdv, GRAD_TOL, "dv")
 
 
+@pytest.mark.parametrize("seqlens,N1,N2,sbs,sbc,dtype", [
+    ([256, 512, 320], 32, 2, 64, 4, "bf16"),   # G = 16
+    ([128, 96], 4, 4, 16, 6, "bf16"),          # G = 1, smallest block size
+    ([256, 384], 32, 1, 128, 2, "fp16"),       # G = 32, largest block size
+    ([192, 240], 12, 2, 48, 4, "bf16"),        # G = 6, block size not a multiple of 32
+])
+@pytest.mark.parametrize("mode", [0, 2])
+def test_fwd_bwd_qk192_v128(seqlens, N1, N2, sbs, sbc, dtype, mode):
+    """Query/key heads of 192 dims over value heads of 128 (the reading of
+    the two distinct head-dim values the constraints section fixes)."""
+    cu, q, k, v, do, topk = W.nsa_inputs(seqlens, N1=N1, N2=N2, D=192, Dv=128, sbs=sbs, sbc=sbc,
+                                          seed_base=110, dtype=dtype)
+    scale = 1 / math.sqrt(192)
+    out, lse, dq, dk, dv = _run(cu, q, k, v, do, topk, sbs, scale, mode)
+    assert out.shape[-1] == 128 and dq.shape[-1] == 192 and dk.shape[-1] == 192
+    ro, rl = oracle.nsa_fwd(_np(q), _np(k), _np(v), topk, cu, cu, sbs, scale, mode)
+    _close(out, ro, OUT_TOL, "out")
+    _lse_close(lse, rl)
+    rdq, rdk, rdv = oracle.nsa_bwd(_np(q), _np(k), _np(v), _np(out), _np(do), topk, cu, cu, sbs,
+                                   scale, mode)
+    _close(dq, rdq, GRAD_TOL, "dq")
+    _close(dk, rdk, GRAD_TOL, "dk")
+    _close(dv, rdv, GRAD_TOL, "dv")
+
+
+def test_qk192_full_size_sampled_and_deterministic():
+    """The nsa_varlen workload (4 sequences, 32/2 heads, 64 x 16 selected)
+    with 192-dim query/key heads: sampled tokens against the oracle, whole KV
+    blocks with every token that selected them, and bit-identical reruns."""
+    cu, q, k, v, do, topk = W.nsa_inputs(D=192, Dv=128, seed_base=120)
+    sbs, scale = 64, 1 / math.sqrt(192)
+    a = _run(cu, q, k, v, do, topk, sbs, scale, 2)
+    b = _run(cu, q, k, v, do, topk, sbs, scale, 2)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    out, lse, dq, dk, dv = a
+    T = int(cu[-1])
+    toks = sorted(set([0, 63, 64, 2047, 2048, 6143, 6144, 14335, 14336, T - 1] +
+                      list(range(100, T, 1499))))
+    qn, kn, vn, don, on = _np(q), _np(k), _np(v), _np(do), _np(out)
+    ro, rl = oracle.nsa_fwd(qn, kn, vn, topk, cu, cu, sbs, scale, 2, tokens=toks)
+    _close(out, ro, OUT_TOL, "out", rows=toks)
+    _lse_close(lse, rl, rows=toks)
+    _, _, rvp, rv, nb = oracle.nsa_compact(topk, cu, cu, sbs, 2)
+    gb = 32 + 64 + 5                       # block 5 of the 8192-token sequence, KV head 0
+    sel = set(toks) | set(rv[rvp[gb]:rvp[gb + 1]].tolist())
+    rows = np.zeros(T, bool)
+    start = int(cu[2]) + 5 * sbs
+    rows[start:start + sbs] = True
+    rdq, rdk, rdv = oracle.nsa_bwd(qn, kn, vn, on, don, topk, cu, cu, sbs, scale, 2,
+                                   tokens=sorted(sel))
+    _close(dq, rdq, GRAD_TOL, "dq", rows=toks)
+    _close(dk[:, 0], rdk[:, 0], GRAD_TOL, "dk", rows=rows)
+    _close(dv[:, 0], rdv[:, 0], GRAD_TOL, "dv", rows=rows)
+
+
 def test_fwd_bwd_fp16_duplicates():
     cu, q, k, v, do, topk = _case([256, 128], 16, 2, 32, 4, 80, dtype="fp16")
     topk[10, 0, 1] = topk[10, 0, 0]                # a block listed twice counts twice

@@ -274,7 +274,8 @@ def _host_i32(x):
 class NsaPlan:
     """Forward and backward of NSA selected attention for fixed tensors.
 
-    q [T, N1, 128], k/v [Tk, N2, 128] (TND), topk int32 [T, N2, sbc] device,
+    q [T, N1, D], k [Tk, N2, D], v [Tk, N2, 128] (TND) with D = 128 or 192,
+    topk int32 [T, N2, sbc] device,
     cu_seqlens_q / cu_seqlens_kv: B+1 prefix sums (host sequences or tensors).
     """
 

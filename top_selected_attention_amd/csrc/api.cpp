@@ -302,8 +302,10 @@ int check_nsa(const A* a, bool tensors = true) {
   if (a->B < 1 || a->B > 1024) return TSA_ERR_INVALID;
   if (a->N1 < 1 || a->N1 > 128 || a->N2 < 1 || a->N1 % a->N2 != 0) return TSA_ERR_INVALID;
   if (a->N1 / a->N2 > 32) return TSA_ERR_INVALID;
-  if (a->D != 128) return TSA_ERR_INVALID;
-  if (a->Dv != a->D) return TSA_ERR_UNSUPPORTED;
+  // constraints (TND shape ranges): the query/key and the value head dims are
+  // each fixed to a value the page's extraction lost; read here as
+  // D = 192 with Dv = 128 (two distinct values), and D = Dv = 128 is built too.
+  if (a->Dv != 128 || (a->D != 128 && a->D != 192)) return TSA_ERR_UNSUPPORTED;
   // constraints: selected_block_size <= 128 and a multiple of 16;
   // selected_block_count in [1, 128]; their product at most 8K.
   if (a->sbs < 16 || a->sbs > 128 || a->sbs % 16 != 0) return TSA_ERR_INVALID;
@@ -386,7 +388,7 @@ size_t nsa_carve(const A* a, void* ws, NsaWs* out, bool with_delta) {
   w.max_segments = with_delta ? nsa_max_segments(R * a->sbc, RR) : 0;
   w.seg_off = with_delta ? c.take<int>(RR + 1) : nullptr;
   w.seg_sums = with_delta ? c.take<int>(scan_sums_len(RR)) : nullptr;
-  w.part = with_delta ? c.take<float>((long)w.max_segments * 2 * a->sbs * a->D) : nullptr;
+  w.part = with_delta ? c.take<float>((long)w.max_segments * a->sbs * (a->D + a->Dv)) : nullptr;
   if (out) *out = w;
   return c.off + kAlign;
 }

@@ -13,7 +13,8 @@
 // of it served by L2), not by MFMA.  Head groups of up to 16 query heads use
 // 16x16x32 MFMA with the group's heads as the 16 columns, and stage the next
 // chunk in registers while the current one computes; larger groups (up to
-// 32) use a 32-wide tile staged by direct global -> LDS loads.
+// 32), and query/key heads of 192 dims (values of 128), use a 32-wide tile
+// staged by direct global -> LDS loads.
 #include <algorithm>
 
 #include "tsa_device.h"
@@ -22,7 +23,8 @@
 namespace tsa {
 
 namespace {
-constexpr int kD = 128;
+constexpr int kD = 128;                    // head dim of the 16-head kernels (query/key = value)
+constexpr int kDv = 128;                   // value head dim
 constexpr int kChunk = 32;                 // keys per chunk (forward / dQ)
 constexpr int kWaveTile = kChunk * kD * 2;  // bytes of one 32-row tile
 
@@ -66,11 +68,17 @@ __device__ __forceinline__ constexpr int key_row4(int u) {
 // ---------------------------------------------------------------------------
 // Forward
 // ---------------------------------------------------------------------------
-template <class E>
+// DQK: query/key head dim, 128 or 192 (values are kDv = 128 wide).  A
+// 192-dim key row is staged as two 256-byte tiles, its bytes 0..255 and
+// 128..383 (dims 0..127 and 64..191): the second tile's pieces 8..15 hold
+// dims 128..191, so both tiles keep the one swizzled 256-byte layout.
+template <class E, int DQK>
 __global__ __launch_bounds__(256) void nsa_fwd_kernel(NsaParams p, int n_items) {
   typedef typename E::T T;
   typedef typename E::V8 V8;
-  __shared__ __attribute__((aligned(1024))) char lds[4][2][kWaveTile];  // per wave: K, V
+  constexpr int NKT = DQK == 128 ? 1 : 2;  // K tiles per chunk
+  static_assert(DQK == 128 || DQK == 192, "query/key head dim 128 or 192");
+  __shared__ __attribute__((aligned(1024))) char lds[4][NKT + 1][kWaveTile];  // per wave: K.., V
 
   const int item = blockIdx.x;
   if (item >= n_items) return;
@@ -89,13 +97,14 @@ __global__ __launch_bounds__(256) void nsa_fwd_kernel(NsaParams p, int n_items) 
   const int kv0 = g.cu_kv[b];
   const int G = p.G;
   char* Kt = lds[wid][0];
-  char* Vt = lds[wid][1];
+  char* Kt2 = lds[wid][NKT - 1];  // dims 64..191 (DQK = 192)
+  char* Vt = lds[wid][NKT];
 
-  const T* qrow = (const T*)p.q + ((long)t * p.N1 + n2 * G + l32) * kD;
+  const T* qrow = (const T*)p.q + ((long)t * p.N1 + n2 * G + l32) * DQK;
   const bool col_ok = l32 < G;
-  V8 qreg[8];
+  V8 qreg[DQK / 16];
 #pragma unroll
-  for (int ds = 0; ds < 8; ds++)
+  for (int ds = 0; ds < DQK / 16; ds++)
     qreg[ds] = col_ok ? as_v8<V8>(ld16(qrow + ds * 16 + 8 * h)) : zero_v8<V8>();
 
   const long row = (long)t * p.N2 + n2;
@@ -105,9 +114,10 @@ __global__ __launch_bounds__(256) void nsa_fwd_kernel(NsaParams p, int n_items) 
   const int cpb = (sbs + kChunk - 1) / kChunk;
   const int nchunks = (e1 - e0) * cpb;
   const float sl2 = p.scale * kLog2e;
-  const long kstride = (long)p.N2 * kD * 2;  // bytes between consecutive tokens of one KV head
-  const char* kbase = (const char*)p.k + ((long)kv0 * p.N2 + n2) * kD * 2;
-  const char* vbase = (const char*)p.v + ((long)kv0 * p.N2 + n2) * kD * 2;
+  // bytes between consecutive tokens of one KV head
+  const long kstride = (long)p.N2 * DQK * 2, vstride = (long)p.N2 * kDv * 2;
+  const char* kbase = (const char*)p.k + ((long)kv0 * p.N2 + n2) * DQK * 2;
+  const char* vbase = (const char*)p.v + ((long)kv0 * p.N2 + n2) * kDv * 2;
 
   float m = -INFINITY, lsum = 0.f;
   f32x16 o[4];
@@ -122,8 +132,10 @@ __global__ __launch_bounds__(256) void nsa_fwd_kernel(NsaParams p, int n_items) 
     const int ke = min(ks + kChunk, (blk + 1) * sbs);
     if (g.causal && ks > pos) continue;                // wholly after the token
     auto rp_k = [&](int r) { return kbase + (long)min(ks + r, ke - 1) * kstride; };
-    auto rp_v = [&](int r) { return vbase + (long)min(ks + r, ke - 1) * kstride; };
+    auto rp_k2 = [&](int r) { return kbase + (long)min(ks + r, ke - 1) * kstride + 128; };
+    auto rp_v = [&](int r) { return vbase + (long)min(ks + r, ke - 1) * vstride; };
     stage32_wave(Kt, rp_k);
+    if constexpr (NKT == 2) stage32_wave(Kt2, rp_k2);
     stage32_wave(Vt, rp_v);
     wait_vm();
 
@@ -131,8 +143,10 @@ __global__ __launch_bounds__(256) void nsa_fwd_kernel(NsaParams p, int n_items) 
 #pragma unroll
     for (int j = 0; j < 16; j++) st[j] = 0.f;
 #pragma unroll
-    for (int ds = 0; ds < 8; ds++)
-      st = E::mfma32(tile_read16<V8>(Kt, l32, 2 * ds + h), qreg[ds], st);
+    for (int ds = 0; ds < DQK / 16; ds++)
+      st = E::mfma32(ds < 8 ? tile_read16<V8>(Kt, l32, 2 * ds + h)
+                            : tile_read16<V8>(Kt2, l32, 2 * (ds - 4) + h),
+                     qreg[ds], st);
 
     float mx = -INFINITY;
 #pragma unroll
@@ -173,7 +187,7 @@ __global__ __launch_bounds__(256) void nsa_fwd_kernel(NsaParams p, int n_items) 
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   if (col_ok) {
     const long orow = (long)t * p.N1 + n2 * G + l32;
-    T* op = (T*)p.out + orow * kD;
+    T* op = (T*)p.out + orow * kDv;
 #pragma unroll
     for (int dt = 0; dt < 4; dt++)
 #pragma unroll
@@ -370,11 +384,13 @@ void nsa_fwd16_kernel(NsaParams p, int n_items) {
 // ---------------------------------------------------------------------------
 // dQ (+ softmax_grad): one wave per (token, KV head)
 // ---------------------------------------------------------------------------
-template <class E>
+// DQK as in the forward: 192-dim key rows staged as two overlapping tiles.
+template <class E, int DQK>
 __global__ __launch_bounds__(256) void nsa_dq_kernel(NsaParams p, int n_items) {
   typedef typename E::T T;
   typedef typename E::V8 V8;
-  __shared__ __attribute__((aligned(1024))) char lds[4][2][kWaveTile];
+  constexpr int NKT = DQK == 128 ? 1 : 2;
+  __shared__ __attribute__((aligned(1024))) char lds[4][NKT + 1][kWaveTile];
 
   const int item = blockIdx.x;
   if (item >= n_items) return;
@@ -389,16 +405,20 @@ __global__ __launch_bounds__(256) void nsa_dq_kernel(NsaParams p, int n_items) {
   const int kv0 = g.cu_kv[b];
   const int G = p.G;
   char* Kt = lds[wid][0];
-  char* Vt = lds[wid][1];
+  char* Kt2 = lds[wid][NKT - 1];  // dims 64..191 (DQK = 192)
+  char* Vt = lds[wid][NKT];
 
   const bool col_ok = l32 < G;
   const long qr = (long)t * p.N1 + n2 * G + l32;
-  V8 qreg[8], doreg[8];
+  V8 qreg[DQK / 16], doreg[kDv / 16];
+#pragma unroll
+  for (int ds = 0; ds < DQK / 16; ds++)
+    qreg[ds] = col_ok ? as_v8<V8>(ld16((const T*)p.q + qr * DQK + ds * 16 + 8 * h))
+                      : zero_v8<V8>();
   float acc = 0.f;
 #pragma unroll
-  for (int ds = 0; ds < 8; ds++) {
-    const long off = qr * kD + ds * 16 + 8 * h;
-    qreg[ds] = col_ok ? as_v8<V8>(ld16((const T*)p.q + off)) : zero_v8<V8>();
+  for (int ds = 0; ds < kDv / 16; ds++) {
+    const long off = qr * kDv + ds * 16 + 8 * h;
     doreg[ds] = col_ok ? as_v8<V8>(ld16((const T*)p.dout + off)) : zero_v8<V8>();
     const V8 ov = col_ok ? as_v8<V8>(ld16((const T*)p.o + off)) : zero_v8<V8>();
 #pragma unroll
@@ -416,13 +436,13 @@ __global__ __launch_bounds__(256) void nsa_dq_kernel(NsaParams p, int n_items) {
   const int cpb = (sbs + kChunk - 1) / kChunk;
   const int nchunks = (e1 - e0) * cpb;
   const float sl2 = p.scale * kLog2e;
-  const long kstride = (long)p.N2 * kD * 2;
-  const char* kbase = (const char*)p.k + ((long)kv0 * p.N2 + n2) * kD * 2;
-  const char* vbase = (const char*)p.v + ((long)kv0 * p.N2 + n2) * kD * 2;
+  const long kstride = (long)p.N2 * DQK * 2, vstride = (long)p.N2 * kDv * 2;
+  const char* kbase = (const char*)p.k + ((long)kv0 * p.N2 + n2) * DQK * 2;
+  const char* vbase = (const char*)p.v + ((long)kv0 * p.N2 + n2) * kDv * 2;
 
-  f32x16 dq[4];
+  f32x16 dq[DQK / 32];
 #pragma unroll
-  for (int dt = 0; dt < 4; dt++)
+  for (int dt = 0; dt < DQK / 32; dt++)
 #pragma unroll
     for (int j = 0; j < 16; j++) dq[dt][j] = 0.f;
 
@@ -432,8 +452,10 @@ __global__ __launch_bounds__(256) void nsa_dq_kernel(NsaParams p, int n_items) {
     const int ke = min(ks + kChunk, (blk + 1) * sbs);
     if (g.causal && ks > pos) continue;
     auto rp_k = [&](int r) { return kbase + (long)min(ks + r, ke - 1) * kstride; };
-    auto rp_v = [&](int r) { return vbase + (long)min(ks + r, ke - 1) * kstride; };
+    auto rp_k2 = [&](int r) { return kbase + (long)min(ks + r, ke - 1) * kstride + 128; };
+    auto rp_v = [&](int r) { return vbase + (long)min(ks + r, ke - 1) * vstride; };
     stage32_wave(Kt, rp_k);
+    if constexpr (NKT == 2) stage32_wave(Kt2, rp_k2);
     stage32_wave(Vt, rp_v);
     wait_vm();
 
@@ -441,10 +463,13 @@ __global__ __launch_bounds__(256) void nsa_dq_kernel(NsaParams p, int n_items) {
 #pragma unroll
     for (int j = 0; j < 16; j++) st[j] = dpt[j] = 0.f;
 #pragma unroll
-    for (int ds = 0; ds < 8; ds++) {
-      st = E::mfma32(tile_read16<V8>(Kt, l32, 2 * ds + h), qreg[ds], st);
+    for (int ds = 0; ds < DQK / 16; ds++)
+      st = E::mfma32(ds < 8 ? tile_read16<V8>(Kt, l32, 2 * ds + h)
+                            : tile_read16<V8>(Kt2, l32, 2 * (ds - 4) + h),
+                     qreg[ds], st);
+#pragma unroll
+    for (int ds = 0; ds < kDv / 16; ds++)
       dpt = E::mfma32(tile_read16<V8>(Vt, l32, 2 * ds + h), doreg[ds], dpt);
-    }
 #pragma unroll
     for (int j = 0; j < 16; j++) {
       const int key = ks + 8 * (j >> 2) + 4 * h + (j & 3);
@@ -458,14 +483,16 @@ __global__ __launch_bounds__(256) void nsa_dq_kernel(NsaParams p, int n_items) {
 #pragma unroll
       for (int e = 0; e < 8; e++) bs[e] = E::from_f32(st[8 * k2 + e]);
 #pragma unroll
-      for (int dt = 0; dt < 4; dt++) dq[dt] = E::mfma32(tile_read_tr<V8>(Kt, k2, dt), bs, dq[dt]);
+      for (int dt = 0; dt < DQK / 32; dt++)
+        dq[dt] = E::mfma32(dt < 4 ? tile_read_tr<V8>(Kt, k2, dt) : tile_read_tr<V8>(Kt2, k2, dt - 2),
+                           bs, dq[dt]);
     }
   }
 
   if (col_ok) {
-    T* dp = (T*)p.out + qr * kD;
+    T* dp = (T*)p.out + qr * DQK;
 #pragma unroll
-    for (int dt = 0; dt < 4; dt++)
+    for (int dt = 0; dt < DQK / 32; dt++)
 #pragma unroll
       for (int jj = 0; jj < 4; jj++) {
         const int d0 = dt * 32 + 8 * jj + 4 * h;
@@ -669,15 +696,20 @@ __global__ void nsa_seg_count(const int* rev_ptr, int nblocks, int* seg_cnt) {
   seg_cnt[r] = max(1, (len + kSegEntries - 1) / kSegEntries);
 }
 
-template <class E, int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+// DQK: query/key head dim (128 or 192); 192-dim K and Q rows are staged as
+// two overlapping 256-byte tiles (bytes 0..255 and 128..383), as in the
+// forward.  The 192 variant runs one wave per SIMD (its dK accumulators take
+// 32 more registers).
+template <class E, int NW, int DQK>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DQK == 128 ? 2 : 1)))
 void nsa_dkdv_seg_kernel(NsaParams p, int nblocks, float* part) {
   typedef typename E::T T;
   typedef typename E::V8 V8;
   constexpr int kQC = 32;                  // query rows per chunk
   constexpr int kQTile = kQC * kD * 2;
-  __shared__ __attribute__((aligned(1024))) char lds_k[NW * 32 * kD * 2];
-  __shared__ __attribute__((aligned(1024))) char lds_q[2][kQTile];
+  constexpr int NKT = DQK == 128 ? 1 : 2;  // 256-byte tiles per K / Q row
+  __shared__ __attribute__((aligned(1024))) char lds_k[NKT][NW * 32 * kD * 2];
+  __shared__ __attribute__((aligned(1024))) char lds_q[2][NKT][kQTile];
   __shared__ __attribute__((aligned(1024))) char lds_do[2][kQTile];
   // a direct LDS load writes all 64 lanes' dwords: rows 32..63 are never read
   __shared__ float lds_lse[2][64];
@@ -742,16 +774,18 @@ void nsa_dkdv_seg_kernel(NsaParams p, int nblocks, float* part) {
         const int inst = wid * 8 + u;
         const int rr = inst * 4 + sub;
         const long key = kv0 + min(key_lo + rr, key_hi - 1);
-        g2lds16((const char*)((const T*)p.k + (key * p.N2 + n2) * kD) + ((pc ^ swz(rr)) << 4),
-                lds_k + inst * 1024);
+        const char* krow = (const char*)((const T*)p.k + (key * p.N2 + n2) * DQK);
+#pragma unroll
+        for (int kt = 0; kt < NKT; kt++)
+          g2lds16(krow + 128 * kt + ((pc ^ swz(rr)) << 4), lds_k[kt] + inst * 1024);
       }
     }
-    V8 vreg[8];
+    V8 vreg[kDv / 16];
     {
       const int mykey = wkey0 + l32;
-      const long vrow = ((long)(kv0 + min(mykey, key_hi - 1)) * p.N2 + n2) * kD;
+      const long vrow = ((long)(kv0 + min(mykey, key_hi - 1)) * p.N2 + n2) * kDv;
 #pragma unroll
-      for (int ds = 0; ds < 8; ds++)
+      for (int ds = 0; ds < kDv / 16; ds++)
         vreg[ds] = mykey < key_hi ? as_v8<V8>(ld16((const T*)p.v + vrow + ds * 16 + 8 * h))
                                   : zero_v8<V8>();
     }
@@ -785,9 +819,11 @@ void nsa_dkdv_seg_kernel(NsaParams p, int nblocks, float* part) {
         const int inst = wid * U + u;
         const int rr = inst * 4 + sub;
         const long qrw = (long)tok[u] * p.N1 + n2 * G + gh[u];
-        g2lds16((const char*)((const T*)p.q + qrw * kD) + ((pc ^ swz(rr)) << 4),
-                lds_q[buf] + inst * 1024);
-        g2lds16((const char*)((const T*)p.dout + qrw * kD) + ((pc ^ swz(rr)) << 4),
+        const char* qrow = (const char*)((const T*)p.q + qrw * DQK);
+#pragma unroll
+        for (int kt = 0; kt < NKT; kt++)
+          g2lds16(qrow + 128 * kt + ((pc ^ swz(rr)) << 4), lds_q[buf][kt] + inst * 1024);
+        g2lds16((const char*)((const T*)p.dout + qrw * kDv) + ((pc ^ swz(rr)) << 4),
                 lds_do[buf] + inst * 1024);
       }
       if (wid == 0) {
@@ -803,11 +839,15 @@ void nsa_dkdv_seg_kernel(NsaParams p, int nblocks, float* part) {
       }
     };
 
-    f32x16 dvt[4], dkt[4];
+    f32x16 dvt[kDv / 32], dkt[DQK / 32];
 #pragma unroll
-    for (int dt = 0; dt < 4; dt++)
+    for (int dt = 0; dt < kDv / 32; dt++)
 #pragma unroll
-      for (int j = 0; j < 16; j++) dvt[dt][j] = dkt[dt][j] = 0.f;
+      for (int j = 0; j < 16; j++) dvt[dt][j] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DQK / 32; dt++)
+#pragma unroll
+      for (int j = 0; j < 16; j++) dkt[dt][j] = 0.f;
 
     if (nchunks > 0) load_chunk(0, 0);
     wait_vm();
@@ -820,7 +860,8 @@ void nsa_dkdv_seg_kernel(NsaParams p, int nblocks, float* part) {
       int ln = lane;
       asm volatile("" : "+v"(ln));
       const int l32i = ln & 31, hi2 = ln >> 5;
-      const char* Qb = lds_q[buf];
+      const char* Qb = lds_q[buf][0];
+      const char* Qb2 = lds_q[buf][NKT - 1];  // dims 64..191 (DQK = 192)
       const char* Db = lds_do[buf];
       // S = Q K^T and dP = dO V^T: 32 rows x this wave's 32 keys
       f32x16 sc, dp;
@@ -829,9 +870,13 @@ void nsa_dkdv_seg_kernel(NsaParams p, int nblocks, float* part) {
 #pragma unroll
       for (int ds = 0; ds < 8; ds++) {
         sc = E::mfma32(tile_read16<V8>(Qb, l32i, 2 * ds + hi2),
-                       tile_read16<V8>(lds_k, wid * 32 + l32i, 2 * ds + hi2), sc);
+                       tile_read16<V8>(lds_k[0], wid * 32 + l32i, 2 * ds + hi2), sc);
         dp = E::mfma32(tile_read16<V8>(Db, l32i, 2 * ds + hi2), vreg[ds], dp);
       }
+#pragma unroll
+      for (int ds = 8; ds < DQK / 16; ds++)
+        sc = E::mfma32(tile_read16<V8>(Qb2, l32i, 2 * (ds - 4) + hi2),
+                       tile_read16<V8>(lds_k[NKT - 1], wid * 32 + l32i, 2 * (ds - 4) + hi2), sc);
       // element j of a lane is row 8*(j/4) + 4*h + j%4 of the chunk, column key l32
       const int mykey = wkey0 + l32i;
       const int need = g.causal ? mykey : 0;
@@ -859,29 +904,40 @@ void nsa_dkdv_seg_kernel(NsaParams p, int nblocks, float* part) {
       }
       // dV^T += dO^T P ; dK^T += Q^T dS  (16 rows per step)
 #pragma unroll
-      for (int k2 = 0; k2 < 2; k2++)
+      for (int k2 = 0; k2 < 2; k2++) {
 #pragma unroll
         for (int dt = 0; dt < 4; dt++) {
           dvt[dt] = E::mfma32(tile_read_tr<V8>(Db, k2, dt, ln), bp[k2], dvt[dt]);
           dkt[dt] = E::mfma32(tile_read_tr<V8>(Qb, k2, dt, ln), bd[k2], dkt[dt]);
         }
+#pragma unroll
+        for (int dt = 4; dt < DQK / 32; dt++)
+          dkt[dt] = E::mfma32(tile_read_tr<V8>(Qb2, k2, dt - 2, ln), bd[k2], dkt[dt]);
+      }
       wait_vm();
       __syncthreads();
       buf ^= 1;
     }
 
-    // fp32 partials of this segment: [segment][key within block][d], dK then dV
+    // fp32 partials of this segment: [segment][dK: key][DQK], then [dV: key][kDv]
     const int mykey = wkey0 + l32;
     if (mykey < key_hi) {
-      float* pk = part + ((long)sg * 2 * sbs + (mykey - key_lo)) * kD;
-      float* pv = pk + (long)sbs * kD;
+      float* sb = part + (long)sg * sbs * (DQK + kDv);
+      float* pk = sb + (long)(mykey - key_lo) * DQK;
+      float* pv = sb + (long)sbs * DQK + (long)(mykey - key_lo) * kDv;
 #pragma unroll
-      for (int dt = 0; dt < 4; dt++)
+      for (int dt = 0; dt < DQK / 32; dt++)
 #pragma unroll
         for (int jj = 0; jj < 4; jj++) {
           const int d0 = dt * 32 + 8 * jj + 4 * h;
           *reinterpret_cast<float4*>(pk + d0) =
               make_float4(dkt[dt][4 * jj], dkt[dt][4 * jj + 1], dkt[dt][4 * jj + 2], dkt[dt][4 * jj + 3]);
+        }
+#pragma unroll
+      for (int dt = 0; dt < kDv / 32; dt++)
+#pragma unroll
+        for (int jj = 0; jj < 4; jj++) {
+          const int d0 = dt * 32 + 8 * jj + 4 * h;
           *reinterpret_cast<float4*>(pv + d0) =
               make_float4(dvt[dt][4 * jj], dvt[dt][4 * jj + 1], dvt[dt][4 * jj + 2], dvt[dt][4 * jj + 3]);
         }
@@ -892,17 +948,20 @@ void nsa_dkdv_seg_kernel(NsaParams p, int nblocks, float* part) {
 
 // dK = scale * sum of a block's segment partials, dV = their sum, in segment
 // order; one thread per (block, key, 4 columns).
-template <class E>
+template <class E, int DQK>
 __global__ __launch_bounds__(256) void nsa_dkdv_reduce(NsaParams p, const int* seg_off, int nblocks,
                                                        const float* part) {
   const NsaGeom& g = p.g;
   const int sbs = g.sbs;
   const long i = (long)blockIdx.x * 256 + threadIdx.x;
-  const long per_block = (long)sbs * (kD / 4);
+  // one thread per (block, key, 4 columns of dK and the same 4 of dV; the
+  // threads of columns DQK-kDv.. handle dK only)
+  constexpr int C4 = DQK / 4;
+  const long per_block = (long)sbs * C4;
   if (i >= (long)nblocks * per_block) return;
   const int r = (int)(i / per_block);
-  const int key = (int)(i % per_block) / (kD / 4);
-  const int d0 = 4 * ((int)(i % per_block) % (kD / 4));
+  const int key = (int)(i % per_block) / C4;
+  const int d0 = 4 * ((int)(i % per_block) % C4);
   const int n2 = r / g.NB, gb = r % g.NB;
   const int b = seq_of_dev(g.blk_off, g.B, gb);
   const int blk = gb - g.blk_off[b];
@@ -910,19 +969,22 @@ __global__ __launch_bounds__(256) void nsa_dkdv_reduce(NsaParams p, const int* s
   const int skv = g.cu_kv[b + 1] - kv0;
   const int kpos = blk * sbs + key;
   if (kpos >= skv) return;
+  const bool has_v = d0 < kDv;
   float4 ak = make_float4(0.f, 0.f, 0.f, 0.f), av = ak;
   for (int sg = seg_off[r]; sg < seg_off[r + 1]; sg++) {
-    const float* pk = part + ((long)sg * 2 * sbs + key) * kD + d0;
-    const float4 x = *reinterpret_cast<const float4*>(pk);
-    const float4 y = *reinterpret_cast<const float4*>(pk + (long)sbs * kD);
+    const float* sb = part + (long)sg * sbs * (DQK + kDv);
+    const float4 x = *reinterpret_cast<const float4*>(sb + (long)key * DQK + d0);
     ak.x += x.x; ak.y += x.y; ak.z += x.z; ak.w += x.w;
-    av.x += y.x; av.y += y.y; av.z += y.z; av.w += y.w;
+    if (has_v) {
+      const float4 y = *reinterpret_cast<const float4*>(sb + (long)sbs * DQK + (long)key * kDv + d0);
+      av.x += y.x; av.y += y.y; av.z += y.z; av.w += y.w;
+    }
   }
-  const long orow = ((long)(kv0 + kpos) * p.N2 + n2) * kD + d0;
+  const long krow = (long)(kv0 + kpos) * p.N2 + n2;
   typedef typename E::T T;
-  *reinterpret_cast<uint2*>((T*)p.dk + orow) =
+  *reinterpret_cast<uint2*>((T*)p.dk + krow * DQK + d0) =
       pack4<E>(ak.x * p.scale, ak.y * p.scale, ak.z * p.scale, ak.w * p.scale);
-  *reinterpret_cast<uint2*>((T*)p.dv + orow) = pack4<E>(av.x, av.y, av.z, av.w);
+  if (has_v) *reinterpret_cast<uint2*>((T*)p.dv + krow * kDv + d0) = pack4<E>(av.x, av.y, av.z, av.w);
 }
 
 template <class E>
@@ -930,17 +992,35 @@ static hipError_t fwd_t(const NsaParams& p, hipStream_t st) {
   const int units = p.T * p.N2;
   const int n_items = (units + 3) / 4;
   if (n_items == 0) return hipSuccess;
-  if (p.G <= 16)
+  // 192-dim query/key heads: the 32-column kernel for every group size
+  if (p.D == 192)
+    hipLaunchKernelGGL((nsa_fwd_kernel<E, 192>), dim3(8 * ((n_items + 7) / 8)), dim3(256), 0, st,
+                       p, n_items);
+  else if (p.G <= 16)
     hipLaunchKernelGGL((nsa_fwd16_kernel<E>), dim3(8 * ((n_items + 7) / 8)), dim3(256), 0, st, p,
                        n_items);
   else
-    hipLaunchKernelGGL((nsa_fwd_kernel<E>), dim3(8 * ((n_items + 7) / 8)), dim3(256), 0, st, p,
-                       n_items);
+    hipLaunchKernelGGL((nsa_fwd_kernel<E, 128>), dim3(8 * ((n_items + 7) / 8)), dim3(256), 0, st,
+                       p, n_items);
   return hipGetLastError();
 }
 
 hipError_t launch_nsa_fwd(const NsaParams& p, int fp16, hipStream_t st) {
   return fp16 ? fwd_t<FP16>(p, st) : fwd_t<BF16>(p, st);
+}
+
+template <class E, int DQK>
+static hipError_t dkdv_launch(const NsaParams& p, int nw, int grid, int nb, hipStream_t st) {
+  if (nw <= 1)
+    hipLaunchKernelGGL((nsa_dkdv_seg_kernel<E, 1, DQK>), dim3(grid), dim3(64), 0, st, p, nb,
+                       p.part);
+  else if (nw <= 2)
+    hipLaunchKernelGGL((nsa_dkdv_seg_kernel<E, 2, DQK>), dim3(grid), dim3(128), 0, st, p, nb,
+                       p.part);
+  else
+    hipLaunchKernelGGL((nsa_dkdv_seg_kernel<E, 4, DQK>), dim3(grid), dim3(256), 0, st, p, nb,
+                       p.part);
+  return hipGetLastError();
 }
 
 template <class E>
@@ -949,12 +1029,15 @@ static hipError_t bwd_t(const NsaParams& p, hipStream_t st, void* const* ev, int
   const int units = p.T * p.N2;
   const int n_items = (units + 3) / 4;
   if (e == hipSuccess && n_items > 0) {
-    if (p.G <= 16)
+    if (p.D == 192)
+      hipLaunchKernelGGL((nsa_dq_kernel<E, 192>), dim3(8 * ((n_items + 7) / 8)), dim3(256), 0, st,
+                         p, n_items);
+    else if (p.G <= 16)
       hipLaunchKernelGGL((nsa_dq16_kernel<E>), dim3(8 * ((n_items + 7) / 8)), dim3(256), 0, st,
                          p, n_items);
     else
-      hipLaunchKernelGGL((nsa_dq_kernel<E>), dim3(8 * ((n_items + 7) / 8)), dim3(256), 0, st, p,
-                         n_items);
+      hipLaunchKernelGGL((nsa_dq_kernel<E, 128>), dim3(8 * ((n_items + 7) / 8)), dim3(256), 0, st,
+                         p, n_items);
     e = hipGetLastError();
   }
   if (e == hipSuccess) e = mark_event(ev, n_ev, 1, 1, st);
@@ -969,23 +1052,21 @@ static hipError_t bwd_t(const NsaParams& p, hipStream_t st, void* const* ev, int
   if (e == hipSuccess && nb > 0) {
     const int nw = (p.g.sbs + 31) / 32;  // 1..4 waves, 32 keys each
     const int grid = nsa_dkdv_grid(p);
-    if (nw <= 1)
-      hipLaunchKernelGGL((nsa_dkdv_seg_kernel<E, 1>), dim3(grid), dim3(64), 0, st, p, nb,
-                         p.part);
-    else if (nw <= 2)
-      hipLaunchKernelGGL((nsa_dkdv_seg_kernel<E, 2>), dim3(grid), dim3(128), 0, st, p, nb,
-                         p.part);
+    if (p.D == 192)
+      e = dkdv_launch<E, 192>(p, nw, grid, nb, st);
     else
-      hipLaunchKernelGGL((nsa_dkdv_seg_kernel<E, 4>), dim3(grid), dim3(256), 0, st, p, nb,
-                         p.part);
-    e = hipGetLastError();
+      e = dkdv_launch<E, 128>(p, nw, grid, nb, st);
   }
   if (e == hipSuccess) e = mark_event(ev, n_ev, 2, 1, st);
   if (e == hipSuccess) e = mark_event(ev, n_ev, 3, 0, st);
   if (e == hipSuccess && nb > 0) {
-    const long n = (long)nb * p.g.sbs * (kD / 4);
-    hipLaunchKernelGGL((nsa_dkdv_reduce<E>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
-                       p, p.seg_off, nb, (const float*)p.part);
+    const long n = (long)nb * p.g.sbs * (p.D / 4);
+    if (p.D == 192)
+      hipLaunchKernelGGL((nsa_dkdv_reduce<E, 192>), dim3((unsigned)((n + 255) / 256)), dim3(256),
+                         0, st, p, p.seg_off, nb, (const float*)p.part);
+    else
+      hipLaunchKernelGGL((nsa_dkdv_reduce<E, 128>), dim3((unsigned)((n + 255) / 256)), dim3(256),
+                         0, st, p, p.seg_off, nb, (const float*)p.part);
     e = hipGetLastError();
   }
   if (e == hipSuccess) e = mark_event(ev, n_ev, 3, 1, st);

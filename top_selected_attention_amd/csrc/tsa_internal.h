@@ -157,12 +157,12 @@ struct NsaParams {
   const int* rev_ptr;
   const int* rev;
   NsaGeom g;
-  int T, Tk, N1, N2, G, D;
+  int T, Tk, N1, N2, G, D;  // D: query/key head dim (128 or 192); values are 128 wide
   float scale;
   // backward dK/dV segments (workspace)
   int* seg_off;        // [N2*NB + 1] exclusive scan of segments per block
   int* seg_sums;       // scan scratch
-  float* part;         // [max_segments][2][sbs][D] fp32 partial dK, dV
+  float* part;         // [max_segments][sbs*D (dK) + sbs*128 (dV)] fp32 partials
   int max_segments;
 };
 
