@@ -72,7 +72,7 @@ def parse():
 
 
 WORKLOADS = ["bsa_window_128k", "bsa_causal_8k", "bsa_small", "bsa_tnd_varlen", "nsa_varlen",
-             "sfa_decode", "sfa_sharedkv_decode"]
+             "sfa_decode", "sfa_sharedkv_decode", "floyd_256"]
 
 
 def _warm(step, args):
@@ -652,6 +652,80 @@ def cpu_baseline_sfa_skv(ctx, seconds):
             "sample": f"{done} of {T} decode tokens (float64) of {w['name']}, {el:.1f} s"}
 
 
+# ----------------------------------------------------------------------------
+# FloydAttention
+# ----------------------------------------------------------------------------
+
+def bench_floyd(args):
+    import torch
+    import workloads as W
+    import top_selected_attention_amd as tsa
+
+    w = W.floyd_workload()
+    q, k1, v1, k2, v2, do = W.floyd_inputs()
+    scale = 1.0 / math.sqrt(w["D"])
+    dev = torch.device("cuda", 0)
+    plan = tsa.FloydPlan(*(t.to(dev) for t in (q, k1, v1, k2, v2)), scale=scale)
+    plan.set_dout(do.to(dev))
+    # one GEMM term: 2 * N * M * K * D per head; forward 4 terms (S over n and
+    # over m, P V1, P V2), backward the method's 10 (S, dP, dV, dQ, dK, each
+    # over n and over m)
+    term = 2.0 * w["B"] * w["H"] * w["N"] * w["M"] * w["K"] * w["D"]
+    fwd_flops, bwd_flops = 4.0 * term, 10.0 * term
+    st, ms_step, K, ms_ev = _timed_steps(args, plan, 3, 5)
+    fwd_ms, bwd_ms = sum(st[:3]), sum(st[3:])
+    names = ["fwd_scores", "fwd_softmax", "fwd_pv", "bwd_scores_dp", "bwd_p_ds", "bwd_dv",
+             "bwd_dq", "bwd_dk"]
+    stage = dict(zip(names, st))
+    # dominant stage: the backward scores and dP (four GEMM terms)
+    rl_ms, rl_flops = stage["bwd_scores_dp"], 4.0 * term
+    achieved = rl_flops / (rl_ms * 1e-3) / 1e12
+    value = (fwd_flops + bwd_flops) / (ms_step * 1e-3) / 1e12
+    res = {
+        "metric": "effective TFLOP/s on selected blocks (fwd, bwd) and % of bf16 MFMA peak",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w["dtype"], "data": "synthetic",
+        "config": {"workload": w["name"], "B": w["B"], "H": w["H"], "N": w["N"], "M": w["M"],
+                   "K": w["K"], "D": w["D"],
+                   "flop_count": "2*N*M*K*D per GEMM term and head; forward 4 terms, backward 10"},
+        "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "fwd_tflops": round(fwd_flops / (fwd_ms * 1e-3) / 1e12, 2),
+        "bwd_tflops": round(bwd_flops / (bwd_ms * 1e-3) / 1e12, 2),
+        "stage_ms": {k_: round(v_, 4) for k_, v_ in stage.items()},
+        "ms_per_step_instrumented": round(ms_ev, 4),
+        "step_ms_events": _step_stats(plan.step_ms),
+        "ms_per_step_cold": round(plan.cold_ms, 4),
+        "settle_steps": plan.settle_steps,
+        "roofline": {"kernel": "floyd_gemm_kernel (backward scores and dP)", "bound": "mfma",
+                     "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+    }
+    return res, (w, q, k1, v1, k2, v2, do, scale, term)
+
+
+def cpu_baseline_floyd(ctx, seconds):
+    """Oracle (float64 numpy) fwd + bwd, one head at a time."""
+    import oracle
+    w, q, k1, v1, k2, v2, do, scale, term = ctx
+    f = [t.float().numpy() for t in (q, k1, v1, k2, v2, do)]
+    done = 0
+    t0 = time.perf_counter()
+    for h in range(w["H"]):
+        s_ = (slice(0, 1), slice(h, h + 1))
+        args = [x[s_] for x in f[:5]]
+        y, _ = oracle.floyd_fwd(*args, scale)
+        oracle.floyd_bwd(*args, y, f[5][s_], scale)
+        done += 1
+        if time.perf_counter() - t0 > seconds:
+            break
+    el = time.perf_counter() - t0
+    per_head = 14.0 * term / (w["B"] * w["H"])
+    return {"value": round(per_head * done / el / 1e12, 6), "unit": "TFLOP/s", "cores": _threads(),
+            "kind": "oracle",
+            "sample": f"{done} of {w['H']} heads (fwd + bwd, float64) of {w['name']}, {el:.1f} s"}
+
+
 def _flush_buffer():
     """512 MiB that one write sweeps through L2 (8 x 4 MiB) and MALL (256 MiB)."""
     import torch
@@ -1016,10 +1090,10 @@ def _kind(name):
 
 
 BENCH = {"bsa": bench_bsa, "bsa_tnd_varlen": bench_bsa_tnd, "nsa_varlen": bench_nsa,
-         "sfa_decode": bench_sfa, "sfa_sharedkv_decode": bench_sfa_skv}
+         "sfa_decode": bench_sfa, "sfa_sharedkv_decode": bench_sfa_skv, "floyd_256": bench_floyd}
 CPU_BASELINE = {"bsa": cpu_baseline_bsa, "bsa_tnd_varlen": cpu_baseline_bsa_tnd,
                 "nsa_varlen": cpu_baseline_nsa, "sfa_decode": cpu_baseline_sfa,
-                "sfa_sharedkv_decode": cpu_baseline_sfa_skv}
+                "sfa_sharedkv_decode": cpu_baseline_sfa_skv, "floyd_256": cpu_baseline_floyd}
 
 
 def run_workload(name, args):

@@ -81,7 +81,8 @@ TSA_API const char* tsa_status_string(int status);
 
 /* sizeof of each argument struct, for binding checks: which = 0 bsa_fwd,
  * 1 bsa_bwd, 2 nsa_select_fwd, 3 nsa_select_bwd, 4 sfa_paged_fwd,
- * 5 sfa_sharedkv_fwd; returns 0 for an unknown value. */
+ * 5 sfa_sharedkv_fwd, 6 floyd_fwd, 7 floyd_bwd; returns 0 for an unknown
+ * value. */
 TSA_API size_t tsa_args_sizeof(int which);
 
 /* ------------------------------------------------------------------------
@@ -349,9 +350,10 @@ TSA_API int nsa_compact(const nsa_select_fwd_args* args, int32_t* row_ptr, int32
  *   its causal offset; topk_indices [T, N2, topk], out [T, N1, Dv], lse
  *   [T, N1].
  * key_cache [num_pages, page_size, N2, D], key_rope_cache [num_pages,
- *   page_size, N2, Dr], value_cache [num_pages, page_size, N2, Dv] (PA_ND);
- *   value_cache must equal key_cache (shared KV: V is the key row; a
- *   separate value cache returns TSA_ERR_UNSUPPORTED).
+ *   page_size, N2, Dr], value_cache [num_pages, page_size, N2, Dv] (PA_ND,
+ *   paged like the key cache through the same block table); value_cache may
+ *   equal key_cache (shared KV: V is the key row, gathered once) or be a
+ *   cache of its own (its rows are gathered beside the key rows).
  * block_table int32 DEVICE [B, max_pages]: physical page of logical page p.
  * kv_lens int32 DEVICE [B]: active KV tokens of each sequence.
  * topk_indices int32 DEVICE [B, Sq, N2, topk]: selected sparse-block ids
@@ -496,6 +498,78 @@ TSA_API int sfa_sharedkv_metadata(const sfa_sharedkv_fwd_args* args, void* tasks
 TSA_API int sfa_sharedkv_fwd_workspace_size(const sfa_sharedkv_fwd_args* args, size_t* bytes);
 TSA_API int sfa_sharedkv_fwd(const sfa_sharedkv_fwd_args* args, void* workspace,
                              size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * FloydAttention ("aclnnFusedFloydAttentionGrad", function description and
+ * formula section): the query keeps two sequence axes, and the scores of
+ * query row (n, m) against key k add two products, each batched over one of
+ * those axes:
+ *   S = scale * (Q K1^T + Q K2^T),  P = Softmax over k (S),  Y = P V1 + P V2;
+ * backward: dP = dY V1^T + dY V2^T, dS = P * (dP - rowsum(dY * Y)),
+ *   dV1 = P^T dY, dV2 = P^T dY, dQ = (dS K1 + dS K2) scale,
+ *   dK1 = dS^T Q scale, dK2 = dS^T Q scale.
+ * Layouts (the page's shape table is lost; read from its constraints: axes
+ * 0, 2 and 4 of query and key1 agree, key1/value1 and key2/value2 share
+ * shapes, and the second pair is batched over the query's other sequence
+ * axis): q [B, H, N, M, D]; k1, v1 [B, H, N, K, D]; k2, v2 [B, H, M, K, D];
+ * out like q; lse fp32 [B, H, N, M] (one natural-log LSE per query row: the
+ * page's softmaxMax / softmaxSum pair carries the same).
+ * Constraints (shape constraints, read in this order): B in [1, 2048], H in
+ * [1, 256], N a multiple of 16 in [16, 2^20], M and K multiples of 128 in
+ * [128, 2^20], D in {32, 64, 128}; scale finite and > 0.  No atten_mask
+ * (the page gives no layout for it).
+ * Built from small operators (the page advises them once M x D or K x D is
+ * large): strided batched MFMA GEMMs with the scores materialised in the
+ * workspace (fp32 S and a 16-bit P, plus fp32 dP and a 16-bit dS in the
+ * backward, B*H*N*M*K elements each, and an fp32 [B*H*N*M*D] accumulator).
+ * Deterministic (no atomics).  Stages: forward 0 = scores, 1 = softmax,
+ * 2 = P V1 + P V2; backward 0 = scores and dP, 1 = P and dS, 2 = dV1 / dV2,
+ * 3 = dQ, 4 = dK1 / dK2.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  int32_t dtype;            /* TSA_BF16 or TSA_FP16 (every 16-bit tensor) */
+  int32_t B, H, N, M, K, D;
+  float scale;              /* finite, > 0; typically 1/sqrt(D) */
+  const void* q;            /* DEVICE [B, H, N, M, D] */
+  const void* k1;           /* DEVICE [B, H, N, K, D] */
+  const void* v1;           /* DEVICE [B, H, N, K, D] */
+  const void* k2;           /* DEVICE [B, H, M, K, D] */
+  const void* v2;           /* DEVICE [B, H, M, K, D] */
+  void* out;                /* DEVICE, written [B, H, N, M, D] */
+  float* lse;               /* DEVICE, written [B, H, N, M] */
+  int32_t reuse_lists;      /* unused (no lists); keep 0 */
+  int32_t n_events;         /* number of stages to time (0 = off) */
+  void* const* events;      /* HOST array of 2*n_events hipEvent_t (see above) */
+} floyd_fwd_args;
+
+typedef struct {
+  int32_t dtype;
+  int32_t B, H, N, M, K, D;
+  float scale;
+  const void* q;            /* DEVICE, as in the forward */
+  const void* k1;
+  const void* v1;
+  const void* k2;
+  const void* v2;
+  const void* out;          /* DEVICE, the forward output */
+  const void* dout;         /* DEVICE, its gradient [B, H, N, M, D] */
+  const float* lse;         /* DEVICE, the forward LSE */
+  void* dq;                 /* DEVICE, written, like q */
+  void* dk1;                /* DEVICE, written, like k1 */
+  void* dv1;                /* DEVICE, written, like v1 */
+  void* dk2;                /* DEVICE, written, like k2 */
+  void* dv2;                /* DEVICE, written, like v2 */
+  int32_t reuse_lists;      /* unused; keep 0 */
+  int32_t n_events;
+  void* const* events;
+} floyd_bwd_args;
+
+TSA_API int floyd_fwd_workspace_size(const floyd_fwd_args* args, size_t* bytes);
+TSA_API int floyd_fwd(const floyd_fwd_args* args, void* workspace, size_t workspace_bytes,
+                      void* stream);
+TSA_API int floyd_bwd_workspace_size(const floyd_bwd_args* args, size_t* bytes);
+TSA_API int floyd_bwd(const floyd_bwd_args* args, void* workspace, size_t workspace_bytes,
+                      void* stream);
 
 #ifdef __cplusplus
 }

@@ -244,7 +244,8 @@ def test_sfa_tnd_validation(tsa, cq, T, status):
     (dict(page_size=2048), 2),
     (dict(sparse_block_size=3), 2),        # must divide the page size
     (dict(sparse_mode=2), 2),
-    (dict(value_cache=24), 3),             # separate value cache: not built
+    (dict(value_cache=32), 0),             # a value cache of its own
+    (dict(value_cache=24), 2),             # (16-byte aligned)
     (dict(key_cache=24, value_cache=24), 2),   # caches 16-byte aligned
     (dict(q_rope=40), 2),
     (dict(q_layout=1), 1),                 # TND queries need cu_seqlens_q
@@ -338,3 +339,43 @@ def test_sfa_sharedkv_metadata_size_and_buffer_checks(tsa):
     assert tsa.lib.sfa_sharedkv_fwd(ctypes.byref(a), ctypes.c_void_p(256), w.value, None) == 2
     bad = _skv(tsa, N1=48)
     assert tsa.lib.sfa_sharedkv_metadata_size(ctypes.byref(bad), ctypes.byref(n)) == 2
+
+
+def _floyd(tsa, bwd=False, **kw):
+    a = dict(dtype=0, B=1, H=2, N=16, M=128, K=128, D=64, scale=0.125, q=256, k1=512, v1=768,
+             k2=1024, v2=1280, out=1536, lse=1792)
+    if bwd:
+        a.update(dout=2048, dq=2304, dk1=2560, dv1=2816, dk2=3072, dv2=3328)
+    a.update(kw)
+    return (tsa._abi.FloydBwdArgs if bwd else tsa._abi.FloydFwdArgs)(**a)
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({}, 0),
+    (dict(N=24), 2),                       # N a multiple of 16
+    (dict(N=0), 2),
+    (dict(M=192), 2),                      # M a multiple of 128
+    (dict(K=64), 2),                       # K at least 128
+    (dict(D=48), 2),                       # D in {32, 64, 128}
+    (dict(H=257), 2),
+    (dict(B=2049), 2),
+    (dict(scale=0.0), 2),
+    (dict(dtype=3), 2),
+    (dict(k2=0), 1),
+    (dict(v1=264), 2),                     # 16-byte aligned tensors
+])
+def test_floyd_validation(tsa, kw, status):
+    assert _size(tsa, tsa.lib.floyd_fwd_workspace_size, _floyd(tsa, **kw))[0] == status
+    assert _size(tsa, tsa.lib.floyd_bwd_workspace_size, _floyd(tsa, True, **kw))[0] == status
+
+
+def test_floyd_workspace_sizes(tsa):
+    """fp32 S + 16-bit P + fp32 [rows, D] forward; the backward adds fp32 dP
+    and a 16-bit dS (each B*H*N*M*K elements)."""
+    s, f = _size(tsa, tsa.lib.floyd_fwd_workspace_size, _floyd(tsa))
+    s2, b = _size(tsa, tsa.lib.floyd_bwd_workspace_size, _floyd(tsa, True))
+    el, rows = 2 * 16 * 128 * 128, 2 * 16 * 128
+    assert s == s2 == 0
+    assert el * 6 + rows * 64 * 4 <= f <= el * 6 + rows * 64 * 4 + 4096
+    assert el * 12 + rows * 64 * 4 <= b <= el * 12 + rows * 64 * 4 + 4096
+    assert _size(tsa, tsa.lib.floyd_bwd_workspace_size, _floyd(tsa, True, dq=0))[0] == 1

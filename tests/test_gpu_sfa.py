@@ -196,3 +196,58 @@ def test_sfa_unselected_rows_are_never_read():
     krc2[noise] = (W.normal(tuple(krc.shape), 94) * 50)[noise]
     o2, l2 = _run(q, qr, kc2, krc2, bt, kv_lens, idx, scale, 3)
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# ----------------------------------------------------------------------------
+# A value cache of its own (not the key cache)
+# ----------------------------------------------------------------------------
+
+def _run_sepv(q, qr, kc, krc, vc, bt, kv_lens, idx, scale, mode, sbs=1):
+    tsa = _tsa()
+    d = torch.device("cuda")
+    out, lse = tsa.sfa_paged_fwd(q.to(d), qr.to(d), kc.to(d), krc.to(d), vc.to(d),
+                                 torch.from_numpy(bt).to(d), torch.from_numpy(kv_lens).to(d),
+                                 torch.from_numpy(idx).to(d), scale, mode, sbs)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+@pytest.mark.parametrize("N1,page,kv_len,K,mode,sbs,dtype", [
+    (64, 16, 200, 40, 3, 1, "bf16"),     # one split, K not a multiple of 32
+    (64, 32, 1000, 300, 3, 1, "bf16"),   # several splits
+    (16, 16, 64, 64, 0, 1, "fp16"),      # 16 heads (idle waves), no mask
+    (128, 64, 700, 100, 3, 1, "bf16"),   # two head groups
+    (32, 32, 512, 12, 3, 8, "bf16"),     # sparse blocks of 8 positions
+])
+def test_sfa_separate_value_cache(N1, page, kv_len, K, mode, sbs, dtype):
+    """"aclnnSparseFlashAttention", constraints section: value rows of
+    D = 512 of their own; the oracle gathers them from value_cache."""
+    q, qr, kc, krc, bt, kv_lens, idx = W.sfa_inputs(B=2, Sq=3, N1=N1, page=page, kv_len=kv_len,
+                                                    topk=K, seed_base=55, extra_pages=3,
+                                                    dtype=dtype)
+    vc = W.normal(tuple(kc.shape), 59, dtype)
+    if sbs > 1:
+        rng = np.random.default_rng(57)
+        nblk = kv_len // sbs
+        idx = np.stack([np.stack([np.sort(rng.choice(nblk, K, replace=False)) for _ in range(3)])
+                        for _ in range(2)])[:, :, None, :].astype(np.int32)
+    kv_lens[1] = kv_len - 5
+    idx[0, 1, 0, -3:] = -1
+    idx[1] = np.where(idx[1] * sbs >= kv_lens[1], -1, idx[1])
+    scale = 1 / math.sqrt(576)
+    out, lse = _run_sepv(q, qr, kc, krc, vc, bt, kv_lens, idx, scale, mode, sbs)
+    ro, rl = oracle.sfa_fwd(_np(q), _np(qr), _np(kc), _np(krc), _np(vc), bt, kv_lens, idx, scale,
+                            sparse_mode=mode, sparse_block_size=sbs)
+    _check(out, lse, ro, rl)
+
+
+def test_sfa_separate_value_cache_equal_to_keys_matches_shared():
+    """A value cache that holds the key rows (a copy, not the same pointer)
+    gives the shared-KV result within rounding of the summation order."""
+    q, qr, kc, krc, bt, kv_lens, idx = W.sfa_inputs(B=2, Sq=2, N1=64, page=32, kv_len=800,
+                                                    topk=200, seed_base=65)
+    scale = 1 / math.sqrt(576)
+    o1, l1 = _run(q, qr, kc, krc, bt, kv_lens, idx, scale, 3)
+    o2, l2 = _run_sepv(q, qr, kc, krc, kc.clone(), bt, kv_lens, idx, scale, 3)
+    assert torch.allclose(o1.float(), o2.float(), atol=2e-2, rtol=0)
+    assert torch.allclose(l1, l2, atol=1e-4, rtol=0)

@@ -13,7 +13,10 @@ Entry points (names as in the C ABI):
   sfa_paged_fwd                              sparse flash attention decode
   sfa_sharedkv_fwd                           shared-KV decode: band over the
                                              original cache + compressed top-k
-The ``*Plan`` classes (BsaPlan, NsaPlan, SfaPlan, SfaSharedkvPlan)
+  floyd_fwd, floyd_bwd                       FloydAttention (two score products
+                                             batched over the query's two
+                                             sequence axes, one softmax)
+The ``*Plan`` classes (BsaPlan, NsaPlan, SfaPlan, SfaSharedkvPlan, FloydPlan)
 pre-allocate outputs and workspace for repeated calls.
 """
 
@@ -570,3 +573,93 @@ def sfa_sharedkv_fwd(q, q_rope, seqused_kv, ori=None, cmp=None, scale=None, win_
     return SfaSharedkvPlan(q, q_rope, seqused_kv, ori, cmp, scale, win_left, win_right,
                            cmp_ratio, cu_seqlens_q).fwd()
 
+
+
+# ----------------------------------------------------------------------------
+# FloydAttention
+# ----------------------------------------------------------------------------
+
+class FloydPlan:
+    """Forward and backward of FloydAttention for fixed tensors.
+
+    q [B, H, N, M, D]; k1, v1 [B, H, N, K, D]; k2, v2 [B, H, M, K, D] (bf16 or
+    fp16).  ``fwd()`` returns (out [B, H, N, M, D], lse [B, H, N, M]);
+    ``bwd(dout)`` returns (dq, dk1, dv1, dk2, dv2).
+    """
+
+    def __init__(self, q, k1, v1, k2, v2, scale=None, backward=True):
+        _check(q, "q")
+        for t, n in ((k1, "k1"), (v1, "v1"), (k2, "k2"), (v2, "v2")):
+            _check(t, n, q.dtype)
+        if q.dim() != 5:
+            raise ValueError("q must be [B, H, N, M, D]")
+        B, H, N, M, D = q.shape
+        K = k1.shape[3]
+        if tuple(k1.shape) != (B, H, N, K, D) or v1.shape != k1.shape:
+            raise ValueError(f"k1 / v1 must be {(B, H, N, K, D)}")
+        if tuple(k2.shape) != (B, H, M, K, D) or v2.shape != k2.shape:
+            raise ValueError(f"k2 / v2 must be {(B, H, M, K, D)}")
+        self.q, self.k1, self.v1, self.k2, self.v2 = q, k1, v1, k2, v2
+        self.scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+        dev = q.device
+        self.out = torch.empty_like(q)
+        self.lse = torch.empty((B, H, N, M), dtype=torch.float32, device=dev)
+        common = dict(dtype=_dtype_code(q), B=B, H=H, N=N, M=M, K=K, D=D, scale=self.scale,
+                      q=q.data_ptr(), k1=k1.data_ptr(), v1=v1.data_ptr(), k2=k2.data_ptr(),
+                      v2=v2.data_ptr())
+        self.fa = _abi.FloydFwdArgs(out=self.out.data_ptr(), lse=self.lse.data_ptr(), **common)
+        nb = ctypes.c_size_t()
+        _abi.call(lib.floyd_fwd_workspace_size, ctypes.byref(self.fa), ctypes.byref(nb))
+        size = nb.value
+        if backward:
+            self.dq = torch.empty_like(q)
+            self.dk1, self.dv1 = torch.empty_like(k1), torch.empty_like(v1)
+            self.dk2, self.dv2 = torch.empty_like(k2), torch.empty_like(v2)
+            self.ba = _abi.FloydBwdArgs(out=self.out.data_ptr(), dout=0, lse=self.lse.data_ptr(),
+                                        dq=self.dq.data_ptr(), dk1=self.dk1.data_ptr(),
+                                        dv1=self.dv1.data_ptr(), dk2=self.dk2.data_ptr(),
+                                        dv2=self.dv2.data_ptr(), **common)
+            self.ba.dout = self.out.data_ptr()          # a placeholder for the size query
+            _abi.call(lib.floyd_bwd_workspace_size, ctypes.byref(self.ba), ctypes.byref(nb))
+            size = max(size, nb.value)
+            self.dout = None
+        # one workspace serves both directions
+        self.ws = _workspace(size, dev)
+
+    def fwd(self):
+        _abi.call(lib.floyd_fwd, ctypes.byref(self.fa), _ptr(self.ws),
+                  ctypes.c_size_t(self.ws.numel()), _stream())
+        return self.out, self.lse
+
+    def set_out(self, out, lse):
+        """Use an externally produced forward output / LSE in the backward."""
+        _check(out, "out", self.q.dtype, self.q.shape)
+        _check(lse, "lse", torch.float32, self.lse.shape)
+        self.ba.out, self.ba.lse = out.data_ptr(), lse.data_ptr()
+        self._ext = (out, lse)
+
+    def set_dout(self, dout):
+        _check(dout, "dout", self.q.dtype, self.q.shape)
+        self.dout = dout
+        self.ba.dout = dout.data_ptr()
+
+    def bwd(self, dout=None):
+        if dout is not None and dout is not self.dout:
+            self.set_dout(dout)
+        if self.dout is None:
+            raise ValueError("bwd needs dout")
+        _abi.call(lib.floyd_bwd, ctypes.byref(self.ba), _ptr(self.ws),
+                  ctypes.c_size_t(self.ws.numel()), _stream())
+        return self.dq, self.dk1, self.dv1, self.dk2, self.dv2
+
+
+def floyd_fwd(q, k1, v1, k2, v2, scale=None):
+    """FloydAttention forward: returns (out, lse)."""
+    return FloydPlan(q, k1, v1, k2, v2, scale, backward=False).fwd()
+
+
+def floyd_bwd(q, k1, v1, k2, v2, out, dout, lse, scale=None):
+    """FloydAttention backward: returns (dq, dk1, dv1, dk2, dv2)."""
+    plan = FloydPlan(q, k1, v1, k2, v2, scale, backward=True)
+    plan.set_out(out, lse)
+    return plan.bwd(dout)

@@ -21,6 +21,7 @@ EXPORTS = [
     "sfa_paged_fwd_noalloc_max_bytes", "sfa_paged_fwd_noalloc",
     "sfa_sharedkv_fwd_workspace_size", "sfa_sharedkv_fwd",
     "sfa_sharedkv_metadata_size", "sfa_sharedkv_metadata",
+    "floyd_fwd_workspace_size", "floyd_fwd", "floyd_bwd_workspace_size", "floyd_bwd",
 ]
 
 
@@ -115,7 +116,27 @@ class SfaSharedkvArgs(ctypes.Structure):
     ] + TRAIL
 
 
-ARG_STRUCTS = [BsaFwdArgs, BsaBwdArgs, NsaFwdArgs, NsaBwdArgs, SfaArgs, SfaSharedkvArgs]
+_FLOYD_COMMON = [
+    ("dtype", c_int32), ("B", c_int32), ("H", c_int32), ("N", c_int32), ("M", c_int32),
+    ("K", c_int32), ("D", c_int32), ("scale", c_float),
+    ("q", c_void_p), ("k1", c_void_p), ("v1", c_void_p), ("k2", c_void_p), ("v2", c_void_p),
+]
+
+
+class FloydFwdArgs(ctypes.Structure):
+    _fields_ = _FLOYD_COMMON + [("out", c_void_p), ("lse", c_void_p)] + TRAIL
+
+
+class FloydBwdArgs(ctypes.Structure):
+    _fields_ = _FLOYD_COMMON + [
+        ("out", c_void_p), ("dout", c_void_p), ("lse", c_void_p),
+        ("dq", c_void_p), ("dk1", c_void_p), ("dv1", c_void_p), ("dk2", c_void_p),
+        ("dv2", c_void_p),
+    ] + TRAIL
+
+
+ARG_STRUCTS = [BsaFwdArgs, BsaBwdArgs, NsaFwdArgs, NsaBwdArgs, SfaArgs, SfaSharedkvArgs,
+               FloydFwdArgs, FloydBwdArgs]
 
 _lib = None
 
@@ -142,6 +163,8 @@ def load(path):
         "sfa_paged_fwd_noalloc": [P, P],
         "sfa_sharedkv_fwd_workspace_size": [P, P], "sfa_sharedkv_fwd": [P, P, c_size_t, P],
         "sfa_sharedkv_metadata_size": [P, P], "sfa_sharedkv_metadata": [P, P, c_size_t, P],
+        "floyd_fwd_workspace_size": [P, P], "floyd_fwd": [P, P, c_size_t, P],
+        "floyd_bwd_workspace_size": [P, P], "floyd_bwd": [P, P, c_size_t, P],
     }
     for name, args in sig.items():
         f = getattr(lib, name)

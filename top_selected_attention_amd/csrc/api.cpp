@@ -503,11 +503,10 @@ int check_sfa(const sfa_paged_fwd_args* a) {
       (!a->q || !a->q_rope || !a->key_cache || !a->key_rope_cache || !a->value_cache ||
        !a->block_table || !a->kv_lens || !a->topk_indices || !a->out))
     return TSA_ERR_NULL;
-  // Shared KV ("SparseAttnSharedkvMetadata": sharedkv): the value row is the
-  // key row; a separate value cache is not built.
-  if (a->value_cache != a->key_cache) return TSA_ERR_UNSUPPORTED;
+  // value_cache may alias key_cache (shared KV, "SparseAttnSharedkvMetadata":
+  // sharedkv) or be a cache of its own with the same paging.
   if (!a16(a->q) || !a16(a->q_rope) || !a16(a->key_cache) || !a16(a->key_rope_cache) ||
-      !a16(a->out))
+      !a16(a->value_cache) || !a16(a->out))
     return TSA_ERR_INVALID;
   return TSA_OK;
 }
@@ -659,6 +658,56 @@ size_t sfa_carve(const SfaParams& p, void* ws, SfaParams* out) {
   return c.off + kAlign;
 }
 
+// ----- FloydAttention ----------------------------------------------------------
+
+// "aclnnFusedFloydAttentionGrad", shape constraints (read as B, H, N, M, K,
+// D): B in [1, 2K], H in [1, 256], N a multiple of 16 in [16, 1M], M and K
+// multiples of 128 in [128, 1M], D in {32, 64, 128}.
+template <class A>
+int check_floyd(const A* a) {
+  if (!a) return TSA_ERR_NULL;
+  if (a->dtype != TSA_BF16 && a->dtype != TSA_FP16) return TSA_ERR_INVALID;
+  if (a->B < 1 || a->B > 2048 || a->H < 1 || a->H > 256) return TSA_ERR_INVALID;
+  if (a->N < 16 || a->N > (1 << 20) || a->N % 16) return TSA_ERR_INVALID;
+  if (a->M < 128 || a->M > (1 << 20) || a->M % 128) return TSA_ERR_INVALID;
+  if (a->K < 128 || a->K > (1 << 20) || a->K % 128) return TSA_ERR_INVALID;
+  if (a->D != 32 && a->D != 64 && a->D != 128) return TSA_ERR_INVALID;
+  if (!std::isfinite(a->scale) || !(a->scale > 0.f)) return TSA_ERR_INVALID;
+  // launch sizes: the largest GEMM grids and the row kernels fit 31 bits
+  const long Z = (long)a->B * a->H;
+  const long rows = Z * a->N * a->M;
+  const double s1 = (double)Z * a->N * cdiv(a->M, 64) * cdiv(a->K, 128);
+  const double s2 = (double)Z * a->M * cdiv(a->N, 64) * cdiv(a->K, 128);
+  if (s1 > 2147483647.0 || s2 > 2147483647.0 || rows / 4 + 1 > 2147483647L)
+    return TSA_ERR_INVALID;
+  if ((double)rows * a->K * 12 > 9.0e18) return TSA_ERR_INVALID;
+  if (!a->q || !a->k1 || !a->v1 || !a->k2 || !a->v2) return TSA_ERR_NULL;
+  if (!a16(a->q) || !a16(a->k1) || !a16(a->v1) || !a16(a->k2) || !a16(a->v2))
+    return TSA_ERR_INVALID;
+  return TSA_OK;
+}
+
+// Workspace: fp32 S, (backward: fp32 dP), 16-bit P, (backward: 16-bit dS),
+// fp32 [rows, D] accumulator.
+template <class A>
+size_t floyd_carve(const A* a, void* ws, FloydParams* p, bool bwd) {
+  const long rows = (long)a->B * a->H * a->N * a->M;
+  const long el = rows * a->K;
+  Carver c(ws);
+  FloydParams w;
+  std::memset(&w, 0, sizeof(w));
+  w.s = c.take<float>(el);
+  w.dp = bwd ? c.take<float>(el) : nullptr;
+  w.p = c.take<uint16_t>(el);
+  w.ds = bwd ? c.take<uint16_t>(el) : nullptr;
+  w.acc = c.take<float>(rows * a->D);
+  w.Z = a->B * a->H; w.N = a->N; w.M = a->M; w.K = a->K; w.D = a->D;
+  w.scale = a->scale;
+  w.q = a->q; w.k1 = a->k1; w.v1 = a->v1; w.k2 = a->k2; w.v2 = a->v2;
+  if (p) *p = w;
+  return c.off + kAlign;
+}
+
 // ----- fixed scratch for the entry point that allocates nothing -------------
 
 // Every GPU the library runs on holds its own copy of this array until the
@@ -716,6 +765,8 @@ size_t tsa_args_sizeof(int which) {
     case 3: return sizeof(nsa_select_bwd_args);
     case 4: return sizeof(sfa_paged_fwd_args);
     case 5: return sizeof(sfa_sharedkv_fwd_args);
+    case 6: return sizeof(floyd_fwd_args);
+    case 7: return sizeof(floyd_bwd_args);
     default: return 0;
   }
 }
@@ -1007,6 +1058,61 @@ int sfa_paged_fwd_noalloc(const sfa_paged_fwd_args* a, void* stream) {
   // the split partials are written in full before the combine reads them,
   // so nothing in the scratch needs clearing between calls
   return sfa_paged_fwd(a, ptr, kScratchBytes, stream);
+}
+
+// ----- FloydAttention ----------------------------------------------------------
+
+int floyd_fwd_workspace_size(const floyd_fwd_args* a, size_t* bytes) {
+  if (!bytes) return TSA_ERR_NULL;
+  int s = check_floyd(a);
+  if (s) return s;
+  if (!a->out || !a->lse) return TSA_ERR_NULL;
+  if (!a16(a->out)) return TSA_ERR_INVALID;
+  *bytes = floyd_carve(a, nullptr, nullptr, false);
+  return TSA_OK;
+}
+
+int floyd_fwd(const floyd_fwd_args* a, void* ws, size_t ws_bytes, void* stream) {
+  size_t need;
+  int s = floyd_fwd_workspace_size(a, &need);
+  if (s) return s;
+  if (!ws || !a16(ws) || ws_bytes < need) return TSA_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  FloydParams p;
+  floyd_carve(a, ws, &p, false);
+  p.out = a->out;
+  p.lse = a->lse;
+  const StageTimer tm = timer_of(a, st);
+  return hip_status(launch_floyd_fwd(p, a->dtype == TSA_FP16, st, tm.ev, tm.n));
+}
+
+int floyd_bwd_workspace_size(const floyd_bwd_args* a, size_t* bytes) {
+  if (!bytes) return TSA_ERR_NULL;
+  int s = check_floyd(a);
+  if (s) return s;
+  if (!a->out || !a->dout || !a->lse || !a->dq || !a->dk1 || !a->dv1 || !a->dk2 || !a->dv2)
+    return TSA_ERR_NULL;
+  if (!a16(a->out) || !a16(a->dout) || !a16(a->dq) || !a16(a->dk1) || !a16(a->dv1) ||
+      !a16(a->dk2) || !a16(a->dv2))
+    return TSA_ERR_INVALID;
+  *bytes = floyd_carve(a, nullptr, nullptr, true);
+  return TSA_OK;
+}
+
+int floyd_bwd(const floyd_bwd_args* a, void* ws, size_t ws_bytes, void* stream) {
+  size_t need;
+  int s = floyd_bwd_workspace_size(a, &need);
+  if (s) return s;
+  if (!ws || !a16(ws) || ws_bytes < need) return TSA_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  FloydParams p;
+  floyd_carve(a, ws, &p, true);
+  p.o = a->out;
+  p.dout = a->dout;
+  p.lse = (float*)a->lse;
+  p.dq = a->dq; p.dk1 = a->dk1; p.dv1 = a->dv1; p.dk2 = a->dk2; p.dv2 = a->dv2;
+  const StageTimer tm = timer_of(a, st);
+  return hip_status(launch_floyd_bwd(p, a->dtype == TSA_FP16, st, tm.ev, tm.n));
 }
 
 // ----- shared-KV two-branch decode -------------------------------------------

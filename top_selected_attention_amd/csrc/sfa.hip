@@ -9,8 +9,9 @@
 // position kv_len - Sq + s); and its task list of per-core (batch, head,
 // Q block, K block) ranges, which here is the split-KV work decomposition.
 //
-// Shared KV: the value row is the key row (value_cache may alias key_cache),
-// so one gathered 1 KB row feeds both the scores and P V.
+// Shared KV: the value row is the key row (value_cache aliases key_cache),
+// so one gathered 1 KB row feeds both the scores and P V.  A separate value
+// cache takes sfa_split_sepv_kernel, which gathers the value rows too.
 //
 // Split kernel: one workgroup per (decode token, split of its selected keys,
 // group of 64 query heads); 8 waves = 2 groups of 32 heads x 4 quarters of
@@ -381,6 +382,210 @@ __global__ __launch_bounds__(512) void sfa_split_kernel(SfaParams p, int n_items
   }
 }
 
+// Split kernel for a separate value cache ("aclnnSparseFlashAttention",
+// constraints section: query, key and value share D = 512; the value rows
+// are gathered beside the key rows).  One workgroup per (decode token, split,
+// group of 64 query heads); 4 waves, each owning 16 heads and the whole
+// 576-dim score contraction (no partial-score exchange).  Per chunk of 32
+// selected slots the key row (1 KB), its rope row (128 B) and the value row
+// (1 KB) are staged by direct loads into a two-stage ring; per wave
+// S^T (32 keys x 16 heads) = K Q^T on 16x16x32 MFMA, online softmax along
+// the keys, O^T (512 x 16) += V^T P^T with V^T read transposed from the
+// value tile.  Same slot table, masks, partials and combine as the shared-KV
+// kernel.
+template <class E>
+__global__ __launch_bounds__(256) void sfa_split_sepv_kernel(SfaParams p, int n_items, int hgroups,
+                                                             int per_split) {
+  typedef typename E::T T;
+  typedef typename E::V8 V8;
+  constexpr int NS = 2;
+  __shared__ __attribute__((aligned(1024))) char lds_k[NS][kMainB];
+  __shared__ __attribute__((aligned(1024))) char lds_v[NS][kMainB];
+  __shared__ __attribute__((aligned(1024))) char lds_r[NS][kRopeB];
+  __shared__ __attribute__((aligned(16))) int lds_tab[kTab];
+  __shared__ unsigned lds_cmask[kTab / kKeys];
+
+  const int item = xcd_remap(blockIdx.x, n_items);
+  if (item < 0) return;
+  const int hg = item % hgroups;
+  const int sp = (item / hgroups) % p.splits;
+  const int tk = item / (hgroups * p.splits);
+  int b, s, sq;
+  sfa_token(p, tk, b, s, sq);
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int kv_len = p.kv_lens[b];
+  const int qpos = kv_len - sq + s;
+  const int total = sfa_total_slots(p);
+  const int slot_lo = sp * per_split;
+  const int slot_hi = min(slot_lo + per_split, total);
+  const int* topk = p.topk + (long)tk * p.topk_n;
+  const int* btab = p.block_table + (long)b * p.max_pages;
+  const float sl2 = p.scale * kLog2e;
+
+  // Q^T as B operands: lane (g, head l16) holds dims 32*ks + 8*g .. +7
+  const int head = hg * 64 + wid * 16 + l16;
+  const bool hok = head < p.N1;
+  V8 qm[16], qr[2];
+  {
+    const T* qrow = (const T*)p.q + ((long)tk * p.N1 + (hok ? head : 0)) * kDv;
+    const T* qrr = (const T*)p.q_rope + ((long)tk * p.N1 + (hok ? head : 0)) * kDr;
+#pragma unroll
+    for (int ks = 0; ks < 16; ks++)
+      qm[ks] = hok ? as_v8<V8>(ld16(qrow + 32 * ks + 8 * g)) : zero_v8<V8>();
+#pragma unroll
+    for (int ks = 0; ks < 2; ks++)
+      qr[ks] = hok ? as_v8<V8>(ld16(qrr + 32 * ks + 8 * g)) : zero_v8<V8>();
+  }
+
+  // physical rows of a run of slots and per-chunk masks (bit r = key r kept);
+  // a dropped slot holds its chunk's first kept row, or row 0 when none
+  auto fill_table = [&](int seg_lo, int seg_n) {
+#pragma unroll
+    for (int i = 0; i < kTab / 256; i++) {
+      const int t = tid + 256 * i;
+      const int gs = seg_lo + t;
+      const int id = t < seg_n ? topk[gs / p.sbs] : -1;
+      const bool idok = id >= 0 && id <= (kv_len - 1) / p.sbs;
+      const int pos = idok ? id * p.sbs + gs % p.sbs : 0;
+      const bool ok = t < seg_n && idok && pos < kv_len && (!p.causal || pos <= qpos);
+      const int lp = ok ? min(pos / p.page, p.max_pages - 1) : 0;
+      const int phys = ok ? btab[lp] : 0;
+      const int row = ok ? min(max(phys, 0), p.num_pages - 1) * p.page + pos % p.page : 0;
+      const unsigned long long bal = __ballot(ok);
+      const unsigned half = lane < 32 ? (unsigned)bal : (unsigned)(bal >> 32);
+      const int first = (half ? __builtin_ctz(half) : 0) + (lane & 32);
+      const int frow = __shfl(row, first);
+      lds_tab[t] = ok ? row : (half ? frow : 0);
+      if ((lane & 31) == 0) lds_cmask[t >> 5] = half;
+    }
+  };
+  // 4 waves x 8 key rows and 8 value rows (one 1-KB row per instruction),
+  // and one 1-KB slice of 8 rope rows per wave
+  auto load_chunk = [&](int c, int buf) {
+    const int* tb = lds_tab + c * kKeys;
+#pragma unroll
+    for (int u = 0; u < 8; u++) {
+      const int r = wid * 8 + u;
+      const long row = tb[r];
+      g2lds16((const char*)p.kc + row * (kDv * 2) + ((lane ^ swz1k(r)) << 4), lds_k[buf] + r * 1024);
+      g2lds16((const char*)p.vc + row * (kDv * 2) + ((lane ^ swz1k(r)) << 4), lds_v[buf] + r * 1024);
+    }
+    const int r = wid * 8 + (lane >> 3);
+    g2lds16((const char*)p.krc + (long)tb[r] * (kDr * 2) + (((lane & 7) ^ swzr(r)) << 4),
+            lds_r[buf] + wid * 1024);
+  };
+
+  constexpr float kLazy = 8.f;
+  float m = -INFINITY, lsum = 0.f;
+  f32x4_t o[32];  // O^T tiles: rows d = 16*dt + 4*g + j, column head l16
+#pragma unroll
+  for (int dt = 0; dt < 32; dt++) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (int seg_lo = slot_lo; seg_lo < slot_hi; seg_lo += kTab) {
+    const int seg_n = min(kTab, slot_hi - seg_lo);
+    const int nchunks = (seg_n + kKeys - 1) / kKeys;
+    __syncthreads();  // the previous run's table and tiles are no longer read
+    fill_table(seg_lo, seg_n);
+    __syncthreads();
+    load_chunk(0, 0);
+    wait_vm();
+    __syncthreads();
+    int buf = 0;
+    for (int c = 0; c < nchunks; c++) {
+      if (c + 1 < nchunks) load_chunk(c + 1, buf ^ 1);
+      const unsigned mcur = __builtin_amdgcn_readfirstlane(lds_cmask[c]);
+      if (mcur) {
+        const char* Kt = lds_k[buf];
+        const char* Vt = lds_v[buf];
+        const char* Rt = lds_r[buf];
+        // element j of st[kt] is key 16*kt + 4*g + j, head l16
+        f32x4_t st[2];
+#pragma unroll
+        for (int kt = 0; kt < 2; kt++) {
+          const int r = kt * 16 + l16;
+          st[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < 16; ks++) {
+            const int c16 = 4 * ks + g;
+            st[kt] = E::mfma16(lds_read16<V8>(Kt + r * 1024 + ((c16 ^ swz1k(r)) << 4)), qm[ks], st[kt]);
+          }
+#pragma unroll
+          for (int ks = 0; ks < 2; ks++)
+            st[kt] = E::mfma16(lds_read16<V8>(Rt + r * 128 + (((4 * ks + g) ^ swzr(r)) << 4)),
+                               qr[ks], st[kt]);
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < 2; kt++)
+#pragma unroll
+          for (int j = 0; j < 4; j++) {
+            const int key = kt * 16 + 4 * g + j;
+            const float v = ((mcur >> key) & 1u) ? st[kt][j] : -INFINITY;
+            st[kt][j] = v;
+            mx = fmaxf(mx, v);
+          }
+        mx = max_xor16_32(mx) * sl2;
+        if (__builtin_amdgcn_ballot_w64(mx > m + kLazy)) {
+          const float m_new = fmaxf(m, mx);
+          const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m - m_new);
+          m = m_new;
+          lsum *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < 32; dt++) o[dt] *= alpha;
+        }
+        const float mneg = m == -INFINITY ? 0.f : -m;
+        V8 pb;
+#pragma unroll
+        for (int kt = 0; kt < 2; kt++)
+#pragma unroll
+          for (int j = 0; j < 4; j++) {
+            const float pv = fast_exp2(__builtin_fmaf(st[kt][j], sl2, mneg));
+            lsum += pv;
+            pb[4 * kt + j] = E::from_f32(pv);
+          }
+        // O^T += V^T P^T: V^T rows d = 16*dt + l16, keys {4g..4g+3, 16+4g..16+4g+3}
+        const int r0 = 4 * g + (l16 >> 2), r1 = r0 + 16;
+        const int cq = l16 & 3;
+#pragma unroll
+        for (int dt = 0; dt < 32; dt++) {
+          const int c16 = 2 * dt + (cq >> 1);
+          const int b8 = 8 * (cq & 1);
+          const V8 a = lds_read_tr_pair<V8>(Vt + r0 * 1024 + ((c16 ^ swz1k(r0)) << 4) + b8,
+                                            Vt + r1 * 1024 + ((c16 ^ swz1k(r1)) << 4) + b8);
+          o[dt] = E::mfma16(a, pb, o[dt]);
+        }
+      }
+      wait_vm();
+      __syncthreads();
+      buf ^= 1;
+    }
+  }
+
+  float lt = lsum + __shfl_xor(lsum, 16);
+  lt += __shfl_xor(lt, 32);
+  if (!hok) return;
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  // element j of o[dt] is d = 16*dt + 4*g + j
+  if (p.splits == 1) {
+    T* orow = (T*)p.out + ((long)tk * p.N1 + head) * kDv;
+#pragma unroll
+    for (int dt = 0; dt < 32; dt++)
+      *reinterpret_cast<uint2*>(orow + 16 * dt + 4 * g) =
+          pack4<E>(o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv);
+    if (g == 0 && p.lse)
+      p.lse[(long)tk * p.N1 + head] = lt > 0.f ? (m + log2f(lt)) * kLn2 : -INFINITY;
+  } else {
+    const long pr = ((long)tk * p.splits + sp) * p.N1 + head;
+    float* po = p.part_o + pr * kDv;
+#pragma unroll
+    for (int dt = 0; dt < 32; dt++)
+      *reinterpret_cast<float4*>(po + 16 * dt + 4 * g) =
+          make_float4(o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv);
+    if (g == 0) p.part_lse[pr] = lt > 0.f ? m + log2f(lt) : -INFINITY;
+  }
+}
+
 // One wave per (token, head): merges the splits' partials.
 template <class E>
 __global__ __launch_bounds__(256) void sfa_combine_kernel(SfaParams p) {
@@ -480,8 +685,13 @@ static hipError_t sfa_t(const SfaParams& p, hipStream_t st, void* const* ev, int
   const long n_items = tokens * p.splits * hgroups;
   hipError_t e = mark_event(ev, n_ev, 0, 0, st);
   if (e == hipSuccess) {
-    hipLaunchKernelGGL((sfa_split_kernel<E>), dim3((unsigned)(8 * ((n_items + 7) / 8))), dim3(512),
-                       0, st, p, (int)n_items, hgroups, per_split);
+    // a value cache apart from the key cache: its own gather (plain SFA only)
+    if (p.vc != p.kc && p.ckc == nullptr)
+      hipLaunchKernelGGL((sfa_split_sepv_kernel<E>), dim3((unsigned)(8 * ((n_items + 7) / 8))),
+                         dim3(256), 0, st, p, (int)n_items, hgroups, per_split);
+    else
+      hipLaunchKernelGGL((sfa_split_kernel<E>), dim3((unsigned)(8 * ((n_items + 7) / 8))),
+                         dim3(512), 0, st, p, (int)n_items, hgroups, per_split);
     e = hipGetLastError();
   }
   if (e == hipSuccess) e = mark_event(ev, n_ev, 0, 1, st);

@@ -234,4 +234,53 @@ hipError_t launch_sfa_fwd(const SfaParams& p, int fp16, hipStream_t st, void* co
 hipError_t launch_sfa_check(const SfaParams& p, hipStream_t st);
 hipError_t launch_fill_i32(int* p, int n, int v, hipStream_t st);
 
+// ----- FloydAttention --------------------------------------------------------
+
+// One strided, two-level-batched GEMM: C(z1, z2, r, c) = alpha * sum_l
+// A(z1, z2, r, l) B(z1, z2, l, c); strides in elements.
+struct FloydGemm {
+  const void* a;
+  const void* b;
+  void* c;
+  void* c16;  // 16-bit destination of the accumulate-and-convert mode
+  long a_s1, a_s2, a_sr, a_sl;
+  long b_s1, b_s2, b_sl, b_sc;
+  long c_s1, c_s2, c_sr, c_sc;
+  int Z1, Z2, R, Cn, L;
+  float alpha;
+};
+
+struct FloydParams {
+  const void* q;      // [Z, N, M, D]
+  const void* k1;     // [Z, N, K, D]
+  const void* v1;
+  const void* k2;     // [Z, M, K, D]
+  const void* v2;
+  const void* o;      // backward: the forward output
+  const void* dout;   // backward: its gradient
+  void* out;          // forward output
+  float* lse;         // [Z, N, M]
+  void* dq;
+  void* dk1;
+  void* dv1;
+  void* dk2;
+  void* dv2;
+  // workspace
+  float* s;           // scores [Z, N, M, K]
+  float* dp;          // backward: dP [Z, N, M, K]
+  float* acc;         // fp32 accumulator [Z, N, M, D]
+  void* p;            // P [Z, N, M, K], 16-bit
+  void* ds;           // backward: dS [Z, N, M, K], 16-bit
+  int Z, N, M, K, D;
+  float scale;
+};
+
+// forward stages: 0 = scores, 1 = softmax, 2 = P V1 + P V2
+hipError_t launch_floyd_fwd(const FloydParams& p, int fp16, hipStream_t st, void* const* ev,
+                            int n_ev);
+// backward stages: 0 = scores and dP, 1 = P and dS, 2 = dV1 / dV2, 3 = dQ,
+// 4 = dK1 / dK2
+hipError_t launch_floyd_bwd(const FloydParams& p, int fp16, hipStream_t st, void* const* ev,
+                            int n_ev);
+
 }  // namespace tsa

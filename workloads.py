@@ -294,3 +294,29 @@ def sfa_inputs(B=32, Sq=4, N1=64, D=512, Dr=64, page=128, kv_len=65536, topk=204
     kc = normal((P, page, 1, D), seed_base + 3, dtype)
     krc = normal((P, page, 1, Dr), seed_base + 4, dtype)
     return q, q_rope, kc, krc, block_table, kv_lens, idx
+
+
+# ----------------------------------------------------------------------------
+# FloydAttention
+# ----------------------------------------------------------------------------
+
+def floyd_workload():
+    """Pair-representation sized FloydAttention: 256 x 256 query rows per head
+    over 256 keys, 8 heads of 64 dims."""
+    return dict(name="floyd_256", B=1, H=8, N=256, M=256, K=256, D=64, dtype="bf16")
+
+
+def floyd_inputs(B=None, H=None, N=None, M=None, K=None, D=None, seed_base=140, dtype=None):
+    """(q [B,H,N,M,D], k1 [B,H,N,K,D], v1, k2 [B,H,M,K,D], v2, dout [B,H,N,M,D]):
+    standard normals rounded to the working dtype; defaults from floyd_workload()."""
+    w = floyd_workload()
+    B, H, N, M, K, D = (w[k] if v is None else v for k, v in
+                        (("B", B), ("H", H), ("N", N), ("M", M), ("K", K), ("D", D)))
+    dtype = w["dtype"] if dtype is None else dtype
+    q = normal((B, H, N, M, D), seed_base + 1, dtype)
+    k1 = normal((B, H, N, K, D), seed_base + 2, dtype)
+    v1 = normal((B, H, N, K, D), seed_base + 3, dtype)
+    k2 = normal((B, H, M, K, D), seed_base + 4, dtype)
+    v2 = normal((B, H, M, K, D), seed_base + 5, dtype)
+    do = normal((B, H, N, M, D), seed_base + 6, dtype)
+    return q, k1, v1, k2, v2, do
