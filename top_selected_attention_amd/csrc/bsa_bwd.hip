@@ -117,11 +117,49 @@ __global__ __launch_bounds__(NW * 64) void bsa_dq_kernel(BsaParams p, int qsub, 
     }
     return c;
   };
+  // A whole chunk takes a scalar base (its first key row) plus per-lane
+  // offsets fixed for the walk; a ragged chunk clamps its rows lane by lane.
+  constexpr int NU = 16 / NW;  // 1-KB slices (4 rows) per wave and tile
+  unsigned goff[NU];
+  {
+    const int sub = lane >> 4, pc = lane & 15;
+#pragma unroll
+    for (int u = 0; u < NU; u++) {
+      const int r = (wid * NU + u) * 4 + sub;
+      goff[u] = (unsigned)(r * krow_bytes) + (unsigned)((pc ^ swz(r)) << 4);
+    }
+  }
   auto load_chunk = [&](int ks, int ke, int buf) {
-    auto row_of = [&](int r) { return min(ks + r, ke - 1); };
-    stage_tile64<NW>((const char*)kh, krow_bytes, lds_k[buf], row_of);
-    stage_tile64<NW>((const char*)vh, krow_bytes, lds_v[buf], row_of);
+    if (ke - ks == 64) {
+      const char* kb = (const char*)kh + (long)ks * krow_bytes;
+      const char* vb = (const char*)vh + (long)ks * krow_bytes;
+#pragma unroll
+      for (int u = 0; u < NU; u++) g2lds16_so(kb, goff[u], lds_k[buf] + (wid * NU + u) * 1024);
+#pragma unroll
+      for (int u = 0; u < NU; u++) g2lds16_so(vb, goff[u], lds_v[buf] + (wid * NU + u) * 1024);
+    } else {
+      auto row_of = [&](int r) { return min(ks + r, ke - 1); };
+      stage_tile64<NW>((const char*)kh, krow_bytes, lds_k[buf], row_of);
+      stage_tile64<NW>((const char*)vh, krow_bytes, lds_v[buf], row_of);
+    }
   };
+  // per-lane LDS byte offsets of the MFMA operands (see the forward): rows
+  // l32 (+32 per key tile), pieces 2*ds + h; K^T by transpose reads
+  unsigned kro[8], ktr[4][2];
+  {
+    const int i16 = lane & 15, g16 = lane >> 4;
+#pragma unroll
+    for (int ds = 0; ds < 8; ds++)
+      kro[ds] = (unsigned)(l32 * 256 + (((2 * ds + h) ^ swz(l32)) << 4));
+    const int r0 = 4 * h + (i16 >> 2), r1 = r0 + 8;
+    const int b8 = 8 * (i16 & 1);
+#pragma unroll
+    for (int dt = 0; dt < 4; dt++) {
+      const int c = 4 * dt + 2 * (g16 & 1) + ((i16 & 3) >> 1);
+      ktr[dt][0] = (unsigned)(r0 * 256 + ((c ^ swz(r0)) << 4) + b8);
+      ktr[dt][1] = (unsigned)(r1 * 256 + ((c ^ swz(r1)) << 4) + b8);
+    }
+  }
 
   f32x16 dq[4];
 #pragma unroll
@@ -165,8 +203,8 @@ __global__ __launch_bounds__(NW * 64) void bsa_dq_kernel(BsaParams p, int qsub, 
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int ds = 0; ds < 8; ds++) {
-        st = E::mfma32(tile_read16<V8>(Kb, kt * 32 + l32, 2 * ds + h), qreg[ds], st);
-        dpt = E::mfma32(tile_read16<V8>(Vb, kt * 32 + l32, 2 * ds + h), doreg[ds], dpt);
+        st = E::mfma32(lds_read16<V8>(Kb + kt * 32 * 256 + kro[ds]), qreg[ds], st);
+        dpt = E::mfma32(lds_read16<V8>(Vb + kt * 32 * 256 + kro[ds]), doreg[ds], dpt);
       }
       __builtin_amdgcn_s_setprio(0);
       // dS^T = P^T * (dP^T - D), P^T = exp2(S^T * scale*log2e - LSE2);
@@ -198,7 +236,9 @@ __global__ __launch_bounds__(NW * 64) void bsa_dq_kernel(BsaParams p, int qsub, 
       for (int k2 = 0; k2 < 2; k2++)
 #pragma unroll
         for (int dt = 0; dt < 4; dt++)
-          dq[dt] = E::mfma32(tile_read_tr<V8>(Kb, kt * 2 + k2, dt), bs[k2], dq[dt]);
+          dq[dt] = E::mfma32(lds_read_tr_pair<V8>(Kb + (kt * 2 + k2) * 16 * 256 + ktr[dt][0],
+                                                  Kb + (kt * 2 + k2) * 16 * 256 + ktr[dt][1]),
+                             bs[k2], dq[dt]);
       __builtin_amdgcn_s_setprio(0);
     }
     wait_vm();
@@ -329,23 +369,42 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     }
     return c;
   };
-  // 32 rows of Q and of dO (8 KB each) plus their LSE / softmax_grad
+  // 32 rows of Q and of dO (8 KB each) plus their LSE / softmax_grad.  A
+  // whole chunk takes a scalar base (its first row) plus per-lane offsets
+  // fixed for the walk; a ragged chunk clamps its rows lane by lane.
+  constexpr int NU = 8 / NW;  // 1-KB slices (4 rows) per wave and tile
+  unsigned goff[NU];
+  {
+    const int sub = lane >> 4, pc = lane & 15;
+#pragma unroll
+    for (int u = 0; u < NU; u++) {
+      const int r = (wid * NU + u) * 4 + sub;
+      goff[u] = (unsigned)(r * qm.row * 2) + (unsigned)((pc ^ swz(r)) << 4);
+    }
+  }
   auto load_chunk = [&](int n1, int qs, int qe, int buf) {
     const long qoff = qm.at(n1, 0), soff = sm.at(n1, 0);
-    // The per-lane address terms are rebuilt here from an opaque copy of the
-    // lane id: hoisted out of the loop they would be spilled, and a scratch
-    // reload between two direct loads waits for the first to land.
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-    const int sub = ln >> 4, pc = ln & 15;
+    const int ln = lane;
+    if (qe - qs == kQC) {
+      const char* qb = (const char*)((const T*)p.q + qoff + (long)qs * qm.row);
+      const char* db = (const char*)((const T*)p.dout + qoff + (long)qs * qm.row);
 #pragma unroll
-    for (int u = 0; u < 8 / NW; u++) {
-      const int inst = wid * (8 / NW) + u;
-      const int r = inst * 4 + sub;
-      const long row = qoff + (long)min(qs + r, qe - 1) * qm.row;
-      g2lds16((const char*)((const T*)p.q + row) + ((pc ^ swz(r)) << 4), lds_q[buf] + inst * 1024);
-      g2lds16((const char*)((const T*)p.dout + row) + ((pc ^ swz(r)) << 4),
-              lds_do[buf] + inst * 1024);
+      for (int u = 0; u < NU; u++) {
+        g2lds16_so(qb, goff[u], lds_q[buf] + (wid * NU + u) * 1024);
+        g2lds16_so(db, goff[u], lds_do[buf] + (wid * NU + u) * 1024);
+      }
+    } else {
+      const int sub = ln >> 4, pc = ln & 15;
+#pragma unroll
+      for (int u = 0; u < NU; u++) {
+        const int inst = wid * NU + u;
+        const int r = inst * 4 + sub;
+        const long row = qoff + (long)min(qs + r, qe - 1) * qm.row;
+        g2lds16((const char*)((const T*)p.q + row) + ((pc ^ swz(r)) << 4),
+                lds_q[buf] + inst * 1024);
+        g2lds16((const char*)((const T*)p.dout + row) + ((pc ^ swz(r)) << 4),
+                lds_do[buf] + inst * 1024);
+      }
     }
     if (wid == 0) {
       // a direct LDS load writes lane l's dword at base + 4*l for all 64
@@ -355,6 +414,26 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
       g2lds4(p.delta + r, lds_dlt[buf]);
     }
   };
+
+  // per-lane LDS byte offsets of the MFMA operands: rows l32 (Q, dO; the
+  // wave's K rows 32*wid + l32 share the swizzle), pieces 2*ds + h; dO^T and
+  // Q^T by transpose reads
+  unsigned kro[8], ktr[4][2];
+  {
+    const int i16 = lane & 15, g16 = lane >> 4;
+#pragma unroll
+    for (int ds = 0; ds < 8; ds++)
+      kro[ds] = (unsigned)(l32 * 256 + (((2 * ds + h) ^ swz(l32)) << 4));
+    const int r0 = 4 * h + (i16 >> 2), r1 = r0 + 8;
+    const int b8 = 8 * (i16 & 1);
+#pragma unroll
+    for (int dt = 0; dt < 4; dt++) {
+      const int c = 4 * dt + 2 * (g16 & 1) + ((i16 & 3) >> 1);
+      ktr[dt][0] = (unsigned)(r0 * 256 + ((c ^ swz(r0)) << 4) + b8);
+      ktr[dt][1] = (unsigned)(r1 * 256 + ((c ^ swz(r1)) << 4) + b8);
+    }
+  }
+  const char* Kw = lds_k + wid * 32 * 256;
 
   f32x16 dvt[4], dkt[4];
 #pragma unroll
@@ -397,9 +476,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     for (int j = 0; j < 16; j++) s[j] = dp[j] = 0.f;
 #pragma unroll
     for (int ds = 0; ds < 8; ds++) {
-      s = E::mfma32(tile_read16<V8>(Qb, l32i, 2 * ds + hi),
-                    tile_read16<V8>(lds_k, wid * 32 + l32i, 2 * ds + hi), s);
-      dp = E::mfma32(tile_read16<V8>(Db, l32i, 2 * ds + hi), vreg[ds], dp);
+      s = E::mfma32(lds_read16<V8>(Qb + kro[ds]), lds_read16<V8>(Kw + kro[ds]), s);
+      dp = E::mfma32(lds_read16<V8>(Db + kro[ds]), vreg[ds], dp);
     }
     // three LDS reads feed two MFMAs per step
     __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
@@ -457,8 +535,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     for (int k2 = 0; k2 < 2; k2++)
 #pragma unroll
       for (int dt = 0; dt < 4; dt++) {
-        dvt[dt] = E::mfma32(tile_read_tr<V8>(Db, k2, dt, ln), bp[k2], dvt[dt]);
-        dkt[dt] = E::mfma32(tile_read_tr<V8>(Qb, k2, dt, ln), bd[k2], dkt[dt]);
+        dvt[dt] = E::mfma32(lds_read_tr_pair<V8>(Db + k2 * 16 * 256 + ktr[dt][0],
+                                                 Db + k2 * 16 * 256 + ktr[dt][1]),
+                            bp[k2], dvt[dt]);
+        dkt[dt] = E::mfma32(lds_read_tr_pair<V8>(Qb + k2 * 16 * 256 + ktr[dt][0],
+                                                 Qb + k2 * 16 * 256 + ktr[dt][1]),
+                            bd[k2], dkt[dt]);
       }
     sched_mfma_lds<16, 2, 4>();
     __builtin_amdgcn_s_setprio(0);

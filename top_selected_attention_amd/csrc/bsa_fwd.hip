@@ -15,6 +15,8 @@
 // exchange with lane l^32.  P^T leaves the accumulator directly as the B
 // operand of O^T += V^T P^T, with V^T read from the natural-layout V tile by
 // LDS transpose reads (ds_read_b64_tr_b16).
+#include <type_traits>
+
 #include "tsa_device.h"
 #include "tsa_internal.h"
 
@@ -99,12 +101,51 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_kernel(BsaParams p, int qsub,
   };
   // Direct global -> LDS loads (no registers) into the swizzled layout.  Keys
   // past the chunk's end re-read its last key (finite data; their scores are
-  // masked, so P = 0 exactly there).
-  auto load_chunk = [&](int ks, int ke, int buf) {
-    auto row_of = [&](int r) { return min(ks + r, ke - 1); };
-    stage_tile64<NW>((const char*)kh, krow_bytes, lds_k[buf], row_of);
-    stage_tile64<NW>((const char*)vh, krow_bytes, lds_v[buf], row_of);
+  // masked, so P = 0 exactly there).  A whole chunk takes a scalar base (its
+  // first key row) plus per-lane offsets fixed for the walk; a ragged chunk
+  // clamps its rows lane by lane.
+  constexpr int NU = 16 / NW;  // 1-KB slices (4 rows) per wave and tile
+  const int sub = lane >> 4, pc = lane & 15;
+  unsigned goff[NU];
+#pragma unroll
+  for (int u = 0; u < NU; u++) {
+    const int r = (wid * NU + u) * 4 + sub;
+    goff[u] = (unsigned)(r * krow_bytes) + (unsigned)((pc ^ swz(r)) << 4);
+  }
+  auto load_chunk = [&](int ks, int ke, char* kt, char* vt) {
+    if (ke - ks == kKC) {
+      const char* kb = (const char*)kh + (long)ks * krow_bytes;
+      const char* vb = (const char*)vh + (long)ks * krow_bytes;
+#pragma unroll
+      for (int u = 0; u < NU; u++) g2lds16_so(kb, goff[u], kt + (wid * NU + u) * 1024);
+#pragma unroll
+      for (int u = 0; u < NU; u++) g2lds16_so(vb, goff[u], vt + (wid * NU + u) * 1024);
+    } else {
+      auto row_of = [&](int r) { return min(ks + r, ke - 1); };
+      stage_tile64<NW>((const char*)kh, krow_bytes, kt, row_of);
+      stage_tile64<NW>((const char*)vh, krow_bytes, vt, row_of);
+    }
   };
+  // Per-lane LDS byte offsets of the MFMA operands, fixed for the walk (the
+  // tiles' bases and the 32-row / 16-row steps are compile-time immediates):
+  // K rows l32 (and 32 + l32: the same swizzle), pieces 2*ds + h; V^T by
+  // transpose reads, rows 4h + i16/4 (+8) of each 16-key step, the 16-byte
+  // piece of dims 32*dt + ...
+  unsigned kro[8], vtr[4][2];
+  {
+    const int i16 = lane & 15, g16 = lane >> 4;
+#pragma unroll
+    for (int ds = 0; ds < 8; ds++)
+      kro[ds] = (unsigned)(l32 * 256 + (((2 * ds + h) ^ swz(l32)) << 4));
+    const int r0 = 4 * h + (i16 >> 2), r1 = r0 + 8;
+    const int b8 = 8 * (i16 & 1);
+#pragma unroll
+    for (int dt = 0; dt < 4; dt++) {
+      const int c = 4 * dt + 2 * (g16 & 1) + ((i16 & 3) >> 1);
+      vtr[dt][0] = (unsigned)(r0 * 256 + ((c ^ swz(r0)) << 4) + b8);
+      vtr[dt][1] = (unsigned)(r1 * 256 + ((c ^ swz(r1)) << 4) + b8);
+    }
+  }
 
   // Online softmax state of this lane's query, base 2.  The reference m only
   // moves when a chunk's max exceeds it by more than kLazy (so P <= 2^kLazy);
@@ -121,7 +162,7 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_kernel(BsaParams p, int qsub,
   if (i.e < e1) {
     int ks, ke;
     chunk_range(i, ks, ke);
-    load_chunk(ks, ke, 0);
+    load_chunk(ks, ke, lds_k[0], lds_v[0]);
   }
   wait_vm();
   __syncthreads();
@@ -133,7 +174,7 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_kernel(BsaParams p, int qsub,
     if (inext.e < e1) {
       int ks2, ke2;
       chunk_range(inext, ks2, ke2);
-      load_chunk(ks2, ke2, buf ^ 1);
+      load_chunk(ks2, ke2, lds_k[buf ^ 1], lds_v[buf ^ 1]);
     }
     const char* Kb = lds_k[buf];
     const char* Vb = lds_v[buf];
@@ -146,8 +187,8 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_kernel(BsaParams p, int qsub,
       for (int j = 0; j < 16; j++) st[kt][j] = 0.f;
 #pragma unroll
     for (int ds = 0; ds < 8; ds++) {
-      st[0] = E::mfma32(tile_read16<V8>(Kb, l32, 2 * ds + h), qreg[ds], st[0]);
-      st[1] = E::mfma32(tile_read16<V8>(Kb, 32 + l32, 2 * ds + h), qreg[ds], st[1]);
+      st[0] = E::mfma32(lds_read16<V8>(Kb + kro[ds]), qreg[ds], st[0]);
+      st[1] = E::mfma32(lds_read16<V8>(Kb + 32 * 256 + kro[ds]), qreg[ds], st[1]);
     }
     sched_mfma_lds<16, 1, 4>();
     // Element j of tile kt is key ks + kt*32 + 8*(j/4) + 4*h + j%4.  A chunk
@@ -199,7 +240,9 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_kernel(BsaParams p, int qsub,
     for (int k4 = 0; k4 < 4; k4++)
 #pragma unroll
       for (int dt = 0; dt < 4; dt++)
-        o[dt] = E::mfma32(tile_read_tr<V8>(Vb, k4, dt), pb[k4], o[dt]);
+        o[dt] = E::mfma32(lds_read_tr_pair<V8>(Vb + k4 * 16 * 256 + vtr[dt][0],
+                                               Vb + k4 * 16 * 256 + vtr[dt][1]),
+                          pb[k4], o[dt]);
     sched_mfma_lds<16, 2, 4>();
 
     wait_vm();

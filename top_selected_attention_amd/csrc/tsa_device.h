@@ -164,6 +164,25 @@ __device__ __forceinline__ void g2lds16(const void* g, void* lds_base) {
       : "v"(g), "s"(l)
       : "memory");
 }
+// The same copy from a wave-uniform base plus a per-lane 32-bit byte offset
+// (the scalar-base form: the per-lane address needs no 64-bit arithmetic).
+__device__ __forceinline__ void g2lds16_so(const void* sbase, unsigned voff, void* lds_base) {
+  const unsigned l = __builtin_amdgcn_readfirstlane(
+      (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)lds_base);
+  // readfirstlane yields a signed int: each half goes back to unsigned
+  // before widening, or a low word with bit 31 set would fill the high word
+  const unsigned long long b = (unsigned long long)(uintptr_t)sbase;
+  const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)b);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)(b >> 32));
+  const unsigned long long sb = ((unsigned long long)hi << 32) | lo;
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0\n\ts_nop 0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(sb), "s"(l)
+      : "memory");
+}
 // Same with 4 bytes per lane (lane l's dword lands at lds_base + 4*l).
 __device__ __forceinline__ void g2lds4(const void* g, void* lds_base) {
   const unsigned l = __builtin_amdgcn_readfirstlane(
