@@ -14,7 +14,7 @@
 //     selected the KV block (the reverse CSR), over all query heads of the
 //     KV head's group.
 // Both stage their streamed operand (K/V resp. Q/dO) in 64-row chunks through
-// double-buffered, swizzled LDS with direct global -> LDS loads, keep the
+// double-buffered, padded LDS tiles with direct global -> LDS loads, keep the
 // stationary operand in registers, and feed accumulator tiles straight back
 // into the next MFMA as operands (see tsa_device.h).
 #include <type_traits>
@@ -28,7 +28,7 @@ namespace tsa {
 
 namespace {
 constexpr int kD = 128;
-constexpr int kTileB = 64 * kD * 2;  // one 64-row chunk of a [rows][128] 16-bit tensor
+constexpr int kTileB = ptile_bytes(64);  // one padded 64-row chunk of a [rows][128] 16-bit tensor
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -42,8 +42,7 @@ __global__ __launch_bounds__(NW * 64) void bsa_dq_kernel(BsaParams p, int qsub, 
   typedef typename E::T T;
   typedef typename E::V8 V8;
   constexpr int NR = NW * 32;
-  __shared__ __attribute__((aligned(1024))) char lds_k[2][kTileB];
-  __shared__ __attribute__((aligned(1024))) char lds_v[2][kTileB];
+  __shared__ __attribute__((aligned(1024))) char lds_kv[2][2][kTileB];  // [stage][K, V]
 
   const int item = blockIdx.x;
   if (item >= n_items) return;
@@ -61,7 +60,8 @@ __global__ __launch_bounds__(NW * 64) void bsa_dq_kernel(BsaParams p, int qsub, 
   const int row_hi = min((qb + 1) * p.bq, qm.len);
   if (row_lo >= row_hi) return;
 
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6) & (NW - 1);  // wave-uniform
   const int l32 = lane & 31, h = lane >> 5;
   const int wrow0 = row_lo + wid * 32;
   const int qrow = wrow0 + l32;
@@ -117,49 +117,27 @@ __global__ __launch_bounds__(NW * 64) void bsa_dq_kernel(BsaParams p, int qsub, 
     }
     return c;
   };
-  // A whole chunk takes a scalar base (its first key row) plus per-lane
-  // offsets fixed for the walk; a ragged chunk clamps its rows lane by lane.
-  constexpr int NU = 16 / NW;  // 1-KB slices (4 rows) per wave and tile
-  unsigned goff[NU];
-  {
-    const int sub = lane >> 4, pc = lane & 15;
-#pragma unroll
-    for (int u = 0; u < NU; u++) {
-      const int r = (wid * NU + u) * 4 + sub;
-      goff[u] = (unsigned)(r * krow_bytes) + (unsigned)((pc ^ swz(r)) << 4);
-    }
-  }
+  // Padded K/V tiles by direct loads; a whole chunk takes a scalar base (its
+  // first key row) plus per-lane offsets fixed for the walk, a ragged chunk
+  // re-reads its last key.
+  PStage<NW, 64> stg;
+  stg.init(wid, lane, krow_bytes);
+  const unsigned lds0 = lds_addr(&lds_kv[0][0][0]);
   auto load_chunk = [&](int ks, int ke, int buf) {
+    const unsigned lk = lds0 + buf * 2 * kTileB, lv = lk + kTileB;
+    const char* kb = (const char*)kh + (long)ks * krow_bytes;
+    const char* vb = (const char*)vh + (long)ks * krow_bytes;
     if (ke - ks == 64) {
-      const char* kb = (const char*)kh + (long)ks * krow_bytes;
-      const char* vb = (const char*)vh + (long)ks * krow_bytes;
-#pragma unroll
-      for (int u = 0; u < NU; u++) g2lds16_so(kb, goff[u], lds_k[buf] + (wid * NU + u) * 1024);
-#pragma unroll
-      for (int u = 0; u < NU; u++) g2lds16_so(vb, goff[u], lds_v[buf] + (wid * NU + u) * 1024);
+      stg.full(kb, lk, wid, lane);
+      stg.full(vb, lv, wid, lane);
     } else {
-      auto row_of = [&](int r) { return min(ks + r, ke - 1); };
-      stage_tile64<NW>((const char*)kh, krow_bytes, lds_k[buf], row_of);
-      stage_tile64<NW>((const char*)vh, krow_bytes, lds_v[buf], row_of);
+      stg.ragged(kb, krow_bytes, ke - 1 - ks, lk, wid, lane);
+      stg.ragged(vb, krow_bytes, ke - 1 - ks, lv, wid, lane);
     }
   };
-  // per-lane LDS byte offsets of the MFMA operands (see the forward): rows
-  // l32 (+32 per key tile), pieces 2*ds + h; K^T by transpose reads
-  unsigned kro[8], ktr[4][2];
-  {
-    const int i16 = lane & 15, g16 = lane >> 4;
-#pragma unroll
-    for (int ds = 0; ds < 8; ds++)
-      kro[ds] = (unsigned)(l32 * 256 + (((2 * ds + h) ^ swz(l32)) << 4));
-    const int r0 = 4 * h + (i16 >> 2), r1 = r0 + 8;
-    const int b8 = 8 * (i16 & 1);
-#pragma unroll
-    for (int dt = 0; dt < 4; dt++) {
-      const int c = 4 * dt + 2 * (g16 & 1) + ((i16 & 3) >> 1);
-      ktr[dt][0] = (unsigned)(r0 * 256 + ((c ^ swz(r0)) << 4) + b8);
-      ktr[dt][1] = (unsigned)(r1 * 256 + ((c ^ swz(r1)) << 4) + b8);
-    }
-  }
+  // per-lane bases of the operand reads: K and V rows (key l32, +32 per key
+  // tile), K^T by transpose reads
+  const unsigned rb = prow_base(lane), tb = ptr_base(lane);
 
   f32x16 dq[4];
 #pragma unroll
@@ -186,8 +164,9 @@ __global__ __launch_bounds__(NW * 64) void bsa_dq_kernel(BsaParams p, int qsub, 
       chunk_range(inext, ks2, ke2);
       load_chunk(ks2, ke2, buf ^ 1);
     }
-    const char* Kb = lds_k[buf];
-    const char* Vb = lds_v[buf];
+    const char* Kr = &lds_kv[buf][0][0] + rb;
+    const char* Vr = &lds_kv[buf][1][0] + rb;
+    const char* Kt = &lds_kv[buf][0][0] + tb;
     const bool full =
         !AM && (ke - ks == 64) && wrow0 + 32 <= row_hi && (!p.causal || ke - 1 <= wrow0);
     // atten_mask keep bits of this lane's row: bit 16*kt + j for element j of tile kt
@@ -203,8 +182,8 @@ __global__ __launch_bounds__(NW * 64) void bsa_dq_kernel(BsaParams p, int qsub, 
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int ds = 0; ds < 8; ds++) {
-        st = E::mfma32(lds_read16<V8>(Kb + kt * 32 * 256 + kro[ds]), qreg[ds], st);
-        dpt = E::mfma32(lds_read16<V8>(Vb + kt * 32 * 256 + kro[ds]), doreg[ds], dpt);
+        st = E::mfma32(lds_read16<V8>(Kr + kt * 32 * kPadPitch + 32 * ds), qreg[ds], st);
+        dpt = E::mfma32(lds_read16<V8>(Vr + kt * 32 * kPadPitch + 32 * ds), doreg[ds], dpt);
       }
       __builtin_amdgcn_s_setprio(0);
       // dS^T = P^T * (dP^T - D), P^T = exp2(S^T * scale*log2e - LSE2);
@@ -236,9 +215,8 @@ __global__ __launch_bounds__(NW * 64) void bsa_dq_kernel(BsaParams p, int qsub, 
       for (int k2 = 0; k2 < 2; k2++)
 #pragma unroll
         for (int dt = 0; dt < 4; dt++)
-          dq[dt] = E::mfma32(lds_read_tr_pair<V8>(Kb + (kt * 2 + k2) * 16 * 256 + ktr[dt][0],
-                                                  Kb + (kt * 2 + k2) * 16 * 256 + ktr[dt][1]),
-                             bs[k2], dq[dt]);
+          dq[dt] = E::mfma32(ptile_tr<V8>(Kt + (kt * 2 + k2) * 16 * kPadPitch + 64 * dt), bs[k2],
+                             dq[dt]);
       __builtin_amdgcn_s_setprio(0);
     }
     wait_vm();
@@ -281,10 +259,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   typedef typename E::V8 V8;
   constexpr int NK = NW * 32;       // keys per workgroup
   constexpr int kQC = 32;           // queries per chunk
-  constexpr int kQTile = kQC * kD * 2;
-  __shared__ __attribute__((aligned(1024))) char lds_k[NK * kD * 2];
-  __shared__ __attribute__((aligned(1024))) char lds_q[2][kQTile];
-  __shared__ __attribute__((aligned(1024))) char lds_do[2][kQTile];
+  constexpr int kQTile = ptile_bytes(kQC);
+  __shared__ __attribute__((aligned(1024))) char lds_k[ptile_bytes(NK)];
+  __shared__ __attribute__((aligned(1024))) char lds_qd[2][2][kQTile];  // [stage][Q, dO]
   __shared__ float lds_lse[2][64];
   __shared__ float lds_dlt[2][64];
 
@@ -317,7 +294,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int key_hi = min((kb + 1) * p.bkv, km.len);
   if (key_lo >= key_hi) return;
 
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6) & (NW - 1);  // wave-uniform
   const int l32 = lane & 31, h = lane >> 5;
   const int wkey0 = key_lo + wid * 32;
   const int mykey = wkey0 + l32;
@@ -327,16 +305,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   const T* kh = (const T*)p.k + kvoff;
   const T* vh = (const T*)p.v + kvoff;
 
-  // K rows of the workgroup into LDS (rows past key_hi re-read the last key)
+  // K rows of the workgroup into a padded LDS tile (rows past key_hi re-read
+  // the last key)
   {
-    const int sub = lane >> 4, pc = lane & 15;
-#pragma unroll
-    for (int u = 0; u < NK / 4 / NW; u++) {
-      const int inst = wid * (NK / 4 / NW) + u;
-      const int r = inst * 4 + sub;
-      const long key = min(key_lo + r, key_hi - 1);
-      g2lds16((const char*)(kh + key * km.row) + ((pc ^ swz(r)) << 4), lds_k + inst * 1024);
-    }
+    PStage<NW, NK> kst;
+    kst.ragged((const char*)(kh + (long)key_lo * km.row), (long)km.row * 2, key_hi - 1 - key_lo,
+               lds_addr(lds_k), wid, lane);
   }
   V8 vreg[8];
 #pragma unroll
@@ -369,71 +343,39 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     }
     return c;
   };
-  // 32 rows of Q and of dO (8 KB each) plus their LSE / softmax_grad.  A
+  // 32 rows of Q and of dO (padded tiles) plus their LSE / softmax_grad.  A
   // whole chunk takes a scalar base (its first row) plus per-lane offsets
-  // fixed for the walk; a ragged chunk clamps its rows lane by lane.
-  constexpr int NU = 8 / NW;  // 1-KB slices (4 rows) per wave and tile
-  unsigned goff[NU];
-  {
-    const int sub = lane >> 4, pc = lane & 15;
-#pragma unroll
-    for (int u = 0; u < NU; u++) {
-      const int r = (wid * NU + u) * 4 + sub;
-      goff[u] = (unsigned)(r * qm.row * 2) + (unsigned)((pc ^ swz(r)) << 4);
-    }
-  }
+  // fixed for the walk; a ragged chunk re-reads its last row.
+  const long qrow_bytes = (long)qm.row * 2;
+  PStage<NW, kQC> stg;
+  stg.init(wid, lane, qrow_bytes);
+  const unsigned lds0 = lds_addr(&lds_qd[0][0][0]);
   auto load_chunk = [&](int n1, int qs, int qe, int buf) {
     const long qoff = qm.at(n1, 0), soff = sm.at(n1, 0);
-    const int ln = lane;
+    const unsigned lq = lds0 + buf * 2 * kQTile, ld = lq + kQTile;
+    const char* qb = (const char*)((const T*)p.q + qoff + (long)qs * qm.row);
+    const char* db = (const char*)((const T*)p.dout + qoff + (long)qs * qm.row);
     if (qe - qs == kQC) {
-      const char* qb = (const char*)((const T*)p.q + qoff + (long)qs * qm.row);
-      const char* db = (const char*)((const T*)p.dout + qoff + (long)qs * qm.row);
-#pragma unroll
-      for (int u = 0; u < NU; u++) {
-        g2lds16_so(qb, goff[u], lds_q[buf] + (wid * NU + u) * 1024);
-        g2lds16_so(db, goff[u], lds_do[buf] + (wid * NU + u) * 1024);
-      }
+      stg.full(qb, lq, wid, lane);
+      stg.full(db, ld, wid, lane);
     } else {
-      const int sub = ln >> 4, pc = ln & 15;
-#pragma unroll
-      for (int u = 0; u < NU; u++) {
-        const int inst = wid * NU + u;
-        const int r = inst * 4 + sub;
-        const long row = qoff + (long)min(qs + r, qe - 1) * qm.row;
-        g2lds16((const char*)((const T*)p.q + row) + ((pc ^ swz(r)) << 4),
-                lds_q[buf] + inst * 1024);
-        g2lds16((const char*)((const T*)p.dout + row) + ((pc ^ swz(r)) << 4),
-                lds_do[buf] + inst * 1024);
-      }
+      stg.ragged(qb, qrow_bytes, qe - 1 - qs, lq, wid, lane);
+      stg.ragged(db, qrow_bytes, qe - 1 - qs, ld, wid, lane);
     }
     if (wid == 0) {
       // a direct LDS load writes lane l's dword at base + 4*l for all 64
       // lanes: the arrays hold 64 entries; entries past 32 are never read
-      const long r = soff + (long)min(qs + ln, qe - 1) * sm.row;
+      const long r = soff + (long)min(qs + lane, qe - 1) * sm.row;
       g2lds4(p.lse + r, lds_lse[buf]);
       g2lds4(p.delta + r, lds_dlt[buf]);
     }
   };
 
-  // per-lane LDS byte offsets of the MFMA operands: rows l32 (Q, dO; the
-  // wave's K rows 32*wid + l32 share the swizzle), pieces 2*ds + h; dO^T and
-  // Q^T by transpose reads
-  unsigned kro[8], ktr[4][2];
-  {
-    const int i16 = lane & 15, g16 = lane >> 4;
-#pragma unroll
-    for (int ds = 0; ds < 8; ds++)
-      kro[ds] = (unsigned)(l32 * 256 + (((2 * ds + h) ^ swz(l32)) << 4));
-    const int r0 = 4 * h + (i16 >> 2), r1 = r0 + 8;
-    const int b8 = 8 * (i16 & 1);
-#pragma unroll
-    for (int dt = 0; dt < 4; dt++) {
-      const int c = 4 * dt + 2 * (g16 & 1) + ((i16 & 3) >> 1);
-      ktr[dt][0] = (unsigned)(r0 * 256 + ((c ^ swz(r0)) << 4) + b8);
-      ktr[dt][1] = (unsigned)(r1 * 256 + ((c ^ swz(r1)) << 4) + b8);
-    }
-  }
-  const char* Kw = lds_k + wid * 32 * 256;
+  // Per-lane bases of the operand reads: Q and dO rows l32, the wave's K
+  // rows 32*wid + l32 (pieces 2*ds + h at +32*ds); dO^T and Q^T by transpose
+  // reads.
+  const unsigned rb = prow_base(lane), tb = ptr_base(lane);
+  const char* Kr = lds_k + wid * 32 * kPadPitch + rb;
 
   f32x16 dvt[4], dkt[4];
 #pragma unroll
@@ -451,12 +393,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   __syncthreads();
   int buf = 0;
   while (i.e < e1) {
-    // Lane-derived terms of this iteration come from an opaque copy of the
-    // lane id, so they are recomputed here rather than kept (and spilled)
-    // across iterations.
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-    const int l32i = ln & 31, hi = ln >> 5;
     int n1, qs, qe;
     chunk_range(i, n1, qs, qe);
     const ChunkPos inext = next_valid(chunk_advance(i, cpq));
@@ -465,8 +401,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
       chunk_range(inext, n1b, qs2, qe2);
       load_chunk(n1b, qs2, qe2, buf ^ 1);
     }
-    const char* Qb = lds_q[buf];
-    const char* Db = lds_do[buf];
+    const char* Qr = &lds_qd[buf][0][0] + rb;
+    const char* Dr = &lds_qd[buf][1][0] + rb;
+    const char* Qt = &lds_qd[buf][0][0] + tb;
+    const char* Dt = &lds_qd[buf][1][0] + tb;
 
     // raised wave priority over the MFMA runs (see the dQ kernel)
     __builtin_amdgcn_s_setprio(1);
@@ -476,8 +414,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     for (int j = 0; j < 16; j++) s[j] = dp[j] = 0.f;
 #pragma unroll
     for (int ds = 0; ds < 8; ds++) {
-      s = E::mfma32(lds_read16<V8>(Qb + kro[ds]), lds_read16<V8>(Kw + kro[ds]), s);
-      dp = E::mfma32(lds_read16<V8>(Db + kro[ds]), vreg[ds], dp);
+      s = E::mfma32(lds_read16<V8>(Qr + 32 * ds), lds_read16<V8>(Kr + 32 * ds), s);
+      dp = E::mfma32(lds_read16<V8>(Dr + 32 * ds), vreg[ds], dp);
     }
     // three LDS reads feed two MFMAs per step
     __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
@@ -494,9 +432,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     // atten_mask keep bits of this lane's key column: bit j for element j
     uint32_t keep = 0xffffffffu;
     if constexpr (AM) {
-      const int key = wkey0 + l32i;
+      const int key = wkey0 + l32;
       keep = key < key_hi ? am_keep_col(p.am + b * p.am_sb + n1 * p.am_sn + (long)qs * p.am_pitch +
-                                            key, p.am_pitch, qe - qs, hi)
+                                            key, p.am_pitch, qe - qs, h)
                           : 0u;
     }
     // element j of a lane is query 8*(j/4) + 4*h + j%4 of the chunk, column key l32
@@ -504,12 +442,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     auto form = [&](auto masked) {
       int lo = 0, up = 0;
       if (masked) {
-        lo = (p.causal ? wkey0 + l32i - qs : 0) - 4 * hi;
-        up = wkey0 + l32i < key_hi ? qe - qs - 1 - 4 * hi : -1000000;
+        lo = (p.causal ? wkey0 + l32 - qs : 0) - 4 * h;
+        up = wkey0 + l32 < key_hi ? qe - qs - 1 - 4 * h : -1000000;
       }
 #pragma unroll
       for (int j4 = 0; j4 < 4; j4++) {
-        const int rbase = 8 * j4 + 4 * hi;
+        const int rbase = 8 * j4 + 4 * h;
         const float4 lse4 = *reinterpret_cast<const float4*>(&lds_lse[buf][rbase]);
         const float4 dl4 = *reinterpret_cast<const float4*>(&lds_dlt[buf][rbase]);
         const float lv[4] = {lse4.x, lse4.y, lse4.z, lse4.w};
@@ -535,12 +473,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     for (int k2 = 0; k2 < 2; k2++)
 #pragma unroll
       for (int dt = 0; dt < 4; dt++) {
-        dvt[dt] = E::mfma32(lds_read_tr_pair<V8>(Db + k2 * 16 * 256 + ktr[dt][0],
-                                                 Db + k2 * 16 * 256 + ktr[dt][1]),
-                            bp[k2], dvt[dt]);
-        dkt[dt] = E::mfma32(lds_read_tr_pair<V8>(Qb + k2 * 16 * 256 + ktr[dt][0],
-                                                 Qb + k2 * 16 * 256 + ktr[dt][1]),
-                            bd[k2], dkt[dt]);
+        dvt[dt] = E::mfma32(ptile_tr<V8>(Dt + k2 * 16 * kPadPitch + 64 * dt), bp[k2], dvt[dt]);
+        dkt[dt] = E::mfma32(ptile_tr<V8>(Qt + k2 * 16 * kPadPitch + 64 * dt), bd[k2], dkt[dt]);
       }
     sched_mfma_lds<16, 2, 4>();
     __builtin_amdgcn_s_setprio(0);

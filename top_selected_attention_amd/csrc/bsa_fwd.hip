@@ -14,9 +14,9 @@
 // 16 keys of it, so the online-softmax max and sum are in-lane plus one
 // exchange with lane l^32.  P^T leaves the accumulator directly as the B
 // operand of O^T += V^T P^T, with V^T read from the natural-layout V tile by
-// LDS transpose reads (ds_read_b64_tr_b16).
-#include <type_traits>
-
+// LDS transpose reads (ds_read_b64_tr_b16).  The tiles are padded (272-byte
+// rows, rows permuted within 16) so that every operand read is one base
+// register plus an immediate.
 #include "tsa_device.h"
 #include "tsa_internal.h"
 
@@ -24,7 +24,7 @@ namespace tsa {
 
 constexpr int kD = 128;        // head dim (the page's constraint: headdim = 128)
 constexpr int kKC = 64;        // keys per chunk
-constexpr int kTileB = kKC * kD * 2;  // bytes per staged K or V chunk
+constexpr int kTileB = ptile_bytes(kKC);  // bytes per staged (padded) K or V chunk
 
 // AM: an element mask (atten_mask) is given; its entries are read per chunk.
 template <class E, int NW, bool AM>
@@ -32,8 +32,7 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_kernel(BsaParams p, int qsub,
   typedef typename E::T T;
   typedef typename E::V8 V8;
   constexpr int NR = NW * 32;  // query rows per workgroup (32 per wave)
-  __shared__ __attribute__((aligned(1024))) char lds_k[2][kTileB];
-  __shared__ __attribute__((aligned(1024))) char lds_v[2][kTileB];
+  __shared__ __attribute__((aligned(1024))) char lds_kv[2][2][kTileB];  // [stage][K, V]
 
   const int item = blockIdx.x;
   if (item >= n_items) return;
@@ -56,7 +55,8 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_kernel(BsaParams p, int qsub,
   const int row_hi = min((qb + 1) * p.bq, qm.len);
   if (row_lo >= row_hi) return;
 
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6) & (NW - 1);  // wave-uniform
   const int l32 = lane & 31, h = lane >> 5;
   const int wrow0 = row_lo + wid * 32;
   const int qrow = wrow0 + l32;  // this lane's query column
@@ -99,53 +99,28 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_kernel(BsaParams p, int qsub,
     }
     return c;
   };
-  // Direct global -> LDS loads (no registers) into the swizzled layout.  Keys
-  // past the chunk's end re-read its last key (finite data; their scores are
+  // Direct global -> LDS loads (no registers) into padded tiles.  Keys past
+  // the chunk's end re-read its last key (finite data; their scores are
   // masked, so P = 0 exactly there).  A whole chunk takes a scalar base (its
-  // first key row) plus per-lane offsets fixed for the walk; a ragged chunk
-  // clamps its rows lane by lane.
-  constexpr int NU = 16 / NW;  // 1-KB slices (4 rows) per wave and tile
-  const int sub = lane >> 4, pc = lane & 15;
-  unsigned goff[NU];
-#pragma unroll
-  for (int u = 0; u < NU; u++) {
-    const int r = (wid * NU + u) * 4 + sub;
-    goff[u] = (unsigned)(r * krow_bytes) + (unsigned)((pc ^ swz(r)) << 4);
-  }
-  auto load_chunk = [&](int ks, int ke, char* kt, char* vt) {
+  // first key row) plus per-lane offsets fixed for the walk.
+  PStage<NW, kKC> stg;
+  stg.init(wid, lane, krow_bytes);
+  const unsigned lds0 = lds_addr(&lds_kv[0][0][0]);
+  auto load_chunk = [&](int ks, int ke, int buf) {
+    const unsigned lk = lds0 + buf * 2 * kTileB, lv = lk + kTileB;
+    const char* kb = (const char*)kh + (long)ks * krow_bytes;
+    const char* vb = (const char*)vh + (long)ks * krow_bytes;
     if (ke - ks == kKC) {
-      const char* kb = (const char*)kh + (long)ks * krow_bytes;
-      const char* vb = (const char*)vh + (long)ks * krow_bytes;
-#pragma unroll
-      for (int u = 0; u < NU; u++) g2lds16_so(kb, goff[u], kt + (wid * NU + u) * 1024);
-#pragma unroll
-      for (int u = 0; u < NU; u++) g2lds16_so(vb, goff[u], vt + (wid * NU + u) * 1024);
+      stg.full(kb, lk, wid, lane);
+      stg.full(vb, lv, wid, lane);
     } else {
-      auto row_of = [&](int r) { return min(ks + r, ke - 1); };
-      stage_tile64<NW>((const char*)kh, krow_bytes, kt, row_of);
-      stage_tile64<NW>((const char*)vh, krow_bytes, vt, row_of);
+      stg.ragged(kb, krow_bytes, ke - 1 - ks, lk, wid, lane);
+      stg.ragged(vb, krow_bytes, ke - 1 - ks, lv, wid, lane);
     }
   };
-  // Per-lane LDS byte offsets of the MFMA operands, fixed for the walk (the
-  // tiles' bases and the 32-row / 16-row steps are compile-time immediates):
-  // K rows l32 (and 32 + l32: the same swizzle), pieces 2*ds + h; V^T by
-  // transpose reads, rows 4h + i16/4 (+8) of each 16-key step, the 16-byte
-  // piece of dims 32*dt + ...
-  unsigned kro[8], vtr[4][2];
-  {
-    const int i16 = lane & 15, g16 = lane >> 4;
-#pragma unroll
-    for (int ds = 0; ds < 8; ds++)
-      kro[ds] = (unsigned)(l32 * 256 + (((2 * ds + h) ^ swz(l32)) << 4));
-    const int r0 = 4 * h + (i16 >> 2), r1 = r0 + 8;
-    const int b8 = 8 * (i16 & 1);
-#pragma unroll
-    for (int dt = 0; dt < 4; dt++) {
-      const int c = 4 * dt + 2 * (g16 & 1) + ((i16 & 3) >> 1);
-      vtr[dt][0] = (unsigned)(r0 * 256 + ((c ^ swz(r0)) << 4) + b8);
-      vtr[dt][1] = (unsigned)(r1 * 256 + ((c ^ swz(r1)) << 4) + b8);
-    }
-  }
+  // Per-lane bases of the MFMA operand reads: K rows (key l32, +32 per key
+  // tile; pieces 2*ds + h at +32*ds) and V^T by transpose reads.
+  const unsigned rb = prow_base(lane), tb = ptr_base(lane);
 
   // Online softmax state of this lane's query, base 2.  The reference m only
   // moves when a chunk's max exceeds it by more than kLazy (so P <= 2^kLazy);
@@ -162,7 +137,7 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_kernel(BsaParams p, int qsub,
   if (i.e < e1) {
     int ks, ke;
     chunk_range(i, ks, ke);
-    load_chunk(ks, ke, lds_k[0], lds_v[0]);
+    load_chunk(ks, ke, 0);
   }
   wait_vm();
   __syncthreads();
@@ -174,10 +149,10 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_kernel(BsaParams p, int qsub,
     if (inext.e < e1) {
       int ks2, ke2;
       chunk_range(inext, ks2, ke2);
-      load_chunk(ks2, ke2, lds_k[buf ^ 1], lds_v[buf ^ 1]);
+      load_chunk(ks2, ke2, buf ^ 1);
     }
-    const char* Kb = lds_k[buf];
-    const char* Vb = lds_v[buf];
+    const char* Kr = &lds_kv[buf][0][0] + rb;
+    const char* Vt = &lds_kv[buf][1][0] + tb;
 
     // S^T = K Q^T: 64 keys x 32 queries (two 32x32 tiles)
     f32x16 st[2];
@@ -187,8 +162,8 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_kernel(BsaParams p, int qsub,
       for (int j = 0; j < 16; j++) st[kt][j] = 0.f;
 #pragma unroll
     for (int ds = 0; ds < 8; ds++) {
-      st[0] = E::mfma32(lds_read16<V8>(Kb + kro[ds]), qreg[ds], st[0]);
-      st[1] = E::mfma32(lds_read16<V8>(Kb + 32 * 256 + kro[ds]), qreg[ds], st[1]);
+      st[0] = E::mfma32(lds_read16<V8>(Kr + 32 * ds), qreg[ds], st[0]);
+      st[1] = E::mfma32(lds_read16<V8>(Kr + 32 * kPadPitch + 32 * ds), qreg[ds], st[1]);
     }
     sched_mfma_lds<16, 1, 4>();
     // Element j of tile kt is key ks + kt*32 + 8*(j/4) + 4*h + j%4.  A chunk
@@ -240,9 +215,7 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_kernel(BsaParams p, int qsub,
     for (int k4 = 0; k4 < 4; k4++)
 #pragma unroll
       for (int dt = 0; dt < 4; dt++)
-        o[dt] = E::mfma32(lds_read_tr_pair<V8>(Vb + k4 * 16 * 256 + vtr[dt][0],
-                                               Vb + k4 * 16 * 256 + vtr[dt][1]),
-                          pb[k4], o[dt]);
+        o[dt] = E::mfma32(ptile_tr<V8>(Vt + k4 * 16 * kPadPitch + 64 * dt), pb[k4], o[dt]);
     sched_mfma_lds<16, 2, 4>();
 
     wait_vm();

@@ -196,6 +196,130 @@ __device__ __forceinline__ void g2lds4(const void* g, void* lds_base) {
       : "memory");
 }
 
+// Direct loads addressed by 32-bit LDS byte addresses (see lds_addr): the
+// vector-address form and the scalar-base form above.
+__device__ __forceinline__ void g2lds16_at(const void* g, unsigned lds) {
+  const unsigned l = __builtin_amdgcn_readfirstlane(lds);
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0\n\ts_nop 0"
+      : "=&s"(saved)
+      : "v"(g), "s"(l)
+      : "memory");
+}
+__device__ __forceinline__ void g2lds16_so_at(const void* sbase, unsigned voff, unsigned lds) {
+  const unsigned l = __builtin_amdgcn_readfirstlane(lds);
+  const unsigned long long b = (unsigned long long)(uintptr_t)sbase;
+  const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)b);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)(b >> 32));
+  const unsigned long long sb = ((unsigned long long)hi << 32) | lo;
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0\n\ts_nop 0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(sb), "s"(l)
+      : "memory");
+}
+// LDS byte address of a __shared__ object (a compile-time constant for a
+// __shared__ array, so arithmetic on it stays in scalar registers).
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return (unsigned)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+
+// ---------------------------------------------------------------------------
+// Padded tiles.  A [rows][128] 16-bit tile staged in LDS with a 272-byte row
+// pitch (256 bytes of data, 16 of padding), logical row k in physical row
+// prow(k), which swaps the two 2-bit fields of k mod 16 (prow is its own
+// inverse).  Every MFMA operand read of a lane is then one base register
+// plus a compile-time offset, and the read patterns stay free of bank
+// conflicts on 64 four-byte banks:
+//  * 16-byte row reads by 16 lanes of 16 consecutive rows: the physical rows
+//    are a permutation of 16 consecutive ones, whose starts lie 4 banks
+//    apart (272 bytes = 68 banks);
+//  * transpose reads (ds_read_b64_tr_b16) by 32 lanes of the rows 4q + i,
+//    i < 4, times 4 aligned pieces: the physical rows are 4 apart (16
+//    banks), so the four 64-byte row segments tile the 64 banks.
+// Direct global -> LDS loads fill a tile in 1-KB slices: byte o holds
+// logical row prow(o / 272), piece (o % 272) / 16; padding pieces re-read
+// row 0, piece 0 (never read back).  A tile of 32 rows ends half-way into
+// its ninth slice, whose upper 32 lanes stay idle.
+// ---------------------------------------------------------------------------
+constexpr int kPadPitch = 272;
+__host__ __device__ constexpr int ptile_bytes(int rows) { return rows * kPadPitch; }
+__device__ __forceinline__ int prow(int k) {
+  return (k & ~15) | ((k & 3) << 2) | ((k >> 2) & 3);
+}
+// The logical row k and 16-byte piece pc that byte o of a padded tile of
+// `rows` rows holds.
+__device__ __forceinline__ void pslot(int o, int rows, int& k, int& pc) {
+  const int r = o / kPadPitch, c = (o - r * kPadPitch) >> 4;
+  const bool ok = c < 16 && r < rows;  // r >= rows: lanes of a partial slice
+  k = ok ? prow(r) : 0;
+  pc = ok ? c : 0;
+}
+// Base offset of a lane's 16-byte row reads: row lane%32 (a 32-row step is
+// +32*272 bytes), piece 2*ds + lane/32 at +32*ds bytes.
+__device__ __forceinline__ unsigned prow_base(int lane) {
+  return (unsigned)(prow(lane & 31) * kPadPitch + 16 * (lane >> 5));
+}
+// Base offset of a lane's transpose reads: the k-major operand of rows
+// 16*k16 + {4h..4h+3, 8+4h..8+4h+3} (h = lane/32) and column dt*32 +
+// lane%32, in the row order of a 32x32 accumulator's elements 8*k2 ..
+// 8*k2+7.  The 16-row step is +16*272 bytes, dt is +64, and the second row
+// group (+8 rows) lies 2*272 bytes after the first.
+__device__ __forceinline__ unsigned ptr_base(int lane) {
+  const int g16 = lane >> 4, i16 = lane & 15, h = lane >> 5;
+  return (unsigned)((4 * (i16 >> 2) + h) * kPadPitch + (2 * (g16 & 1) + ((i16 & 3) >> 1)) * 16 +
+                    8 * (i16 & 1));
+}
+template <typename V8>
+__device__ __forceinline__ V8 ptile_tr(const char* p) {
+  return lds_read_tr_pair<V8>(p, p + 2 * kPadPitch);
+}
+
+// Staging of a padded tile of R rows by the NW waves of a workgroup: wave w
+// loads slices w, w + NW, ...  The per-lane source offsets of a whole tile
+// (rows row_bytes apart) are fixed at set-up; a ragged tile clamps its rows.
+template <int NW, int R>
+struct PStage {
+  static constexpr int S = (ptile_bytes(R) + 1023) / 1024;        // slices
+  static constexpr int kTail = (ptile_bytes(R) - 1024 * (S - 1)) / 16;  // lanes of the last
+  static constexpr int NU = (S + NW - 1) / NW;
+  unsigned off[NU];
+  __device__ __forceinline__ void init(int wid, int lane, long row_bytes) {
+#pragma unroll
+    for (int u = 0; u < NU; u++) {
+      int k, pc;
+      pslot(1024 * (u * NW + wid) + 16 * lane, R, k, pc);
+      off[u] = (unsigned)(k * row_bytes) + (unsigned)(16 * pc);
+    }
+  }
+  // rows base, base + row_bytes, ... (wid wave-uniform)
+  __device__ __forceinline__ void full(const char* base, unsigned lds, int wid, int lane) const {
+#pragma unroll
+    for (int u = 0; u < NU; u++) {
+      const int sl = u * NW + wid;
+      if (sl < S && (kTail == 64 || sl < S - 1 || lane < kTail))
+        g2lds16_so_at(base, off[u], lds + 1024 * sl);
+    }
+  }
+  // logical rows past `last` re-read row `last`
+  __device__ __forceinline__ void ragged(const char* base, long row_bytes, int last, unsigned lds,
+                                         int wid, int lane) const {
+#pragma unroll
+    for (int u = 0; u < NU; u++) {
+      const int sl = u * NW + wid;
+      if (sl < S && (kTail == 64 || sl < S - 1 || lane < kTail)) {
+        int k, pc;
+        pslot(1024 * sl + 16 * lane, R, k, pc);
+        g2lds16_at(base + (long)min(k, last) * row_bytes + 16 * pc, lds + 1024 * sl);
+      }
+    }
+  }
+};
+
 // Position in a walk over the chunks of a block list: entry e of the list
 // and sub-chunk s of that entry (advanced by counting, with no division).
 struct ChunkPos {
