@@ -167,7 +167,8 @@ size_t bsa_carve(const A* a, void* ws, BsaWs* out, bool with_delta) {
   w.seg_off = c.take<int>(ds.n_items + 1);
   w.part_off = c.take<int>(ds.n_items + 1);
   w.seg_meta = c.take<int>(1);
-  w.delta = with_delta ? c.take<float>((long)a->B * a->N1 * a->Sq) : nullptr;
+  // per row: LSE in base 2 and softmax_grad, interleaved
+  w.delta = with_delta ? c.take<float>(2L * a->B * a->N1 * a->Sq) : nullptr;
   w.part = with_delta ? c.take<float>(ds.max_parts * 2 * ds.nk * 128) : nullptr;
   if (out) *out = w;
   return c.off + kAlign;

@@ -93,7 +93,9 @@ __global__ __launch_bounds__(NW * 64) void bsa_dq_kernel(BsaParams p, int qsub, 
     acc += __shfl_xor(acc, 32);
     dlt = acc;
     lse2 = row_ok ? p.lse[sm.at(n1, qrow)] * kLog2e : 0.f;
-    if (row_ok && h == 0) p.delta[sm.at(n1, qrow)] = acc;
+    // stored beside the row's LSE in base 2, the pair the dK/dV kernel reads
+    if (row_ok && h == 0)
+      *reinterpret_cast<float2*>(p.delta + 2 * sm.at(n1, qrow)) = make_float2(lse2, acc);
   }
 
   const unsigned char* amrow = nullptr;
@@ -262,8 +264,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   constexpr int kQTile = ptile_bytes(kQC);
   __shared__ __attribute__((aligned(1024))) char lds_k[ptile_bytes(NK)];
   __shared__ __attribute__((aligned(1024))) char lds_qd[2][2][kQTile];  // [stage][Q, dO]
-  __shared__ float lds_lse[2][64];
-  __shared__ float lds_dlt[2][64];
+  __shared__ float lds_ld[2][64];  // per chunk row: LSE (base 2), softmax_grad
 
   // One workgroup per segment: segment sg belongs to work item rank (the
   // largest r with seg_off[r] <= sg), items in the order of p.order_kv
@@ -365,9 +366,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     if (wid == 0) {
       // a direct LDS load writes lane l's dword at base + 4*l for all 64
       // lanes: the arrays hold 64 entries; entries past 32 are never read
-      const long r = soff + (long)min(qs + lane, qe - 1) * sm.row;
-      g2lds4(p.lse + r, lds_lse[buf]);
-      g2lds4(p.delta + r, lds_dlt[buf]);
+      // lanes 2r, 2r + 1: the LSE / softmax_grad pair of the chunk's row r
+      const long r = soff + (long)min(qs + (lane >> 1), qe - 1) * sm.row;
+      g2lds4(p.delta + 2 * r + (lane & 1), lds_ld[buf]);
     }
   };
 
@@ -448,14 +449,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
       for (int j4 = 0; j4 < 4; j4++) {
         const int rbase = 8 * j4 + 4 * h;
-        const float4 lse4 = *reinterpret_cast<const float4*>(&lds_lse[buf][rbase]);
-        const float4 dl4 = *reinterpret_cast<const float4*>(&lds_dlt[buf][rbase]);
-        const float lv[4] = {lse4.x, lse4.y, lse4.z, lse4.w};
-        const float dv[4] = {dl4.x, dl4.y, dl4.z, dl4.w};
+        const float4 a4 = *reinterpret_cast<const float4*>(&lds_ld[buf][2 * rbase]);
+        const float4 b4 = *reinterpret_cast<const float4*>(&lds_ld[buf][2 * rbase + 4]);
+        const float lv[4] = {a4.x, a4.z, b4.x, b4.z};
+        const float dv[4] = {a4.y, a4.w, b4.y, b4.w};
 #pragma unroll
         for (int jj = 0; jj < 4; jj++) {
           const int j = 4 * j4 + jj;
-          float pr = fast_exp2(__builtin_fmaf(s[j], sl2, -lv[jj] * kLog2e));
+          float pr = fast_exp2(__builtin_fmaf(s[j], sl2, -lv[jj]));
           if (masked) {
             const int off = 8 * j4 + jj;
             pr = (off >= lo && off <= up && ((keep >> j) & 1u)) ? pr : 0.f;

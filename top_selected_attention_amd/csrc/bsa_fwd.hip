@@ -185,12 +185,12 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_kernel(BsaParams p, int qsub,
           st[kt][j] = ((kt * 32 + 8 * (j >> 2) + (j & 3)) <= lim && ((keep >> (16 * kt + j)) & 1u))
                           ? st[kt][j] : -INFINITY;
     }
-    float mx = fmaxf(st[0][0], st[1][0]);
+    float mx = vmax(st[0][0], st[1][0]);
 #pragma unroll
-    for (int j = 1; j < 16; j++) mx = fmaxf(mx, fmaxf(st[0][j], st[1][j]));
-    mx = wave_max_half_swap(mx) * sl2;
+    for (int j = 1; j < 16; j++) mx = vmax(mx, vmax(st[0][j], st[1][j]));
+    mx = max_xor32(mx) * sl2;
     if (__builtin_amdgcn_ballot_w64(mx > m + kLazy)) {
-      const float m_new = fmaxf(m, mx);
+      const float m_new = vmax(m, mx);
       const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m - m_new);
       m = m_new;
       lsum *= alpha;

@@ -155,9 +155,9 @@ __global__ __launch_bounds__(256) void nsa_fwd_kernel(NsaParams p, int n_items) 
       const bool ok = key < ke && (!g.causal || key <= pos);
       const float s = ok ? st[j] * sl2 : -INFINITY;
       st[j] = s;
-      mx = fmaxf(mx, s);
+      mx = vmax(mx, s);
     }
-    mx = wave_max_half_swap(mx);
+    mx = max_xor32(mx);
     const float m_new = fmaxf(m, mx);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
     const float alpha = fast_exp2(m - m_use);
@@ -329,7 +329,7 @@ void nsa_fwd16_kernel(NsaParams p, int n_items) {
       for (int j = 0; j < 4; j++) {
         const float v = (16 * kt + 4 * gq + j) <= lim ? st[kt][j] : -INFINITY;
         st[kt][j] = v;
-        mx = fmaxf(mx, v);
+        mx = vmax(mx, v);
       }
     mx = max_xor16_32(mx) * sl2;
     if (__builtin_amdgcn_ballot_w64(mx > m + kLazy)) {

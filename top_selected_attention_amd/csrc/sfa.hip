@@ -313,7 +313,7 @@ __global__ __launch_bounds__(512) void sfa_split_kernel(SfaParams p, int n_items
               const int key = kt * 16 + 4 * g + j;
               const float v = ((mcur >> key) & 1u) ? st[kt][hh][j] : -INFINITY;
               st[kt][hh][j] = v;
-              mx = fmaxf(mx, v);
+              mx = vmax(mx, v);
             }
           mx = max_xor16_32(mx) * sl2;
           if (__builtin_amdgcn_ballot_w64(mx > m[hh] + kLazy)) {
@@ -523,7 +523,7 @@ __global__ __launch_bounds__(256) void sfa_split_sepv_kernel(SfaParams p, int n_
             const int key = kt * 16 + 4 * g + j;
             const float v = ((mcur >> key) & 1u) ? st[kt][j] : -INFINITY;
             st[kt][j] = v;
-            mx = fmaxf(mx, v);
+            mx = vmax(mx, v);
           }
         mx = max_xor16_32(mx) * sl2;
         if (__builtin_amdgcn_ballot_w64(mx > m + kLazy)) {

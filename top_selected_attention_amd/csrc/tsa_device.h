@@ -87,21 +87,22 @@ __device__ __forceinline__ V8 lds_read16(const void* p) {
   return __builtin_bit_cast(V8, *reinterpret_cast<const uint4*>(p));
 }
 
-__device__ __forceinline__ float wave_max_half_swap(float x) {
-  // combine lanes l and l^32
-  return fmaxf(x, __shfl_xor(x, 32));
-}
+// IEEE maximum (a NaN operand gives NaN).  On gfx950 it is v_maximum3_f32,
+// two operands per instruction and no canonicalising of its inputs, which
+// fmaxf (maxnum) needs for values such as MFMA results.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 
 // Max over lanes l and l ^ 32, and over l, l ^ 16, l ^ 32, l ^ 48, on the
 // VALU lane-swap instructions (a swap of 16-lane rows 1, 3 with 0, 2, and of
 // the two 32-lane halves) instead of LDS-routed shuffles.
 __device__ __forceinline__ float max_xor32(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float max_xor16_32(float x) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return max_xor32(fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
+  return max_xor32(vmax(__uint_as_float(r[0]), __uint_as_float(r[1])));
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -75,7 +75,7 @@ struct BsaParams {
   void* dk;
   void* dv;
   float* lse;         // forward: written; backward: read
-  float* delta;       // backward: rowsum(dO * O), fp32 [B, N1, Sq]
+  float* delta;       // backward: per row {LSE * log2 e, rowsum(dO * O)}, fp32 [B, N1, Sq, 2]
   const int* row_ptr;
   const int* col;
   const int* rev_ptr;
