@@ -11,15 +11,16 @@ attention, then dQ (with softmax_grad) + dK/dV reusing the lists.
 Prints ONE JSON line.  ``value`` is effective TFLOP/s counted on the
 selected blocks only (forward 4*rows*keys*D per selected block pair,
 backward 2.5x that), i.e. algorithmic FLOPs / measured step time.  The same
-run then times the further workloads named by ``--also`` (by default
-bsa_causal_8k, nsa_varlen and sfa_decode) and reports them under
-``workloads``; only the main workload carries the oracle CPU baseline.
+run then times the further workloads named by ``--also`` (by default all
+the others but bsa_small) and reports them under ``workloads``; only the
+main workload carries the oracle CPU baseline.
 
 Workloads (``--workload``): bsa_window_128k, bsa_causal_8k (B=2, N=16,
 S=8192, causal block mask with p=0.25), bsa_small, bsa_tnd_varlen
 (block-sparse in TND layout over sequences of 2048, 4096, 8192, 2048 tokens,
 16 query / 4 KV heads), nsa_varlen (forward + backward), sfa_decode and
-sfa_sharedkv_decode (forward; value in GB/s of algorithmic gathered bytes).
+sfa_sharedkv_decode (forward; value in GB/s of algorithmic gathered bytes),
+floyd_256 (FloydAttention forward + backward, B=1, H=8, N=M=K=256, D=64).
 """
 
 import argparse
@@ -48,7 +49,8 @@ def parse():
     # cold start reads several percent slow)
     ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--workload", default="bsa_window_128k", choices=WORKLOADS)
-    ap.add_argument("--also", default="bsa_causal_8k,nsa_varlen,sfa_decode",
+    ap.add_argument("--also", default="bsa_causal_8k,bsa_tnd_varlen,nsa_varlen,sfa_decode,"
+                    "sfa_sharedkv_decode,floyd_256",
                     help="comma-separated workloads timed after the main one in the same run "
                          "(same steps and warm-up) and reported under 'workloads'; 'none' = "
                          "only the main workload")
@@ -677,9 +679,16 @@ def bench_floyd(args):
     names = ["fwd_scores", "fwd_softmax", "fwd_pv", "bwd_scores_dp", "bwd_p_ds", "bwd_dv",
              "bwd_dq", "bwd_dk"]
     stage = dict(zip(names, st))
-    # dominant stage: the backward scores and dP (four GEMM terms)
-    rl_ms, rl_flops = stage["bwd_scores_dp"], 4.0 * term
-    achieved = rl_flops / (rl_ms * 1e-3) / 1e12
+    # dominant stage: the backward scores and dP (four GEMM terms).  With
+    # D = 64 these products write 4 bytes of fp32 score per 2*D FLOP, so the
+    # stage is bound by HBM: algorithmic bytes = its six operand tensors read
+    # once (q, k1, k2, dY, v1, v2) + S and dP written once in fp32.
+    rl_ms = stage["bwd_scores_dp"]
+    elems_in = w["B"] * w["H"] * w["N"] * w["M"] * w["D"]        # q and dY
+    elems_kv = w["B"] * w["H"] * (w["N"] + w["M"]) * w["K"] * w["D"]  # k1 + k2, v1 + v2
+    scores = w["B"] * w["H"] * w["N"] * w["M"] * w["K"]
+    rl_bytes = 2.0 * (2 * elems_in + 2 * elems_kv) + 2 * 4.0 * scores
+    achieved = rl_bytes / (rl_ms * 1e-3) / 1e9
     value = (fwd_flops + bwd_flops) / (ms_step * 1e-3) / 1e12
     res = {
         "metric": "effective TFLOP/s on selected blocks (fwd, bwd) and % of bf16 MFMA peak",
@@ -697,9 +706,11 @@ def bench_floyd(args):
         "step_ms_events": _step_stats(plan.step_ms),
         "ms_per_step_cold": round(plan.cold_ms, 4),
         "settle_steps": plan.settle_steps,
-        "roofline": {"kernel": "floyd_gemm_kernel (backward scores and dP)", "bound": "mfma",
-                     "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        "roofline": {"kernel": "floyd_gemm_kernel", "stage": "backward scores and dP",
+                     "bound": "hbm",
+                     "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "bytes_per_launch": int(rl_bytes)},
     }
     return res, (w, q, k1, v1, k2, v2, do, scale, term)
 

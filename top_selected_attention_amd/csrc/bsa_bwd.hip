@@ -179,15 +179,11 @@ __global__ __launch_bounds__(NW * 64) void bsa_dq_kernel(BsaParams p, int qsub, 
       f32x16 st, dpt;
 #pragma unroll
       for (int j = 0; j < 16; j++) st[j] = dpt[j] = 0.f;
-      // raised wave priority over MFMA runs: the arbiter then lets this wave
-      // keep the matrix unit busy while others do softmax / loads
-      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int ds = 0; ds < 8; ds++) {
         st = E::mfma32(lds_read16<V8>(Kr + kt * 32 * kPadPitch + 32 * ds), qreg[ds], st);
         dpt = E::mfma32(lds_read16<V8>(Vr + kt * 32 * kPadPitch + 32 * ds), doreg[ds], dpt);
       }
-      __builtin_amdgcn_s_setprio(0);
       // dS^T = P^T * (dP^T - D), P^T = exp2(S^T * scale*log2e - LSE2);
       // element j is key ks + kt*32 + 8*(j/4) + 4*h + j%4.  Outside a full
       // chunk, key offsets above this lane's limit are masked (two copies of
@@ -212,14 +208,12 @@ __global__ __launch_bounds__(NW * 64) void bsa_dq_kernel(BsaParams p, int qsub, 
       if (full) form_ds(std::false_type());
       else form_ds(std::true_type());
       // dQ^T += K^T dS^T over the tile's 32 keys (two 16-key steps)
-      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int k2 = 0; k2 < 2; k2++)
 #pragma unroll
         for (int dt = 0; dt < 4; dt++)
           dq[dt] = E::mfma32(ptile_tr<V8>(Kt + (kt * 2 + k2) * 16 * kPadPitch + 64 * dt), bs[k2],
                              dq[dt]);
-      __builtin_amdgcn_s_setprio(0);
     }
     wait_vm();
     __syncthreads();
@@ -407,8 +401,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     const char* Qt = &lds_qd[buf][0][0] + tb;
     const char* Dt = &lds_qd[buf][1][0] + tb;
 
-    // raised wave priority over the MFMA runs (see the dQ kernel)
-    __builtin_amdgcn_s_setprio(1);
     // S = Q K^T and dP = dO V^T for 32 queries (rows) x this wave's 32 keys
     f32x16 s, dp;
 #pragma unroll
@@ -425,7 +417,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
     }
-    __builtin_amdgcn_s_setprio(0);
     // a chunk whose every query row is valid and at or after every key of
     // this wave needs no mask
     const bool full =
@@ -468,7 +459,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     };
     if (full) form(std::false_type());
     else form(std::true_type());
-    __builtin_amdgcn_s_setprio(1);
     // dV^T += dO^T P ; dK^T += Q^T dS  (16 queries per step)
 #pragma unroll
     for (int k2 = 0; k2 < 2; k2++)
@@ -478,7 +468,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         dkt[dt] = E::mfma32(ptile_tr<V8>(Qt + k2 * 16 * kPadPitch + 64 * dt), bd[k2], dkt[dt]);
       }
     sched_mfma_lds<16, 2, 4>();
-    __builtin_amdgcn_s_setprio(0);
     wait_vm();
     __syncthreads();
     buf ^= 1;

@@ -288,20 +288,26 @@ __global__ __launch_bounds__(512) void sfa_split_kernel(SfaParams p, int n_items
             st[kt][1] = E::mfma16(ka[kt][4], qrp[1], st[kt][1]);
           }
         }
+        // Partial tiles summed by reduce-scatter: wave (h2, qd) sums tile qd
+        // of its head group over the four quarters, S = ((p0 + p1) + p2) + p3
+        // in that order, into a slot only it read; then every wave of the
+        // group reads the four sums.
         char* xs = lds_xs + lane * 16;
 #pragma unroll
         for (int t = 0; t < 4; t++)
           *reinterpret_cast<f32x4_t*>(xs + (wid * 4 + t) * 1024) = st[t >> 1][t & 1];
         __syncthreads();
-        // S = ((p0 + p1) + p2) + p3 over the head group's quarters, in that order
-#pragma unroll
-        for (int t = 0; t < 4; t++) {
-          f32x4_t acc = *reinterpret_cast<const f32x4_t*>(xs + (h2 * 4 + t) * 1024);
+        {
+          f32x4_t acc = *reinterpret_cast<const f32x4_t*>(xs + (h2 * 4 + qd) * 1024);
 #pragma unroll
           for (int q = 1; q < 4; q++)
-            acc += *reinterpret_cast<const f32x4_t*>(xs + ((2 * q + h2) * 4 + t) * 1024);
-          st[t >> 1][t & 1] = acc;
+            acc += *reinterpret_cast<const f32x4_t*>(xs + ((2 * q + h2) * 4 + qd) * 1024);
+          *reinterpret_cast<f32x4_t*>(xs + (h2 * 4 + qd) * 1024) = acc;
         }
+        __syncthreads();
+#pragma unroll
+        for (int t = 0; t < 4; t++)
+          st[t >> 1][t & 1] = *reinterpret_cast<const f32x4_t*>(xs + (h2 * 4 + t) * 1024);
         V8 pb[2];
 #pragma unroll
         for (int hh = 0; hh < 2; hh++) {
