@@ -960,10 +960,10 @@ def ingest(d, workload):
             if fl > 0:
                 mlines.append(f"| `{k}` | {util.get(k, 0.0):.1f} | {fl / 1e9:.2f} |")
     rl = bench["roofline"]
-    cmd = (f"python3 bench.py --workload {workload} --steps {bench['steps']} "
-           f"--warmup {bench['warmup']} --cpu-seconds 0 --no-peaks")
-    pcmd = (f"python3 bench.py --workload {workload} --steps 2 --warmup 1 --cpu-seconds 0 "
-            f"--no-peaks")
+    cmd = (f"python3 bench.py --workload {workload} --also none --steps {bench['steps']} "
+           f"--warmup {bench['warmup']} --settle-seconds 0 --cpu-seconds 0 --no-peaks")
+    pcmd = (f"python3 bench.py --workload {workload} --also none --steps 2 --warmup 1 "
+            f"--settle-seconds 0 --cpu-seconds 0 --no-peaks")
     d = os.path.normpath(d)
     cdir = os.path.join(os.path.dirname(d), "copy")   # the copy calibration beside it
     out = [

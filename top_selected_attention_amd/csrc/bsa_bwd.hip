@@ -112,12 +112,12 @@ __global__ __launch_bounds__(NW * 64) void bsa_dq_kernel(BsaParams p, int qsub, 
     ke = min(min(ks + 64, (kb + 1) * p.bkv), km.len);
   };
   auto next_valid = [&](ChunkPos c) {
-    for (; c.e < e1; c = chunk_advance(c, cpb)) {
-      int ks, ke;
-      chunk_range(c, ks, ke);
-      if (ks < ke && !(p.causal && ks > row_hi - 1)) break;
+    ChunkAt a;
+    for (a.c = c; a.c.e < e1; a.c = chunk_advance(a.c, cpb)) {
+      chunk_range(a.c, a.lo, a.hi);
+      if (a.lo < a.hi && !(p.causal && a.lo > row_hi - 1)) break;
     }
-    return c;
+    return a;
   };
   // Padded K/V tiles by direct loads; a whole chunk takes a scalar base (its
   // first key row) plus per-lane offsets fixed for the walk, a ragged chunk
@@ -148,24 +148,15 @@ __global__ __launch_bounds__(NW * 64) void bsa_dq_kernel(BsaParams p, int qsub, 
     for (int j = 0; j < 16; j++) dq[dt][j] = 0.f;
   const float lneg = -lse2;
 
-  ChunkPos i = next_valid(ChunkPos{e0, 0});
-  if (i.e < e1) {
-    int ks, ke;
-    chunk_range(i, ks, ke);
-    load_chunk(ks, ke, 0);
-  }
+  ChunkAt cur = next_valid(ChunkPos{e0, 0});
+  if (cur.c.e < e1) load_chunk(cur.lo, cur.hi, 0);
   wait_vm();
   __syncthreads();
   int buf = 0;
-  while (i.e < e1) {
-    int ks, ke;
-    chunk_range(i, ks, ke);
-    const ChunkPos inext = next_valid(chunk_advance(i, cpb));
-    if (inext.e < e1) {
-      int ks2, ke2;
-      chunk_range(inext, ks2, ke2);
-      load_chunk(ks2, ke2, buf ^ 1);
-    }
+  while (cur.c.e < e1) {
+    const int ks = cur.lo, ke = cur.hi;
+    const ChunkAt nxt = next_valid(chunk_advance(cur.c, cpb));
+    if (nxt.c.e < e1) load_chunk(nxt.lo, nxt.hi, buf ^ 1);
     const char* Kr = &lds_kv[buf][0][0] + rb;
     const char* Vr = &lds_kv[buf][1][0] + rb;
     const char* Kt = &lds_kv[buf][0][0] + tb;
@@ -218,7 +209,7 @@ __global__ __launch_bounds__(NW * 64) void bsa_dq_kernel(BsaParams p, int qsub, 
     wait_vm();
     __syncthreads();
     buf ^= 1;
-    i = inext;
+    cur = nxt;
   }
 
   if (row_ok) {

@@ -326,6 +326,12 @@ struct PStage {
 struct ChunkPos {
   int e, s;
 };
+// A chunk of a walk with its row range [lo, hi), so that the range found
+// while looking for the next valid chunk is not computed again.
+struct ChunkAt {
+  ChunkPos c;
+  int lo, hi;
+};
 __device__ __forceinline__ ChunkPos chunk_advance(ChunkPos c, int per_entry) {
   if (++c.s == per_entry) {
     c.s = 0;
