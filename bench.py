@@ -161,6 +161,11 @@ def _pair_flops(mask, bq, bkv, Sq, Skv, D=128):
     return float(np.einsum("bnqk,q,k->", sel, rows, keys)) * D
 
 
+# the library's timed stages of a BSA forward (lists, attention) and backward
+# (lists, dQ, the dK/dV kernel, the reduction of split tiles' partials)
+BSA_STAGES = ["fwd_lists", "fwd_attention", "bwd_lists", "bwd_dq", "bwd_dkdv", "bwd_dkdv_reduce"]
+
+
 def bench_bsa(args):
     import torch
     import workloads as W
@@ -177,10 +182,10 @@ def bench_bsa(args):
     plan.set_dout(dod)
 
     Wm = args.warmup
-    stl, ms_step, K, ms_ev = _timed_steps(args, plan, 2, 3)
-    st = dict(zip(["fwd_lists", "fwd_attention", "bwd_lists", "bwd_dq", "bwd_dkdv"], stl))
+    stl, ms_step, K, ms_ev = _timed_steps(args, plan, 2, 4)
+    st = dict(zip(BSA_STAGES, stl))
     fwd_ms = st["fwd_lists"] + st["fwd_attention"]
-    bwd_ms = st["bwd_lists"] + st["bwd_dq"] + st["bwd_dkdv"]
+    bwd_ms = st["bwd_lists"] + st["bwd_dq"] + st["bwd_dkdv"] + st["bwd_dkdv_reduce"]
     # Per-kernel algorithmic FLOPs per launch, in units of rows*keys*D per
     # selected pair: forward 2 GEMMs (S, PV) = 4; dQ kernel S, dP, dQ = 6;
     # dK/dV kernel S, dP, dV, dK = 8 (the split recomputes S and dP).
@@ -279,10 +284,10 @@ def bench_bsa_tnd(args):
     plan = tsa.BsaPlan(qd, kd, vd, torch.from_numpy(mask).to(dev), bq, bkv, scale, 0,
                        cu_seqlens_q=cu, cu_seqlens_kv=cu)
     plan.set_dout(dod)
-    stl, ms_step, K, ms_ev = _timed_steps(args, plan, 2, 3)
-    st = dict(zip(["fwd_lists", "fwd_attention", "bwd_lists", "bwd_dq", "bwd_dkdv"], stl))
+    stl, ms_step, K, ms_ev = _timed_steps(args, plan, 2, 4)
+    st = dict(zip(BSA_STAGES, stl))
     fwd_ms = st["fwd_lists"] + st["fwd_attention"]
-    bwd_ms = st["bwd_lists"] + st["bwd_dq"] + st["bwd_dkdv"]
+    bwd_ms = st["bwd_lists"] + st["bwd_dq"] + st["bwd_dkdv"] + st["bwd_dkdv_reduce"]
     kern = {"bsa_fwd_kernel": (st["fwd_attention"], 4.0 * unit),
             "bsa_dq_kernel": (st["bwd_dq"], 6.0 * unit),
             "bsa_dkdv_kernel": (st["bwd_dkdv"], 8.0 * unit)}

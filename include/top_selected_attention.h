@@ -35,7 +35,8 @@
  *
  * Every args struct ends with reuse_lists, n_events and events.  Stages
  * that can be timed, per entry point: bsa_fwd 0 = lists, 1 = attention;
- * bsa_bwd 0 = lists, 1 = dQ (with softmax_grad), 2 = dK/dV; nsa_select_fwd
+ * bsa_bwd 0 = lists, 1 = dQ (with softmax_grad), 2 = dK/dV (the kernel), 3 = the
+ * ordered reduction of the fp32 partials of split KV tiles; nsa_select_fwd
  * 0 = lists, 1 = attention; nsa_select_bwd 0 = lists, 1 = dQ, 2 = dK/dV
  * fp32 partials (segment table + partial kernel), 3 = their reduction;
  * sfa_paged_fwd 0 = split attention, 1 = split combine.  A stage that a call

@@ -114,8 +114,8 @@ def test_bsa_backward_with_zero_rows_ignores_stale_lists():
                       out=q.data_ptr(), dout=q.data_ptr(), lse=lse.data_ptr(), dq=q.data_ptr(),
                       dk=dk.data_ptr(), dv=dv.data_ptr())
     ws = _ws(tsa.lib, tsa.lib.bsa_bwd_workspace_size, ba)
-    evs, arr = _events(3)
-    ba.reuse_lists, ba.n_events, ba.events = 1, 3, ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
+    evs, arr = _events(4)
+    ba.reuse_lists, ba.n_events, ba.events = 1, 4, ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
     A.call(tsa.lib.bsa_bwd, ctypes.byref(ba), ctypes.c_void_p(ws.data_ptr()),
            ctypes.c_size_t(ws.numel()), _stream())
     _all_recorded(evs)

@@ -547,21 +547,33 @@ static hipError_t launch_dq_t(const BsaParams& p, hipStream_t st) {
   return hipGetLastError();
 }
 
+// The dK/dV kernel and then the reduction of split items' partials, each a
+// timed stage of its own (2 and 3).
 template <class E, int NW>
-static hipError_t launch_dkdv_t(const BsaParams& p, hipStream_t st) {
+static hipError_t launch_dkdv_t(const BsaParams& p, hipStream_t st, void* const* ev, int n_ev) {
   const int ksub = (p.bkv + NW * 32 - 1) / (NW * 32);
   const int n_items = p.B * p.N2 * p.KB * ksub;
-  if (n_items == 0) return hipSuccess;
+  hipError_t e = mark_event(ev, n_ev, 2, 0, st);
   // the segment plan was made with the lists (launch_tile_order); at most
   // n_items + kBsaMaxParts segments, the surplus workgroups exit
-  if (p.am)
-    hipLaunchKernelGGL((bsa_dkdv_kernel<E, NW, true>), dim3(n_items + kBsaMaxParts), dim3(NW * 64),
-                       0, st, p, ksub, n_items);
-  else
-    hipLaunchKernelGGL((bsa_dkdv_kernel<E, NW, false>), dim3(n_items + kBsaMaxParts),
-                       dim3(NW * 64), 0, st, p, ksub, n_items);
-  hipLaunchKernelGGL((bsa_dkdv_reduce<E, NW>), dim3(n_items), dim3(256), 0, st, p, ksub, n_items);
-  return hipGetLastError();
+  if (e == hipSuccess && n_items > 0) {
+    if (p.am)
+      hipLaunchKernelGGL((bsa_dkdv_kernel<E, NW, true>), dim3(n_items + kBsaMaxParts),
+                         dim3(NW * 64), 0, st, p, ksub, n_items);
+    else
+      hipLaunchKernelGGL((bsa_dkdv_kernel<E, NW, false>), dim3(n_items + kBsaMaxParts),
+                         dim3(NW * 64), 0, st, p, ksub, n_items);
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess) e = mark_event(ev, n_ev, 2, 1, st);
+  if (e == hipSuccess) e = mark_event(ev, n_ev, 3, 0, st);
+  if (e == hipSuccess && n_items > 0) {
+    hipLaunchKernelGGL((bsa_dkdv_reduce<E, NW>), dim3(n_items), dim3(256), 0, st, p, ksub,
+                       n_items);
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess) e = mark_event(ev, n_ev, 3, 1, st);
+  return e;
 }
 
 BsaDkdvShape bsa_dkdv_shape(int B, int N1, int N2, int QB, int KB, int bkv) {
@@ -583,11 +595,10 @@ static hipError_t launch_bwd_t(const BsaParams& p, hipStream_t st, void* const* 
     e = p.bq <= 32 ? launch_dq_t<E, 1>(p, st)
                    : (p.bq <= 64 ? launch_dq_t<E, 2>(p, st) : launch_dq_t<E, 4>(p, st));
   if (e == hipSuccess) e = mark_event(ev, n_ev, 1, 1, st);
-  if (e == hipSuccess) e = mark_event(ev, n_ev, 2, 0, st);
   if (e == hipSuccess)
-    e = p.bkv <= 32 ? launch_dkdv_t<E, 1>(p, st)
-                    : (p.bkv <= 64 ? launch_dkdv_t<E, 2>(p, st) : launch_dkdv_t<E, 4>(p, st));
-  if (e == hipSuccess) e = mark_event(ev, n_ev, 2, 1, st);
+    e = p.bkv <= 32 ? launch_dkdv_t<E, 1>(p, st, ev, n_ev)
+                    : (p.bkv <= 64 ? launch_dkdv_t<E, 2>(p, st, ev, n_ev)
+                                   : launch_dkdv_t<E, 4>(p, st, ev, n_ev));
   return e;
 }
 
