@@ -165,25 +165,6 @@ __device__ __forceinline__ void g2lds16(const void* g, void* lds_base) {
       : "v"(g), "s"(l)
       : "memory");
 }
-// The same copy from a wave-uniform base plus a per-lane 32-bit byte offset
-// (the scalar-base form: the per-lane address needs no 64-bit arithmetic).
-__device__ __forceinline__ void g2lds16_so(const void* sbase, unsigned voff, void* lds_base) {
-  const unsigned l = __builtin_amdgcn_readfirstlane(
-      (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)lds_base);
-  // readfirstlane yields a signed int: each half goes back to unsigned
-  // before widening, or a low word with bit 31 set would fill the high word
-  const unsigned long long b = (unsigned long long)(uintptr_t)sbase;
-  const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)b);
-  const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)(b >> 32));
-  const unsigned long long sb = ((unsigned long long)hi << 32) | lo;
-  unsigned saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0\n\ts_nop 0"
-      : "=&s"(saved)
-      : "v"(voff), "s"(sb), "s"(l)
-      : "memory");
-}
 // Same with 4 bytes per lane (lane l's dword lands at lds_base + 4*l).
 __device__ __forceinline__ void g2lds4(const void* g, void* lds_base) {
   const unsigned l = __builtin_amdgcn_readfirstlane(
@@ -198,7 +179,10 @@ __device__ __forceinline__ void g2lds4(const void* g, void* lds_base) {
 }
 
 // Direct loads addressed by 32-bit LDS byte addresses (see lds_addr): the
-// vector-address form and the scalar-base form above.
+// vector-address form and the scalar-base form (a wave-uniform base plus a
+// per-lane 32-bit byte offset, so the per-lane address needs no 64-bit
+// arithmetic; readfirstlane yields a signed int, so each half of the base
+// goes back to unsigned before widening).
 __device__ __forceinline__ void g2lds16_at(const void* g, unsigned lds) {
   const unsigned l = __builtin_amdgcn_readfirstlane(lds);
   unsigned saved;
@@ -381,23 +365,6 @@ struct ListWindow {
     return __builtin_amdgcn_readlane(val, idx - base);
   }
 };
-
-// Stages rows [0, 64) of a 64 x 256-byte tile into swizzled LDS.  Row r of
-// the tile is the 256 bytes at gbase + row_of(r) * row_bytes (the caller
-// clamps row_of into range).  The NW waves of the workgroup split the 16
-// 1-KB slices.
-template <int NW, class RowFn>
-__device__ __forceinline__ void stage_tile64(const char* gbase, long row_bytes, char* lds_tile,
-                                             RowFn row_of) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int sub = lane >> 4, pc = lane & 15;
-#pragma unroll
-  for (int u = 0; u < 16 / NW; u++) {
-    const int inst = wid * (16 / NW) + u;
-    const int r = inst * 4 + sub;
-    g2lds16(gbase + (long)row_of(r) * row_bytes + ((pc ^ swz(r)) << 4), lds_tile + inst * 1024);
-  }
-}
 
 // 16-byte read of logical piece c of row r from a swizzled tile.
 template <typename V8>
