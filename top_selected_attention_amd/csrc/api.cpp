@@ -359,6 +359,7 @@ struct NsaWs {
   float* delta;
   int* seg_off;
   int* seg_sums;
+  int* seg_ctr;
   float* part;
   int max_segments;
 };
@@ -385,10 +386,11 @@ size_t nsa_carve(const A* a, void* ws, NsaWs* out, bool with_delta) {
   w.rhist = c.take<int>(nh);
   w.rsums = c.take<int>(w.rs.usable ? scan_sums_len(nh) : 0);
   w.bad = c.take<int>(1);
-  w.delta = with_delta ? c.take<float>((long)a->T * a->N1) : nullptr;
+  w.delta = with_delta ? c.take<float>(2L * a->T * a->N1) : nullptr;
   w.max_segments = with_delta ? nsa_max_segments(R * a->sbc, RR) : 0;
   w.seg_off = with_delta ? c.take<int>(RR + 1) : nullptr;
   w.seg_sums = with_delta ? c.take<int>(scan_sums_len(RR)) : nullptr;
+  w.seg_ctr = with_delta ? c.take<int>(1) : nullptr;
   w.part = with_delta ? c.take<float>((long)w.max_segments * a->sbs * (a->D + a->Dv)) : nullptr;
   if (out) *out = w;
   return c.off + kAlign;
@@ -1003,7 +1005,8 @@ int nsa_select_bwd(const nsa_select_bwd_args* a, void* ws, size_t ws_bytes, void
   p.row_ptr = w.row_ptr; p.col = w.col; p.rev_ptr = w.rev_ptr; p.rev = w.rev;
   p.T = a->T; p.Tk = a->Tk; p.N1 = a->N1; p.N2 = a->N2; p.G = a->N1 / a->N2; p.D = a->D;
   p.scale = a->scale;
-  p.seg_off = w.seg_off; p.seg_sums = w.seg_sums; p.part = w.part; p.max_segments = w.max_segments;
+  p.seg_off = w.seg_off; p.seg_sums = w.seg_sums; p.seg_ctr = w.seg_ctr; p.part = w.part;
+  p.max_segments = w.max_segments;
   return hip_status(launch_nsa_bwd(p, a->dtype == TSA_FP16, st, tm.ev, tm.n));
 }
 

@@ -250,6 +250,9 @@ void nsa_fwd16_kernel(NsaParams p, int n_items) {
   const long row = (long)t * p.N2 + n2;
   const int e0 = p.row_ptr[row], e1 = p.row_ptr[row + 1];
   const ShortList blocks(p.col + e0, e1 - e0);  // sbc <= 128 entries
+  // Q is taken as landed here (see the dQ kernel)
+#pragma unroll
+  for (int ks = 0; ks < 4; ks++) asm volatile("" : "+v"(qreg[ks]));
   const int sbs = g.sbs;
   const int cpb = (sbs + kChunk - 1) / kChunk;
   const float sl2 = p.scale * kLog2e;
@@ -427,7 +430,7 @@ __global__ __launch_bounds__(256) void nsa_dq_kernel(NsaParams p, int n_items) {
   acc += __shfl_xor(acc, 32);
   const float dlt = acc;
   const float lse2 = col_ok ? p.lse[qr] * kLog2e : 0.f;
-  if (col_ok && h == 0) p.delta[qr] = dlt;
+  if (col_ok && h == 0) *reinterpret_cast<float2*>(p.delta + 2 * qr) = make_float2(lse2, dlt);
 
   const long row = (long)t * p.N2 + n2;
   const int e0 = p.row_ptr[row], e1 = p.row_ptr[row + 1];
@@ -551,7 +554,12 @@ void nsa_dq16_kernel(NsaParams p, int n_items) {
   acc += __shfl_xor(acc, 32);
   const float dlt = acc;
   const float lse2 = col_ok ? p.lse[qr] * kLog2e : 0.f;
-  if (col_ok && gq == 0) p.delta[qr] = dlt;
+  if (col_ok && gq == 0) *reinterpret_cast<float2*>(p.delta + 2 * qr) = make_float2(lse2, dlt);
+  // Q and dO are taken as landed here: a first use inside the chunk loop
+  // would make the compiler wait for every load in flight there, the next
+  // chunk's included
+#pragma unroll
+  for (int ks = 0; ks < 4; ks++) asm volatile("" : "+v"(qreg[ks]), "+v"(doreg[ks]));
 
   const long row = (long)t * p.N2 + n2;
   const int e0 = p.row_ptr[row], e1 = p.row_ptr[row + 1];
@@ -667,93 +675,130 @@ void nsa_dq16_kernel(NsaParams p, int n_items) {
 // ---------------------------------------------------------------------------
 // dK / dV.  The tokens that selected a (KV head, block) -- its reverse list --
 // are cut into segments of at most kSegEntries listings, so a block that
-// thousands of tokens selected is shared by many workgroups.  A workgroup
-// walks its segments' tokens in chunks of 32 query rows (32 / G tokens x G
-// heads); each wave owns 32 of the block's keys:
+// thousands of tokens selected is shared by many workgroups.  Workgroups
+// take segments in list order from a counter.  A workgroup walks its
+// segment's tokens in chunks of 32 query rows (32 / G tokens x G heads);
+// each wave owns 32 of the block's keys:
 //   S = Q K^T, dP = dO V^T, P = exp2(S*scale*log2e - LSE2),
 //   dS = P (dP - softmax_grad), dV^T += dO^T P, dK^T += Q^T dS,
-// and writes fp32 partial dK/dV of its segment.  A reduction kernel then sums
-// each block's segments in segment order: no atomics, a fixed summation
-// order, bit-identical reruns.
+// and writes fp32 partial dK/dV of its segment into the segment's slot.  A
+// reduction kernel then sums each block's segments in segment order: no
+// atomics on the data, a fixed summation order, bit-identical reruns
+// whichever workgroup ran which segment.
 // ---------------------------------------------------------------------------
-constexpr int kSegEntries = 256;
+constexpr int kSegEntries = kNsaSegEntries;
 
 // Workgroups of the dK/dV partial kernel: about three resident per CU on
-// 256 CUs, a multiple of the 8 XCDs, never more than the segments.
+// 256 CUs, never more than the segments.
 int nsa_dkdv_grid(const NsaParams& p) {
-  const int g = std::min(kNsaDkdvMaxGrid, std::max(1, p.max_segments));
-  return 8 * ((g + 7) / 8);
+  return std::min(kNsaDkdvMaxGrid, std::max(1, p.max_segments));
 }
 
+// every list with listings has at most len / kSegEntries + 1 segments
 int nsa_max_segments(long total_entries, long nblocks) {
   return (int)(nblocks + (total_entries + kSegEntries - 1) / kSegEntries);
 }
 
-__global__ void nsa_seg_count(const int* rev_ptr, int nblocks, int* seg_cnt) {
+// Segments per list; also clears the dK/dV kernel's work counter.
+__global__ void nsa_seg_count(const int* rev_ptr, int nblocks, int* seg_cnt, int* ctr) {
   const int r = blockIdx.x * 256 + threadIdx.x;
+  if (r == 0) ctr[0] = 0;
   if (r >= nblocks) return;
   const int len = rev_ptr[r + 1] - rev_ptr[r];
-  seg_cnt[r] = max(1, (len + kSegEntries - 1) / kSegEntries);
+  seg_cnt[r] = (len + kSegEntries - 1) / kSegEntries;
 }
 
-// DQK: query/key head dim (128 or 192); 192-dim K and Q rows are staged as
-// two overlapping 256-byte tiles (bytes 0..255 and 128..383), as in the
-// forward.  The 192 variant runs one wave per SIMD (its dK accumulators take
-// 32 more registers).
+// DQK: query/key head dim (128 or 192); a 192-dim K or Q row is staged as
+// two padded tiles of 128 dims each (bytes 0..255 and 128..383 of the row),
+// as in the forward.  The 192 variant runs one wave per SIMD (its dK
+// accumulators take 32 more registers).
+//
+// Q, dO and K sit in padded LDS tiles (272-byte rows, see PStage), so every
+// operand read is a base register plus a constant.  A chunk's 32 rows are
+// gathered rows -- row k is head k % G of the chunk's token k / G -- so each
+// lane keeps, for each 1-KB slice it loads, the row's (token slot, head) and
+// its 16-byte piece, fixed for the whole kernel; per chunk a load is then
+// the token id (from LDS) times the row stride plus those constants, added
+// as a 32-bit offset to a scalar base.
 template <class E, int NW, int DQK>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DQK == 128 ? 2 : 1)))
-void nsa_dkdv_seg_kernel(NsaParams p, int nblocks, float* part) {
+void nsa_dkdv_seg_kernel(NsaParams p) {
   typedef typename E::T T;
   typedef typename E::V8 V8;
   constexpr int kQC = 32;                  // query rows per chunk
-  constexpr int kQTile = kQC * kD * 2;
-  constexpr int NKT = DQK == 128 ? 1 : 2;  // 256-byte tiles per K / Q row
-  __shared__ __attribute__((aligned(1024))) char lds_k[NKT][NW * 32 * kD * 2];
+  constexpr int kQTile = ptile_bytes(kQC);
+  constexpr int NK = NW * 32;              // keys per workgroup (the block)
+  constexpr int NKT = DQK == 128 ? 1 : 2;  // padded tiles per K / Q row
+  typedef PStage<NW, kQC> QStage;
+  constexpr int NU = QStage::NU;
+  __shared__ __attribute__((aligned(1024))) char lds_k[NKT][ptile_bytes(NK)];
   __shared__ __attribute__((aligned(1024))) char lds_q[2][NKT][kQTile];
   __shared__ __attribute__((aligned(1024))) char lds_do[2][kQTile];
-  // a direct LDS load writes all 64 lanes' dwords: rows 32..63 are never read
-  __shared__ float lds_lse[2][64];
-  __shared__ float lds_dlt[2][64];
-  __shared__ int lds_pos[2][64];
+  // per chunk row r: (LSE * log2 e, softmax_grad) at [2r], [2r + 1], loaded
+  // by one direct load of 64 lanes; the row's token position, or -1 for a
+  // padding row (always masked)
+  __shared__ float lds_ld[2][64];
+  __shared__ int lds_pos[2][kQC];
   __shared__ int lds_tok[kSegEntries];  // the segment's token ids
 
   const NsaGeom& g = p.g;
-  const int* seg_off = p.seg_off;
-  // Segments are dealt round-robin (workgroup w takes w, w + grid, ...), so
-  // all workgroups move through the (KV head, sequence, block) order
-  // together: the Q and dO rows in use at any time are those of one stretch
-  // of sequences, which stay in MALL, rather than of every sequence and head
-  // at once.
-  const int w = blockIdx.x;
-  const int nseg = seg_off[nblocks];
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  // the next segment from the counter, or -1 when all are taken
+  __shared__ int s_next;
+  const int nblocks = p.N2 * g.NB, nseg = min(p.seg_off[nblocks], p.max_segments);
+  auto next_segment = [&]() -> int {
+    if (threadIdx.x == 0) s_next = atomicAdd(p.seg_ctr, 1);
+    __syncthreads();
+    const int k = s_next;
+    __syncthreads();
+    return k < nseg ? k : -1;
+  };
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6) & (NW - 1);  // wave-uniform
   const int l32 = lane & 31, h = lane >> 5;
   const int G = p.G;
   const int tpc = max(1, kQC / G);  // tokens per chunk (G <= 32)
   const int sbs = g.sbs;
   const float sl2 = p.scale * kLog2e;
-  // chunk row -> (token of the chunk, head): shifts when G is a power of two
-  const bool gpow2 = (G & (G - 1)) == 0;
-  const int gsh = __builtin_ctz(G);
-  auto div_g = [&](int x, int& qq, int& rr) {
-    if (gpow2) {
-      qq = x >> gsh;
-      rr = x & (G - 1);
-    } else {
-      qq = x / G;
-      rr = x - qq * G;
-    }
-  };
+  // byte strides of a (token, head) row of Q and dO: row t * N1 + n1 of
+  // T * N1 rows, each offset below 2^32 (T * N1 * D fits 31 bits)
+  constexpr unsigned qstride = DQK * 2, dstride = kDv * 2;
 
-  for (int sg = w; sg < nseg; sg += gridDim.x) {
-    // segment -> block (largest r with seg_off[r] <= sg)
-    int lo = 0, hi = nblocks - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (seg_off[mid] <= sg) lo = mid; else hi = mid - 1;
+  // This lane's rows of the chunk tiles, fixed for the kernel and packed in
+  // one register each: for slice u * NW + wid, bits 0-5 hold the row's token
+  // slot + 1 (0: a row past the chunk's tpc * G), bits 8-12 its head, bits
+  // 16-19 its 16-byte piece; the same for the LSE / softmax_grad load (wave
+  // 0), row lane / 2.
+  auto rowcode = [&](int k, int pc) {
+    const bool row_ok = k < tpc * G;
+    return (row_ok ? k / G + 1 : 0) | ((row_ok ? k % G : G - 1) << 8) | (pc << 16);
+  };
+  int rcode[NU];
+#pragma unroll
+  for (int u = 0; u < NU; u++) {
+    int k, pc;
+    pslot(1024 * (u * NW + wid) + 16 * lane, kQC, k, pc);
+    rcode[u] = rowcode(k, pc);
+  }
+  const int lcode = rowcode(lane >> 1, 0);
+
+  // Per-lane bases of the operand reads: Q and dO rows l32, the wave's K
+  // rows 32*wid + l32 (pieces 2*ds + h at +32*ds); dO^T and Q^T by transpose
+  // reads.
+  const unsigned rb = prow_base(lane), tb = ptr_base(lane);
+  const unsigned lq0 = lds_addr(&lds_q[0][0][0]), ld0 = lds_addr(&lds_do[0][0]);
+
+  for (int sg = next_segment(); sg >= 0; sg = next_segment()) {
+    // segment -> list (largest r with seg_off[r] <= sg) and its listings
+    int r = 0;
+    {
+      int hi = nblocks - 1;
+      while (r < hi) {
+        const int mid = (r + hi + 1) >> 1;
+        if (p.seg_off[mid] <= sg) r = mid; else hi = mid - 1;
+      }
     }
-    const int r = lo;
-    const int k = sg - seg_off[r];
+    const int e0 = p.rev_ptr[r] + (sg - p.seg_off[r]) * kSegEntries;
+    const int e1 = min(e0 + kSegEntries, p.rev_ptr[r + 1]);
     const int n2 = r / g.NB, gb = r % g.NB;
     const int b = seq_of_dev(g.blk_off, g.B, gb);
     const int blk = gb - g.blk_off[b];
@@ -762,23 +807,20 @@ void nsa_dkdv_seg_kernel(NsaParams p, int nblocks, float* part) {
     const int key_lo = blk * sbs;
     const int key_hi = min((blk + 1) * sbs, skv);
     const int wkey0 = key_lo + wid * 32;
-    const int e0 = p.rev_ptr[r] + k * kSegEntries;
-    const int e1 = min(e0 + kSegEntries, p.rev_ptr[r + 1]);
+    const int n2G = n2 * G;
 
-    // K rows of the block into LDS (rows past key_hi re-read the last key);
-    // V rows of this wave's keys as the B operand of dP in registers
+    // K rows of the block into padded tiles (rows past key_hi re-read the
+    // last key); V rows of this wave's keys as the B operand of dP in
+    // registers
     {
-      const int sub = lane >> 4, pc = lane & 15;
+      const char* krow0 = (const char*)((const T*)p.k + ((long)(kv0 + key_lo) * p.N2 + n2) * DQK);
+      PStage<NW, NK> kst;
+      int ln = lane;
+      asm volatile("" : "+v"(ln));  // slice offsets formed per segment, not kept
 #pragma unroll
-      for (int u = 0; u < 8; u++) {
-        const int inst = wid * 8 + u;
-        const int rr = inst * 4 + sub;
-        const long key = kv0 + min(key_lo + rr, key_hi - 1);
-        const char* krow = (const char*)((const T*)p.k + (key * p.N2 + n2) * DQK);
-#pragma unroll
-        for (int kt = 0; kt < NKT; kt++)
-          g2lds16(krow + 128 * kt + ((pc ^ swz(rr)) << 4), lds_k[kt] + inst * 1024);
-      }
+      for (int kt = 0; kt < NKT; kt++)
+        kst.ragged(krow0 + 128 * kt, (long)p.N2 * DQK * 2, key_hi - 1 - key_lo,
+                   lds_addr(lds_k[kt]), wid, ln);
     }
     V8 vreg[kDv / 16];
     {
@@ -795,47 +837,46 @@ void nsa_dkdv_seg_kernel(NsaParams p, int nblocks, float* part) {
     for (int x = tid; x < e1 - e0; x += NW * 64) lds_tok[x] = p.rev[e0 + x];
     __syncthreads();
 
-    // chunk row rr -> (entry c*tpc + rr/G of the segment, head rr%G); rows
-    // past the chunk's tokens re-read its last valid row and are masked.
-    // The token ids of all of a wave's rows are read from LDS first, then
-    // the direct loads are issued.
+    // Chunk c: entries c*tpc .. of the segment; rows of tokens past its nt
+    // re-read its last token's last head and are masked by position -1.
     auto load_chunk = [&](int c, int buf) {
-      int ln = lane;
-      asm volatile("" : "+v"(ln));
-      const int sub = ln >> 4, pc = ln & 15;
       const int nt = min(tpc, e1 - e0 - c * tpc);
-      constexpr int U = 8 / NW;
-      int tok[U], gh[U];
+      const int* tk = lds_tok + c * tpc;
+      const unsigned lq = lq0 + buf * (NKT * kQTile), ld = ld0 + buf * kQTile;
+      // row of a code: its token (the chunk's last for a row past nt) and
+      // head (the last for such a row).  The code passes through an empty
+      // asm so that its fields are unpacked here, per chunk, rather than
+      // hoisted out of the loop into registers of their own.
+      auto row_of = [&](int code, int& t) {
+        asm volatile("" : "+v"(code));
+        const int tq1 = code & 63;
+        const bool ok = tq1 > 0 && tq1 <= nt;
+        t = tk[ok ? tq1 - 1 : nt - 1];
+        return (unsigned)(t * p.N1 + n2G) + (unsigned)(ok ? (code >> 8) & 31 : G - 1);
+      };
 #pragma unroll
-      for (int u = 0; u < U; u++) {
-        const int rr = (wid * U + u) * 4 + sub;
-        int tq, tr;
-        div_g(rr, tq, tr);
-        gh[u] = (tq < nt && rr < tpc * G) ? tr : G - 1;
-        tok[u] = lds_tok[c * tpc + min(tq, nt - 1)];
-      }
+      for (int u = 0; u < NU; u++) {
+        const int sl = u * NW + wid;
+        if (sl < QStage::S && (QStage::kTail == 64 || sl < QStage::S - 1 || lane < QStage::kTail)) {
+          int t, code = rcode[u];
+          const unsigned row = row_of(code, t);
+          asm volatile("" : "+v"(code));
+          const unsigned pcb = (unsigned)(code >> 12) & 0xf0u;
 #pragma unroll
-      for (int u = 0; u < U; u++) {
-        const int inst = wid * U + u;
-        const int rr = inst * 4 + sub;
-        const long qrw = (long)tok[u] * p.N1 + n2 * G + gh[u];
-        const char* qrow = (const char*)((const T*)p.q + qrw * DQK);
-#pragma unroll
-        for (int kt = 0; kt < NKT; kt++)
-          g2lds16(qrow + 128 * kt + ((pc ^ swz(rr)) << 4), lds_q[buf][kt] + inst * 1024);
-        g2lds16((const char*)((const T*)p.dout + qrw * kDv) + ((pc ^ swz(rr)) << 4),
-                lds_do[buf] + inst * 1024);
+          for (int kt = 0; kt < NKT; kt++)
+            g2lds16_so_at(p.q, row * qstride + 128 * kt + pcb, lq + kt * kQTile + 1024 * sl);
+          g2lds16_so_at(p.dout, row * dstride + pcb, ld + 1024 * sl);
+        }
       }
       if (wid == 0) {
-        int tq, tr;
-        div_g(ln & 31, tq, tr);
-        const bool valid = ln < kQC && tq < nt && ln < tpc * G;
-        const int t = lds_tok[c * tpc + min(tq, nt - 1)];
-        const long qrw = (long)t * p.N1 + n2 * G + (valid ? tr : G - 1);
-        g2lds4(p.lse + qrw, lds_lse[buf]);
-        g2lds4(p.delta + qrw, lds_dlt[buf]);
-        // position of the row's token, or -1 for padding rows (always masked)
-        lds_pos[buf][ln] = valid ? t - q0 : -1;
+        int t, code = lcode;
+        const unsigned row = row_of(code, t);
+        asm volatile("" : "+v"(code));
+        const int tq1 = code & 63;
+        g2lds4_so_at(p.delta, (2 * row + (lane & 1)) * 4, lds_addr(lds_ld[buf]));
+        int ln = lane;
+        asm volatile("" : "+v"(ln));  // the address is formed here, not kept
+        if (!(ln & 1)) lds_pos[buf][ln >> 1] = tq1 > 0 && tq1 <= nt ? t - q0 : -1;
       }
     };
 
@@ -843,63 +884,67 @@ void nsa_dkdv_seg_kernel(NsaParams p, int nblocks, float* part) {
 #pragma unroll
     for (int dt = 0; dt < kDv / 32; dt++)
 #pragma unroll
-      for (int j = 0; j < 16; j++) dvt[dt][j] = 0.f;
+      for (int jj = 0; jj < 16; jj++) dvt[dt][jj] = 0.f;
 #pragma unroll
     for (int dt = 0; dt < DQK / 32; dt++)
 #pragma unroll
-      for (int j = 0; j < 16; j++) dkt[dt][j] = 0.f;
+      for (int jj = 0; jj < 16; jj++) dkt[dt][jj] = 0.f;
+
+    const char* Kr = lds_k[0] + wid * 32 * kPadPitch + rb;
+    const char* Kr2 = lds_k[NKT - 1] + wid * 32 * kPadPitch + rb;  // dims 64..191 (DQK = 192)
+    const int mykey = wkey0 + l32;
+    const int need = g.causal ? mykey : 0;
+    const bool key_ok = mykey < key_hi;
 
     if (nchunks > 0) load_chunk(0, 0);
     wait_vm();
+    // the V rows are taken as landed here: otherwise the compiler waits for
+    // them inside the loop, which also waits for the next chunk's loads
+#pragma unroll
+    for (int ds = 0; ds < kDv / 16; ds++) asm volatile("" : "+v"(vreg[ds]));
     __syncthreads();
     int buf = 0;
     for (int c = 0; c < nchunks; c++) {
       if (c + 1 < nchunks) load_chunk(c + 1, buf ^ 1);
-      // lane terms of this iteration from an opaque lane id (not kept, and
-      // spilled, across iterations)
-      int ln = lane;
-      asm volatile("" : "+v"(ln));
-      const int l32i = ln & 31, hi2 = ln >> 5;
-      const char* Qb = lds_q[buf][0];
-      const char* Qb2 = lds_q[buf][NKT - 1];  // dims 64..191 (DQK = 192)
-      const char* Db = lds_do[buf];
+      const char* Qr = &lds_q[buf][0][0] + rb;
+      const char* Qr2 = &lds_q[buf][NKT - 1][0] + rb;
+      const char* Dr = &lds_do[buf][0] + rb;
+      const char* Qt = &lds_q[buf][0][0] + tb;
+      const char* Qt2 = &lds_q[buf][NKT - 1][0] + tb;
+      const char* Dt = &lds_do[buf][0] + tb;
       // S = Q K^T and dP = dO V^T: 32 rows x this wave's 32 keys
       f32x16 sc, dp;
 #pragma unroll
-      for (int j = 0; j < 16; j++) sc[j] = dp[j] = 0.f;
+      for (int jj = 0; jj < 16; jj++) sc[jj] = dp[jj] = 0.f;
 #pragma unroll
       for (int ds = 0; ds < 8; ds++) {
-        sc = E::mfma32(tile_read16<V8>(Qb, l32i, 2 * ds + hi2),
-                       tile_read16<V8>(lds_k[0], wid * 32 + l32i, 2 * ds + hi2), sc);
-        dp = E::mfma32(tile_read16<V8>(Db, l32i, 2 * ds + hi2), vreg[ds], dp);
+        sc = E::mfma32(lds_read16<V8>(Qr + 32 * ds), lds_read16<V8>(Kr + 32 * ds), sc);
+        dp = E::mfma32(lds_read16<V8>(Dr + 32 * ds), vreg[ds], dp);
       }
 #pragma unroll
       for (int ds = 8; ds < DQK / 16; ds++)
-        sc = E::mfma32(tile_read16<V8>(Qb2, l32i, 2 * (ds - 4) + hi2),
-                       tile_read16<V8>(lds_k[NKT - 1], wid * 32 + l32i, 2 * (ds - 4) + hi2), sc);
-      // element j of a lane is row 8*(j/4) + 4*h + j%4 of the chunk, column key l32
-      const int mykey = wkey0 + l32i;
-      const int need = g.causal ? mykey : 0;
-      const bool key_ok = mykey < key_hi;
+        sc = E::mfma32(lds_read16<V8>(Qr2 + 32 * (ds - 4)), lds_read16<V8>(Kr2 + 32 * (ds - 4)),
+                       sc);
+      // element jj of a lane is row 8*(jj/4) + 4*h + jj%4 of the chunk, column key l32
       V8 bp[2], bd[2];
 #pragma unroll
       for (int j4 = 0; j4 < 4; j4++) {
-        const int rbase = 8 * j4 + 4 * hi2;
-        const float4 lse4 = *reinterpret_cast<const float4*>(&lds_lse[buf][rbase]);
-        const float4 dl4 = *reinterpret_cast<const float4*>(&lds_dlt[buf][rbase]);
+        const int rbase = 8 * j4 + 4 * h;
+        const float4 a4 = *reinterpret_cast<const float4*>(&lds_ld[buf][2 * rbase]);
+        const float4 b4 = *reinterpret_cast<const float4*>(&lds_ld[buf][2 * rbase + 4]);
         const int4 ps4 = *reinterpret_cast<const int4*>(&lds_pos[buf][rbase]);
-        const float lv[4] = {lse4.x, lse4.y, lse4.z, lse4.w};
-        const float dv[4] = {dl4.x, dl4.y, dl4.z, dl4.w};
+        const float lv[4] = {a4.x, a4.z, b4.x, b4.z};
+        const float dv[4] = {a4.y, a4.w, b4.y, b4.w};
         const int pv4[4] = {ps4.x, ps4.y, ps4.z, ps4.w};
 #pragma unroll
         for (int jj = 0; jj < 4; jj++) {
-          const int j = 4 * j4 + jj;
+          const int e = 4 * j4 + jj;
           // a valid row (pos >= 0) at or after this key (causal) keeps it
           const bool ok = key_ok && pv4[jj] >= need;
-          float pr = fast_exp2(__builtin_fmaf(sc[j], sl2, -lv[jj] * kLog2e));
+          float pr = fast_exp2(__builtin_fmaf(sc[e], sl2, -lv[jj]));
           pr = ok ? pr : 0.f;
-          bp[j >> 3][j & 7] = E::from_f32(pr);
-          bd[j >> 3][j & 7] = E::from_f32(pr * (dp[j] - dv[jj]));
+          bp[e >> 3][e & 7] = E::from_f32(pr);
+          bd[e >> 3][e & 7] = E::from_f32(pr * (dp[e] - dv[jj]));
         }
       }
       // dV^T += dO^T P ; dK^T += Q^T dS  (16 rows per step)
@@ -907,12 +952,13 @@ void nsa_dkdv_seg_kernel(NsaParams p, int nblocks, float* part) {
       for (int k2 = 0; k2 < 2; k2++) {
 #pragma unroll
         for (int dt = 0; dt < 4; dt++) {
-          dvt[dt] = E::mfma32(tile_read_tr<V8>(Db, k2, dt, ln), bp[k2], dvt[dt]);
-          dkt[dt] = E::mfma32(tile_read_tr<V8>(Qb, k2, dt, ln), bd[k2], dkt[dt]);
+          dvt[dt] = E::mfma32(ptile_tr<V8>(Dt + k2 * 16 * kPadPitch + 64 * dt), bp[k2], dvt[dt]);
+          dkt[dt] = E::mfma32(ptile_tr<V8>(Qt + k2 * 16 * kPadPitch + 64 * dt), bd[k2], dkt[dt]);
         }
 #pragma unroll
         for (int dt = 4; dt < DQK / 32; dt++)
-          dkt[dt] = E::mfma32(tile_read_tr<V8>(Qb2, k2, dt - 2, ln), bd[k2], dkt[dt]);
+          dkt[dt] = E::mfma32(ptile_tr<V8>(Qt2 + k2 * 16 * kPadPitch + 64 * (dt - 2)), bd[k2],
+                              dkt[dt]);
       }
       wait_vm();
       __syncthreads();
@@ -920,9 +966,8 @@ void nsa_dkdv_seg_kernel(NsaParams p, int nblocks, float* part) {
     }
 
     // fp32 partials of this segment: [segment][dK: key][DQK], then [dV: key][kDv]
-    const int mykey = wkey0 + l32;
-    if (mykey < key_hi) {
-      float* sb = part + (long)sg * sbs * (DQK + kDv);
+    if (key_ok) {
+      float* sb = p.part + (long)sg * sbs * (DQK + kDv);
       float* pk = sb + (long)(mykey - key_lo) * DQK;
       float* pv = sb + (long)sbs * DQK + (long)(mykey - key_lo) * kDv;
 #pragma unroll
@@ -949,8 +994,8 @@ void nsa_dkdv_seg_kernel(NsaParams p, int nblocks, float* part) {
 // dK = scale * sum of a block's segment partials, dV = their sum, in segment
 // order; one thread per (block, key, 4 columns).
 template <class E, int DQK>
-__global__ __launch_bounds__(256) void nsa_dkdv_reduce(NsaParams p, const int* seg_off, int nblocks,
-                                                       const float* part) {
+__global__ __launch_bounds__(256) void nsa_dkdv_reduce(NsaParams p, const int* seg_off,
+                                                       int nblocks, const float* part) {
   const NsaGeom& g = p.g;
   const int sbs = g.sbs;
   const long i = (long)blockIdx.x * 256 + threadIdx.x;
@@ -1010,16 +1055,13 @@ hipError_t launch_nsa_fwd(const NsaParams& p, int fp16, hipStream_t st) {
 }
 
 template <class E, int DQK>
-static hipError_t dkdv_launch(const NsaParams& p, int nw, int grid, int nb, hipStream_t st) {
+static hipError_t dkdv_launch(const NsaParams& p, int nw, int grid, hipStream_t st) {
   if (nw <= 1)
-    hipLaunchKernelGGL((nsa_dkdv_seg_kernel<E, 1, DQK>), dim3(grid), dim3(64), 0, st, p, nb,
-                       p.part);
+    hipLaunchKernelGGL((nsa_dkdv_seg_kernel<E, 1, DQK>), dim3(grid), dim3(64), 0, st, p);
   else if (nw <= 2)
-    hipLaunchKernelGGL((nsa_dkdv_seg_kernel<E, 2, DQK>), dim3(grid), dim3(128), 0, st, p, nb,
-                       p.part);
+    hipLaunchKernelGGL((nsa_dkdv_seg_kernel<E, 2, DQK>), dim3(grid), dim3(128), 0, st, p);
   else
-    hipLaunchKernelGGL((nsa_dkdv_seg_kernel<E, 4, DQK>), dim3(grid), dim3(256), 0, st, p, nb,
-                       p.part);
+    hipLaunchKernelGGL((nsa_dkdv_seg_kernel<E, 4, DQK>), dim3(grid), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
@@ -1044,18 +1086,19 @@ static hipError_t bwd_t(const NsaParams& p, hipStream_t st, void* const* ev, int
   if (e == hipSuccess) e = mark_event(ev, n_ev, 2, 0, st);
   const int nb = p.N2 * p.g.NB;
   if (e == hipSuccess && nb > 0) {
-    // segment table: counts, then their exclusive scan (total at the end)
+    // segments per list, then their exclusive scan (total at the end)
     hipLaunchKernelGGL(nsa_seg_count, dim3((nb + 255) / 256), dim3(256), 0, st, p.rev_ptr, nb,
-                       p.seg_off);
-    e = exclusive_scan_total(p.seg_off, nb, p.seg_sums, st);
+                       p.seg_off, p.seg_ctr);
+    e = hipGetLastError();
+    if (e == hipSuccess) e = exclusive_scan_total(p.seg_off, nb, p.seg_sums, st);
   }
   if (e == hipSuccess && nb > 0) {
     const int nw = (p.g.sbs + 31) / 32;  // 1..4 waves, 32 keys each
     const int grid = nsa_dkdv_grid(p);
     if (p.D == 192)
-      e = dkdv_launch<E, 192>(p, nw, grid, nb, st);
+      e = dkdv_launch<E, 192>(p, nw, grid, st);
     else
-      e = dkdv_launch<E, 128>(p, nw, grid, nb, st);
+      e = dkdv_launch<E, 128>(p, nw, grid, st);
   }
   if (e == hipSuccess) e = mark_event(ev, n_ev, 2, 1, st);
   if (e == hipSuccess) e = mark_event(ev, n_ev, 3, 0, st);

@@ -207,6 +207,21 @@ __device__ __forceinline__ void g2lds16_so_at(const void* sbase, unsigned voff, 
       : "v"(voff), "s"(sb), "s"(l)
       : "memory");
 }
+// 4 bytes per lane from a wave-uniform base plus a per-lane 32-bit byte offset.
+__device__ __forceinline__ void g2lds4_so_at(const void* sbase, unsigned voff, unsigned lds) {
+  const unsigned l = __builtin_amdgcn_readfirstlane(lds);
+  const unsigned long long b = (unsigned long long)(uintptr_t)sbase;
+  const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)b);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)(b >> 32));
+  const unsigned long long sb = ((unsigned long long)hi << 32) | lo;
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
+      "global_load_lds_dword %1, %2\n\ts_mov_b32 m0, %0\n\ts_nop 0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(sb), "s"(l)
+      : "memory");
+}
 // LDS byte address of a __shared__ object (a compile-time constant for a
 // __shared__ array, so arithmetic on it stays in scalar registers).
 __device__ __forceinline__ unsigned lds_addr(const void* p) {

@@ -151,7 +151,7 @@ struct NsaParams {
   void* dk;
   void* dv;
   float* lse;
-  float* delta;
+  float* delta;       // backward: per row {LSE * log2 e, rowsum(dO * O)}, fp32 [T, N1, 2]
   const int* row_ptr;
   const int* col;
   const int* rev_ptr;
@@ -159,15 +159,19 @@ struct NsaParams {
   NsaGeom g;
   int T, Tk, N1, N2, G, D;  // D: query/key head dim (128 or 192); values are 128 wide
   float scale;
-  // backward dK/dV segments (workspace)
-  int* seg_off;        // [N2*NB + 1] exclusive scan of segments per block
+  // backward dK/dV segments (workspace): the reverse list of (KV head,
+  // block) r is cut into seg_off[r+1] - seg_off[r] segments of at most
+  // kNsaSegEntries listings; segment j writes fp32 partials into slot j.
+  int* seg_off;        // [N2*NB + 1] exclusive scan of segments per list, then the total
   int* seg_sums;       // scan scratch
+  int* seg_ctr;        // [1] segments taken by the dK/dV workgroups
   float* part;         // [max_segments][sbs*D (dK) + sbs*128 (dV)] fp32 partials
   int max_segments;
 };
 
-int nsa_max_segments(long total_entries, long nblocks);
+constexpr int kNsaSegEntries = 256;  // reverse-list listings per dK/dV segment at most
 constexpr int kNsaDkdvMaxGrid = 768;
+int nsa_max_segments(long total_entries, long nblocks);
 int nsa_dkdv_grid(const NsaParams& p);
 
 hipError_t launch_nsa_fwd(const NsaParams& p, int fp16, hipStream_t st);
