@@ -925,6 +925,15 @@ void nsa_dkdv_seg_kernel(NsaParams p) {
       for (int ds = 8; ds < DQK / 16; ds++)
         sc = E::mfma32(lds_read16<V8>(Qr2 + 32 * (ds - 4)), lds_read16<V8>(Kr2 + 32 * (ds - 4)),
                        sc);
+      if constexpr (DQK == 128) {
+        // three LDS reads feed two MFMAs per step
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+#pragma unroll
+        for (int u = 0; u < 8; u++) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+        }
+      }
       // element jj of a lane is row 8*(jj/4) + 4*h + jj%4 of the chunk, column key l32
       V8 bp[2], bd[2];
 #pragma unroll
