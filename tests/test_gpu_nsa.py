@@ -315,3 +315,42 @@ def test_unselected_block_is_never_read():
         assert torch.equal(r1[i], r2[i])
     assert torch.equal(r1[3][:, 1 - n2], r2[3][:, 1 - n2])
     assert (r2[3][rows, n2] == 0).all() and (r2[4][rows, n2] == 0).all()
+
+
+@pytest.mark.parametrize("N1,N2,sbs,sbc", [(32, 2, 32, 3), (8, 2, 16, 4), (4, 4, 48, 2)])
+@pytest.mark.parametrize("mode", [0, 2])
+def test_ragged_token_groups(N1, N2, sbs, sbc, mode):
+    """Query sequences shorter than their key sequences and not a multiple of
+    16 tokens (the forward and dQ work on runs of 16 consecutive tokens, so
+    these end in partial runs), one query sequence with no tokens, and a
+    block listed twice by one token."""
+    kvlens = [(sbc + 1) * sbs, (sbc + 3) * sbs, sbc * sbs, (sbc + 2) * sbs]
+    qlens = [kvlens[0] - 5, 37, 0, 2 * sbs + 3]
+    rng = np.random.default_rng(7)
+    full = W.nsa_topk_causal(rng, kvlens, N2, sbs, sbc)
+    kcu = np.concatenate([[0], np.cumsum(kvlens)]).astype(np.int32)
+    qcu = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    topk = np.concatenate([full[kcu[b]:kcu[b] + qlens[b]] for b in range(4)], axis=0)
+    topk = np.ascontiguousarray(topk)
+    topk[20, 1, 1] = topk[20, 1, 0]
+    T, Tk = int(qcu[-1]), int(kcu[-1])
+    q = W.normal((T, N1, 128), 131)
+    k = W.normal((Tk, N2, 128), 132)
+    v = W.normal((Tk, N2, 128), 133)
+    do = W.normal((T, N1, 128), 134)
+    scale = 1 / math.sqrt(128)
+    tsa = _tsa()
+    dev = torch.device("cuda")
+    plan = tsa.NsaPlan(q.to(dev), k.to(dev), v.to(dev), torch.from_numpy(topk).to(dev), qcu, kcu,
+                       sbs, scale, mode)
+    out, lse = plan.fwd()
+    dq, dk, dv = plan.bwd(do.to(dev))
+    torch.cuda.synchronize()
+    ro, rl = oracle.nsa_fwd(_np(q), _np(k), _np(v), topk, qcu, kcu, sbs, scale, mode)
+    _close(out, ro, OUT_TOL, "out")
+    _lse_close(lse, rl)
+    rdq, rdk, rdv = oracle.nsa_bwd(_np(q), _np(k), _np(v), _np(out), _np(do), topk, qcu, kcu, sbs,
+                                   scale, mode)
+    _close(dq, rdq, GRAD_TOL, "dq")
+    _close(dk, rdk, GRAD_TOL, "dk")
+    _close(dv, rdv, GRAD_TOL, "dv")

@@ -341,8 +341,22 @@ int nsa_blocks_total(const int32_t* ck, int B, int sbs) {
   return (int)nb;
 }
 
+// The token-group forward and dQ kernels take head groups of up to 16 query
+// heads of 128 dims (values 128); other shapes use the per-token kernels.
+template <class A>
+bool nsa_grouped(const A* a) {
+  return a->N2 > 0 && a->N1 / a->N2 <= 16 && a->D == 128 && a->Dv == 128;
+}
+// Token groups per KV head: sum over sequences of ceil(Sq_b / kNsaGroup).
+template <class A>
+long nsa_groups_total(const A* a) {
+  long ng = 0;
+  for (int b = 0; b < a->B; b++) ng += cdiv((long)a->cu_seqlens_q[b + 1] - a->cu_seqlens_q[b], kNsaGroup);
+  return ng;
+}
+
 struct NsaWs {
-  int* meta;     // cu_q [B+1], cu_kv [B+1], blk_off [B+1]
+  int* meta;     // cu_q [B+1], cu_kv [B+1], blk_off [B+1], group offsets [B+1]
   int* cnt;
   int* sums;
   int* row_ptr;
@@ -362,6 +376,7 @@ struct NsaWs {
   int* seg_ctr;
   float* part;
   int max_segments;
+  NsaGroups grp;
 };
 
 template <class A>
@@ -371,7 +386,7 @@ size_t nsa_carve(const A* a, void* ws, NsaWs* out, bool with_delta) {
   const long RR = (long)a->N2 * NB;
   Carver c(ws);
   NsaWs w;
-  w.meta = c.take<int>(3 * (a->B + 1));
+  w.meta = c.take<int>(4 * (a->B + 1));
   w.cnt = c.take<int>(R);
   w.sums = c.take<int>(scan_sums_len(R > RR ? R : RR));
   w.row_ptr = c.take<int>(R + 1);
@@ -386,6 +401,17 @@ size_t nsa_carve(const A* a, void* ws, NsaWs* out, bool with_delta) {
   w.rhist = c.take<int>(nh);
   w.rsums = c.take<int>(w.rs.usable ? scan_sums_len(nh) : 0);
   w.bad = c.take<int>(1);
+  // the group lists precede the backward-only buffers, so that a forward and
+  // a backward carving one workspace place them alike
+  std::memset(&w.grp, 0, sizeof(w.grp));
+  if (nsa_grouped(a)) {
+    const long units = (long)a->N2 * nsa_groups_total(a);
+    w.grp.NG = (int)nsa_groups_total(a);
+    w.grp.cap = kNsaGroup * a->sbc * (int)cdiv(a->sbs, kNsaGroupChunk);
+    w.grp.gcu = w.meta + 3 * (a->B + 1);
+    w.grp.cnt = c.take<int>(units);
+    w.grp.ent = c.take<int>(units * w.grp.cap * 2);
+  }
   w.delta = with_delta ? c.take<float>(2L * a->T * a->N1) : nullptr;
   w.max_segments = with_delta ? nsa_max_segments(R * a->sbc, RR) : 0;
   w.seg_off = with_delta ? c.take<int>(RR + 1) : nullptr;
@@ -404,17 +430,21 @@ void nsa_geom(const A* a, const NsaWs& w, NsaGeom* g);
 template <class A>
 int nsa_setup(const A* a, const NsaWs& w, NsaGeom* g, hipStream_t st) {
   const int n = a->B + 1;
-  int* host = new int[3 * n];
+  int* host = new int[4 * n];
   host[0 * n] = 0;
   for (int b = 0; b < n; b++) {
     host[0 * n + b] = a->cu_seqlens_q[b];
     host[1 * n + b] = a->cu_seqlens_kv[b];
   }
   host[2 * n] = 0;
-  for (int b = 0; b < a->B; b++)
+  host[3 * n] = 0;
+  for (int b = 0; b < a->B; b++) {
     host[2 * n + b + 1] =
         host[2 * n + b] + (int)cdiv((long)a->cu_seqlens_kv[b + 1] - a->cu_seqlens_kv[b], a->sbs);
-  hipError_t e = hipMemcpyAsync(w.meta, host, sizeof(int) * 3 * n, hipMemcpyHostToDevice, st);
+    host[3 * n + b + 1] =
+        host[3 * n + b] + (int)cdiv((long)a->cu_seqlens_q[b + 1] - a->cu_seqlens_q[b], kNsaGroup);
+  }
+  hipError_t e = hipMemcpyAsync(w.meta, host, sizeof(int) * 4 * n, hipMemcpyHostToDevice, st);
   // the copy from pageable memory is staged before hipMemcpyAsync returns
   delete[] host;
   if (e != hipSuccess) return TSA_ERR_HIP;
@@ -454,6 +484,8 @@ int nsa_lists(const A* a, const NsaWs& w, const NsaGeom& g, int parts, hipStream
   hipError_t e = hipSuccess;
   if (parts & kNsaForward)
     e = launch_nsa_forward_lists(a->topk, g, w.cnt, w.sums, w.row_ptr, w.col, w.ekey, w.etok, st);
+  if (e == hipSuccess && (parts & kNsaForward) && w.grp.NG > 0)
+    e = launch_nsa_group_lists(g, w.row_ptr, w.col, w.grp, st);
   if (e == hipSuccess && (parts & kNsaReverse))
     e = launch_nsa_reverse_lists(g, w.row_ptr, w.col, w.sums, w.rcnt, w.rev_ptr, w.rev, w.ekey,
                                  w.etok, w.rs, w.rhist, w.rsums, st);
@@ -950,6 +982,7 @@ int nsa_select_fwd(const nsa_select_fwd_args* a, void* ws, size_t ws_bytes, void
   p.row_ptr = w.row_ptr; p.col = w.col; p.rev_ptr = w.rev_ptr; p.rev = w.rev;
   p.T = a->T; p.Tk = a->Tk; p.N1 = a->N1; p.N2 = a->N2; p.G = a->N1 / a->N2; p.D = a->D;
   p.scale = a->scale;
+  p.grp = w.grp;
   hipError_t e = tm.mark(1, 0);
   if (e == hipSuccess) e = launch_nsa_fwd(p, a->dtype == TSA_FP16, st);
   if (e == hipSuccess) e = tm.mark(1, 1);
@@ -1007,6 +1040,7 @@ int nsa_select_bwd(const nsa_select_bwd_args* a, void* ws, size_t ws_bytes, void
   p.scale = a->scale;
   p.seg_off = w.seg_off; p.seg_sums = w.seg_sums; p.seg_ctr = w.seg_ctr; p.part = w.part;
   p.max_segments = w.max_segments;
+  p.grp = w.grp;
   return hip_status(launch_nsa_bwd(p, a->dtype == TSA_FP16, st, tm.ev, tm.n));
 }
 

@@ -621,6 +621,78 @@ __global__ void nsa_rev_ptr(const int* n_entries, const int* hist, int NK, int n
 }
 
 // Data check for validate = 1: counts ids outside [0, nblk).
+// Token-group chunk lists: one wave per (KV head, token group).  Lane j
+// holds token p0 + j's sorted row (staged in LDS) and a cursor into it; each
+// step takes the smallest id at the cursors (a k-way merge), emits that
+// block's 32-key chunks with the mask of the lanes at that id (under causal
+// mode without the tokens placed before the chunk), and advances those
+// lanes by one, so an id a token lists twice is emitted twice.
+constexpr int kNoId = 0x7fffffff;
+__global__ __launch_bounds__(64) void nsa_group_chunks(NsaGeom g, const int* row_ptr,
+                                                       const int* col, NsaGroups gr) {
+  __shared__ int rows[kNsaGroup * 128];  // sbc <= 128
+  const int lane = threadIdx.x;
+  const int unit = blockIdx.x;
+  const int n2 = unit / gr.NG, gi = unit - n2 * gr.NG;
+  const int b = seq_of(gr.gcu, g.B, gi);
+  const int p0 = (gi - gr.gcu[b]) * kNsaGroup;
+  const int t0 = g.cu_q[b] + p0;
+  const int ntok = min(kNsaGroup, g.cu_q[b + 1] - t0);
+  const int sbc = g.sbc, sbs = g.sbs;
+  int r0 = 0, n = 0;
+  if (lane < ntok) {
+    const long row = (long)(t0 + lane) * g.N2 + n2;
+    r0 = row_ptr[row];
+    n = row_ptr[row + 1] - r0;
+  }
+  for (int j = 0; j < ntok; j++) {
+    const int rj = __shfl(r0, j), nj = __shfl(n, j);
+    for (int e = lane; e < nj; e += 64) rows[j * sbc + e] = col[rj + e];
+  }
+  __syncthreads();
+  const int cpb = (sbs + kNsaGroupChunk - 1) / kNsaGroupChunk;
+  int* out = gr.ent + (long)unit * gr.cap * 2;
+  int c = 0, count = 0;
+  int head = c < n ? rows[lane * sbc] : kNoId;  // lanes >= ntok have n = 0
+  while (true) {
+    int mn = head;
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) mn = min(mn, __shfl_xor(mn, o));
+    mn = __shfl(mn, 0);  // lanes 0..31 hold every token (kNsaGroup <= 32)
+    if (mn == kNoId) break;
+    const unsigned sel = (unsigned)__ballot(head == mn);
+    for (int s = 0; s < cpb; s++) {
+      const int ks = mn * sbs + kNsaGroupChunk * s;
+      unsigned m = sel;
+      if (g.causal) {
+        const int d = ks - p0;  // tokens j < d sit before the chunk
+        if (d >= 32) m = 0u;
+        else if (d > 0) m &= ~((1u << d) - 1u);
+      }
+      if (m) {
+        if (lane == 0) {
+          out[2 * count] = ks;
+          out[2 * count + 1] = (int)m;
+        }
+        count++;
+      }
+    }
+    if (head == mn) {
+      c++;
+      head = c < n ? rows[lane * sbc + c] : kNoId;
+    }
+  }
+  if (lane == 0) gr.cnt[unit] = count;
+}
+
+hipError_t launch_nsa_group_lists(const NsaGeom& g, const int* row_ptr, const int* col,
+                                  const NsaGroups& gr, hipStream_t st) {
+  const long units = (long)g.N2 * gr.NG;
+  if (units == 0) return hipSuccess;
+  hipLaunchKernelGGL(nsa_group_chunks, dim3((unsigned)units), dim3(64), 0, st, g, row_ptr, col, gr);
+  return hipGetLastError();
+}
+
 __global__ __launch_bounds__(256) void nsa_check_ids(const int* topk, NsaGeom g, int* bad) {
   const long r = (long)blockIdx.x * 256 + threadIdx.x;
   if (r >= (long)g.T * g.N2) return;

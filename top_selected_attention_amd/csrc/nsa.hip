@@ -16,6 +16,7 @@
 // 32), and query/key heads of 192 dims (values of 128), use a 32-wide tile
 // staged by direct global -> LDS loads.
 #include <algorithm>
+#include <type_traits>
 
 #include "tsa_device.h"
 #include "tsa_internal.h"
@@ -673,6 +674,468 @@ void nsa_dq16_kernel(NsaParams p, int n_items) {
 }
 
 // ---------------------------------------------------------------------------
+// Token-group forward and dQ (head groups of up to 16 query heads, 128-dim
+// heads).  A workgroup of 8 waves takes kNsaGroup = 16 consecutive tokens of
+// one sequence and one KV head, and walks the group's chunk list (the
+// ascending union of its tokens' selected blocks in 32-key chunks, each with
+// the mask of the tokens that attend to it) four chunks at a time.  Each wave
+// loads one 32-key K or V tile of the next window straight into LDS while
+// the current window computes, so a K/V row is gathered once per group
+// instead of once per token.  Wave w owns tokens w and 15 - w (pairing early
+// and late positions evens out the causal work) and, for each chunk one of
+// them attends to, computes that token's 16-head x 32-key scores on
+// 16x16x32 MFMA from the shared tiles; when both attend, every fragment read
+// from LDS feeds both tokens' MFMAs.  A token visits its chunks in ascending
+// block order, as the per-token kernels do.
+// ---------------------------------------------------------------------------
+namespace {
+constexpr int kGrpTPW = 1;                                // tokens per wave (1 or 2)
+constexpr int kGrpSlots = 4;                              // chunks per window
+constexpr int kGrpTile = kChunk * 256;                    // one K or V tile, 8 KB
+constexpr int kGrpLds = 2 * kGrpSlots * 2 * kGrpTile;     // two windows, 128 KB
+static_assert(kNsaGroupChunk == kChunk, "list chunks are kernel chunks");
+
+// Tiles of the token-group kernels: key k of a chunk in row k (256 bytes),
+// its 16-byte piece c at piece c ^ gswz(k).  gswz is a bijection on each run
+// of 16 rows, and gswz >> 1 is one on rows 0-7, on rows 8-15, on the even
+// and on the odd rows of a run; so the operand reads below -- 16 rows x one
+// piece, 16 rows x two adjacent pieces (32 lanes), and transpose reads of 4
+// or 8 consecutive rows x one aligned piece pair -- touch distinct banks
+// whether a read is served 16 or 32 lanes at a time.  A lane's read
+// addresses differ only in bits the loop index XORs in, so each is the
+// lane's base address XOR a constant.
+__device__ __forceinline__ int gswz(int k) {
+  return ((((k & 7) ^ ((k >> 3) & 1)) << 1) | ((k >> 3) & 1));
+}
+typedef __attribute__((address_space(3))) const uint4 lds_u4_t;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
+template <typename V8>
+__device__ __forceinline__ V8 lds16_at(unsigned a) {
+  return __builtin_bit_cast(V8, *(lds_u4_t*)(uintptr_t)a);
+}
+template <typename V8>
+__device__ __forceinline__ V8 ldstr_at(unsigned a0, unsigned a1) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(uintptr_t)a0);
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(uintptr_t)a1);
+  const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(V8, v);
+}
+// Per-lane base of the row reads (key 16*kt + l16, logical piece 4*q4 + gq:
+// base ^ 64*q4, + 4096*kt) and of the transpose reads (keys 4*gq + l16/4
+// (+16), bytes 32*dt + 8*(l16%4): base ^ 32*dt, + 4096 for the second half).
+__device__ __forceinline__ unsigned grp_row_base(int l16, int gq) {
+  return (unsigned)(l16 * 256 + 16 * (gq ^ gswz(l16)));
+}
+__device__ __forceinline__ unsigned grp_tr_base(int l16, int gq) {
+  const int k = 4 * gq + (l16 >> 2);
+  return (unsigned)(k * 256 + 16 * (((l16 & 3) >> 1) ^ gswz(k)) + 8 * (l16 & 1));
+}
+
+struct GrpUnit {
+  int n2, p0, ntok, t0, kv0;
+};
+__device__ __forceinline__ GrpUnit grp_unit(const NsaParams& p, int unit) {
+  GrpUnit u;
+  u.n2 = unit / p.grp.NG;
+  const int gi = unit - u.n2 * p.grp.NG;
+  const int b = seq_of_dev(p.grp.gcu, p.g.B, gi);
+  u.p0 = (gi - p.grp.gcu[b]) * kNsaGroup;
+  u.t0 = p.g.cu_q[b] + u.p0;
+  u.ntok = min(kNsaGroup, p.g.cu_q[b + 1] - u.t0);
+  u.kv0 = p.g.cu_kv[b];
+  return u;
+}
+
+// A wave's share of a window's loads: of the 8 tiles (K and V of 4 slots),
+// tile wid % 8 (slot tile / 2, K for even tiles, V for odd), slices
+// (wid / 8) * SPW .. + SPW - 1 of its eight 1-KB slices of direct loads;
+// lane l's bytes of slice sl land in row 4*sl + l/16, physical piece l%16.
+// A chunk of 16 keys (a block size that is an odd multiple of 16) re-reads
+// keys 0..15 into rows 16..31, which no score keeps.
+template <int SPW>
+struct GrpLoader {
+  const char* base;  // key row 0 of the sequence's KV head
+  unsigned rowb;     // bytes between consecutive tokens of one KV head
+  int s0;            // first slice
+  __device__ __forceinline__ void init(const NsaParams& p, const GrpUnit& u, int wid) {
+    rowb = (unsigned)p.N2 * kD * 2;
+    base = (const char*)((wid & 1) ? p.v : p.k) + ((long)u.kv0 * p.N2 + u.n2) * kD * 2;
+    s0 = (wid >> 3) * SPW;
+  }
+  // chunk of keys [ks, ks + nvalid) into the tile at LDS address lds
+  __device__ __forceinline__ void issue(int ks, int nvalid, unsigned lds, int lane) const {
+    const char* sb = base + (long)ks * rowb;
+#pragma unroll
+    for (int u = 0; u < SPW; u++) {
+      const int sl = s0 + u;
+      const int k = 4 * sl + (lane >> 4);
+      const int kk = nvalid < kChunk ? (k & 15) : k;
+      g2lds16_so_at(sb, (unsigned)kk * rowb + 16u * (unsigned)((lane & 15) ^ gswz(k)),
+                    lds + 1024u * sl);
+    }
+  }
+};
+
+// A window's four list entries, held by lanes 0..3 (read back with readlane).
+struct GrpWin {
+  int ks, msk;
+  __device__ __forceinline__ void fetch(const int* ent, int cnt, int w, int lane) {
+    const int e = w * kGrpSlots + lane;
+    ks = 0;
+    msk = 0;
+    if (lane < kGrpSlots && e < cnt) {
+      ks = ent[2 * e];
+      msk = ent[2 * e + 1];
+    }
+  }
+};
+}  // namespace
+
+template <class E, int TPW>
+__global__ __launch_bounds__(kNsaGroup / TPW * 64) void nsa_fwd_grp_kernel(NsaParams p) {
+  constexpr int NW = kNsaGroup / TPW;  // waves
+  typedef typename E::T T;
+  typedef typename E::V8 V8;
+  typedef float f32x4_t __attribute__((ext_vector_type(4)));
+  __shared__ __attribute__((aligned(1024))) char lds[kGrpLds];
+
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar branches
+  const int l16 = lane & 15, gq = lane >> 4;
+  const GrpUnit u = grp_unit(p, blockIdx.x);
+  const NsaGeom& g = p.g;
+  const int G = p.G;
+  const bool col_ok = l16 < G;
+  const int sbs = g.sbs;
+  const float sl2 = p.scale * kLog2e;
+  constexpr float kLazy = 8.f;
+
+  // the wave's two tokens: j = wid and 15 - wid of the group
+  const int jt[2] = {wid, TPW == 2 ? kNsaGroup - 1 - wid : wid};
+  bool live[2];
+  V8 q[2][4];
+  f32x4_t o[2][8];
+  float m[2], lsum[2];
+#pragma unroll
+  for (int i = 0; i < TPW; i++) {
+    live[i] = jt[i] < u.ntok;
+    const bool ok = live[i] && col_ok;
+    const T* qrow = (const T*)p.q + ((long)(u.t0 + (live[i] ? jt[i] : 0)) * p.N1 + u.n2 * G +
+                                     (col_ok ? l16 : 0)) * kD;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; q4++) q[i][q4] = ok ? as_v8<V8>(ld16(qrow + 32 * q4 + 8 * gq)) : zero_v8<V8>();
+#pragma unroll
+    for (int dt = 0; dt < 8; dt++) o[i][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    m[i] = -INFINITY;
+    lsum[i] = 0.f;
+  }
+
+  const int cnt = p.grp.cnt[blockIdx.x];
+  const int* ent = p.grp.ent + (long)blockIdx.x * p.grp.cap * 2;
+  const int nwin = (cnt + kGrpSlots - 1) / kGrpSlots;
+  GrpLoader<64 / NW> ld;
+  ld.init(p, u, wid);
+  const unsigned lds0 = lds_addr(lds);
+  const int my_slot = (wid & 7) >> 1;
+  auto tile_addr = [&](int buf, int slot, int kv) {
+    return lds0 + (unsigned)(((buf * kGrpSlots + slot) * 2 + kv) * kGrpTile);
+  };
+  auto nvalid_of = [&](int ks) { return min(kChunk, sbs - ks % sbs); };
+  auto issue = [&](const GrpWin& wn, int w, int buf) {
+    if (w * kGrpSlots + my_slot < cnt) {
+      const int ks = __builtin_amdgcn_readlane(wn.ks, my_slot);
+      ld.issue(ks, nvalid_of(ks), tile_addr(buf, my_slot, wid & 1), lane);
+    }
+  };
+
+  const unsigned rd = grp_row_base(l16, gq), tt = grp_tr_base(l16, gq);
+
+  // One chunk for the tokens the compile-time flags A, B (tokens 0, 1 of the
+  // wave) name: straight-line code, so every LDS read can be issued ahead of
+  // the MFMAs that use it.
+  auto chunk = [&](auto A, auto B, unsigned Kt, int ks) {
+    constexpr bool sa = decltype(A)::value, sb = decltype(B)::value;
+    const int nv = nvalid_of(ks);
+    const unsigned Vt = Kt + kGrpTile;
+    V8 f[2][4];
+#pragma unroll
+    for (int kt = 0; kt < 2; kt++)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; q4++) f[kt][q4] = lds16_at<V8>(((Kt + rd) ^ (64u * q4)) + 4096u * kt);
+    // S^T tiles: element j of st[i][kt] is key ks + 16*kt + 4*gq + j, head l16
+    f32x4_t st[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+      if (!(i == 0 ? sa : sb)) continue;
+#pragma unroll
+      for (int kt = 0; kt < 2; kt++) {
+        st[i][kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int q4 = 0; q4 < 4; q4++) st[i][kt] = E::mfma16(f[kt][q4], q[i][q4], st[i][kt]);
+      }
+    }
+    // V^T rows d = 16*dt + l16, keys {4gq..4gq+3, 16+4gq..16+4gq+3}, read
+    // while the softmax runs
+    V8 vf[8];
+#pragma unroll
+    for (int dt = 0; dt < 8; dt++)
+      vf[dt] = ldstr_at<V8>((Vt + tt) ^ (32u * dt), ((Vt + tt) ^ (32u * dt)) + 4096u);
+    V8 pb[2];
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+      if (!(i == 0 ? sa : sb)) continue;
+      const int lim = min(nv - 1, g.causal ? u.p0 + jt[i] - ks : 0x7fffffff);
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 2; kt++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const float v = (16 * kt + 4 * gq + j) <= lim ? st[i][kt][j] : -INFINITY;
+          st[i][kt][j] = v;
+          mx = vmax(mx, v);
+        }
+      mx = max_xor16_32(mx) * sl2;
+      if (__builtin_amdgcn_ballot_w64(mx > m[i] + kLazy)) {
+        const float m_new = fmaxf(m[i], mx);
+        const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m[i] - m_new);
+        m[i] = m_new;
+        lsum[i] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 8; dt++) o[i][dt] *= alpha;
+      }
+      const float mneg = m[i] == -INFINITY ? 0.f : -m[i];
+#pragma unroll
+      for (int kt = 0; kt < 2; kt++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const float pv = fast_exp2(__builtin_fmaf(st[i][kt][j], sl2, mneg));
+          lsum[i] += pv;
+          pb[i][4 * kt + j] = E::from_f32(pv);
+        }
+    }
+    // O^T += V^T P^T
+#pragma unroll
+    for (int dt = 0; dt < 8; dt++) {
+      if (sa) o[0][dt] = E::mfma16(vf[dt], pb[0], o[0][dt]);
+      if (sb) o[1][dt] = E::mfma16(vf[dt], pb[1], o[1][dt]);
+    }
+  };
+
+  GrpWin cur, nxt;
+  cur.fetch(ent, cnt, 0, lane);
+  nxt.fetch(ent, cnt, 1, lane);
+  if (nwin > 0) issue(cur, 0, 0);
+  for (int w = 0; w < nwin; w++) {
+    wait_vm();
+    __syncthreads();  // window w landed; window w - 1's buffer is free
+    GrpWin nn;
+    nn.fetch(ent, cnt, w + 2, lane);
+    if (w + 1 < nwin) issue(nxt, w + 1, (w + 1) & 1);
+    const int nslot = min(kGrpSlots, cnt - w * kGrpSlots);
+    for (int s = 0; s < nslot; s++) {
+      const unsigned msk = (unsigned)__builtin_amdgcn_readlane(cur.msk, s);
+      const bool sel0 = (msk >> jt[0]) & 1u, sel1 = TPW == 2 && ((msk >> jt[1]) & 1u);
+      if (!(sel0 || sel1)) continue;
+      const int ks = __builtin_amdgcn_readlane(cur.ks, s);
+      const unsigned Kt = tile_addr(w & 1, s, 0);
+      if (sel0 && sel1) chunk(std::true_type{}, std::true_type{}, Kt, ks);
+      else if (sel0) chunk(std::true_type{}, std::false_type{}, Kt, ks);
+      else chunk(std::false_type{}, std::true_type{}, Kt, ks);
+    }
+    cur = nxt;
+    nxt = nn;
+  }
+
+#pragma unroll
+  for (int i = 0; i < TPW; i++) {
+    if (!live[i]) continue;
+    float lt = lsum[i] + __shfl_xor(lsum[i], 16);
+    lt += __shfl_xor(lt, 32);
+    if (col_ok) {
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      const long orow = (long)(u.t0 + jt[i]) * p.N1 + u.n2 * G + l16;
+      T* op = (T*)p.out + orow * kD;
+#pragma unroll
+      for (int dt = 0; dt < 8; dt++)
+        *reinterpret_cast<uint2*>(op + 16 * dt + 4 * gq) =
+            pack4<E>(o[i][dt][0] * inv, o[i][dt][1] * inv, o[i][dt][2] * inv, o[i][dt][3] * inv);
+      if (gq == 0) p.lse[orow] = lt > 0.f ? (m[i] + log2f(lt)) * kLn2 : -INFINITY;
+    }
+  }
+}
+
+// dQ (+ softmax_grad) over the same token groups and chunk lists:
+// S^T = K Q^T and dP^T = V dO^T from the K and V tiles, dS^T = P^T (dP^T -
+// softmax_grad), dQ^T += K^T dS^T with K^T read transposed from the K tile.
+template <class E, int TPW>
+__global__ __launch_bounds__(kNsaGroup / TPW * 64) void nsa_dq_grp_kernel(NsaParams p) {
+  constexpr int NW = kNsaGroup / TPW;  // waves
+  typedef typename E::T T;
+  typedef typename E::V8 V8;
+  typedef float f32x4_t __attribute__((ext_vector_type(4)));
+  __shared__ __attribute__((aligned(1024))) char lds[kGrpLds];
+
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar branches
+  const int l16 = lane & 15, gq = lane >> 4;
+  const GrpUnit u = grp_unit(p, blockIdx.x);
+  const NsaGeom& g = p.g;
+  const int G = p.G;
+  const bool col_ok = l16 < G;
+  const int sbs = g.sbs;
+  const float sl2 = p.scale * kLog2e;
+
+  const int jt[2] = {wid, TPW == 2 ? kNsaGroup - 1 - wid : wid};
+  bool live[2];
+  V8 q[2][4], dov[2][4];
+  f32x4_t dq[2][8];
+  float lse2[2], dlt[2];
+#pragma unroll
+  for (int i = 0; i < TPW; i++) {
+    live[i] = jt[i] < u.ntok;
+    const bool ok = live[i] && col_ok;
+    const long qr = (long)(u.t0 + (live[i] ? jt[i] : 0)) * p.N1 + u.n2 * G + (col_ok ? l16 : 0);
+    float acc = 0.f;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; q4++) {
+      const long off = qr * kD + 32 * q4 + 8 * gq;
+      q[i][q4] = ok ? as_v8<V8>(ld16((const T*)p.q + off)) : zero_v8<V8>();
+      dov[i][q4] = ok ? as_v8<V8>(ld16((const T*)p.dout + off)) : zero_v8<V8>();
+      const V8 ov = ok ? as_v8<V8>(ld16((const T*)p.o + off)) : zero_v8<V8>();
+#pragma unroll
+      for (int e = 0; e < 8; e++) acc += E::to_f32(dov[i][q4][e]) * E::to_f32(ov[e]);
+    }
+    acc += __shfl_xor(acc, 16);
+    acc += __shfl_xor(acc, 32);
+    dlt[i] = acc;
+    lse2[i] = ok ? p.lse[qr] * kLog2e : 0.f;
+    if (ok && gq == 0) *reinterpret_cast<float2*>(p.delta + 2 * qr) = make_float2(lse2[i], dlt[i]);
+#pragma unroll
+    for (int dt = 0; dt < 8; dt++) dq[i][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const int cnt = p.grp.cnt[blockIdx.x];
+  const int* ent = p.grp.ent + (long)blockIdx.x * p.grp.cap * 2;
+  const int nwin = (cnt + kGrpSlots - 1) / kGrpSlots;
+  GrpLoader<64 / NW> ld;
+  ld.init(p, u, wid);
+  const unsigned lds0 = lds_addr(lds);
+  const int my_slot = (wid & 7) >> 1;
+  auto tile_addr = [&](int buf, int slot, int kv) {
+    return lds0 + (unsigned)(((buf * kGrpSlots + slot) * 2 + kv) * kGrpTile);
+  };
+  auto nvalid_of = [&](int ks) { return min(kChunk, sbs - ks % sbs); };
+  auto issue = [&](const GrpWin& wn, int w, int buf) {
+    if (w * kGrpSlots + my_slot < cnt) {
+      const int ks = __builtin_amdgcn_readlane(wn.ks, my_slot);
+      ld.issue(ks, nvalid_of(ks), tile_addr(buf, my_slot, wid & 1), lane);
+    }
+  };
+  const unsigned rd = grp_row_base(l16, gq), tt = grp_tr_base(l16, gq);
+
+  // One chunk for the tokens the compile-time flags A, B name (see the forward).
+  auto chunk = [&](auto A, auto B, unsigned Kt, int ks) {
+    constexpr bool sa = decltype(A)::value, sb = decltype(B)::value;
+    const int nv = nvalid_of(ks);
+    const unsigned Vt = Kt + kGrpTile;
+    // element j of st[i][kt] / dpt[i][kt]: key ks + 16*kt + 4*gq + j, head l16
+    f32x4_t st[2][2], dpt[2][2];
+    V8 f[2][4];
+#pragma unroll
+    for (int kt = 0; kt < 2; kt++)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; q4++) f[kt][q4] = lds16_at<V8>(((Kt + rd) ^ (64u * q4)) + 4096u * kt);
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+      if (!(i == 0 ? sa : sb)) continue;
+#pragma unroll
+      for (int kt = 0; kt < 2; kt++) {
+        st[i][kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int q4 = 0; q4 < 4; q4++) st[i][kt] = E::mfma16(f[kt][q4], q[i][q4], st[i][kt]);
+      }
+    }
+#pragma unroll
+    for (int kt = 0; kt < 2; kt++)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; q4++) f[kt][q4] = lds16_at<V8>(((Vt + rd) ^ (64u * q4)) + 4096u * kt);
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+      if (!(i == 0 ? sa : sb)) continue;
+#pragma unroll
+      for (int kt = 0; kt < 2; kt++) {
+        dpt[i][kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int q4 = 0; q4 < 4; q4++) dpt[i][kt] = E::mfma16(f[kt][q4], dov[i][q4], dpt[i][kt]);
+      }
+    }
+    // K^T rows d = 16*dt + l16, keys {4gq..4gq+3, 16+4gq..16+4gq+3}, read
+    // while dS is formed
+    V8 kf[8];
+#pragma unroll
+    for (int dt = 0; dt < 8; dt++)
+      kf[dt] = ldstr_at<V8>((Kt + tt) ^ (32u * dt), ((Kt + tt) ^ (32u * dt)) + 4096u);
+    V8 bs[2];
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+      if (!(i == 0 ? sa : sb)) continue;
+      const int lim = min(nv - 1, g.causal ? u.p0 + jt[i] - ks : 0x7fffffff);
+#pragma unroll
+      for (int kt = 0; kt < 2; kt++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const bool ok = col_ok && (16 * kt + 4 * gq + j) <= lim;
+          const float pv = ok ? fast_exp2(__builtin_fmaf(st[i][kt][j], sl2, -lse2[i])) : 0.f;
+          bs[i][4 * kt + j] = E::from_f32(pv * (dpt[i][kt][j] - dlt[i]));
+        }
+    }
+    // dQ^T += K^T dS^T
+#pragma unroll
+    for (int dt = 0; dt < 8; dt++) {
+      if (sa) dq[0][dt] = E::mfma16(kf[dt], bs[0], dq[0][dt]);
+      if (sb) dq[1][dt] = E::mfma16(kf[dt], bs[1], dq[1][dt]);
+    }
+  };
+
+  GrpWin cur, nxt;
+  cur.fetch(ent, cnt, 0, lane);
+  nxt.fetch(ent, cnt, 1, lane);
+  if (nwin > 0) issue(cur, 0, 0);
+  for (int w = 0; w < nwin; w++) {
+    wait_vm();
+    __syncthreads();
+    GrpWin nn;
+    nn.fetch(ent, cnt, w + 2, lane);
+    if (w + 1 < nwin) issue(nxt, w + 1, (w + 1) & 1);
+    const int nslot = min(kGrpSlots, cnt - w * kGrpSlots);
+    for (int s = 0; s < nslot; s++) {
+      const unsigned msk = (unsigned)__builtin_amdgcn_readlane(cur.msk, s);
+      const bool sel0 = (msk >> jt[0]) & 1u, sel1 = TPW == 2 && ((msk >> jt[1]) & 1u);
+      if (!(sel0 || sel1)) continue;
+      const int ks = __builtin_amdgcn_readlane(cur.ks, s);
+      const unsigned Kt = tile_addr(w & 1, s, 0);
+      if (sel0 && sel1) chunk(std::true_type{}, std::true_type{}, Kt, ks);
+      else if (sel0) chunk(std::true_type{}, std::false_type{}, Kt, ks);
+      else chunk(std::false_type{}, std::true_type{}, Kt, ks);
+    }
+    cur = nxt;
+    nxt = nn;
+  }
+
+#pragma unroll
+  for (int i = 0; i < TPW; i++) {
+    if (!live[i] || !col_ok) continue;
+    const long qr = (long)(u.t0 + jt[i]) * p.N1 + u.n2 * G + l16;
+    T* dp = (T*)p.out + qr * kD;
+#pragma unroll
+    for (int dt = 0; dt < 8; dt++)
+      *reinterpret_cast<uint2*>(dp + 16 * dt + 4 * gq) =
+          pack4<E>(dq[i][dt][0] * p.scale, dq[i][dt][1] * p.scale, dq[i][dt][2] * p.scale,
+                   dq[i][dt][3] * p.scale);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // dK / dV.  The tokens that selected a (KV head, block) -- its reverse list --
 // are cut into segments of at most kSegEntries listings, so a block that
 // thousands of tokens selected is shared by many workgroups.  Workgroups
@@ -1050,6 +1513,9 @@ static hipError_t fwd_t(const NsaParams& p, hipStream_t st) {
   if (p.D == 192)
     hipLaunchKernelGGL((nsa_fwd_kernel<E, 192>), dim3(8 * ((n_items + 7) / 8)), dim3(256), 0, st,
                        p, n_items);
+  else if (p.G <= 16 && p.grp.NG > 0)
+    hipLaunchKernelGGL((nsa_fwd_grp_kernel<E, kGrpTPW>), dim3(p.N2 * p.grp.NG),
+                       dim3(kNsaGroup / kGrpTPW * 64), 0, st, p);
   else if (p.G <= 16)
     hipLaunchKernelGGL((nsa_fwd16_kernel<E>), dim3(8 * ((n_items + 7) / 8)), dim3(256), 0, st, p,
                        n_items);
@@ -1083,6 +1549,9 @@ static hipError_t bwd_t(const NsaParams& p, hipStream_t st, void* const* ev, int
     if (p.D == 192)
       hipLaunchKernelGGL((nsa_dq_kernel<E, 192>), dim3(8 * ((n_items + 7) / 8)), dim3(256), 0, st,
                          p, n_items);
+    else if (p.G <= 16 && p.grp.NG > 0)
+      hipLaunchKernelGGL((nsa_dq_grp_kernel<E, kGrpTPW>), dim3(p.N2 * p.grp.NG),
+                         dim3(kNsaGroup / kGrpTPW * 64), 0, st, p);
     else if (p.G <= 16)
       hipLaunchKernelGGL((nsa_dq16_kernel<E>), dim3(8 * ((n_items + 7) / 8)), dim3(256), 0, st,
                          p, n_items);

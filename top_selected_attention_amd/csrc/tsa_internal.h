@@ -49,6 +49,25 @@ struct NsaGeom {
 // given.  Reverse: per (n2, block) ascending token lists, by a stable
 // counting sort of those entries when the key count allows (rs.usable),
 // else by a per-list scan of the forward rows.
+// Token groups of the NSA token-group forward and dQ kernels: runs of
+// kNsaGroup consecutive tokens of one sequence, group g of sequence b holding
+// positions [g * kNsaGroup, (g + 1) * kNsaGroup).  Each (KV head, group) has
+// a chunk list: the ascending union of its tokens' selected blocks cut into
+// 32-key chunks, one {key start within the sequence, token mask} entry per
+// chunk that at least one token attends to (bit j = token p0 + j; a token
+// listing a block twice attends to its chunks twice).
+constexpr int kNsaGroup = 16;
+constexpr int kNsaGroupChunk = 32;
+struct NsaGroups {
+  const int* gcu;  // [B+1] prefix sums of ceil(Sq_b / kNsaGroup)
+  int NG;          // groups per KV head
+  int cap;         // entries per (KV head, group): kNsaGroup * sbc * ceil(sbs / 32)
+  int* cnt;        // [N2 * NG] entries of each list, unit = n2 * NG + group
+  int* ent;        // [N2 * NG][cap][2]
+};
+hipError_t launch_nsa_group_lists(const NsaGeom& g, const int* row_ptr, const int* col,
+                                  const NsaGroups& gr, hipStream_t st);
+
 constexpr int kNsaRevMaxKeys = 16384;  // LDS counters of one sort tile (64 KB)
 struct NsaRevSort {
   int NK, bits, rounds, n_tiles;
@@ -165,6 +184,7 @@ struct NsaParams {
   int* seg_off;        // [N2*NB + 1] exclusive scan of segments per list, then the total
   int* seg_sums;       // scan scratch
   int* seg_ctr;        // [1] segments taken by the dK/dV workgroups
+  NsaGroups grp;       // token-group chunk lists (grouped kernels only; NG = 0 otherwise)
   float* part;         // [max_segments][sbs*D (dK) + sbs*128 (dV)] fp32 partials
   int max_segments;
 };
