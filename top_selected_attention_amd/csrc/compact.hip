@@ -645,22 +645,42 @@ __global__ __launch_bounds__(64) void nsa_group_chunks(NsaGeom g, const int* row
     r0 = row_ptr[row];
     n = row_ptr[row + 1] - r0;
   }
-  for (int j = 0; j < ntok; j++) {
-    const int rj = __shfl(r0, j), nj = __shfl(n, j);
-    for (int e = lane; e < nj; e += 64) rows[j * sbc + e] = col[rj + e];
+  // stage the rows: slot i = j * sbc + e of the tile holds entry e of token
+  // j's row; eight independent loads per lane in flight at a time
+  const int tot = ntok * sbc;
+  for (int i0 = 0; i0 < tot; i0 += 8 * 64) {
+    int v[8];
+#pragma unroll
+    for (int u = 0; u < 8; u++) {
+      const int i = i0 + u * 64 + lane;
+      const int j = min(i / sbc, kNsaGroup - 1), e = i - j * sbc;
+      const int rj = __shfl(r0, j), nj = __shfl(n, j);
+      v[u] = (i < tot && e < nj) ? col[rj + e] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; u++) {
+      const int i = i0 + u * 64 + lane;
+      if (i < tot) rows[i] = v[u];
+    }
   }
   __syncthreads();
   const int cpb = (sbs + kNsaGroupChunk - 1) / kNsaGroupChunk;
   int* out = gr.ent + (long)unit * gr.cap * 2;
+  static_assert(kNsaGroup <= 16, "one DPP row of lanes holds the group's tokens");
+  // lane j's cursor c, its id (head) and the id after it (nxt)
   int c = 0, count = 0;
   int head = c < n ? rows[lane * sbc] : kNoId;  // lanes >= ntok have n = 0
+  int nxt = c + 1 < n ? rows[lane * sbc + 1] : kNoId;
   while (true) {
+    // minimum over lanes 0..15 by row rotations (DPP), read from lane 0
     int mn = head;
-#pragma unroll
-    for (int o = 16; o >= 1; o >>= 1) mn = min(mn, __shfl_xor(mn, o));
-    mn = __shfl(mn, 0);  // lanes 0..31 hold every token (kNsaGroup <= 32)
+    mn = min(mn, __builtin_amdgcn_update_dpp(kNoId, mn, 0x128, 0xf, 0xf, false));  // row_ror:8
+    mn = min(mn, __builtin_amdgcn_update_dpp(kNoId, mn, 0x124, 0xf, 0xf, false));  // row_ror:4
+    mn = min(mn, __builtin_amdgcn_update_dpp(kNoId, mn, 0x122, 0xf, 0xf, false));  // row_ror:2
+    mn = min(mn, __builtin_amdgcn_update_dpp(kNoId, mn, 0x121, 0xf, 0xf, false));  // row_ror:1
+    mn = __builtin_amdgcn_readfirstlane(mn);
     if (mn == kNoId) break;
-    const unsigned sel = (unsigned)__ballot(head == mn);
+    const unsigned sel = (unsigned)__ballot(lane < 16 && head == mn);
     for (int s = 0; s < cpb; s++) {
       const int ks = mn * sbs + kNsaGroupChunk * s;
       unsigned m = sel;
@@ -679,7 +699,8 @@ __global__ __launch_bounds__(64) void nsa_group_chunks(NsaGeom g, const int* row
     }
     if (head == mn) {
       c++;
-      head = c < n ? rows[lane * sbc + c] : kNoId;
+      head = nxt;
+      nxt = c + 1 < n ? rows[lane * sbc + c + 1] : kNoId;
     }
   }
   if (lane == 0) gr.cnt[unit] = count;
