@@ -117,6 +117,8 @@ KERNEL_SOURCES = {
     "nsa_fwd16_kernel": ["nsa.hip"],
     "nsa_dq_kernel": ["nsa.hip"],
     "nsa_dq16_kernel": ["nsa.hip"],
+    "nsa_fwd_grp_kernel": ["nsa.hip"],
+    "nsa_dq_grp_kernel": ["nsa.hip"],
     "nsa_dkdv_seg_kernel": ["nsa.hip"],
     "sfa_split_kernel": ["sfa.hip"],
 }
@@ -380,14 +382,23 @@ def bench_nsa(args):
     fwd_ms = st[0] + st[1]
     bwd_ms = st[2] + st[3] + st[4] + st[5]
     # dK/dV: the partial kernel does the 4 GEMMs; the reduction is a separate stage
-    # head groups of up to 16 heads run the 16-column forward / dQ kernels
-    sfx = "16" if G <= 16 else ""
+    # head groups of up to 16 heads of 128 dims run the token-group forward / dQ kernels
+    sfx = "_grp" if G <= 16 and D == 128 else ""
     kern = {f"nsa_fwd{sfx}_kernel": (st[1], 4.0 * unit), f"nsa_dq{sfx}_kernel": (st[3], 6.0 * unit),
             "nsa_dkdv_seg_kernel": (st[4], 8.0 * unit)}
     dom = max(kern, key=lambda n: kern[n][0])
     dms, dfl = kern[dom]
     achieved = dfl / (dms * 1e-3) / 1e12
-    gathered = triples * sbs * D * 2 * 2      # K and V rows brought to the CUs per pass
+    gathered = triples * sbs * D * 2 * 2      # K and V rows of every kept (token, block)
+    # K/V rows the token-group kernels stage per pass: each group of 16
+    # consecutive tokens of a sequence loads the union of its tokens' kept
+    # blocks once (a block listed twice by one token counted once here)
+    T = int(cu[-1])
+    seq = np.repeat(np.arange(len(cu) - 1), np.diff(cu))
+    grp = (seq.astype(np.int64) << 32) | (pos // 16)
+    n2i = np.broadcast_to(np.arange(w["N2"])[None, :, None], topk.shape)
+    key = (np.broadcast_to(grp[:, None, None], topk.shape) * w["N2"] + n2i) * (1 << 20) + topk
+    staged = int(np.unique(key[kept]).size) * sbs * D * 2 * 2
     value = (fwd_flops + bwd_flops) / (ms_step * 1e-3) / 1e12
     res = {
         "metric": "effective TFLOP/s on selected blocks (fwd, bwd) and % of bf16 MFMA peak",
@@ -410,7 +421,9 @@ def bench_nsa(args):
         "step_ms_events": _step_stats(plan.step_ms),
         "ms_per_step_cold": round(plan.cold_ms, 4),
         "settle_steps": plan.settle_steps,
-        "fwd_gathered_GBps": round(gathered / (st[1] * 1e-3) / 1e9, 1),
+        "fwd_kv_rows_GBps": round(gathered / (st[1] * 1e-3) / 1e9, 1),
+        "fwd_staged_GBps": round(staged / (st[1] * 1e-3) / 1e9, 1),
+        "fwd_staged_bytes": staged,
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
