@@ -339,24 +339,6 @@ __device__ __forceinline__ ChunkPos chunk_advance(ChunkPos c, int per_entry) {
   return c;
 }
 
-// A short int32 list (at most 128 entries, e.g. the sorted block ids of one
-// NSA row) held in two VGPRs per lane and read with uniform readlane: no
-// memory access after the constructor, so a loop over it leaves the
-// vector-memory counter to the loop's own loads.
-struct ShortList {
-  int lo, hi;
-  __device__ __forceinline__ ShortList(const int* l, int n) {
-    const int lane = (int)(threadIdx.x & 63);
-    lo = lane < n ? l[lane] : 0;
-    hi = lane + 64 < n ? l[lane + 64] : 0;
-    // consume the loads here, so no later readlane waits on the memory counter
-    asm volatile("" : "+v"(lo), "+v"(hi));
-  }
-  __device__ __forceinline__ int operator()(int i) const {
-    return i < 64 ? __builtin_amdgcn_readlane(lo, i) : __builtin_amdgcn_readlane(hi, i - 64);
-  }
-};
-
 // Wave-uniform lookups into an int32 list (e.g. the column ids of one row of
 // a compacted block mask): 64 consecutive entries are held one per lane and
 // read back with readlane, so a loop over the list issues no global load per
