@@ -628,9 +628,24 @@ __global__ void nsa_rev_ptr(const int* n_entries, const int* hist, int NK, int n
 // mode without the tokens placed before the chunk), and advances those
 // lanes by one, so an id a token lists twice is emitted twice.
 constexpr int kNoId = 0x7fffffff;
+// Minimum of x over lanes 0..15 (one DPP row), in every lane of that row.
+__device__ __forceinline__ int row_min16(int x) {
+  x = min(x, __builtin_amdgcn_update_dpp(kNoId, x, 0x128, 0xf, 0xf, false));  // row_ror:8
+  x = min(x, __builtin_amdgcn_update_dpp(kNoId, x, 0x124, 0xf, 0xf, false));  // row_ror:4
+  x = min(x, __builtin_amdgcn_update_dpp(kNoId, x, 0x122, 0xf, 0xf, false));  // row_ror:2
+  x = min(x, __builtin_amdgcn_update_dpp(kNoId, x, 0x121, 0xf, 0xf, false));  // row_ror:1
+  return x;
+}
+// Dynamic LDS of the list kernel: the group's rows (kNsaGroup * sbc ints),
+// then its ascending chunk list (cap entries of two ints).
+size_t nsa_group_lds_bytes(int sbc, int cap) {
+  return sizeof(int) * ((size_t)kNsaGroup * sbc + 2 * (size_t)cap);
+}
 __global__ __launch_bounds__(64) void nsa_group_chunks(NsaGeom g, const int* row_ptr,
                                                        const int* col, NsaGroups gr) {
-  __shared__ int rows[kNsaGroup * 128];  // sbc <= 128
+  extern __shared__ int dyn[];
+  int* rows = dyn;                         // [kNsaGroup][sbc]
+  int* lst = dyn + kNsaGroup * g.sbc;      // [cap][2]
   const int lane = threadIdx.x;
   const int unit = blockIdx.x;
   const int n2 = unit / gr.NG, gi = unit - n2 * gr.NG;
@@ -691,8 +706,8 @@ __global__ __launch_bounds__(64) void nsa_group_chunks(NsaGeom g, const int* row
       }
       if (m) {
         if (lane == 0) {
-          out[2 * count] = ks;
-          out[2 * count + 1] = (int)m;
+          lst[2 * count] = ks;
+          lst[2 * count + 1] = (int)m;
         }
         count++;
       }
@@ -704,13 +719,70 @@ __global__ __launch_bounds__(64) void nsa_group_chunks(NsaGeom g, const int* row
     }
   }
   if (lane == 0) gr.cnt[unit] = count;
+  __syncthreads();
+
+  // Window balancing.  The consumer walks the list four chunks (one window)
+  // per barrier, token j on wave j, so a window lasts as long as the SIMD
+  // with the most work in it; waves of a workgroup go to the SIMDs in turn,
+  // so token j works on SIMD j % 4.  Each window slot takes, among the next
+  // 16 chunks of the ascending list not yet placed (held by lanes 0..15), the
+  // one that keeps the window's largest per-SIMD token count lowest (the
+  // earliest on a tie).  Any order gives each token the same set of chunks;
+  // the online softmax is order-free up to rounding.
+  // Candidates: lanes 0..63 hold the next 64 unplaced chunks in list order
+  // (lanes past the list's end hold none).  A pick drops its lane and moves
+  // the lanes after it down by one (a whole-wave DPP shift), so after 16
+  // picks lanes 48..63 are empty and take the next 16 chunks.
+  int cks = 0, cm = 0, ok = 0;
+  if (lane < count) {
+    cks = lst[2 * lane];
+    cm = lst[2 * lane + 1];
+    ok = 1;
+  }
+  int fetched = 64;
+  int l0 = 0, l1 = 0, l2 = 0, l3 = 0;  // the window's tokens per SIMD
+  for (int k = 0; k < count; k++) {
+    if ((k & 3) == 0) l0 = l1 = l2 = l3 = 0;
+    const int a = max(max(l0 + __popc((unsigned)cm & 0x1111u), l1 + __popc((unsigned)cm & 0x2222u)),
+                      max(l2 + __popc((unsigned)cm & 0x4444u), l3 + __popc((unsigned)cm & 0x8888u)));
+    const int key = ok && lane < 16 ? a * 16 + lane : kNoId;
+    const int best = __builtin_amdgcn_readfirstlane(row_min16(key)) & 15;
+    const int bks = __builtin_amdgcn_readlane(cks, best);
+    const unsigned bm = (unsigned)__builtin_amdgcn_readlane(cm, best);
+    if (lane == 0) {
+      out[2 * k] = bks;
+      out[2 * k + 1] = (int)bm;
+    }
+    l0 += __popc(bm & 0x1111u);
+    l1 += __popc(bm & 0x2222u);
+    l2 += __popc(bm & 0x4444u);
+    l3 += __popc(bm & 0x8888u);
+    const int nks = __builtin_amdgcn_update_dpp(0, cks, 0x130, 0xf, 0xf, false);  // wave_shl:1
+    const int nm = __builtin_amdgcn_update_dpp(0, cm, 0x130, 0xf, 0xf, false);
+    const int nok = __builtin_amdgcn_update_dpp(0, ok, 0x130, 0xf, 0xf, false);
+    if (lane >= best) {
+      cks = nks;
+      cm = nm;
+      ok = nok;
+    }
+    if ((k & 15) == 15) {
+      const int e = fetched + lane - 48;
+      if (lane >= 48) {
+        ok = e < count;
+        cks = ok ? lst[2 * e] : 0;
+        cm = ok ? lst[2 * e + 1] : 0;
+      }
+      fetched += 16;
+    }
+  }
 }
 
 hipError_t launch_nsa_group_lists(const NsaGeom& g, const int* row_ptr, const int* col,
                                   const NsaGroups& gr, hipStream_t st) {
   const long units = (long)g.N2 * gr.NG;
   if (units == 0) return hipSuccess;
-  hipLaunchKernelGGL(nsa_group_chunks, dim3((unsigned)units), dim3(64), 0, st, g, row_ptr, col, gr);
+  hipLaunchKernelGGL(nsa_group_chunks, dim3((unsigned)units), dim3(64),
+                     nsa_group_lds_bytes(g.sbc, gr.cap), st, g, row_ptr, col, gr);
   return hipGetLastError();
 }
 
