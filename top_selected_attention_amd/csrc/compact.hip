@@ -707,7 +707,7 @@ __global__ __launch_bounds__(64) void nsa_group_chunks(NsaGeom g, const int* row
       if (m) {
         if (lane == 0) {
           lst[2 * count] = ks;
-          lst[2 * count + 1] = (int)m;
+          lst[2 * count + 1] = (int)(m | (sbs - kNsaGroupChunk * s < kNsaGroupChunk ? kNsaChunkHalf : 0u));
         }
         count++;
       }

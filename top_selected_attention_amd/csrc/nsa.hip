@@ -477,11 +477,12 @@ __global__ __launch_bounds__(kNsaGroup / TPW * 64) void nsa_fwd_grp_kernel(NsaPa
   auto tile_addr = [&](int buf, int slot, int kv) {
     return lds0 + (unsigned)(((buf * kGrpSlots + slot) * 2 + kv) * kGrpTile);
   };
-  auto nvalid_of = [&](int ks) { return min(kChunk, sbs - ks % sbs); };
+  auto nvalid_of = [&](unsigned msk) { return (msk & kNsaChunkHalf) ? kChunk / 2 : kChunk; };
   auto issue = [&](const GrpWin& wn, int w, int buf) {
     if (w * kGrpSlots + my_slot < cnt) {
       const int ks = __builtin_amdgcn_readlane(wn.ks, my_slot);
-      ld.issue(ks, nvalid_of(ks), tile_addr(buf, my_slot, wid & 1), lane);
+      const unsigned msk = (unsigned)__builtin_amdgcn_readlane(wn.msk, my_slot);
+      ld.issue(ks, nvalid_of(msk), tile_addr(buf, my_slot, wid & 1), lane);
     }
   };
 
@@ -490,9 +491,8 @@ __global__ __launch_bounds__(kNsaGroup / TPW * 64) void nsa_fwd_grp_kernel(NsaPa
   // One chunk for the tokens the compile-time flags A, B (tokens 0, 1 of the
   // wave) name: straight-line code, so every LDS read can be issued ahead of
   // the MFMAs that use it.
-  auto chunk = [&](auto A, auto B, unsigned Kt, int ks) {
+  auto chunk = [&](auto A, auto B, unsigned Kt, int ks, int nv) {
     constexpr bool sa = decltype(A)::value, sb = decltype(B)::value;
-    const int nv = nvalid_of(ks);
     const unsigned Vt = Kt + kGrpTile;
     V8 f[2][4];
 #pragma unroll
@@ -575,9 +575,10 @@ __global__ __launch_bounds__(kNsaGroup / TPW * 64) void nsa_fwd_grp_kernel(NsaPa
       if (!(sel0 || sel1)) continue;
       const int ks = __builtin_amdgcn_readlane(cur.ks, s);
       const unsigned Kt = tile_addr(w & 1, s, 0);
-      if (sel0 && sel1) chunk(std::true_type{}, std::true_type{}, Kt, ks);
-      else if (sel0) chunk(std::true_type{}, std::false_type{}, Kt, ks);
-      else chunk(std::false_type{}, std::true_type{}, Kt, ks);
+      const int nv = nvalid_of(msk);
+      if (sel0 && sel1) chunk(std::true_type{}, std::true_type{}, Kt, ks, nv);
+      else if (sel0) chunk(std::true_type{}, std::false_type{}, Kt, ks, nv);
+      else chunk(std::false_type{}, std::true_type{}, Kt, ks, nv);
     }
     cur = nxt;
     nxt = nn;
@@ -661,19 +662,19 @@ __global__ __launch_bounds__(kNsaGroup / TPW * 64) void nsa_dq_grp_kernel(NsaPar
   auto tile_addr = [&](int buf, int slot, int kv) {
     return lds0 + (unsigned)(((buf * kGrpSlots + slot) * 2 + kv) * kGrpTile);
   };
-  auto nvalid_of = [&](int ks) { return min(kChunk, sbs - ks % sbs); };
+  auto nvalid_of = [&](unsigned msk) { return (msk & kNsaChunkHalf) ? kChunk / 2 : kChunk; };
   auto issue = [&](const GrpWin& wn, int w, int buf) {
     if (w * kGrpSlots + my_slot < cnt) {
       const int ks = __builtin_amdgcn_readlane(wn.ks, my_slot);
-      ld.issue(ks, nvalid_of(ks), tile_addr(buf, my_slot, wid & 1), lane);
+      const unsigned msk = (unsigned)__builtin_amdgcn_readlane(wn.msk, my_slot);
+      ld.issue(ks, nvalid_of(msk), tile_addr(buf, my_slot, wid & 1), lane);
     }
   };
   const unsigned rd = grp_row_base(l16, gq), tt = grp_tr_base(l16, gq);
 
   // One chunk for the tokens the compile-time flags A, B name (see the forward).
-  auto chunk = [&](auto A, auto B, unsigned Kt, int ks) {
+  auto chunk = [&](auto A, auto B, unsigned Kt, int ks, int nv) {
     constexpr bool sa = decltype(A)::value, sb = decltype(B)::value;
-    const int nv = nvalid_of(ks);
     const unsigned Vt = Kt + kGrpTile;
     // element j of st[i][kt] / dpt[i][kt]: key ks + 16*kt + 4*gq + j, head l16
     f32x4_t st[2][2], dpt[2][2];
@@ -751,9 +752,10 @@ __global__ __launch_bounds__(kNsaGroup / TPW * 64) void nsa_dq_grp_kernel(NsaPar
       if (!(sel0 || sel1)) continue;
       const int ks = __builtin_amdgcn_readlane(cur.ks, s);
       const unsigned Kt = tile_addr(w & 1, s, 0);
-      if (sel0 && sel1) chunk(std::true_type{}, std::true_type{}, Kt, ks);
-      else if (sel0) chunk(std::true_type{}, std::false_type{}, Kt, ks);
-      else chunk(std::false_type{}, std::true_type{}, Kt, ks);
+      const int nv = nvalid_of(msk);
+      if (sel0 && sel1) chunk(std::true_type{}, std::true_type{}, Kt, ks, nv);
+      else if (sel0) chunk(std::true_type{}, std::false_type{}, Kt, ks, nv);
+      else chunk(std::false_type{}, std::true_type{}, Kt, ks, nv);
     }
     cur = nxt;
     nxt = nn;

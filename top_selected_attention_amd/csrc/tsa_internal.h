@@ -58,6 +58,9 @@ struct NsaGeom {
 // listing a block twice attends to its chunks twice).
 constexpr int kNsaGroup = 16;
 constexpr int kNsaGroupChunk = 32;
+// set in an entry's mask word when its chunk holds 16 keys, not 32 (the tail
+// of a block whose size is an odd multiple of 16)
+constexpr unsigned kNsaChunkHalf = 1u << 30;
 struct NsaGroups {
   const int* gcu;  // [B+1] prefix sums of ceil(Sq_b / kNsaGroup)
   int NG;          // groups per KV head
