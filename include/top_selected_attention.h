@@ -268,9 +268,11 @@ typedef struct {
   const void* v;            /* DEVICE */
   void* out;                /* DEVICE, written */
   float* lse;               /* DEVICE, written */
-  int32_t reuse_lists;      /* 0: build the per-row lists (the reverse lists are left to the
-                               backward); 1: they are there from an earlier call with the same
-                               indices on this workspace; other values: TSA_ERR_INVALID */
+  int32_t reuse_lists;      /* 0: build the per-row lists (and, for head groups of up to 16
+                               with 128-dim heads, the token-group chunk lists the forward and
+                               dQ kernels walk; the reverse lists are left to the backward);
+                               1: they are there from an earlier call with the same indices on
+                               this workspace; other values: TSA_ERR_INVALID */
   int32_t n_events;         /* number of stages to time (0 = off) */
   void* const* events;      /* HOST array of 2*n_events hipEvent_t: events[2i] / [2i+1] are
                                recorded on `stream` before / after stage i (see each entry) */
@@ -304,9 +306,10 @@ typedef struct {
   void* dv;                 /* DEVICE, written [Tk, N2, Dv] */
   int32_t reuse_lists;      /* 0: build per-row and reverse lists; 1: both are there from an
                                earlier nsa_select_bwd call with the same indices on this
-                               workspace; 2: the per-row lists are there from an earlier
-                               nsa_select_fwd call with the same indices and cu_seqlens on this
-                               workspace (its size being this call's): build only the reverse
+                               workspace; 2: the per-row (and token-group) lists are there
+                               from an earlier nsa_select_fwd call with the same indices and
+                               cu_seqlens on this workspace (its size being this call's):
+                               build only the reverse
                                lists; other values: TSA_ERR_INVALID */
   int32_t n_events;         /* number of stages to time (0 = off) */
   void* const* events;      /* HOST array of 2*n_events hipEvent_t: events[2i] / [2i+1] are
