@@ -114,9 +114,7 @@ KERNEL_SOURCES = {
     "bsa_dq_kernel": ["bsa_bwd.hip"],
     "bsa_dkdv_kernel": ["bsa_bwd.hip"],
     "nsa_fwd_kernel": ["nsa.hip"],
-    "nsa_fwd16_kernel": ["nsa.hip"],
     "nsa_dq_kernel": ["nsa.hip"],
-    "nsa_dq16_kernel": ["nsa.hip"],
     "nsa_fwd_grp_kernel": ["nsa.hip"],
     "nsa_dq_grp_kernel": ["nsa.hip"],
     "nsa_dkdv_seg_kernel": ["nsa.hip"],
