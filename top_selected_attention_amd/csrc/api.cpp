@@ -166,7 +166,7 @@ size_t bsa_carve(const A* a, void* ws, BsaWs* out, bool with_delta) {
   const BsaDkdvShape ds = bsa_dkdv_shape(a->B, a->N1, a->N2, QB, KB, a->block_kv);
   w.seg_off = c.take<int>(ds.n_items + 1);
   w.part_off = c.take<int>(ds.n_items + 1);
-  w.seg_meta = c.take<int>(1);
+  w.seg_meta = c.take<int>(2 + kBsaDkdvSlots);
   // per row: LSE in base 2 and softmax_grad, interleaved
   w.delta = with_delta ? c.take<float>(2L * a->B * a->N1 * a->Sq) : nullptr;
   w.part = with_delta ? c.take<float>(ds.max_parts * 2 * ds.nk * 128) : nullptr;

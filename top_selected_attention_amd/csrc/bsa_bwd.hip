@@ -498,16 +498,21 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 
 // Sums the segments' fp32 partials of each split dK/dV work item in segment
 // order (fixed order: bit-identical reruns) and writes dK (times scale) and
-// dV.  One workgroup per work item; items with one segment wrote their rows
-// themselves.
+// dV.  Items with one segment wrote their rows themselves; the grid covers
+// only the split items (their ranks listed by the segment plan), with
+// kReduceParts workgroups per item, each a slice of its rows (a thread then
+// sums a handful of 16-byte columns, so the segments' loads of one item are
+// in flight together).
+constexpr int kReduceParts = 8;
 template <class E, int NW>
-__global__ __launch_bounds__(256) void bsa_dkdv_reduce(BsaParams p, int ksub, int n_items) {
+__global__ __launch_bounds__(256) void bsa_dkdv_reduce(BsaParams p, int ksub) {
   typedef typename E::T T;
   constexpr int NK = NW * 32;
-  const int rank = blockIdx.x;
-  if (rank >= n_items) return;
+  constexpr int kPer = 2 * NK * (kD / 4) / kReduceParts;  // 16-byte columns per workgroup
+  static_assert(kPer % 256 == 0, "whole passes of the workgroup");
+  if ((int)blockIdx.x >= p.seg_meta[1]) return;
+  const int rank = p.seg_meta[2 + blockIdx.x];
   const int nseg = p.seg_off[rank + 1] - p.seg_off[rank];
-  if (nseg <= 1) return;
   const int ksl = rank % ksub;
   const int tile = p.order_kv[rank / ksub];
   const int kb = tile % p.KB, bh = tile / p.KB;
@@ -516,12 +521,13 @@ __global__ __launch_bounds__(256) void bsa_dkdv_reduce(BsaParams p, int ksub, in
   const int key_lo = kb * p.bkv + ksl * NK;
   const int key_hi = min((kb + 1) * p.bkv, km.len);
   const float* base = p.part + (long)p.part_off[rank] * 2 * NK * kD;
-  for (int i = threadIdx.x; i < 2 * NK * (kD / 4); i += 256) {
+  for (int i = blockIdx.y * kPer + threadIdx.x; i < (blockIdx.y + 1) * kPer; i += 256) {
     const int which = i / (NK * (kD / 4));  // 0 dK, 1 dV
     const int kk = (i / (kD / 4)) % NK, d4 = i % (kD / 4);
     const int key = key_lo + kk;
     if (key >= key_hi) continue;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
     for (int sgi = 0; sgi < nseg; sgi++) {
       const float4 x = *reinterpret_cast<const float4*>(
           base + ((long)sgi * 2 * NK + which * NK + kk) * kD + 4 * d4);
@@ -567,9 +573,12 @@ static hipError_t launch_dkdv_t(const BsaParams& p, hipStream_t st, void* const*
   }
   if (e == hipSuccess) e = mark_event(ev, n_ev, 2, 1, st);
   if (e == hipSuccess) e = mark_event(ev, n_ev, 3, 0, st);
-  if (e == hipSuccess && n_items > 0) {
-    hipLaunchKernelGGL((bsa_dkdv_reduce<E, NW>), dim3(n_items), dim3(256), 0, st, p, ksub,
-                       n_items);
+  // fewer than kBsaDkdvSlots split items, and at most half the partial slots
+  const BsaDkdvShape ds = bsa_dkdv_shape(p.B, p.N1, p.N2, p.QB, p.KB, p.bkv);
+  const int max_split = (int)std::min<long>(kBsaDkdvSlots, ds.max_parts / 2);
+  if (e == hipSuccess && n_items > 0 && max_split > 0) {
+    hipLaunchKernelGGL((bsa_dkdv_reduce<E, NW>), dim3(max_split, kReduceParts), dim3(256), 0, st,
+                       p, ksub);
     e = hipGetLastError();
   }
   if (e == hipSuccess) e = mark_event(ev, n_ev, 3, 1, st);

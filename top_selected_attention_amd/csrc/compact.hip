@@ -304,13 +304,14 @@ constexpr int kOrderBins = 256;
 // max(1, ceil(L / S)) segments, and fp32 partial slots only when it has more
 // than one: fewer than 2 * kBsaDkdvSlots slots in all (each split item has
 // L > S, so ceil(L / S) < 2 L / S).  Writes exclusive prefix sums with their
-// totals at [n_items].
+// totals at [n_items], and the split items' ranks in ascending order at
+// seg_meta[2..] with their count at seg_meta[1] (fewer than kBsaDkdvSlots).
 __device__ void bsa_seg_plan(const int* rev_ptr, int n_tiles, const int* order, int ksub,
                              int n_items, int* seg_off, int* part_off, int* seg_meta) {
   const long E = rev_ptr[n_tiles];
   const int S = (int)max(1L, (E * ksub + kBsaDkdvSlots - 1) / kBsaDkdvSlots);
   if (threadIdx.x == 0) seg_meta[0] = S;
-  int carry_s = 0, carry_p = 0;
+  int carry_s = 0, carry_p = 0, carry_x = 0;
   for (int base = 0; base < n_items; base += blockDim.x) {
     const int r = base + threadIdx.x;
     int ns = 0;
@@ -319,19 +320,25 @@ __device__ void bsa_seg_plan(const int* rev_ptr, int n_tiles, const int* order, 
       ns = max(1, (rev_ptr[tile + 1] - rev_ptr[tile] + S - 1) / S);
     }
     const int np = ns > 1 ? ns : 0;
-    int ts, tp;
+    int ts;
     const int es = block_excl_scan(ns, &ts);
-    const int ep = block_excl_scan(np, &tp);
+    // partial slots (fewer than 2^16 in all) in the low half, split items in
+    // the high half: one scan for both
+    int tpx;
+    const int epx = block_excl_scan(np | (np > 0 ? 1 << 16 : 0), &tpx);
     if (r < n_items) {
       seg_off[r] = carry_s + es;
-      part_off[r] = carry_p + ep;
+      part_off[r] = carry_p + (epx & 0xffff);
+      if (np > 0) seg_meta[2 + carry_x + (epx >> 16)] = r;
     }
     carry_s += ts;
-    carry_p += tp;
+    carry_p += tpx & 0xffff;
+    carry_x += tpx >> 16;
   }
   if (threadIdx.x == 0) {
     seg_off[n_items] = carry_s;
     part_off[n_items] = carry_p;
+    seg_meta[1] = carry_x;
   }
 }
 

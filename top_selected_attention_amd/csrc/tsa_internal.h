@@ -119,10 +119,11 @@ struct BsaParams {
   // backward dK/dV segments (workspace): work item r (in order_kv order) has
   // seg_off[r+1] - seg_off[r] segments of at most seg_meta[0] reverse-list
   // entries; a split item's segments write fp32 partials from slot
-  // part_off[r] on, which a reduction sums in segment order.
+  // part_off[r] on, which a reduction sums in segment order.  seg_meta: the
+  // segment length, the count of split items and their ranks.
   int* seg_off;        // [n_items + 1]
   int* part_off;       // [n_items + 1]
-  int* seg_meta;       // [1]
+  int* seg_meta;       // [2 + kBsaDkdvSlots]
   float* part;         // [kBsaMaxParts][2][keys per item][D]
 };
 
