@@ -783,7 +783,8 @@ def _step_stats(ms):
 
 def measured_peaks():
     """What this machine sustains, beside the published peaks: the library's own
-    MFMA issue and HBM copy / read kernels (libtsa_peaks.so), and
+    MFMA issue and HBM copy / read kernels (libtsa_peaks.so; the read also of
+    a buffer the memory-side cache holds), and
     torch.matmul (hipBLASLt) of two 8192 x 8192 bf16 matrices."""
     import torch
     from top_selected_attention_amd import peaks
@@ -795,7 +796,9 @@ def measured_peaks():
     res["hipblaslt_bf16_gemm_tflops"] = round(2 * 8192 ** 3 / (ms * 1e-3) / 1e12, 1)
     res["how"] = ("MFMA: 4 independent 32x32x16 chains per wave, 2048 x 256 threads; "
                   "HBM: 1 GiB with nontemporal 16-byte loads / stores, 8192 x 256 threads, copy "
-                  "counts read + write; GEMM: torch.matmul 8192^3 bf16")
+                  "counts read + write; MALL: 160 MiB read with plain 16-byte loads after "
+                  "warm-up reads (past the L2s, inside the memory-side cache); GEMM: "
+                  "torch.matmul 8192^3 bf16")
     return res
 
 

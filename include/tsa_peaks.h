@@ -39,11 +39,16 @@ int tsa_peak_mfma(int dtype, int n_blocks, int iters, float a, float* out,
  * (1 <= n_blocks <= 65536).  HBM traffic: 2 * bytes. */
 int tsa_peak_copy(const void* src, void* dst, size_t bytes, int n_blocks, void* stream);
 
-/* Reads `bytes` bytes (a multiple of 16, 16-byte aligned) with 16-byte vector
- * loads over a grid-stride loop and writes, per workgroup, the xor of every
+/* Reads `bytes` bytes (a multiple of 16, 16-byte aligned) with nontemporal
+ * 16-byte vector loads over a grid-stride loop and writes, per workgroup, the xor of every
  * 32-bit word it read to out[blk] (device, n_blocks words).  HBM traffic:
  * bytes.  Limits as for tsa_peak_copy. */
 int tsa_peak_read(const void* src, size_t bytes, int n_blocks, unsigned* out, void* stream);
+
+/* As tsa_peak_read with plain (cached) loads: a buffer larger than the L2s
+ * (4 MB per XCD) and smaller than the 256 MB memory-side cache (MALL), read
+ * twice in a row, is then served from the MALL the second time. */
+int tsa_peak_read_cached(const void* src, size_t bytes, int n_blocks, unsigned* out, void* stream);
 
 /* Test aid: 4096 workgroups of 256 threads, one wave per SIMD at 512
  * registers each, write `pattern` into all 256 VGPRs and 256 AGPRs of their

@@ -23,7 +23,7 @@ def _lib():
 def test_exports_match_header():
     names = re.findall(r"^int (tsa_\w+)\(", open(HEADER).read(), re.M)
     assert sorted(names) == ["tsa_fill_registers", "tsa_peak_copy", "tsa_peak_mfma",
-                             "tsa_peak_read"]
+                             "tsa_peak_read", "tsa_peak_read_cached"]
     L = _lib()
     for n in names:
         assert hasattr(L, n), n
@@ -37,6 +37,7 @@ def test_invalid_arguments_rejected_before_launch():
                                 ctypes.c_void_p]
     L.tsa_peak_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p,
                                 ctypes.c_void_p]
+    L.tsa_peak_read_cached.argtypes = L.tsa_peak_read.argtypes
     fl = ctypes.c_double()
     fake = ctypes.c_void_p(0x1000)
     assert L.tsa_peak_mfma(2, 1, 1, 1.0, fake, ctypes.byref(fl), None) == -1    # dtype
@@ -48,6 +49,8 @@ def test_invalid_arguments_rejected_before_launch():
     assert L.tsa_peak_copy(fake, ctypes.c_void_p(0x1010), 64, 1, None) == -1    # overlap
     assert L.tsa_peak_read(fake, 16, 0, fake, None) == -1                       # no blocks
     assert L.tsa_peak_read(None, 16, 1, fake, None) == -1                       # null src
+    assert L.tsa_peak_read_cached(fake, 16, 0, fake, None) == -1                # no blocks
+    assert L.tsa_peak_read_cached(fake, 24, 1, fake, None) == -1                # not 16-byte sized
 
 
 @pytest.mark.gpu
@@ -74,8 +77,10 @@ def test_copy_and_read_are_exact():
     peaks.copy(xd, yd, n_blocks=64)
     o = torch.zeros(64, dtype=torch.int32, device="cuda")
     peaks.read(xd, o, n_blocks=64)
+    oc = torch.zeros(64, dtype=torch.int32, device="cuda")
+    peaks.read(xd, oc, n_blocks=64, cached=True)
     torch.cuda.synchronize()
     assert torch.equal(yd.cpu(), x)
-    got = np.bitwise_xor.reduce(o.cpu().numpy().view(np.uint32))
     want = np.bitwise_xor.reduce(x.numpy().view(np.uint32))
-    assert got == want
+    for out in (o, oc):
+        assert np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32)) == want

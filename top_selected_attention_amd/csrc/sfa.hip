@@ -747,6 +747,7 @@ __global__ __launch_bounds__(256) void sfa_task_kernel(SfaParams p) {
   const int total = sfa_total_slots(p);
   const int nch = (total + kKeys - 1) / kKeys;
   const int* topk = p.topk + tk * p.topk_n;
+  const int max_id = (t_len - 1) / p.sbs;  // ids above it start past the cache
   auto weight = [&](int c) {
     if (c >= nch) return 0;
     const int lo = c * kKeys, hi = min(lo + kKeys, total);
@@ -756,14 +757,31 @@ __global__ __launch_bounds__(256) void sfa_task_kernel(SfaParams p) {
       const int e = min(min(hi, p.win_len), kv_len - qpos + p.win_left);
       kept = max(0, e - a);
     } else {
-      // a fixed-length loop: the chunk's id loads issue back to back
+      // slot lo + u is entry ent[u] of the token's top-k row, offset off[u]
+      // within that sparse block: one division per chunk, then a walk.  The
+      // id loads are unconditional (entries clamped into the row; slots past
+      // hi are dropped below), so they issue back to back.
+      int ent[kKeys], off[kKeys];
+      {
+        const int r0 = lo - p.win_pad;
+        int e = r0 / p.sbs, o = r0 - e * p.sbs;
+#pragma unroll
+        for (int u = 0; u < kKeys; u++) {
+          ent[u] = min(e, p.topk_n - 1);
+          off[u] = o;
+          if (++o == p.sbs) {
+            o = 0;
+            ++e;
+          }
+        }
+      }
       int id[kKeys];
 #pragma unroll
-      for (int u = 0; u < kKeys; u++) id[u] = lo + u < hi ? topk[(lo + u - p.win_pad) / p.sbs] : -1;
+      for (int u = 0; u < kKeys; u++) id[u] = topk[ent[u]];
 #pragma unroll
       for (int u = 0; u < kKeys; u++) {
-        const bool idok = id[u] >= 0 && id[u] <= (t_len - 1) / p.sbs;
-        const int pos = idok ? id[u] * p.sbs + (lo + u - p.win_pad) % p.sbs : 0;
+        const bool idok = lo + u < hi && id[u] >= 0 && id[u] <= max_id;
+        const int pos = idok ? id[u] * p.sbs + off[u] : 0;
         kept += idok && pos < t_len && pos <= t_qpos;
       }
     }

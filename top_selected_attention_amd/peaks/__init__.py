@@ -1,6 +1,7 @@
 """What this chip sustains, measured with the kernels of libtsa_peaks.so
-(declared in include/tsa_peaks.h): dense bf16 / fp16 MFMA issue rate and HBM
-copy / read bandwidth.  Launches go to torch's current stream and are timed
+(declared in include/tsa_peaks.h): dense bf16 / fp16 MFMA issue rate, HBM
+copy / read bandwidth, and the read bandwidth of data that misses the L2s
+but stays in the 256 MB memory-side cache (MALL).  Launches go to torch's current stream and are timed
 with events on it."""
 
 import ctypes
@@ -25,8 +26,10 @@ def lib():
                                     ctypes.c_int, ctypes.c_void_p]
         L.tsa_peak_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
                                     ctypes.c_void_p, ctypes.c_void_p]
+        L.tsa_peak_read_cached.argtypes = L.tsa_peak_read.argtypes
         L.tsa_fill_registers.argtypes = [ctypes.c_uint, ctypes.c_void_p]
-        for f in (L.tsa_peak_mfma, L.tsa_peak_copy, L.tsa_peak_read, L.tsa_fill_registers):
+        for f in (L.tsa_peak_mfma, L.tsa_peak_copy, L.tsa_peak_read, L.tsa_peak_read_cached,
+                  L.tsa_fill_registers):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -60,12 +63,15 @@ def copy(src, dst, n_blocks=8192):
            "tsa_peak_copy")
 
 
-def read(src, out, n_blocks=8192):
+def read(src, out, n_blocks=8192, cached=False):
+    """Reads all of src (nontemporal loads, or plain ones with cached=True);
+    out[b] = xor of the words workgroup b read."""
     if out.numel() * out.element_size() < 4 * n_blocks:
         raise ValueError("out holds fewer than n_blocks words")
-    _check(lib().tsa_peak_read(ctypes.c_void_p(src.data_ptr()), src.numel() * src.element_size(),
-                               n_blocks, ctypes.c_void_p(out.data_ptr()), _stream()),
-           "tsa_peak_read")
+    f = lib().tsa_peak_read_cached if cached else lib().tsa_peak_read
+    _check(f(ctypes.c_void_p(src.data_ptr()), src.numel() * src.element_size(), n_blocks,
+             ctypes.c_void_p(out.data_ptr()), _stream()),
+           "tsa_peak_read_cached" if cached else "tsa_peak_read")
 
 
 def fill_registers(pattern):
@@ -104,4 +110,10 @@ def measure(n_bytes=1 << 30):
     res["hbm_copy_gbs"] = round(2 * n_bytes / (ms * 1e-3) / 1e9, 1)
     ms = _timed(lambda: read(x, o), 20)
     res["hbm_read_gbs"] = round(n_bytes / (ms * 1e-3) / 1e9, 1)
+    # 160 MiB with plain loads: far past the eight 4 MB L2s, inside the MALL
+    # once read (the warm-up reads of _timed bring it in)
+    m_bytes = 160 << 20
+    xm = x[: m_bytes // 4]
+    ms = _timed(lambda: read(xm, o, cached=True), 50)
+    res["mall_read_gbs"] = round(m_bytes / (ms * 1e-3) / 1e9, 1)
     return res

@@ -61,6 +61,15 @@ __global__ __launch_bounds__(kThreads) void peak_copy_kernel(const u32x4* __rest
   for (; i < n; i += stride) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
 
+// NT: nontemporal loads (streamed past the caches); plain loads otherwise, so
+// that a buffer read twice can be served by the memory-side cache.
+template <bool NT>
+__device__ __forceinline__ u32x4 peak_load(const u32x4* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+
+template <bool NT>
 __global__ __launch_bounds__(kThreads) void peak_read_kernel(const u32x4* __restrict__ src, size_t n,
                                                              unsigned* out) {
   __shared__ unsigned wx[kThreads / 64];
@@ -68,13 +77,13 @@ __global__ __launch_bounds__(kThreads) void peak_read_kernel(const u32x4* __rest
   size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x;
   u32x4 acc = {0u, 0u, 0u, 0u};
   for (; i + 3 * stride < n; i += 4 * stride) {
-    u32x4 v0 = __builtin_nontemporal_load(src + i);
-    u32x4 v1 = __builtin_nontemporal_load(src + i + stride);
-    u32x4 v2 = __builtin_nontemporal_load(src + i + 2 * stride);
-    u32x4 v3 = __builtin_nontemporal_load(src + i + 3 * stride);
+    u32x4 v0 = peak_load<NT>(src + i);
+    u32x4 v1 = peak_load<NT>(src + i + stride);
+    u32x4 v2 = peak_load<NT>(src + i + 2 * stride);
+    u32x4 v3 = peak_load<NT>(src + i + 3 * stride);
     acc ^= v0 ^ v1 ^ v2 ^ v3;
   }
-  for (; i < n; i += stride) acc ^= __builtin_nontemporal_load(src + i);
+  for (; i < n; i += stride) acc ^= peak_load<NT>(src + i);
   unsigned x = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
   for (int o = 32; o > 0; o >>= 1) x ^= __shfl_xor(x, o);
   if ((threadIdx.x & 63) == 0) wx[threadIdx.x >> 6] = x;
@@ -127,8 +136,17 @@ extern "C" __attribute__((visibility("default")))
 int tsa_peak_read(const void* src, size_t bytes, int n_blocks, unsigned* out, void* stream) {
   if (!src || !out || bytes % 16 || (uintptr_t)src % 16 || n_blocks < 1 || n_blocks > 65536)
     return -1;
-  peak_read_kernel<<<n_blocks, kThreads, 0, (hipStream_t)stream>>>((const u32x4*)src, bytes / 16,
+  peak_read_kernel<true><<<n_blocks, kThreads, 0, (hipStream_t)stream>>>((const u32x4*)src, bytes / 16,
                                                                    out);
+  return launched();
+}
+
+extern "C" __attribute__((visibility("default")))
+int tsa_peak_read_cached(const void* src, size_t bytes, int n_blocks, unsigned* out, void* stream) {
+  if (!src || !out || bytes % 16 || (uintptr_t)src % 16 || n_blocks < 1 || n_blocks > 65536)
+    return -1;
+  peak_read_kernel<false><<<n_blocks, kThreads, 0, (hipStream_t)stream>>>((const u32x4*)src,
+                                                                    bytes / 16, out);
   return launched();
 }
 
