@@ -266,8 +266,9 @@ hipError_t bsa_build_lists(const A* a, const BsaWs& w, const BsaParams& p, hipSt
     e = launch_bsa_compact(a->block_mask, a->B, a->N1, a->N2, p.QB, p.KB, w.parts, w.sums,
                            w.row_ptr, w.col, w.rev_ptr, w.rev, st);
   } else {
-    e = hipMemsetAsync(w.row_ptr, 0, sizeof(int) * (R + 1), st);
-    if (e == hipSuccess) e = hipMemsetAsync(w.rev_ptr, 0, sizeof(int) * (C + 1), st);
+    // fill kernels rather than memset nodes, so that a captured call replays them
+    e = launch_fill_i32(w.row_ptr, (int)(R + 1), 0, st);
+    if (e == hipSuccess) e = launch_fill_i32(w.rev_ptr, (int)(C + 1), 0, st);
   }
   if (e == hipSuccess)
     e = launch_tile_order(w.row_ptr, (int)R, w.order_q, w.rev_ptr, (int)C, w.order_kv,
@@ -473,7 +474,7 @@ enum NsaListParts { kNsaForward = 1, kNsaReverse = 2, kNsaAll = 3 };
 template <class A>
 int nsa_lists(const A* a, const NsaWs& w, const NsaGeom& g, int parts, hipStream_t st) {
   if (a->validate && (parts & kNsaForward)) {
-    hipError_t e = hipMemsetAsync(w.bad, 0, sizeof(int), st);
+    hipError_t e = launch_fill_i32(w.bad, 1, 0, st);
     if (e == hipSuccess) e = launch_nsa_check(a->topk, g, w.bad, st);
     int bad = 0;
     if (e == hipSuccess) e = hipMemcpyAsync(&bad, w.bad, sizeof(int), hipMemcpyDeviceToHost, st);
@@ -838,9 +839,8 @@ int bsa_compact(const bsa_fwd_args* a, int32_t* row_ptr, int32_t* col, int32_t* 
   const int QB = (int)cdiv(a->Sq, a->block_q), KB = (int)cdiv(a->Skv, a->block_kv);
   hipStream_t st = (hipStream_t)stream;
   if ((long)a->B * QB * KB == 0) {
-    hipError_t e = hipMemsetAsync(row_ptr, 0, sizeof(int) * ((long)a->B * a->N1 * QB + 1), st);
-    if (e == hipSuccess)
-      e = hipMemsetAsync(rev_ptr, 0, sizeof(int) * ((long)a->B * a->N2 * KB + 1), st);
+    hipError_t e = launch_fill_i32(row_ptr, (int)((long)a->B * a->N1 * QB + 1), 0, st);
+    if (e == hipSuccess) e = launch_fill_i32(rev_ptr, (int)((long)a->B * a->N2 * KB + 1), 0, st);
     return hip_status(e);
   }
   return hip_status(launch_bsa_compact(a->block_mask, a->B, a->N1, a->N2, QB, KB, w.parts, w.sums,
@@ -1022,7 +1022,7 @@ int nsa_select_bwd(const nsa_select_bwd_args* a, void* ws, size_t ws_bytes, void
       s = nsa_lists(a, w, p.g, kNsaAll, st);
       if (s) return s;
     } else {
-      if (hipMemsetAsync(w.rev_ptr, 0, sizeof(int) * ((long)a->N2 * p.g.NB + 1), st) != hipSuccess)
+      if (launch_fill_i32(w.rev_ptr, (int)((long)a->N2 * p.g.NB + 1), 0, st) != hipSuccess)
         return TSA_ERR_HIP;
     }
   } else {

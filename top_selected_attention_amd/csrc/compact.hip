@@ -857,7 +857,7 @@ hipError_t launch_nsa_reverse_lists(const NsaGeom& g, const int* row_ptr, const 
                                     int* hist, int* hsums, hipStream_t st) {
   // reverse: counts -> scan -> fill
   const long rrows = (long)g.N2 * g.NB;
-  if (rrows == 0) return hipMemsetAsync(rev_ptr, 0, sizeof(int), st);
+  if (rrows == 0) return launch_fill_i32(rev_ptr, 1, 0, st);
   if (ekey && rs.usable) {
     const int* n_entries = row_ptr + (long)g.T * g.N2;
     const size_t lds = sizeof(int) * rs.NK;
