@@ -635,6 +635,9 @@ __global__ void nsa_rev_ptr(const int* n_entries, const int* hist, int NK, int n
 // mode without the tokens placed before the chunk), and advances those
 // lanes by one, so an id a token lists twice is emitted twice.
 constexpr int kNoId = 0x7fffffff;
+// A group whose ids span at most this many blocks, with no id listed twice by
+// one token, takes the bitmap path below instead of the merge.
+constexpr int kGroupBitmapIds = 1024;
 // Minimum of x over lanes 0..15 (one DPP row), in every lane of that row.
 __device__ __forceinline__ int row_min16(int x) {
   x = min(x, __builtin_amdgcn_update_dpp(kNoId, x, 0x128, 0xf, 0xf, false));  // row_ror:8
@@ -689,9 +692,76 @@ __global__ __launch_bounds__(64) void nsa_group_chunks(NsaGeom g, const int* row
   const int cpb = (sbs + kNsaGroupChunk - 1) / kNsaGroupChunk;
   int* out = gr.ent + (long)unit * gr.cap * 2;
   static_assert(kNsaGroup <= 16, "one DPP row of lanes holds the group's tokens");
-  // lane j's cursor c, its id (head) and the id after it (nxt)
-  int c = 0, count = 0;
-  int head = c < n ? rows[lane * sbc] : kNoId;  // lanes >= ntok have n = 0
+  // Mask of the tokens (bit j: token p0 + j) that attend to chunk s of block
+  // id, given the tokens that listed the block: under causal mode the tokens
+  // placed before the chunk's first key drop out.
+  auto chunk_mask = [&](int id, unsigned sel, int s) {
+    unsigned m = sel;
+    if (g.causal) {
+      const int d = id * sbs + kNsaGroupChunk * s - p0;  // tokens j < d sit before the chunk
+      if (d >= 32) m = 0u;
+      else if (d > 0) m &= ~((1u << d) - 1u);
+    }
+    return m;
+  };
+  auto half_flag = [&](int s) {
+    return sbs - kNsaGroupChunk * s < kNsaGroupChunk ? kNsaChunkHalf : 0u;
+  };
+  int count = 0;
+  // Bitmap path: every listed (token, id) ORs the token's bit into the id's
+  // LDS word, then one ascending pass over the words emits each listed id's
+  // chunks, placed by a wave prefix sum.  It gives the list the merge below
+  // gives, without a serial step per id, when the group's ids span at most
+  // kGroupBitmapIds blocks and no token lists an id twice (rows are sorted,
+  // so a repeat sits next to its twin); otherwise the merge runs.
+  __shared__ unsigned bm[kGroupBitmapIds];
+  bool merged = false;
+  {
+    int lo = n > 0 ? rows[lane * sbc] : kNoId;        // lanes >= ntok have n = 0
+    int hi = n > 0 ? rows[lane * sbc + n - 1] : -1;
+    lo = __builtin_amdgcn_readfirstlane(row_min16(lo));
+    hi = -__builtin_amdgcn_readfirstlane(row_min16(-hi));
+    if (lo != kNoId && hi - lo < kGroupBitmapIds) {
+      const int W = hi - lo + 1;
+      for (int i = lane; i < W; i += 64) bm[i] = 0u;
+      __syncthreads();
+      bool odd = false;  // a repeated (or out-of-order) id
+      for (int i0 = 0; i0 < tot; i0 += 64) {
+        const int i = i0 + lane;
+        const int j = min(i / sbc, kNsaGroup - 1), e = i - j * sbc;
+        const int nj = __shfl(n, j);
+        const bool live = i < tot && e < nj;
+        const int v = live ? rows[i] : lo;
+        if (live && ((e > 0 && rows[i - 1] >= v) || v < lo || v > hi)) odd = true;
+        else if (live) atomicOr(&bm[v - lo], 1u << j);
+      }
+      const bool any_odd = __ballot(odd) != 0;
+      __syncthreads();
+      if (!any_odd) {
+        for (int i0 = 0; i0 < W; i0 += 64) {
+          const int i = i0 + lane;
+          const unsigned sel = i < W ? bm[i] : 0u;
+          int mine = 0;
+          for (int s = 0; s < cpb; s++) mine += chunk_mask(lo + i, sel, s) != 0u;
+          const int incl = wave_incl_scan(mine);
+          int pos = count + incl - mine;
+          for (int s = 0; s < cpb; s++) {
+            const unsigned m = chunk_mask(lo + i, sel, s);
+            if (m) {
+              lst[2 * pos] = (lo + i) * sbs + kNsaGroupChunk * s;
+              lst[2 * pos + 1] = (int)(m | half_flag(s));
+              pos++;
+            }
+          }
+          count += __shfl(incl, 63);
+        }
+        merged = true;
+      }
+    }
+  }
+  // Merge: lane j's cursor c, its id (head) and the id after it (nxt)
+  int c = 0;
+  int head = merged ? kNoId : (c < n ? rows[lane * sbc] : kNoId);
   int nxt = c + 1 < n ? rows[lane * sbc + 1] : kNoId;
   while (true) {
     // minimum over lanes 0..15 by row rotations (DPP), read from lane 0
@@ -704,17 +774,11 @@ __global__ __launch_bounds__(64) void nsa_group_chunks(NsaGeom g, const int* row
     if (mn == kNoId) break;
     const unsigned sel = (unsigned)__ballot(lane < 16 && head == mn);
     for (int s = 0; s < cpb; s++) {
-      const int ks = mn * sbs + kNsaGroupChunk * s;
-      unsigned m = sel;
-      if (g.causal) {
-        const int d = ks - p0;  // tokens j < d sit before the chunk
-        if (d >= 32) m = 0u;
-        else if (d > 0) m &= ~((1u << d) - 1u);
-      }
+      const unsigned m = chunk_mask(mn, sel, s);
       if (m) {
         if (lane == 0) {
-          lst[2 * count] = ks;
-          lst[2 * count + 1] = (int)(m | (sbs - kNsaGroupChunk * s < kNsaGroupChunk ? kNsaChunkHalf : 0u));
+          lst[2 * count] = mn * sbs + kNsaGroupChunk * s;
+          lst[2 * count + 1] = (int)(m | half_flag(s));
         }
         count++;
       }
