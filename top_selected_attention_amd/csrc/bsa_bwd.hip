@@ -175,6 +175,8 @@ __global__ __launch_bounds__(NW * 64) void bsa_dq_kernel(BsaParams p, int qsub, 
         st = E::mfma32(lds_read16<V8>(Kr + kt * 32 * kPadPitch + 32 * ds), qreg[ds], st);
         dpt = E::mfma32(lds_read16<V8>(Vr + kt * 32 * kPadPitch + 32 * ds), doreg[ds], dpt);
       }
+      // one K and one V read per MFMA, four reads ahead
+      sched_mfma_lds<16, 1, 4>();
       // dS^T = P^T * (dP^T - D), P^T = exp2(S^T * scale*log2e - LSE2);
       // element j is key ks + kt*32 + 8*(j/4) + 4*h + j%4.  Outside a full
       // chunk, key offsets above this lane's limit are masked (two copies of
@@ -205,6 +207,7 @@ __global__ __launch_bounds__(NW * 64) void bsa_dq_kernel(BsaParams p, int qsub, 
         for (int dt = 0; dt < 4; dt++)
           dq[dt] = E::mfma32(ptile_tr<V8>(Kt + (kt * 2 + k2) * 16 * kPadPitch + 64 * dt), bs[k2],
                              dq[dt]);
+      sched_mfma_lds<8, 2, 4>();  // a transposed K^T pair per MFMA
     }
     wait_vm();
     __syncthreads();
