@@ -1071,6 +1071,8 @@ void nsa_dkdv_seg_kernel(NsaParams p) {
           dkt[dt] = E::mfma32(ptile_tr<V8>(Qt2 + k2 * 16 * kPadPitch + 64 * (dt - 2)), bd[k2],
                               dkt[dt]);
       }
+      // a transposed dO^T / Q^T pair per MFMA, four reads ahead
+      if constexpr (DQK == 128) sched_mfma_lds<16, 2, 4>();
       wait_vm();
       __syncthreads();
       buf ^= 1;
